@@ -1,0 +1,428 @@
+"""Plain fp64 CPU oracle for one CSA2 sparse-attention layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+HIP library (no kernels, headers, helpers, tables or constants) and imports
+nothing from the ``sparse_long_context_csa2_amd`` package.
+
+Every value is upcast exactly to float64 (bf16 bits by shifting, e4m3 codes
+through the decoder below, written from the format definition) and all
+arithmetic is float64.  Each function follows one step of the method as the
+pages describe it; the docstrings name the page and section.  The pages are:
+
+* [V41F]  "DeepSeek V4.1-Flash. Every layer, connected." (interactive figure
+          captions: "The query and output paths", "The global and index
+          paths", the hierarchy toy caption).
+* [EXPL]  "DeepSeek-V4.1-Flash explained" (section 2 "CSA2: share memory
+          without copying the answer", section 3 "Hierarchical indexing:
+          search broadly once", section 7 on the FP4 global KV).
+* [COURSE] "Create DeepSeek from scratch" (lesson "How CSA2 compresses,
+          shares, and selects attention memory"; lesson 06 "Indexer and
+          attention" with its Top-K worked example and unit test; lesson 07
+          "Hierarchical indexing").
+* [INSIDE] "DeepSeek V4 Inside: One Token Through Every Block" (sections
+          "What does layer 0 sliding-window attention do to p?" with eq. (27),
+          "How does CSA compress 8 tokens into 4 KV entries?" with Figs. 9-11,
+          "What does HCA change?").
+
+Readings taken where the pages are silent or disagree (each also listed in
+the design notes of the repository):
+
+* mask first, then Top-K over visible records only (fewer than K visible:
+  take all of them);
+* ties in Top-K go to the lower record id, ties in the block pool to the
+  lower block id;
+* a Full layer that also builds a pool still takes its own Top-K over all
+  visible records; the pool serves the later Reindex layers;
+* the window holds positions max(0, t-W+1) .. t (the query itself included);
+* a selected global record and a window row of the same token are two
+  separate entries (no de-duplication);
+* attention scale 1/sqrt(D) over the whole latent; the sink logit is not
+  scaled and carries no value row;
+* rotary pairs are adjacent (D-r+2j, D-r+2j+1) with angle pos*base^(-2j/r)
+  -- parity unpinned for r > 2 (the pages print one pair only);
+* caches and queries are stored after RoPE, so only the output is rotated
+  (by -t) here.
+
+Nothing in this module is blocked, fused or reordered beyond the definition.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+# --------------------------------------------------------------------------
+# Storage decoders (exact upcasts)
+# --------------------------------------------------------------------------
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 stored as uint16 bit patterns -> float64 (exact).
+
+    A bf16 value is the upper half of an IEEE binary32, so shifting the bits
+    up by 16 gives the float32 with the same value.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _e4m3_value(code: int) -> float:
+    """Value of one OCP e4m3fn code: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal, S.1111.111 is NaN, no infinities.
+    """
+    s = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 3) & 0xF
+    mant = code & 0x7
+    if e == 0xF and mant == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (mant / 8.0) * 2.0 ** (-6)
+    return s * (1.0 + mant / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """e4m3fn codes (uint8) -> float64 (exact)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def dequant(arr: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Storage array -> float64 values.
+
+    float32 and float64 arrays are upcast, uint16 arrays are bf16 bit
+    patterns, uint8 arrays are e4m3 codes and then need ``scale``: one value
+    per row (the array's shape without its last axis).  Quantized cache rows
+    hold code*scale ([COURSE] FP4 lesson, "Quantize after RoPE": values are
+    dequantized before attention).
+    """
+    a = np.asarray(arr)
+    if a.dtype == np.float32 or a.dtype == np.float64:
+        out = a.astype(np.float64)
+    elif a.dtype == np.uint16:
+        out = decode_bf16(a)
+    elif a.dtype == np.uint8:
+        if scale is None:
+            raise ValueError("e4m3 storage needs a per-row scale")
+        out = decode_e4m3(a) * np.asarray(scale, dtype=np.float64)[..., None]
+        return out
+    else:
+        raise TypeError(f"unsupported storage dtype {a.dtype}")
+    if scale is not None:
+        raise ValueError("scale given for a non-quantized array")
+    return out
+
+
+# --------------------------------------------------------------------------
+# Method steps
+# --------------------------------------------------------------------------
+
+
+def visible_records(n_rec: int, m: int, t: int) -> np.ndarray:
+    """Ids of the global records a query at absolute position t may use.
+
+    Record s covers tokens m*s .. m*s+m-1 and is visible only when every
+    token it covers is at or before the query ([INSIDE] "How does CSA
+    compress 8 tokens into 4 KV entries?": an entry is visible only if every
+    token in it is <= the query; [V41F] "The global and index paths": the
+    selection is causal).  Positions are 0-based.
+    """
+    s = np.arange(n_rec, dtype=np.int64)
+    return s[m * s + m - 1 <= t]
+
+
+def index_scores(q_idx: np.ndarray, w: np.ndarray, k_rows: np.ndarray) -> np.ndarray:
+    """Lightning-indexer scores of one query against a list of key rows.
+
+    I[s] = sum_h w[h] * max(0, q_idx[h] . k[s])  ([V41F] "The global and
+    index paths": rectified query-key products combined across 32 weighted
+    heads; [INSIDE] Fig. 10: score, ReLU, rank).
+
+    q_idx: [Hi][Di], w: [Hi], k_rows: [n][Di]  ->  [n], all float64.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    k_rows = np.asarray(k_rows, dtype=np.float64)
+    if k_rows.shape[0] == 0:
+        return np.zeros(0, dtype=np.float64)
+    dots = k_rows @ q_idx.T  # [n][Hi]
+    return np.maximum(dots, 0.0) @ w
+
+
+def top_k(scores: np.ndarray, rec_ids: np.ndarray, k: int) -> np.ndarray:
+    """Addresses of the k best candidates, best first.
+
+    Order: score descending, then record id ascending; the first
+    min(k, n) are kept.  Returns record ids, never scores ([COURSE] lesson 06
+    worked example: keep the positions, not the score values; its unit test
+    sorts by (-score, position); ties use the lower position).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    rec_ids = np.asarray(rec_ids, dtype=np.int64)
+    order = np.lexsort((rec_ids, -scores))
+    return rec_ids[order[: min(k, len(order))]]
+
+
+def block_pool(scores: np.ndarray, rec_ids: np.ndarray, blk: int, p: int) -> np.ndarray:
+    """Hierarchical block pool of one query: ids of the kept blocks.
+
+    Records are grouped into blocks of ``blk`` consecutive ids; a block's
+    score is the maximum score among its candidate (visible) records; the
+    ``p`` best blocks are kept, ordered by block score descending then block
+    id ascending ([V41F] hierarchy caption: each block's score is the maximum
+    among its positions; [EXPL] section 3; [COURSE] lesson 07 "24 positions ->
+    8 candidates").  Blocks with no candidate record are not candidates.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    rec_ids = np.asarray(rec_ids, dtype=np.int64)
+    if len(rec_ids) == 0:
+        return np.zeros(0, dtype=np.int64)
+    blocks = rec_ids // blk
+    ids = np.unique(blocks)
+    beta = np.array([scores[blocks == b].max() for b in ids], dtype=np.float64)
+    order = np.lexsort((ids, -beta))
+    return ids[order[: min(p, len(order))]]
+
+
+def pool_records(pool_blocks: Sequence[int], vis: np.ndarray, blk: int) -> np.ndarray:
+    """Candidate records of a Reindex layer: every visible record whose block
+    is in the pool ([COURSE] lesson 07: the pool includes every position of
+    the selected blocks; later indexers search only the pool)."""
+    kept = set(int(b) for b in pool_blocks if int(b) >= 0)
+    vis = np.asarray(vis, dtype=np.int64)
+    mask = np.array([int(s) // blk in kept for s in vis], dtype=bool)
+    return vis[mask] if len(vis) else vis
+
+
+def window_positions(t: int, w: int) -> np.ndarray:
+    """Local sliding-window positions of a query at t: max(0, t-W+1) .. t
+    ([INSIDE] layer-0 SWA: with window 2 the query sees the previous token
+    and itself)."""
+    return np.arange(max(0, t - w + 1), t + 1, dtype=np.int64)
+
+
+def sink_softmax(z: np.ndarray, sink: float):
+    """Softmax with a learned sink logit in the denominator only.
+
+    weight_j = exp(z_j) / (sum_k exp(z_k) + exp(sink))  ([INSIDE] eq. (27)).
+    Evaluated with the usual max shift.  Returns (weights, sink_mass).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    a = max(float(z.max()) if z.size else NEG_INF, float(sink))
+    if a == NEG_INF:
+        return np.zeros_like(z), 0.0
+    e = np.exp(z - a)
+    es = math.exp(sink - a) if sink != NEG_INF else 0.0
+    den = e.sum() + es
+    return e / den, es / den
+
+
+def rope_rotate(x: np.ndarray, pos: float, rope_dims: int, base: float) -> np.ndarray:
+    """Rotate the last ``rope_dims`` channels of x by position ``pos``.
+
+    Pairs are (D-r+2j, D-r+2j+1); pair j turns by pos*base^(-2j/r) with
+    (x, y) -> (x cos - y sin, x sin + y cos) ([INSIDE] layer-0 SWA: RoPE on
+    the last 2 dims at position 3).  Channels before the tail are unchanged.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    D = x.shape[-1]
+    r = int(rope_dims)
+    if r == 0:
+        return x
+    for j in range(r // 2):
+        theta = pos * base ** (-2.0 * j / r)
+        c, s = math.cos(theta), math.sin(theta)
+        i0 = D - r + 2 * j
+        a = x[..., i0].copy()
+        b = x[..., i0 + 1].copy()
+        x[..., i0] = a * c - b * s
+        x[..., i0 + 1] = a * s + b * c
+    return x
+
+
+def inverse_rope(x: np.ndarray, t: int, rope_dims: int, base: float) -> np.ndarray:
+    """Rotate the output's rotary tail by position -t ([V41F] "The query and
+    output paths": inverse RoPE on the output's rotary coordinates; [INSIDE]
+    Fig. 12: RoPE with position -i, because K = V carry absolute positions)."""
+    return rope_rotate(x, -float(t), rope_dims, base)
+
+
+def attend(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, sm: float) -> np.ndarray:
+    """Shared-latent MQA over a list of entries, one sink per head.
+
+    Every head reads the same rows as key and value ([INSIDE] Fig. 11: the
+    same entry is K and V; [V41F] "The global and index paths").
+    z[h, j] = sm * q[h] . x_j; ctx[h] = sum_j weight[h, j] x_j with the sink
+    softmax of eq. (27).
+
+    q: [H][D], rows: [n][D], sink: [H] -> ctx [H][D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    H, D = q.shape
+    ctx = np.zeros((H, D), dtype=np.float64)
+    if rows.shape[0] == 0:
+        return ctx
+    z = sm * (q @ rows.T)  # [H][n]
+    for h in range(H):
+        wts, _ = sink_softmax(z[h], float(sink[h]))
+        ctx[h] = wts @ rows
+    return ctx
+
+
+# --------------------------------------------------------------------------
+# One query of one layer, and a sharing group of layers
+# --------------------------------------------------------------------------
+
+FULL, REINDEX, REUSE = "full", "reindex", "reuse"
+
+
+def _n_rec(shared: Dict, b: int) -> int:
+    n_rec = shared.get("n_rec")
+    N = shared["N"]
+    return int(N if n_rec is None else n_rec[b])
+
+
+def layer_query(shared: Dict, layer: Dict, b: int, ti: int, mode: str,
+                prev_sel: Optional[np.ndarray] = None,
+                pool_in: Optional[np.ndarray] = None,
+                build_pool: bool = False,
+                sel_override: Optional[np.ndarray] = None) -> Dict:
+    """All steps of one CSA2 layer for query token ``ti`` of sequence ``b``.
+
+    Modes follow [EXPL] section 2's table: Full builds keys and takes a fresh
+    Top-K, Reindex reuses keys but takes a fresh Top-K (restricted to the
+    pool when one is given, [EXPL] section 3), Reuse keeps the preceding
+    Top-K list and runs no indexer.  Every mode computes a fresh output with
+    the layer's own query, local rows and sink.
+
+    ``shared``: N, m, k_idx [B][N][Di] (+ k_scale [B][N]), kv [B][N][D]
+    (+ kv_scale), optional n_rec [B].
+    ``layer``: q_pos [B][Tq], q_idx [B][Tq][Hi][Di], w [B][Tq][Hi],
+    q [B][Tq][H][D], swa [B][S][D] (+ swa_scale [B][S]), sink [H], K, W,
+    rope_dims, rope_base, sm_scale (0 means 1/sqrt(D)), and blk/P for pools.
+    ``sel_override`` replaces the selection (used to evaluate attention on
+    another admissible index set).
+
+    Returns dict(out [H][D], sel (record ids, best first), cand, scores
+    (over cand), pool (block ids or None), n_scored).
+    """
+    m = int(shared["m"])
+    t = int(layer["q_pos"][b, ti])
+    vis = visible_records(_n_rec(shared, b), m, t)
+    res: Dict = {"pool": None, "n_scored": 0, "cand": None, "scores": None}
+
+    if mode == REUSE:
+        if prev_sel is None:
+            raise ValueError("Reuse needs the preceding index set")
+        sel = np.asarray(prev_sel, dtype=np.int64)
+    else:
+        if mode == FULL:
+            cand = vis
+        elif mode == REINDEX:
+            cand = vis if pool_in is None else pool_records(pool_in, vis, int(layer["blk"]))
+        else:
+            raise ValueError(mode)
+        k_rows = dequant(shared["k_idx"][b][cand],
+                         None if shared.get("k_scale") is None else shared["k_scale"][b][cand])
+        q_i = dequant(layer["q_idx"][b, ti])
+        w = np.asarray(layer["w"][b, ti], dtype=np.float64)
+        sc = index_scores(q_i, w, k_rows)
+        res["cand"], res["scores"], res["n_scored"] = cand, sc, len(cand)
+        sel = top_k(sc, cand, int(layer["K"]))
+        if build_pool:
+            res["pool"] = block_pool(sc, cand, int(layer["blk"]), int(layer["P"]))
+    if sel_override is not None:
+        sel = np.asarray(sel_override, dtype=np.int64)
+    res["sel"] = sel
+
+    sel_valid = sel[(sel >= 0) & (sel < shared["N"])]
+    glob = dequant(shared["kv"][b][sel_valid],
+                   None if shared.get("kv_scale") is None else shared["kv_scale"][b][sel_valid])
+    S = layer["swa"].shape[1]
+    pos = window_positions(t, int(layer["W"]))
+    slots = pos % S
+    loc = dequant(layer["swa"][b][slots],
+                  None if layer.get("swa_scale") is None else layer["swa_scale"][b][slots])
+    rows = np.concatenate([glob, loc], axis=0)
+    q = dequant(layer["q"][b, ti])
+    D = q.shape[-1]
+    sm = float(layer.get("sm_scale", 0.0)) or 1.0 / math.sqrt(D)
+    ctx = attend(q, rows, np.asarray(layer["sink"], dtype=np.float64), sm)
+    res["out"] = inverse_rope(ctx, t, int(layer["rope_dims"]), float(layer["rope_base"]))
+    return res
+
+
+def group_query(shared: Dict, layers: List[Dict], b: int, ti: int) -> List[Dict]:
+    """A sharing group for one query: layer modes in order (e.g. Full,
+    Reindex, Reindex, Reuse, Reuse).  A Full layer with ``build_pool`` set
+    builds the candidate pool that later Reindex layers search ([EXPL]
+    section 3; [COURSE] lesson 07); Reuse takes the most recent Full or
+    Reindex selection ([COURSE] lesson 06: Reuse keeps the preceding list).
+    """
+    out: List[Dict] = []
+    prev_sel = None
+    pool = None
+    for lay in layers:
+        mode = lay["mode"]
+        r = layer_query(shared, lay, b, ti, mode, prev_sel=prev_sel,
+                        pool_in=pool if mode == REINDEX else None,
+                        build_pool=bool(lay.get("build_pool", False)) and mode == FULL)
+        if mode == FULL and r["pool"] is not None:
+            pool = r["pool"]
+        if mode in (FULL, REINDEX):
+            prev_sel = r["sel"]
+        out.append(r)
+    return out
+
+
+def full_row_scores(shared: Dict, layer: Dict, b: int, ti: int) -> np.ndarray:
+    """Indexer scores of one query over all N record columns, -inf where the
+    record is not visible (the Full-mode scoring row)."""
+    N = int(shared["N"])
+    t = int(layer["q_pos"][b, ti])
+    vis = visible_records(_n_rec(shared, b), int(shared["m"]), t)
+    row = np.full(N, NEG_INF, dtype=np.float64)
+    if len(vis):
+        k_rows = dequant(shared["k_idx"][b][vis],
+                         None if shared.get("k_scale") is None else shared["k_scale"][b][vis])
+        row[vis] = index_scores(dequant(layer["q_idx"][b, ti]),
+                                np.asarray(layer["w"][b, ti], dtype=np.float64), k_rows)
+    return row
+
+
+def pool_row_scores(shared: Dict, layer: Dict, b: int, ti: int,
+                    pool_blocks: np.ndarray, blk: int) -> np.ndarray:
+    """Indexer scores over the P*blk pool columns of one query: column c is
+    record pool[c // blk]*blk + c % blk; -inf where that block slot is empty
+    or the record is not visible."""
+    P = len(pool_blocks)
+    t = int(layer["q_pos"][b, ti])
+    n_rec = _n_rec(shared, b)
+    m = int(shared["m"])
+    row = np.full(P * blk, NEG_INF, dtype=np.float64)
+    cols, recs = [], []
+    for c in range(P * blk):
+        pb = int(pool_blocks[c // blk])
+        if pb < 0:
+            continue
+        s = pb * blk + c % blk
+        if s >= n_rec or m * s + m - 1 > t:
+            continue
+        cols.append(c)
+        recs.append(s)
+    if cols:
+        recs = np.asarray(recs, dtype=np.int64)
+        k_rows = dequant(shared["k_idx"][b][recs],
+                         None if shared.get("k_scale") is None else shared["k_scale"][b][recs])
+        row[np.asarray(cols)] = index_scores(dequant(layer["q_idx"][b, ti]),
+                                             np.asarray(layer["w"][b, ti], dtype=np.float64),
+                                             k_rows)
+    return row

@@ -1,0 +1,407 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: numbers
+the pages print for a worked example (fixtures under tests/golden/ with
+their citation), closed forms, library routines (torch, scipy) on special
+cases, brute force on tiny inputs, and invariants of the method.  Every
+oracle function is covered so that a dropped term, a wrong sign or index or
+a transposed operand fails at least one test.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+from sparse_long_context_csa2_amd import workloads as WL
+from tests.conftest import golden
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- eq. (27)
+
+def test_sink_softmax_layer0_printed_values():
+    g = golden("sink_softmax_layer0_swa.json")
+    wts, sink_mass = O.sink_softmax(np.array(g["logits"]), g["sink"])
+    assert np.allclose(wts, g["weights"], atol=1e-4)
+    assert abs(sink_mass - g["sink_mass"]) < 1e-4
+    assert abs(wts.sum() + sink_mass - 1.0) < 1e-12
+    # the printed denominator: exponentials without a max shift
+    den = sum(math.exp(z) for z in g["logits"]) + math.exp(g["sink"])
+    assert abs(den - g["den"]) < 1e-4
+
+
+def test_layer0_logit_from_rotated_q_and_k():
+    """The printed score of key p is scale * q.k where q and k were both
+    rotated at position 3: the dot is invariant under the common rotation,
+    so the unrotated head vectors give the printed q.k and logit."""
+    g = golden("sink_softmax_layer0_swa.json")
+    q = np.array(g["q_head1"])
+    k = np.array(g["k_p_head1"])
+    qr = O.rope_rotate(q, 3, 2, 10000.0)
+    kr = O.rope_rotate(k, 3, 2, 10000.0)
+    assert abs(float(qr @ kr) - g["qk_p"]) < 1e-4
+    # the oracle's attention logit path: z = sm * q.k with sm = 1/sqrt(D)
+    ctx = O.attend(qr[None, :], kr[None, :], np.array([-np.inf]), 1.0 / math.sqrt(4))
+    assert np.allclose(ctx[0], kr)  # one entry and no sink: all weight on it
+    z = (1.0 / math.sqrt(4)) * float(qr @ kr)
+    assert abs(z - g["logits"][1]) < 1e-4
+
+
+def test_joint_softmax_record_and_window_printed_values():
+    g = golden("csa_core_sink_weights.json")
+    wts, sink_mass = O.sink_softmax(np.array(g["logits"]), g["sink"])
+    assert np.allclose(wts, g["weights"], atol=1e-4)
+    assert abs(sink_mass - g["sink_mass"]) < 1e-3
+
+
+def test_sink_minus_infinity_is_textbook_softmax():
+    """With no sink the weights are the ordinary softmax (scipy), checked on
+    the two-query toy of the course's lesson 06 (keys [[2,0],[0,2],[1,1]],
+    scale 1/sqrt(2))."""
+    keys = np.array([[2.0, 0.0], [0.0, 2.0], [1.0, 1.0]])
+    for q in (np.array([0.0, 1.0]), np.array([1.0, 0.0])):
+        z = keys @ q / math.sqrt(2)
+        wts, sm = O.sink_softmax(z, -np.inf)
+        assert np.allclose(wts, scipy.special.softmax(z), atol=1e-15)
+        assert sm == 0.0
+    # values for query A: p = (0.140, 0.576, 0.284) -> o = (0.282, 0.718)
+    z = keys @ np.array([0.0, 1.0]) / math.sqrt(2)
+    wts, _ = O.sink_softmax(z, -np.inf)
+    vals = np.array([[1.0, 0.0], [0.0, 1.0], [0.5, 0.5]])
+    assert np.allclose(wts, [0.140, 0.576, 0.284], atol=1e-3)
+    assert np.allclose(wts @ vals, [0.282, 0.718], atol=1e-3)
+
+
+def test_sink_large_and_small_limits():
+    z = np.array([0.3, -0.2, 1.1])
+    w_big, m_big = O.sink_softmax(z, 60.0)
+    assert m_big >= 1 - 1e-15 and w_big.max() < 1e-20
+    w_small, m_small = O.sink_softmax(z, -60.0)
+    assert np.allclose(w_small, scipy.special.softmax(z), atol=1e-20)
+    # adding a constant to every logit and the sink changes nothing
+    w_a, m_a = O.sink_softmax(z + 5.0, -1.0 + 5.0)
+    w_b, m_b = O.sink_softmax(z, -1.0)
+    assert np.allclose(w_a, w_b, atol=1e-15) and abs(m_a - m_b) < 1e-15
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_position3_printed_pair():
+    g = golden("rope_position3.json")
+    assert abs(math.cos(3) - g["cos"]) < 1e-4 and abs(math.sin(3) - g["sin"]) < 1e-4
+    x = np.array([0.0, 0.0] + g["pair_in"])
+    y = O.rope_rotate(x, g["position"], 2, 10000.0)
+    assert np.allclose(y[2:], g["pair_out"], atol=g["tolerance"])
+    assert np.all(y[:2] == 0.0)
+
+
+def test_inverse_rope_restores_and_matches_complex_rotation():
+    rng = np.random.default_rng(5)
+    D, r, base = 16, 8, 10000.0
+    x = rng.standard_normal((3, D))
+    for t in (0, 1, 7, 1048576):
+        y = O.rope_rotate(x, t, r, base)
+        assert np.allclose(O.inverse_rope(y, t, r, base), x, atol=1e-9)
+        # independent form: pairs as complex numbers times exp(i*theta)
+        j = np.arange(r // 2)
+        theta = t * base ** (-2.0 * j / r)
+        tail = x[:, D - r:].reshape(3, r // 2, 2)
+        c = (tail[..., 0] + 1j * tail[..., 1]) * np.exp(1j * theta)
+        ref = np.concatenate([x[:, :D - r], np.stack([c.real, c.imag], -1).reshape(3, r)], 1)
+        assert np.allclose(y, ref, atol=1e-9)
+        # norms of each pair are preserved, non-rotary channels untouched
+        assert np.allclose(y[:, :D - r], x[:, :D - r])
+
+
+# ---------------------------------------------------------------- Top-K
+
+def test_topk_worked_example_and_unit_test():
+    g = golden("topk_worked_example.json")
+    for case in g["cases"]:
+        n = len(case["scores"])
+        sel = O.top_k(np.array(case["scores"]), np.arange(n), case["k"])
+        assert list(sel) == case["selected"]
+        assert [case["values"][i] for i in sel] == case["retrieved"]
+
+
+def test_topk_brute_force_with_ties():
+    """Against a plain Python sort on tiny inputs full of ties."""
+    rng = np.random.default_rng(1)
+    for trial in range(200):
+        n = int(rng.integers(0, 12))
+        scores = rng.integers(0, 4, size=n).astype(np.float64) / 4
+        ids = rng.permutation(40)[:n]
+        k = int(rng.integers(1, 8))
+        ref = sorted(zip(scores, ids), key=lambda p: (-p[0], p[1]))[:k]
+        got = O.top_k(scores, ids, k)
+        assert list(got) == [int(i) for _, i in ref]
+
+
+def test_mask_then_select_printed_example():
+    g = golden("indexer_causal_mask.json")
+    s = np.array(g["scores"])
+    # unmasked ranking as printed
+    assert list(O.top_k(s, np.arange(4), g["k"])) == g["top2_unmasked"]
+    # CSA2 records are non-overlapping groups of m=2 tokens: at t=2 only
+    # record 0 (tokens 0, 1) is complete
+    vis = O.visible_records(4, 2, 2)
+    assert list(vis) == [0]
+    assert list(O.top_k(s[vis], vis, g["k"])) == g["selected_after_mask"]
+
+
+def test_visibility_closed_form():
+    # m = 4: record s visible iff 4s+3 <= t, i.e. floor((t+1)/4) records
+    for t in range(0, 40):
+        assert len(O.visible_records(1024, 4, t)) == (t + 1) // 4
+    # decode at t = L sees every one of the N = L/4 records
+    assert len(O.visible_records(16384, 4, 65536)) == 16384
+    assert len(O.visible_records(128, 1, 5)) == 6
+    # C2: visible (t, s) pairs over the prefill triangle
+    tot = sum(min(1024, (t + 1) // 4) for t in range(4096))
+    assert tot == 2_096_128
+
+
+# ---------------------------------------------------------------- indexer
+
+def test_index_scores_naive_loop_and_scaling():
+    rng = np.random.default_rng(2)
+    Hi, Di, n = 3, 5, 7
+    q = rng.standard_normal((Hi, Di))
+    w = rng.random(Hi)
+    k = rng.standard_normal((n, Di))
+    got = O.index_scores(q, w, k)
+    ref = np.zeros(n)
+    for s in range(n):
+        for h in range(Hi):
+            dot = 0.0
+            for i in range(Di):
+                dot += q[h, i] * k[s, i]
+            ref[s] += w[h] * (dot if dot > 0 else 0.0)
+    assert np.allclose(got, ref, atol=1e-14)
+    # positive scaling of w or of the keys scales the scores, keeps the order
+    assert np.allclose(O.index_scores(q, 3.0 * w, k), 3.0 * got)
+    assert np.allclose(O.index_scores(q, w, 2.5 * k), 2.5 * got)
+    assert list(O.top_k(O.index_scores(q, 7 * w, k), np.arange(n), 3)) == \
+        list(O.top_k(got, np.arange(n), 3))
+    # a head whose products are all negative contributes nothing
+    q2 = q.copy()
+    q2[0] = -np.abs(q[0])
+    k2 = np.abs(k)
+    only12 = O.index_scores(q2[1:], w[1:], k2)
+    assert np.allclose(O.index_scores(q2, w, k2), only12)
+
+
+# ---------------------------------------------------------------- pool
+
+def test_pool_24_positions_structure():
+    g = golden("pool_24_positions.json")
+    n, blk, keep = g["positions"], g["block"], g["keep"]
+    rng = np.random.default_rng(3)
+    s = rng.random(n) * 0.5
+    # give the two printed winning blocks the largest maxima
+    for lo, hi in g["winning_blocks_1based_positions"]:
+        s[lo - 1 + 2] = 0.9 + 0.01 * lo
+    pool = O.block_pool(s, np.arange(n), blk, keep)
+    recs = O.pool_records(pool, np.arange(n), blk)
+    assert sorted(int(r) + 1 for r in recs) == g["candidate_pool_1based"]
+    assert len(recs) == blk * keep
+
+
+def test_pool_brute_force_and_partial_blocks():
+    rng = np.random.default_rng(4)
+    for trial in range(100):
+        n = int(rng.integers(1, 30))
+        blk = int(rng.integers(1, 6))
+        p = int(rng.integers(1, 6))
+        vis = np.arange(n)[: int(rng.integers(0, n + 1))]
+        s = rng.integers(0, 3, size=len(vis)).astype(np.float64)
+        got = O.block_pool(s, vis, blk, p)
+        # brute force: every block with a visible member, scored by the max
+        blocks = {}
+        for r, v in zip(vis, s):
+            blocks[int(r) // blk] = max(blocks.get(int(r) // blk, -np.inf), v)
+        ref = sorted(blocks.items(), key=lambda kv: (-kv[1], kv[0]))[:p]
+        assert list(got) == [b for b, _ in ref]
+        # the pool never contains an invisible record
+        assert set(O.pool_records(got, vis, blk)) <= set(int(v) for v in vis)
+
+
+def test_hierarchy_printed_count_closed_form():
+    g = golden("hierarchy_scored_positions.json")
+    assert g["blocks_kept"] * g["block_size"] == g["candidates"]
+    assert g["context"] + 4 * g["candidates"] == g["one_full_plus_four_pooled"]
+    assert round(g["five_full_scans"] / g["one_full_plus_four_pooled"], 2) == g["ratio_printed"]
+
+
+# ---------------------------------------------------------------- e4m3
+
+def test_e4m3_decoder_all_codes_against_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_bf16_decoder_against_torch():
+    rng = np.random.default_rng(6)
+    bits = rng.integers(0, 65536, size=4096, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = O.decode_bf16(bits)
+    same = np.isnan(ref) == np.isnan(ours)
+    assert same.all()
+    assert np.array_equal(ours[~np.isnan(ref)], ref[~np.isnan(ref)])
+
+
+def test_quantized_row_max_maps_to_448():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((50, 64)).astype(np.float32) / 8
+    codes, scale = WL.quantize_rows_e4m3(x)
+    deq = O.dequant(codes, scale)
+    am = np.abs(x).argmax(axis=1)
+    assert np.allclose(np.abs(deq[np.arange(50), am]), np.abs(x[np.arange(50), am]), rtol=1e-6)
+    assert np.all(np.abs(O.decode_e4m3(codes[np.arange(50), am])) == 448.0)
+    # relative quantization error of e4m3 is at most 2^-4 in the normal range
+    big = np.abs(x) > scale[:, None] * 2 ** -6
+    assert np.all(np.abs(deq - x)[big] <= np.abs(x)[big] * 2 ** -4 + 1e-12)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _dense_reference(shared, layer, b, ti):
+    """The whole layer as dense attention when K and the pool cover every
+    visible record: one torch fp64 softmax over [visible records | window |
+    one sink key with a zero value], then the inverse rotation done with
+    complex numbers."""
+    t = int(layer["q_pos"][b, ti])
+    vis = O.visible_records(shared["N"] if shared["n_rec"] is None else int(shared["n_rec"][b]),
+                            shared["m"], t)
+    glob = O.dequant(shared["kv"][b][vis], None if shared["kv_scale"] is None
+                     else shared["kv_scale"][b][vis])
+    pos = np.arange(max(0, t - layer["W"] + 1), t + 1)
+    S = layer["swa"].shape[1]
+    loc = O.dequant(layer["swa"][b][pos % S], None if layer["swa_scale"] is None
+                    else layer["swa_scale"][b][pos % S])
+    x = torch.from_numpy(np.concatenate([glob, loc], 0))
+    q = torch.from_numpy(O.dequant(layer["q"][b, ti]))
+    H, D = q.shape
+    logits = (q @ x.T) / math.sqrt(D)
+    sink = torch.from_numpy(np.asarray(layer["sink"], dtype=np.float64))[:, None]
+    p = torch.softmax(torch.cat([logits, sink], 1), dim=1)
+    ctx = (p[:, :-1] @ x).numpy()
+    r = layer["rope_dims"]
+    j = np.arange(r // 2)
+    theta = -t * layer["rope_base"] ** (-2.0 * j / r)
+    tail = ctx[:, D - r:].reshape(H, r // 2, 2)
+    c = (tail[..., 0] + 1j * tail[..., 1]) * np.exp(1j * theta)
+    return np.concatenate([ctx[:, :D - r], np.stack([c.real, c.imag], -1).reshape(H, r)], 1)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "e4m3"])
+def test_layer_equals_dense_softmax_when_everything_is_selected(kv_dtype):
+    wl = WL.Workload(name="dense", seed=11, B=2, Tq=24, N=6, m=4, Hi=3, Di=8, H=3, D=12,
+                     rope_dims=4, W=5, K=8, q_idx_dtype="f32", k_dtype=kv_dtype,
+                     q_dtype="f32", kv_dtype=kv_dtype, swa_dtype=kv_dtype, q_std=1.0,
+                     kv_std=1.0, w_dist="uniform")
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    for b in range(2):
+        for ti in range(24):
+            r = O.layer_query(sh, lay, b, ti, O.FULL)
+            ref = _dense_reference(sh, lay, b, ti)
+            assert np.allclose(r["out"], ref, atol=1e-12), (b, ti)
+
+
+def test_c1_hierarchy_invariant_and_counts():
+    """K <= P: Top-K over the pool equals Top-K over all visible records (a
+    block holding a global top-K record has a max at least the K-th score,
+    and at most K such blocks exist)."""
+    inp = WL.make_inputs(WL.CONFIGS["C1"])
+    sh, lay = inp["shared"], inp["layers"][0]
+    for ti in range(128):
+        r = O.layer_query(sh, lay, 0, ti, O.FULL, build_pool=True)
+        pool = r["pool"]
+        assert len(pool) == min(8, (ti + 1 + 3) // 4)
+        r2 = O.layer_query(sh, lay, 0, ti, O.REINDEX, pool_in=pool)
+        assert list(r2["sel"]) == list(r["sel"])
+        assert np.array_equal(r2["out"], r["out"])
+        assert len(r["sel"]) == min(8, ti + 1)
+        assert set(r["sel"]) <= set(range(ti + 1))
+        # the pool covers the whole visible range when P*blk >= |vis|
+        if ti + 1 <= 32:
+            assert sorted(O.pool_records(pool, np.arange(ti + 1), 4)) == list(range(ti + 1))
+
+
+def test_group_counts_and_reuse_identity():
+    """Scored records of a Full(+pool), Reindex, Reindex, Reuse, Reuse group
+    are N + 2*P*blk per query (the closed form behind the pages' 1 full scan +
+    pooled scans count); Reuse keeps the previous index set exactly and gives
+    the previous layer's output when fed that layer's q, window and sink."""
+    wl = WL.Workload(name="grp", seed=12, B=2, Tq=1, N=96, m=4, Hi=4, Di=8, H=4, D=16,
+                     rope_dims=4, W=6, K=5, blk=8, P=3, decode_pos=400,
+                     q_idx_dtype="f32", k_dtype="bf16", q_dtype="bf16", kv_dtype="bf16",
+                     swa_dtype="bf16", modes=("full+pool", "reindex", "reindex", "reuse", "reuse"))
+    inp = WL.make_inputs(wl)
+    sh, lays = inp["shared"], inp["layers"]
+    for b in range(2):
+        res = O.group_query(sh, lays, b, 0)
+        assert sum(r["n_scored"] for r in res) == 96 + 2 * 3 * 8
+        assert list(res[3]["sel"]) == list(res[2]["sel"]) == list(res[4]["sel"])
+        same = dict(lays[3])
+        for key in ("q", "swa", "swa_scale", "sink"):
+            same[key] = lays[2][key]
+        r_same = O.layer_query(sh, same, b, 0, O.REUSE, prev_sel=res[2]["sel"])
+        assert np.array_equal(r_same["out"], res[2]["out"])
+        assert not np.allclose(res[3]["out"], res[2]["out"])
+        # Reindex candidates stay inside the pool built by the Full layer
+        pool = res[0]["pool"]
+        assert set(int(s) // 8 for s in res[1]["sel"]) <= set(int(p) for p in pool)
+
+
+def test_causality_future_rows_do_not_matter():
+    wl = WL.Workload(name="caus", seed=13, B=1, Tq=40, N=10, m=4, Hi=2, Di=4, H=2, D=8,
+                     rope_dims=2, W=4, K=3, q_idx_dtype="f32", k_dtype="f32", q_dtype="f32",
+                     kv_dtype="f32", swa_dtype="f32", kv_std=1.0, q_std=1.0, w_dist="uniform")
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    for ti in (0, 3, 4, 17, 39):
+        base = O.layer_query(sh, lay, 0, ti, O.FULL)
+        t = ti
+        sh2 = dict(sh)
+        lay2 = dict(lay)
+        k2, kv2, swa2 = sh["k_idx"].copy(), sh["kv"].copy(), lay["swa"].copy()
+        fut = [s for s in range(10) if 4 * s + 3 > t]
+        k2[0, fut] += 5.0
+        kv2[0, fut] -= 3.0
+        swa2[0, t + 1:] *= -2.0
+        sh2.update(k_idx=k2, kv=kv2)
+        lay2.update(swa=swa2)
+        r = O.layer_query(sh2, lay2, 0, ti, O.FULL)
+        assert np.array_equal(r["out"], base["out"])
+        assert list(r["sel"]) == list(base["sel"])
+        assert set(base["sel"]) <= set(O.visible_records(10, 4, t))
+
+
+def test_full_row_and_pool_row_scores_agree_with_layer():
+    inp = WL.make_inputs(WL.CONFIGS["C1"])
+    sh, lay = inp["shared"], inp["layers"][0]
+    for ti in (0, 5, 63, 127):
+        r = O.layer_query(sh, lay, 0, ti, O.FULL, build_pool=True)
+        row = O.full_row_scores(sh, lay, 0, ti)
+        assert np.all(np.isinf(row[ti + 1:]))
+        assert np.array_equal(row[r["cand"]], r["scores"])
+        prow = O.pool_row_scores(sh, lay, 0, ti, r["pool"], 4)
+        for c in range(len(r["pool"]) * 4):
+            s = int(r["pool"][c // 4]) * 4 + c % 4
+            if s <= ti:
+                assert prow[c] == row[s]
+            else:
+                assert prow[c] == -np.inf
