@@ -1,0 +1,330 @@
+"""Benchmark of the CSA2 layer on one MI355X.
+
+Default workload: the Flash-shape prefill layer (1 sequence of 4096 query
+tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x 512
+latent with 64 rotary dims, window 128, bf16).  ``--workload`` selects one of
+the decode workloads instead.
+
+A step is one pass of the whole hot path over the workload's batch: for
+every layer of its sharing group, indexer scores (Full / Reindex), block
+pool (when the Full layer builds one), Top-K and sparse attention -- the
+same entry points, in the same order, that csa2_layer enqueues.  HIP
+events on the launch stream bracket each call, so each kernel's average
+duration over the timed steps is measured live; the dominant kernel's
+roofline is reported from it.  Inputs are resident in HBM before timing.
+
+One JSON line is printed.  The fp64 CPU oracle is also timed on a bounded
+sample of the same workload (``cpu_baseline``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- algorithmic work
+
+def entries_per_query(wl, inp):
+    """Selected records + window rows each query attends to (the method's
+    required reads, independent of the GPU's kernels)."""
+    q_pos = inp["layers"][0]["q_pos"]
+    n_rec = np.full(wl.B, wl.N) if wl.n_rec is None else np.asarray(wl.n_rec)
+    t = q_pos.astype(np.int64)
+    vis = np.minimum(n_rec[:, None], (t + 1) // wl.m)
+    sel = np.minimum(wl.K, vis)
+    win = np.minimum(wl.W, t + 1)
+    return sel, win, vis
+
+
+def kernel_work(wl, inp):
+    """Algorithmic bytes and flops per call of each step phase."""
+    elt = {"f32": 4, "bf16": 2, "e4m3": 1}
+    kbytes = wl.Di * elt[wl.k_dtype] + (4 if wl.k_dtype == "e4m3" else 0)
+    rbytes = wl.D * elt[wl.kv_dtype] + (4 if wl.kv_dtype == "e4m3" else 0)
+    qi_bytes = wl.Hi * wl.Di * elt[wl.q_idx_dtype] + wl.Hi * 4
+    q_bytes = wl.H * wl.D * elt[wl.q_dtype]
+    out_bytes = wl.H * wl.D * 4
+    sel, win, vis = entries_per_query(wl, inp)
+    rows = wl.B * wl.Tq
+    work = {}
+    # Full indexer: every visible record's key row once per sequence (decode)
+    # or the key tile set once (prefill, keys are L2-resident and counted once
+    # per sequence); per query its q_idx/w; flops 2*Hi*Di per visible pair.
+    pairs = int(vis.sum())
+    key_reads = int(vis.max(axis=1).sum()) if wl.Tq > 1 else pairs
+    work["index_full"] = dict(bytes=key_reads * kbytes + rows * qi_bytes,
+                              flops=2.0 * wl.Hi * wl.Di * pairs)
+    if wl.P:
+        cand = min(wl.P * wl.blk, wl.N)
+        work["index_pool"] = dict(bytes=rows * (cand * kbytes + qi_bytes),
+                                  flops=2.0 * wl.Hi * wl.Di * rows * cand)
+    ent = int((sel + win).sum())
+    # rows read: per sequence, the distinct records and local rows its queries
+    # need (a decode query's own set; a prefill sequence's records and window
+    # rows are shared by its tokens and read once)
+    t_max = inp["layers"][0]["q_pos"].max(axis=1) + 1
+    uniq = np.minimum(vis.max(axis=1), sel.sum(axis=1)) + np.minimum(np.minimum(wl.S, t_max), win.sum(axis=1))
+    work["attn"] = dict(bytes=int(uniq.sum()) * rbytes + rows * (q_bytes + out_bytes),
+                        flops=4.0 * wl.D * wl.H * ent)
+    return work
+
+
+# --------------------------------------------------------------- the timed step
+
+class Step:
+    """Enqueues the hot path of one workload through the ABI's entry points,
+    recording a HIP event between calls."""
+
+    def __init__(self, grp, torch):
+        from sparse_long_context_csa2_amd import binding as Bd
+        self.Bd, self.torch, self.grp = Bd, torch, grp
+        wl = grp.wl
+        self.calls = []  # (name, fn(copy))
+        dev = grp.device
+        rows = wl.B * wl.Tq
+        self.scores_full = torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device=dev)
+        self.scores_pool = None
+        if wl.P:
+            self.scores_pool = torch.empty((wl.B, wl.Tq, wl.P * wl.blk), dtype=torch.float32, device=dev)
+        nbp = Bd.lib().csa2_block_pool_workspace_bytes(rows, wl.N, wl.blk) if wl.P else 0
+        self.pool_ws = torch.empty(max(nbp, 256), dtype=torch.uint8, device=dev)
+        na = Bd.lib().csa2_sparse_attn_workspace_bytes(wl.B, wl.Tq, wl.H, wl.D, wl.K, wl.W)
+        self.attn_ws = torch.empty(max(na, 256), dtype=torch.uint8, device=dev)
+        for li, lay in enumerate(grp.layers):
+            mode = lay["mode"]
+            if mode == "full":
+                self.calls.append(("index_full", self._index(lay, None)))
+                if lay["build_pool"]:
+                    self.calls.append(("block_pool", self._pool(lay)))
+                self.calls.append(("topk_full", self._topk(lay, li, pooled=False)))
+            elif mode == "reindex":
+                self.calls.append(("index_pool", self._index(lay, grp.pool)))
+                self.calls.append(("topk_pool", self._topk(lay, li, pooled=True)))
+            self.calls.append(("attn", self._attn(lay, li)))
+
+    def _index(self, lay, pool):
+        Bd, grp = self.Bd, self.grp
+
+        def f(copy):
+            sh = grp.shared[copy]
+            out = self.scores_full if pool is None else self.scores_pool
+            Bd.csa2_index_scores(lay["q_idx"], lay["w"], sh["k_idx"], sh["k_scale"], lay["q_pos"], sh["m"],
+                                 n_rec=sh["n_rec"], pool=pool, blk=lay["blk"] if pool is not None else 0, out=out)
+        return f
+
+    def _pool(self, lay):
+        def f(copy):
+            self.Bd.csa2_block_pool(self.scores_full, lay["blk"], lay["P"], out=self.grp.pool, ws=self.pool_ws)
+        return f
+
+    def _topk(self, lay, li, pooled):
+        def f(copy):
+            if pooled:
+                self.Bd.csa2_topk(self.scores_pool, lay["K"], pool=self.grp.pool, blk=lay["blk"],
+                                  out=self.grp.idx[li])
+            else:
+                self.Bd.csa2_topk(self.scores_full, lay["K"], out=self.grp.idx[li])
+        return f
+
+    def _attn(self, lay, li):
+        def f(copy):
+            sh = self.grp.shared[copy]
+            self.Bd.csa2_sparse_attn(lay["q"], sh["kv"], sh["kv_scale"], self.grp.idx[li], lay["swa"],
+                                     lay["swa_scale"], lay["W"], lay["q_pos"], lay["sink"], lay["rope_dims"],
+                                     lay["rope_base"], lay["sm_scale"], out=lay["out"], ws=self.attn_ws)
+        return f
+
+    def run(self, copy, events=None):
+        for i, (_, fn) in enumerate(self.calls):
+            if events is not None:
+                events[i].record()
+            fn(copy)
+        if events is not None:
+            events[len(self.calls)].record()
+
+
+# --------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of query rows of
+    the same workload (spread over the batch and the sequence)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        threads = 1
+    wl = inp["wl"]
+    rows = [(b, t) for t in range(wl.Tq) for b in range(wl.B)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(rows))
+    sh, lays = inp["shared"], inp["layers"]
+    done = 0
+    t0 = time.perf_counter()
+    for k in order:
+        b, ti = rows[k]
+        O.group_query(sh, lays, b, ti)
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(rows)} query rows of the same workload (random order), "
+                      f"{len(lays)} layer(s) each, fp64 NumPy, {dt:.1f} s"}
+
+
+def traffic_for(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_long_context_csa2_amd import runner as R
+    from sparse_long_context_csa2_amd import workloads as WL
+
+    wl = WL.CONFIGS[args.workload]
+    inp = WL.make_inputs(wl)
+    decode = wl.decode_pos is not None
+    copies = args.copies or (2 if decode else 1)
+    grp = R.DeviceGroup(inp, device="cuda:0", copies=copies)
+    step = Step(grp, torch)
+    ncalls = len(step.calls)
+
+    for i in range(args.warmup):
+        step.run(i % copies)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step.run(s % copies, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {}
+    for s in range(args.steps):
+        for i, (name, _) in enumerate(step.calls):
+            per_call.setdefault(name, []).append(evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3)
+    step_s = [evs[s][0].elapsed_time(evs[s][ncalls]) * 1e-3 for s in range(args.steps)]
+    ms_per_step = 1e3 * float(np.mean(step_s))
+    tokens = wl.B * wl.Tq
+    value = tokens / (ms_per_step * 1e-3)
+
+    # csa2_layer itself, same work, for reference
+    for i in range(2):
+        grp.run(i % copies)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(args.steps):
+        grp.run(s % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / args.steps
+
+    work = kernel_work(wl, inp)
+    kern = {}
+    for name, ts in per_call.items():
+        key = "attn" if name == "attn" else name
+        ntimes = sum(1 for n, _ in step.calls if n == name)
+        avg = float(np.mean(ts))
+        kern[name] = {"avg_us": round(avg * 1e6, 2), "calls_per_step": ntimes}
+        if key in work:
+            w = work[key]
+            kern[name]["GB_s"] = round(w["bytes"] / avg / 1e9, 1)
+            kern[name]["TFLOP_s"] = round(w["flops"] / avg / 1e12, 2)
+    # dominant kernel: the largest share of the step
+    dom = max(per_call, key=lambda n: float(np.sum(per_call[n])))
+    w = work.get(dom)
+    avg = float(np.mean(per_call[dom]))
+    if w is not None:
+        t_hbm = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = w["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        if t_mfma > t_hbm:
+            ach, peak, unit, bound = w["flops"] / avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        else:
+            ach, peak, unit, bound = w["bytes"] / avg / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": traffic_for(args.workload, dom), "kernel": dom,
+                "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"], "avg_us": round(avg * 1e6, 2)}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None, "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    line = {
+        "metric": "CSA2 layer query-tokens/s (prefill & decode) + % of HBM/MFMA peak, 1 GPU",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[wl.kv_dtype],
+        "data": "synthetic (seeded N(0,1/d) inputs of the workload's shapes)",
+        "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
+                   "H": wl.H, "D": wl.D, "K": wl.K, "W": wl.W, "blk": wl.blk, "P": wl.P,
+                   "layers": list(wl.modes), "cache_copies": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "layer_api_ms_per_step": round(layer_ms, 4),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,277 @@
+/*
+ * csa2.h -- C ABI of the MI355X (gfx950) CSA2 sparse-attention layer.
+ *
+ * One CSA2 layer separates three operations: creating memory, selecting
+ * positions and attending to those positions ("DeepSeek-V4.1-Flash
+ * explained", section 2 "CSA2: share memory without copying the answer").
+ * This library covers selection and attention over memory the caller has
+ * already built:
+ *
+ *   csa2_index_scores  lightning-indexer scores with causal visibility
+ *   csa2_block_pool    hierarchical block-max candidate pool
+ *   csa2_topk          Top-K record addresses (lower record id wins ties)
+ *   csa2_sparse_attn   shared-latent MQA over selected records + SWA window,
+ *                      per-head sink, inverse RoPE on the output
+ *   csa2_layer         one layer in Full, Reindex or Reuse mode
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to a dense row-major array with
+ *   the shape given in brackets; pointers must be 16-byte aligned.
+ * - Storage dtypes (csa2_dtype): CSA2_F32 = IEEE float32, CSA2_BF16 =
+ *   bfloat16 (uint16 bit patterns), CSA2_E4M3 = OCP fp8 e4m3fn codes with
+ *   one float32 scale per row (value = decode(code) * scale[row]).
+ * - Positions are 0-based absolute token positions (int64).  Record s of
+ *   a cache compressed at ratio m covers tokens m*s .. m*s+m-1 and is
+ *   visible to a query at t only if m*s+m-1 <= t and s < n_rec ("DeepSeek V4
+ *   Inside: One Token Through Every Block", section "How does CSA compress 8
+ *   tokens into 4 KV entries?": an entry is visible only if all its tokens
+ *   are at or before the query).
+ * - The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises, keeps no pointer after returning and has no global
+ *   state; calls on different streams are independent.  `stream` is a
+ *   hipStream_t passed as void* (NULL = the default stream).  Work is only
+ *   enqueued: results are ready after the caller synchronises the stream.
+ * - `ws`/`ws_bytes` is a caller-provided device workspace of at least the
+ *   size the matching *_workspace_bytes function returns (it may be NULL
+ *   when that size is 0).  Its contents on entry do not matter.
+ * - Errors: every argument is validated on the host before anything is
+ *   enqueued; on an error nothing is launched and the return value is
+ *   negative.  csa2_status_str() gives a message (thread-local detail of
+ *   the last error when one was recorded on this thread).
+ * - Device code never dereferences an index outside [0, N): such entries
+ *   (including the -1 padding) are skipped.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_OK 0
+#define CSA2_EINVAL (-1)       /* null required pointer, bad size, bad combination */
+#define CSA2_EUNSUPPORTED (-2) /* valid request with no kernel instance */
+#define CSA2_EWORKSPACE (-3)   /* workspace missing or too small */
+#define CSA2_EHIP (-4)         /* a HIP launch failed */
+
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_E4M3 = 2 } csa2_dtype;
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+
+/* Largest K accepted by csa2_topk and csa2_layer. */
+#define CSA2_MAX_K 2048
+
+/* ------------------------------------------------------------------------
+ * csa2_index_scores -- lightning-indexer scores.
+ *
+ *   I[b,t,s] = sum_h w[b,t,h] * max(0, q_idx[b,t,h,:] . k[b,s,:])
+ *
+ * Rectified query-key products combined over weighted indexer heads
+ * ("DeepSeek V4.1-Flash. Every layer, connected.", caption "The global and
+ * index paths"; "DeepSeek V4 Inside", Fig. 10).  Invisible records score
+ * -INFINITY (the selection is causal).  Arithmetic: products of the stored
+ * values accumulated in float32; e4m3 keys are applied as code*scale.
+ *
+ * Inputs
+ *   B, Tq      sequences and query tokens per sequence (>= 1)
+ *   N          records per sequence in k_idx (>= 1)
+ *   Hi, Di     indexer heads and head dim (1..64, 1..256)
+ *   m          compression ratio (>= 1): tokens per record
+ *   q_idx      [B][Tq][Hi][Di]  q_dtype in {F32, BF16}
+ *   w          [B][Tq][Hi] float32 head weights
+ *   k_idx      [B][N][Di]       k_dtype in {F32, BF16, E4M3}
+ *   k_scale    [B][N] float32, required for E4M3 and NULL otherwise
+ *   q_pos      [B][Tq] int64 absolute query positions
+ *   n_rec      [B] int32 valid record counts (<= N), or NULL for N
+ *   pool, P, blk
+ *              NULL/0/0 scores every record column s in [0, N).
+ *              Otherwise [B][Tq][P] int32 block ids (-1 = empty slot) and
+ *              the output has P*blk columns: column c is record
+ *              pool[b,t,c/blk]*blk + c%blk ("DeepSeek-V4.1-Flash explained",
+ *              section 3: later indexers search only the candidate pool).
+ * Output
+ *   scores     [B][Tq][ncols] float32, ncols = N or P*blk
+ * Workspace: none (ws may be NULL).
+ * ------------------------------------------------------------------------ */
+int csa2_index_scores(int B, int Tq, int N, int Hi, int Di, int m,
+                      const void* q_idx, int q_dtype, const float* w,
+                      const void* k_idx, const float* k_scale, int k_dtype,
+                      const int64_t* q_pos, const int32_t* n_rec,
+                      const int32_t* pool, int P, int blk,
+                      float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_block_pool -- hierarchical candidate pool.
+ *
+ * Records are grouped into blocks of `blk` consecutive ids; a block scores
+ * the maximum of its members' scores; the P best blocks are kept ("DeepSeek
+ * V4.1-Flash. Every layer, connected.", hierarchy caption; "Create DeepSeek
+ * from scratch", lesson 07 "Hierarchical indexing").  Blocks whose members
+ * are all -INFINITY (not visible) are never kept.
+ *
+ * Inputs
+ *   rows       number of score rows (B*Tq)
+ *   N          columns per row; blocks cover [b*blk, min((b+1)*blk, N))
+ *   blk, P     block size (>= 1) and blocks kept (1..CSA2_MAX_K)
+ *   scores     [rows][N] float32 (as written by csa2_index_scores)
+ * Output
+ *   pool       [rows][P] int32 block ids ordered by (block score desc,
+ *              block id asc); -1 pads when fewer blocks qualify.
+ * Workspace: csa2_block_pool_workspace_bytes(rows, N, blk).
+ * ------------------------------------------------------------------------ */
+int csa2_block_pool(int rows, int N, int blk, int P, const float* scores,
+                    int32_t* pool, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_block_pool_workspace_bytes(int rows, int N, int blk);
+
+/* ------------------------------------------------------------------------
+ * csa2_topk -- Top-K record addresses.
+ *
+ * Returns the ADDRESSES of the K best records, never their scores ("Create
+ * DeepSeek from scratch", lesson 06 worked example: keep the positions,
+ * then retrieve the rows).  Order of preference: score descending, then
+ * record id ascending.  -INFINITY and NaN scores are never selected.
+ *
+ * Inputs
+ *   rows, ncols, K  (K in 1..CSA2_MAX_K)
+ *   scores     [rows][ncols] float32
+ *   pool, P, blk
+ *              NULL/0/0: column c is record c.  Otherwise [rows][P] int32
+ *              block ids and ncols == P*blk: column c is record
+ *              pool[row][c/blk]*blk + c%blk (ties then compare these ids).
+ * Output
+ *   idx        [rows][K] int32: the min(K, #selectable) chosen record ids
+ *              in ascending COLUMN order (a set; deterministic), then -1.
+ * Workspace: csa2_topk_workspace_bytes(rows, ncols, K).
+ * ------------------------------------------------------------------------ */
+int csa2_topk(int rows, int ncols, int K, const float* scores,
+              const int32_t* pool, int P, int blk, int32_t* idx,
+              void* ws, size_t ws_bytes, void* stream);
+size_t csa2_topk_workspace_bytes(int rows, int ncols, int K);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn -- shared-latent attention over selected records plus
+ * the local sliding window, with a per-head sink and inverse output RoPE.
+ *
+ * For query (b,t) at position p = q_pos[b,t] and head h, the entries are
+ * the selected global records kv[b, idx[b,t,k]] (k < K, idx in [0,N)) and
+ * the window rows swa[b, (p-W+1 .. p) mod S] (positions >= 0 only); every
+ * entry serves as both key and value ("DeepSeek V4 Inside", Fig. 11: the
+ * compressed entry is both K and V; window and record share one softmax):
+ *
+ *   z_j   = sm_scale * q[b,t,h,:] . x_j
+ *   ctx_h = sum_j exp(z_j) x_j / (sum_j exp(z_j) + exp(sink[h]))
+ *
+ * (the sink enters the denominator only, "DeepSeek V4 Inside", eq. (27)),
+ * then the last `rope_dims` channels of ctx_h are rotated by position -p
+ * in adjacent pairs (D-r+2j, D-r+2j+1) with angle p*rope_base^(-2j/r)
+ * ("DeepSeek V4.1-Flash. Every layer, connected.", caption "The query and
+ * output paths"; "DeepSeek V4 Inside", Fig. 12).  Queries and caches are
+ * post-RoPE.
+ *
+ * Inputs
+ *   B, Tq, H, D, N, K  sizes (K in 0..CSA2_MAX_K; K = 0 means window only)
+ *   q          [B][Tq][H][D]  q_dtype in {F32, BF16}
+ *   kv         [B][N][D]      kv_dtype in {F32, BF16, E4M3}; kv_scale [B][N]
+ *                             for E4M3, NULL otherwise
+ *   idx        [B][Tq][K] int32 record ids (-1 or out of range = empty)
+ *   swa        [B][S][D]      ring of local rows: position p lives in slot
+ *                             p mod S; swa_dtype like kv; swa_scale [B][S]
+ *   S, W       ring slots and window length (1 <= W <= S)
+ *   q_pos      [B][Tq] int64
+ *   sink       [H] float32 sink logits (not multiplied by sm_scale)
+ *   sm_scale   logit scale; 0 means 1/sqrt(D)
+ *   rope_dims  even, 0..D; rope_base > 0
+ * Output
+ *   out        [B][Tq][H][D] float32
+ * Workspace: csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W).
+ * ------------------------------------------------------------------------ */
+int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K,
+                     const void* q, int q_dtype,
+                     const void* kv, const float* kv_scale, int kv_dtype,
+                     const int32_t* idx,
+                     const void* swa, const float* swa_scale, int swa_dtype,
+                     int S, int W, const int64_t* q_pos, const float* sink,
+                     float sm_scale, int rope_dims, float rope_base,
+                     float* out, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int W);
+
+/* ------------------------------------------------------------------------
+ * csa2_layer -- one CSA2 layer in one of the three sharing modes
+ * ("DeepSeek-V4.1-Flash explained", section 2, mode table; "Create DeepSeek
+ * from scratch", lesson "How CSA2 compresses, shares, and selects attention
+ * memory"):
+ *
+ *   FULL     scores every visible record, optionally builds the block pool
+ *            (pool_inout != NULL), takes a fresh Top-K over all visible
+ *            records, attends.  Writes idx_inout (and pool_inout).
+ *   REINDEX  scores the records of the pool in pool_inout when it is not
+ *            NULL (else every visible record) with this layer's own indexer
+ *            queries over the shared keys, takes a fresh Top-K, attends.
+ *            Writes idx_inout.
+ *   REUSE    runs no indexer; attends over the index set in idx_inout (left
+ *            by the preceding Full or Reindex layer) with this layer's own
+ *            query, window rows and sink.
+ *
+ * Every mode computes a fresh output with the layer's own query.
+ * ------------------------------------------------------------------------ */
+typedef struct csa2_layer_desc {
+    int mode;            /* csa2_mode */
+    int B, Tq;           /* sequences, query tokens per sequence */
+    /* shared store (built by the sharing group's Full layer) */
+    int N, m;            /* records per sequence, tokens per record */
+    const int32_t* n_rec;           /* [B] or NULL (= N) */
+    const void* k_idx;              /* [B][N][Di] indexer keys */
+    const float* k_scale;           /* [B][N] for E4M3, else NULL */
+    int k_dtype;
+    const void* kv;                 /* [B][N][D] shared latent (K = V) */
+    const float* kv_scale;          /* [B][N] for E4M3, else NULL */
+    int kv_dtype;
+    /* this layer's indexer */
+    int Hi, Di;
+    const void* q_idx;              /* [B][Tq][Hi][Di] */
+    int q_idx_dtype;
+    const float* w;                 /* [B][Tq][Hi] */
+    /* this layer's attention */
+    int H, D;
+    const void* q;                  /* [B][Tq][H][D] post-RoPE */
+    int q_dtype;
+    const void* swa;                /* [B][S][D] local ring */
+    const float* swa_scale;         /* [B][S] for E4M3, else NULL */
+    int swa_dtype;
+    int S, W;
+    const float* sink;              /* [H] */
+    float sm_scale;                 /* 0 = 1/sqrt(D) */
+    int rope_dims;
+    float rope_base;
+    const int64_t* q_pos;           /* [B][Tq] */
+    /* selection */
+    int K;
+    int32_t* idx_inout;             /* [B][Tq][K] */
+    int blk, P;
+    int32_t* pool_inout;            /* [B][Tq][P] or NULL */
+    /* output and scratch */
+    float* out;                     /* [B][Tq][H][D] */
+    void* ws;
+    size_t ws_bytes;
+} csa2_layer_desc;
+
+int csa2_layer(const csa2_layer_desc* desc, void* stream);
+
+/* Workspace csa2_layer needs for this descriptor (pointers are ignored). */
+size_t csa2_workspace_bytes(const csa2_layer_desc* desc);
+
+/* Static text for a status code; for the last error on the calling thread
+ * it includes the detail recorded then. */
+const char* csa2_status_str(int status);
+
+/* Library version string. */
+const char* csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

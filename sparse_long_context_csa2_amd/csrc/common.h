@@ -1,0 +1,119 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Storage dtype codes (same values as the C ABI's csa2_dtype).
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------- e4m3
+// OCP e4m3fn -> bf16 is exact (3 mantissa bits, exponents 2^-9 .. 2^8 all
+// fit bf16).  gfx950 converts two codes per instruction; the scale operand
+// is 1.0 so nothing is rounded.
+
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes, bool hi_word) {
+    bf16x2 r = hi_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 (four dwords).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
+    u32x4 r;
+    r[0] = e4m3x2_to_bf16x2(c[0], false);
+    r[1] = e4m3x2_to_bf16x2(c[0], true);
+    r[2] = e4m3x2_to_bf16x2(c[1], false);
+    r[3] = e4m3x2_to_bf16x2(c[1], true);
+    return r;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t code) {
+    uint32_t two = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                    static_cast<uint32_t>(code), 1.0f, false));
+    return __uint_as_float((two & 0xFFFFu) << 16);
+}
+
+// Element of a row in any storage dtype, as float (row-wise scale applied
+// by the caller).
+__device__ __forceinline__ float load_elem(const void* base, size_t i, int dt) {
+    if (dt == DT_F32) return static_cast<const float*>(base)[i];
+    if (dt == DT_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+    return e4m3_to_f32(static_cast<const uint8_t*>(base)[i]);
+}
+
+__device__ __forceinline__ int dt_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }
+
+// ---------------------------------------------------------------- ordering
+// Order-preserving float -> uint32 (larger float, larger key).  -inf and NaN
+// become 0, which marks "never selectable".
+
+__device__ __forceinline__ uint32_t score_key(float f) {
+    if (!(f > -__builtin_huge_valf())) return 0u;  // -inf or NaN
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32 bf16 -> f32 (gfx950).  Operand layout, lane l = 0..63:
+//   A[i][k]: i = l % 16, k in group l / 16 (8 values)
+//   B[k][j]: j = l % 16, k in group l / 16 (8 values)
+//   C[i][j]: j = l % 16, i = 4 * (l / 16) + v, v = 0..3
+// Any assignment of the 32 k values to (group, element) works as long as A
+// and B use the same one; the kernels pick it to make loads contiguous.
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- shuffles
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += shfl_xor_f(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int warp_sum_i(int v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+}  // namespace csa2

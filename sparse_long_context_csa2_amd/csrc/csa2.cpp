@@ -1,0 +1,317 @@
+// C ABI of the CSA2 layer: argument validation, workspace carving, kernel
+// dispatch and the Full / Reindex / Reuse composition.  Host code only: it
+// validates everything before enqueuing anything and never allocates,
+// frees or synchronises.
+#include "../../include/csa2.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_detail;
+thread_local int g_detail_code = 0;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    g_detail_code = code;
+    return code;
+}
+
+int hip_fail(int err, const char* what) {
+    return fail(CSA2_EHIP, "%s: HIP error %d", what, err);
+}
+
+bool dtype_ok(int dt) { return dt == CSA2_F32 || dt == CSA2_BF16 || dt == CSA2_E4M3; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int check_scale(const char* name, int dt, const void* scale) {
+    if (!dtype_ok(dt)) return fail(CSA2_EINVAL, "%s: unknown dtype %d", name, dt);
+    if (dt == CSA2_E4M3 && !scale) return fail(CSA2_EINVAL, "%s: e4m3 storage needs a per-row scale", name);
+    if (dt != CSA2_E4M3 && scale) return fail(CSA2_EINVAL, "%s: scale given for a non-quantized tensor", name);
+    return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- indexer
+
+int validate_index(const csa2::IndexArgs& a) {
+    if (a.B < 1 || a.Tq < 1 || a.N < 1 || a.Hi < 1 || a.Di < 1 || a.m < 1)
+        return fail(CSA2_EINVAL, "index_scores: sizes must be >= 1 (B=%d Tq=%d N=%d Hi=%d Di=%d m=%d)", a.B,
+                    a.Tq, a.N, a.Hi, a.Di, a.m);
+    if (!a.q_idx || !a.w || !a.k_idx || !a.q_pos || !a.scores)
+        return fail(CSA2_EINVAL, "index_scores: null required pointer");
+    if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
+        return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
+                    "index_scores: queries must be f32 or bf16");
+    int e = check_scale("index_scores keys", a.k_dtype, a.k_scale);
+    if (e) return e;
+    if (a.pool) {
+        if (a.P < 1 || a.blk < 1) return fail(CSA2_EINVAL, "index_scores: pool needs P >= 1 and blk >= 1");
+        if (static_cast<long long>(a.P) * a.blk > (1LL << 30))
+            return fail(CSA2_EINVAL, "index_scores: P*blk too large");
+    } else if (a.P || a.blk) {
+        return fail(CSA2_EINVAL, "index_scores: P/blk given without a pool");
+    }
+    if (!csa2::index_scores_mfma_ok(a)) {
+        if (a.Hi > 64 || a.Di > 256 || a.Hi * a.Di > 8192)
+            return fail(CSA2_EUNSUPPORTED, "index_scores: no kernel for Hi=%d Di=%d with these dtypes", a.Hi,
+                        a.Di);
+    }
+    return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- attention
+
+int validate_attn(const csa2::AttnArgs& a) {
+    if (a.B < 1 || a.Tq < 1 || a.H < 1 || a.D < 1 || a.N < 1 || a.K < 0 || a.S < 1 || a.W < 1)
+        return fail(CSA2_EINVAL, "sparse_attn: bad sizes (B=%d Tq=%d H=%d D=%d N=%d K=%d S=%d W=%d)", a.B, a.Tq,
+                    a.H, a.D, a.N, a.K, a.S, a.W);
+    if (a.W > a.S) return fail(CSA2_EINVAL, "sparse_attn: window W=%d larger than ring S=%d", a.W, a.S);
+    if (a.K > CSA2_MAX_K) return fail(CSA2_EINVAL, "sparse_attn: K=%d above %d", a.K, CSA2_MAX_K);
+    if (!a.q || !a.kv || !a.swa || !a.q_pos || !a.sink || !a.out || (a.K > 0 && !a.idx))
+        return fail(CSA2_EINVAL, "sparse_attn: null required pointer");
+    if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
+        return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
+                    "sparse_attn: queries must be f32 or bf16");
+    int e = check_scale("sparse_attn kv", a.kv_dtype, a.kv_scale);
+    if (e) return e;
+    e = check_scale("sparse_attn swa", a.swa_dtype, a.swa_scale);
+    if (e) return e;
+    if (a.rope_dims < 0 || a.rope_dims > a.D || (a.rope_dims & 1))
+        return fail(CSA2_EINVAL, "sparse_attn: rope_dims=%d must be even and <= D", a.rope_dims);
+    if (!(a.rope_base > 0.f)) return fail(CSA2_EINVAL, "sparse_attn: rope_base must be > 0");
+    if (!(a.sm_scale >= 0.f) || isinf(a.sm_scale)) return fail(CSA2_EINVAL, "sparse_attn: bad sm_scale");
+    if (!csa2::sparse_attn_mfma_ok(a)) {
+        if (a.D > 1024 || 2LL * a.D + a.K + a.W > 16384)
+            return fail(CSA2_EUNSUPPORTED, "sparse_attn: no kernel for H=%d D=%d K=%d W=%d with these dtypes",
+                        a.H, a.D, a.K, a.W);
+    }
+    return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_index_scores(int B, int Tq, int N, int Hi, int Di, int m, const void* q_idx, int q_dtype,
+                      const float* w, const void* k_idx, const float* k_scale, int k_dtype,
+                      const int64_t* q_pos, const int32_t* n_rec, const int32_t* pool, int P, int blk,
+                      float* scores, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    csa2::IndexArgs a;
+    a.B = B; a.Tq = Tq; a.N = N; a.Hi = Hi; a.Di = Di; a.m = m;
+    a.q_idx = q_idx; a.q_dtype = q_dtype; a.w = w; a.k_idx = k_idx; a.k_scale = k_scale;
+    a.k_dtype = k_dtype; a.q_pos = q_pos; a.n_rec = n_rec; a.pool = pool; a.P = P; a.blk = blk;
+    a.scores = scores;
+    a.ncols = pool ? P * blk : N;
+    int e = validate_index(a);
+    if (e) return e;
+    e = csa2::launch_index_scores(a, stream);
+    return e ? hip_fail(e, "index_scores launch") : CSA2_OK;
+}
+
+size_t csa2_block_pool_workspace_bytes(int rows, int N, int blk) {
+    if (rows < 1 || N < 1 || blk < 1) return 0;
+    return csa2::block_pool_ws_bytes(rows, N, blk);
+}
+
+int csa2_block_pool(int rows, int N, int blk, int P, const float* scores, int32_t* pool, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (rows < 1 || N < 1 || blk < 1 || P < 1)
+        return fail(CSA2_EINVAL, "block_pool: sizes must be >= 1 (rows=%d N=%d blk=%d P=%d)", rows, N, blk, P);
+    if (P > CSA2_MAX_K) return fail(CSA2_EINVAL, "block_pool: P=%d above %d", P, CSA2_MAX_K);
+    if (!scores || !pool) return fail(CSA2_EINVAL, "block_pool: null required pointer");
+    const size_t need = csa2::block_pool_ws_bytes(rows, N, blk);
+    if (ws_bytes < need || (need && !ws))
+        return fail(CSA2_EWORKSPACE, "block_pool: workspace %zu bytes, need %zu", ws_bytes, need);
+    const int e = csa2::launch_block_pool(rows, N, blk, P, scores, pool, ws, ws_bytes, stream);
+    return e ? hip_fail(e, "block_pool launch") : CSA2_OK;
+}
+
+size_t csa2_topk_workspace_bytes(int rows, int ncols, int K) {
+    if (rows < 1 || ncols < 1 || K < 1) return 0;
+    return csa2::topk_ws_bytes(rows, ncols, K);
+}
+
+int csa2_topk(int rows, int ncols, int K, const float* scores, const int32_t* pool, int P, int blk, int32_t* idx,
+              void* ws, size_t ws_bytes, void* stream) {
+    if (rows < 1 || ncols < 1 || K < 1)
+        return fail(CSA2_EINVAL, "topk: sizes must be >= 1 (rows=%d ncols=%d K=%d)", rows, ncols, K);
+    if (K > CSA2_MAX_K) return fail(CSA2_EINVAL, "topk: K=%d above %d", K, CSA2_MAX_K);
+    if (!scores || !idx) return fail(CSA2_EINVAL, "topk: null required pointer");
+    if (pool) {
+        if (P < 1 || blk < 1 || static_cast<long long>(P) * blk != ncols)
+            return fail(CSA2_EINVAL, "topk: pool mapping needs P*blk == ncols (P=%d blk=%d ncols=%d)", P, blk,
+                        ncols);
+    } else if (P || blk) {
+        return fail(CSA2_EINVAL, "topk: P/blk given without a pool");
+    }
+    const size_t need = csa2::topk_ws_bytes(rows, ncols, K);
+    if (ws_bytes < need || (need && !ws))
+        return fail(CSA2_EWORKSPACE, "topk: workspace %zu bytes, need %zu", ws_bytes, need);
+    csa2::TopkArgs a;
+    a.rows = rows; a.ncols = ncols; a.K = K; a.scores = scores; a.pool = pool; a.P = P; a.blk = blk;
+    a.idx = idx; a.sort_by_key = false; a.ws = ws; a.ws_bytes = ws_bytes;
+    const int e = csa2::launch_topk(a, stream);
+    return e ? hip_fail(e, "topk launch") : CSA2_OK;
+}
+
+size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int W) {
+    if (B < 1 || Tq < 1 || H < 1 || D < 1 || K < 0 || W < 1) return 0;
+    return csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
+}
+
+static void fill_attn(csa2::AttnArgs& a, int B, int Tq, int H, int D, int N, int K, const void* q, int q_dtype,
+                      const void* kv, const float* kv_scale, int kv_dtype, const int32_t* idx, const void* swa,
+                      const float* swa_scale, int swa_dtype, int S, int W, const int64_t* q_pos,
+                      const float* sink, float sm_scale, int rope_dims, float rope_base, float* out, void* ws,
+                      size_t ws_bytes) {
+    a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.N = N; a.K = K;
+    a.q = q; a.q_dtype = q_dtype; a.kv = kv; a.kv_scale = kv_scale; a.kv_dtype = kv_dtype; a.idx = idx;
+    a.swa = swa; a.swa_scale = swa_scale; a.swa_dtype = swa_dtype; a.S = S; a.W = W; a.q_pos = q_pos;
+    a.sink = sink; a.sm_scale = sm_scale; a.rope_dims = rope_dims; a.rope_base = rope_base; a.out = out;
+    a.ws = ws; a.ws_bytes = ws_bytes;
+}
+
+int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K, const void* q, int q_dtype, const void* kv,
+                     const float* kv_scale, int kv_dtype, const int32_t* idx, const void* swa,
+                     const float* swa_scale, int swa_dtype, int S, int W, const int64_t* q_pos, const float* sink,
+                     float sm_scale, int rope_dims, float rope_base, float* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+    csa2::AttnArgs a;
+    fill_attn(a, B, Tq, H, D, N, K, q, q_dtype, kv, kv_scale, kv_dtype, idx, swa, swa_scale, swa_dtype, S, W,
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, ws, ws_bytes);
+    int e = validate_attn(a);
+    if (e) return e;
+    const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
+    if (ws_bytes < need || (need && !ws))
+        return fail(CSA2_EWORKSPACE, "sparse_attn: workspace %zu bytes, need %zu", ws_bytes, need);
+    e = csa2::launch_sparse_attn(a, stream);
+    return e ? hip_fail(e, "sparse_attn launch") : CSA2_OK;
+}
+
+// ---------------------------------------------------------------- layer
+
+struct LayerPlan {
+    int rows, ncols;
+    size_t off_scores, off_pool, off_attn, total;
+};
+
+static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
+    if (!d) return fail(CSA2_EINVAL, "layer: null descriptor");
+    if (d->mode != CSA2_FULL && d->mode != CSA2_REINDEX && d->mode != CSA2_REUSE)
+        return fail(CSA2_EINVAL, "layer: unknown mode %d", d->mode);
+    if (d->B < 1 || d->Tq < 1 || d->N < 1 || d->m < 1)
+        return fail(CSA2_EINVAL, "layer: sizes must be >= 1 (B=%d Tq=%d N=%d m=%d)", d->B, d->Tq, d->N, d->m);
+    if (d->K < 1 || d->K > CSA2_MAX_K) return fail(CSA2_EINVAL, "layer: K=%d outside 1..%d", d->K, CSA2_MAX_K);
+    if (!d->idx_inout) return fail(CSA2_EINVAL, "layer: idx_inout is required");
+    pl.rows = d->B * d->Tq;
+    pl.ncols = d->N;
+    const bool scores_needed = d->mode != CSA2_REUSE;
+    if (d->mode == CSA2_FULL && d->pool_inout) {
+        if (d->blk < 1 || d->P < 1 || d->P > CSA2_MAX_K)
+            return fail(CSA2_EINVAL, "layer: pool needs blk >= 1 and 1 <= P <= %d", CSA2_MAX_K);
+    }
+    if (d->mode == CSA2_REINDEX && d->pool_inout) {
+        if (d->blk < 1 || d->P < 1 || static_cast<long long>(d->P) * d->blk > (1LL << 30))
+            return fail(CSA2_EINVAL, "layer: pool needs blk >= 1 and P >= 1");
+        pl.ncols = d->P * d->blk;
+    }
+    size_t off = 0;
+    pl.off_scores = off;
+    if (scores_needed) off += align256(static_cast<size_t>(pl.rows) * pl.ncols * sizeof(float));
+    pl.off_pool = off;
+    if (d->mode == CSA2_FULL && d->pool_inout) off += align256(csa2::block_pool_ws_bytes(pl.rows, d->N, d->blk));
+    pl.off_attn = off;
+    off += align256(csa2::sparse_attn_ws_bytes(d->B, d->Tq, d->H, d->D, d->K, d->W));
+    pl.total = off;
+    return CSA2_OK;
+}
+
+size_t csa2_workspace_bytes(const csa2_layer_desc* desc) {
+    LayerPlan pl;
+    if (plan_layer(desc, pl)) return 0;
+    return pl.total;
+}
+
+int csa2_layer(const csa2_layer_desc* d, void* stream) {
+    LayerPlan pl;
+    int e = plan_layer(d, pl);
+    if (e) return e;
+    csa2::IndexArgs ia;
+    const bool scoring = d->mode != CSA2_REUSE;
+    const bool pooled = d->mode == CSA2_REINDEX && d->pool_inout;
+    float* scores = reinterpret_cast<float*>(static_cast<uint8_t*>(d->ws) + pl.off_scores);
+    if (scoring) {
+        ia.B = d->B; ia.Tq = d->Tq; ia.N = d->N; ia.Hi = d->Hi; ia.Di = d->Di; ia.m = d->m;
+        ia.q_idx = d->q_idx; ia.q_dtype = d->q_idx_dtype; ia.w = d->w; ia.k_idx = d->k_idx;
+        ia.k_scale = d->k_scale; ia.k_dtype = d->k_dtype; ia.q_pos = d->q_pos; ia.n_rec = d->n_rec;
+        ia.pool = pooled ? d->pool_inout : nullptr;
+        ia.P = pooled ? d->P : 0;
+        ia.blk = pooled ? d->blk : 0;
+        ia.scores = scores;
+        ia.ncols = pl.ncols;
+        e = validate_index(ia);
+        if (e) return e;
+    }
+    csa2::AttnArgs aa;
+    fill_attn(aa, d->B, d->Tq, d->H, d->D, d->N, d->K, d->q, d->q_dtype, d->kv, d->kv_scale, d->kv_dtype,
+              d->idx_inout, d->swa, d->swa_scale, d->swa_dtype, d->S, d->W, d->q_pos, d->sink, d->sm_scale,
+              d->rope_dims, d->rope_base, d->out, static_cast<uint8_t*>(d->ws) + pl.off_attn,
+              d->ws_bytes > pl.off_attn ? d->ws_bytes - pl.off_attn : 0);
+    e = validate_attn(aa);
+    if (e) return e;
+    if (pl.total && (!d->ws || d->ws_bytes < pl.total))
+        return fail(CSA2_EWORKSPACE, "layer: workspace %zu bytes, need %zu", d->ws_bytes, pl.total);
+
+    if (scoring) {
+        e = csa2::launch_index_scores(ia, stream);
+        if (e) return hip_fail(e, "layer: index_scores launch");
+        if (d->mode == CSA2_FULL && d->pool_inout) {
+            e = csa2::launch_block_pool(pl.rows, d->N, d->blk, d->P, scores, d->pool_inout,
+                                        static_cast<uint8_t*>(d->ws) + pl.off_pool,
+                                        csa2::block_pool_ws_bytes(pl.rows, d->N, d->blk), stream);
+            if (e) return hip_fail(e, "layer: block_pool launch");
+        }
+        csa2::TopkArgs ta;
+        ta.rows = pl.rows; ta.ncols = pl.ncols; ta.K = d->K; ta.scores = scores;
+        ta.pool = pooled ? d->pool_inout : nullptr;
+        ta.P = pooled ? d->P : 0;
+        ta.blk = pooled ? d->blk : 0;
+        ta.idx = d->idx_inout; ta.sort_by_key = false; ta.ws = nullptr; ta.ws_bytes = 0;
+        e = csa2::launch_topk(ta, stream);
+        if (e) return hip_fail(e, "layer: topk launch");
+    }
+    e = csa2::launch_sparse_attn(aa, stream);
+    return e ? hip_fail(e, "layer: sparse_attn launch") : CSA2_OK;
+}
+
+const char* csa2_status_str(int status) {
+    if (status != CSA2_OK && status == g_detail_code && !g_detail.empty()) return g_detail.c_str();
+    switch (status) {
+        case CSA2_OK: return "ok";
+        case CSA2_EINVAL: return "invalid argument";
+        case CSA2_EUNSUPPORTED: return "unsupported shape or dtype combination";
+        case CSA2_EWORKSPACE: return "workspace missing or too small";
+        case CSA2_EHIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+const char* csa2_version(void) { return "csa2-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,301 @@
+// Lightning-indexer scoring kernels.
+//
+//   I[b,t,s] = sum_h w[b,t,h] * max(0, q_idx[b,t,h,:] . k[b,s,:])
+//
+// with -inf for records the query may not see ("DeepSeek V4.1-Flash. Every
+// layer, connected.", caption "The global and index paths"; "DeepSeek V4
+// Inside: One Token Through Every Block", Fig. 10).
+//
+// Two kernels:
+//  * idx_mfma_kernel -- 32 heads x 128 dims, bf16 queries, bf16 or e4m3
+//    keys.  The heads are the M side of 16x16x32 bf16 MFMAs (two m-tiles),
+//    16 records are the N side, the 128 dims are four k-steps.  Each lane
+//    loads its record's key bytes straight into registers: for one load
+//    instruction the four lanes that share a record read 64 contiguous
+//    bytes, so a wave touches 16 whole 64-byte segments per instruction.
+//    The ReLU, head weights and the sum over heads run in the epilogue:
+//    a lane holds 8 heads of one record, two xor-shuffles finish the sum.
+//    Decode rows (one query token) give each wave its own record tiles;
+//    prefill gives each wave four tokens and all waves the same tiles, so
+//    a key tile fetched once feeds 4 x 4 tokens from L1/L2.
+//  * idx_generic_kernel -- any head count/dim and dtype, one thread per
+//    (row, column), fp32 FMA; used for small shapes such as the toy.
+#include "common.h"
+#include "launch.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kHi = 32;
+constexpr int kDi = 128;
+
+struct IdxP {
+    int B, Tq, N, m, ncols, P, blk;
+    const uint16_t* q;   // bf16 [B][Tq][32][128]
+    const float* w;      // [B][Tq][32]
+    const uint8_t* k;    // key rows, bf16 or e4m3
+    const float* ks;     // e4m3 row scales [B][N]
+    const int64_t* q_pos;
+    const int32_t* n_rec;
+    const int32_t* pool;
+    float* out;
+    int tiles_per_block;
+};
+
+__device__ __forceinline__ int visible_count(int64_t t, int m, int nrec) {
+    // records s with m*s + m - 1 <= t  <=>  s < floor((t + 1) / m)
+    if (t < 0) return 0;
+    int64_t v = (t + 1) / m;
+    return v < nrec ? static_cast<int>(v) : nrec;
+}
+
+// Element offset (in units of 8 values) of k-step `ks` for lane group `g`.
+template <int KDT>
+__device__ __forceinline__ int chunk8(int g, int ks) {
+    if (KDT == DT_BF16) return g + 4 * ks;                 // one 16-byte load per k-step
+    return 2 * (g + 4 * (ks >> 1)) + (ks & 1);             // one 16-byte load per two k-steps
+}
+
+// Loads the lane's share of one key row as four bf16x8 k-step operands.
+// Streaming (decode) reads are marked non-temporal: each key row is used
+// once per call.  Prefill reads keep normal caching: every key tile is
+// reused by all query-token groups.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <int KDT, bool NT>
+__device__ __forceinline__ void load_key(const uint8_t* row, int g, bool valid, bf16x8 (&bk)[4]) {
+    if (KDT == DT_BF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 v = valid ? ld16<NT>(p + g + 4 * ks) : u32x4{0, 0, 0, 0};
+            bk[ks] = as_bf16x8(v);
+        }
+    } else {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            u32x4 v = valid ? ld16<NT>(p + g + 4 * i) : u32x4{0, 0, 0, 0};
+            bk[2 * i] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{v[0], v[1]}));
+            bk[2 * i + 1] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{v[2], v[3]}));
+        }
+    }
+}
+
+// TOKW query tokens per wave.  WAVES_ON_TOKENS: the block's four waves take
+// different tokens and the same record tiles (prefill); otherwise they take
+// the same token and different tiles (decode, or any pooled row).
+template <int KDT, int TOKW, bool WAVES_ON_TOKENS>
+__global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+
+    int b, tok0, ntok;
+    if (WAVES_ON_TOKENS) {
+        const int gps = (p.Tq + 4 * TOKW - 1) / (4 * TOKW);
+        b = blockIdx.y / gps;
+        tok0 = (blockIdx.y % gps) * 4 * TOKW + wave * TOKW;
+        ntok = p.Tq - tok0;
+        ntok = ntok < 0 ? 0 : (ntok > TOKW ? TOKW : ntok);
+    } else {
+        b = blockIdx.y / p.Tq;
+        tok0 = blockIdx.y % p.Tq;
+        ntok = 1;
+    }
+    if (ntok == 0) return;
+    const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+
+    // A operands (queries), head weights and visibility of the wave's tokens.
+    bf16x8 qa[TOKW][2][4];
+    float wv[TOKW][2][4];
+    int vis[TOKW];
+    int vis_max = 0;
+#pragma unroll
+    for (int tk = 0; tk < TOKW; ++tk) {
+        const bool on = tk < ntok;
+        const size_t row = static_cast<size_t>(b) * p.Tq + tok0 + (on ? tk : 0);
+        vis[tk] = on ? visible_count(p.q_pos[row], p.m, nrec) : 0;
+        vis_max = max(vis_max, vis[tk]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4 v = on ? *reinterpret_cast<const u32x4*>(qh + 8 * chunk8<KDT>(g, ks))
+                             : u32x4{0, 0, 0, 0};
+                qa[tk][mt][ks] = as_bf16x8(v);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) wv[tk][mt][v] = on ? p.w[row * kHi + 16 * mt + 4 * g + v] : 0.f;
+        }
+    }
+
+    const int ntiles = (p.ncols + 15) / 16;
+    const int t_begin = blockIdx.x * p.tiles_per_block;
+    const int t_end = min(ntiles, t_begin + p.tiles_per_block);
+    const int t_step = WAVES_ON_TOKENS ? 1 : 4;
+    const int t_first = t_begin + (WAVES_ON_TOKENS ? 0 : wave);
+    const int32_t* prow = p.pool ? p.pool + (static_cast<size_t>(b) * p.Tq + tok0) * p.P : nullptr;
+    const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+
+    for (int ti = t_first; ti < t_end; ti += t_step) {
+        const int c = ti * 16 + n;
+        int rec = -1;
+        if (c < p.ncols) {
+            if (prow) {
+                const int pb = prow[c / p.blk];
+                rec = pb < 0 ? -1 : pb * p.blk + c % p.blk;
+            } else {
+                rec = c;
+            }
+        }
+        const bool ld = rec >= 0 && rec < vis_max;
+        if (!__any(ld)) {
+#pragma unroll
+            for (int tk = 0; tk < TOKW; ++tk) {
+                if (g == 0 && tk < ntok && c < p.ncols)
+                    p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] =
+                        -__builtin_huge_valf();
+            }
+            continue;
+        }
+        bf16x8 bk[4];
+        load_key<KDT, !WAVES_ON_TOKENS>(kbase + static_cast<size_t>(ld ? rec : 0) * kRowBytes, g, ld, bk);
+        float kscale = 1.f;
+        if (KDT == DT_E4M3) kscale = ld ? p.ks[static_cast<size_t>(b) * p.N + rec] : 0.f;
+#pragma unroll
+        for (int tk = 0; tk < TOKW; ++tk) {
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc0 = mfma16x16x32(qa[tk][0][ks], bk[ks], acc0);
+                acc1 = mfma16x16x32(qa[tk][1][ks], bk[ks], acc1);
+            }
+            float part = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float d0 = acc0[v], d1 = acc1[v];
+                if (KDT == DT_E4M3) { d0 *= kscale; d1 *= kscale; }
+                part += wv[tk][0][v] * fmaxf(d0, 0.f);
+                part += wv[tk][1][v] * fmaxf(d1, 0.f);
+            }
+            part += shfl_xor_f(part, 16);
+            part += shfl_xor_f(part, 32);
+            if (g == 0 && tk < ntok && c < p.ncols) {
+                const bool ok = rec >= 0 && rec < vis[tk];
+                p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] =
+                    ok ? part : -__builtin_huge_valf();
+            }
+        }
+    }
+}
+
+struct IdxG {
+    int B, Tq, N, Hi, Di, m, ncols, P, blk, qdt, kdt;
+    const void* q;
+    const float* w;
+    const void* k;
+    const float* ks;
+    const int64_t* q_pos;
+    const int32_t* n_rec;
+    const int32_t* pool;
+    float* out;
+};
+
+__global__ __launch_bounds__(256) void idx_generic_kernel(IdxG p) {
+    extern __shared__ float sh[];  // q row [Hi*Di] then w [Hi]
+    const size_t row = blockIdx.y;
+    const int b = static_cast<int>(row / p.Tq);
+    const int HD = p.Hi * p.Di;
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) sh[i] = load_elem(p.q, row * HD + i, p.qdt);
+    for (int i = threadIdx.x; i < p.Hi; i += blockDim.x) sh[HD + i] = p.w[row * p.Hi + i];
+    __syncthreads();
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= p.ncols) return;
+    const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+    const int vis = visible_count(p.q_pos[row], p.m, nrec);
+    int rec = c;
+    if (p.pool) {
+        const int pb = p.pool[row * p.P + c / p.blk];
+        rec = pb < 0 ? -1 : pb * p.blk + c % p.blk;
+    }
+    float res = -__builtin_huge_valf();
+    if (rec >= 0 && rec < vis) {
+        const size_t kr = (static_cast<size_t>(b) * p.N + rec) * p.Di;
+        const float sc = p.kdt == DT_E4M3 ? p.ks[static_cast<size_t>(b) * p.N + rec] : 1.f;
+        res = 0.f;
+        for (int h = 0; h < p.Hi; ++h) {
+            float dot = 0.f;
+            for (int i = 0; i < p.Di; ++i) dot = fmaf(sh[h * p.Di + i], load_elem(p.k, kr + i, p.kdt), dot);
+            dot *= sc;
+            res += sh[HD + h] * fmaxf(dot, 0.f);
+        }
+    }
+    p.out[row * p.ncols + c] = res;
+}
+
+template <int KDT, int TOKW, bool WOT>
+int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
+    IdxP p;
+    p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
+    p.q = static_cast<const uint16_t*>(a.q_idx);
+    p.w = a.w;
+    p.k = static_cast<const uint8_t*>(a.k_idx);
+    p.ks = a.k_scale;
+    p.q_pos = a.q_pos;
+    p.n_rec = a.n_rec;
+    p.pool = a.pool;
+    p.out = a.scores;
+    p.tiles_per_block = tiles_per_block;
+    const int ntiles = (a.ncols + 15) / 16;
+    dim3 grid((ntiles + tiles_per_block - 1) / tiles_per_block,
+              WOT ? a.B * ((a.Tq + 4 * TOKW - 1) / (4 * TOKW)) : a.B * a.Tq);
+    hipLaunchKernelGGL((idx_mfma_kernel<KDT, TOKW, WOT>), grid, dim3(256), 0, st, p);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+bool index_scores_mfma_ok(const IndexArgs& a) {
+    return a.Hi == kHi && a.Di == kDi && a.q_dtype == DT_BF16 &&
+           (a.k_dtype == DT_BF16 || a.k_dtype == DT_E4M3);
+}
+
+int launch_index_scores(const IndexArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (index_scores_mfma_ok(a)) {
+        const int ntiles = (a.ncols + 15) / 16;
+        const int rows = a.B * a.Tq;
+        // Prefill-shaped work (many tokens of one sequence, no pool): waves
+        // share record tiles across 16 tokens.
+        if (!a.pool && a.Tq >= 16) {
+            const int tpb = 16;
+            return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16, 4, true>(a, tpb, st)
+                                        : launch_mfma<DT_E4M3, 4, true>(a, tpb, st);
+        }
+        // Decode rows: pick tiles per block so the grid has >= ~2048 blocks
+        // while each wave still streams several tiles.
+        int tpb = 32;
+        while (tpb > 4 && static_cast<long>(rows) * ((ntiles + tpb - 1) / tpb) < 2048) tpb >>= 1;
+        return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16, 1, false>(a, tpb, st)
+                                    : launch_mfma<DT_E4M3, 1, false>(a, tpb, st);
+    }
+    IdxG p;
+    p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.Hi = a.Hi; p.Di = a.Di; p.m = a.m; p.ncols = a.ncols;
+    p.P = a.P; p.blk = a.blk; p.qdt = a.q_dtype; p.kdt = a.k_dtype;
+    p.q = a.q_idx; p.w = a.w; p.k = a.k_idx; p.ks = a.k_scale; p.q_pos = a.q_pos;
+    p.n_rec = a.n_rec; p.pool = a.pool; p.out = a.scores;
+    dim3 grid((a.ncols + 255) / 256, a.B * a.Tq);
+    const size_t lds = (static_cast<size_t>(a.Hi) * a.Di + a.Hi) * sizeof(float);
+    hipLaunchKernelGGL(idx_generic_kernel, grid, dim3(256), lds, st, p);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace csa2

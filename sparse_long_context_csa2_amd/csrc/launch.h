@@ -1,0 +1,72 @@
+// Internal interface between the C ABI host code and the kernel translation
+// units.  Every launcher only enqueues work on `stream` and returns a
+// hipError_t value as int (0 = success).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct IndexArgs {
+    int B, Tq, N, Hi, Di, m;
+    const void* q_idx;
+    int q_dtype;
+    const float* w;
+    const void* k_idx;
+    const float* k_scale;
+    int k_dtype;
+    const int64_t* q_pos;
+    const int32_t* n_rec;
+    const int32_t* pool;  // [B][Tq][P] or null
+    int P, blk;
+    float* scores;        // [B][Tq][ncols]
+    int ncols;
+};
+// True when the MFMA indexer handles these shapes and dtypes.
+bool index_scores_mfma_ok(const IndexArgs& a);
+int launch_index_scores(const IndexArgs& a, void* stream);
+
+struct TopkArgs {
+    int rows, ncols, K;
+    const float* scores;
+    const int32_t* pool;  // [rows][P] or null
+    int P, blk;
+    int32_t* idx;         // [rows][K]
+    bool sort_by_key;     // output ordered by (score desc, id asc) instead of by column
+    void* ws;
+    size_t ws_bytes;
+};
+size_t topk_ws_bytes(int rows, int ncols, int K);
+int launch_topk(const TopkArgs& a, void* stream);
+
+size_t block_pool_ws_bytes(int rows, int N, int blk);
+int launch_block_pool(int rows, int N, int blk, int P, const float* scores, int32_t* pool,
+                      void* ws, size_t ws_bytes, void* stream);
+
+struct AttnArgs {
+    int B, Tq, H, D, N, K;
+    const void* q;
+    int q_dtype;
+    const void* kv;
+    const float* kv_scale;
+    int kv_dtype;
+    const int32_t* idx;
+    const void* swa;
+    const float* swa_scale;
+    int swa_dtype;
+    int S, W;
+    const int64_t* q_pos;
+    const float* sink;
+    float sm_scale;
+    int rope_dims;
+    float rope_base;
+    float* out;
+    void* ws;
+    size_t ws_bytes;
+};
+bool sparse_attn_mfma_ok(const AttnArgs& a);
+size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W);
+int launch_sparse_attn(const AttnArgs& a, void* stream);
+
+}  // namespace csa2

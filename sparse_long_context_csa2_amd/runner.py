@@ -1,0 +1,87 @@
+"""Device-side driver of a CSA2 sharing group through the C ABI.
+
+``DeviceGroup`` uploads a workload's storage arrays (see
+:mod:`.workloads`) to the GPU once, owns the per-layer index, pool, output
+and workspace buffers, and enqueues the layers with ``csa2_layer`` in
+order: a Full layer (optionally building the block pool), Reindex layers
+searching that pool, and Reuse layers reading the last index set.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as _b
+
+
+def to_device(arr, device="cuda") -> Optional[torch.Tensor]:
+    """numpy storage array -> device tensor (uint16 bf16 bits become a
+    bfloat16 view, uint8 e4m3 codes stay uint8)."""
+    if arr is None:
+        return None
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceGroup:
+    def __init__(self, inputs: Dict, device: str = "cuda", copies: int = 1):
+        wl = inputs["wl"]
+        self.wl = wl
+        self.device = device
+        sh = inputs["shared"]
+        self.shared = [dict(m=sh["m"], n_rec=to_device(sh["n_rec"], device),
+                            k_idx=to_device(sh["k_idx"], device), k_scale=to_device(sh["k_scale"], device),
+                            kv=to_device(sh["kv"], device), kv_scale=to_device(sh["kv_scale"], device))]
+        # extra copies of the shared store let a benchmark rotate caches
+        for _ in range(copies - 1):
+            self.shared.append({k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                                for k, v in self.shared[0].items()})
+        self.layers: List[Dict] = []
+        B, Tq = wl.B, wl.Tq
+        for lay in inputs["layers"]:
+            d = {k: lay[k] for k in ("mode", "build_pool", "K", "W", "blk", "P", "rope_dims", "rope_base",
+                                     "sm_scale")}
+            for k in ("q_idx", "w", "q", "swa", "swa_scale", "sink", "q_pos"):
+                d[k] = to_device(lay[k], device)
+            d["out"] = torch.empty((B, Tq, wl.H, wl.D), dtype=torch.float32, device=device)
+            self.layers.append(d)
+        # index sets: Full/Reindex write their own; Reuse reads the last one
+        self.idx: List[torch.Tensor] = []
+        cur = None
+        for d in self.layers:
+            if d["mode"] != "reuse":
+                cur = torch.full((B, Tq, d["K"]), -1, dtype=torch.int32, device=device)
+            self.idx.append(cur)
+        self.pool = None
+        if any(d["build_pool"] for d in self.layers):
+            self.pool = torch.full((B, Tq, wl.P), -1, dtype=torch.int32, device=device)
+        self.descs = []
+        ws_need = 0
+        for copy in range(copies):
+            row = []
+            for li, d in enumerate(self.layers):
+                pool = self.pool if (d["build_pool"] or d["mode"] == "reindex") else None
+                desc = _b.make_layer_desc(d["mode"], self.shared[copy], d, self.idx[li], pool, d["out"])
+                ws_need = max(ws_need, _b.csa2_workspace_bytes(desc))
+                row.append(desc)
+            self.descs.append(row)
+        self.ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=device)
+        for row in self.descs:
+            for desc in row:
+                desc.ws = self.ws.data_ptr()
+                desc.ws_bytes = self.ws.numel()
+
+    def run(self, copy: int = 0, stream=None) -> None:
+        for desc in self.descs[copy]:
+            _b.csa2_layer(desc, stream)
+
+    def outputs(self) -> List[np.ndarray]:
+        return [d["out"].cpu().numpy() for d in self.layers]
+
+    def index_sets(self) -> List[np.ndarray]:
+        return [i.cpu().numpy() for i in self.idx]

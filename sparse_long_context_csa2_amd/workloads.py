@@ -57,7 +57,7 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     man = ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
     code_n = (exp << 3) | man
     # subnormal range: multiples of 2^-9
-    code_s = np.rint(a.astype(np.float64) * 512.0).astype(np.int32)
+    code_s = np.rint(a * np.float32(512.0)).astype(np.int32)  # exact scaling, RNE
     code = np.where(a < np.float32(2.0 ** -6), code_s, code_n)
     code = np.minimum(code, 0x7E)  # 448 is the largest finite code
     return (code | (neg.astype(np.int32) << 7)).astype(np.uint8)

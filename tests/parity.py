@@ -1,0 +1,73 @@
+"""Comparison rules between the HIP library and the fp64 oracle.
+
+* Indexer scores: -inf exactly where the oracle has -inf; elsewhere
+  |gpu - oracle| <= 1e-4 * max(|oracle|, 1e-3 * max_s |oracle[row, s]|)
+  (relative 1e-4; the floor keeps a score that fp32 rounds across zero from
+  failing the relative test).
+* Top-K sets: equal sizes; every id valid, unique and a candidate; ids in
+  the symmetric difference must have oracle scores within 1e-4 (relative)
+  of the oracle's K-th score.
+* Attention: evaluated on the GPU's own admissible index set, max-abs error
+  <= 2e-3 for f32/bf16 caches and 5e-2 for e4m3 caches.
+"""
+
+import math
+
+import numpy as np
+
+import oracle as O
+
+SCORE_RTOL = 1e-4
+SET_BAND = 1e-4
+ATTN_TOL = {"f32": 2e-3, "bf16": 2e-3, "e4m3": 5e-2}
+
+
+def check_scores(gpu_row, ora_row, where=""):
+    g = np.asarray(gpu_row, dtype=np.float64)
+    o = np.asarray(ora_row, dtype=np.float64)
+    gi, oi = np.isneginf(g), np.isneginf(o)
+    assert np.array_equal(gi, oi), f"{where}: -inf pattern differs at {np.nonzero(gi != oi)[0][:10]}"
+    fin = ~oi
+    if not fin.any():
+        return 0.0
+    floor = 1e-3 * np.abs(o[fin]).max()
+    tol = SCORE_RTOL * np.maximum(np.abs(o[fin]), floor)
+    err = np.abs(g[fin] - o[fin])
+    bad = err > tol
+    assert not bad.any(), f"{where}: {bad.sum()} scores off, worst rel {(err / np.maximum(np.abs(o[fin]), floor)).max():.3g}"
+    return float((err / np.maximum(np.abs(o[fin]), floor)).max())
+
+
+def check_topk(gpu_ids, cand, ora_scores, K, where=""):
+    """gpu_ids: the GPU's row (ids then -1); cand/ora_scores: the oracle's
+    candidates and fp64 scores."""
+    gpu_ids = np.asarray(gpu_ids)
+    valid = gpu_ids[gpu_ids >= 0]
+    n_exp = min(K, len(cand))
+    assert len(valid) == n_exp, f"{where}: {len(valid)} ids, expected {n_exp}"
+    assert np.all(gpu_ids[len(valid):] == -1), f"{where}: -1 padding not at the tail"
+    assert len(np.unique(valid)) == len(valid), f"{where}: duplicate ids"
+    score_of = dict(zip((int(c) for c in cand), ora_scores))
+    assert all(int(v) in score_of for v in valid), f"{where}: id outside the candidates"
+    ref = O.top_k(ora_scores, cand, K)
+    if n_exp == 0:
+        return 0
+    kth = score_of[int(ref[-1])]
+    diff = set(int(v) for v in valid) ^ set(int(r) for r in ref)
+    band = SET_BAND * max(abs(kth), 1e-30)
+    for d in diff:
+        assert abs(score_of[d] - kth) <= band, f"{where}: id {d} score {score_of[d]} vs K-th {kth}"
+    return len(diff)
+
+
+def oracle_attention(shared, layer, b, ti, ids):
+    """Oracle steps 7-10 (window, logits, sink softmax, inverse RoPE) on a
+    given index set."""
+    r = O.layer_query(shared, layer, b, ti, O.REUSE, prev_sel=np.asarray(ids, dtype=np.int64))
+    return r["out"]
+
+
+def check_attn(gpu_out, ora_out, tol, where=""):
+    err = np.abs(np.asarray(gpu_out, dtype=np.float64) - ora_out).max()
+    assert err <= tol, f"{where}: attention max-abs error {err:.3g} > {tol}"
+    return float(err)

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+that include/csa2.h declares, and rejects bad arguments with the documented
+status codes before anything is launched (no GPU is touched: every call
+below fails validation, and the *_workspace_bytes helpers are pure host
+code)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_context_csa2_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_long_context_csa2_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"csa2_index_scores", "csa2_block_pool", "csa2_topk", "csa2_sparse_attn", "csa2_layer"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.csa2_status_str(code)
+    assert B.version().startswith("csa2")
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_index_scores_validation(L):
+    f = L.csa2_index_scores
+    ok = dict(B=1, Tq=1, N=8, Hi=4, Di=16, m=1)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["B"], a["Tq"], a["N"], a["Hi"], a["Di"], a["m"], kw.get("q", FAKE), kw.get("qdt", 0),
+                 kw.get("w", FAKE), kw.get("k", FAKE), kw.get("ks", None), kw.get("kdt", 0),
+                 kw.get("pos", FAKE), None, kw.get("pool", None), kw.get("P", 0), kw.get("blk", 0),
+                 kw.get("out", FAKE), None, 0, None)
+
+    assert call(B=0) == B.CSA2_EINVAL
+    assert call(m=0) == B.CSA2_EINVAL
+    assert call(q=None) == B.CSA2_EINVAL
+    assert call(out=None) == B.CSA2_EINVAL
+    assert call(kdt=9) == B.CSA2_EINVAL
+    assert call(kdt=2) == B.CSA2_EINVAL              # e4m3 without scale
+    assert call(ks=FAKE) == B.CSA2_EINVAL            # scale for f32 keys
+    assert call(qdt=2) == B.CSA2_EUNSUPPORTED        # e4m3 queries
+    assert call(Hi=65) == B.CSA2_EUNSUPPORTED
+    assert call(pool=FAKE, P=0, blk=4) == B.CSA2_EINVAL
+    assert call(P=2, blk=4) == B.CSA2_EINVAL         # P/blk without a pool
+    msg = L.csa2_status_str(B.CSA2_EINVAL).decode()
+    assert "index_scores" in msg
+
+
+def test_topk_and_pool_validation(L):
+    assert L.csa2_topk(0, 8, 2, FAKE, None, 0, 0, FAKE, None, 0, None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 0, FAKE, None, 0, 0, FAKE, None, 0, None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 2049, FAKE, None, 0, 0, FAKE, None, 0, None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 2, None, None, 0, 0, FAKE, None, 0, None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 2, FAKE, FAKE, 3, 4, FAKE, None, 0, None) == B.CSA2_EINVAL  # 3*4 != 8
+    assert L.csa2_block_pool(1, 64, 0, 4, FAKE, FAKE, FAKE, 1 << 20, None) == B.CSA2_EINVAL
+    assert L.csa2_block_pool(1, 64, 4, 2049, FAKE, FAKE, FAKE, 1 << 20, None) == B.CSA2_EINVAL
+    need = L.csa2_block_pool_workspace_bytes(3, 64, 4)
+    assert need >= 3 * 16 * 4
+    assert L.csa2_block_pool(3, 64, 4, 2, FAKE, FAKE, FAKE, need - 1, None) == B.CSA2_EWORKSPACE
+    assert L.csa2_block_pool(3, 64, 4, 2, FAKE, FAKE, None, need, None) == B.CSA2_EWORKSPACE
+
+
+def _attn(L, **kw):
+    a = dict(B=1, Tq=1, H=64, D=512, N=100, K=16, q=FAKE, qdt=1, kv=FAKE, kvs=None, kvdt=1, idx=FAKE,
+             swa=FAKE, swas=None, swadt=1, S=128, W=128, pos=FAKE, sink=FAKE, sm=0.0, r=64, base=10000.0,
+             out=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return L.csa2_sparse_attn(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["K"], a["q"], a["qdt"], a["kv"],
+                              a["kvs"], a["kvdt"], a["idx"], a["swa"], a["swas"], a["swadt"], a["S"], a["W"],
+                              a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_sparse_attn_validation(L):
+    assert _attn(L, W=129) == B.CSA2_EINVAL           # window larger than ring
+    assert _attn(L, K=2049) == B.CSA2_EINVAL
+    assert _attn(L, r=63) == B.CSA2_EINVAL             # odd rotary dims
+    assert _attn(L, r=1024) == B.CSA2_EINVAL
+    assert _attn(L, base=0.0) == B.CSA2_EINVAL
+    assert _attn(L, sm=-1.0) == B.CSA2_EINVAL
+    assert _attn(L, sink=None) == B.CSA2_EINVAL
+    assert _attn(L, kvdt=2) == B.CSA2_EINVAL           # e4m3 without scale
+    assert _attn(L, kvs=FAKE) == B.CSA2_EINVAL         # scale for bf16
+    assert _attn(L, qdt=2) == B.CSA2_EUNSUPPORTED
+    assert _attn(L, H=3, D=2048, qdt=0, kvdt=0, swadt=0) == B.CSA2_EUNSUPPORTED
+    # decode-shaped calls need split partials: an empty workspace is refused
+    need = L.csa2_sparse_attn_workspace_bytes(1, 1, 64, 512, 512, 128)
+    assert need > 0
+    assert _attn(L, K=512, ws=None, wsb=0) == B.CSA2_EWORKSPACE
+    assert _attn(L, K=512, ws=FAKE, wsb=need - 1) == B.CSA2_EWORKSPACE
+
+
+def test_layer_validation_and_workspace(L):
+    d = B.LayerDesc()
+    d.mode, d.B, d.Tq, d.N, d.m = 0, 2, 1, 1000, 4
+    d.k_idx, d.k_dtype, d.kv, d.kv_dtype = FAKE, 1, FAKE, 1
+    d.Hi, d.Di, d.q_idx, d.q_idx_dtype, d.w = 32, 128, FAKE, 1, FAKE
+    d.H, d.D, d.q, d.q_dtype = 64, 512, FAKE, 1
+    d.swa, d.swa_dtype, d.S, d.W = FAKE, 1, 128, 128
+    d.sink, d.rope_dims, d.rope_base, d.q_pos = FAKE, 64, 10000.0, FAKE
+    d.K, d.idx_inout, d.out = 512, FAKE, FAKE
+    need = L.csa2_workspace_bytes(ctypes.byref(d))
+    assert need >= 2 * 1000 * 4
+    d.ws, d.ws_bytes = FAKE, need - 1
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EWORKSPACE
+    d.mode = 7
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
+    assert L.csa2_workspace_bytes(ctypes.byref(d)) == 0
+    d.mode = 2
+    d.idx_inout = None
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
+    d.idx_inout = FAKE
+    d.K = 0
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
+    # pooled Reindex scores P*blk columns instead of N
+    d.K, d.mode, d.pool_inout, d.P, d.blk = 512, 1, FAKE, 64, 64
+    assert L.csa2_workspace_bytes(ctypes.byref(d)) >= 2 * 64 * 64 * 4
+    assert L.csa2_layer(None, None) == B.CSA2_EINVAL

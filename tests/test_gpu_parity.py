@@ -1,0 +1,363 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle, at sizes
+the oracle finishes in seconds that still span several tiles and ragged
+tails.  Full-size configurations are in test_gpu_configs.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_long_context_csa2_amd import binding as Bd
+from sparse_long_context_csa2_amd import runner as R
+from sparse_long_context_csa2_amd import workloads as WL
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    return R.to_device(x)
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _small(**kw):
+    base = dict(name="small", seed=21, B=3, Tq=2, N=1000, m=4, Hi=32, Di=128, H=64, D=512,
+                rope_dims=64, W=16, K=64, decode_pos=3990)
+    base.update(kw)
+    return WL.Workload(**base)
+
+
+# ------------------------------------------------------------------ indexer
+
+def _run_scores(inp, pool=None, blk=0):
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_index_scores(_dev(lay["q_idx"]), _dev(lay["w"]), _dev(sh["k_idx"]), _dev(sh["k_scale"]),
+                               _dev(lay["q_pos"]), sh["m"], n_rec=_dev(sh["n_rec"]),
+                               pool=None if pool is None else _dev(pool), blk=blk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_index_scores_toy_fp32():
+    _case("index_scores C1 toy fp32 (generic kernel)")
+    inp = WL.make_inputs(WL.CONFIGS["C1"])
+    g = _run_scores(inp)
+    for ti in range(128):
+        PR.check_scores(g[0, ti], O.full_row_scores(inp["shared"], inp["layers"][0], 0, ti), f"t={ti}")
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+def test_index_scores_mfma_decode(kdt):
+    _case(f"index_scores decode rows, {kdt} keys, ragged N=1000, n_rec<N")
+    wl = _small(k_dtype=kdt, n_rec=(1000, 777, 5))
+    inp = WL.make_inputs(wl)
+    inp["layers"][0]["q_pos"][2] = [5, 100]  # partial visibility
+    g = _run_scores(inp)
+    for b in range(3):
+        for ti in range(2):
+            PR.check_scores(g[b, ti], O.full_row_scores(inp["shared"], inp["layers"][0], b, ti), f"b={b} t={ti}")
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+def test_index_scores_mfma_prefill(kdt):
+    _case(f"index_scores prefill tiles, {kdt} keys, Tq=70 (ragged token groups)")
+    wl = _small(B=2, Tq=70, N=40, decode_pos=None, k_dtype=kdt, W=8)
+    inp = WL.make_inputs(wl)
+    inp["layers"][0]["q_pos"][1] += 60  # second sequence later in its context
+    g = _run_scores(inp)
+    for b in range(2):
+        for ti in range(70):
+            PR.check_scores(g[b, ti], O.full_row_scores(inp["shared"], inp["layers"][0], b, ti), f"b={b} t={ti}")
+
+
+@pytest.mark.parametrize("shape", ["mfma", "generic"])
+def test_index_scores_pool_mode(shape):
+    if shape == "mfma":
+        wl, blk, P = _small(N=2048, decode_pos=8000, n_rec=(2048, 1500, 2048)), 64, 6
+    else:
+        wl, blk, P = _small(N=200, Hi=4, Di=16, q_idx_dtype="f32", k_dtype="f32", decode_pos=700), 4, 9
+    _case(f"index_scores pool mode ({shape}, blk={blk}, P={P})")
+    inp = WL.make_inputs(wl)
+    rng = np.random.default_rng(5)
+    nb = wl.N // blk
+    pool = rng.integers(0, nb, size=(wl.B, wl.Tq, P)).astype(np.int32)
+    pool[:, :, -1] = -1
+    pool[0, 0, 0] = nb - 1
+    g = _run_scores(inp, pool=pool, blk=blk)
+    for b in range(wl.B):
+        for ti in range(wl.Tq):
+            o = O.pool_row_scores(inp["shared"], inp["layers"][0], b, ti, pool[b, ti], blk)
+            PR.check_scores(g[b, ti], o, f"b={b} t={ti}")
+
+
+# ------------------------------------------------------------------ top-k
+
+def _ref_topk(row, K, rec=None):
+    n = len(row)
+    rec = np.arange(n) if rec is None else rec
+    ok = np.isfinite(row) | (row == np.inf)
+    ok &= rec >= 0
+    cand = np.nonzero(ok)[0]
+    order = np.lexsort((rec[cand], -row[cand].astype(np.float64)))
+    return cand[order[:K]]
+
+
+def _score_rows(rows, n, seed):
+    rng = np.random.default_rng(seed)
+    s = (rng.integers(0, 50, size=(rows, n)) / 50.0).astype(np.float32)  # many exact ties
+    s[0] = rng.standard_normal(n).astype(np.float32)
+    s[1, ::7] = -np.inf
+    s[1, 3::11] = np.nan
+    if rows > 2:
+        s[2] = 0.0  # all equal
+    if rows > 3:
+        s[3, : n // 2] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("n,K", [(5, 8), (700, 8), (1024, 512), (16384, 512), (20000, 2048), (65536, 512)])
+def test_topk_exact(n, K):
+    _case(f"topk rows=4 n={n} K={K}")
+    s = _score_rows(4, n, n + K)
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(4):
+        ref = np.sort(_ref_topk(s[r], K))
+        got = g[r][g[r] >= 0]
+        assert np.array_equal(got, ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1)
+
+
+def test_topk_pool_mapping_ties_by_record_id():
+    _case("topk with a pool column map")
+    P, blk, K = 6, 64, 100
+    rng = np.random.default_rng(9)
+    s = (rng.integers(0, 20, size=(3, P * blk)) / 20.0).astype(np.float32)
+    pool = np.stack([rng.permutation(40)[:P] for _ in range(3)]).astype(np.int32)
+    pool[1, 2] = -1
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=torch.from_numpy(pool).cuda(), blk=blk)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(3):
+        cols = np.arange(P * blk)
+        pb = pool[r][cols // blk]
+        rec = np.where(pb < 0, -1, pb * blk + cols % blk)
+        ref = set(rec[_ref_topk(s[r], K, rec)].tolist())
+        got = g[r][g[r] >= 0]
+        assert set(got.tolist()) == ref and len(got) == len(ref)
+
+
+@pytest.mark.parametrize("blk,P,N", [(4, 8, 128), (64, 64, 65536), (8, 2048, 20000)])
+def test_block_pool_exact(blk, P, N):
+    _case(f"block_pool blk={blk} P={P} N={N}")
+    rng = np.random.default_rng(blk + P)
+    s = (rng.integers(0, 30, size=(3, N)) / 30.0).astype(np.float32)
+    s[1, N // 3:] = -np.inf  # invisible tail
+    s[2, :] = -np.inf
+    s[2, :blk * 3] = 0.5
+    g = Bd.csa2_block_pool(torch.from_numpy(s).cuda(), blk, P)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(3):
+        fin = np.nonzero(np.isfinite(s[r]))[0]
+        ref = O.block_pool(s[r][fin].astype(np.float64), fin, blk, P)
+        got = g[r][g[r] >= 0]
+        assert np.array_equal(got, ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(kdt, Tq, q_gain=1.0, **kw):
+    wl = _small(B=2, Tq=Tq, N=300, K=48, W=24, swa_slots=32, decode_pos=5000, k_dtype=kdt, kv_dtype=kdt,
+                swa_dtype=kdt, **kw)
+    inp = WL.make_inputs(wl, q_gain=q_gain)
+    rng = np.random.default_rng(Tq)
+    idx = rng.integers(0, 300, size=(2, Tq, 48)).astype(np.int32)
+    idx[:, :, 40:] = -1
+    idx[0, 0, 5] = 300 + 7        # out of range: skipped
+    idx[1, 0, :] = -1             # window only
+    inp["layers"][0]["q_pos"][1, 0] = 3  # window truncated at position 0
+    return wl, inp, idx
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("Tq", [3, 150])
+def test_sparse_attn_mfma(kdt, Tq):
+    _case(f"sparse_attn mfma {kdt} Tq={Tq} ({'split' if Tq < 128 else 'single'} path)")
+    wl, inp, idx = _attn_case(kdt, Tq)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    tol = PR.ATTN_TOL[kdt]
+    worst = 0.0
+    for b in range(2):
+        for ti in (list(range(Tq)) if Tq < 10 else [0, 1, 77, Tq - 1]):
+            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+            worst = max(worst, PR.check_attn(out[b, ti], ref, tol, f"b={b} t={ti}"))
+    print(f"max abs err {worst:.3g}")
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+def test_sparse_attn_sharp_logits(kdt):
+    """Queries scaled by sqrt(D): logits of order 1-10 stress the online
+    max rescaling and the sink; the bf16 hi+lo split keeps P exact enough."""
+    _case(f"sparse_attn sharp logits {kdt}")
+    wl, inp, idx = _attn_case(kdt, 3, q_gain=math.sqrt(512), kv_std=1.0)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(2):
+        for ti in range(3):
+            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+            # unit-scale rows: hold bf16 to the stated 2e-3, e4m3 to 5e-2
+            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+
+
+@pytest.mark.parametrize("H,D,dt", [(2, 16, "f32"), (3, 48, "bf16")])
+def test_sparse_attn_generic(H, D, dt):
+    _case(f"sparse_attn generic H={H} D={D} {dt}")
+    wl = _small(B=2, Tq=5, N=50, K=12, H=H, D=D, rope_dims=4, W=6, swa_slots=8, decode_pos=60,
+                q_dtype=dt, kv_dtype=dt, swa_dtype=dt, q_std=1.0, kv_std=1.0)
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    rng = np.random.default_rng(3)
+    idx = rng.integers(-1, 50, size=(2, 5, 12)).astype(np.int32)
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), None, _dev(idx), _dev(lay["swa"]), None, wl.W,
+                              _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(2):
+        for ti in range(5):
+            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+            PR.check_attn(out[b, ti], ref, 1e-4 if dt == "f32" else PR.ATTN_TOL[dt], f"b={b} t={ti}")
+
+
+# ------------------------------------------------------------------ layers
+
+def _check_group(inp, grp, rows):
+    """Checks every layer of a group on the given (b, ti) rows."""
+    sh, lays = inp["shared"], inp["layers"]
+    outs = grp.outputs()
+    idxs = grp.index_sets()
+    pool = None if grp.pool is None else grp.pool.cpu().numpy()
+    for (b, ti) in rows:
+        prev = None
+        for li, lay in enumerate(lays):
+            mode = lay["mode"]
+            where = f"layer {li} ({mode}) b={b} t={ti}"
+            ids = idxs[li][b, ti]
+            if mode == "full":
+                r = O.layer_query(sh, lay, b, ti, O.FULL, build_pool=lay["build_pool"])
+                PR.check_topk(ids, r["cand"], r["scores"], lay["K"], where)
+                if lay["build_pool"]:
+                    _check_pool(pool[b, ti], r["cand"], r["scores"], lay["blk"], lay["P"], where + " pool")
+            elif mode == "reindex":
+                gp = pool[b, ti]
+                r = O.layer_query(sh, lay, b, ti, O.REINDEX, pool_in=gp[gp >= 0])
+                PR.check_topk(ids, r["cand"], r["scores"], lay["K"], where)
+            else:
+                assert np.array_equal(ids, prev), where
+            ref = PR.oracle_attention(sh, lay, b, ti, ids)
+            PR.check_attn(outs[li][b, ti], ref, PR.ATTN_TOL[inp["wl"].kv_dtype], where)
+            prev = ids
+
+
+def _block_scores(cand, scores, blk):
+    blocks = np.asarray(cand) // blk
+    ids = np.unique(blocks)
+    beta = np.array([scores[blocks == b].max() for b in ids])
+    return ids, beta
+
+
+def _check_pool(gpool, cand, scores, blk, P, where):
+    """Pool = Top-P blocks by oracle block maximum (set rule with the tie
+    band), listed in non-increasing block-maximum order."""
+    valid = gpool[gpool >= 0]
+    ids, beta = _block_scores(cand, scores, blk)
+    padded = np.concatenate([np.sort(valid), gpool[len(valid):]])
+    PR.check_topk(padded, ids, beta, P, where)
+    bm = dict(zip(ids.tolist(), beta.tolist()))
+    seq = [bm[int(x)] for x in valid]
+    for a, c in zip(seq, seq[1:]):
+        assert c <= a + PR.SET_BAND * abs(a), f"{where}: pool not ordered by block maximum"
+
+
+def test_layer_toy_c1():
+    _case("layer C1 toy (Full + pool)")
+    inp = WL.make_inputs(WL.CONFIGS["C1"])
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    _check_group(inp, grp, [(0, t) for t in range(128)])
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+def test_layer_group_small(kdt):
+    _case(f"layer group Full+pool, Reindex x2, Reuse x2 ({kdt})")
+    wl = _small(B=3, Tq=1, N=4096, blk=64, P=8, K=128, W=32, decode_pos=16400, k_dtype=kdt, kv_dtype=kdt,
+                swa_dtype=kdt, modes=("full+pool", "reindex", "reindex", "reuse", "reuse"),
+                n_rec=(4096, 3000, 4096))
+    inp = WL.make_inputs(wl)
+    inp["layers"][0]["q_pos"][2, 0] = 900  # sees 225 records: a ragged last block
+    for lay in inp["layers"][1:]:
+        lay["q_pos"] = inp["layers"][0]["q_pos"]
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    _check_group(inp, grp, [(b, 0) for b in range(3)])
+
+
+def test_determinism_and_reuse_identity():
+    _case("two runs give identical index sets and outputs")
+    wl = _small(B=2, Tq=1, N=3000, blk=64, P=8, K=96, decode_pos=20000,
+                modes=("full+pool", "reindex", "reuse"))
+    inp = WL.make_inputs(wl)
+    # the Reuse layer gets the Reindex layer's own query, window and sink
+    for k in ("q", "swa", "swa_scale", "sink"):
+        inp["layers"][2][k] = inp["layers"][1][k]
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    o1, i1 = grp.outputs(), grp.index_sets()
+    grp.run()
+    torch.cuda.synchronize()
+    o2, i2 = grp.outputs(), grp.index_sets()
+    for a, b in zip(i1, i2):
+        assert np.array_equal(a, b)
+    for a, b in zip(o1, o2):
+        assert np.array_equal(a, b)
+    assert np.array_equal(o1[2], o1[1])  # same indices + same query -> same output
+
+
+def test_prefill_row_equals_decode():
+    """A prefill row at position t and a decode call at t over the same
+    caches give the same selection and output (cached vs full-prefix
+    consistency)."""
+    _case("prefill row t == decode at t")
+    wl = _small(B=1, Tq=48, N=12, decode_pos=None, W=8, K=6)
+    inp = WL.make_inputs(wl)
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    out_p, idx_p = grp.outputs()[0], grp.index_sets()[0]
+    for t in (3, 20, 47):
+        one = {"shared": inp["shared"], "wl": wl.with_(Tq=1), "layers": [dict(inp["layers"][0])]}
+        lay = one["layers"][0]
+        for k in ("q_idx", "w", "q", "q_pos"):
+            lay[k] = np.ascontiguousarray(inp["layers"][0][k][:, t:t + 1])
+        g1 = R.DeviceGroup(one)
+        g1.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(g1.index_sets()[0][0, 0]), np.sort(idx_p[0, t]))
+        assert np.abs(g1.outputs()[0][0, 0] - out_p[0, t]).max() <= 1e-5
