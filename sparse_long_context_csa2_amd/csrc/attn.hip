@@ -14,8 +14,11 @@
 // paths").
 //
 // attn_mfma_kernel (64 heads x 512 dims, bf16 queries, bf16 or e4m3 rows):
-//  * one workgroup = 4 waves per (query, split of the entry list); wave w
-//    owns heads 16w .. 16w+15;
+//  * one workgroup = 8 waves per (query, split of the entry list); wave w
+//    owns heads 16*(w%4) .. +15 and channel half w/4 of the 512-dim latent,
+//    so each lane keeps only 64 fp32 accumulators and 32 query registers
+//    and two waves share every SIMD; the two halves of a head exchange
+//    their partial logits through LDS (2 KiB per wave per tile);
 //  * the valid selected records are first compacted into an LDS list, so
 //    -1 padding costs nothing;
 //  * entries are processed in tiles of 32 rows (32 KiB of bf16).  A tile is
@@ -38,6 +41,8 @@
 //    attn_combine_kernel merges the splits.
 // attn_generic_kernel: any head count and dim (one workgroup per query and
 // head, fp32 throughout); used for small shapes such as the toy.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -47,10 +52,10 @@ namespace {
 constexpr int kH = 64;
 constexpr int kD = 512;
 constexpr int kTile = 32;
-constexpr int kXrPitch = kD * 2 + 16;  // bytes per row-major LDS row
 constexpr int kMaxKList = 2048;
 constexpr int kMaxRope = kD / 2;
 constexpr int kMaxSplits = 32;
+constexpr float kLazy = 8.f;  // nats
 
 struct AttnP {
     int B, Tq, N, K, S, W, nsplit, per_split;
@@ -70,53 +75,111 @@ struct AttnP {
     float* part_ml;           // [Q][nsplit][64][2]
 };
 
+constexpr int kXPitch = kD * 2 + 32;  // bytes per LDS tile row (bf16); 32-byte skew per row
+constexpr int kBuf = kTile * kXPitch;   // one tile buffer
+constexpr int kIdxPerThread = kMaxKList / 512;
+
+// cos/sin of the rotary angle t * base^(-2j/r): the angle is formed and
+// reduced modulo 2*pi in double precision (t reaches 2^20), the reduced
+// angle goes through single-precision sincos.
+__device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base, float& c, float& s) {
+    const double inv = pow(static_cast<double>(base), -2.0 * j / rd);
+    const double th = static_cast<double>(t) * inv;
+    const double k = rint(th * 0.15915494309189533577);       // 1 / (2 pi)
+    double r = fma(-k, 6.283185307179586232, th);              // 2 pi, high part
+    r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi, low part
+    sincosf(static_cast<float>(r), &s, &c);
+}
+
+// Barrier for LDS hand-offs: this wave's LDS writes are complete, then all
+// waves meet.  Unlike __syncthreads() it does not wait for outstanding
+// global loads (the tile prefetches keep flowing across it); the asm is
+// also a compiler memory barrier.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// This wave's tile copies except the newest n (0..4) have completed.
+__device__ __forceinline__ void wait_tile_copies(int n) {
+    switch (n) {  // wave-uniform
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// Copies 16 bytes per lane from global memory straight into LDS at
+// lds_row + 16 * lane (gfx950 global_load_lds_dwordx4; M0 holds the LDS
+// byte address).  Issued as asm so that the compiler does not serialise
+// later LDS reads of the other tile buffers behind it: completion is
+// awaited explicitly with wait_tile_copies().
+__device__ __forceinline__ void row_copy16(const void* gptr, const void* lds_row) {
+    const uint32_t lds = static_cast<uint32_t>(
+        reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)(lds_row)));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
+constexpr int kNBuf = 3;  // tiles in flight: computing t, landing t+1 and t+2
+
 struct __align__(16) AttnShared {
-    uint8_t xr[kTile * kXrPitch];         // row-major tile
-    uint8_t xt[4 * kD * 16];              // [entry group][d (swizzled)][8 entries]
+    uint8_t xb[kNBuf][kBuf];              // tile buffers (row-major: entry, channel)
+    float sx[8][64][8];                   // partial logits exchanged between channel halves
     int32_t list[kMaxKList];              // compacted valid record ids
-    float esc[kTile];                     // per-entry scale
-    int evalid[kTile];
     float rope_cs[kMaxRope][2];
-    int wave_cnt[4];
-    int nsel;
+    float esc[kNBuf][kTile];              // per-entry scale (0 for empty entries)
+    int evalid[kNBuf][kTile];
+    int wave_cnt[8];
 };
 
-// Physical d slot of (entry group grp, channel d) in the transposed tile:
-// an XOR inside each aligned block of 16 channels.
-__device__ __forceinline__ int xt_slot(int grp, int d) {
-    return grp * kD + ((d & ~15) | ((d ^ (d >> 4) ^ (grp << 2)) & 15));
+// Query row handled by workgroup L of a launch over Q rows.  Workgroups
+// are dispatched to the 8 XCDs round-robin (L % 8); giving each XCD whole
+// chunks of 64 consecutive query positions keeps the rows those queries
+// gather (shared records and overlapping windows) inside that XCD's L2.
+// Later positions (more entries) go first.
+__device__ __forceinline__ int query_of_block(int L, int Q) {
+    constexpr int kChunkQ = 64, kXcd = 8;
+    const int full = (Q / (kChunkQ * kXcd)) * (kChunkQ * kXcd);
+    int qr = L;
+    if (L < full) {
+        const int x = L % kXcd, m = L / kXcd;
+        qr = ((m / kChunkQ) * kXcd + x) * kChunkQ + (m % kChunkQ);
+    }
+    return Q - 1 - qr;
 }
 
+// 8 waves: wave w owns heads 16*(w&3) .. +15 and channels 256*(w>>2) ..
+// +255.  Tile rows are copied global -> LDS in row-major order (entry,
+// channel), two tiles ahead of the one being multiplied.  S^T = X Q^T
+// reads 16-byte row chunks; O^T += X^T P^T reads its operand with the
+// gfx950 transposing LDS load: within each 16-lane group, lane j receives
+// element j%4 of the 64-bit chunk addressed by lane 4k+j/4 (k = 0..3), so
+// pointing lane s of group g at X[4g + s/4][d0 + 4(s%4) ..] hands lane j
+// the four entries 4g..4g+3 of channel d0 + j -- the MFMA A operand.
 template <int KVDT>
-__device__ __forceinline__ u32x4 load_row_chunk(const uint8_t* row, int c, bool ok) {
-    if (!ok) return u32x4{0, 0, 0, 0};
-    if (KVDT == DT_BF16) return *reinterpret_cast<const u32x4*>(row + 16 * c);
-    const u32x2 v = *reinterpret_cast<const u32x2*>(row + 8 * c);
-    return e4m3x8_to_bf16x8(v);
-}
-
-__device__ __forceinline__ uint32_t pick_half(uint32_t a, uint32_t b, int k) {
-    // element k of two bf16x8 dwords -> packed pair (a's, b's)
-    return (k & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-}
-
-template <int KVDT>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnP p) {
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
     __shared__ AttnShared sh;
+    typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
+    constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int l16 = lane & 15;
     const int g = lane >> 4;
+    const int hg = wave & 3;   // head group
+    const int dh = wave >> 2;  // channel half
+    const int h = 16 * hg + l16;
     const int split = blockIdx.x;
-    const int qr = blockIdx.y;
+    const int Q = p.B * p.Tq;
+    const int qr = p.nsplit == 1 ? query_of_block(blockIdx.y, Q) : static_cast<int>(blockIdx.y);
     const int b = qr / p.Tq;
     const int64_t t = p.q_pos[qr];
-    constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
+    const int rd = p.rope_dims;
 
     // ---- compact the valid selected records (in order) ----
     const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
     int nsel = 0;
-    for (int base = 0; base < p.K; base += 256) {
+    for (int base = 0; base < p.K; base += 512) {
         const int j = base + threadIdx.x;
         int rec = -1;
         if (j < p.K) rec = irow[j];
@@ -127,122 +190,158 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnP p) {
         int off = nsel;
         for (int i = 0; i < wave; ++i) off += sh.wave_cnt[i];
         if (ok) sh.list[off + __popcll(bal & ((1ull << lane) - 1ull))] = rec;
-        for (int i = 0; i < 4; ++i) nsel += sh.wave_cnt[i];
+        for (int i = 0; i < 8; ++i) nsel += sh.wave_cnt[i];
         __syncthreads();
     }
     const int nwin = t < 0 ? 0 : static_cast<int>(t + 1 < p.W ? t + 1 : p.W);
-    const int64_t win0 = t - nwin + 1;
+    const int slot0 = static_cast<int>((t - nwin + 1) % p.S);  // ring slot of the first window row
     const int E = nsel + nwin;
     const int j0 = split * p.per_split;
     const int j1 = min(E, j0 + p.per_split);
+    for (int i = threadIdx.x; i < rd / 2; i += 512) rope_angle(t, i, rd, p.rope_base, sh.rope_cs[i][0], sh.rope_cs[i][1]);
 
-    // rotary angles of this query (double precision: t reaches 2^20)
-    const int rd = p.rope_dims;
-    for (int i = threadIdx.x; i < rd / 2; i += 256) {
-        const double inv = pow(static_cast<double>(p.rope_base), -2.0 * i / rd);
-        double s, c;
-        sincos(static_cast<double>(t) * inv, &s, &c);
-        sh.rope_cs[i][0] = static_cast<float>(c);
-        sh.rope_cs[i][1] = static_cast<float>(s);
-    }
-
-    // ---- query fragments: head 16*wave + l16, 16 k-steps of 8 channels ----
-    const int h = 16 * wave + l16;
-    bf16x8 qf[16];
+    // ---- query fragments: head h, this wave's 8 k-steps of 32 channels ----
+    bf16x8 qf[8];
     {
         const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks)
-            qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (g + 4 * ks)));
+        for (int i = 0; i < 8; ++i)
+            qf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (g + 4 * (8 * dh + i))));
     }
 
-    // ---- staging geometry: rows 8*g .. 8*g+7 of the tile, chunk c ----
-    const int c = 16 * wave + l16;  // 8-channel chunk owned by this lane
-    auto row_ptr = [&](int e, bool& ok, float& scale) -> const uint8_t* {
+    auto row_of = [&](int e, bool& ok, float& scale) -> const uint8_t* {
         ok = e < j1;
         scale = 0.f;
         if (!ok) return nullptr;
         if (e < nsel) {
-            const int rec = sh.list[e];
-            const size_t r = static_cast<size_t>(b) * p.N + rec;
+            const size_t r = static_cast<size_t>(b) * p.N + sh.list[e];
             scale = KVDT == DT_E4M3 ? p.kv_scale[r] : 1.f;
             return p.kv + r * kRowBytes;
         }
-        const int64_t pos = win0 + (e - nsel);
-        const size_t r = static_cast<size_t>(b) * p.S + static_cast<size_t>(pos % p.S);
+        int slot = slot0 + (e - nsel);  // < 2S since the window has at most S rows
+        if (slot >= p.S) slot -= p.S;
+        const size_t r = static_cast<size_t>(b) * p.S + slot;
         scale = KVDT == DT_E4M3 ? p.swa_scale[r] : 1.f;
         return p.swa + r * kRowBytes;
     };
 
-    u32x4 stg[8];
-    auto fetch = [&](int tb) {
+    // Tile staging: wave w fills rows 4w .. 4w+3.  bf16 rows go straight
+    // from global memory into LDS (one 1 KiB row per wave instruction); rows
+    // past the end are zero-filled.  e4m3 rows are converted to bf16 in
+    // registers on the way (staged one tile ahead).
+    Raw stg[4];
+    auto issue = [&](int tb, int k) {
+        uint8_t* xb = sh.xb[k];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * wave + i;
             bool ok;
             float sc;
-            const uint8_t* rp = row_ptr(tb + 8 * g + i, ok, sc);
-            stg[i] = load_row_chunk<KVDT>(rp, c, ok);
-        }
-    };
-
-    float m_run = -__builtin_huge_valf();
-    float l_run = 0.f;
-    f32x4 acc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    __syncthreads();  // list, rope table visible
-    if (j0 < j1) fetch(j0);
-
-    for (int tb = j0; tb < j1; tb += kTile) {
-        __syncthreads();  // previous tile fully consumed
-        // ---- write the staged tile: row-major and transposed ----
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4*>(sh.xr + (8 * g + i) * kXrPitch + 16 * c) = stg[i];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            u32x4 v;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) v[m] = pick_half(stg[2 * m][k >> 1], stg[2 * m + 1][k >> 1], k);
-            *reinterpret_cast<u32x4*>(sh.xt + 16 * xt_slot(g, 8 * c + k)) = v;
+            const uint8_t* rp = row_of(tb + r, ok, sc);
+            if constexpr (KVDT == DT_BF16) {
+                if (ok) row_copy16(rp + 16 * lane, xb + r * kXPitch);
+                else *reinterpret_cast<u32x4*>(xb + r * kXPitch + 16 * lane) = u32x4{0, 0, 0, 0};
+            } else {
+                stg[i] = ok ? *reinterpret_cast<const Raw*>(rp + 8 * lane) : Raw{};
+            }
         }
         if (threadIdx.x < kTile) {
             bool ok;
             float sc;
-            row_ptr(tb + threadIdx.x, ok, sc);
-            sh.esc[threadIdx.x] = sc;
-            sh.evalid[threadIdx.x] = ok ? 1 : 0;
+            row_of(tb + threadIdx.x, ok, sc);
+            sh.esc[k][threadIdx.x] = sc;
+            sh.evalid[k][threadIdx.x] = ok ? 1 : 0;
         }
-        // prefetch the next tile while this one is computed
-        if (tb + kTile < j1) fetch(tb + kTile);
-        __syncthreads();
-
-        // ---- S^T = X Q^T : entries 16*mt + 4g + v, head h ----
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    };
+    auto land = [&](int k) {  // e4m3 only: staged registers -> LDS
+        if constexpr (KVDT == DT_E4M3) {
+            uint8_t* xb = sh.xb[k];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const int ch = g + 4 * ks;
-            const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.xr + l16 * kXrPitch + 16 * ch));
-            const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.xr + (16 + l16) * kXrPitch + 16 * ch));
-            s0 = mfma16x16x32(a0, qf[ks], s0);
-            s1 = mfma16x16x32(a1, qf[ks], s1);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(xb + (4 * wave + i) * kXPitch + 16 * lane) = e4m3x8_to_bf16x8(stg[i]);
         }
-        // ---- online softmax over this tile ----
+    };
+    // copies this wave issues for the tile at tb (rows at or past j1 are
+    // zero-filled instead)
+    auto copies = [&](int tb) { return min(4, max(0, j1 - tb - 4 * wave)); };
+
+    float m_run = -__builtin_huge_valf();
+    float l_run = 0.f;
+    f32x4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // list, rope table visible
+    const int ntile = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+    if constexpr (KVDT == DT_BF16) {
+        // settle the query-fragment loads now (a wait the compiler tracks), so
+        // that it places no vmcnt waits inside the loop, where they would
+        // also wait for the tile copies in flight
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+        if (ntile > 0) issue(j0, 0);
+        if (ntile > 1) issue(j0 + kTile, 1);
+    } else {
+        if (ntile > 0) issue(j0, 0);
+    }
+
+    for (int it = 0; it < ntile; ++it) {
+        const int tb = j0 + it * kTile;
+        const int cb = it % kNBuf;
+        if constexpr (KVDT == DT_BF16) {
+            wait_tile_copies(it + 1 < ntile ? copies(tb + kTile) : 0);
+            lds_sync();  // every wave's rows of tile `it` landed; tile it-1 consumed
+            if (it + 2 < ntile) issue(tb + 2 * kTile, (it + 2) % kNBuf);
+        } else {
+            land(cb);
+            if (it + 1 < ntile) issue(tb + kTile, (it + 1) % kNBuf);
+            lds_sync();
+        }
+        const uint8_t* xb = sh.xb[cb];
+        // ---- partial S^T over this wave's channel half ----
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const int ch = g + 4 * (8 * dh + i);
+            const uint8_t* r0 = xb + l16 * kXPitch + 16 * ch;
+            const uint8_t* r1 = r0 + 16 * kXPitch;
+            const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(r0));
+            const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(r1));
+            const bf16x8 a2 = as_bf16x8(*reinterpret_cast<const u32x4*>(r0 + 64));
+            const bf16x8 a3 = as_bf16x8(*reinterpret_cast<const u32x4*>(r1 + 64));
+            s0 = mfma16x16x32(a0, qf[i], s0);
+            s1 = mfma16x16x32(a1, qf[i], s1);
+            s2 = mfma16x16x32(a2, qf[i + 1], s2);
+            s3 = mfma16x16x32(a3, qf[i + 1], s3);
+        }
+        s0 += s2;
+        s1 += s3;
+        *reinterpret_cast<f32x4*>(&sh.sx[wave][lane][0]) = s0;
+        *reinterpret_cast<f32x4*>(&sh.sx[wave][lane][4]) = s1;
+        lds_sync();
+        // full logits: mine + the other channel half's (same sum in both waves)
+        s0 += *reinterpret_cast<const f32x4*>(&sh.sx[wave ^ 4][lane][0]);
+        s1 += *reinterpret_cast<const f32x4*>(&sh.sx[wave ^ 4][lane][4]);
+
+        // ---- online softmax over this tile: entries 16*mt + 4g + v, head h ----
+        const float* esc = sh.esc[cb];
+        const int* ev = sh.evalid[cb];
         float z[8];
         float tmax = -__builtin_huge_valf();
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int e0 = 4 * g + v, e1 = 16 + 4 * g + v;
-            z[v] = sh.evalid[e0] ? s0[v] * p.sm * sh.esc[e0] : -__builtin_huge_valf();
-            z[4 + v] = sh.evalid[e1] ? s1[v] * p.sm * sh.esc[e1] : -__builtin_huge_valf();
+            z[v] = ev[e0] ? s0[v] * p.sm * esc[e0] : -__builtin_huge_valf();
+            z[4 + v] = ev[e1] ? s1[v] * p.sm * esc[e1] : -__builtin_huge_valf();
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -__builtin_huge_valf()) ? 1.f : __expf(m_run - m_new);
+        // The reference max only moves when this tile exceeds it by more than
+        // kLazy (so probabilities stay below e^kLazy); otherwise O needs no
+        // rescale.  The result is the same: every term is relative to m_run.
+        const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
+        const float alpha = (m_run == -__builtin_huge_valf() || m_new == m_run) ? 1.f : __expf(m_run - m_new);
         float psum = 0.f;
         uint32_t phi[4], plo[4];
 #pragma unroll
@@ -253,14 +352,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnP p) {
                 const int ii = i + u;
                 const int e = (ii < 4) ? 4 * g + ii : 16 + 4 * g + (ii - 4);
                 pp[u] = (z[ii] == -__builtin_huge_valf()) ? 0.f : __expf(z[ii] - m_new);
-                pw[u] = pp[u] * sh.esc[e];
+                pw[u] = pp[u] * esc[e];
                 psum += pp[u];
             }
             const uint32_t hi = pack_bf16x2(pw[0], pw[1]);
-            const float r0 = pw[0] - __uint_as_float(hi << 16);
-            const float r1 = pw[1] - __uint_as_float(hi & 0xFFFF0000u);
+            const float q0 = pw[0] - __uint_as_float(hi << 16);
+            const float q1 = pw[1] - __uint_as_float(hi & 0xFFFF0000u);
             phi[i >> 1] = hi;
-            plo[i >> 1] = pack_bf16x2(r0, r1);
+            plo[i >> 1] = pack_bf16x2(q0, q1);
         }
         psum += shfl_xor_f(psum, 16);
         psum += shfl_xor_f(psum, 32);
@@ -269,38 +368,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnP p) {
         const bf16x8 bhi = as_bf16x8(u32x4{phi[0], phi[1], phi[2], phi[3]});
         const bf16x8 blo = as_bf16x8(u32x4{plo[0], plo[1], plo[2], plo[3]});
 
-        // ---- O^T += X^T P^T : channels 16*dt + 4g + v, head h ----
-        const int half = 8 * (g & 1);
-        const int ga = g >> 1, gb = 2 + (g >> 1);
+        // ---- O^T += X^T P^T : channels 256*dh + 16*u + 4g + v, head h ----
+        if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-            const int d = 16 * dt + l16;
-            const u32x2 xa = *reinterpret_cast<const u32x2*>(sh.xt + 16 * xt_slot(ga, d) + half);
-            const u32x2 xb = *reinterpret_cast<const u32x2*>(sh.xt + 16 * xt_slot(gb, d) + half);
-            const bf16x8 a = as_bf16x8(u32x4{xa[0], xa[1], xb[0], xb[1]});
-            f32x4 o = acc[dt] * alpha;
-            o = mfma16x16x32(a, bhi, o);
-            acc[dt] = mfma16x16x32(a, blo, o);
+            for (int u = 0; u < 16; ++u) acc[u] *= alpha;
         }
+        // transposing-read source: lane s of group g -> row 4g + s/4 (and
+        // 16 + ...), channels d0 + 4(s%4) .. +3
+        const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3) + 2 * 256 * dh;
+        const uint8_t* tr1 = tr0 + 16 * kXPitch;
+#pragma unroll
+        for (int uh = 0; uh < 16; uh += 4) {
+            bf16x8 a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(tr0 + 32 * (uh + u)));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(tr1 + 32 * (uh + u)));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                a[u] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(a[u], bhi, acc[uh + u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(a[u], blo, acc[uh + u]);
+        }
+
     }
 
     // ---- finish ----
     if (p.nsplit == 1) {
-        const float sk = p.sink[h];
-        const float a = fmaxf(m_run, sk);
+        const float skv = p.sink[h];
+        const float a = fmaxf(m_run, skv);
         float f = 0.f;
         if (a != -__builtin_huge_valf()) {
             const float em = (m_run == -__builtin_huge_valf()) ? 0.f : __expf(m_run - a);
-            const float es = (sk == -__builtin_huge_valf()) ? 0.f : __expf(sk - a);
+            const float es = (skv == -__builtin_huge_valf()) ? 0.f : __expf(skv - a);
             const float den = l_run * em + es;
             f = den > 0.f ? em / den : 0.f;
         }
         float* orow = p.out + (static_cast<size_t>(qr) * kH + h) * kD;
         const int r0 = kD - rd;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-            const int d = 16 * dt + 4 * g;
-            f32x4 o = acc[dt] * f;
+        for (int u = 0; u < 16; ++u) {
+            const int d = 256 * dh + 16 * u + 4 * g;
+            f32x4 o = acc[u] * f;
             if (d + 3 >= r0) {
 #pragma unroll
                 for (int v = 0; v < 4; v += 2) {
@@ -320,39 +435,35 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnP p) {
         const size_t slot = (static_cast<size_t>(qr) * p.nsplit + split) * kH + h;
         float* po = p.part_o + slot * kD;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = acc[dt];
-        if (g == 0) {
+        for (int u = 0; u < 16; ++u) *reinterpret_cast<f32x4*>(po + 256 * dh + 16 * u + 4 * g) = acc[u];
+        if (g == 0 && dh == 0) {
             p.part_ml[2 * slot] = m_run;
             p.part_ml[2 * slot + 1] = l_run;
         }
     }
 }
 
-// Merges split partials: one workgroup per query, each thread one channel
-// pair of every head.
+// Merges split partials: one workgroup per (query, group of 4 heads); each
+// thread owns 8 consecutive channels of one head.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
     __shared__ float rope_cs[kMaxRope][2];
-    __shared__ float wts[kH][kMaxSplits + 1];
+    __shared__ float wts[4][kMaxSplits];
     const int qr = blockIdx.x;
+    const int h0 = 4 * blockIdx.y;
     const int64_t t = p.q_pos[qr];
     const int rd = p.rope_dims;
-    for (int i = threadIdx.x; i < rd / 2; i += 256) {
-        const double inv = pow(static_cast<double>(p.rope_base), -2.0 * i / rd);
-        double s, c;
-        sincos(static_cast<double>(t) * inv, &s, &c);
-        rope_cs[i][0] = static_cast<float>(c);
-        rope_cs[i][1] = static_cast<float>(s);
-    }
+    for (int i = threadIdx.x; i < rd / 2; i += 256) rope_angle(t, i, rd, p.rope_base, rope_cs[i][0], rope_cs[i][1]);
     const int ns = p.nsplit;
     // per-head split weights: w_s = e^{m_s - a} / den
-    if (threadIdx.x < kH) {
-        const int h = threadIdx.x;
+    if (threadIdx.x < 4) {
+        const int h = h0 + threadIdx.x;
         const float* ml = p.part_ml + (static_cast<size_t>(qr) * ns * kH + h) * 2;
-        float a = p.sink[h];
+        const float sk = p.sink[h];
+        float a = sk;
         for (int s = 0; s < ns; ++s) a = fmaxf(a, ml[static_cast<size_t>(s) * kH * 2]);
         float den = 0.f;
         if (a != -__builtin_huge_valf()) {
-            den = (p.sink[h] == -__builtin_huge_valf()) ? 0.f : __expf(p.sink[h] - a);
+            den = (sk == -__builtin_huge_valf()) ? 0.f : __expf(sk - a);
             for (int s = 0; s < ns; ++s) {
                 const float m = ml[static_cast<size_t>(s) * kH * 2];
                 if (m != -__builtin_huge_valf()) den += ml[static_cast<size_t>(s) * kH * 2 + 1] * __expf(m - a);
@@ -360,29 +471,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
         }
         for (int s = 0; s < ns; ++s) {
             const float m = ml[static_cast<size_t>(s) * kH * 2];
-            wts[h][s] = (den > 0.f && m != -__builtin_huge_valf()) ? __expf(m - a) / den : 0.f;
+            wts[threadIdx.x][s] = (den > 0.f && m != -__builtin_huge_valf()) ? __expf(m - a) / den : 0.f;
         }
     }
     __syncthreads();
-    const int d = 2 * threadIdx.x;
-    const int r0 = kD - rd;
-    for (int h = 0; h < kH; ++h) {
-        float x = 0.f, y = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float* po = p.part_o + ((static_cast<size_t>(qr) * ns + s) * kH + h) * kD;
-            const float2 v = *reinterpret_cast<const float2*>(po + d);
-            x += wts[h][s] * v.x;
-            y += wts[h][s] * v.y;
-        }
-        if (d >= r0) {
-            const int jp = (d - r0) >> 1;
-            const float cs = rope_cs[jp][0], sn = rope_cs[jp][1];
-            const float nx = x * cs + y * sn;
-            y = -x * sn + y * cs;
-            x = nx;
-        }
-        *reinterpret_cast<float2*>(p.out + (static_cast<size_t>(qr) * kH + h) * kD + d) = make_float2(x, y);
+    const int hl = threadIdx.x >> 6;
+    const int h = h0 + hl;
+    const int d = 8 * (threadIdx.x & 63);
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    for (int s = 0; s < ns; ++s) {
+        const float* po = p.part_o + ((static_cast<size_t>(qr) * ns + s) * kH + h) * kD + d;
+        const float wgt = wts[hl][s];
+        x0 += wgt * *reinterpret_cast<const f32x4*>(po);
+        x1 += wgt * *reinterpret_cast<const f32x4*>(po + 4);
     }
+    float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    const int r0 = kD - rd;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const int dd = d + i;
+        if (dd >= r0) {
+            const int jp = (dd - r0) >> 1;
+            const float cs = rope_cs[jp][0], sn = rope_cs[jp][1];
+            const float x = v[i], y = v[i + 1];
+            v[i] = x * cs + y * sn;
+            v[i + 1] = -x * sn + y * cs;
+        }
+    }
+    float* o = p.out + (static_cast<size_t>(qr) * kH + h) * kD + d;
+    *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
 // ---------------------------------------------------------------- generic
@@ -490,14 +608,20 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnG p) {
             orow[i] = ctx[i];
         } else {
             const int jp = (i - r0) >> 1;
-            const double th = static_cast<double>(t) * pow(static_cast<double>(p.rope_base), -2.0 * jp / rd);
-            double s, cth;
-            sincos(th, &s, &cth);
-            const float cs = static_cast<float>(cth), sn = static_cast<float>(s);
+            float cs, sn;
+            rope_angle(t, jp, rd, p.rope_base, cs, sn);
             const float x = ctx[r0 + 2 * jp], y = ctx[r0 + 2 * jp + 1];
             orow[i] = ((i - r0) & 1) ? (-x * sn + y * cs) : (x * cs + y * sn);
         }
     }
+}
+
+int num_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
 }
 
 int choose_splits(int Q, int K, int W, int& per) {
@@ -562,12 +686,12 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         }
         dim3 grid(p.nsplit, Q);
         if (a.kv_dtype == DT_BF16)
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_BF16>, grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_mfma_kernel<DT_BF16>, grid, dim3(512), 0, st, p);
         else
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(512), 0, st, p);
         int e = static_cast<int>(hipGetLastError());
         if (e || p.nsplit == 1) return e;
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(Q), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(Q, kH / 4), dim3(256), 0, st, p);
         return static_cast<int>(hipGetLastError());
     }
     AttnG p;

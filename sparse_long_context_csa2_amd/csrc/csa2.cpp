@@ -208,7 +208,7 @@ int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K, const void* q, i
 
 struct LayerPlan {
     int rows, ncols;
-    size_t off_scores, off_pool, off_attn, total;
+    size_t off_scores, off_pool, off_topk, off_attn, total;
 };
 
 static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
@@ -236,6 +236,8 @@ static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
     if (scores_needed) off += align256(static_cast<size_t>(pl.rows) * pl.ncols * sizeof(float));
     pl.off_pool = off;
     if (d->mode == CSA2_FULL && d->pool_inout) off += align256(csa2::block_pool_ws_bytes(pl.rows, d->N, d->blk));
+    pl.off_topk = off;
+    if (scores_needed) off += align256(csa2::topk_ws_bytes(pl.rows, pl.ncols, d->K));
     pl.off_attn = off;
     off += align256(csa2::sparse_attn_ws_bytes(d->B, d->Tq, d->H, d->D, d->K, d->W));
     pl.total = off;
@@ -292,7 +294,9 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
         ta.pool = pooled ? d->pool_inout : nullptr;
         ta.P = pooled ? d->P : 0;
         ta.blk = pooled ? d->blk : 0;
-        ta.idx = d->idx_inout; ta.sort_by_key = false; ta.ws = nullptr; ta.ws_bytes = 0;
+        ta.idx = d->idx_inout; ta.sort_by_key = false;
+        ta.ws = static_cast<uint8_t*>(d->ws) + pl.off_topk;
+        ta.ws_bytes = csa2::topk_ws_bytes(pl.rows, pl.ncols, d->K);
         e = csa2::launch_topk(ta, stream);
         if (e) return hip_fail(e, "layer: topk launch");
     }

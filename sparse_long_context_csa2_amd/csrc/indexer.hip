@@ -145,55 +145,71 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     const int32_t* prow = p.pool ? p.pool + (static_cast<size_t>(b) * p.Tq + tok0) * p.P : nullptr;
     const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
 
-    for (int ti = t_first; ti < t_end; ti += t_step) {
-        const int c = ti * 16 + n;
-        int rec = -1;
-        if (c < p.ncols) {
+    // One record tile in flight ahead of the one being multiplied.
+    struct Tile {
+        int c, rec;
+        bool ld, any;
+        bf16x8 bk[4];
+        float kscale;
+    };
+    auto fetch = [&](int ti, Tile& T) {
+        T.c = ti * 16 + n;
+        T.rec = -1;
+        if (T.c < p.ncols) {
             if (prow) {
-                const int pb = prow[c / p.blk];
-                rec = pb < 0 ? -1 : pb * p.blk + c % p.blk;
+                const int pb = prow[T.c / p.blk];
+                T.rec = pb < 0 ? -1 : pb * p.blk + T.c % p.blk;
             } else {
-                rec = c;
+                T.rec = T.c;
             }
         }
-        const bool ld = rec >= 0 && rec < vis_max;
-        if (!__any(ld)) {
+        T.ld = T.rec >= 0 && T.rec < vis_max;
+        T.any = __any(T.ld);
+        T.kscale = 1.f;
+        if (T.any) {
+            load_key<KDT, !WAVES_ON_TOKENS>(kbase + static_cast<size_t>(T.ld ? T.rec : 0) * kRowBytes, g, T.ld,
+                                            T.bk);
+            if (KDT == DT_E4M3) T.kscale = T.ld ? p.ks[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+        }
+    };
+    Tile cur, nxt;
+    if (t_first < t_end) fetch(t_first, cur);
+    for (int ti = t_first; ti < t_end; ti += t_step) {
+        if (ti + t_step < t_end) fetch(ti + t_step, nxt);
+        const int c = cur.c;
+        if (!cur.any) {
 #pragma unroll
             for (int tk = 0; tk < TOKW; ++tk) {
                 if (g == 0 && tk < ntok && c < p.ncols)
+                    p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] = -__builtin_huge_valf();
+            }
+        } else {
+#pragma unroll
+            for (int tk = 0; tk < TOKW; ++tk) {
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc0 = mfma16x16x32(qa[tk][0][ks], cur.bk[ks], acc0);
+                    acc1 = mfma16x16x32(qa[tk][1][ks], cur.bk[ks], acc1);
+                }
+                float part = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float d0 = acc0[v], d1 = acc1[v];
+                    if (KDT == DT_E4M3) { d0 *= cur.kscale; d1 *= cur.kscale; }
+                    part += wv[tk][0][v] * fmaxf(d0, 0.f);
+                    part += wv[tk][1][v] * fmaxf(d1, 0.f);
+                }
+                part += shfl_xor_f(part, 16);
+                part += shfl_xor_f(part, 32);
+                if (g == 0 && tk < ntok && c < p.ncols) {
+                    const bool ok = cur.rec >= 0 && cur.rec < vis[tk];
                     p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] =
-                        -__builtin_huge_valf();
-            }
-            continue;
-        }
-        bf16x8 bk[4];
-        load_key<KDT, !WAVES_ON_TOKENS>(kbase + static_cast<size_t>(ld ? rec : 0) * kRowBytes, g, ld, bk);
-        float kscale = 1.f;
-        if (KDT == DT_E4M3) kscale = ld ? p.ks[static_cast<size_t>(b) * p.N + rec] : 0.f;
-#pragma unroll
-        for (int tk = 0; tk < TOKW; ++tk) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                acc0 = mfma16x16x32(qa[tk][0][ks], bk[ks], acc0);
-                acc1 = mfma16x16x32(qa[tk][1][ks], bk[ks], acc1);
-            }
-            float part = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float d0 = acc0[v], d1 = acc1[v];
-                if (KDT == DT_E4M3) { d0 *= kscale; d1 *= kscale; }
-                part += wv[tk][0][v] * fmaxf(d0, 0.f);
-                part += wv[tk][1][v] * fmaxf(d1, 0.f);
-            }
-            part += shfl_xor_f(part, 16);
-            part += shfl_xor_f(part, 32);
-            if (g == 0 && tk < ntok && c < p.ncols) {
-                const bool ok = rec >= 0 && rec < vis[tk];
-                p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] =
-                    ok ? part : -__builtin_huge_valf();
+                        ok ? part : -__builtin_huge_valf();
+                }
             }
         }
+        cur = nxt;
     }
 }
 

@@ -6,60 +6,59 @@
 // really occur (a ReLU sum is exactly 0 whenever every head's product is
 // negative), so the tie-break is part of the result.
 //
-// Each element gets the 64-bit composite key (score_key(score) << 32 |
-// ~record_id); with unique record ids the keys are unique and "the K
-// largest composite keys" is exactly the required set.
+// Every element has the 64-bit composite key (score_key(score) << 32 |
+// ~record_id); with unique record ids the keys are unique, and "the K
+// largest composite keys" is exactly the required set.  Selection runs in
+// two levels:
+//  1. a 4096-bin histogram of the top 12 key bits (sign, exponent, 3
+//     mantissa bits) finds the boundary bin B*: fewer than K elements lie
+//     in higher bins, which are all chosen;
+//  2. an exact 8-bit-digit radix select over the composite keys of the
+//     boundary bin's elements (usually a few dozen) picks the rest.
+// All bin searches are parallel block scans.
 //
-// One workgroup (1024 threads) per row:
-//  1. min/max of the selectable scores (block reduction);
-//  2. histogram of a monotone bucket index b = (score - min) * 2048/(max-min)
-//     -- spreading the scores over 2048 LDS bins keeps same-address atomic
-//     contention low, unlike the top bits of the float, which cluster in a
-//     few exponents;
-//  3. the boundary bucket B*: fewer than K elements lie above it;
-//  4. the boundary bucket's elements (usually a handful) go to LDS and an
-//     exact 8-bit radix select over their composite keys picks the ones
-//     still needed;
-//  5. ordered compaction writes the chosen record ids in column order (or,
-//     for the pool, a bitonic sort orders them by composite key).
-// Rows of up to 16384 columns are cached in LDS; longer rows are re-read
-// from global memory (L2) in each pass.
+// Rows of up to 16384 columns: one 256-thread workgroup per row with the
+// keys cached in LDS (rows up to 4096 use a 41 KiB variant so several rows
+// share a CU).
+// Longer rows: the row is split into 4096-column chunks over many
+// workgroups -- a histogram kernel accumulates the row histogram with
+// global atomics, then a select kernel classifies its chunk (chosen /
+// boundary candidate) into per-row lists; the last workgroup to finish a
+// row (atomic ticket after a device-scope fence) resolves the boundary bin
+// and writes the row.  Output ids are sorted by column, so results are
+// deterministic whatever the order in which workgroups ran.
 //
-// The block pool scores block b of a row by the maximum of its members
-// ("DeepSeek V4.1-Flash. Every layer, connected.", hierarchy caption) in a
-// small kernel, then runs the same selection on the block maxima.
+// The block pool scores block b by the maximum of its members ("DeepSeek
+// V4.1-Flash. Every layer, connected.", hierarchy caption) -- one wave per
+// block -- then runs the same selection on the block maxima with the
+// output ordered by (block maximum desc, block id asc).
 #include "common.h"
 #include "launch.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kNB = 2048;          // buckets of the first level
-constexpr int kLdsCols = 16384;    // rows up to this length are cached in LDS
-constexpr int kCandCap = 4096;     // boundary-bucket candidates held in LDS
-constexpr int kMaxK = 2048;        // largest K (and P) accepted
+constexpr int kNT = 256;             // threads per workgroup
+constexpr int kNW = kNT / kWave;     // waves per workgroup
+constexpr int kBins = 4096;          // first-level bins: key >> 20
+constexpr int kBinShift = 20;
+constexpr int kSmallCols = 4096;     // short rows: one workgroup, 3 per CU
+constexpr int kMedCols = 16384;      // rows up to this length: one workgroup
+constexpr int kChunk = 4096;         // columns per workgroup on long rows
+constexpr int kCandCap = 2048;       // boundary candidates held in LDS
+constexpr int kMaxK = 2048;
 
 struct TopkP {
-    int rows, ncols, K, P, blk;
+    int rows, ncols, K, P, blk, nchunks;
     const float* scores;
     const int32_t* pool;
     int32_t* idx;
     int sort_by_key;
-};
-
-struct Shared {
-    float vals[kLdsCols];
-    int hist[kNB];
-    uint32_t cand_hi[kCandCap];
-    uint32_t cand_lo[kCandCap];
-    uint32_t sel_hi[kMaxK];
-    uint32_t sel_lo[kMaxK];
-    float red_f[2][kWaves];
-    int red_i[kWaves + 1];
-    int hist8[256];
-    int misc[8];
+    // long-row workspace
+    int* ghist;      // [rows][kBins]
+    int* cnt;        // [rows][4]: chosen count, candidate count, finished chunks
+    int* sure;       // [rows][K]
+    int* cand;       // [rows][ncols]
 };
 
 __device__ __forceinline__ int rec_of(const TopkP& p, const int32_t* prow, int c) {
@@ -68,304 +67,476 @@ __device__ __forceinline__ int rec_of(const TopkP& p, const int32_t* prow, int c
     return pb < 0 ? -1 : pb * p.blk + c % p.blk;
 }
 
-// Block-wide sum; every thread gets the result.
-__device__ int block_sum(int v, int* red) {
+// Key of column c (0 = never selectable).
+__device__ __forceinline__ uint32_t key_of(const TopkP& p, const int32_t* prow, const float* srow, int c) {
+    const uint32_t k = score_key(srow[c]);
+    if (k == 0u) return 0u;
+    return rec_of(p, prow, c) >= 0 ? k : 0u;
+}
+
+__device__ __forceinline__ unsigned long long composite(uint32_t key, int rec) {
+    return (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(rec));
+}
+
+struct Scan {
+    int wave_tot[kNW];
+    int res[3];
+};
+
+// Exclusive prefix sum over the block (thread order); returns this
+// thread's exclusive prefix, and the block total in *total.
+__device__ int block_excl_scan(int v, Scan& s, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = warp_sum_i(v);
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    int t = 0;
+    int x = v;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) t += red[i];
-    return t;
-}
-
-// Finds the digit d of a 256-bin histogram such that the count of larger
-// digits is < need <= count of digits >= d.  Returns d and updates need to
-// the number still to take among digit d.  Called by all threads after a
-// barrier; thread 0 computes, everyone reads.
-__device__ int pick_digit(int* hist8, int* misc, int& need) {
-    if (threadIdx.x == 0) {
-        int above = 0, d = 255;
-        for (; d > 0; --d) {
-            if (above + hist8[d] >= need) break;
-            above += hist8[d];
-        }
-        misc[0] = d;
-        misc[1] = need - above;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
     }
     __syncthreads();
-    const int d = misc[0];
-    need = misc[1];
+    if (lane == 63) s.wave_tot[wave] = x;
     __syncthreads();
-    return d;
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+        if (i < wave) off += s.wave_tot[i];
+        tot += s.wave_tot[i];
+    }
+    *total = tot;
+    return off + x - v;
 }
 
-// Exact selection of the `need` largest composite keys among the elements
-// that `src(i, hi, lo)` yields for i in [0, count); returns the threshold
-// (thr_hi, thr_lo): chosen = hi > thr_hi || (hi == thr_hi && lo >= thr_lo).
+// Finds, scanning bins from the top, the bin where the running count first
+// reaches `need`; returns it and sets *rest to the number still needed
+// from that bin.  hist has nbins = kNT * PER entries.  If the total is
+// below `need` the result is -1 (everything is chosen).
+template <int PER>
+__device__ int find_from_top(const int* hist, int need, Scan& s, int* rest, int* bin_count = nullptr) {
+    int loc[PER];
+    int sum = 0;
+    const int top = kNT * PER - 1 - threadIdx.x * PER;  // this thread's highest bin
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        loc[j] = hist[top - j];
+        sum += loc[j];
+    }
+    int total;
+    const int excl = block_excl_scan(sum, s, &total);
+    if (threadIdx.x == 0) { s.res[0] = -1; s.res[1] = 0; s.res[2] = 0; }
+    __syncthreads();
+    if (excl < need && excl + sum >= need) {
+        int acc = excl;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (acc + loc[j] >= need) {
+                s.res[0] = top - j;
+                s.res[1] = need - acc;
+                s.res[2] = loc[j];
+                break;
+            }
+            acc += loc[j];
+        }
+    }
+    __syncthreads();
+    const int bin = s.res[0];
+    *rest = s.res[1];
+    if (bin_count) *bin_count = s.res[2];
+    __syncthreads();
+    return bin;
+}
+
+// Exact radix select of the `need` largest composite keys among the
+// elements src(i) yields, i in [0, count).  Returns the threshold:
+// chosen = composite >= thr.  src(i, key, rec) returns false to skip.
 template <class Src>
-__device__ void radix_select(Src src, int count, int need, Shared& sh, uint32_t& thr_hi,
-                             uint32_t& thr_lo) {
-    uint32_t pre_hi = 0, mask_hi = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += kThreads) sh.hist8[i] = 0;
+__device__ unsigned long long radix_select(Src src, int count, int need, int* hist8, Scan& s) {
+    unsigned long long prefix = 0, mask = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        // stop as soon as the remaining prefix class holds exactly `need`
+        hist8[threadIdx.x] = 0;
         __syncthreads();
-        for (int i = threadIdx.x; i < count; i += kThreads) {
-            uint32_t hi, lo;
-            if (src(i, hi, lo) && (hi & mask_hi) == pre_hi) atomicAdd(&sh.hist8[(hi >> shift) & 255], 1);
+        for (int i = threadIdx.x; i < count; i += kNT) {
+            uint32_t key;
+            int rec;
+            if (!src(i, key, rec)) continue;
+            const unsigned long long ck = composite(key, rec);
+            if ((ck & mask) == prefix) atomicAdd(&hist8[(ck >> shift) & 255], 1);
         }
         __syncthreads();
-        const int d = pick_digit(sh.hist8, sh.misc, need);
-        pre_hi |= static_cast<uint32_t>(d) << shift;
-        mask_hi |= 255u << shift;
-    }
-    thr_hi = pre_hi;
-    // how many carry exactly thr_hi?
-    int eq = 0;
-    for (int i = threadIdx.x; i < count; i += kThreads) {
-        uint32_t hi, lo;
-        if (src(i, hi, lo) && hi == pre_hi) ++eq;
-    }
-    eq = block_sum(eq, sh.red_i);
-    if (eq == need) {
-        thr_lo = 0;
-        return;
-    }
-    uint32_t pre_lo = 0, mask_lo = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += kThreads) sh.hist8[i] = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < count; i += kThreads) {
-            uint32_t hi, lo;
-            if (src(i, hi, lo) && hi == pre_hi && (lo & mask_lo) == pre_lo)
-                atomicAdd(&sh.hist8[(lo >> shift) & 255], 1);
+        int rest, cnt_d;
+        const int d = find_from_top<1>(hist8, need, s, &rest, &cnt_d);
+        prefix |= static_cast<unsigned long long>(d) << shift;
+        mask |= 255ull << shift;
+        if (cnt_d == rest) {
+            need = rest;
+            break;  // the whole digit class is chosen: threshold is its prefix
         }
-        __syncthreads();
-        const int d = pick_digit(sh.hist8, sh.misc, need);
-        pre_lo |= static_cast<uint32_t>(d) << shift;
-        mask_lo |= 255u << shift;
+        need = rest;
     }
-    thr_lo = pre_lo;
+    return prefix;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_row_kernel(TopkP p) {
-    __shared__ Shared sh;
+// ---------------------------------------------------------------- rows <= 4096
+
+template <int CAP>
+struct SmallShared {
+    uint32_t keys[CAP];
+    union {                       // the histogram is dead once the bin is found
+        int hist[kBins];
+        unsigned long long fin[kMaxK];
+    };
+    int cand[kCandCap];
+    int hist8[256];
+    Scan scan;
+    int misc[4];
+};
+
+template <int CAP>
+__global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
+    __shared__ SmallShared<CAP> sh;
     const int row = blockIdx.x;
     const int n = p.ncols;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = p.K;
     const float* srow = p.scores + static_cast<size_t>(row) * n;
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
-    int32_t* orow = p.idx + static_cast<size_t>(row) * p.K;
-    const bool cached = n <= kLdsCols;
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
 
-    auto value = [&](int c) -> float { return cached ? sh.vals[c] : srow[c]; };
-    auto selectable = [&](int c, float v) -> bool {
-        return score_key(v) != 0u && rec_of(p, prow, c) >= 0;
-    };
-
-    // 1. load, count, min/max
-    float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
     int nvalid = 0;
-    for (int c = threadIdx.x; c < n; c += kThreads) {
-        const float v = srow[c];
-        if (cached) sh.vals[c] = v;
-        if (selectable(c, v)) {
-            ++nvalid;
-            vmin = fminf(vmin, v);
-            vmax = fmaxf(vmax, v);
-        }
+    for (int c = threadIdx.x; c < n; c += kNT) {
+        const uint32_t k = key_of(p, prow, srow, c);
+        sh.keys[c] = k;
+        nvalid += k != 0u;
     }
-    vmin = -warp_max(-vmin);
-    vmax = warp_max(vmax);
-    if (lane == 0) { sh.red_f[0][wave] = vmin; sh.red_f[1][wave] = vmax; }
-    nvalid = block_sum(nvalid, sh.red_i);  // contains barriers
-    vmin = sh.red_f[0][0];
-    vmax = sh.red_f[1][0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) {
-        vmin = fminf(vmin, sh.red_f[0][i]);
-        vmax = fmaxf(vmax, sh.red_f[1][i]);
-    }
+    for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = 0;
+    int total;
+    block_excl_scan(nvalid, sh.scan, &total);  // barriers inside
+    nvalid = total;
 
-    const int K = p.K;
-    const int take = nvalid < K ? nvalid : K;
-    // bucket mapping; degenerate ranges put everything in bucket 0
-    const float span = vmax - vmin;
-    const float bscale = (span > 0.f && span < __builtin_huge_valf()) ? static_cast<float>(kNB) / span : 0.f;
-    auto bucket = [&](float v) -> int {
-        const int b = static_cast<int>((v - vmin) * bscale);
-        return b < 0 ? 0 : (b >= kNB ? kNB - 1 : b);
-    };
-
-    int bstar = -1;  // elements in buckets > bstar are chosen outright
-    uint32_t thr_hi = 0, thr_lo = 0;
+    int bstar = -1;
+    unsigned long long thr = 0;
     if (nvalid > K) {
-        // 2. bucket histogram
-        for (int i = threadIdx.x; i < kNB; i += kThreads) sh.hist[i] = 0;
-        __syncthreads();
-        for (int c = threadIdx.x; c < n; c += kThreads) {
-            const float v = value(c);
-            if (selectable(c, v)) atomicAdd(&sh.hist[bucket(v)], 1);
+        for (int c = threadIdx.x; c < n; c += kNT) {
+            const uint32_t k = sh.keys[c];
+            if (k) atomicAdd(&sh.hist[k >> kBinShift], 1);
         }
         __syncthreads();
-        // 3. boundary bucket (thread 0 walks down from the top)
-        if (threadIdx.x == 0) {
-            int above = 0, b = kNB - 1;
-            for (; b > 0; --b) {
-                if (above + sh.hist[b] >= K) break;
-                above += sh.hist[b];
-            }
-            sh.misc[2] = b;
-            sh.misc[3] = K - above;  // still needed from bucket b
-            sh.misc[4] = 0;          // candidate count
-        }
+        int need;
+        bstar = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need);
+        if (threadIdx.x == 0) sh.misc[0] = 0;
         __syncthreads();
-        bstar = sh.misc[2];
-        const int need = sh.misc[3];
-        // 4. candidates of the boundary bucket
-        for (int c = threadIdx.x; c < n; c += kThreads) {
-            const float v = value(c);
-            if (selectable(c, v) && bucket(v) == bstar) {
-                const int slot = atomicAdd(&sh.misc[4], 1);
-                if (slot < kCandCap) {
-                    sh.cand_hi[slot] = score_key(v);
-                    sh.cand_lo[slot] = ~static_cast<uint32_t>(rec_of(p, prow, c));
-                }
+        for (int c = threadIdx.x; c < n; c += kNT) {
+            const uint32_t k = sh.keys[c];
+            if (k && static_cast<int>(k >> kBinShift) == bstar) {
+                const int slot = atomicAdd(&sh.misc[0], 1);
+                if (slot < kCandCap) sh.cand[slot] = c;
             }
         }
         __syncthreads();
-        const int ncand = sh.misc[4];
+        const int ncand = sh.misc[0];
         if (ncand <= kCandCap) {
-            auto src = [&](int i, uint32_t& hi, uint32_t& lo) -> bool {
-                hi = sh.cand_hi[i];
-                lo = sh.cand_lo[i];
+            auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+                const int c = sh.cand[i];
+                key = sh.keys[c];
+                rec = rec_of(p, prow, c);
                 return true;
             };
-            radix_select(src, ncand, need, sh, thr_hi, thr_lo);
+            thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
         } else {
-            auto src = [&](int c, uint32_t& hi, uint32_t& lo) -> bool {
-                const float v = value(c);
-                if (!selectable(c, v) || bucket(v) != bstar) return false;
-                hi = score_key(v);
-                lo = ~static_cast<uint32_t>(rec_of(p, prow, c));
+            auto src = [&](int c, uint32_t& key, int& rec) -> bool {
+                key = sh.keys[c];
+                if (!key || static_cast<int>(key >> kBinShift) != bstar) return false;
+                rec = rec_of(p, prow, c);
                 return true;
             };
-            radix_select(src, n, need, sh, thr_hi, thr_lo);
+            thr = radix_select(src, n, need, sh.hist8, sh.scan);
         }
     }
-
     auto chosen = [&](int c) -> bool {
-        const float v = value(c);
-        if (!selectable(c, v)) return false;
-        if (bstar < 0) return true;
-        const int b = bucket(v);
+        const uint32_t k = sh.keys[c];
+        if (!k) return false;
+        const int b = static_cast<int>(k >> kBinShift);
         if (b != bstar) return b > bstar;
-        const uint32_t hi = score_key(v);
-        if (hi != thr_hi) return hi > thr_hi;
-        return ~static_cast<uint32_t>(rec_of(p, prow, c)) >= thr_lo;
+        return composite(k, rec_of(p, prow, c)) >= thr;
     };
+    const int take = nvalid < K ? nvalid : K;
 
     if (!p.sort_by_key) {
-        // 5a. ordered compaction: each wave owns a contiguous column range
-        const int span_w = ((n + kWaves - 1) / kWaves + 63) & ~63;
-        const int c0 = wave * span_w, c1 = min(n, c0 + span_w);
+        // ordered compaction: each thread owns a contiguous run of columns
+        const int per = (n + kNT - 1) / kNT;
+        const int c0 = threadIdx.x * per, c1 = min(n, c0 + per);
         int cnt = 0;
-        for (int base = c0; base < c1; base += 64) {
-            const int c = base + lane;
-            const bool s = c < c1 && chosen(c);
-            cnt += __popcll(__ballot(s));
-        }
-        __syncthreads();
-        if (lane == 0) sh.red_i[wave] = cnt;
-        __syncthreads();
-        int off = 0;
-        for (int i = 0; i < wave; ++i) off += sh.red_i[i];
-        for (int base = c0; base < c1; base += 64) {
-            const int c = base + lane;
-            const bool s = c < c1 && chosen(c);
-            const unsigned long long bal = __ballot(s);
-            const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
-            if (s && pos < K) orow[pos] = rec_of(p, prow, c);
-            off += __popcll(bal);
-        }
-        for (int i = take + threadIdx.x; i < K; i += kThreads) orow[i] = -1;
+        for (int c = c0; c < c1; ++c) cnt += chosen(c);
+        int tot;
+        int pos = block_excl_scan(cnt, sh.scan, &tot);
+        for (int c = c0; c < c1; ++c)
+            if (chosen(c) && pos < K) orow[pos++] = rec_of(p, prow, c);
+        for (int i = take + threadIdx.x; i < K; i += kNT) orow[i] = -1;
     } else {
-        // 5b. gather the chosen keys, bitonic sort descending, write ids
-        if (threadIdx.x == 0) sh.misc[5] = 0;
+        if (threadIdx.x == 0) sh.misc[1] = 0;
         __syncthreads();
-        for (int c = threadIdx.x; c < n; c += kThreads) {
+        for (int c = threadIdx.x; c < n; c += kNT) {
             if (chosen(c)) {
-                const int slot = atomicAdd(&sh.misc[5], 1);
-                if (slot < K) {
-                    sh.sel_hi[slot] = score_key(value(c));
-                    sh.sel_lo[slot] = ~static_cast<uint32_t>(rec_of(p, prow, c));
-                }
+                const int slot = atomicAdd(&sh.misc[1], 1);
+                if (slot < K) sh.fin[slot] = composite(sh.keys[c], rec_of(p, prow, c));
             }
         }
         __syncthreads();
         int m2 = 1;
         while (m2 < take) m2 <<= 1;
-        for (int i = take + threadIdx.x; i < m2; i += kThreads) { sh.sel_hi[i] = 0; sh.sel_lo[i] = 0; }
+        for (int i = take + threadIdx.x; i < m2; i += kNT) sh.fin[i] = 0ull;
         __syncthreads();
         for (int k = 2; k <= m2; k <<= 1) {
             for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = threadIdx.x; i < m2; i += kThreads) {
+                for (int i = threadIdx.x; i < m2; i += kNT) {
                     const int ij = i ^ j;
                     if (ij > i) {
-                        const unsigned long long a = (static_cast<unsigned long long>(sh.sel_hi[i]) << 32) | sh.sel_lo[i];
-                        const unsigned long long b = (static_cast<unsigned long long>(sh.sel_hi[ij]) << 32) | sh.sel_lo[ij];
+                        const unsigned long long a = sh.fin[i], b = sh.fin[ij];
                         const bool desc = (i & k) == 0;
-                        if (desc ? (a < b) : (a > b)) {
-                            sh.sel_hi[i] = static_cast<uint32_t>(b >> 32); sh.sel_lo[i] = static_cast<uint32_t>(b);
-                            sh.sel_hi[ij] = static_cast<uint32_t>(a >> 32); sh.sel_lo[ij] = static_cast<uint32_t>(a);
-                        }
+                        if (desc ? (a < b) : (a > b)) { sh.fin[i] = b; sh.fin[ij] = a; }
                     }
                 }
                 __syncthreads();
             }
         }
-        for (int i = threadIdx.x; i < K; i += kThreads)
-            orow[i] = i < take ? static_cast<int32_t>(~sh.sel_lo[i]) : -1;
+        for (int i = threadIdx.x; i < K; i += kNT)
+            orow[i] = i < take ? static_cast<int32_t>(~static_cast<uint32_t>(sh.fin[i])) : -1;
     }
 }
 
-// Block maxima: beta[row][j] = max over columns [j*blk, min((j+1)*blk, N)).
+// ---------------------------------------------------------------- long rows
+
+__global__ __launch_bounds__(kNT) void topk_zero_kernel(TopkP p) {
+    const int row = blockIdx.x;
+    int* h = p.ghist + static_cast<size_t>(row) * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kNT) h[i] = 0;
+    if (threadIdx.x < 4) p.cnt[row * 4 + threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
+    __shared__ int hist[kBins];
+    const int row = blockIdx.y;
+    const int c0 = blockIdx.x * kChunk;
+    const int c1 = min(p.ncols, c0 + kChunk);
+    const float* srow = p.scores + static_cast<size_t>(row) * p.ncols;
+    const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
+    for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;
+    __syncthreads();
+    for (int c = c0 + threadIdx.x; c < c1; c += kNT) {
+        const uint32_t k = key_of(p, prow, srow, c);
+        if (k) atomicAdd(&hist[k >> kBinShift], 1);
+    }
+    __syncthreads();
+    int* g = p.ghist + static_cast<size_t>(row) * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kNT)
+        if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+struct LongShared {
+    int hist[kBins];
+    int hist8[256];
+    unsigned long long fin[kMaxK];
+    uint32_t ckey[kCandCap];
+    int crec[kCandCap];
+    int ccol[kCandCap];
+    Scan scan;
+    int misc[4];
+};
+
+__global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
+    __shared__ LongShared sh;
+    const int row = blockIdx.y;
+    const int K = p.K;
+    const int c0 = blockIdx.x * kChunk;
+    const int c1 = min(p.ncols, c0 + kChunk);
+    const float* srow = p.scores + static_cast<size_t>(row) * p.ncols;
+    const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
+    const int* g = p.ghist + static_cast<size_t>(row) * kBins;
+    int* cnt = p.cnt + row * 4;
+    int* sure = p.sure + static_cast<size_t>(row) * K;
+    int* cand = p.cand + static_cast<size_t>(row) * p.ncols;
+
+    for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = g[i];
+    __syncthreads();
+    int need;
+    const int bstar = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need);
+    // classify this chunk
+    for (int c = c0 + threadIdx.x; c < c1; c += kNT) {
+        const uint32_t k = key_of(p, prow, srow, c);
+        if (!k) continue;
+        const int b = static_cast<int>(k >> kBinShift);
+        if (b > bstar) {
+            sure[atomicAdd(&cnt[0], 1)] = c;
+        } else if (b == bstar) {
+            cand[atomicAdd(&cnt[1], 1)] = c;
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) sh.misc[0] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
+    __syncthreads();
+    if (!sh.misc[0]) return;
+    __threadfence();
+
+    // ---- last workgroup of this row: resolve the boundary bin ----
+    const int nsure = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
+    const int ncand = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
+    unsigned long long thr = ~0ull;  // nothing from the boundary bin
+    const bool in_lds = ncand <= kCandCap;
+    if (bstar >= 0 && in_lds) {
+        for (int i = threadIdx.x; i < ncand; i += kNT) {
+            const int c = __builtin_nontemporal_load(cand + i);
+            sh.ccol[i] = c;
+            sh.ckey[i] = key_of(p, prow, srow, c);
+            sh.crec[i] = rec_of(p, prow, c);
+        }
+        __syncthreads();
+        auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+            key = sh.ckey[i];
+            rec = sh.crec[i];
+            return true;
+        };
+        thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
+    } else if (bstar >= 0) {
+        auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+            const int c = __builtin_nontemporal_load(cand + i);
+            key = key_of(p, prow, srow, c);
+            rec = rec_of(p, prow, c);
+            return true;
+        };
+        thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
+    }
+    if (threadIdx.x == 0) sh.misc[1] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nsure; i += kNT) {
+        const int c = __builtin_nontemporal_load(sure + i);
+        const int slot = atomicAdd(&sh.misc[1], 1);
+        if (slot < K) {
+            sh.fin[slot] = p.sort_by_key ? composite(key_of(p, prow, srow, c), rec_of(p, prow, c))
+                                         : static_cast<unsigned long long>(c);
+        }
+    }
+    if (bstar >= 0) {
+        for (int i = threadIdx.x; i < ncand; i += kNT) {
+            const int c = in_lds ? sh.ccol[i] : __builtin_nontemporal_load(cand + i);
+            const unsigned long long ck = in_lds ? composite(sh.ckey[i], sh.crec[i])
+                                                 : composite(key_of(p, prow, srow, c), rec_of(p, prow, c));
+            if (ck >= thr) {
+                const int slot = atomicAdd(&sh.misc[1], 1);
+                if (slot < K) sh.fin[slot] = p.sort_by_key ? ck : static_cast<unsigned long long>(c);
+            }
+        }
+    }
+    __syncthreads();
+    const int take = min(sh.misc[1], K);
+    int m2 = 1;
+    while (m2 < take) m2 <<= 1;
+    // pad so the padding sorts last: descending by key, ascending by column
+    for (int i = take + threadIdx.x; i < m2; i += kNT) sh.fin[i] = p.sort_by_key ? 0ull : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= m2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < m2; i += kNT) {
+                const int ij = i ^ j;
+                if (ij > i) {
+                    const unsigned long long a = sh.fin[i], b = sh.fin[ij];
+                    const bool first = (i & k) == 0;
+                    const bool swap = p.sort_by_key ? (first ? a < b : a > b) : (first ? a > b : a < b);
+                    if (swap) { sh.fin[i] = b; sh.fin[ij] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    for (int i = threadIdx.x; i < K; i += kNT) {
+        int32_t v = -1;
+        if (i < take) {
+            v = p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(sh.fin[i]))
+                              : rec_of(p, prow, static_cast<int>(sh.fin[i]));
+        }
+        orow[i] = v;
+    }
+}
+
+// One wave per block: beta[row][j] = max over columns [j*blk, min((j+1)*blk, N)).
 __global__ __launch_bounds__(256) void block_max_kernel(const float* scores, int N, int blk, int nb,
                                                         float* beta) {
     const int row = blockIdx.y;
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (j >= nb) return;
     const float* s = scores + static_cast<size_t>(row) * N + static_cast<size_t>(j) * blk;
     const int len = min(blk, N - j * blk);
     float m = -__builtin_huge_valf();
-    for (int i = 0; i < len; ++i) {
+    for (int i = lane; i < len; i += 64) {
         const float v = s[i];
         if (v > m) m = v;  // NaN never raises the maximum
     }
-    beta[static_cast<size_t>(row) * nb + j] = m;
+    m = warp_max(m);
+    if (lane == 0) beta[static_cast<size_t>(row) * nb + j] = m;
 }
 
-int launch_rows(const TopkP& p, hipStream_t st) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(p.rows), dim3(kThreads), 0, st, p);
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct LongLayout {
+    size_t hist, cnt, sure, cand, total;
+};
+
+LongLayout long_layout(int rows, int ncols, int K) {
+    LongLayout L;
+    size_t off = 0;
+    L.hist = off;
+    off += align256(static_cast<size_t>(rows) * kBins * sizeof(int));
+    L.cnt = off;
+    off += align256(static_cast<size_t>(rows) * 4 * sizeof(int));
+    L.sure = off;
+    off += align256(static_cast<size_t>(rows) * K * sizeof(int));
+    L.cand = off;
+    off += align256(static_cast<size_t>(rows) * ncols * sizeof(int));
+    L.total = off;
+    return L;
+}
+
+int run_topk(TopkP p, void* ws, hipStream_t st) {
+    if (p.ncols <= kSmallCols) {
+        hipLaunchKernelGGL(topk_small_kernel<kSmallCols>, dim3(p.rows), dim3(kNT), 0, st, p);
+        return static_cast<int>(hipGetLastError());
+    }
+    if (p.ncols <= kMedCols) {
+        hipLaunchKernelGGL(topk_small_kernel<kMedCols>, dim3(p.rows), dim3(kNT), 0, st, p);
+        return static_cast<int>(hipGetLastError());
+    }
+    const LongLayout L = long_layout(p.rows, p.ncols, p.K);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.ghist = reinterpret_cast<int*>(base + L.hist);
+    p.cnt = reinterpret_cast<int*>(base + L.cnt);
+    p.sure = reinterpret_cast<int*>(base + L.sure);
+    p.cand = reinterpret_cast<int*>(base + L.cand);
+    p.nchunks = (p.ncols + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(topk_zero_kernel, dim3(p.rows), dim3(kNT), 0, st, p);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
+    hipLaunchKernelGGL(topk_select_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
     return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
 
-size_t topk_ws_bytes(int, int, int) { return 0; }
+size_t topk_ws_bytes(int rows, int ncols, int K) {
+    if (ncols <= kMedCols) return 0;
+    return long_layout(rows, ncols, K).total;
+}
 
 int launch_topk(const TopkArgs& a, void* stream) {
-    TopkP p;
+    TopkP p = {};
     p.rows = a.rows; p.ncols = a.ncols; p.K = a.K; p.P = a.P; p.blk = a.blk;
     p.scores = a.scores; p.pool = a.pool; p.idx = a.idx; p.sort_by_key = a.sort_by_key ? 1 : 0;
-    return launch_rows(p, static_cast<hipStream_t>(stream));
+    return run_topk(p, a.ws, static_cast<hipStream_t>(stream));
 }
 
 size_t block_pool_ws_bytes(int rows, int N, int blk) {
     const size_t nb = (static_cast<size_t>(N) + blk - 1) / blk;
-    return ((static_cast<size_t>(rows) * nb * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+    return align256(static_cast<size_t>(rows) * nb * sizeof(float)) + topk_ws_bytes(rows, static_cast<int>(nb),
+                                                                                     kMaxK);
 }
 
 int launch_block_pool(int rows, int N, int blk, int P, const float* scores, int32_t* pool, void* ws,
@@ -373,14 +544,14 @@ int launch_block_pool(int rows, int N, int blk, int P, const float* scores, int3
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int nb = (N + blk - 1) / blk;
     float* beta = static_cast<float*>(ws);
-    hipLaunchKernelGGL(block_max_kernel, dim3((nb + 255) / 256, rows), dim3(256), 0, st, scores, N, blk,
-                       nb, beta);
+    hipLaunchKernelGGL(block_max_kernel, dim3((nb + 3) / 4, rows), dim3(256), 0, st, scores, N, blk, nb, beta);
     int e = static_cast<int>(hipGetLastError());
     if (e) return e;
-    TopkP p;
+    TopkP p = {};
     p.rows = rows; p.ncols = nb; p.K = P; p.P = 0; p.blk = 0;
     p.scores = beta; p.pool = nullptr; p.idx = pool; p.sort_by_key = 1;
-    return launch_rows(p, st);
+    void* tws = static_cast<uint8_t*>(ws) + align256(static_cast<size_t>(rows) * nb * sizeof(float));
+    return run_topk(p, tws, st);
 }
 
 }  // namespace csa2
