@@ -41,6 +41,8 @@
 //    attn_combine_kernel merges the splits.
 // attn_generic_kernel: any head count and dim (one workgroup per query and
 // head, fp32 throughout); used for small shapes such as the toy.
+#include <stdint.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -77,7 +79,9 @@ struct AttnP {
 
 constexpr int kXPitch = kD * 2 + 32;  // bytes per LDS tile row (bf16); 32-byte skew per row
 constexpr int kBuf = kTile * kXPitch;   // one tile buffer
-constexpr int kIdxPerThread = kMaxKList / 512;
+constexpr int kMaxWin = 256;
+constexpr int kMaxEnt = kMaxKList + kMaxWin;  // entries of one split (multiple of kTile)
+constexpr float kLog2e = 1.4426950408889634f;
 
 // cos/sin of the rotary angle t * base^(-2j/r): the angle is formed and
 // reduced modulo 2*pi in double precision (t reaches 2^20), the reduced
@@ -91,45 +95,54 @@ __device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base,
     sincosf(static_cast<float>(r), &s, &c);
 }
 
-// Barrier for LDS hand-offs: this wave's LDS writes are complete, then all
-// waves meet.  Unlike __syncthreads() it does not wait for outstanding
+// Barrier for LDS hand-offs: this wave's LDS accesses are complete, then
+// all waves meet.  Unlike __syncthreads() it does not wait for outstanding
 // global loads (the tile prefetches keep flowing across it); the asm is
 // also a compiler memory barrier.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// This wave's tile copies except the newest n (0..4) have completed.
-__device__ __forceinline__ void wait_tile_copies(int n) {
-    switch (n) {  // wave-uniform
-        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
+// Every tile copy of this wave except the newest four has completed.
+__device__ __forceinline__ void wait_copies_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+__device__ __forceinline__ void wait_copies_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copies the 1 KiB row at rp (a wave-uniform address, held in SGPRs)
+// straight into LDS at byte address lds: lane l moves the 16 bytes at
+// rp + voff with voff = 16 l (gfx950 global_load_lds_dwordx4, LDS address
+// in M0).  Issued as asm so that the compiler does not serialise later LDS
+// reads of the other tile buffers behind it: completion is awaited
+// explicitly with the waits above.
+__device__ __forceinline__ void row_copy16(const uint8_t* rp, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(rp)
+                 : "memory", "m0");
 }
 
-// Copies 16 bytes per lane from global memory straight into LDS at
-// lds_row + 16 * lane (gfx950 global_load_lds_dwordx4; M0 holds the LDS
-// byte address).  Issued as asm so that the compiler does not serialise
-// later LDS reads of the other tile buffers behind it: completion is
-// awaited explicitly with wait_tile_copies().
-__device__ __forceinline__ void row_copy16(const void* gptr, const void* lds_row) {
-    const uint32_t lds = static_cast<uint32_t>(
-        reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)(lds_row)));
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr)
-                 : "memory", "m0");
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
+}
+
+// 64-bit address held by the first lane, as a wave-uniform (SGPR) value.
+// readfirstlane returns a signed int: both halves go through uint32_t so
+// that the low half is not sign-extended into the high one.
+__device__ __forceinline__ const uint8_t* uniform_ptr(uint32_t lo, uint32_t hi) {
+    const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lo)));
+    const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(hi)));
+    return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(h) << 32) | l);
 }
 
 constexpr int kNBuf = 3;  // tiles in flight: computing t, landing t+1 and t+2
 
+template <int KVDT>
 struct __align__(16) AttnShared {
+    static constexpr int kScaled = (KVDT == DT_E4M3) ? kMaxEnt : 4;
     uint8_t xb[kNBuf][kBuf];              // tile buffers (row-major: entry, channel)
-    float sx[8][64][8];                   // partial logits exchanged between channel halves
-    int32_t list[kMaxKList];              // compacted valid record ids
+    union {
+        int32_t list[kMaxKList];          // compacted valid record ids (set-up only)
+        float sx[8][64][8];               // partial logits exchanged between channel halves
+    } u;
+    uint64_t eptr[kMaxEnt];               // row address of each entry of this split
+    float ezf[kScaled];                   // e4m3: logit factor sm * log2(e) * row scale
+    float epf[kScaled];                   // e4m3: row scale (weights the probability)
     float rope_cs[kMaxRope][2];
-    float esc[kNBuf][kTile];              // per-entry scale (0 for empty entries)
-    int evalid[kNBuf][kTile];
     int wave_cnt[8];
 };
 
@@ -150,20 +163,24 @@ __device__ __forceinline__ int query_of_block(int L, int Q) {
 }
 
 // 8 waves: wave w owns heads 16*(w&3) .. +15 and channels 256*(w>>2) ..
-// +255.  Tile rows are copied global -> LDS in row-major order (entry,
-// channel), two tiles ahead of the one being multiplied.  S^T = X Q^T
-// reads 16-byte row chunks; O^T += X^T P^T reads its operand with the
-// gfx950 transposing LDS load: within each 16-lane group, lane j receives
-// element j%4 of the 64-bit chunk addressed by lane 4k+j/4 (k = 0..3), so
-// pointing lane s of group g at X[4g + s/4][d0 + 4(s%4) ..] hands lane j
-// the four entries 4g..4g+3 of channel d0 + j -- the MFMA A operand.
+// +255.  Set-up builds, for the entries [j0, j1) of this split, a table of
+// row addresses (entries past j1, up to the next multiple of the tile,
+// repeat the last row so that every tile is a full one; their
+// probabilities are zeroed).  Tile rows are then copied global -> LDS in
+// row-major order (entry, channel), two tiles ahead of the one being
+// multiplied; each wave copies four rows per tile from wave-uniform
+// addresses.  S^T = X Q^T reads 16-byte row chunks; O^T += X^T P^T reads
+// its operand with the gfx950 transposing LDS load: within each 16-lane
+// group, lane j receives element j%4 of the 64-bit chunk addressed by lane
+// 4k+j/4 (k = 0..3), so pointing lane s of group g at X[4g + s/4][d0 +
+// 4(s%4) ..] hands lane j the four entries 4g..4g+3 of channel d0 + j --
+// the MFMA A operand.  Logits are kept in log2 units (exp2 on the VALU).
 template <int KVDT>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
-    __shared__ AttnShared sh;
-    typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
+    __shared__ AttnShared<KVDT> sh;
     constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15;
     const int g = lane >> 4;
     const int hg = wave & 3;   // head group
@@ -175,6 +192,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
     const int b = qr / p.Tq;
     const int64_t t = p.q_pos[qr];
     const int rd = p.rope_dims;
+    const float cz = p.sm * kLog2e;
 
     // ---- compact the valid selected records (in order) ----
     const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
@@ -189,15 +207,41 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
         __syncthreads();
         int off = nsel;
         for (int i = 0; i < wave; ++i) off += sh.wave_cnt[i];
-        if (ok) sh.list[off + __popcll(bal & ((1ull << lane) - 1ull))] = rec;
+        if (ok) sh.u.list[off + __popcll(bal & ((1ull << lane) - 1ull))] = rec;
         for (int i = 0; i < 8; ++i) nsel += sh.wave_cnt[i];
         __syncthreads();
     }
+    nsel = __builtin_amdgcn_readfirstlane(nsel);
     const int nwin = t < 0 ? 0 : static_cast<int>(t + 1 < p.W ? t + 1 : p.W);
     const int slot0 = static_cast<int>((t - nwin + 1) % p.S);  // ring slot of the first window row
     const int E = nsel + nwin;
     const int j0 = split * p.per_split;
     const int j1 = min(E, j0 + p.per_split);
+    const int nvalid = j1 - j0;  // entries of this split
+    const int ntile = nvalid > 0 ? (nvalid + kTile - 1) / kTile : 0;
+
+    // ---- entry table ----
+    for (int e = threadIdx.x; e < ntile * kTile; e += 512) {
+        const int ge = min(j0 + e, j1 - 1);
+        const uint8_t* rp;
+        float sc = 1.f;
+        if (ge < nsel) {
+            const size_t r = static_cast<size_t>(b) * p.N + sh.u.list[ge];
+            if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
+            rp = p.kv + r * kRowBytes;
+        } else {
+            int slot = slot0 + (ge - nsel);  // < 2S since the window has at most S rows
+            if (slot >= p.S) slot -= p.S;
+            const size_t r = static_cast<size_t>(b) * p.S + slot;
+            if constexpr (KVDT == DT_E4M3) sc = p.swa_scale[r];
+            rp = p.swa + r * kRowBytes;
+        }
+        sh.eptr[e] = reinterpret_cast<uint64_t>(rp);
+        if constexpr (KVDT == DT_E4M3) {
+            sh.ezf[e] = cz * sc;
+            sh.epf[e] = sc;
+        }
+    }
     for (int i = threadIdx.x; i < rd / 2; i += 512) rope_angle(t, i, rd, p.rope_base, sh.rope_cs[i][0], sh.rope_cs[i][1]);
 
     // ---- query fragments: head h, this wave's 8 k-steps of 32 channels ----
@@ -209,48 +253,24 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
             qf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (g + 4 * (8 * dh + i))));
     }
 
-    auto row_of = [&](int e, bool& ok, float& scale) -> const uint8_t* {
-        ok = e < j1;
-        scale = 0.f;
-        if (!ok) return nullptr;
-        if (e < nsel) {
-            const size_t r = static_cast<size_t>(b) * p.N + sh.list[e];
-            scale = KVDT == DT_E4M3 ? p.kv_scale[r] : 1.f;
-            return p.kv + r * kRowBytes;
-        }
-        int slot = slot0 + (e - nsel);  // < 2S since the window has at most S rows
-        if (slot >= p.S) slot -= p.S;
-        const size_t r = static_cast<size_t>(b) * p.S + slot;
-        scale = KVDT == DT_E4M3 ? p.swa_scale[r] : 1.f;
-        return p.swa + r * kRowBytes;
-    };
-
-    // Tile staging: wave w fills rows 4w .. 4w+3.  bf16 rows go straight
-    // from global memory into LDS (one 1 KiB row per wave instruction); rows
-    // past the end are zero-filled.  e4m3 rows are converted to bf16 in
-    // registers on the way (staged one tile ahead).
+    // Tile staging: wave w fills rows 4w .. 4w+3 of the tile.  bf16 rows go
+    // straight from global memory into LDS; e4m3 rows are converted to bf16
+    // in registers on the way (staged one tile ahead).
+    const uint32_t voff = 16u * lane;
+    typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
     Raw stg[4];
-    auto issue = [&](int tb, int k) {
-        uint8_t* xb = sh.xb[k];
+    auto issue = [&](int it, int k) {
+        const u32x4* ep = reinterpret_cast<const u32x4*>(&sh.eptr[it * kTile + 4 * wave]);
+        const u32x4 pa = ep[0], pb = ep[1];
+        const uint8_t* rp[4] = {uniform_ptr(pa[0], pa[1]), uniform_ptr(pa[2], pa[3]), uniform_ptr(pb[0], pb[1]),
+                                uniform_ptr(pb[2], pb[3])};
+        if constexpr (KVDT == DT_BF16) {
+            const uint32_t dst = lds_addr(sh.xb[k]) + 4 * wave * kXPitch;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * wave + i;
-            bool ok;
-            float sc;
-            const uint8_t* rp = row_of(tb + r, ok, sc);
-            if constexpr (KVDT == DT_BF16) {
-                if (ok) row_copy16(rp + 16 * lane, xb + r * kXPitch);
-                else *reinterpret_cast<u32x4*>(xb + r * kXPitch + 16 * lane) = u32x4{0, 0, 0, 0};
-            } else {
-                stg[i] = ok ? *reinterpret_cast<const Raw*>(rp + 8 * lane) : Raw{};
-            }
-        }
-        if (threadIdx.x < kTile) {
-            bool ok;
-            float sc;
-            row_of(tb + threadIdx.x, ok, sc);
-            sh.esc[k][threadIdx.x] = sc;
-            sh.evalid[k][threadIdx.x] = ok ? 1 : 0;
+            for (int i = 0; i < 4; ++i) row_copy16(rp[i], voff, dst + i * kXPitch);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) stg[i] = *reinterpret_cast<const Raw*>(rp[i] + 8 * lane);
         }
     };
     auto land = [&](int k) {  // e4m3 only: staged registers -> LDS
@@ -261,39 +281,35 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
                 *reinterpret_cast<u32x4*>(xb + (4 * wave + i) * kXPitch + 16 * lane) = e4m3x8_to_bf16x8(stg[i]);
         }
     };
-    // copies this wave issues for the tile at tb (rows at or past j1 are
-    // zero-filled instead)
-    auto copies = [&](int tb) { return min(4, max(0, j1 - tb - 4 * wave)); };
 
-    float m_run = -__builtin_huge_valf();
-    float l_run = 0.f;
+    float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
+    float l_run = 0.f;                     // this lane's share of the running sum
     f32x4 acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // list, rope table visible
-    const int ntile = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+    __syncthreads();  // entry table, rope table visible; list no longer needed
     if constexpr (KVDT == DT_BF16) {
         // settle the query-fragment loads now (a wait the compiler tracks), so
         // that it places no vmcnt waits inside the loop, where they would
         // also wait for the tile copies in flight
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-        if (ntile > 0) issue(j0, 0);
-        if (ntile > 1) issue(j0 + kTile, 1);
+        if (ntile > 0) issue(0, 0);
+        if (ntile > 1) issue(1, 1);
     } else {
-        if (ntile > 0) issue(j0, 0);
+        if (ntile > 0) issue(0, 0);
     }
 
+    int cb = 0;  // buffer of tile it
     for (int it = 0; it < ntile; ++it) {
-        const int tb = j0 + it * kTile;
-        const int cb = it % kNBuf;
         if constexpr (KVDT == DT_BF16) {
-            wait_tile_copies(it + 1 < ntile ? copies(tb + kTile) : 0);
+            if (it + 1 < ntile) wait_copies_but_4();
+            else wait_copies_all();
             lds_sync();  // every wave's rows of tile `it` landed; tile it-1 consumed
-            if (it + 2 < ntile) issue(tb + 2 * kTile, (it + 2) % kNBuf);
+            if (it + 2 < ntile) issue(it + 2, cb == 0 ? 2 : cb - 1);
         } else {
             land(cb);
-            if (it + 1 < ntile) issue(tb + kTile, (it + 1) % kNBuf);
+            if (it + 1 < ntile) issue(it + 1, cb == 2 ? 0 : cb + 1);
             lds_sync();
         }
         const uint8_t* xb = sh.xb[cb];
@@ -315,56 +331,70 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
         }
         s0 += s2;
         s1 += s3;
-        *reinterpret_cast<f32x4*>(&sh.sx[wave][lane][0]) = s0;
-        *reinterpret_cast<f32x4*>(&sh.sx[wave][lane][4]) = s1;
+        *reinterpret_cast<f32x4*>(&sh.u.sx[wave][lane][0]) = s0;
+        *reinterpret_cast<f32x4*>(&sh.u.sx[wave][lane][4]) = s1;
         lds_sync();
         // full logits: mine + the other channel half's (same sum in both waves)
-        s0 += *reinterpret_cast<const f32x4*>(&sh.sx[wave ^ 4][lane][0]);
-        s1 += *reinterpret_cast<const f32x4*>(&sh.sx[wave ^ 4][lane][4]);
+        s0 += *reinterpret_cast<const f32x4*>(&sh.u.sx[wave ^ 4][lane][0]);
+        s1 += *reinterpret_cast<const f32x4*>(&sh.u.sx[wave ^ 4][lane][4]);
 
         // ---- online softmax over this tile: entries 16*mt + 4g + v, head h ----
-        const float* esc = sh.esc[cb];
-        const int* ev = sh.evalid[cb];
+        // z in log2 units.  Padding entries repeat a real row, so they may
+        // take part in the max; only their probabilities are dropped.
         float z[8];
-        float tmax = -__builtin_huge_valf();
+        if constexpr (KVDT == DT_E4M3) {
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 4 * g]);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int e0 = 4 * g + v, e1 = 16 + 4 * g + v;
-            z[v] = ev[e0] ? s0[v] * p.sm * esc[e0] : -__builtin_huge_valf();
-            z[4 + v] = ev[e1] ? s1[v] * p.sm * esc[e1] : -__builtin_huge_valf();
+            for (int v = 0; v < 4; ++v) {
+                z[v] = s0[v] * f0[v];
+                z[4 + v] = s1[v] * f1[v];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                z[v] = s0[v] * cz;
+                z[4 + v] = s1[v] * cz;
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+        tmax = max4_rows(tmax);
         // The reference max only moves when this tile exceeds it by more than
-        // kLazy (so probabilities stay below e^kLazy); otherwise O needs no
+        // kLazy (so probabilities stay below 2^kLazy); otherwise O needs no
         // rescale.  The result is the same: every term is relative to m_run.
+        // On the first tile m_run is -inf and alpha is 0 (O and l are 0).
         const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
-        const float alpha = (m_run == -__builtin_huge_valf() || m_new == m_run) ? 1.f : __expf(m_run - m_new);
-        float psum = 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+        const int lim = nvalid - it * kTile;  // entries of this tile that are real
+        if (lim < kTile) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (4 * g + v >= lim) pr[v] = 0.f;
+                if (16 + 4 * g + v >= lim) pr[4 + v] = 0.f;
+            }
+        }
+        l_run = l_run * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+        m_run = m_new;
+        if constexpr (KVDT == DT_E4M3) {  // value rows carry their scale
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                pr[v] *= f0[v];
+                pr[4 + v] *= f1[v];
+            }
+        }
+        // P = hi + lo, both bf16: hi is P rounded, lo the rounding error
         uint32_t phi[4], plo[4];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            float pp[2], pw[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int ii = i + u;
-                const int e = (ii < 4) ? 4 * g + ii : 16 + 4 * g + (ii - 4);
-                pp[u] = (z[ii] == -__builtin_huge_valf()) ? 0.f : __expf(z[ii] - m_new);
-                pw[u] = pp[u] * esc[e];
-                psum += pp[u];
-            }
-            const uint32_t hi = pack_bf16x2(pw[0], pw[1]);
-            const float q0 = pw[0] - __uint_as_float(hi << 16);
-            const float q1 = pw[1] - __uint_as_float(hi & 0xFFFF0000u);
-            phi[i >> 1] = hi;
-            plo[i >> 1] = pack_bf16x2(q0, q1);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t hi = cvt_bf16x2(pr[2 * i], pr[2 * i + 1]);
+            phi[i] = hi;
+            plo[i] = cvt_bf16x2(pr[2 * i] - __uint_as_float(hi << 16), pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
         }
-        psum += shfl_xor_f(psum, 16);
-        psum += shfl_xor_f(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
         const bf16x8 bhi = as_bf16x8(u32x4{phi[0], phi[1], phi[2], phi[3]});
         const bf16x8 blo = as_bf16x8(u32x4{plo[0], plo[1], plo[2], plo[3]});
 
@@ -396,17 +426,18 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(a[u], blo, acc[uh + u]);
         }
-
+        cb = (cb == 2) ? 0 : cb + 1;
     }
+    l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
 
     // ---- finish ----
     if (p.nsplit == 1) {
-        const float skv = p.sink[h];
-        const float a = fmaxf(m_run, skv);
+        const float sk = p.sink[h] * kLog2e;
+        const float a = fmaxf(m_run, sk);
         float f = 0.f;
         if (a != -__builtin_huge_valf()) {
-            const float em = (m_run == -__builtin_huge_valf()) ? 0.f : __expf(m_run - a);
-            const float es = (skv == -__builtin_huge_valf()) ? 0.f : __expf(skv - a);
+            const float em = __builtin_amdgcn_exp2f(m_run - a);
+            const float es = __builtin_amdgcn_exp2f(sk - a);
             const float den = l_run * em + es;
             f = den > 0.f ? em / den : 0.f;
         }
@@ -437,7 +468,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) *reinterpret_cast<f32x4*>(po + 256 * dh + 16 * u + 4 * g) = acc[u];
         if (g == 0 && dh == 0) {
-            p.part_ml[2 * slot] = m_run;
+            p.part_ml[2 * slot] = m_run;  // log2 units
             p.part_ml[2 * slot + 1] = l_run;
         }
     }
@@ -458,20 +489,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
     if (threadIdx.x < 4) {
         const int h = h0 + threadIdx.x;
         const float* ml = p.part_ml + (static_cast<size_t>(qr) * ns * kH + h) * 2;
-        const float sk = p.sink[h];
+        const float sk = p.sink[h] * kLog2e;  // partial maxima are in log2 units
         float a = sk;
         for (int s = 0; s < ns; ++s) a = fmaxf(a, ml[static_cast<size_t>(s) * kH * 2]);
         float den = 0.f;
         if (a != -__builtin_huge_valf()) {
-            den = (sk == -__builtin_huge_valf()) ? 0.f : __expf(sk - a);
+            den = __builtin_amdgcn_exp2f(sk - a);
             for (int s = 0; s < ns; ++s) {
                 const float m = ml[static_cast<size_t>(s) * kH * 2];
-                if (m != -__builtin_huge_valf()) den += ml[static_cast<size_t>(s) * kH * 2 + 1] * __expf(m - a);
+                if (m != -__builtin_huge_valf()) den += ml[static_cast<size_t>(s) * kH * 2 + 1] * __builtin_amdgcn_exp2f(m - a);
             }
         }
         for (int s = 0; s < ns; ++s) {
             const float m = ml[static_cast<size_t>(s) * kH * 2];
-            wts[threadIdx.x][s] = (den > 0.f && m != -__builtin_huge_valf()) ? __expf(m - a) / den : 0.f;
+            wts[threadIdx.x][s] = (den > 0.f && m != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m - a) / den : 0.f;
         }
     }
     __syncthreads();
@@ -640,7 +671,7 @@ int choose_splits(int Q, int K, int W, int& per) {
 }  // namespace
 
 bool sparse_attn_mfma_ok(const AttnArgs& a) {
-    return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && a.K <= kMaxKList &&
+    return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && a.K <= kMaxKList && a.W <= kMaxWin &&
            (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_E4M3) && a.swa_dtype == a.kv_dtype &&
            a.rope_dims <= kD;
 }

@@ -35,6 +35,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Same rounding (to nearest even) with gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
 // ---------------------------------------------------------------- e4m3
 // OCP e4m3fn -> bf16 is exact (3 mantissa bits, exponents 2^-9 .. 2^8 all
 // fit bf16).  gfx950 converts two codes per instruction; the scale operand
@@ -99,6 +105,40 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);
+}
+
+// x of this lane and x of lane l ^ 16 (resp. l ^ 32), in either order.
+// gfx950's v_permlane16_swap exchanges the odd 16-lane rows of its first
+// operand with the even rows of its second (v_permlane32_swap: the upper
+// half with the lower half); with x in both operands each lane ends up
+// holding both values of its pair, in one VALU op and no LDS traffic.
+__device__ __forceinline__ void pair_xor16(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float max4_rows(float x) {
+    float a, b;
+    pair_xor16(x, a, b);
+    x = fmaxf(a, b);
+    pair_xor32(x, a, b);
+    return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float sum4_rows(float x) {
+    float a, b;
+    pair_xor16(x, a, b);
+    x = a + b;
+    pair_xor32(x, a, b);
+    return a + b;
 }
 
 __device__ __forceinline__ float warp_max(float v) {
