@@ -57,7 +57,7 @@ constexpr int kTile = 32;
 constexpr int kMaxKList = 2048;
 constexpr int kMaxRope = kD / 2;
 constexpr int kMaxSplits = 32;
-constexpr float kLazy = 8.f;  // nats
+constexpr float kJump = 64.f;  // log2 units: largest probability is 2^kJump
 
 struct AttnP {
     int B, Tq, N, K, S, W, nsplit, per_split;
@@ -86,13 +86,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 // cos/sin of the rotary angle t * base^(-2j/r): the angle is formed and
 // reduced modulo 2*pi in double precision (t reaches 2^20), the reduced
 // angle goes through single-precision sincos.
-__device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base, float& c, float& s) {
-    const double inv = pow(static_cast<double>(base), -2.0 * j / rd);
+__device__ __forceinline__ double rope_inv_freq(int j, int rd, float base) {
+    return pow(static_cast<double>(base), -2.0 * j / rd);
+}
+
+__device__ __forceinline__ void rope_cos_sin(int64_t t, double inv, float& c, float& s) {
     const double th = static_cast<double>(t) * inv;
     const double k = rint(th * 0.15915494309189533577);       // 1 / (2 pi)
     double r = fma(-k, 6.283185307179586232, th);              // 2 pi, high part
     r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi, low part
     sincosf(static_cast<float>(r), &s, &c);
+}
+
+__device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base, float& c, float& s) {
+    rope_cos_sin(t, rope_inv_freq(j, rd, base), c, s);
 }
 
 // Barrier for LDS hand-offs: this wave's LDS accesses are complete, then
@@ -101,8 +108,9 @@ __device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base,
 // also a compiler memory barrier.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Every tile copy of this wave except the newest four has completed.
-__device__ __forceinline__ void wait_copies_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+// Every tile copy of this wave except the newest eight (one tile's) has
+// completed.
+__device__ __forceinline__ void wait_copies_but_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 __device__ __forceinline__ void wait_copies_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Copies the 1 KiB row at rp (a wave-uniform address, held in SGPRs)
@@ -129,348 +137,449 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(uint32_t lo, uint32_t hi) 
     return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(h) << 32) | l);
 }
 
-constexpr int kNBuf = 3;  // tiles in flight: computing t, landing t+1 and t+2
+constexpr int kNBuf = 3;    // tiles in flight: computing t, landing t+1 and t+2
+constexpr int kWaves = 4;   // one wave per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kIdsPerThread = kMaxKList / kThreads;
+constexpr int kRowsPerWave = kTile / kWaves;  // tile rows each wave copies
 
 template <int KVDT>
 struct __align__(16) AttnShared {
     static constexpr int kScaled = (KVDT == DT_E4M3) ? kMaxEnt : 4;
-    uint8_t xb[kNBuf][kBuf];              // tile buffers (row-major: entry, channel)
-    union {
-        int32_t list[kMaxKList];          // compacted valid record ids (set-up only)
-        float sx[8][64][8];               // partial logits exchanged between channel halves
-    } u;
-    uint64_t eptr[kMaxEnt];               // row address of each entry of this split
-    float ezf[kScaled];                   // e4m3: logit factor sm * log2(e) * row scale
-    float epf[kScaled];                   // e4m3: row scale (weights the probability)
+    uint8_t xb[kNBuf][kBuf];                // tile buffers (row-major: entry, channel)
+    uint64_t eptr[kMaxEnt];                 // row address of each entry of the work item
+    float ezf[kScaled];                     // e4m3: logit factor sm * log2(e) * row scale
+    float epf[kScaled];                     // e4m3: row scale (weights the probability)
+    int32_t list[kMaxKList];                // compacted valid record ids
     float rope_cs[kMaxRope][2];
-    int wave_cnt[8];
+    double rope_inv[kMaxRope];              // base^(-2j/r), once per workgroup
+    int cnt[kIdsPerThread][kWaves];         // valid ids per (chunk, wave)
 };
 
-// Query row handled by workgroup L of a launch over Q rows.  Workgroups
-// are dispatched to the 8 XCDs round-robin (L % 8); giving each XCD whole
-// chunks of 64 consecutive query positions keeps the rows those queries
-// gather (shared records and overlapping windows) inside that XCD's L2.
-// Later positions (more entries) go first.
-__device__ __forceinline__ int query_of_block(int L, int Q) {
-    constexpr int kChunkQ = 64, kXcd = 8;
-    const int full = (Q / (kChunkQ * kXcd)) * (kChunkQ * kXcd);
-    int qr = L;
-    if (L < full) {
-        const int x = L % kXcd, m = L / kXcd;
-        qr = ((m / kChunkQ) * kXcd + x) * kChunkQ + (m % kChunkQ);
-    }
-    return Q - 1 - qr;
+// The next work item's slice of the index row, fetched into registers
+// while the current item runs.
+struct ItemFetch {
+    int ids[kIdsPerThread];
+};
+
+// Work items are (query, split) pairs; with one split, item i is query
+// Q-1-i so that later positions (more entries) come first.  Persistent
+// workgroup g takes the items of round r at r*G + g for even r and
+// r*G + G-1-g for odd r, which evens out the per-workgroup totals.
+__device__ __forceinline__ int item_of(int round, int g, int G) {
+    return round * G + ((round & 1) ? (G - 1 - g) : g);
 }
 
-// 8 waves: wave w owns heads 16*(w&3) .. +15 and channels 256*(w>>2) ..
-// +255.  Set-up builds, for the entries [j0, j1) of this split, a table of
-// row addresses (entries past j1, up to the next multiple of the tile,
-// repeat the last row so that every tile is a full one; their
-// probabilities are zeroed).  Tile rows are then copied global -> LDS in
-// row-major order (entry, channel), two tiles ahead of the one being
-// multiplied; each wave copies four rows per tile from wave-uniform
-// addresses.  S^T = X Q^T reads 16-byte row chunks; O^T += X^T P^T reads
-// its operand with the gfx950 transposing LDS load: within each 16-lane
-// group, lane j receives element j%4 of the 64-bit chunk addressed by lane
-// 4k+j/4 (k = 0..3), so pointing lane s of group g at X[4g + s/4][d0 +
-// 4(s%4) ..] hands lane j the four entries 4g..4g+3 of channel d0 + j --
-// the MFMA A operand.  Logits are kept in log2 units (exp2 on the VALU).
+// Persistent: gridDim.x workgroups of 4 waves (one per SIMD) walk the work
+// items.  Wave w owns heads 16w .. 16w+15 over all 512 channels, so each
+// wave has the complete logits of its heads and no partial sums cross
+// waves.  Per work item:
+//  * the valid selected records are compacted in order and, for the
+//    item's entries [j0, j1), a table of row addresses is built (entries
+//    past j1 up to the next multiple of the tile repeat the last row, so
+//    every tile is a full one; their probabilities are zeroed);
+//  * tile rows are copied global -> LDS in row-major order (entry,
+//    channel), two tiles ahead of the one being multiplied; each wave
+//    copies eight rows per tile from wave-uniform addresses;
+//  * S^T = X Q^T reads 16-byte row chunks (entries on M, heads on N);
+//    O^T += X^T P^T reads its operand with the gfx950 transposing LDS load:
+//    within each 16-lane group, lane j receives element j%4 of the 64-bit
+//    chunk addressed by lane 4k+j/4 (k = 0..3), so pointing lane s of group
+//    g at X[4g + s/4][d0 + 4(s%4) ..] hands lane j the four entries
+//    4g..4g+3 of channel d0 + j -- the MFMA A operand;
+//  * logits are kept in log2 units (exp2 on the VALU).
+// While an item runs, the next item's slice of the index row is loaded
+// into registers, so compaction starts without a global round trip.
 template <int KVDT>
-__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnP p) {
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     __shared__ AttnShared<KVDT> sh;
     constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // An operand in an accumulation register tells the compiler that this
+    // kernel uses them, so it selects the MFMA form whose accumulator lives
+    // in AGPRs: the 128 accumulators then stay there across the tile loop
+    // instead of being copied to and from VGPRs on every iteration.
+    asm volatile("" ::"a"(0.f));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g = lane >> 4;
-    const int hg = wave & 3;   // head group
-    const int dh = wave >> 2;  // channel half
-    const int h = 16 * hg + l16;
-    const int split = blockIdx.x;
+    const int h = 16 * wave + l16;
     const int Q = p.B * p.Tq;
-    const int qr = p.nsplit == 1 ? query_of_block(blockIdx.y, Q) : static_cast<int>(blockIdx.y);
-    const int b = qr / p.Tq;
-    const int64_t t = p.q_pos[qr];
-    const int rd = p.rope_dims;
+    const int n_items = Q * p.nsplit;
+    const int G = gridDim.x;
     const float cz = p.sm * kLog2e;
-
-    // ---- compact the valid selected records (in order) ----
-    const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
-    int nsel = 0;
-    for (int base = 0; base < p.K; base += 512) {
-        const int j = base + threadIdx.x;
-        int rec = -1;
-        if (j < p.K) rec = irow[j];
-        const bool ok = rec >= 0 && rec < p.N;
-        const unsigned long long bal = __ballot(ok);
-        if (lane == 0) sh.wave_cnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = nsel;
-        for (int i = 0; i < wave; ++i) off += sh.wave_cnt[i];
-        if (ok) sh.u.list[off + __popcll(bal & ((1ull << lane) - 1ull))] = rec;
-        for (int i = 0; i < 8; ++i) nsel += sh.wave_cnt[i];
-        __syncthreads();
-    }
-    nsel = __builtin_amdgcn_readfirstlane(nsel);
-    const int nwin = t < 0 ? 0 : static_cast<int>(t + 1 < p.W ? t + 1 : p.W);
-    const int slot0 = static_cast<int>((t - nwin + 1) % p.S);  // ring slot of the first window row
-    const int E = nsel + nwin;
-    const int j0 = split * p.per_split;
-    const int j1 = min(E, j0 + p.per_split);
-    const int nvalid = j1 - j0;  // entries of this split
-    const int ntile = nvalid > 0 ? (nvalid + kTile - 1) / kTile : 0;
-
-    // ---- entry table ----
-    for (int e = threadIdx.x; e < ntile * kTile; e += 512) {
-        const int ge = min(j0 + e, j1 - 1);
-        const uint8_t* rp;
-        float sc = 1.f;
-        if (ge < nsel) {
-            const size_t r = static_cast<size_t>(b) * p.N + sh.u.list[ge];
-            if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
-            rp = p.kv + r * kRowBytes;
-        } else {
-            int slot = slot0 + (ge - nsel);  // < 2S since the window has at most S rows
-            if (slot >= p.S) slot -= p.S;
-            const size_t r = static_cast<size_t>(b) * p.S + slot;
-            if constexpr (KVDT == DT_E4M3) sc = p.swa_scale[r];
-            rp = p.swa + r * kRowBytes;
-        }
-        sh.eptr[e] = reinterpret_cast<uint64_t>(rp);
-        if constexpr (KVDT == DT_E4M3) {
-            sh.ezf[e] = cz * sc;
-            sh.epf[e] = sc;
-        }
-    }
-    for (int i = threadIdx.x; i < rd / 2; i += 512) rope_angle(t, i, rd, p.rope_base, sh.rope_cs[i][0], sh.rope_cs[i][1]);
-
-    // ---- query fragments: head h, this wave's 8 k-steps of 32 channels ----
-    bf16x8 qf[8];
-    {
-        const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            qf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (g + 4 * (8 * dh + i))));
-    }
-
-    // Tile staging: wave w fills rows 4w .. 4w+3 of the tile.  bf16 rows go
-    // straight from global memory into LDS; e4m3 rows are converted to bf16
-    // in registers on the way (staged one tile ahead).
+    const int nids = (p.K + kThreads - 1) / kThreads;  // index chunks per thread
     const uint32_t voff = 16u * lane;
-    typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
-    Raw stg[4];
-    auto issue = [&](int it, int k) {
-        const u32x4* ep = reinterpret_cast<const u32x4*>(&sh.eptr[it * kTile + 4 * wave]);
-        const u32x4 pa = ep[0], pb = ep[1];
-        const uint8_t* rp[4] = {uniform_ptr(pa[0], pa[1]), uniform_ptr(pa[2], pa[3]), uniform_ptr(pb[0], pb[1]),
-                                uniform_ptr(pb[2], pb[3])};
-        if constexpr (KVDT == DT_BF16) {
-            const uint32_t dst = lds_addr(sh.xb[k]) + 4 * wave * kXPitch;
+
+    auto query_of = [&](int item) { return p.nsplit == 1 ? Q - 1 - item : item / p.nsplit; };
+    auto fetch = [&](int item, ItemFetch& f) {
+        const int qr = query_of(item);
+        const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) row_copy16(rp[i], voff, dst + i * kXPitch);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) stg[i] = *reinterpret_cast<const Raw*>(rp[i] + 8 * lane);
-        }
-    };
-    auto land = [&](int k) {  // e4m3 only: staged registers -> LDS
-        if constexpr (KVDT == DT_E4M3) {
-            uint8_t* xb = sh.xb[k];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4*>(xb + (4 * wave + i) * kXPitch + 16 * lane) = e4m3x8_to_bf16x8(stg[i]);
+        for (int j = 0; j < kIdsPerThread; ++j) {
+            const int c = j * kThreads + tid;
+            f.ids[j] = (j < nids && c < p.K) ? irow[c] : -1;
         }
     };
 
-    float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
-    float l_run = 0.f;                     // this lane's share of the running sum
-    f32x4 acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the pow() is far costlier than the per-item angle, so it runs once
+    for (int i = tid; i < p.rope_dims / 2; i += kThreads) sh.rope_inv[i] = rope_inv_freq(i, p.rope_dims, p.rope_base);
 
-    __syncthreads();  // entry table, rope table visible; list no longer needed
-    if constexpr (KVDT == DT_BF16) {
-        // settle the query-fragment loads now (a wait the compiler tracks), so
-        // that it places no vmcnt waits inside the loop, where they would
-        // also wait for the tile copies in flight
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-        if (ntile > 0) issue(0, 0);
-        if (ntile > 1) issue(1, 1);
-    } else {
-        if (ntile > 0) issue(0, 0);
-    }
+    ItemFetch nx;
+    int round = 0;
+    int item = item_of(0, blockIdx.x, G);
+    if (item < n_items) fetch(item, nx);
 
-    int cb = 0;  // buffer of tile it
-    for (int it = 0; it < ntile; ++it) {
-        if constexpr (KVDT == DT_BF16) {
-            if (it + 1 < ntile) wait_copies_but_4();
-            else wait_copies_all();
-            lds_sync();  // every wave's rows of tile `it` landed; tile it-1 consumed
-            if (it + 2 < ntile) issue(it + 2, cb == 0 ? 2 : cb - 1);
-        } else {
-            land(cb);
-            if (it + 1 < ntile) issue(it + 1, cb == 2 ? 0 : cb + 1);
-            lds_sync();
-        }
-        const uint8_t* xb = sh.xb[cb];
-        // ---- partial S^T over this wave's channel half ----
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+    while (item < n_items) {
+        const int qr = query_of(item);
+        const int split = p.nsplit == 1 ? 0 : item % p.nsplit;
+        const int b = qr / p.Tq;
+        const int64_t t = p.q_pos[qr];
+        const int rd = p.rope_dims;
+        // query fragments of head h, k-step i covering channels 32i .. 32i+31
+        // (lane group g takes 8 of them); issued first so that their latency
+        // overlaps the set-up below
+        bf16x8 qf[16];
+        {
+            const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            const int ch = g + 4 * (8 * dh + i);
-            const uint8_t* r0 = xb + l16 * kXPitch + 16 * ch;
-            const uint8_t* r1 = r0 + 16 * kXPitch;
-            const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(r0));
-            const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(r1));
-            const bf16x8 a2 = as_bf16x8(*reinterpret_cast<const u32x4*>(r0 + 64));
-            const bf16x8 a3 = as_bf16x8(*reinterpret_cast<const u32x4*>(r1 + 64));
-            s0 = mfma16x16x32(a0, qf[i], s0);
-            s1 = mfma16x16x32(a1, qf[i], s1);
-            s2 = mfma16x16x32(a2, qf[i + 1], s2);
-            s3 = mfma16x16x32(a3, qf[i + 1], s3);
+            for (int i = 0; i < 16; ++i) qf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * i + g)));
+            // held in accumulation registers (the MFMA reads its B operand
+            // from there): the architectural VGPRs stay free for the tile
+            // operands, so LDS reads can run further ahead of the MFMAs
+#pragma unroll
+            for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(qf[i]));
         }
-        s0 += s2;
-        s1 += s3;
-        *reinterpret_cast<f32x4*>(&sh.u.sx[wave][lane][0]) = s0;
-        *reinterpret_cast<f32x4*>(&sh.u.sx[wave][lane][4]) = s1;
+
+        // ---- compact the valid selected records (in order) ----
+        int ok_bits = 0;
+#pragma unroll
+        for (int j = 0; j < kIdsPerThread; ++j) {
+            if (j < nids) {
+                const int rec = nx.ids[j];
+                const bool ok = rec >= 0 && rec < p.N;
+                const unsigned long long bal = __ballot(ok);
+                if (ok) ok_bits |= 1 << j;
+                if (lane == 0) sh.cnt[j][wave] = __popcll(bal);
+            }
+        }
         lds_sync();
-        // full logits: mine + the other channel half's (same sum in both waves)
-        s0 += *reinterpret_cast<const f32x4*>(&sh.u.sx[wave ^ 4][lane][0]);
-        s1 += *reinterpret_cast<const f32x4*>(&sh.u.sx[wave ^ 4][lane][4]);
+        int nsel = 0;
+#pragma unroll
+        for (int j = 0; j < kIdsPerThread; ++j) {
+            if (j < nids) {
+                int before = 0;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) before += (w < wave) ? sh.cnt[j][w] : 0;
+                const bool ok = (ok_bits >> j) & 1;
+                const unsigned long long bal = __ballot(ok);
+                if (ok) sh.list[nsel + before + __popcll(bal & ((1ull << lane) - 1ull))] = nx.ids[j];
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) nsel += sh.cnt[j][w];
+            }
+        }
+        nsel = __builtin_amdgcn_readfirstlane(nsel);
+        const int nwin = t < 0 ? 0 : static_cast<int>(t + 1 < p.W ? t + 1 : p.W);
+        const int slot0 = static_cast<int>((t - nwin + 1) % p.S);  // ring slot of the first window row
+        const int E = nsel + nwin;
+        const int j0 = split * p.per_split;
+        const int j1 = min(E, j0 + p.per_split);
+        const int nvalid = j1 - j0;  // entries of this item
+        const int ntile = nvalid > 0 ? (nvalid + kTile - 1) / kTile : 0;
+        lds_sync();  // list complete
 
-        // ---- online softmax over this tile: entries 16*mt + 4g + v, head h ----
-        // z in log2 units.  Padding entries repeat a real row, so they may
-        // take part in the max; only their probabilities are dropped.
-        float z[8];
-        if constexpr (KVDT == DT_E4M3) {
-            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 4 * g]);
-            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                z[v] = s0[v] * f0[v];
-                z[4 + v] = s1[v] * f1[v];
+        // ---- entry table ----
+        for (int e = tid; e < ntile * kTile; e += kThreads) {
+            const int ge = min(j0 + e, j1 - 1);
+            const uint8_t* rp;
+            float sc = 1.f;
+            if (ge < nsel) {
+                const size_t r = static_cast<size_t>(b) * p.N + sh.list[ge];
+                if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
+                rp = p.kv + r * kRowBytes;
+            } else {
+                int slot = slot0 + (ge - nsel);  // < 2S since the window has at most S rows
+                if (slot >= p.S) slot -= p.S;
+                const size_t r = static_cast<size_t>(b) * p.S + slot;
+                if constexpr (KVDT == DT_E4M3) sc = p.swa_scale[r];
+                rp = p.swa + r * kRowBytes;
             }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                z[v] = s0[v] * cz;
-                z[4 + v] = s1[v] * cz;
-            }
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-        tmax = max4_rows(tmax);
-        // The reference max only moves when this tile exceeds it by more than
-        // kLazy (so probabilities stay below 2^kLazy); otherwise O needs no
-        // rescale.  The result is the same: every term is relative to m_run.
-        // On the first tile m_run is -inf and alpha is 0 (O and l are 0).
-        const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float pr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
-        const int lim = nvalid - it * kTile;  // entries of this tile that are real
-        if (lim < kTile) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                if (4 * g + v >= lim) pr[v] = 0.f;
-                if (16 + 4 * g + v >= lim) pr[4 + v] = 0.f;
+            sh.eptr[e] = reinterpret_cast<uint64_t>(rp);
+            if constexpr (KVDT == DT_E4M3) {
+                sh.ezf[e] = cz * sc;
+                sh.epf[e] = sc;
             }
         }
-        l_run = l_run * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-        m_run = m_new;
-        if constexpr (KVDT == DT_E4M3) {  // value rows carry their scale
-            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
-            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                pr[v] *= f0[v];
-                pr[4 + v] *= f1[v];
-            }
-        }
-        // P = hi + lo, both bf16: hi is P rounded, lo the rounding error
-        uint32_t phi[4], plo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t hi = cvt_bf16x2(pr[2 * i], pr[2 * i + 1]);
-            phi[i] = hi;
-            plo[i] = cvt_bf16x2(pr[2 * i] - __uint_as_float(hi << 16), pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
-        }
-        const bf16x8 bhi = as_bf16x8(u32x4{phi[0], phi[1], phi[2], phi[3]});
-        const bf16x8 blo = as_bf16x8(u32x4{plo[0], plo[1], plo[2], plo[3]});
+        lds_sync();  // table visible
 
-        // ---- O^T += X^T P^T : channels 256*dh + 16*u + 4g + v, head h ----
-        if (__any(alpha != 1.f)) {
+        // Tile staging: wave w fills rows 8w .. 8w+7 of the tile.  bf16 rows
+        // go straight from global memory into LDS; e4m3 rows are converted to
+        // bf16 in registers on the way (staged one tile ahead).
+        typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
+        Raw stg[kRowsPerWave];
+        auto issue = [&](int it, int k) {
+            const u32x4* ep = reinterpret_cast<const u32x4*>(&sh.eptr[it * kTile + kRowsPerWave * wave]);
+            if constexpr (KVDT == DT_BF16) {
+                // all addresses first: each copy is asm with a memory clobber,
+                // which no later LDS read may pass
+                u32x4 pa[kRowsPerWave / 2];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) acc[u] *= alpha;
-        }
-        // transposing-read source: lane s of group g -> row 4g + s/4 (and
-        // 16 + ...), channels d0 + 4(s%4) .. +3
-        const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3) + 2 * 256 * dh;
-        const uint8_t* tr1 = tr0 + 16 * kXPitch;
+                for (int i = 0; i < kRowsPerWave / 2; ++i) pa[i] = ep[i];
+                const uint32_t dst = lds_addr(sh.xb[k]) + kRowsPerWave * wave * kXPitch;
 #pragma unroll
-        for (int uh = 0; uh < 16; uh += 4) {
-            bf16x8 a[4];
+                for (int i = 0; i < kRowsPerWave; i += 2) {
+                    row_copy16(uniform_ptr(pa[i / 2][0], pa[i / 2][1]), voff, dst + i * kXPitch);
+                    row_copy16(uniform_ptr(pa[i / 2][2], pa[i / 2][3]), voff, dst + (i + 1) * kXPitch);
+                }
+            } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                typedef short s16x4 __attribute__((ext_vector_type(4)));
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(tr0 + 32 * (uh + u)));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(tr1 + 32 * (uh + u)));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                a[u] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(a[u], bhi, acc[uh + u]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(a[u], blo, acc[uh + u]);
-        }
-        cb = (cb == 2) ? 0 : cb + 1;
-    }
-    l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
-
-    // ---- finish ----
-    if (p.nsplit == 1) {
-        const float sk = p.sink[h] * kLog2e;
-        const float a = fmaxf(m_run, sk);
-        float f = 0.f;
-        if (a != -__builtin_huge_valf()) {
-            const float em = __builtin_amdgcn_exp2f(m_run - a);
-            const float es = __builtin_amdgcn_exp2f(sk - a);
-            const float den = l_run * em + es;
-            f = den > 0.f ? em / den : 0.f;
-        }
-        float* orow = p.out + (static_cast<size_t>(qr) * kH + h) * kD;
-        const int r0 = kD - rd;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int d = 256 * dh + 16 * u + 4 * g;
-            f32x4 o = acc[u] * f;
-            if (d + 3 >= r0) {
-#pragma unroll
-                for (int v = 0; v < 4; v += 2) {
-                    const int dd = d + v;
-                    if (dd >= r0) {
-                        const int jp = (dd - r0) >> 1;
-                        const float cs = sh.rope_cs[jp][0], sn = sh.rope_cs[jp][1];
-                        const float x = o[v], y = o[v + 1];
-                        o[v] = x * cs + y * sn;
-                        o[v + 1] = -x * sn + y * cs;
-                    }
+                for (int i = 0; i < kRowsPerWave; i += 2) {
+                    const u32x4 pa = ep[i / 2];
+                    stg[i] = *reinterpret_cast<const Raw*>(uniform_ptr(pa[0], pa[1]) + 8 * lane);
+                    stg[i + 1] = *reinterpret_cast<const Raw*>(uniform_ptr(pa[2], pa[3]) + 8 * lane);
                 }
             }
-            *reinterpret_cast<f32x4*>(orow + d) = o;
-        }
-    } else {
-        const size_t slot = (static_cast<size_t>(qr) * p.nsplit + split) * kH + h;
-        float* po = p.part_o + slot * kD;
+        };
+        auto land = [&](int k) {  // e4m3 only: staged registers -> LDS
+            if constexpr (KVDT == DT_E4M3) {
+                uint8_t* xb = sh.xb[k];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) *reinterpret_cast<f32x4*>(po + 256 * dh + 16 * u + 4 * g) = acc[u];
-        if (g == 0 && dh == 0) {
-            p.part_ml[2 * slot] = m_run;  // log2 units
-            p.part_ml[2 * slot + 1] = l_run;
+                for (int i = 0; i < kRowsPerWave; ++i)
+                    *reinterpret_cast<u32x4*>(xb + (kRowsPerWave * wave + i) * kXPitch + 16 * lane) =
+                        e4m3x8_to_bf16x8(stg[i]);
+            }
+        };
+
+        float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
+        float l_run = 0.f;                     // this lane's share of the running sum
+        f32x4 acc[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // next item's index slice first: the copies below are then the newest
+        // loads, as the copy waits in the loop assume
+        const int nxt = item_of(round + 1, blockIdx.x, G);
+        if (nxt < n_items) fetch(nxt, nx);
+        if (ntile > 0) issue(0, 0);
+        if constexpr (KVDT == DT_BF16) {
+            if (ntile > 1) issue(1, 1);
         }
+        if (p.nsplit == 1)
+            for (int i = tid; i < rd / 2; i += kThreads)
+                rope_cos_sin(t, sh.rope_inv[i], sh.rope_cs[i][0], sh.rope_cs[i][1]);
+
+        // Per tile: copies landed and the next ones issued; S^T; the tile max
+        // of each head; probabilities relative to the head's reference max;
+        // P.V.  The reference only moves when a tile exceeds it by more than
+        // kJump (log2 units), so probabilities stay below 2^kJump and O never
+        // needs a rescale in the loop.  When it does move, every earlier term
+        // weighs less than kMaxEnt * 2^-kJump relative to the new maximum --
+        // below fp32 resolution -- so O and l restart from zero, which is the
+        // rescale's result to fp32 accuracy.  (The first tile sets the
+        // reference; O and l are still zero then.)
+        int cb = 0;  // buffer of tile it
+        f32x4 s0, s1;
+        float z[8];
+        float tmax = -__builtin_huge_valf();
+        auto tile_logits = [&](int it) {
+            if constexpr (KVDT == DT_BF16) {
+                if (it + 1 < ntile) wait_copies_but_8();
+                else wait_copies_all();
+                lds_sync();  // every wave's rows of tile `it` landed; tile it-1 consumed
+                if (it + 2 < ntile) issue(it + 2, cb == 0 ? 2 : cb - 1);
+            } else {
+                land(cb);
+                if (it + 1 < ntile) issue(it + 1, cb == 2 ? 0 : cb + 1);
+                lds_sync();
+            }
+            const uint8_t* xb = sh.xb[cb];
+            // ---- S^T for entries 0..15 (s0, s2) and 16..31 (s1, s3) ----
+            // k-step pairs: the four row chunks of pair i+2 are read before
+            // the MFMAs of pair i (two pairs in flight hide the LDS latency)
+            f32x4 s2 = {0.f, 0.f, 0.f, 0.f}, s3 = s2;
+            s0 = s2;
+            s1 = s2;
+            const uint8_t* r0 = xb + l16 * kXPitch + 16 * g;
+            const uint8_t* r1 = r0 + 16 * kXPitch;
+            u32x4 ka[3][4];
+            auto kload = [&](int i, u32x4* d) {
+                d[0] = *reinterpret_cast<const u32x4*>(r0 + 64 * i);
+                d[1] = *reinterpret_cast<const u32x4*>(r1 + 64 * i);
+                d[2] = *reinterpret_cast<const u32x4*>(r0 + 64 * (i + 1));
+                d[3] = *reinterpret_cast<const u32x4*>(r1 + 64 * (i + 1));
+            };
+            kload(0, ka[0]);
+            kload(2, ka[1]);
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const int k = (i / 2) % 3;
+                if (i + 4 < 16) kload(i + 4, ka[(i / 2 + 2) % 3]);
+                __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
+                s0 = mfma16x16x32(as_bf16x8(ka[k][0]), qf[i], s0);
+                s1 = mfma16x16x32(as_bf16x8(ka[k][1]), qf[i], s1);
+                s2 = mfma16x16x32(as_bf16x8(ka[k][2]), qf[i + 1], s2);
+                s3 = mfma16x16x32(as_bf16x8(ka[k][3]), qf[i + 1], s3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            s0 += s2;
+            s1 += s3;
+            // z in log2 units, entries 16*mt + 4g + v of head h.  Padding
+            // entries repeat a real row, so they may take part in the max;
+            // only their probabilities are dropped.
+            if constexpr (KVDT == DT_E4M3) {
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 4 * g]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    z[v] = s0[v] * f0[v];
+                    z[4 + v] = s1[v] * f1[v];
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    z[v] = s0[v] * cz;
+                    z[4 + v] = s1[v] * cz;
+                }
+            }
+            tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+            tmax = max4_rows(tmax);
+        };
+        // probabilities relative to m_run, l update, P.V accumulation
+        auto tile_pv = [&](int it) {
+            float pr[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_run);
+            const int lim = nvalid - it * kTile;  // entries of this tile that are real
+            if (lim < kTile) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (4 * g + v >= lim) pr[v] = 0.f;
+                    if (16 + 4 * g + v >= lim) pr[4 + v] = 0.f;
+                }
+            }
+            l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            if constexpr (KVDT == DT_E4M3) {  // value rows carry their scale
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    pr[v] *= f0[v];
+                    pr[4 + v] *= f1[v];
+                }
+            }
+            // P = hi + lo, both bf16: hi is P rounded, lo the rounding error
+            uint32_t phi[4], plo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t hi = cvt_bf16x2(pr[2 * i], pr[2 * i + 1]);
+                phi[i] = hi;
+                plo[i] = cvt_bf16x2(pr[2 * i] - __uint_as_float(hi << 16),
+                                    pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
+            }
+            const bf16x8 bhi = as_bf16x8(u32x4{phi[0], phi[1], phi[2], phi[3]});
+            const bf16x8 blo = as_bf16x8(u32x4{plo[0], plo[1], plo[2], plo[3]});
+            // ---- O^T += X^T P^T : channels 16*u + 4g + v, head h ----
+            // transposing-read source: lane s of group g -> row 4g + s/4 (and
+            // 16 + ...), channels d0 + 4(s%4) .. +3
+            const uint8_t* xb = sh.xb[cb];
+            const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3);
+            const uint8_t* tr1 = tr0 + 16 * kXPitch;
+            // channel groups of 4 x 16: the operands of group k+1 are read
+            // before the MFMAs of group k
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            bf16x8 va[2][4];
+            auto vload = [&](int uh, bf16x8* d) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(tr0 + 32 * (uh + u)));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(tr1 + 32 * (uh + u)));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                    d[u] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+                }
+            };
+            vload(0, va[0]);
+#pragma unroll
+            for (int uh = 0; uh < 32; uh += 4) {
+                const int k = (uh / 4) & 1;
+                if (uh + 4 < 32) vload(uh + 4, va[k ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], bhi, acc[uh + u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], blo, acc[uh + u]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            cb = (cb == 2) ? 0 : cb + 1;
+        };
+
+        for (int it = 0; it < ntile; ++it) {
+            tile_logits(it);
+            const bool jump = tmax > m_run + kJump;
+            if (__any(jump && m_run != -__builtin_huge_valf())) {  // rare
+                if (jump) {
+#pragma unroll
+                    for (int u = 0; u < 32; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    l_run = 0.f;
+                }
+            }
+            m_run = jump ? tmax : m_run;
+            tile_pv(it);
+        }
+        l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
+        // the next item's fetch and every copy have landed (a wait the
+        // compiler tracks, placed before the output stores so that no later
+        // wait for the fetched registers has to cover stores as well)
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+        lds_sync();  // rope table visible; tiles, list and table no longer read
+
+        // ---- finish ----
+        if (p.nsplit == 1) {
+            const float sk = p.sink[h] * kLog2e;
+            const float a = fmaxf(m_run, sk);
+            float f = 0.f;
+            if (a != -__builtin_huge_valf()) {
+                const float em = __builtin_amdgcn_exp2f(m_run - a);
+                const float es = __builtin_amdgcn_exp2f(sk - a);
+                const float den = l_run * em + es;
+                f = den > 0.f ? em / den : 0.f;
+            }
+            float* orow = p.out + (static_cast<size_t>(qr) * kH + h) * kD;
+            const int r0 = kD - rd;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int d = 16 * u + 4 * g;
+                f32x4 o = acc[u] * f;
+                if (d + 3 >= r0) {
+#pragma unroll
+                    for (int v = 0; v < 4; v += 2) {
+                        const int dd = d + v;
+                        if (dd >= r0) {
+                            const int jp = (dd - r0) >> 1;
+                            const float cs = sh.rope_cs[jp][0], sn = sh.rope_cs[jp][1];
+                            const float x = o[v], y = o[v + 1];
+                            o[v] = x * cs + y * sn;
+                            o[v + 1] = -x * sn + y * cs;
+                        }
+                    }
+                }
+                *reinterpret_cast<f32x4*>(orow + d) = o;
+            }
+        } else {
+            const size_t slot = (static_cast<size_t>(qr) * p.nsplit + split) * kH + h;
+            float* po = p.part_o + slot * kD;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) *reinterpret_cast<f32x4*>(po + 16 * u + 4 * g) = acc[u];
+            if (g == 0) {
+                p.part_ml[2 * slot] = m_run;  // log2 units
+                p.part_ml[2 * slot + 1] = l_run;
+            }
+        }
+        ++round;
+        item = nxt;
     }
 }
 
@@ -715,11 +824,14 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
             p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) +
                                                  ((o + 255) & ~static_cast<size_t>(255)));
         }
-        dim3 grid(p.nsplit, Q);
+        // persistent: one workgroup per compute unit (the LDS footprint
+        // allows one), each walking its share of the work items
+        const int n_items = Q * p.nsplit;
+        const dim3 grid(n_items < num_cus() ? n_items : num_cus());
         if (a.kv_dtype == DT_BF16)
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_BF16>, grid, dim3(512), 0, st, p);
+            hipLaunchKernelGGL(attn_mfma_kernel<DT_BF16>, grid, dim3(kThreads), 0, st, p);
         else
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(512), 0, st, p);
+            hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(kThreads), 0, st, p);
         int e = static_cast<int>(hipGetLastError());
         if (e || p.nsplit == 1) return e;
         hipLaunchKernelGGL(attn_combine_kernel, dim3(Q, kH / 4), dim3(256), 0, st, p);

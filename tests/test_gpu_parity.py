@@ -224,6 +224,48 @@ def test_sparse_attn_sharp_logits(kdt):
             PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
 
 
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("Tq", [3, 150])
+def test_sparse_attn_late_dominant_entry(kdt, Tq):
+    """Every query's own window row (its last entry) gets a logit about 150
+    nats above all others, so the running maximum jumps by far more than
+    any lazy threshold in the last tile: the kernel must drop the earlier
+    terms' scale correctly (single-launch and split paths)."""
+    _case(f"sparse_attn late dominant entry {kdt} Tq={Tq}")
+    wl, inp, idx = _attn_case(kdt, Tq)
+    sh, lay = inp["shared"], inp["layers"][0]
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal(wl.D)
+    u /= np.linalg.norm(u)
+    sm = 1.0 / math.sqrt(wl.D)
+    row_norm, z_big = 10.0, 150.0
+    gq = z_big / (sm * row_norm)
+    q = lay["q"].copy()
+    q[:, :, :, :] = WL.f32_to_bf16_bits((gq * u).astype(np.float32))
+    lay["q"] = q
+    big = (row_norm * u).astype(np.float32)[None, :]
+    swa, swa_scale = lay["swa"].copy(), None if lay["swa_scale"] is None else lay["swa_scale"].copy()
+    for b in range(wl.B):
+        for ti in range(Tq):
+            slot = int(lay["q_pos"][b, ti]) % wl.S
+            if kdt == "e4m3":
+                codes, sc = WL.quantize_rows_e4m3(big)
+                swa[b, slot] = codes[0]
+                swa_scale[b, slot] = sc[0]
+            else:
+                swa[b, slot] = WL.f32_to_bf16_bits(big)[0]
+    lay["swa"], lay["swa_scale"] = swa, swa_scale
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b in range(2):
+        for ti in (list(range(Tq)) if Tq < 10 else [0, 1, 77, Tq - 1]):
+            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+
+
 @pytest.mark.parametrize("H,D,dt", [(2, 16, "f32"), (3, 48, "bf16")])
 def test_sparse_attn_generic(H, D, dt):
     _case(f"sparse_attn generic H={H} D={D} {dt}")
