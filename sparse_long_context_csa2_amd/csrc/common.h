@@ -99,6 +99,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 -> f32 (gfx950).  Operand layout, lane l = 0..63:
+//   A[i][k]: i = l % 32, k in group l / 32 (8 values)
+//   B[k][j]: j = l % 32, k in group l / 32 (8 values)
+//   C[i][j]: j = l % 32, i = 8 * (v / 4) + 4 * (l / 32) + v % 4, v = 0..15
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- shuffles

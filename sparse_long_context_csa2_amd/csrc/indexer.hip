@@ -15,11 +15,13 @@
 //    bytes, so a wave touches 16 whole 64-byte segments per instruction.
 //    The ReLU, head weights and the sum over heads run in the epilogue:
 //    a lane holds 8 heads of one record, two xor-shuffles finish the sum.
-//    Decode rows (one query token) give each wave its own record tiles;
-//    prefill gives each wave four tokens and all waves the same tiles, so
-//    a key tile fetched once feeds 4 x 4 tokens from L1/L2.
+//    Decode rows (one query token) give each wave its own record tiles.
+//  * idx_prefill_kernel -- many tokens of one sequence (no pool): 32x32x16
+//    MFMAs over LDS-staged key tiles shared by a workgroup's 8 tokens.
 //  * idx_generic_kernel -- any head count/dim and dtype, one thread per
 //    (row, column), fp32 FMA; used for small shapes such as the toy.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -213,6 +215,196 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     }
 }
 
+// Prefill scoring: many query tokens of one sequence against the records
+// they may see -- a causal GEMM (tokens x heads) x 128 x records with a
+// ReLU and weighted head-sum epilogue.  32x32x16 MFMAs: M = the 32 heads of
+// one token, N = 32 records, K = 128 dims in 8 k-steps.  A workgroup takes
+// kPfTok consecutive tokens (kPfTokW per wave, their query fragments and
+// head weights in registers) and streams the 32-record key tiles they can
+// see through LDS (double-buffered, fetched two tiles ahead); each lane
+// ends a tile holding 16 heads of one record, so the head sum is a short
+// tree and one lane swap.  The grid is (column chunk of kPfChunk, token
+// block): later token blocks see more records, and the chunks keep the
+// longest workgroup short.  Scores collect in LDS and leave in whole rows
+// at the end: no global store sits in the tile loop, so the waits for the
+// key prefetches stay exact.
+constexpr int kPfTokW = 2;             // tokens per wave
+constexpr int kPfTok = 4 * kPfTokW;    // tokens per workgroup
+constexpr int kPfRec = 32;             // records per tile
+constexpr int kPfPitch = kDi + 8;      // bf16 per LDS key row: 272 B keeps 16 lanes' reads on distinct banks
+constexpr int kPfChunk = 512;          // score columns per workgroup
+
+template <int KDT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void idx_prefill_kernel(IdxP p) {
+    __shared__ __align__(16) uint16_t kt[2][kPfRec * kPfPitch];
+    __shared__ float kts[2][kPfRec];
+    __shared__ __align__(16) float scs[kPfTok][kPfChunk];
+    __shared__ __align__(16) float wl[kPfTok][kHi];
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 31;   // record within the tile (B and C column)
+    const int kg = lane >> 5;  // k group
+    // Workgroup L runs on XCD L % 8 (round-robin dispatch).  The column
+    // chunks of one token block get ids that are equal mod 8, so its query
+    // rows are fetched into one L2 and shared; later token blocks (more
+    // visible records) come first.
+    const int gps = (p.Tq + kPfTok - 1) / kPfTok;
+    const int nblk = p.B * gps;
+    const int nch = (p.ncols + kPfChunk - 1) / kPfChunk;
+    const int L = static_cast<int>(blockIdx.x);
+    const int mi = L / 8;
+    const int tbi = (mi / nch) * 8 + L % 8;
+    if (tbi >= nblk) return;  // padding of the id space to a multiple of 8 blocks
+    const int blk = nblk - 1 - tbi;
+    const int c0 = (mi % nch) * kPfChunk;
+    const int cw = min(kPfChunk, p.ncols - c0);
+    const int b = blk / gps;
+    const int tb = (blk % gps) * kPfTok;
+    const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+    const size_t row0 = static_cast<size_t>(b) * p.Tq;
+
+    // Every global read the block needs before its first tile goes out
+    // at once: positions (lanes 0..7 of each wave), query fragments, head
+    // weights (to LDS) and, below, the first key tiles.
+    const int pt = tb + (lane & 7);
+    const int64_t pos = pt < p.Tq ? p.q_pos[row0 + pt] : -1;
+    bf16x8 qa[kPfTokW][8];
+#pragma unroll
+    for (int tk = 0; tk < kPfTokW; ++tk) {
+        const int t = min(tb + kPfTokW * wave + tk, p.Tq - 1);
+        const uint16_t* qh = p.q + ((row0 + t) * kHi + j) * kDi + 8 * kg;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qa[tk][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ks));
+    }
+    {
+        const int t = min(tb + tid / kHi, p.Tq - 1);
+        wl[tid / kHi][tid % kHi] = p.w[(row0 + t) * kHi + tid % kHi];  // 256 threads = 8 tokens x 32 heads
+    }
+    // key tile staging: thread -> (record tid / 8, 16-dim chunk tid % 8)
+    const int sr = tid >> 3, sc = tid & 7;
+    const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+    typedef typename std::conditional<KDT == DT_BF16, u32x4, u32x2>::type Raw;
+    struct Stage {
+        Raw d[2];
+        float s;
+    };
+    auto fetch = [&](int ti, Stage& st) {
+        const int rec = ti * kPfRec + sr;
+        const bool ok = rec < p.N;  // rows past the visible ones are masked after the product
+        const uint8_t* r = kbase + static_cast<size_t>(ok ? rec : 0) * kRowBytes;
+        if constexpr (KDT == DT_BF16) {
+            st.d[0] = ok ? reinterpret_cast<const u32x4*>(r)[2 * sc] : u32x4{0, 0, 0, 0};
+            st.d[1] = ok ? reinterpret_cast<const u32x4*>(r)[2 * sc + 1] : u32x4{0, 0, 0, 0};
+            st.s = 1.f;
+        } else {
+            st.d[0] = ok ? reinterpret_cast<const u32x2*>(r)[2 * sc] : u32x2{0, 0};
+            st.d[1] = ok ? reinterpret_cast<const u32x2*>(r)[2 * sc + 1] : u32x2{0, 0};
+            st.s = (ok && sc == 0) ? p.ks[static_cast<size_t>(b) * p.N + rec] : 0.f;
+        }
+    };
+    auto land = [&](int buf, const Stage& st) {
+        u32x4* d = reinterpret_cast<u32x4*>(&kt[buf][sr * kPfPitch + 16 * sc]);
+        if constexpr (KDT == DT_BF16) {
+            d[0] = st.d[0];
+            d[1] = st.d[1];
+        } else {
+            d[0] = e4m3x8_to_bf16x8(st.d[0]);
+            d[1] = e4m3x8_to_bf16x8(st.d[1]);
+            if (sc == 0) kts[buf][sr] = st.s;
+        }
+    };
+
+    const int it0 = c0 / kPfRec;
+    const int it_cap = (c0 + cw + kPfRec - 1) / kPfRec;  // tiles of this chunk
+    Stage s0, sa, sb;  // tiles it0, it+1 and it+2
+    fetch(it0, s0);
+    if (it0 + 1 < it_cap) fetch(it0 + 1, sa);
+    if (it0 + 2 < it_cap) fetch(it0 + 2, sb);
+
+    // visibility: lanes 0..7 hold the block's tokens; the block's maximum
+    // bounds the tiles, each token masks its own columns
+    int v8 = (lane < kPfTok && pt < p.Tq) ? visible_count(pos, p.m, nrec) : 0;
+#pragma unroll
+    for (int o = 1; o < kPfTok; o <<= 1) v8 = max(v8, __shfl_xor(v8, o, kWave));
+    const int vis_blk = min(__builtin_amdgcn_readfirstlane(v8), p.ncols);
+    int vis[kPfTokW];
+#pragma unroll
+    for (int tk = 0; tk < kPfTokW; ++tk) {
+        const int i = kPfTokW * wave + tk;
+        const int vi = (tb + i < p.Tq) ? visible_count(__shfl(pos, i, kWave), p.m, nrec) : 0;
+        vis[tk] = __builtin_amdgcn_readfirstlane(vi);
+    }
+    // tiles of this chunk that any token of the block can see
+    const int it_end = min((min(vis_blk, c0 + cw) + kPfRec - 1) / kPfRec, it_cap);
+    if (it0 < it_end) land(0, s0);
+    // columns no tile writes stay -inf
+    for (int i = tid; i < kPfTok * kPfChunk / 4; i += 256)
+        reinterpret_cast<f32x4*>(&scs[0][0])[i] = f32x4{-__builtin_huge_valf(), -__builtin_huge_valf(),
+                                                        -__builtin_huge_valf(), -__builtin_huge_valf()};
+    {
+        for (int it = it0; it < it_end; ++it) {
+            const int buf = (it - it0) & 1;
+            __syncthreads();  // tile `it` in LDS; tile it-1's buffer free; score rows cleared
+            bf16x8 bk[8];
+            const uint16_t* kr = &kt[buf][j * kPfPitch + 8 * kg];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) bk[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * ks));
+            f32x16 c[kPfTokW];
+#pragma unroll
+            for (int tk = 0; tk < kPfTokW; ++tk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) c[tk][v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int tk = 0; tk < kPfTokW; ++tk) c[tk] = mfma32x32x16(qa[tk][ks], bk[ks], c[tk]);
+            const int rec = it * kPfRec + j;
+            const float ksc = (KDT == DT_E4M3) ? kts[buf][j] : 1.f;
+#pragma unroll
+            for (int tk = 0; tk < kPfTokW; ++tk) {
+                // head weights of this lane's 16 heads: 8 (v / 4) + 4 kg + v % 4
+                float wv[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wl[kPfTokW * wave + tk][8 * q4 + 4 * kg]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) wv[4 * q4 + v] = w4[v];
+                }
+                float pr[8];
+#pragma unroll
+                for (int v = 0; v < 8; ++v)
+                    pr[v] = fmaf(wv[2 * v + 1], fmaxf(c[tk][2 * v + 1], 0.f), wv[2 * v] * fmaxf(c[tk][2 * v], 0.f));
+                const float part = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                float x, y;
+                pair_xor32(part, x, y);
+                const float val = (x + y) * ksc;  // the row scale is >= 0, so it commutes with the ReLU
+                if (kg == 0 && rec < c0 + cw && rec < vis[tk]) scs[kPfTokW * wave + tk][rec - c0] = val;
+            }
+            if (it + 1 < it_end) {
+                land(buf ^ 1, sa);
+                sa = sb;
+                if (it + 3 < it_end) fetch(it + 3, sb);
+            }
+        }
+        __syncthreads();  // score rows complete
+        // 16-byte stores when every output row starts 16-byte aligned
+        const int cw4 = (p.ncols % 4 == 0) ? cw / 4 : 0;
+        for (int i = tid; i < kPfTok * cw4; i += 256) {
+            const int tk = i / cw4, q4 = i % cw4;
+            if (tb + tk < p.Tq)
+                *reinterpret_cast<f32x4*>(&p.out[(row0 + tb + tk) * p.ncols + c0 + 4 * q4]) =
+                    reinterpret_cast<const f32x4*>(&scs[tk][0])[q4];
+        }
+        const int rest = cw - 4 * cw4;  // columns left for single stores
+        for (int i = tid; i < kPfTok * rest; i += 256) {
+            const int tk = i / rest, col = 4 * cw4 + i % rest;
+            if (tb + tk < p.Tq) p.out[(row0 + tb + tk) * p.ncols + c0 + col] = scs[tk][col];
+        }
+    }
+}
+
 struct IdxG {
     int B, Tq, N, Hi, Di, m, ncols, P, blk, qdt, kdt;
     const void* q;
@@ -292,9 +484,24 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
         // Prefill-shaped work (many tokens of one sequence, no pool): waves
         // share record tiles across 16 tokens.
         if (!a.pool && a.Tq >= 16) {
-            const int tpb = 16;
-            return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16, 4, true>(a, tpb, st)
-                                        : launch_mfma<DT_E4M3, 4, true>(a, tpb, st);
+            IdxP p;
+            p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
+            p.q = static_cast<const uint16_t*>(a.q_idx);
+            p.w = a.w;
+            p.k = static_cast<const uint8_t*>(a.k_idx);
+            p.ks = a.k_scale;
+            p.q_pos = a.q_pos;
+            p.n_rec = a.n_rec;
+            p.pool = nullptr;
+            p.out = a.scores;
+            p.tiles_per_block = 0;
+            const int nblk8 = (a.B * ((a.Tq + kPfTok - 1) / kPfTok) + 7) / 8 * 8;
+            const dim3 grid(nblk8 * ((a.ncols + kPfChunk - 1) / kPfChunk));
+            if (a.k_dtype == DT_BF16)
+                hipLaunchKernelGGL(idx_prefill_kernel<DT_BF16>, grid, dim3(256), 0, st, p);
+            else
+                hipLaunchKernelGGL(idx_prefill_kernel<DT_E4M3>, grid, dim3(256), 0, st, p);
+            return static_cast<int>(hipGetLastError());
         }
         // Decode rows: pick tiles per block so the grid has >= ~2048 blocks
         // while each wave still streams several tiles.

@@ -64,14 +64,17 @@ def test_index_scores_mfma_decode(kdt):
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
-def test_index_scores_mfma_prefill(kdt):
-    _case(f"index_scores prefill tiles, {kdt} keys, Tq=70 (ragged token groups)")
-    wl = _small(B=2, Tq=70, N=40, decode_pos=None, k_dtype=kdt, W=8)
+@pytest.mark.parametrize("Tq,N", [(70, 40), (37, 700), (21, 301)])
+def test_index_scores_mfma_prefill(kdt, Tq, N):
+    """Ragged token groups; several 256-column chunks (N=700); a row length
+    that is not a multiple of 4 (N=301)."""
+    _case(f"index_scores prefill tiles, {kdt} keys, Tq={Tq} N={N}")
+    wl = _small(B=2, Tq=Tq, N=N, decode_pos=None, k_dtype=kdt, W=8)
     inp = WL.make_inputs(wl)
-    inp["layers"][0]["q_pos"][1] += 60  # second sequence later in its context
+    inp["layers"][0]["q_pos"][1] += 60 if N < 100 else 2000  # second sequence later in its context
     g = _run_scores(inp)
     for b in range(2):
-        for ti in range(70):
+        for ti in range(Tq):
             PR.check_scores(g[b, ti], O.full_row_scores(inp["shared"], inp["layers"][0], b, ti), f"b={b} t={ti}")
 
 
