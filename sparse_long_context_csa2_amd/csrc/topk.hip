@@ -17,16 +17,18 @@
 //     boundary bin's elements (usually a few dozen) picks the rest.
 // All bin searches are parallel block scans.
 //
-// Rows of up to 16384 columns: one 256-thread workgroup per row with the
-// keys cached in LDS (rows up to 4096 use a 41 KiB variant so several rows
-// share a CU).
+// Rows of up to 4096 columns: one 256-thread workgroup per row with the
+// keys cached in LDS.
 // Longer rows: the row is split into 4096-column chunks over many
-// workgroups -- a histogram kernel accumulates the row histogram with
-// global atomics, then a select kernel classifies its chunk (chosen /
-// boundary candidate) into per-row lists; the last workgroup to finish a
-// row (atomic ticket after a device-scope fence) resolves the boundary bin
-// and writes the row.  Output ids are sorted by column, so results are
-// deterministic whatever the order in which workgroups ran.
+// workgroups.  A histogram kernel accumulates the row histogram (LDS-
+// private per workgroup, merged with global atomics); a select kernel then
+// classifies each chunk in LDS -- keys above the boundary bin are chosen
+// outright, keys inside it are candidates -- and appends both lists to the
+// row's with one atomic.  The last workgroup to finish a row (atomic
+// ticket after a device-scope fence) resolves the boundary bin exactly
+// and writes the row.  Output ids are sorted by
+// column, so results are deterministic whatever the order in which
+// workgroups ran.
 //
 // The block pool scores block b by the maximum of its members ("DeepSeek
 // V4.1-Flash. Every layer, connected.", hierarchy caption) -- one wave per
@@ -42,8 +44,7 @@ constexpr int kNT = 256;             // threads per workgroup
 constexpr int kNW = kNT / kWave;     // waves per workgroup
 constexpr int kBins = 4096;          // first-level bins: key >> 20
 constexpr int kBinShift = 20;
-constexpr int kSmallCols = 4096;     // short rows: one workgroup, 3 per CU
-constexpr int kMedCols = 16384;      // rows up to this length: one workgroup
+constexpr int kSmallCols = 4096;     // short rows: one workgroup per row
 constexpr int kChunk = 4096;         // columns per workgroup on long rows
 constexpr int kCandCap = 2048;       // boundary candidates held in LDS
 constexpr int kMaxK = 2048;
@@ -55,10 +56,11 @@ struct TopkP {
     int32_t* idx;
     int sort_by_key;
     // long-row workspace
-    int* ghist;      // [rows][kBins]
-    int* cnt;        // [rows][4]: chosen count, candidate count, finished chunks
-    int* sure;       // [rows][K]
-    int* cand;       // [rows][ncols]
+    int* ghist;      // [rows][kBins]: histogram of the keys' top 12 bits
+    int* cnt;        // [rows][4]: candidate count, chosen count (one 64-bit word), finished chunks
+    int* sure;       // [rows][K]: columns chosen outright
+    uint32_t* ckey;  // [rows][ncols]: boundary-bin candidates (key, column)
+    int* ccol;
 };
 
 __device__ __forceinline__ int rec_of(const TopkP& p, const int32_t* prow, int c) {
@@ -148,10 +150,14 @@ __device__ int find_from_top(const int* hist, int need, Scan& s, int* rest, int*
 // Exact radix select of the `need` largest composite keys among the
 // elements src(i) yields, i in [0, count).  Returns the threshold:
 // chosen = composite >= thr.  src(i, key, rec) returns false to skip.
+// The digits above `shift0` must be the same for all elements (`known`
+// holds them; bits of `known` below those digits are ignored).
 template <class Src>
-__device__ unsigned long long radix_select(Src src, int count, int need, int* hist8, Scan& s) {
-    unsigned long long prefix = 0, mask = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+__device__ unsigned long long radix_select(Src src, int count, int need, int* hist8, Scan& s,
+                                           int shift0 = 56, unsigned long long known = 0) {
+    unsigned long long mask = shift0 >= 56 ? 0ull : ~0ull << (shift0 + 8);
+    unsigned long long prefix = known & mask;
+    for (int shift = shift0; shift >= 0; shift -= 8) {
         // stop as soon as the remaining prefix class holds exactly `need`
         hist8[threadIdx.x] = 0;
         __syncthreads();
@@ -305,6 +311,20 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
 
 // ---------------------------------------------------------------- long rows
 
+// Slot for this lane in a list appended to through *counter, one atomic
+// per wave (ballot, then this lane's rank among the appending lanes).
+__device__ __forceinline__ int wave_append(int* counter, bool pred) {
+    const unsigned long long bal = __ballot(pred);
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    if (bal) {
+        const int leader = __ffsll(static_cast<long long>(bal)) - 1;
+        if (lane == leader) base = atomicAdd(counter, __popcll(bal));
+        base = __shfl(base, leader, kWave);
+    }
+    return base + __popcll(bal & ((1ull << lane) - 1ull));
+}
+
 __global__ __launch_bounds__(kNT) void topk_zero_kernel(TopkP p) {
     const int row = blockIdx.x;
     int* h = p.ghist + static_cast<size_t>(row) * kBins;
@@ -319,12 +339,18 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
     const int c1 = min(p.ncols, c0 + kChunk);
     const float* srow = p.scores + static_cast<size_t>(row) * p.ncols;
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
+    // the chunk's keys first, all loads in flight at once
+    uint32_t kk[kChunk / kNT];
+#pragma unroll
+    for (int i = 0; i < kChunk / kNT; ++i) {
+        const int c = c0 + i * kNT + threadIdx.x;
+        kk[i] = c < c1 ? key_of(p, prow, srow, c) : 0u;
+    }
     for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;
     __syncthreads();
-    for (int c = c0 + threadIdx.x; c < c1; c += kNT) {
-        const uint32_t k = key_of(p, prow, srow, c);
-        if (k) atomicAdd(&hist[k >> kBinShift], 1);
-    }
+#pragma unroll
+    for (int i = 0; i < kChunk / kNT; ++i)
+        if (kk[i]) atomicAdd(&hist[kk[i] >> kBinShift], 1);
     __syncthreads();
     int* g = p.ghist + static_cast<size_t>(row) * kBins;
     for (int i = threadIdx.x; i < kBins; i += kNT)
@@ -334,10 +360,19 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
 struct LongShared {
     int hist[kBins];
     int hist8[256];
-    unsigned long long fin[kMaxK];
-    uint32_t ckey[kCandCap];
-    int crec[kCandCap];
-    int ccol[kCandCap];
+    union {
+        struct {                      // classification of one chunk
+            uint32_t key[kChunk];     // its level-1 boundary candidates
+            int col[kChunk];
+            int sure[kMaxK];          // its keys above the boundary bin
+        } chunk;
+        struct {                      // the row's final resolution
+            unsigned long long fin[kMaxK];
+            uint32_t key[kCandCap];   // the row's boundary candidates
+            int rec[kCandCap];
+            int col[kCandCap];
+        } fin;
+    } u;
     Scan scan;
     int misc[4];
 };
@@ -350,112 +385,157 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     const int c1 = min(p.ncols, c0 + kChunk);
     const float* srow = p.scores + static_cast<size_t>(row) * p.ncols;
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
-    const int* g = p.ghist + static_cast<size_t>(row) * kBins;
     int* cnt = p.cnt + row * 4;
     int* sure = p.sure + static_cast<size_t>(row) * K;
-    int* cand = p.cand + static_cast<size_t>(row) * p.ncols;
+    uint32_t* gkey = p.ckey + static_cast<size_t>(row) * p.ncols;
+    int* gcol = p.ccol + static_cast<size_t>(row) * p.ncols;
 
+    // the chunk's keys and the row histogram, all loads in flight at once
+    uint32_t kk[kChunk / kNT];
+#pragma unroll
+    for (int i = 0; i < kChunk / kNT; ++i) {
+        const int c = c0 + i * kNT + threadIdx.x;
+        kk[i] = c < c1 ? key_of(p, prow, srow, c) : 0u;
+    }
+    const int* g = p.ghist + static_cast<size_t>(row) * kBins;
     for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = g[i];
+    if (threadIdx.x == 0) {
+        sh.misc[0] = 0;  // candidates of the chunk
+        sh.misc[1] = 0;  // keys above the boundary
+    }
     __syncthreads();
-    int need;
-    const int bstar = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need);
-    // classify this chunk
-    for (int c = c0 + threadIdx.x; c < c1; c += kNT) {
-        const uint32_t k = key_of(p, prow, srow, c);
-        if (!k) continue;
+    int need1;
+    const int b1 = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need1);
+    // classify into LDS lists: above b1 chosen outright, inside b1 candidates
+#pragma unroll
+    for (int i = 0; i < kChunk / kNT; ++i) {
+        const int c = c0 + i * kNT + threadIdx.x;
+        const uint32_t k = kk[i];
         const int b = static_cast<int>(k >> kBinShift);
-        if (b > bstar) {
-            sure[atomicAdd(&cnt[0], 1)] = c;
-        } else if (b == bstar) {
-            cand[atomicAdd(&cnt[1], 1)] = c;
+        const bool up = k != 0u && b > b1;
+        const bool in = k != 0u && b == b1;
+        const int su = wave_append(&sh.misc[1], up);
+        if (up) sh.u.chunk.sure[su] = c;  // fewer than K keys lie above b1
+        const int sl = wave_append(&sh.misc[0], in);
+        if (in) {
+            sh.u.chunk.key[sl] = k;
+            sh.u.chunk.col[sl] = c;
         }
     }
+    __syncthreads();
+    const int nloc = sh.misc[0], nsu = sh.misc[1];
+    // one atomic reserves room in both of the row's lists
+    if (threadIdx.x == 0) {
+        const unsigned long long add = (static_cast<unsigned long long>(nsu) << 32) | static_cast<unsigned>(nloc);
+        const unsigned long long base = (nloc | nsu) ? atomicAdd(reinterpret_cast<unsigned long long*>(cnt), add) : 0ull;
+        sh.misc[2] = static_cast<int>(base & 0xFFFFFFFFull);
+        sh.misc[3] = static_cast<int>(base >> 32);
+    }
+    __syncthreads();
+    const int gbase = sh.misc[2], sbase = sh.misc[3];
+    for (int i = threadIdx.x; i < nloc; i += kNT) {
+        gkey[gbase + i] = sh.u.chunk.key[i];
+        gcol[gbase + i] = sh.u.chunk.col[i];
+    }
+    for (int i = threadIdx.x; i < nsu; i += kNT) sure[sbase + i] = sh.u.chunk.sure[i];
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) sh.misc[0] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
+    if (threadIdx.x == 0) sh.misc[2] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
     __syncthreads();
-    if (!sh.misc[0]) return;
+    if (!sh.misc[2]) return;
     __threadfence();
 
     // ---- last workgroup of this row: resolve the boundary bin ----
-    const int nsure = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
-    const int ncand = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
-    unsigned long long thr = ~0ull;  // nothing from the boundary bin
-    const bool in_lds = ncand <= kCandCap;
-    if (bstar >= 0 && in_lds) {
-        for (int i = threadIdx.x; i < ncand; i += kNT) {
-            const int c = __builtin_nontemporal_load(cand + i);
-            sh.ccol[i] = c;
-            sh.ckey[i] = key_of(p, prow, srow, c);
-            sh.crec[i] = rec_of(p, prow, c);
-        }
-        __syncthreads();
-        auto src = [&](int i, uint32_t& key, int& rec) -> bool {
-            key = sh.ckey[i];
-            rec = sh.crec[i];
-            return true;
-        };
-        thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
-    } else if (bstar >= 0) {
-        auto src = [&](int i, uint32_t& key, int& rec) -> bool {
-            const int c = __builtin_nontemporal_load(cand + i);
-            key = key_of(p, prow, srow, c);
-            rec = rec_of(p, prow, c);
-            return true;
-        };
-        thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
-    }
-    if (threadIdx.x == 0) sh.misc[1] = 0;
+    const int ncand = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
+    const int nsure = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
+    if (threadIdx.x == 0) sh.misc[0] = 0;  // final count
     __syncthreads();
+    auto take_col = [&](int c, uint32_t key) {
+        const int slot = atomicAdd(&sh.misc[0], 1);
+        if (slot < K)
+            sh.u.fin.fin[slot] = p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
+    };
     for (int i = threadIdx.x; i < nsure; i += kNT) {
         const int c = __builtin_nontemporal_load(sure + i);
-        const int slot = atomicAdd(&sh.misc[1], 1);
-        if (slot < K) {
-            sh.fin[slot] = p.sort_by_key ? composite(key_of(p, prow, srow, c), rec_of(p, prow, c))
-                                         : static_cast<unsigned long long>(c);
-        }
+        take_col(c, p.sort_by_key ? key_of(p, prow, srow, c) : 0u);
     }
-    if (bstar >= 0) {
-        for (int i = threadIdx.x; i < ncand; i += kNT) {
-            const int c = in_lds ? sh.ccol[i] : __builtin_nontemporal_load(cand + i);
-            const unsigned long long ck = in_lds ? composite(sh.ckey[i], sh.crec[i])
-                                                 : composite(key_of(p, prow, srow, c), rec_of(p, prow, c));
-            if (ck >= thr) {
-                const int slot = atomicAdd(&sh.misc[1], 1);
-                if (slot < K) sh.fin[slot] = p.sort_by_key ? ck : static_cast<unsigned long long>(c);
+    if (b1 >= 0) {
+        // every candidate shares the key's top 12 bits (bin b1)
+        const unsigned long long known = static_cast<unsigned long long>(static_cast<uint32_t>(b1) << kBinShift) << 32;
+        unsigned long long thr;
+        if (ncand <= kCandCap) {
+            for (int i = threadIdx.x; i < ncand; i += kNT) {
+                const int c = __builtin_nontemporal_load(gcol + i);
+                sh.u.fin.key[i] = __builtin_nontemporal_load(gkey + i);
+                sh.u.fin.col[i] = c;
+                sh.u.fin.rec[i] = rec_of(p, prow, c);
+            }
+            __syncthreads();
+            auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+                key = sh.u.fin.key[i];
+                rec = sh.u.fin.rec[i];
+                return true;
+            };
+            thr = radix_select(src, ncand, need1, sh.hist8, sh.scan, 48, known);
+            for (int i = threadIdx.x; i < ncand; i += kNT)
+                if (composite(sh.u.fin.key[i], sh.u.fin.rec[i]) >= thr) take_col(sh.u.fin.col[i], sh.u.fin.key[i]);
+        } else {  // a crowded boundary bin: select from the row's list
+            auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+                key = __builtin_nontemporal_load(gkey + i);
+                rec = rec_of(p, prow, __builtin_nontemporal_load(gcol + i));
+                return true;
+            };
+            thr = radix_select(src, ncand, need1, sh.hist8, sh.scan, 48, known);
+            for (int i = threadIdx.x; i < ncand; i += kNT) {
+                const uint32_t k = __builtin_nontemporal_load(gkey + i);
+                const int c = __builtin_nontemporal_load(gcol + i);
+                if (composite(k, rec_of(p, prow, c)) >= thr) take_col(c, k);
             }
         }
     }
     __syncthreads();
-    const int take = min(sh.misc[1], K);
+    const int take = min(sh.misc[0], K);
+    unsigned long long* fin = sh.u.fin.fin;
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    auto out_of = [&](unsigned long long v) -> int32_t {
+        return p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(v)) : rec_of(p, prow, static_cast<int>(v));
+    };
+    for (int i = take + threadIdx.x; i < K; i += kNT) orow[i] = -1;
+    if (take <= 1024) {
+        // rank by counting: the values are unique, so an element's place is
+        // the number of values ahead of it (all lanes read the same LDS
+        // word at each step)
+        for (int i = threadIdx.x; i < take; i += kNT) {
+            const unsigned long long v = fin[i];
+            int r = 0;
+            for (int jj = 0; jj < take; ++jj) {
+                const unsigned long long w = fin[jj];
+                r += p.sort_by_key ? (w > v) : (w < v);
+            }
+            orow[r] = out_of(v);
+        }
+        return;
+    }
     int m2 = 1;
     while (m2 < take) m2 <<= 1;
     // pad so the padding sorts last: descending by key, ascending by column
-    for (int i = take + threadIdx.x; i < m2; i += kNT) sh.fin[i] = p.sort_by_key ? 0ull : ~0ull;
+    for (int i = take + threadIdx.x; i < m2; i += kNT) fin[i] = p.sort_by_key ? 0ull : ~0ull;
     __syncthreads();
     for (int k = 2; k <= m2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = threadIdx.x; i < m2; i += kNT) {
                 const int ij = i ^ j;
                 if (ij > i) {
-                    const unsigned long long a = sh.fin[i], b = sh.fin[ij];
+                    const unsigned long long a = fin[i], b = fin[ij];
                     const bool first = (i & k) == 0;
                     const bool swap = p.sort_by_key ? (first ? a < b : a > b) : (first ? a > b : a < b);
-                    if (swap) { sh.fin[i] = b; sh.fin[ij] = a; }
+                    if (swap) { fin[i] = b; fin[ij] = a; }
                 }
             }
             __syncthreads();
         }
     }
-    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
-    for (int i = threadIdx.x; i < K; i += kNT) {
-        int32_t v = -1;
-        if (i < take) {
-            v = p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(sh.fin[i]))
-                              : rec_of(p, prow, static_cast<int>(sh.fin[i]));
-        }
-        orow[i] = v;
-    }
+    for (int i = threadIdx.x; i < take; i += kNT) orow[i] = out_of(fin[i]);
 }
 
 // One wave per block: beta[row][j] = max over columns [j*blk, min((j+1)*blk, N)).
@@ -479,7 +559,7 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* scores, int
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct LongLayout {
-    size_t hist, cnt, sure, cand, total;
+    size_t hist, cnt, sure, ckey, ccol, total;
 };
 
 LongLayout long_layout(int rows, int ncols, int K) {
@@ -491,7 +571,9 @@ LongLayout long_layout(int rows, int ncols, int K) {
     off += align256(static_cast<size_t>(rows) * 4 * sizeof(int));
     L.sure = off;
     off += align256(static_cast<size_t>(rows) * K * sizeof(int));
-    L.cand = off;
+    L.ckey = off;
+    off += align256(static_cast<size_t>(rows) * ncols * sizeof(uint32_t));
+    L.ccol = off;
     off += align256(static_cast<size_t>(rows) * ncols * sizeof(int));
     L.total = off;
     return L;
@@ -502,16 +584,13 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
         hipLaunchKernelGGL(topk_small_kernel<kSmallCols>, dim3(p.rows), dim3(kNT), 0, st, p);
         return static_cast<int>(hipGetLastError());
     }
-    if (p.ncols <= kMedCols) {
-        hipLaunchKernelGGL(topk_small_kernel<kMedCols>, dim3(p.rows), dim3(kNT), 0, st, p);
-        return static_cast<int>(hipGetLastError());
-    }
     const LongLayout L = long_layout(p.rows, p.ncols, p.K);
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.ghist = reinterpret_cast<int*>(base + L.hist);
     p.cnt = reinterpret_cast<int*>(base + L.cnt);
     p.sure = reinterpret_cast<int*>(base + L.sure);
-    p.cand = reinterpret_cast<int*>(base + L.cand);
+    p.ckey = reinterpret_cast<uint32_t*>(base + L.ckey);
+    p.ccol = reinterpret_cast<int*>(base + L.ccol);
     p.nchunks = (p.ncols + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(topk_zero_kernel, dim3(p.rows), dim3(kNT), 0, st, p);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
@@ -522,7 +601,7 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
 }  // namespace
 
 size_t topk_ws_bytes(int rows, int ncols, int K) {
-    if (ncols <= kMedCols) return 0;
+    if (ncols <= kSmallCols) return 0;
     return long_layout(rows, ncols, K).total;
 }
 
