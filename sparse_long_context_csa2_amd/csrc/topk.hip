@@ -76,6 +76,28 @@ __device__ __forceinline__ uint32_t key_of(const TopkP& p, const int32_t* prow, 
     return rec_of(p, prow, c) >= 0 ? k : 0u;
 }
 
+// Keys of columns c0 + i * kNT + threadIdx.x, i < N (0 past c1).  All
+// loads are issued before any key is formed: branches between a load and
+// the next would make each load wait for the one before.
+template <int N>
+__device__ __forceinline__ void load_keys(const TopkP& p, const int32_t* prow, const float* srow, int c0, int c1,
+                                          uint32_t (&kk)[N]) {
+    float sv[N];
+    int pv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c = min(c0 + i * kNT + static_cast<int>(threadIdx.x), c1 - 1);
+        sv[i] = srow[c];
+        pv[i] = prow ? prow[c / p.blk] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c = c0 + i * kNT + static_cast<int>(threadIdx.x);
+        const uint32_t k = score_key(sv[i]);
+        kk[i] = (c < c1 && pv[i] >= 0) ? k : 0u;
+    }
+}
+
 __device__ __forceinline__ unsigned long long composite(uint32_t key, int rec) {
     return (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(rec));
 }
@@ -208,10 +230,15 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
 
     int nvalid = 0;
-    for (int c = threadIdx.x; c < n; c += kNT) {
-        const uint32_t k = key_of(p, prow, srow, c);
-        sh.keys[c] = k;
-        nvalid += k != 0u;
+    for (int c0 = 0; c0 < n; c0 += 4 * kNT) {  // four keys per thread per round, loads issued together
+        uint32_t kk[4];
+        load_keys(p, prow, srow, c0, n, kk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + i * kNT + static_cast<int>(threadIdx.x);
+            if (c < n) sh.keys[c] = kk[i];
+            nvalid += kk[i] != 0u;
+        }
     }
     for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = 0;
     int total;
@@ -311,6 +338,21 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
 
 // ---------------------------------------------------------------- long rows
 
+// The row lists that the workgroups of a row hand to its last workgroup
+// are written and read as device-scope relaxed atomics: those bypass the
+// per-XCD L2s, so the hand-off needs only this wave's stores to be
+// complete before the ticket -- not a device-wide fence, which on this
+// chip writes back and invalidates the whole L2.
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }  // vmcnt(0)
+
 // Slot for this lane in a list appended to through *counter, one atomic
 // per wave (ballot, then this lane's rank among the appending lanes).
 __device__ __forceinline__ int wave_append(int* counter, bool pred) {
@@ -341,11 +383,7 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
     // the chunk's keys first, all loads in flight at once
     uint32_t kk[kChunk / kNT];
-#pragma unroll
-    for (int i = 0; i < kChunk / kNT; ++i) {
-        const int c = c0 + i * kNT + threadIdx.x;
-        kk[i] = c < c1 ? key_of(p, prow, srow, c) : 0u;
-    }
+    load_keys(p, prow, srow, c0, c1, kk);
     for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -392,11 +430,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
 
     // the chunk's keys and the row histogram, all loads in flight at once
     uint32_t kk[kChunk / kNT];
-#pragma unroll
-    for (int i = 0; i < kChunk / kNT; ++i) {
-        const int c = c0 + i * kNT + threadIdx.x;
-        kk[i] = c < c1 ? key_of(p, prow, srow, c) : 0u;
-    }
+    load_keys(p, prow, srow, c0, c1, kk);
     const int* g = p.ghist + static_cast<size_t>(row) * kBins;
     for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = g[i];
     if (threadIdx.x == 0) {
@@ -434,16 +468,15 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     __syncthreads();
     const int gbase = sh.misc[2], sbase = sh.misc[3];
     for (int i = threadIdx.x; i < nloc; i += kNT) {
-        gkey[gbase + i] = sh.u.chunk.key[i];
-        gcol[gbase + i] = sh.u.chunk.col[i];
+        st_dev(gkey + gbase + i, sh.u.chunk.key[i]);
+        st_dev(gcol + gbase + i, sh.u.chunk.col[i]);
     }
-    for (int i = threadIdx.x; i < nsu; i += kNT) sure[sbase + i] = sh.u.chunk.sure[i];
-    __threadfence();
+    for (int i = threadIdx.x; i < nsu; i += kNT) st_dev(sure + sbase + i, sh.u.chunk.sure[i]);
+    wait_stores();  // this wave's list entries are visible device-wide
     __syncthreads();
     if (threadIdx.x == 0) sh.misc[2] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
     __syncthreads();
     if (!sh.misc[2]) return;
-    __threadfence();
 
     // ---- last workgroup of this row: resolve the boundary bin ----
     const int ncand = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
@@ -456,7 +489,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
             sh.u.fin.fin[slot] = p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
     };
     for (int i = threadIdx.x; i < nsure; i += kNT) {
-        const int c = __builtin_nontemporal_load(sure + i);
+        const int c = ld_dev(sure + i);
         take_col(c, p.sort_by_key ? key_of(p, prow, srow, c) : 0u);
     }
     if (b1 >= 0) {
@@ -465,8 +498,8 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         unsigned long long thr;
         if (ncand <= kCandCap) {
             for (int i = threadIdx.x; i < ncand; i += kNT) {
-                const int c = __builtin_nontemporal_load(gcol + i);
-                sh.u.fin.key[i] = __builtin_nontemporal_load(gkey + i);
+                const int c = ld_dev(gcol + i);
+                sh.u.fin.key[i] = ld_dev(gkey + i);
                 sh.u.fin.col[i] = c;
                 sh.u.fin.rec[i] = rec_of(p, prow, c);
             }
@@ -481,14 +514,14 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 if (composite(sh.u.fin.key[i], sh.u.fin.rec[i]) >= thr) take_col(sh.u.fin.col[i], sh.u.fin.key[i]);
         } else {  // a crowded boundary bin: select from the row's list
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
-                key = __builtin_nontemporal_load(gkey + i);
-                rec = rec_of(p, prow, __builtin_nontemporal_load(gcol + i));
+                key = ld_dev(gkey + i);
+                rec = rec_of(p, prow, ld_dev(gcol + i));
                 return true;
             };
             thr = radix_select(src, ncand, need1, sh.hist8, sh.scan, 48, known);
             for (int i = threadIdx.x; i < ncand; i += kNT) {
-                const uint32_t k = __builtin_nontemporal_load(gkey + i);
-                const int c = __builtin_nontemporal_load(gcol + i);
+                const uint32_t k = ld_dev(gkey + i);
+                const int c = ld_dev(gcol + i);
                 if (composite(k, rec_of(p, prow, c)) >= thr) take_col(c, k);
             }
         }
