@@ -89,6 +89,31 @@ def _check(code: int) -> None:
         raise CSA2Error(code, lib().csa2_status_str(code).decode())
 
 
+class Prepared:
+    """One entry-point call with its arguments converted to ctypes values
+    once; calling it enqueues the same work again (same tensors, same
+    stream) with almost no host cost per launch."""
+
+    def __init__(self, cfunc, args, result=None, keep=()):
+        self._f = cfunc
+        self._args = tuple(t(a) if a is not None else None for t, a in zip(cfunc.argtypes, args))
+        self.result = result
+        self._keep = keep  # buffers the call uses that no caller holds (an allocated workspace)
+
+    def __call__(self):
+        code = self._f(*self._args)
+        if code != CSA2_OK:
+            _check(code)
+        return self.result
+
+
+def _call(cfunc, args, result, prepare: bool, keep=()):
+    if prepare:
+        return Prepared(cfunc, args, result, keep)
+    _check(cfunc(*args))
+    return result
+
+
 def dtype_code(t: Optional[torch.Tensor]) -> int:
     if t is None:
         return F32
@@ -124,21 +149,23 @@ def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tenso
 
 
 def csa2_index_scores(q_idx, w, k_idx, k_scale, q_pos, m: int, n_rec=None, pool=None, blk: int = 0,
-                      out=None, stream=None) -> torch.Tensor:
-    """Scores [B][Tq][N] (or [B][Tq][P*blk] with a pool); see csa2.h."""
+                      out=None, stream=None, prepare: bool = False) -> torch.Tensor:
+    """Scores [B][Tq][N] (or [B][Tq][P*blk] with a pool); see csa2.h.
+    With ``prepare`` the call is returned as a ``Prepared`` instead of
+    being enqueued (likewise for the other entry points)."""
     B, Tq, Hi, Di = q_idx.shape
     N = k_idx.shape[1]
     P = 0 if pool is None else pool.shape[-1]
     ncols = N if pool is None else P * blk
     if out is None:
         out = torch.empty((B, Tq, ncols), dtype=torch.float32, device=q_idx.device)
-    _check(lib().csa2_index_scores(B, Tq, N, Hi, Di, m, _p(q_idx), dtype_code(q_idx), _p(w), _p(k_idx),
-                                   _p(k_scale), dtype_code(k_idx), _p(q_pos), _p(n_rec), _p(pool), P,
-                                   blk if pool is not None else 0, _p(out), None, 0, _stream(stream)))
-    return out
+    return _call(lib().csa2_index_scores,
+                 (B, Tq, N, Hi, Di, m, _p(q_idx), dtype_code(q_idx), _p(w), _p(k_idx), _p(k_scale),
+                  dtype_code(k_idx), _p(q_pos), _p(n_rec), _p(pool), P, blk if pool is not None else 0, _p(out),
+                  None, 0, _stream(stream)), out, prepare)
 
 
-def csa2_block_pool(scores, blk: int, P: int, out=None, ws=None, stream=None) -> torch.Tensor:
+def csa2_block_pool(scores, blk: int, P: int, out=None, ws=None, stream=None, prepare: bool = False) -> torch.Tensor:
     """Block ids [rows][P] ordered by (block max desc, id asc), -1 padded."""
     N = scores.shape[-1]
     rows = scores.numel() // N
@@ -146,11 +173,12 @@ def csa2_block_pool(scores, blk: int, P: int, out=None, ws=None, stream=None) ->
         out = torch.empty(scores.shape[:-1] + (P,), dtype=torch.int32, device=scores.device)
     nb = lib().csa2_block_pool_workspace_bytes(rows, N, blk)
     ws = _ws(nb, scores.device, ws)
-    _check(lib().csa2_block_pool(rows, N, blk, P, _p(scores), _p(out), _p(ws), nb, _stream(stream)))
-    return out
+    return _call(lib().csa2_block_pool, (rows, N, blk, P, _p(scores), _p(out), _p(ws), nb, _stream(stream)), out,
+                 prepare, (ws,))
 
 
-def csa2_topk(scores, K: int, pool=None, blk: int = 0, out=None, ws=None, stream=None) -> torch.Tensor:
+def csa2_topk(scores, K: int, pool=None, blk: int = 0, out=None, ws=None, stream=None,
+              prepare: bool = False) -> torch.Tensor:
     """Record ids [rows][K] of the K best scores (set, column order), -1 padded."""
     ncols = scores.shape[-1]
     rows = scores.numel() // ncols
@@ -159,14 +187,13 @@ def csa2_topk(scores, K: int, pool=None, blk: int = 0, out=None, ws=None, stream
         out = torch.empty(scores.shape[:-1] + (K,), dtype=torch.int32, device=scores.device)
     nb = lib().csa2_topk_workspace_bytes(rows, ncols, K)
     ws = _ws(nb, scores.device, ws)
-    _check(lib().csa2_topk(rows, ncols, K, _p(scores), _p(pool), P, blk if pool is not None else 0, _p(out),
-                           _p(ws), nb, _stream(stream)))
-    return out
+    return _call(lib().csa2_topk, (rows, ncols, K, _p(scores), _p(pool), P, blk if pool is not None else 0, _p(out),
+                                   _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
 
 def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, rope_dims: int,
                      rope_base: float = 10000.0, sm_scale: float = 0.0, out=None, ws=None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, prepare: bool = False) -> torch.Tensor:
     """Attention output [B][Tq][H][D] float32; see csa2.h."""
     B, Tq, H, D = q.shape
     N = kv.shape[1]
@@ -176,11 +203,10 @@ def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, 
         out = torch.empty((B, Tq, H, D), dtype=torch.float32, device=q.device)
     nb = lib().csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W)
     ws = _ws(nb, q.device, ws)
-    _check(lib().csa2_sparse_attn(B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale),
-                                  dtype_code(kv), _p(idx), _p(swa), _p(swa_scale), dtype_code(swa), S, W,
-                                  _p(q_pos), _p(sink), float(sm_scale), rope_dims, float(rope_base), _p(out),
-                                  _p(ws), nb, _stream(stream)))
-    return out
+    return _call(lib().csa2_sparse_attn,
+                 (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(idx), _p(swa),
+                  _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,
+                  float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
 
 def make_layer_desc(mode: str, shared: dict, layer: dict, idx_inout, pool_inout, out, ws=None) -> LayerDesc:
