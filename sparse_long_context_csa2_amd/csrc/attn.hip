@@ -57,7 +57,10 @@ constexpr int kTile = 32;
 constexpr int kMaxKList = 2048;
 constexpr int kMaxRope = kD / 2;
 constexpr int kMaxSplits = 32;
-constexpr float kJump = 64.f;  // log2 units: largest probability is 2^kJump
+constexpr float kJump = 64.f;
+// sched_barrier mask: VALU, SALU and transcendental instructions may be
+// scheduled across; memory and MFMA instructions keep their order
+constexpr int kMayCross = 0x0002 | 0x0004 | 0x0400;  // log2 units: largest probability is 2^kJump
 
 struct AttnP {
     int B, Tq, N, K, S, W, nsplit, per_split;
@@ -137,35 +140,53 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(uint32_t lo, uint32_t hi) 
     return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(h) << 32) | l);
 }
 
-constexpr int kNBuf = 3;    // tiles in flight: computing t, landing t+1 and t+2
 constexpr int kWaves = 4;   // one wave per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kIdsPerThread = kMaxKList / kThreads;
 constexpr int kRowsPerWave = kTile / kWaves;  // tile rows each wave copies
+constexpr int kStagePitch = 1040;  // finish: padded LDS row (bytes) staging 256 f32 channels
 
 template <int KVDT>
 struct __align__(16) AttnShared {
+    // tile buffers: P.V on tile t, S^T on t+1, copies of t+2 (and, for
+    // bf16, t+3) in flight
+    static constexpr int kNB = (KVDT == DT_BF16) ? 4 : 3;
     static constexpr int kScaled = (KVDT == DT_E4M3) ? kMaxEnt : 4;
-    uint8_t xb[kNBuf][kBuf];                // tile buffers (row-major: entry, channel)
+    // bf16 keeps the compacted id list in the last tile buffer: it is only
+    // live while an item is set up, when no copy is in flight
+    static constexpr int kListOwn = (KVDT == DT_BF16) ? 4 : kMaxKList;
+    uint8_t xb[kNB][kBuf];                  // tile buffers (row-major: entry, channel)
     uint64_t eptr[kMaxEnt];                 // row address of each entry of the work item
     float ezf[kScaled];                     // e4m3: logit factor sm * log2(e) * row scale
     float epf[kScaled];                     // e4m3: row scale (weights the probability)
-    int32_t list[kMaxKList];                // compacted valid record ids
+    int32_t list_own[kListOwn];             // compacted valid record ids (e4m3)
     float rope_cs[kMaxRope][2];
     double rope_inv[kMaxRope];              // base^(-2j/r), once per workgroup
     int cnt[kIdsPerThread][kWaves];         // valid ids per (chunk, wave)
+    __device__ __forceinline__ int32_t* list() {
+        if constexpr (KVDT == DT_BF16) return reinterpret_cast<int32_t*>(xb[kNB - 1]);
+        else return list_own;
+    }
 };
 
-// The next work item's slice of the index row, fetched into registers
-// while the current item runs.
+// The next work item's inputs, fetched into registers while the current
+// item runs: its slice of the index row, its position and the wave's query
+// fragments (head h, k-step i covering channels 32i .. 32i+31, lane group
+// g taking 8 of them).
 struct ItemFetch {
     int ids[kIdsPerThread];
+    int64_t t;
+    bf16x8 q[16];
 };
 
 // Work items are (query, split) pairs; with one split, item i is query
 // Q-1-i so that later positions (more entries) come first.  Persistent
-// workgroup g takes the items of round r at r*G + g for even r and
-// r*G + G-1-g for odd r, which evens out the per-workgroup totals.
+// workgroup g takes the item of round r at r*G + g for even r and
+// r*G + G-1-g for odd r, which evens out the per-workgroup totals.  It
+// walks the rounds starting at round g mod R (wrapping): workgroups that
+// all finished an item at the same moment would write their outputs in one
+// burst that saturates HBM while the matrix units idle; staggered starts
+// spread those writes over the run.
 __device__ __forceinline__ int item_of(int round, int g, int G) {
     return round * G + ((round & 1) ? (G - 1 - g) : g);
 }
@@ -188,8 +209,9 @@ __device__ __forceinline__ int item_of(int round, int g, int G) {
 //    g at X[4g + s/4][d0 + 4(s%4) ..] hands lane j the four entries
 //    4g..4g+3 of channel d0 + j -- the MFMA A operand;
 //  * logits are kept in log2 units (exp2 on the VALU).
-// While an item runs, the next item's slice of the index row is loaded
-// into registers, so compaction starts without a global round trip.
+// While an item runs, the next item's index slice, position and query
+// fragments are loaded into registers, so an item starts without waiting
+// for global memory.
 template <int KVDT>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     __shared__ AttnShared<KVDT> sh;
@@ -221,36 +243,109 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             const int c = j * kThreads + tid;
             f.ids[j] = (j < nids && c < p.K) ? irow[c] : -1;
         }
+        f.t = p.q_pos[qr];
+        const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f.q[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * i + g)));
     };
 
     // the pow() is far costlier than the per-item angle, so it runs once
     for (int i = tid; i < p.rope_dims / 2; i += kThreads) sh.rope_inv[i] = rope_inv_freq(i, p.rope_dims, p.rope_base);
 
+    const float sk = p.sink[h] * kLog2e;  // the head's sink logit, log2 units
     ItemFetch nx;
-    int round = 0;
-    int item = item_of(0, blockIdx.x, G);
+    const int R = (n_items + G - 1) / G;  // rounds
+    const int rot = static_cast<int>(blockIdx.x) % R;
+    int k_next = 0;  // position in this workgroup's round order
+    auto next_item = [&]() -> int {
+        while (k_next < R) {
+            const int r = k_next + rot < R ? k_next + rot : k_next + rot - R;
+            ++k_next;
+            const int it = item_of(r, blockIdx.x, G);
+            if (it < n_items) return it;  // only the last round is partial
+        }
+        return n_items;
+    };
+    int item = next_item();
     if (item < n_items) fetch(item, nx);
+
+    // Output of an item.  It runs once the next item's first tile copies
+    // are in flight (its stores then drain while those copies land), so O,
+    // m and l persist across items.  O leaves through LDS: each wave stages
+    // its 16 heads, 256 channels at a time, in the last two tile buffers (the
+    // next item's first copies target the first two; rows padded so the
+    // lanes of one write pass hit distinct banks), and every global store
+    // then writes 1 KB of one head's row.  The wave's 16 output rows are
+    // contiguous in both the final output and the split partials.
+    f32x4 acc[32];
+    float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
+    float l_run = 0.f;                     // this lane's share of the running sum
+    int prev_qr = -1, prev_split = 0;      // the item whose output is pending
+    auto finish = [&](int qr_f, int split_f) {
+        float f = 1.f;  // normalisation (one split) or none (partials)
+        float* dst;
+        if (p.nsplit == 1) {
+            const float a = fmaxf(m_run, sk);
+            f = 0.f;
+            if (a != -__builtin_huge_valf()) {
+                const float em = __builtin_amdgcn_exp2f(m_run - a);
+                const float es = __builtin_amdgcn_exp2f(sk - a);
+                const float den = l_run * em + es;
+                f = den > 0.f ? em / den : 0.f;
+            }
+            dst = p.out + (static_cast<size_t>(qr_f) * kH + 16 * wave) * kD;
+        } else {
+            const size_t slot0 = (static_cast<size_t>(qr_f) * p.nsplit + split_f) * kH + 16 * wave;
+            dst = p.part_o + slot0 * kD;
+            if (g == 0) {
+                p.part_ml[2 * (slot0 + l16)] = m_run;  // log2 units
+                p.part_ml[2 * (slot0 + l16) + 1] = l_run;
+            }
+        }
+        // rotary channels [r0, kD) get the inverse rotation (one split
+        // only).  In the read-back layout a lane keeps the same 4 channels
+        // for all 16 rows, so it fetches its two rotations once per half.
+        const int r0 = p.nsplit == 1 ? kD - p.rope_dims : kD;
+        static_assert(kWaves * 16 * kStagePitch <= 2 * kBuf, "staging fits the last two tile buffers");
+        uint8_t* stage = &sh.xb[AttnShared<KVDT>::kNB - 2][0] + wave * 16 * kStagePitch;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                *reinterpret_cast<f32x4*>(stage + l16 * kStagePitch + 4 * (16 * u + 4 * g)) = acc[16 * half + u] * f;
+            const int c0 = 256 * half + 4 * lane;  // this lane's channels c0 .. c0+3
+            const bool rot0 = c0 >= r0, rot1 = c0 + 2 >= r0;
+            const int j0 = rot0 ? (c0 - r0) >> 1 : 0, j1 = rot1 ? (c0 + 2 - r0) >> 1 : 0;
+            const float cs0 = sh.rope_cs[j0][0], sn0 = sh.rope_cs[j0][1];
+            const float cs1 = sh.rope_cs[j1][0], sn1 = sh.rope_cs[j1][1];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows visible to the wave
+            f32x4 rows[16];  // all reads in flight at once
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rows[r] = *reinterpret_cast<const f32x4*>(stage + r * kStagePitch + 16 * lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                f32x4 v = rows[r];
+                const float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
+                v[0] = rot0 ? x0 * cs0 + y0 * sn0 : x0;
+                v[1] = rot0 ? -x0 * sn0 + y0 * cs0 : y0;
+                v[2] = rot1 ? x1 * cs1 + y1 * sn1 : x1;
+                v[3] = rot1 ? -x1 * sn1 + y1 * cs1 : y1;
+                *reinterpret_cast<f32x4*>(dst + r * kD + 256 * half + 4 * lane) = v;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites
+        }
+    };
+
 
     while (item < n_items) {
         const int qr = query_of(item);
         const int split = p.nsplit == 1 ? 0 : item % p.nsplit;
         const int b = qr / p.Tq;
-        const int64_t t = p.q_pos[qr];
+        const int64_t t = nx.t;
         const int rd = p.rope_dims;
-        // query fragments of head h, k-step i covering channels 32i .. 32i+31
-        // (lane group g takes 8 of them); issued first so that their latency
-        // overlaps the set-up below
         bf16x8 qf[16];
-        {
-            const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) qf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * i + g)));
-            // held in accumulation registers (the MFMA reads its B operand
-            // from there): the architectural VGPRs stay free for the tile
-            // operands, so LDS reads can run further ahead of the MFMAs
-#pragma unroll
-            for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(qf[i]));
-        }
+        for (int i = 0; i < 16; ++i) qf[i] = nx.q[i];
 
         // ---- compact the valid selected records (in order) ----
         int ok_bits = 0;
@@ -274,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 for (int w = 0; w < kWaves; ++w) before += (w < wave) ? sh.cnt[j][w] : 0;
                 const bool ok = (ok_bits >> j) & 1;
                 const unsigned long long bal = __ballot(ok);
-                if (ok) sh.list[nsel + before + __popcll(bal & ((1ull << lane) - 1ull))] = nx.ids[j];
+                if (ok) sh.list()[nsel + before + __popcll(bal & ((1ull << lane) - 1ull))] = nx.ids[j];
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) nsel += sh.cnt[j][w];
             }
@@ -295,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             const uint8_t* rp;
             float sc = 1.f;
             if (ge < nsel) {
-                const size_t r = static_cast<size_t>(b) * p.N + sh.list[ge];
+                const size_t r = static_cast<size_t>(b) * p.N + sh.list()[ge];
                 if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
                 rp = p.kv + r * kRowBytes;
             } else {
@@ -336,8 +431,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
                 for (int i = 0; i < kRowsPerWave; i += 2) {
                     const u32x4 pa = ep[i / 2];
-                    stg[i] = *reinterpret_cast<const Raw*>(uniform_ptr(pa[0], pa[1]) + 8 * lane);
-                    stg[i + 1] = *reinterpret_cast<const Raw*>(uniform_ptr(pa[2], pa[3]) + 8 * lane);
+                    // global (not flat) loads: a flat load would also count
+                    // against the LDS wait counter, so every LDS wait would
+                    // wait for these staging loads as well
+                    typedef const __attribute__((address_space(1))) Raw GRaw;
+                    stg[i] = *(GRaw*)(uniform_ptr(pa[0], pa[1]) + 8 * lane);
+                    stg[i + 1] = *(GRaw*)(uniform_ptr(pa[2], pa[3]) + 8 * lane);
                 }
             }
         };
@@ -351,82 +450,97 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             }
         };
 
-        float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
-        float l_run = 0.f;                     // this lane's share of the running sum
-        f32x4 acc[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // next item's index slice first: the copies below are then the newest
-        // loads, as the copy waits in the loop assume
-        const int nxt = item_of(round + 1, blockIdx.x, G);
-        if (nxt < n_items) fetch(nxt, nx);
+        // Pipeline over tiles: iteration t runs the P.V of tile t with the
+        // S^T and the softmax of tile t+1 interleaved (independent work in one
+        // basic block, so the matrix units stay busy while the LDS reads and
+        // the VALU softmax proceed).  Copies run two tiles ahead of the S^T:
+        // bf16 copies tile t+3 into tile t-1's buffer (4 buffers); e4m3
+        // stages the next tile in registers (3 buffers).
+        //
+        // Each head keeps a reference max, set by the first tile: it only
+        // moves when a tile exceeds it by more than kJump (log2 units), so
+        // probabilities stay below 2^kJump and the usual per-tile rescale of
+        // O and l happens only on such a (rare) move.
+        constexpr int NB = AttnShared<KVDT>::kNB;
+        const int nxt = next_item();
         if (ntile > 0) issue(0, 0);
         if constexpr (KVDT == DT_BF16) {
             if (ntile > 1) issue(1, 1);
         }
+        if (prev_qr >= 0) {
+            finish(prev_qr, prev_split);
+            lds_sync();  // every wave is done with the previous item's rope table
+        }
+        m_run = -__builtin_huge_valf();
+        l_run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (p.nsplit == 1)
             for (int i = tid; i < rd / 2; i += kThreads)
                 rope_cos_sin(t, sh.rope_inv[i], sh.rope_cs[i][0], sh.rope_cs[i][1]);
 
-        // Per tile: copies landed and the next ones issued; S^T; the tile max
-        // of each head; probabilities relative to the head's reference max;
-        // P.V.  The reference only moves when a tile exceeds it by more than
-        // kJump (log2 units), so probabilities stay below 2^kJump and O never
-        // needs a rescale in the loop.  When it does move, every earlier term
-        // weighs less than kMaxEnt * 2^-kJump relative to the new maximum --
-        // below fp32 resolution -- so O and l restart from zero, which is the
-        // rescale's result to fp32 accuracy.  (The first tile sets the
-        // reference; O and l are still zero then.)
-        int cb = 0;  // buffer of tile it
-        f32x4 s0, s1;
-        float z[8];
-        float tmax = -__builtin_huge_valf();
-        auto tile_logits = [&](int it) {
+        // tile `it` visible in LDS to every wave; the copies of the tile two
+        // ahead go out.  The next item's inputs are fetched in tile 0, after
+        // its wait and before those copies: the copy waits then cover the
+        // fetch only from tile 1 on, one tile after it was issued.
+        auto tile_ready = [&](int it) {
+            const int buf = it % NB;
             if constexpr (KVDT == DT_BF16) {
                 if (it + 1 < ntile) wait_copies_but_8();
                 else wait_copies_all();
-                lds_sync();  // every wave's rows of tile `it` landed; tile it-1 consumed
-                if (it + 2 < ntile) issue(it + 2, cb == 0 ? 2 : cb - 1);
+                lds_sync();  // tile `it` landed; the buffer two tiles ahead is free
+                if (it == 0 && nxt < n_items) fetch(nxt, nx);
+                if (it + 2 < ntile) issue(it + 2, (it + 2) % NB);
             } else {
-                land(cb);
-                if (it + 1 < ntile) issue(it + 1, cb == 2 ? 0 : cb + 1);
+                land(buf);
+                if (it == 0 && nxt < n_items) fetch(nxt, nx);
+                if (it + 1 < ntile) issue(it + 1, (it + 1) % NB);
                 lds_sync();
             }
-            const uint8_t* xb = sh.xb[cb];
-            // ---- S^T for entries 0..15 (s0, s2) and 16..31 (s1, s3) ----
-            // k-step pairs: the four row chunks of pair i+2 are read before
-            // the MFMAs of pair i (two pairs in flight hide the LDS latency)
-            f32x4 s2 = {0.f, 0.f, 0.f, 0.f}, s3 = s2;
-            s0 = s2;
-            s1 = s2;
-            const uint8_t* r0 = xb + l16 * kXPitch + 16 * g;
-            const uint8_t* r1 = r0 + 16 * kXPitch;
+        };
+        // S^T of tile `it` (entries 0..15: s[0], s[2]; 16..31: s[1], s[3]) in
+        // four steps of two k-step pairs each, which the P.V of the previous
+        // tile interleaves with its MFMAs; the row chunks of pair i+2 are
+        // read before the MFMAs of pair i (two pairs in flight hide the LDS
+        // latency).  qk_end turns the sums into z in log2 units (entries
+        // 16*mt + 4g + v of head h) and returns the head's tile max.  Padding
+        // entries repeat a real row, so they may take part in the max; only
+        // their probabilities are dropped.
+        struct Qk {
+            f32x4 s[4];
             u32x4 ka[3][4];
-            auto kload = [&](int i, u32x4* d) {
-                d[0] = *reinterpret_cast<const u32x4*>(r0 + 64 * i);
-                d[1] = *reinterpret_cast<const u32x4*>(r1 + 64 * i);
-                d[2] = *reinterpret_cast<const u32x4*>(r0 + 64 * (i + 1));
-                d[3] = *reinterpret_cast<const u32x4*>(r1 + 64 * (i + 1));
-            };
-            kload(0, ka[0]);
-            kload(2, ka[1]);
+            const uint8_t* r0;
+        };
+        auto kload = [&](const Qk& q, int i, u32x4* d) {
+            const uint8_t* r1 = q.r0 + 16 * kXPitch;
+            d[0] = *reinterpret_cast<const u32x4*>(q.r0 + 64 * i);
+            d[1] = *reinterpret_cast<const u32x4*>(r1 + 64 * i);
+            d[2] = *reinterpret_cast<const u32x4*>(q.r0 + 64 * (i + 1));
+            d[3] = *reinterpret_cast<const u32x4*>(r1 + 64 * (i + 1));
+        };
+        auto qk_begin = [&](int it, Qk& q) {
+            q.r0 = sh.xb[it % NB] + l16 * kXPitch + 16 * g;
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
+            for (int m = 0; m < 4; ++m) q.s[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kload(q, 0, q.ka[0]);
+            kload(q, 2, q.ka[1]);
+        };
+        auto qk_step = [&](Qk& q, int j) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 4 * j + 2 * e;  // k-step pair i, i+1
                 const int k = (i / 2) % 3;
-                if (i + 4 < 16) kload(i + 4, ka[(i / 2 + 2) % 3]);
-                __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
-                s0 = mfma16x16x32(as_bf16x8(ka[k][0]), qf[i], s0);
-                s1 = mfma16x16x32(as_bf16x8(ka[k][1]), qf[i], s1);
-                s2 = mfma16x16x32(as_bf16x8(ka[k][2]), qf[i + 1], s2);
-                s3 = mfma16x16x32(as_bf16x8(ka[k][3]), qf[i + 1], s3);
-                __builtin_amdgcn_sched_barrier(0);
+                if (i + 4 < 16) kload(q, i + 4, q.ka[(i / 2 + 2) % 3]);
+                q.s[0] = mfma16x16x32(as_bf16x8(q.ka[k][0]), qf[i], q.s[0]);
+                q.s[1] = mfma16x16x32(as_bf16x8(q.ka[k][1]), qf[i], q.s[1]);
+                q.s[2] = mfma16x16x32(as_bf16x8(q.ka[k][2]), qf[i + 1], q.s[2]);
+                q.s[3] = mfma16x16x32(as_bf16x8(q.ka[k][3]), qf[i + 1], q.s[3]);
             }
-            s0 += s2;
-            s1 += s3;
-            // z in log2 units, entries 16*mt + 4g + v of head h.  Padding
-            // entries repeat a real row, so they may take part in the max;
-            // only their probabilities are dropped.
+        };
+        auto qk_end = [&](int it, Qk& q, float (&z)[8]) -> float {
+            const f32x4 s0 = q.s[0] + q.s[2];
+            const f32x4 s1 = q.s[1] + q.s[3];
             if constexpr (KVDT == DT_E4M3) {
                 const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 4 * g]);
                 const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
@@ -442,51 +556,61 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     z[4 + v] = s1[v] * cz;
                 }
             }
-            tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-            tmax = max4_rows(tmax);
+            const float tm =
+                fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+            return max4_rows(tm);
         };
-        // probabilities relative to m_run, l update, P.V accumulation
-        auto tile_pv = [&](int it) {
+        // Softmax of tile `it` relative to m, in eight steps that the P.V of
+        // the previous tile interleaves with its MFMAs.  Steps 0-3: two
+        // probabilities each (padding entries dropped without a branch);
+        // step 4: their sum (and the e4m3 row scales); steps 4-7: one packed
+        // pair each of P = hi + lo in bf16 (hi is P rounded, lo the rounding
+        // error).
+        struct Soft {
             float pr[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_run);
-            const int lim = nvalid - it * kTile;  // entries of this tile that are real
-            if (lim < kTile) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    if (4 * g + v >= lim) pr[v] = 0.f;
-                    if (16 + 4 * g + v >= lim) pr[4 + v] = 0.f;
-                }
-            }
-            l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-            if constexpr (KVDT == DT_E4M3) {  // value rows carry their scale
-                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
-                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    pr[v] *= f0[v];
-                    pr[4 + v] *= f1[v];
-                }
-            }
-            // P = hi + lo, both bf16: hi is P rounded, lo the rounding error
+            float psum;
             uint32_t phi[4], plo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t hi = cvt_bf16x2(pr[2 * i], pr[2 * i + 1]);
-                phi[i] = hi;
-                plo[i] = cvt_bf16x2(pr[2 * i] - __uint_as_float(hi << 16),
-                                    pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
+        };
+        auto soft_step = [&](int j, int it, const float (&z)[8], float m, Soft& s) {
+            if (j < 4) {
+                const int lim = nvalid - it * kTile;  // entries of this tile that are real
+                s.pr[j] = (4 * g + j < lim) ? __builtin_amdgcn_exp2f(z[j] - m) : 0.f;
+                s.pr[4 + j] = (16 + 4 * g + j < lim) ? __builtin_amdgcn_exp2f(z[4 + j] - m) : 0.f;
+                // computed here, in the MFMA shadow: the results are only read
+                // after the loop's branch, past which the compiler would sink them
+                asm volatile("" : "+v"(s.pr[j]), "+v"(s.pr[4 + j]));
+                return;
             }
-            const bf16x8 bhi = as_bf16x8(u32x4{phi[0], phi[1], phi[2], phi[3]});
-            const bf16x8 blo = as_bf16x8(u32x4{plo[0], plo[1], plo[2], plo[3]});
-            // ---- O^T += X^T P^T : channels 16*u + 4g + v, head h ----
-            // transposing-read source: lane s of group g -> row 4g + s/4 (and
-            // 16 + ...), channels d0 + 4(s%4) .. +3
-            const uint8_t* xb = sh.xb[cb];
+            if (j == 4) {
+                s.psum = ((s.pr[0] + s.pr[1]) + (s.pr[2] + s.pr[3])) + ((s.pr[4] + s.pr[5]) + (s.pr[6] + s.pr[7]));
+                if constexpr (KVDT == DT_E4M3) {
+                    const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
+                    const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        s.pr[v] *= f0[v];
+                        s.pr[4 + v] *= f1[v];
+                    }
+                }
+            }
+            const int i = j - 4;
+            const uint32_t hi = cvt_bf16x2(s.pr[2 * i], s.pr[2 * i + 1]);
+            s.phi[i] = hi;
+            s.plo[i] = cvt_bf16x2(s.pr[2 * i] - __uint_as_float(hi << 16),
+                                  s.pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
+            asm volatile("" : "+v"(s.phi[i]), "+v"(s.plo[i]));
+            if (j == 4) asm volatile("" : "+v"(s.psum));
+        };
+        auto packed = [](const uint32_t (&w)[4]) { return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}); };
+        // O^T += X^T P^T for tile `it`: channels 16*u + 4g + v, head h.  The
+        // transposing read: lane s of group g -> row 4g + s/4 (and 16 + ...),
+        // channels d0 + 4(s%4) .. +3; the operands of channel group k+1 are
+        // read before the MFMAs of group k.  side(step) runs between the
+        // MFMAs of each of the eight channel groups.
+        auto tile_pv = [&](int it, const bf16x8& bhi, const bf16x8& blo, auto&& side) {
+            const uint8_t* xb = sh.xb[it % NB];
             const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3);
             const uint8_t* tr1 = tr0 + 16 * kXPitch;
-            // channel groups of 4 x 16: the operands of group k+1 are read
-            // before the MFMAs of group k
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             bf16x8 va[2][4];
             auto vload = [&](int uh, bf16x8* d) {
@@ -509,77 +633,82 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], bhi, acc[uh + u]);
+                side(uh / 4);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], blo, acc[uh + u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            cb = (cb == 2) ? 0 : cb + 1;
         };
 
-        for (int it = 0; it < ntile; ++it) {
-            tile_logits(it);
-            const bool jump = tmax > m_run + kJump;
-            if (__any(jump && m_run != -__builtin_huge_valf())) {  // rare
-                if (jump) {
+        bf16x8 bhi, blo;  // P of the tile whose P.V comes next
+        if (ntile > 0) {
+            float z[8];
+            Soft s;
+            Qk q;
+            tile_ready(0);
+            qk_begin(0, q);
 #pragma unroll
-                    for (int u = 0; u < 32; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    l_run = 0.f;
-                }
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                qk_step(q, j);
             }
-            m_run = jump ? tmax : m_run;
-            tile_pv(it);
+            m_run = qk_end(0, q, z);  // the first tile sets the reference
+#pragma unroll
+            for (int j = 0; j < 8; ++j) soft_step(j, 0, z, m_run, s);
+            l_run = s.psum;
+            bhi = packed(s.phi);
+            blo = packed(s.plo);
         }
+        // Iteration `it`: one stream of MFMAs -- the P.V of tile it, with the
+        // S^T of tile it+1 in its first half and that tile's softmax in its
+        // second half.
+        for (int it = 0; it + 1 < ntile; ++it) {
+            tile_ready(it + 1);
+            Qk q;
+            qk_begin(it + 1, q);
+            float zn[8];
+            float m_new = m_run;
+            bool jump = false;
+            Soft s;
+            tile_pv(it, bhi, blo, [&](int j) {
+                if (j < 4) {
+                    qk_step(q, j);
+                    return;
+                }
+                if (j == 4) {
+                    const float tmn = qk_end(it + 1, q, zn);
+                    jump = tmn > m_run + kJump;
+                    m_new = jump ? tmn : m_run;
+                }
+                soft_step(2 * (j - 4), it + 1, zn, m_new, s);
+                soft_step(2 * (j - 4) + 1, it + 1, zn, m_new, s);
+            });
+            if (__any(jump)) {  // rare: the reference moves; O and l follow it
+                const float sc = jump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+#pragma unroll
+                for (int u = 0; u < 32; ++u) acc[u] *= sc;
+                l_run *= sc;
+            }
+            l_run += s.psum;
+            // O stays in the accumulation registers across iterations (else
+            // the compiler keeps it in VGPRs and copies it in and out of the
+            // MFMA accumulators every tile)
+#pragma unroll
+            for (int u = 0; u < 32; ++u) asm volatile("" : "+a"(acc[u]));
+            m_run = m_new;
+            bhi = packed(s.phi);
+            blo = packed(s.plo);
+        }
+        if (ntile > 0) tile_pv(ntile - 1, bhi, blo, [](int) {});
+        if (ntile == 0 && nxt < n_items) fetch(nxt, nx);
         l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
-        // the next item's fetch and every copy have landed (a wait the
-        // compiler tracks, placed before the output stores so that no later
-        // wait for the fetched registers has to cover stores as well)
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-        lds_sync();  // rope table visible; tiles, list and table no longer read
-
-        // ---- finish ----
-        if (p.nsplit == 1) {
-            const float sk = p.sink[h] * kLog2e;
-            const float a = fmaxf(m_run, sk);
-            float f = 0.f;
-            if (a != -__builtin_huge_valf()) {
-                const float em = __builtin_amdgcn_exp2f(m_run - a);
-                const float es = __builtin_amdgcn_exp2f(sk - a);
-                const float den = l_run * em + es;
-                f = den > 0.f ? em / den : 0.f;
-            }
-            float* orow = p.out + (static_cast<size_t>(qr) * kH + h) * kD;
-            const int r0 = kD - rd;
-#pragma unroll
-            for (int u = 0; u < 32; ++u) {
-                const int d = 16 * u + 4 * g;
-                f32x4 o = acc[u] * f;
-                if (d + 3 >= r0) {
-#pragma unroll
-                    for (int v = 0; v < 4; v += 2) {
-                        const int dd = d + v;
-                        if (dd >= r0) {
-                            const int jp = (dd - r0) >> 1;
-                            const float cs = sh.rope_cs[jp][0], sn = sh.rope_cs[jp][1];
-                            const float x = o[v], y = o[v + 1];
-                            o[v] = x * cs + y * sn;
-                            o[v + 1] = -x * sn + y * cs;
-                        }
-                    }
-                }
-                *reinterpret_cast<f32x4*>(orow + d) = o;
-            }
-        } else {
-            const size_t slot = (static_cast<size_t>(qr) * p.nsplit + split) * kH + h;
-            float* po = p.part_o + slot * kD;
-#pragma unroll
-            for (int u = 0; u < 32; ++u) *reinterpret_cast<f32x4*>(po + 16 * u + 4 * g) = acc[u];
-            if (g == 0) {
-                p.part_ml[2 * slot] = m_run;  // log2 units
-                p.part_ml[2 * slot + 1] = l_run;
-            }
-        }
-        ++round;
+        prev_qr = qr;
+        prev_split = split;
         item = nxt;
+    }
+    if (prev_qr >= 0) {
+        lds_sync();  // the last item's tiles are no longer read
+        finish(prev_qr, prev_split);
     }
 }
 

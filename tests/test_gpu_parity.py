@@ -269,6 +269,70 @@ def test_sparse_attn_late_dominant_entry(kdt, Tq):
             PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
 
 
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("Tq", [64, 150])
+def test_sparse_attn_rising_maximum(kdt, Tq):
+    """Logits climb in steps across the tiles of one item: tile 0 near 0,
+    tile 1 about 63.3 log2 units higher, tile 2 about 64.8 (a kernel that
+    lets its reference maximum lag by up to 64 units moves it only at tile
+    2, while tile 1's terms still weigh about 2^-1.5 each against tile 2's).
+    Every term must keep its weight when the maximum moves: dropping tiles 0
+    and 1 would move the output by about 8e-2.  Tq=64 runs the split path
+    (two splits of three tiles), Tq=150 the single-launch path."""
+    _case(f"sparse_attn rising maximum {kdt} Tq={Tq}")
+    wl, inp, idx = _rising_case(kdt, Tq)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b in range(wl.B):
+        for ti in [0, 1, Tq // 2, Tq - 1]:
+            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+
+
+def _rising_case(kdt, Tq):
+    wl = _small(B=2, Tq=Tq, N=300, K=128, W=24, swa_slots=32, decode_pos=5000, k_dtype=kdt, kv_dtype=kdt,
+                swa_dtype=kdt)
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    rng = np.random.default_rng(2026)
+    u = rng.standard_normal(wl.D)
+    u /= np.linalg.norm(u)
+    sm = 1.0 / math.sqrt(wl.D)
+    log2e = 1.0 / math.log(2.0)
+    c_top, z_top = 10.0, 64.8          # tile 2: logit z_top (log2 units) for rows c_top * u + noise
+    gq = z_top / (log2e * sm * c_top)
+    q = lay["q"].copy()
+    q[:, :, :, :] = WL.f32_to_bf16_bits((gq * u).astype(np.float32))
+    lay["q"] = q
+    # records 0..31: tile 0 (logit ~0), 32..63: tile 1 (~63), 64..95: tile 2
+    # (~65.5), 96..127: tile 3 (~0); noise orthogonal to u
+    coef = np.zeros(wl.N)
+    coef[32:64] = c_top * 63.3 / z_top
+    coef[64:96] = c_top
+    kv = sh["kv"].copy()
+    kv_scale = None if sh["kv_scale"] is None else sh["kv_scale"].copy()
+    for b in range(wl.B):
+        noise = rng.standard_normal((128, wl.D)) * 0.5
+        noise -= np.outer(noise @ u, u)
+        rows = (coef[:128, None] * u[None, :] + noise).astype(np.float32)
+        if kdt == "e4m3":
+            codes, sc = WL.quantize_rows_e4m3(rows)
+            kv[b, :128] = codes
+            kv_scale[b, :128] = sc
+        else:
+            kv[b, :128] = WL.f32_to_bf16_bits(rows)
+    sh["kv"], sh["kv_scale"] = kv, kv_scale
+    idx = np.empty((wl.B, Tq, 128), np.int32)
+    for b in range(wl.B):
+        for ti in range(Tq):
+            idx[b, ti] = np.concatenate([rng.permutation(32) + 32 * k for k in range(4)])
+    return wl, inp, idx
+
+
 @pytest.mark.parametrize("H,D,dt", [(2, 16, "f32"), (3, 48, "bf16")])
 def test_sparse_attn_generic(H, D, dt):
     _case(f"sparse_attn generic H={H} D={D} {dt}")
