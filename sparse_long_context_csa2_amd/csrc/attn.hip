@@ -170,9 +170,10 @@ struct __align__(16) AttnShared {
 };
 
 // The next work item's inputs, fetched into registers while the current
-// item runs: its slice of the index row, its position and the wave's query
-// fragments (head h, k-step i covering channels 32i .. 32i+31, lane group
-// g taking 8 of them).
+// item runs: its slice of the index row and its position (during the first
+// tile), and the wave's query fragments (head h, k-step i covering channels
+// 32i .. 32i+31, lane group g taking 8 of them) once the tile loop is done,
+// so that they occupy no registers during it.
 struct ItemFetch {
     int ids[kIdsPerThread];
     int64_t t;
@@ -244,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             f.ids[j] = (j < nids && c < p.K) ? irow[c] : -1;
         }
         f.t = p.q_pos[qr];
-        const uint16_t* qh = p.q + (static_cast<size_t>(qr) * kH + h) * kD;
+    };
+    auto fetch_q = [&](int item, ItemFetch& f) {
+        const uint16_t* qh = p.q + (static_cast<size_t>(query_of(item)) * kH + h) * kD;
 #pragma unroll
         for (int i = 0; i < 16; ++i) f.q[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * i + g)));
     };
@@ -267,7 +270,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         return n_items;
     };
     int item = next_item();
-    if (item < n_items) fetch(item, nx);
+    if (item < n_items) {
+        fetch(item, nx);
+        fetch_q(item, nx);
+    }
 
     // Output of an item.  It runs once the next item's first tile copies
     // are in flight (its stores then drain while those copies land), so O,
@@ -343,9 +349,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         const int b = qr / p.Tq;
         const int64_t t = nx.t;
         const int rd = p.rope_dims;
-        bf16x8 qf[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) qf[i] = nx.q[i];
+        bf16x8 qf[16];  // filled from nx just before the first S^T (its loads land meanwhile)
 
         // ---- compact the valid selected records (in order) ----
         int ok_bits = 0;
@@ -640,6 +644,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             }
         };
 
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qf[i] = nx.q[i];
         bf16x8 bhi, blo;  // P of the tile whose P.V comes next
         if (ntile > 0) {
             float z[8];
@@ -701,6 +707,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         }
         if (ntile > 0) tile_pv(ntile - 1, bhi, blo, [](int) {});
         if (ntile == 0 && nxt < n_items) fetch(nxt, nx);
+        if (nxt < n_items) fetch_q(nxt, nx);
         l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
         prev_qr = qr;
         prev_split = split;
