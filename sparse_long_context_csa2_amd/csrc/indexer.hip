@@ -217,191 +217,171 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
 
 // Prefill scoring: many query tokens of one sequence against the records
 // they may see -- a causal GEMM (tokens x heads) x 128 x records with a
-// ReLU and weighted head-sum epilogue.  32x32x16 MFMAs: M = the 32 heads of
-// one token, N = 32 records, K = 128 dims in 8 k-steps.  A workgroup takes
-// kPfTok consecutive tokens (kPfTokW per wave, their query fragments and
-// head weights in registers) and streams the 32-record key tiles they can
-// see through LDS (double-buffered, fetched two tiles ahead); each lane
-// ends a tile holding 16 heads of one record, so the head sum is a short
-// tree and one lane swap.  The grid is (column chunk of kPfChunk, token
-// block): later token blocks see more records, and the chunks keep the
-// longest workgroup short.  Scores collect in LDS and leave in whole rows
-// at the end: no global store sits in the tile loop, so the waits for the
-// key prefetches stay exact.
-constexpr int kPfTokW = 2;             // tokens per wave
-constexpr int kPfTok = 4 * kPfTokW;    // tokens per workgroup
-constexpr int kPfRec = 32;             // records per tile
-constexpr int kPfPitch = kDi + 8;      // bf16 per LDS key row: 272 B keeps 16 lanes' reads on distinct banks
-constexpr int kPfChunk = 512;          // score columns per workgroup
+// ReLU and weighted head-sum epilogue.  Records are stationary: a
+// workgroup owns kP2Rec consecutive records, converts their keys to bf16
+// in LDS once, and its waves stream query tokens past them, each token's
+// query fragments read straight from global memory by the one wave that
+// scores it.  32x32x16 MFMAs: M = the 32 heads of the token, N = 32
+// records, K = 128 dims in 8 k-steps.  Lane group kg takes dims
+// 64 kg + 8 ks .. +7 at k-step ks in both operands, so a lane's query
+// fragments are 128 contiguous bytes of one head row.  Records come in
+// pairs of 32-record sets: after the epilogue one lane swap leaves lane l
+// holding the score of record 64 sp + l, and a wave stores 256 contiguous
+// bytes.  Sets that the token cannot see at all are skipped.
+constexpr int kP2Rec = 256;            // records per workgroup
+constexpr int kP2TokW = 8;             // tokens per wave
+constexpr int kP2Tok = 4 * kP2TokW;    // tokens per workgroup
+constexpr int kP2Pitch = kDi * 2 + 16; // bytes per LDS key row: conflict-free operand reads
 
 template <int KDT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void idx_prefill_kernel(IdxP p) {
-    __shared__ __align__(16) uint16_t kt[2][kPfRec * kPfPitch];
-    __shared__ float kts[2][kPfRec];
-    __shared__ __align__(16) float scs[kPfTok][kPfChunk];
-    __shared__ __align__(16) float wl[kPfTok][kHi];
+__global__ __launch_bounds__(256, 2) void idx_prefill_kernel(IdxP p) {
+    __shared__ __align__(16) uint8_t kl[kP2Rec * kP2Pitch];
+    __shared__ float ksl[kP2Rec];
     constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    constexpr int kPairs = kP2Rec / 64;  // 64-record set pairs of the group
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int j = lane & 31;   // record within the tile (B and C column)
+    const int j = lane & 31;   // record within a set (B and C column), head (A row)
     const int kg = lane >> 5;  // k group
-    // Workgroup L runs on XCD L % 8 (round-robin dispatch).  The column
-    // chunks of one token block get ids that are equal mod 8, so its query
-    // rows are fetched into one L2 and shared; later token blocks (more
-    // visible records) come first.
-    const int gps = (p.Tq + kPfTok - 1) / kPfTok;
-    const int nblk = p.B * gps;
-    const int nch = (p.ncols + kPfChunk - 1) / kPfChunk;
+    // Workgroup L runs on XCD L % 8 (round-robin dispatch).  The record
+    // groups of one token block get ids that are equal mod 8 and adjacent in
+    // that XCD's order, so the block's query rows are read into one L2;
+    // later token blocks (more visible records) come first.
+    const int ntb = (p.Tq + kP2Tok - 1) / kP2Tok;
+    const int nblk = p.B * ntb;
+    const int ngr = (p.ncols + kP2Rec - 1) / kP2Rec;
     const int L = static_cast<int>(blockIdx.x);
     const int mi = L / 8;
-    const int tbi = (mi / nch) * 8 + L % 8;
+    const int tbi = (mi / ngr) * 8 + L % 8;
     if (tbi >= nblk) return;  // padding of the id space to a multiple of 8 blocks
     const int blk = nblk - 1 - tbi;
-    const int c0 = (mi % nch) * kPfChunk;
-    const int cw = min(kPfChunk, p.ncols - c0);
-    const int b = blk / gps;
-    const int tb = (blk % gps) * kPfTok;
+    const int b = blk / ntb;
+    const int t0 = (blk % ntb) * kP2Tok;
+    const int R0 = (mi % ngr) * kP2Rec;
+    const int nr = min(kP2Rec, p.ncols - R0);  // columns of this group
     const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
     const size_t row0 = static_cast<size_t>(b) * p.Tq;
 
-    // Every global read the block needs before its first tile goes out
-    // at once: positions (lanes 0..7 of each wave), query fragments, head
-    // weights (to LDS) and, below, the first key tiles.
-    const int pt = tb + (lane & 7);
-    const int64_t pos = pt < p.Tq ? p.q_pos[row0 + pt] : -1;
-    bf16x8 qa[kPfTokW][8];
+    // this wave's tokens: visibility (lane i holds token i's), and the
+    // first token's query fragments and head weights
+    const int tw0 = t0 + kP2TokW * wave;
+    const int tw1 = min(tw0 + kP2TokW, p.Tq);
+    const int vis_l = (lane < tw1 - tw0) ? visible_count(p.q_pos[row0 + tw0 + lane], p.m, nrec) : 0;
+    struct Tok {
+        bf16x8 a[8];
+        f32x4 w[4];
+    };
+    auto tload = [&](int t, Tok& x) {
+        const u32x4* qh = reinterpret_cast<const u32x4*>(p.q + ((row0 + t) * kHi + j) * kDi + 64 * kg);
 #pragma unroll
-    for (int tk = 0; tk < kPfTokW; ++tk) {
-        const int t = min(tb + kPfTokW * wave + tk, p.Tq - 1);
-        const uint16_t* qh = p.q + ((row0 + t) * kHi + j) * kDi + 8 * kg;
+        for (int ks = 0; ks < 8; ++ks) x.a[ks] = as_bf16x8(qh[ks]);
+        // weights of this lane's 16 heads: 8 (v / 4) + 4 kg + v % 4
+        const float* wr = p.w + (row0 + t) * kHi + 4 * kg;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qa[tk][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ks));
-    }
-    {
-        const int t = min(tb + tid / kHi, p.Tq - 1);
-        wl[tid / kHi][tid % kHi] = p.w[(row0 + t) * kHi + tid % kHi];  // 256 threads = 8 tokens x 32 heads
-    }
-    // key tile staging: thread -> (record tid / 8, 16-dim chunk tid % 8)
-    const int sr = tid >> 3, sc = tid & 7;
-    const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
-    typedef typename std::conditional<KDT == DT_BF16, u32x4, u32x2>::type Raw;
-    struct Stage {
-        Raw d[2];
-        float s;
+        for (int q4 = 0; q4 < 4; ++q4) x.w[q4] = *reinterpret_cast<const f32x4*>(wr + 8 * q4);
     };
-    auto fetch = [&](int ti, Stage& st) {
-        const int rec = ti * kPfRec + sr;
-        const bool ok = rec < p.N;  // rows past the visible ones are masked after the product
-        const uint8_t* r = kbase + static_cast<size_t>(ok ? rec : 0) * kRowBytes;
-        if constexpr (KDT == DT_BF16) {
-            st.d[0] = ok ? reinterpret_cast<const u32x4*>(r)[2 * sc] : u32x4{0, 0, 0, 0};
-            st.d[1] = ok ? reinterpret_cast<const u32x4*>(r)[2 * sc + 1] : u32x4{0, 0, 0, 0};
-            st.s = 1.f;
-        } else {
-            st.d[0] = ok ? reinterpret_cast<const u32x2*>(r)[2 * sc] : u32x2{0, 0};
-            st.d[1] = ok ? reinterpret_cast<const u32x2*>(r)[2 * sc + 1] : u32x2{0, 0};
-            st.s = (ok && sc == 0) ? p.ks[static_cast<size_t>(b) * p.N + rec] : 0.f;
-        }
-    };
-    auto land = [&](int buf, const Stage& st) {
-        u32x4* d = reinterpret_cast<u32x4*>(&kt[buf][sr * kPfPitch + 16 * sc]);
-        if constexpr (KDT == DT_BF16) {
-            d[0] = st.d[0];
-            d[1] = st.d[1];
-        } else {
-            d[0] = e4m3x8_to_bf16x8(st.d[0]);
-            d[1] = e4m3x8_to_bf16x8(st.d[1]);
-            if (sc == 0) kts[buf][sr] = st.s;
-        }
-    };
+    Tok cur;
+    if (tw0 < tw1) tload(tw0, cur);
 
-    const int it0 = c0 / kPfRec;
-    const int it_cap = (c0 + cw + kPfRec - 1) / kPfRec;  // tiles of this chunk
-    Stage s0, sa, sb;  // tiles it0, it+1 and it+2
-    fetch(it0, s0);
-    if (it0 + 1 < it_cap) fetch(it0 + 1, sa);
-    if (it0 + 2 < it_cap) fetch(it0 + 2, sb);
-
-    // visibility: lanes 0..7 hold the block's tokens; the block's maximum
-    // bounds the tiles, each token masks its own columns
-    int v8 = (lane < kPfTok && pt < p.Tq) ? visible_count(pos, p.m, nrec) : 0;
-#pragma unroll
-    for (int o = 1; o < kPfTok; o <<= 1) v8 = max(v8, __shfl_xor(v8, o, kWave));
-    const int vis_blk = min(__builtin_amdgcn_readfirstlane(v8), p.ncols);
-    int vis[kPfTokW];
-#pragma unroll
-    for (int tk = 0; tk < kPfTokW; ++tk) {
-        const int i = kPfTokW * wave + tk;
-        const int vi = (tb + i < p.Tq) ? visible_count(__shfl(pos, i, kWave), p.m, nrec) : 0;
-        vis[tk] = __builtin_amdgcn_readfirstlane(vi);
-    }
-    // tiles of this chunk that any token of the block can see
-    const int it_end = min((min(vis_blk, c0 + cw) + kPfRec - 1) / kPfRec, it_cap);
-    if (it0 < it_end) land(0, s0);
-    // columns no tile writes stay -inf
-    for (int i = tid; i < kPfTok * kPfChunk / 4; i += 256)
-        reinterpret_cast<f32x4*>(&scs[0][0])[i] = f32x4{-__builtin_huge_valf(), -__builtin_huge_valf(),
-                                                        -__builtin_huge_valf(), -__builtin_huge_valf()};
+    // keys of the group -> bf16 rows in LDS (records past N are zero rows,
+    // masked below like every record the token cannot see)
     {
-        for (int it = it0; it < it_end; ++it) {
-            const int buf = (it - it0) & 1;
-            __syncthreads();  // tile `it` in LDS; tile it-1's buffer free; score rows cleared
-            bf16x8 bk[8];
-            const uint16_t* kr = &kt[buf][j * kPfPitch + 8 * kg];
+        typedef typename std::conditional<KDT == DT_BF16, u32x4, u32x2>::type Raw;
+        constexpr int kChunkBytes = (KDT == DT_BF16) ? 16 : 8;  // 8 dims
+        const uint8_t* kb = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+        // all loads first and unconditional (a clamped row, zeroed after):
+        // a branch around each load would serialise them
+        Raw raw[16];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) bk[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * ks));
-            f32x16 c[kPfTokW];
+        for (int i = 0; i < 16; ++i) {
+            const int c = i * 256 + tid;  // 16 chunks per record
+            const int rec = min(R0 + (c >> 4), p.N - 1);
+            raw[i] = *reinterpret_cast<const Raw*>(kb + static_cast<size_t>(rec) * kRowBytes + kChunkBytes * (c & 15));
+        }
 #pragma unroll
-            for (int tk = 0; tk < kPfTokW; ++tk)
+        for (int i = 0; i < 16; ++i) {
+            const int c = i * 256 + tid;
+            u32x4 v;
+            if constexpr (KDT == DT_BF16) v = raw[i];
+            else v = e4m3x8_to_bf16x8(raw[i]);
+            if (R0 + (c >> 4) >= p.N) v = u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(kl + (c >> 4) * kP2Pitch + 16 * (c & 15)) = v;
+        }
+        if constexpr (KDT == DT_E4M3)
+            ksl[tid] = R0 + tid < p.N ? p.ks[static_cast<size_t>(b) * p.N + R0 + tid] : 0.f;
+    }
+    __syncthreads();
+
+    // Set pairs 0 .. NP-1 of one token in one branch-free block (their
+    // MFMAs, operand reads and epilogues interleave); pairs past NP are
+    // out of the token's sight and score -inf.
+    float sc[kP2TokW][kPairs];
+    auto score_pairs = [&](auto np_tag, const Tok& x, int vis, float (&out)[kPairs]) {
+        constexpr int NP = decltype(np_tag)::value;
+        float wv[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) c[tk][v] = 0.f;
+        for (int v = 0; v < 16; ++v) wv[v] = x.w[v / 4][v % 4];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
+        for (int sp = 0; sp < kPairs; ++sp) {
+            out[sp] = -__builtin_huge_valf();
+            if (sp < NP) {  // folds: sp is unrolled, NP a constant
+                const int rb = 64 * sp;
+                const uint8_t* k0 = kl + (rb + j) * kP2Pitch + 128 * kg;
+                const uint8_t* k1 = k0 + 32 * kP2Pitch;
+                f32x16 c0, c1;
 #pragma unroll
-                for (int tk = 0; tk < kPfTokW; ++tk) c[tk] = mfma32x32x16(qa[tk][ks], bk[ks], c[tk]);
-            const int rec = it * kPfRec + j;
-            const float ksc = (KDT == DT_E4M3) ? kts[buf][j] : 1.f;
+                for (int v = 0; v < 16; ++v) c0[v] = c1[v] = 0.f;
 #pragma unroll
-            for (int tk = 0; tk < kPfTokW; ++tk) {
-                // head weights of this lane's 16 heads: 8 (v / 4) + 4 kg + v % 4
-                float wv[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wl[kPfTokW * wave + tk][8 * q4 + 4 * kg]);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) wv[4 * q4 + v] = w4[v];
+                for (int ks = 0; ks < 8; ++ks) {
+                    const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(k0 + 16 * ks));
+                    const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(k1 + 16 * ks));
+                    c0 = mfma32x32x16(x.a[ks], b0, c0);
+                    c1 = mfma32x32x16(x.a[ks], b1, c1);
                 }
-                float pr[8];
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                for (int v = 0; v < 8; ++v)
-                    pr[v] = fmaf(wv[2 * v + 1], fmaxf(c[tk][2 * v + 1], 0.f), wv[2 * v] * fmaxf(c[tk][2 * v], 0.f));
-                const float part = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-                float x, y;
-                pair_xor32(part, x, y);
-                const float val = (x + y) * ksc;  // the row scale is >= 0, so it commutes with the ReLU
-                if (kg == 0 && rec < c0 + cw && rec < vis[tk]) scs[kPfTokW * wave + tk][rec - c0] = val;
-            }
-            if (it + 1 < it_end) {
-                land(buf ^ 1, sa);
-                sa = sb;
-                if (it + 3 < it_end) fetch(it + 3, sb);
+                for (int v = 0; v < 16; ++v) {
+                    s0 = fmaf(wv[v], fmaxf(c0[v], 0.f), s0);
+                    s1 = fmaf(wv[v], fmaxf(c1[v], 0.f), s1);
+                }
+                // lanes 0..31 finish set 0 (records rb + l), lanes 32..63 set 1
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+                float tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                if constexpr (KDT == DT_E4M3) tot *= ksl[rb + lane];  // the row scale is >= 0: it commutes with the ReLU
+                if (R0 + rb + lane < vis) out[sp] = tot;
             }
         }
-        __syncthreads();  // score rows complete
-        // 16-byte stores when every output row starts 16-byte aligned
-        const int cw4 = (p.ncols % 4 == 0) ? cw / 4 : 0;
-        for (int i = tid; i < kPfTok * cw4; i += 256) {
-            const int tk = i / cw4, q4 = i % cw4;
-            if (tb + tk < p.Tq)
-                *reinterpret_cast<f32x4*>(&p.out[(row0 + tb + tk) * p.ncols + c0 + 4 * q4]) =
-                    reinterpret_cast<const f32x4*>(&scs[tk][0])[q4];
+    };
+    // Scores stay in registers until the wave's tokens are done: a store
+    // inside the loop would make every wait for the next token's loads wait
+    // for the stores as well.
+#pragma unroll
+    for (int i = 0; i < kP2TokW; ++i) {
+        const int t = tw0 + i;
+        if (t >= tw1) break;
+        Tok nxt;
+        if (t + 1 < tw1) tload(t + 1, nxt);
+        const int vis = __builtin_amdgcn_readlane(vis_l, i);
+        // set pairs holding a record the token sees (all of them hold columns)
+        const int np = min(max(vis - R0 + 63, 0) >> 6, (nr + 63) >> 6);
+        switch (np) {
+            case 0: score_pairs(std::integral_constant<int, 0>{}, cur, vis, sc[i]); break;
+            case 1: score_pairs(std::integral_constant<int, 1>{}, cur, vis, sc[i]); break;
+            case 2: score_pairs(std::integral_constant<int, 2>{}, cur, vis, sc[i]); break;
+            case 3: score_pairs(std::integral_constant<int, 3>{}, cur, vis, sc[i]); break;
+            default: score_pairs(std::integral_constant<int, 4>{}, cur, vis, sc[i]); break;
         }
-        const int rest = cw - 4 * cw4;  // columns left for single stores
-        for (int i = tid; i < kPfTok * rest; i += 256) {
-            const int tk = i / rest, col = 4 * cw4 + i % rest;
-            if (tb + tk < p.Tq) p.out[(row0 + tb + tk) * p.ncols + c0 + col] = scs[tk][col];
-        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int i = 0; i < kP2TokW; ++i) {
+        const int t = tw0 + i;
+        if (t >= tw1) break;
+        float* orow = p.out + (row0 + t) * p.ncols + R0;
+#pragma unroll
+        for (int sp = 0; sp < kPairs; ++sp)
+            if (64 * sp + lane < nr) orow[64 * sp + lane] = sc[i][sp];
     }
 }
 
@@ -495,8 +475,8 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
             p.pool = nullptr;
             p.out = a.scores;
             p.tiles_per_block = 0;
-            const int nblk8 = (a.B * ((a.Tq + kPfTok - 1) / kPfTok) + 7) / 8 * 8;
-            const dim3 grid(nblk8 * ((a.ncols + kPfChunk - 1) / kPfChunk));
+            const int nblk8 = (a.B * ((a.Tq + kP2Tok - 1) / kP2Tok) + 7) / 8 * 8;
+            const dim3 grid(nblk8 * ((a.ncols + kP2Rec - 1) / kP2Rec));
             if (a.k_dtype == DT_BF16)
                 hipLaunchKernelGGL(idx_prefill_kernel<DT_BF16>, grid, dim3(256), 0, st, p);
             else

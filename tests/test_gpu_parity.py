@@ -64,14 +64,18 @@ def test_index_scores_mfma_decode(kdt):
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
-@pytest.mark.parametrize("Tq,N", [(70, 40), (37, 700), (21, 301)])
-def test_index_scores_mfma_prefill(kdt, Tq, N):
-    """Ragged token groups; several 256-column chunks (N=700); a row length
-    that is not a multiple of 4 (N=301)."""
-    _case(f"index_scores prefill tiles, {kdt} keys, Tq={Tq} N={N}")
-    wl = _small(B=2, Tq=Tq, N=N, decode_pos=None, k_dtype=kdt, W=8)
+@pytest.mark.parametrize("Tq,N,n_rec", [(70, 40, None), (37, 700, None), (21, 301, None), (48, 600, (450, 600))])
+def test_index_scores_mfma_prefill(kdt, Tq, N, n_rec):
+    """Ragged token groups; several 256-record groups (N=700); a row length
+    that is not a multiple of 4 (N=301); fewer records written than the
+    cache holds (n_rec)."""
+    _case(f"index_scores prefill tiles, {kdt} keys, Tq={Tq} N={N} n_rec={n_rec}")
+    kw = {} if n_rec is None else {"n_rec": n_rec}
+    wl = _small(B=2, Tq=Tq, N=N, decode_pos=None, k_dtype=kdt, W=8, **kw)
     inp = WL.make_inputs(wl)
     inp["layers"][0]["q_pos"][1] += 60 if N < 100 else 2000  # second sequence later in its context
+    if n_rec is not None:
+        inp["layers"][0]["q_pos"][0] += 2400  # would see ~600 records; only 450 are written
     g = _run_scores(inp)
     for b in range(2):
         for ti in range(Tq):
