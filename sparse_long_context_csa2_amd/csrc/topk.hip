@@ -22,11 +22,11 @@
 // Longer rows: the row is split into 4096-column chunks over many
 // workgroups.  A histogram kernel accumulates the row histogram (LDS-
 // private per workgroup, merged with global atomics); a select kernel then
-// classifies each chunk in LDS -- keys above the boundary bin are chosen
-// outright, keys inside it are candidates -- and appends both lists to the
-// row's with one atomic.  The last workgroup to finish a row (atomic
-// ticket after a device-scope fence) resolves the boundary bin exactly
-// and writes the row.  Output ids are sorted by
+// classifies each chunk -- keys above the boundary bin are chosen
+// outright, keys inside it are candidates -- places both lists with one
+// block scan and appends them to the row's with one atomic.  The last
+// workgroup to finish a row (atomic ticket) resolves the boundary bin
+// exactly and writes the row, sorted in LDS.  Output ids are sorted by
 // column, so results are deterministic whatever the order in which
 // workgroups ran.
 //
@@ -85,10 +85,13 @@ __device__ __forceinline__ void load_keys(const TopkP& p, const int32_t* prow, c
     float sv[N];
     int pv[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int c = min(c0 + i * kNT + static_cast<int>(threadIdx.x), c1 - 1);
-        sv[i] = srow[c];
-        pv[i] = prow ? prow[c / p.blk] : 0;
+    for (int i = 0; i < N; ++i) sv[i] = srow[min(c0 + i * kNT + static_cast<int>(threadIdx.x), c1 - 1)];
+    if (prow) {  // one uniform branch around all the pool loads
+#pragma unroll
+        for (int i = 0; i < N; ++i) pv[i] = prow[min(c0 + i * kNT + static_cast<int>(threadIdx.x), c1 - 1) / p.blk];
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) pv[i] = 0;
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -353,20 +356,6 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }  // vmcnt(0)
 
-// Slot for this lane in a list appended to through *counter, one atomic
-// per wave (ballot, then this lane's rank among the appending lanes).
-__device__ __forceinline__ int wave_append(int* counter, bool pred) {
-    const unsigned long long bal = __ballot(pred);
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    if (bal) {
-        const int leader = __ffsll(static_cast<long long>(bal)) - 1;
-        if (lane == leader) base = atomicAdd(counter, __popcll(bal));
-        base = __shfl(base, leader, kWave);
-    }
-    return base + __popcll(bal & ((1ull << lane) - 1ull));
-}
-
 __global__ __launch_bounds__(kNT) void topk_zero_kernel(TopkP p) {
     const int row = blockIdx.x;
     int* h = p.ghist + static_cast<size_t>(row) * kBins;
@@ -395,15 +384,16 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
         if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
+constexpr int kBitWords = 8192;  // column bitmap of the final ordering: rows up to 262144 columns
 struct LongShared {
-    int hist[kBins];
-    int hist8[256];
     union {
-        struct {                      // classification of one chunk
-            uint32_t key[kChunk];     // its level-1 boundary candidates
-            int col[kChunk];
-            int sure[kMaxK];          // its keys above the boundary bin
-        } chunk;
+        struct {
+            int hist[kBins];
+            int hist8[256];
+        } h;
+        unsigned bits[kBitWords];  // once the selection is made
+    } a;
+    union {
         struct {                      // the row's final resolution
             unsigned long long fin[kMaxK];
             uint32_t key[kCandCap];   // the row's boundary candidates
@@ -431,33 +421,31 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     // the chunk's keys and the row histogram, all loads in flight at once
     uint32_t kk[kChunk / kNT];
     load_keys(p, prow, srow, c0, c1, kk);
-    const int* g = p.ghist + static_cast<size_t>(row) * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = g[i];
-    if (threadIdx.x == 0) {
-        sh.misc[0] = 0;  // candidates of the chunk
-        sh.misc[1] = 0;  // keys above the boundary
+    {
+        const int* g = p.ghist + static_cast<size_t>(row) * kBins;
+        int hv[kBins / kNT];
+#pragma unroll
+        for (int j = 0; j < kBins / kNT; ++j) hv[j] = g[j * kNT + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < kBins / kNT; ++j) sh.a.h.hist[j * kNT + threadIdx.x] = hv[j];
     }
     __syncthreads();
     int need1;
-    const int b1 = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need1);
-    // classify into LDS lists: above b1 chosen outright, inside b1 candidates
+    const int b1 = find_from_top<kBins / kNT>(sh.a.h.hist, K, sh.scan, &need1);
+    // classify: keys above b1 are chosen outright (fewer than K in the row),
+    // keys inside b1 are candidates.  Each thread counts its own; one block
+    // scan of (chosen << 16 | candidates) places both lists.
+    int nu = 0, ni = 0;
 #pragma unroll
     for (int i = 0; i < kChunk / kNT; ++i) {
-        const int c = c0 + i * kNT + threadIdx.x;
         const uint32_t k = kk[i];
         const int b = static_cast<int>(k >> kBinShift);
-        const bool up = k != 0u && b > b1;
-        const bool in = k != 0u && b == b1;
-        const int su = wave_append(&sh.misc[1], up);
-        if (up) sh.u.chunk.sure[su] = c;  // fewer than K keys lie above b1
-        const int sl = wave_append(&sh.misc[0], in);
-        if (in) {
-            sh.u.chunk.key[sl] = k;
-            sh.u.chunk.col[sl] = c;
-        }
+        nu += (k != 0u && b > b1) ? 1 : 0;
+        ni += (k != 0u && b == b1) ? 1 : 0;
     }
-    __syncthreads();
-    const int nloc = sh.misc[0], nsu = sh.misc[1];
+    int tot;
+    const int off = block_excl_scan((nu << 16) | ni, sh.scan, &tot);
+    const int nloc = tot & 0xFFFF, nsu = tot >> 16;
     // one atomic reserves room in both of the row's lists
     if (threadIdx.x == 0) {
         const unsigned long long add = (static_cast<unsigned long long>(nsu) << 32) | static_cast<unsigned>(nloc);
@@ -466,12 +454,21 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         sh.misc[3] = static_cast<int>(base >> 32);
     }
     __syncthreads();
-    const int gbase = sh.misc[2], sbase = sh.misc[3];
-    for (int i = threadIdx.x; i < nloc; i += kNT) {
-        st_dev(gkey + gbase + i, sh.u.chunk.key[i]);
-        st_dev(gcol + gbase + i, sh.u.chunk.col[i]);
+    {
+        int sl = sh.misc[2] + (off & 0xFFFF), su = sh.misc[3] + (off >> 16);
+#pragma unroll
+        for (int i = 0; i < kChunk / kNT; ++i) {
+            const int c = c0 + i * kNT + threadIdx.x;
+            const uint32_t k = kk[i];
+            const int b = static_cast<int>(k >> kBinShift);
+            if (k != 0u && b > b1) st_dev(sure + su++, c);
+            if (k != 0u && b == b1) {
+                st_dev(gkey + sl, k);
+                st_dev(gcol + sl, c);
+                ++sl;
+            }
+        }
     }
-    for (int i = threadIdx.x; i < nsu; i += kNT) st_dev(sure + sbase + i, sh.u.chunk.sure[i]);
     wait_stores();  // this wave's list entries are visible device-wide
     __syncthreads();
     if (threadIdx.x == 0) sh.misc[2] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
@@ -488,20 +485,49 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         if (slot < K)
             sh.u.fin.fin[slot] = p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
     };
-    for (int i = threadIdx.x; i < nsure; i += kNT) {
-        const int c = ld_dev(sure + i);
-        take_col(c, p.sort_by_key ? key_of(p, prow, srow, c) : 0u);
+    // The list reads below are issued all at once per thread (clamped
+    // indices, unused results dropped): a loop that waits for each
+    // device-scope load before the next would pay a memory round trip per
+    // element.
+    {
+        constexpr int kPer = kMaxK / kNT;  // nsure < K <= kMaxK
+        int cs[kPer];
+        uint32_t kv[kPer];
+        const int last = max(nsure - 1, 0);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) cs[j] = nsure > 0 ? ld_dev(sure + min(j * kNT + static_cast<int>(threadIdx.x), last)) : 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) kv[j] = p.sort_by_key && nsure > 0 ? key_of(p, prow, srow, cs[j]) : 0u;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j * kNT + static_cast<int>(threadIdx.x) < nsure) take_col(cs[j], kv[j]);
     }
     if (b1 >= 0) {
         // every candidate shares the key's top 12 bits (bin b1)
         const unsigned long long known = static_cast<unsigned long long>(static_cast<uint32_t>(b1) << kBinShift) << 32;
         unsigned long long thr;
         if (ncand <= kCandCap) {
-            for (int i = threadIdx.x; i < ncand; i += kNT) {
-                const int c = ld_dev(gcol + i);
-                sh.u.fin.key[i] = ld_dev(gkey + i);
-                sh.u.fin.col[i] = c;
-                sh.u.fin.rec[i] = rec_of(p, prow, c);
+            constexpr int kPer = kCandCap / kNT;
+            const int last = max(ncand - 1, 0);
+            int cc[kPer];
+            uint32_t ck[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = min(j * kNT + static_cast<int>(threadIdx.x), last);
+                cc[j] = ncand > 0 ? ld_dev(gcol + i) : 0;
+                ck[j] = ncand > 0 ? ld_dev(gkey + i) : 0u;
+            }
+            int cr[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) cr[j] = rec_of(p, prow, cc[j]);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = j * kNT + static_cast<int>(threadIdx.x);
+                if (i < ncand) {
+                    sh.u.fin.key[i] = ck[j];
+                    sh.u.fin.col[i] = cc[j];
+                    sh.u.fin.rec[i] = cr[j];
+                }
             }
             __syncthreads();
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
@@ -509,7 +535,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 rec = sh.u.fin.rec[i];
                 return true;
             };
-            thr = radix_select(src, ncand, need1, sh.hist8, sh.scan, 48, known);
+            thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
             for (int i = threadIdx.x; i < ncand; i += kNT)
                 if (composite(sh.u.fin.key[i], sh.u.fin.rec[i]) >= thr) take_col(sh.u.fin.col[i], sh.u.fin.key[i]);
         } else {  // a crowded boundary bin: select from the row's list
@@ -518,7 +544,7 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 rec = rec_of(p, prow, ld_dev(gcol + i));
                 return true;
             };
-            thr = radix_select(src, ncand, need1, sh.hist8, sh.scan, 48, known);
+            thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
             for (int i = threadIdx.x; i < ncand; i += kNT) {
                 const uint32_t k = ld_dev(gkey + i);
                 const int c = ld_dev(gcol + i);
@@ -534,21 +560,36 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         return p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(v)) : rec_of(p, prow, static_cast<int>(v));
     };
     for (int i = take + threadIdx.x; i < K; i += kNT) orow[i] = -1;
-    if (take <= 1024) {
-        // rank by counting: the values are unique, so an element's place is
-        // the number of values ahead of it (all lanes read the same LDS
-        // word at each step)
+    if (!p.sort_by_key && p.ncols <= kBitWords * 32) {
+        // column order: mark the chosen columns in a bitmap, then each
+        // thread writes the set bits of its run of words at its place
+        // from one block scan of the popcounts
+        const int nw = (p.ncols + 31) / 32;
+        for (int i = threadIdx.x; i < nw; i += kNT) sh.a.bits[i] = 0u;
+        __syncthreads();
         for (int i = threadIdx.x; i < take; i += kNT) {
-            const unsigned long long v = fin[i];
-            int r = 0;
-            for (int jj = 0; jj < take; ++jj) {
-                const unsigned long long w = fin[jj];
-                r += p.sort_by_key ? (w > v) : (w < v);
+            const int c = static_cast<int>(fin[i]);
+            atomicOr(&sh.a.bits[c >> 5], 1u << (c & 31));
+        }
+        __syncthreads();
+        const int wpt = (nw + kNT - 1) / kNT;
+        const int w0 = min(static_cast<int>(threadIdx.x) * wpt, nw);
+        const int w1 = min(w0 + wpt, nw);
+        int cntb = 0;
+        for (int w = w0; w < w1; ++w) cntb += __popc(sh.a.bits[w]);
+        int total;
+        int pos = block_excl_scan(cntb, sh.scan, &total);
+        for (int w = w0; w < w1; ++w) {
+            unsigned bw = sh.a.bits[w];
+            while (bw) {
+                const int bit = __ffs(static_cast<int>(bw)) - 1;
+                bw &= bw - 1u;
+                orow[pos++] = rec_of(p, prow, 32 * w + bit);
             }
-            orow[r] = out_of(v);
         }
         return;
     }
+    // otherwise a bitonic sort in LDS (log^2 stages, one block pass each)
     int m2 = 1;
     while (m2 < take) m2 <<= 1;
     // pad so the padding sorts last: descending by key, ascending by column
