@@ -385,13 +385,16 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
 }
 
 constexpr int kBitWords = 8192;  // column bitmap of the final ordering: rows up to 262144 columns
+// word w of the bitmap lives at w + w / 32: a thread's run of 32 words then
+// starts one bank further than its neighbour's
+__device__ __forceinline__ int bit_slot(int w) { return w + (w >> 5); }
 struct LongShared {
     union {
         struct {
             int hist[kBins];
             int hist8[256];
         } h;
-        unsigned bits[kBitWords];  // once the selection is made
+        unsigned bits[kBitWords + kBitWords / 32];  // once the selection is made
     } a;
     union {
         struct {                      // the row's final resolution
@@ -565,26 +568,34 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         // thread writes the set bits of its run of words at its place
         // from one block scan of the popcounts
         const int nw = (p.ncols + 31) / 32;
-        for (int i = threadIdx.x; i < nw; i += kNT) sh.a.bits[i] = 0u;
+        for (int i = threadIdx.x; i < bit_slot(nw); i += kNT) sh.a.bits[i] = 0u;
         __syncthreads();
         for (int i = threadIdx.x; i < take; i += kNT) {
             const int c = static_cast<int>(fin[i]);
-            atomicOr(&sh.a.bits[c >> 5], 1u << (c & 31));
+            atomicOr(&sh.a.bits[bit_slot(c >> 5)], 1u << (c & 31));
         }
         __syncthreads();
+        constexpr int kWpt = kBitWords / kNT;  // words per thread at most
         const int wpt = (nw + kNT - 1) / kNT;
-        const int w0 = min(static_cast<int>(threadIdx.x) * wpt, nw);
-        const int w1 = min(w0 + wpt, nw);
+        const int w0 = static_cast<int>(threadIdx.x) * wpt;
+        unsigned wv[kWpt];  // this thread's words, all read at once
         int cntb = 0;
-        for (int w = w0; w < w1; ++w) cntb += __popc(sh.a.bits[w]);
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) wv[k] = sh.a.bits[bit_slot(w0 + k)];  // w0 + k < kBitWords always
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) {
+            if (!(k < wpt && w0 + k < nw)) wv[k] = 0u;  // not this thread's, or past the zeroed words
+            cntb += __popc(wv[k]);
+        }
         int total;
         int pos = block_excl_scan(cntb, sh.scan, &total);
-        for (int w = w0; w < w1; ++w) {
-            unsigned bw = sh.a.bits[w];
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) {
+            unsigned bw = wv[k];
             while (bw) {
                 const int bit = __ffs(static_cast<int>(bw)) - 1;
                 bw &= bw - 1u;
-                orow[pos++] = rec_of(p, prow, 32 * w + bit);
+                orow[pos++] = rec_of(p, prow, 32 * (w0 + k) + bit);
             }
         }
         return;
