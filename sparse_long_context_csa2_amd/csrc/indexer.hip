@@ -58,161 +58,148 @@ __device__ __forceinline__ int chunk8(int g, int ks) {
     return 2 * (g + 4 * (ks >> 1)) + (ks & 1);             // one 16-byte load per two k-steps
 }
 
-// Loads the lane's share of one key row as four bf16x8 k-step operands.
-// Streaming (decode) reads are marked non-temporal: each key row is used
-// once per call.  Prefill reads keep normal caching: every key tile is
-// reused by all query-token groups.
-template <bool NT>
-__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
-    if (NT) return __builtin_nontemporal_load(p);
-    return *p;
+// Non-temporal 16-byte load: in decode each key row is used once per call.
+__device__ __forceinline__ u32x4 ld16_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+// The lane's share of one key row, as loaded (bf16: four 16-byte k-step
+// chunks; e4m3: two, each holding two k-steps).  Nothing here uses the
+// bytes, so no wait follows the loads; key_operands converts them where
+// they are multiplied.  `row` is always a real row: for a record the query
+// may not see, the caller passes another one and drops that column's score.
+template <int KDT>
+__device__ __forceinline__ void load_key_raw(const uint8_t* row, int g, u32x4 (&raw)[4]) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row);
+    constexpr int kLoads = (KDT == DT_BF16) ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) raw[i] = ld16_nt(p + g + 4 * i);
 }
 
-template <int KDT, bool NT>
-__device__ __forceinline__ void load_key(const uint8_t* row, int g, bool valid, bf16x8 (&bk)[4]) {
-    if (KDT == DT_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row);
+template <int KDT>
+__device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], bf16x8 (&bk)[4]) {
+    if constexpr (KDT == DT_BF16) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4 v = valid ? ld16<NT>(p + g + 4 * ks) : u32x4{0, 0, 0, 0};
-            bk[ks] = as_bf16x8(v);
-        }
+        for (int ks = 0; ks < 4; ++ks) bk[ks] = as_bf16x8(raw[ks]);
     } else {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            u32x4 v = valid ? ld16<NT>(p + g + 4 * i) : u32x4{0, 0, 0, 0};
-            bk[2 * i] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{v[0], v[1]}));
-            bk[2 * i + 1] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{v[2], v[3]}));
+            bk[2 * i] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{raw[i][0], raw[i][1]}));
+            bk[2 * i + 1] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{raw[i][2], raw[i][3]}));
         }
     }
 }
 
-// TOKW query tokens per wave.  WAVES_ON_TOKENS: the block's four waves take
-// different tokens and the same record tiles (prefill); otherwise they take
-// the same token and different tiles (decode, or any pooled row).
-template <int KDT, int TOKW, bool WAVES_ON_TOKENS>
+// Decode scoring: one query token per row (or any pooled row).  The four
+// waves of a workgroup take alternate 16-record tiles of the row's column
+// range; each lane loads its record's key bytes straight into registers
+// (non-temporal: every key row is read once per call), two tiles ahead of
+// the one being multiplied.  Scores collect in LDS and leave as whole
+// column runs at the end: no store sits between a prefetch and its wait.
+constexpr int kDecTpbMax = 128;  // tiles per workgroup, at most
+
+template <int KDT>
 __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
+    __shared__ float osc[kDecTpbMax * 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
     constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
 
-    int b, tok0, ntok;
-    if (WAVES_ON_TOKENS) {
-        const int gps = (p.Tq + 4 * TOKW - 1) / (4 * TOKW);
-        b = blockIdx.y / gps;
-        tok0 = (blockIdx.y % gps) * 4 * TOKW + wave * TOKW;
-        ntok = p.Tq - tok0;
-        ntok = ntok < 0 ? 0 : (ntok > TOKW ? TOKW : ntok);
-    } else {
-        b = blockIdx.y / p.Tq;
-        tok0 = blockIdx.y % p.Tq;
-        ntok = 1;
-    }
-    if (ntok == 0) return;
+    const int b = blockIdx.y / p.Tq;
+    const int tok = blockIdx.y % p.Tq;
+    const size_t row = static_cast<size_t>(b) * p.Tq + tok;
     const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
 
-    // A operands (queries), head weights and visibility of the wave's tokens.
-    bf16x8 qa[TOKW][2][4];
-    float wv[TOKW][2][4];
-    int vis[TOKW];
-    int vis_max = 0;
+    // A operands (the token's queries), head weights and visibility
+    bf16x8 qa[2][4];
+    float wv[2][4];
+    const int vis = visible_count(p.q_pos[row], p.m, nrec);
 #pragma unroll
-    for (int tk = 0; tk < TOKW; ++tk) {
-        const bool on = tk < ntok;
-        const size_t row = static_cast<size_t>(b) * p.Tq + tok0 + (on ? tk : 0);
-        vis[tk] = on ? visible_count(p.q_pos[row], p.m, nrec) : 0;
-        vis_max = max(vis_max, vis[tk]);
+    for (int mt = 0; mt < 2; ++mt) {
+        const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
+        for (int ks = 0; ks < 4; ++ks)
+            qa[mt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * chunk8<KDT>(g, ks)));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x4 v = on ? *reinterpret_cast<const u32x4*>(qh + 8 * chunk8<KDT>(g, ks))
-                             : u32x4{0, 0, 0, 0};
-                qa[tk][mt][ks] = as_bf16x8(v);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) wv[tk][mt][v] = on ? p.w[row * kHi + 16 * mt + 4 * g + v] : 0.f;
-        }
+        for (int v = 0; v < 4; ++v) wv[mt][v] = p.w[row * kHi + 16 * mt + 4 * g + v];
     }
 
     const int ntiles = (p.ncols + 15) / 16;
     const int t_begin = blockIdx.x * p.tiles_per_block;
     const int t_end = min(ntiles, t_begin + p.tiles_per_block);
-    const int t_step = WAVES_ON_TOKENS ? 1 : 4;
-    const int t_first = t_begin + (WAVES_ON_TOKENS ? 0 : wave);
-    const int32_t* prow = p.pool ? p.pool + (static_cast<size_t>(b) * p.Tq + tok0) * p.P : nullptr;
+    const int32_t* prow = p.pool ? p.pool + row * p.P : nullptr;
     const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
 
-    // One record tile in flight ahead of the one being multiplied.
     struct Tile {
-        int c, rec;
-        bool ld, any;
-        bf16x8 bk[4];
+        int rec;
+        bool any;
+        u32x4 raw[4];
         float kscale;
     };
     auto fetch = [&](int ti, Tile& T) {
-        T.c = ti * 16 + n;
+        const int c = ti * 16 + n;
         T.rec = -1;
-        if (T.c < p.ncols) {
+        if (c < p.ncols) {
             if (prow) {
-                const int pb = prow[T.c / p.blk];
-                T.rec = pb < 0 ? -1 : pb * p.blk + T.c % p.blk;
+                const int pb = prow[c / p.blk];
+                T.rec = pb < 0 ? -1 : pb * p.blk + c % p.blk;
             } else {
-                T.rec = T.c;
+                T.rec = c;
             }
         }
-        T.ld = T.rec >= 0 && T.rec < vis_max;
-        T.any = __any(T.ld);
+        const bool ld = T.rec >= 0 && T.rec < vis;
+        T.any = __any(ld);
         T.kscale = 1.f;
         if (T.any) {
-            load_key<KDT, !WAVES_ON_TOKENS>(kbase + static_cast<size_t>(T.ld ? T.rec : 0) * kRowBytes, g, T.ld,
-                                            T.bk);
-            if (KDT == DT_E4M3) T.kscale = T.ld ? p.ks[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+            load_key_raw<KDT>(kbase + static_cast<size_t>(ld ? T.rec : 0) * kRowBytes, g, T.raw);
+            if (KDT == DT_E4M3) T.kscale = ld ? p.ks[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
         }
     };
-    Tile cur, nxt;
-    if (t_first < t_end) fetch(t_first, cur);
-    for (int ti = t_first; ti < t_end; ti += t_step) {
-        if (ti + t_step < t_end) fetch(ti + t_step, nxt);
-        const int c = cur.c;
-        if (!cur.any) {
+    auto score = [&](int ti, const Tile& T) {
+        float val = -__builtin_huge_valf();
+        if (T.any) {
+            bf16x8 bk[4];
+            key_operands<KDT>(T.raw, bk);
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tk = 0; tk < TOKW; ++tk) {
-                if (g == 0 && tk < ntok && c < p.ncols)
-                    p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] = -__builtin_huge_valf();
+            for (int ks = 0; ks < 4; ++ks) {
+                acc0 = mfma16x16x32(qa[0][ks], bk[ks], acc0);
+                acc1 = mfma16x16x32(qa[1][ks], bk[ks], acc1);
             }
-        } else {
+            float part = 0.f;
 #pragma unroll
-            for (int tk = 0; tk < TOKW; ++tk) {
-                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    acc0 = mfma16x16x32(qa[tk][0][ks], cur.bk[ks], acc0);
-                    acc1 = mfma16x16x32(qa[tk][1][ks], cur.bk[ks], acc1);
-                }
-                float part = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float d0 = acc0[v], d1 = acc1[v];
-                    if (KDT == DT_E4M3) { d0 *= cur.kscale; d1 *= cur.kscale; }
-                    part += wv[tk][0][v] * fmaxf(d0, 0.f);
-                    part += wv[tk][1][v] * fmaxf(d1, 0.f);
-                }
-                part += shfl_xor_f(part, 16);
-                part += shfl_xor_f(part, 32);
-                if (g == 0 && tk < ntok && c < p.ncols) {
-                    const bool ok = cur.rec >= 0 && cur.rec < vis[tk];
-                    p.out[(static_cast<size_t>(b) * p.Tq + tok0 + tk) * p.ncols + c] =
-                        ok ? part : -__builtin_huge_valf();
-                }
+            for (int v = 0; v < 4; ++v) {
+                float d0 = acc0[v], d1 = acc1[v];
+                if (KDT == DT_E4M3) { d0 *= T.kscale; d1 *= T.kscale; }
+                part += wv[0][v] * fmaxf(d0, 0.f);
+                part += wv[1][v] * fmaxf(d1, 0.f);
             }
+            part += shfl_xor_f(part, 16);
+            part += shfl_xor_f(part, 32);
+            if (T.rec >= 0 && T.rec < vis) val = part;
         }
-        cur = nxt;
+        if (g == 0) osc[(ti - t_begin) * 16 + n] = val;
+    };
+    // tiles wave, wave + 4, ... of the range, two in flight ahead
+    Tile t0, t1, t2;
+    int ti = t_begin + wave;
+    if (ti < t_end) fetch(ti, t0);
+    if (ti + 4 < t_end) fetch(ti + 4, t1);
+    for (; ti < t_end; ti += 12) {
+        if (ti + 8 < t_end) fetch(ti + 8, t2);
+        score(ti, t0);
+        if (ti + 4 >= t_end) break;
+        if (ti + 12 < t_end) fetch(ti + 12, t0);
+        score(ti + 4, t1);
+        if (ti + 8 >= t_end) break;
+        if (ti + 16 < t_end) fetch(ti + 16, t1);
+        score(ti + 8, t2);
     }
+    __syncthreads();
+    const int c0 = t_begin * 16;
+    const int c1 = min(t_end * 16, p.ncols);
+    float* orow = p.out + row * p.ncols;
+    for (int c = c0 + static_cast<int>(threadIdx.x); c < c1; c += 256) orow[c] = osc[c - c0];
 }
 
 // Prefill scoring: many query tokens of one sequence against the records
@@ -429,7 +416,7 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(IdxG p) {
     p.out[row * p.ncols + c] = res;
 }
 
-template <int KDT, int TOKW, bool WOT>
+template <int KDT>
 int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     IdxP p;
     p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
@@ -443,9 +430,8 @@ int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     p.out = a.scores;
     p.tiles_per_block = tiles_per_block;
     const int ntiles = (a.ncols + 15) / 16;
-    dim3 grid((ntiles + tiles_per_block - 1) / tiles_per_block,
-              WOT ? a.B * ((a.Tq + 4 * TOKW - 1) / (4 * TOKW)) : a.B * a.Tq);
-    hipLaunchKernelGGL((idx_mfma_kernel<KDT, TOKW, WOT>), grid, dim3(256), 0, st, p);
+    dim3 grid((ntiles + tiles_per_block - 1) / tiles_per_block, a.B * a.Tq);
+    hipLaunchKernelGGL(idx_mfma_kernel<KDT>, grid, dim3(256), 0, st, p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -483,12 +469,12 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
                 hipLaunchKernelGGL(idx_prefill_kernel<DT_E4M3>, grid, dim3(256), 0, st, p);
             return static_cast<int>(hipGetLastError());
         }
-        // Decode rows: pick tiles per block so the grid has >= ~2048 blocks
-        // while each wave still streams several tiles.
-        int tpb = 32;
-        while (tpb > 4 && static_cast<long>(rows) * ((ntiles + tpb - 1) / tpb) < 2048) tpb >>= 1;
-        return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16, 1, false>(a, tpb, st)
-                                    : launch_mfma<DT_E4M3, 1, false>(a, tpb, st);
+        // Decode rows: the largest tiles per block that still gives >= 1024
+        // blocks (four per CU), so each wave streams many tiles and the
+        // start-up latency is paid rarely.
+        int tpb = kDecTpbMax;
+        while (tpb > 4 && static_cast<long>(rows) * ((ntiles + tpb - 1) / tpb) < 1024) tpb >>= 1;
+        return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16>(a, tpb, st) : launch_mfma<DT_E4M3>(a, tpb, st);
     }
     IdxG p;
     p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.Hi = a.Hi; p.Di = a.Di; p.m = a.m; p.ncols = a.ncols;
