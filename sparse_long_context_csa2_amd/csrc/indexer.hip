@@ -91,8 +91,8 @@ __device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], bf16x8 (&bk)
 // Decode scoring: one query token per row (or any pooled row).  The four
 // waves of a workgroup take alternate 16-record tiles of the row's column
 // range; each lane loads its record's key bytes straight into registers
-// (non-temporal: every key row is read once per call), two tiles ahead of
-// the one being multiplied.  Scores collect in LDS and leave as whole
+// (non-temporal: every key row is read once per call), several tiles
+// ahead of the one being multiplied.  Scores collect in LDS and leave as whole
 // column runs at the end: no store sits between a prefetch and its wait.
 constexpr int kDecTpbMax = 128;  // tiles per workgroup, at most
 
@@ -180,20 +180,24 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
         }
         if (g == 0) osc[(ti - t_begin) * 16 + n] = val;
     };
-    // tiles wave, wave + 4, ... of the range, two in flight ahead
-    Tile t0, t1, t2;
-    int ti = t_begin + wave;
-    if (ti < t_end) fetch(ti, t0);
-    if (ti + 4 < t_end) fetch(ti + 4, t1);
-    for (; ti < t_end; ti += 12) {
-        if (ti + 8 < t_end) fetch(ti + 8, t2);
-        score(ti, t0);
-        if (ti + 4 >= t_end) break;
-        if (ti + 12 < t_end) fetch(ti + 12, t0);
-        score(ti + 4, t1);
-        if (ti + 8 >= t_end) break;
-        if (ti + 16 < t_end) fetch(ti + 16, t1);
-        score(ti + 8, t2);
+    // tiles wave, wave + 4, ... of the range, through a ring of kRing
+    // tiles: kRing - 1 in flight ahead of the one being multiplied (e4m3
+    // tiles carry half the bytes, so more of them)
+    constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;
+    Tile tt[kRing];
+    const int ti0 = t_begin + wave;
+#pragma unroll
+    for (int d = 0; d + 1 < kRing; ++d)
+        if (ti0 + 4 * d < t_end) fetch(ti0 + 4 * d, tt[d]);
+    for (int base = ti0; base < t_end; base += 4 * kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+            const int ti = base + 4 * d;
+            if (ti >= t_end) break;
+            const int tf = ti + 4 * (kRing - 1);
+            if (tf < t_end) fetch(tf, tt[(d + kRing - 1) % kRing]);
+            score(ti, tt[d]);
+        }
     }
     __syncthreads();
     const int c0 = t_begin * 16;
