@@ -495,7 +495,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 else wait_copies_all();
                 lds_sync();  // tile `it` landed; the buffer two tiles ahead is free
                 if (it == 0 && nxt < n_items) fetch(nxt, nx);
-                if (it + 2 < ntile) issue(it + 2, (it + 2) % NB);
+                // later copies go out from inside the MFMA stream (below)
+                if (it == 0 && it + 2 < ntile) issue(it + 2, (it + 2) % NB);
             } else {
                 land(buf);
                 if (it == 0 && nxt < n_items) fetch(nxt, nx);
@@ -668,7 +669,28 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         // Iteration `it`: one stream of MFMAs -- the P.V of tile it, with the
         // S^T of tile it+1 in its first half and that tile's softmax in its
         // second half.
-        for (int it = 0; it + 1 < ntile; ++it) {
+        // One iteration.  With CP (bf16, tile it+3 exists) the copies of tile
+        // it+3 (into tile it-1's buffer, free since the barrier) go out one
+        // row per channel group of the MFMA stream instead of stalling the
+        // barrier phase; the two variants keep the stream branch-free.
+        auto step = [&](int it, auto cp_tag) {
+            constexpr bool CP = decltype(cp_tag)::value;
+            // row addresses of the copies (wave-uniform, scalar registers),
+            // read before the barrier so the reads land during its wait
+            const uint8_t* rp[kRowsPerWave];
+            uint32_t cdst = 0;
+            if constexpr (CP) {
+                const u32x4* ep = reinterpret_cast<const u32x4*>(&sh.eptr[(it + 3) * kTile + kRowsPerWave * wave]);
+                u32x4 pa[kRowsPerWave / 2];
+#pragma unroll
+                for (int i = 0; i < kRowsPerWave / 2; ++i) pa[i] = ep[i];
+#pragma unroll
+                for (int i = 0; i < kRowsPerWave / 2; ++i) {
+                    rp[2 * i] = uniform_ptr(pa[i][0], pa[i][1]);
+                    rp[2 * i + 1] = uniform_ptr(pa[i][2], pa[i][3]);
+                }
+                cdst = lds_addr(sh.xb[(it + 3) % NB]) + kRowsPerWave * wave * kXPitch;
+            }
             tile_ready(it + 1);
             Qk q;
             qk_begin(it + 1, q);
@@ -677,6 +699,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             bool jump = false;
             Soft s;
             tile_pv(it, bhi, blo, [&](int j) {
+                if constexpr (CP) row_copy16(rp[j], voff, cdst + j * kXPitch);
                 if (j < 4) {
                     qk_step(q, j);
                     return;
@@ -704,7 +727,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             m_run = m_new;
             bhi = packed(s.phi);
             blo = packed(s.plo);
-        }
+        };
+        int it = 0;
+        if constexpr (KVDT == DT_BF16)
+            for (; it + 3 < ntile; ++it) step(it, std::true_type{});
+        for (; it + 1 < ntile; ++it) step(it, std::false_type{});
         if (ntile > 0) tile_pv(ntile - 1, bhi, blo, [](int) {});
         if (ntile == 0 && nxt < n_items) fetch(nxt, nx);
         if (nxt < n_items) fetch_q(nxt, nx);
