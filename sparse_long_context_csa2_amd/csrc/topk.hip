@@ -17,8 +17,10 @@
 //     boundary bin's elements (usually a few dozen) picks the rest.
 // All bin searches are parallel block scans.
 //
-// Rows of up to 4096 columns: one 256-thread workgroup per row with the
-// keys cached in LDS.
+// Rows of up to 2048 columns in column order: one wave per row, keys in
+// registers, the boundary key by binary search over key values.
+// Rows of up to 4096 columns otherwise: one 256-thread workgroup per row
+// with the keys cached in LDS.
 // Longer rows: the row is split into 4096-column chunks over many
 // workgroups.  A histogram kernel accumulates the row histogram (LDS-
 // private per workgroup, merged with global atomics); a select kernel then
@@ -205,6 +207,92 @@ __device__ unsigned long long radix_select(Src src, int count, int need, int* hi
         need = rest;
     }
     return prefix;
+}
+
+// ---------------------------------------------------------------- rows <= 2048, one wave each
+
+// Short rows in column order (no pool): one wave per row, the row's keys in
+// registers (lane l owns columns KPL*l .. KPL*l + KPL - 1).  The K-th
+// largest score key k* comes from a 32-step binary search over key values
+// (counts by per-lane compares and a wave sum); every key above k* is
+// chosen, and of the keys equal to k* the ones in the lowest columns --
+// their composite keys are the larger ones, as rec = column here.  One
+// wave scan of the per-lane counts places the chosen columns in order.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+template <int KPL>
+__global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kNW + (threadIdx.x >> 6);
+    if (row >= p.rows) return;
+    const int n = p.ncols;
+    const int K = p.K;
+    const float* srow = p.scores + static_cast<size_t>(row) * n;
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    const int c0 = KPL * lane;
+    uint32_t kk[KPL];
+    {
+        float sv[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) sv[i] = srow[min(c0 + i, n - 1)];  // all loads at once
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) kk[i] = c0 + i < n ? score_key(sv[i]) : 0u;
+    }
+    auto count_ge = [&](uint32_t x) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) c += kk[i] >= x ? 1 : 0;
+        return wave_sum(c);
+    };
+    const int nvalid = count_ge(1u);
+    uint32_t kstar = 1u;  // with nvalid <= K every valid key is chosen
+    int need_tie = KPL * 64;
+    if (nvalid > K) {
+        // largest x with count(key >= x) >= K
+        uint32_t x = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = x | (1u << bit);
+            if (count_ge(cand) >= K) x = cand;
+        }
+        kstar = x;
+        need_tie = K - (kstar == 0xFFFFFFFFu ? 0 : count_ge(kstar + 1u));  // keys equal to k* still needed
+    }
+    // this lane's chosen columns and its ties' order
+    int ties = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) ties += kk[i] == kstar ? 1 : 0;
+    int tie_before = ties;  // inclusive prefix over lanes, then exclusive
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(tie_before, o, kWave);
+        if (lane >= o) tie_before += y;
+    }
+    tie_before -= ties;
+    bool ch[KPL];
+    int cnt = 0, tr = tie_before;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const bool tie = kk[i] == kstar;
+        ch[i] = kk[i] > kstar || (tie && tr < need_tie);
+        tr += tie ? 1 : 0;
+        cnt += ch[i] ? 1 : 0;
+    }
+    int pos = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(pos, o, kWave);
+        if (lane >= o) pos += y;
+    }
+    const int take = __shfl(pos, 63, kWave);  // = min(nvalid, K)
+    pos -= cnt;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+        if (ch[i]) orow[pos++] = c0 + i;
+    for (int i = take + lane; i < K; i += kWave) orow[i] = -1;
 }
 
 // ---------------------------------------------------------------- rows <= 4096
@@ -665,6 +753,14 @@ LongLayout long_layout(int rows, int ncols, int K) {
 }
 
 int run_topk(TopkP p, void* ws, hipStream_t st) {
+    if (!p.pool && !p.sort_by_key && p.ncols <= 64 * 32) {
+        const dim3 grid((p.rows + kNW - 1) / kNW);
+        if (p.ncols <= 64 * 16)
+            hipLaunchKernelGGL(topk_wave_kernel<16>, grid, dim3(kNT), 0, st, p);
+        else
+            hipLaunchKernelGGL(topk_wave_kernel<32>, grid, dim3(kNT), 0, st, p);
+        return static_cast<int>(hipGetLastError());
+    }
     if (p.ncols <= kSmallCols) {
         hipLaunchKernelGGL(topk_small_kernel<kSmallCols>, dim3(p.rows), dim3(kNT), 0, st, p);
         return static_cast<int>(hipGetLastError());

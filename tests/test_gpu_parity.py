@@ -127,7 +127,8 @@ def _score_rows(rows, n, seed):
     return s
 
 
-@pytest.mark.parametrize("n,K", [(5, 8), (700, 8), (1024, 512), (16384, 512), (20000, 2048), (65536, 512)])
+@pytest.mark.parametrize("n,K", [(5, 8), (700, 8), (1024, 512), (1500, 300), (2048, 1), (2049, 2048), (4096, 100),
+                                 (16384, 512), (20000, 2048), (65536, 512)])
 def test_topk_exact(n, K):
     _case(f"topk rows=4 n={n} K={K}")
     s = _score_rows(4, n, n + K)
