@@ -212,18 +212,13 @@ __device__ unsigned long long radix_select(Src src, int count, int need, int* hi
 // ---------------------------------------------------------------- rows <= 2048, one wave each
 
 // Short rows in column order (no pool): one wave per row, the row's keys in
-// registers (lane l owns columns KPL*l .. KPL*l + KPL - 1).  The K-th
-// largest score key k* comes from a 32-step binary search over key values
-// (counts by per-lane compares and a wave sum); every key above k* is
-// chosen, and of the keys equal to k* the ones in the lowest columns --
-// their composite keys are the larger ones, as rec = column here.  One
-// wave scan of the per-lane counts places the chosen columns in order.
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
+// registers -- lane l owns columns 64 i + l, so each load instruction reads
+// 256 contiguous bytes.  The K-th largest score key k* comes from a
+// 32-step binary search over key values, counting with ballots (no
+// cross-lane data movement); every key above k* is chosen, and of the keys
+// equal to k* the ones in the lowest columns -- their composite keys are
+// the larger ones, as rec = column here.  Output places are ballot
+// prefixes in column order.
 template <int KPL>
 __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
     const int lane = threadIdx.x & 63;
@@ -233,20 +228,19 @@ __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
     const int K = p.K;
     const float* srow = p.scores + static_cast<size_t>(row) * n;
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
-    const int c0 = KPL * lane;
     uint32_t kk[KPL];
     {
         float sv[KPL];
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) sv[i] = srow[min(c0 + i, n - 1)];  // all loads at once
+        for (int i = 0; i < KPL; ++i) sv[i] = srow[min(64 * i + lane, n - 1)];  // all loads at once
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) kk[i] = c0 + i < n ? score_key(sv[i]) : 0u;
+        for (int i = 0; i < KPL; ++i) kk[i] = 64 * i + lane < n ? score_key(sv[i]) : 0u;
     }
     auto count_ge = [&](uint32_t x) {
         int c = 0;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) c += kk[i] >= x ? 1 : 0;
-        return wave_sum(c);
+        for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(kk[i] >= x));
+        return c;
     };
     const int nvalid = count_ge(1u);
     uint32_t kstar = 1u;  // with nvalid <= K every valid key is chosen
@@ -261,38 +255,20 @@ __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
         kstar = x;
         need_tie = K - (kstar == 0xFFFFFFFFu ? 0 : count_ge(kstar + 1u));  // keys equal to k* still needed
     }
-    // this lane's chosen columns and its ties' order
-    int ties = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) ties += kk[i] == kstar ? 1 : 0;
-    int tie_before = ties;  // inclusive prefix over lanes, then exclusive
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(tie_before, o, kWave);
-        if (lane >= o) tie_before += y;
-    }
-    tie_before -= ties;
-    bool ch[KPL];
-    int cnt = 0, tr = tie_before;
+    // column order: row i of the register array holds columns 64 i .. 64 i + 63
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0, tseen = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
-        const bool tie = kk[i] == kstar;
-        ch[i] = kk[i] > kstar || (tie && tr < need_tie);
-        tr += tie ? 1 : 0;
-        cnt += ch[i] ? 1 : 0;
+        const unsigned long long tie = __ballot(kk[i] == kstar);
+        const int trank = tseen + __popcll(tie & below);  // ties in lower columns
+        const bool ch = kk[i] > kstar || ((tie >> lane) & 1ull && trank < need_tie);
+        const unsigned long long cm = __ballot(ch);
+        if (ch) orow[base + __popcll(cm & below)] = 64 * i + lane;
+        base += __popcll(cm);
+        tseen += __popcll(tie);
     }
-    int pos = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(pos, o, kWave);
-        if (lane >= o) pos += y;
-    }
-    const int take = __shfl(pos, 63, kWave);  // = min(nvalid, K)
-    pos -= cnt;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i)
-        if (ch[i]) orow[pos++] = c0 + i;
-    for (int i = take + lane; i < K; i += kWave) orow[i] = -1;
+    for (int i = base + lane; i < K; i += kWave) orow[i] = -1;
 }
 
 // ---------------------------------------------------------------- rows <= 4096
