@@ -17,10 +17,10 @@
 //     boundary bin's elements (usually a few dozen) picks the rest.
 // All bin searches are parallel block scans.
 //
-// Rows of up to 2048 columns in column order: one wave per row, keys in
-// registers, the boundary key by binary search over key values.
-// Rows of up to 4096 columns otherwise: one 256-thread workgroup per row
-// with the keys cached in LDS.
+// Rows of up to 4096 columns (score order only for K <= 64): one wave per
+// row, keys in registers, the boundary key by binary search over key
+// values.  Other rows of up to 4096 columns: one 256-thread workgroup per
+// row with the keys cached in LDS.
 // Longer rows: the row is split into 4096-column chunks over many
 // workgroups.  A histogram kernel accumulates the row histogram (LDS-
 // private per workgroup, merged with global atomics); a select kernel then
@@ -209,32 +209,52 @@ __device__ unsigned long long radix_select(Src src, int count, int need, int* hi
     return prefix;
 }
 
-// ---------------------------------------------------------------- rows <= 2048, one wave each
+// ---------------------------------------------------------------- rows <= 4096, one wave each
 
-// Short rows in column order (no pool): one wave per row, the row's keys in
-// registers -- lane l owns columns 64 i + l, so each load instruction reads
-// 256 contiguous bytes.  The K-th largest score key k* comes from a
-// 32-step binary search over key values, counting with ballots (no
-// cross-lane data movement); every key above k* is chosen, and of the keys
-// equal to k* the ones in the lowest columns -- their composite keys are
-// the larger ones, as rec = column here.  Output places are ballot
-// prefixes in column order.
-template <int KPL>
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+    const int lo = __shfl_xor(static_cast<int>(v & 0xFFFFFFFFull), m, kWave);
+    const int hi = __shfl_xor(static_cast<int>(v >> 32), m, kWave);
+    return (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// One wave per row, the row's keys in registers: lane l owns columns
+// 64 i + l, so each load instruction reads 256 contiguous bytes.  The K-th
+// largest score key k* comes from a 32-step binary search over key values,
+// counting with ballots (no cross-lane data movement); every key above k*
+// is chosen, and of the keys equal to k* the ones with the smallest record
+// ids (the larger composite keys): in the lowest columns without a pool,
+// by a second binary search over record ids with one.  Column order comes
+// from ballot prefixes; score order (K <= 64) from a bitonic sort across
+// the wave's lanes.
+template <int KPL, bool POOL>
 __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
+    __shared__ unsigned long long slot[kNW][64];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kNW + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * kNW + wave;
     if (row >= p.rows) return;
     const int n = p.ncols;
     const int K = p.K;
     const float* srow = p.scores + static_cast<size_t>(row) * n;
+    const int32_t* prow = POOL ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
     uint32_t kk[KPL];
+    int rr[KPL];  // record ids (the column itself without a pool)
     {
         float sv[KPL];
+        int pv[KPL];
 #pragma unroll
         for (int i = 0; i < KPL; ++i) sv[i] = srow[min(64 * i + lane, n - 1)];  // all loads at once
+        if constexpr (POOL) {
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) kk[i] = 64 * i + lane < n ? score_key(sv[i]) : 0u;
+            for (int i = 0; i < KPL; ++i) pv[i] = prow[min(64 * i + lane, n - 1) / p.blk];
+        }
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int c = 64 * i + lane;
+            rr[i] = POOL ? (pv[i] < 0 ? -1 : pv[i] * p.blk + c % p.blk) : c;
+            kk[i] = (c < n && rr[i] >= 0) ? score_key(sv[i]) : 0u;
+        }
     }
     auto count_ge = [&](uint32_t x) {
         int c = 0;
@@ -255,18 +275,48 @@ __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
         kstar = x;
         need_tie = K - (kstar == 0xFFFFFFFFu ? 0 : count_ge(kstar + 1u));  // keys equal to k* still needed
     }
+    int rstar = 0x7FFFFFFF;  // with a pool: ties chosen when rec <= rstar
+    if (POOL && nvalid > K) {
+        // the need_tie-th smallest record id among the ties
+        auto ties_below = [&](int y) {
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) c += __popcll(__ballot(kk[i] == kstar && rr[i] < y));
+            return c;
+        };
+        int r = 0;
+        for (int bit = 30; bit >= 0; --bit)
+            if (ties_below(r + (1 << bit)) < need_tie) r += 1 << bit;
+        rstar = r;
+    }
     // column order: row i of the register array holds columns 64 i .. 64 i + 63
     const unsigned long long below = (1ull << lane) - 1ull;
     int base = 0, tseen = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const unsigned long long tie = __ballot(kk[i] == kstar);
-        const int trank = tseen + __popcll(tie & below);  // ties in lower columns
-        const bool ch = kk[i] > kstar || ((tie >> lane) & 1ull && trank < need_tie);
+        const bool tie_in = POOL ? rr[i] <= rstar : tseen + __popcll(tie & below) < need_tie;
+        const bool ch = kk[i] > kstar || (((tie >> lane) & 1ull) && tie_in);
         const unsigned long long cm = __ballot(ch);
-        if (ch) orow[base + __popcll(cm & below)] = 64 * i + lane;
+        if (ch) {
+            const int pos = base + __popcll(cm & below);
+            if (p.sort_by_key) slot[wave][pos] = composite(kk[i], rr[i]);  // pos < K <= 64
+            else orow[pos] = rr[i];
+        }
         base += __popcll(cm);
         tseen += __popcll(tie);
+    }
+    if (p.sort_by_key) {
+        __builtin_amdgcn_wave_barrier();
+        unsigned long long v = lane < base ? slot[wave][lane] : 0ull;
+        for (int k = 2; k <= 64; k <<= 1)
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const unsigned long long o = shfl_xor_u64(v, j);
+                const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+                v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+            }
+        if (lane < K) orow[lane] = lane < base ? static_cast<int32_t>(~static_cast<uint32_t>(v)) : -1;
+        return;
     }
     for (int i = base + lane; i < K; i += kWave) orow[i] = -1;
 }
@@ -729,12 +779,19 @@ LongLayout long_layout(int rows, int ncols, int K) {
 }
 
 int run_topk(TopkP p, void* ws, hipStream_t st) {
-    if (!p.pool && !p.sort_by_key && p.ncols <= 64 * 32) {
+    // one wave per row pays off when rows are many or short: a few long rows
+    // are faster with a whole workgroup each (the LDS path below)
+    if (p.ncols <= 64 * 64 && (!p.sort_by_key || p.K <= 64) && (p.ncols <= 64 * 16 || p.rows >= 1024)) {
         const dim3 grid((p.rows + kNW - 1) / kNW);
-        if (p.ncols <= 64 * 16)
-            hipLaunchKernelGGL(topk_wave_kernel<16>, grid, dim3(kNT), 0, st, p);
-        else
-            hipLaunchKernelGGL(topk_wave_kernel<32>, grid, dim3(kNT), 0, st, p);
+        if (p.pool) {
+            if (p.ncols <= 64 * 16) hipLaunchKernelGGL((topk_wave_kernel<16, true>), grid, dim3(kNT), 0, st, p);
+            else if (p.ncols <= 64 * 32) hipLaunchKernelGGL((topk_wave_kernel<32, true>), grid, dim3(kNT), 0, st, p);
+            else hipLaunchKernelGGL((topk_wave_kernel<64, true>), grid, dim3(kNT), 0, st, p);
+        } else {
+            if (p.ncols <= 64 * 16) hipLaunchKernelGGL((topk_wave_kernel<16, false>), grid, dim3(kNT), 0, st, p);
+            else if (p.ncols <= 64 * 32) hipLaunchKernelGGL((topk_wave_kernel<32, false>), grid, dim3(kNT), 0, st, p);
+            else hipLaunchKernelGGL((topk_wave_kernel<64, false>), grid, dim3(kNT), 0, st, p);
+        }
         return static_cast<int>(hipGetLastError());
     }
     if (p.ncols <= kSmallCols) {

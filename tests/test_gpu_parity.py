@@ -161,6 +161,39 @@ def test_topk_pool_mapping_ties_by_record_id():
         assert set(got.tolist()) == ref and len(got) == len(ref)
 
 
+@pytest.mark.parametrize("pooled", [False, True])
+@pytest.mark.parametrize("ncols", [1536, 4096])
+def test_topk_many_rows(pooled, ncols):
+    """1024 rows: the one-wave-per-row path at 32 and 64 keys per lane, with
+    and without a pool column map (ties broken by record id)."""
+    _case(f"topk 1024 rows ncols={ncols} pooled={pooled}")
+    rows, K, blk = 1024, 300, 64
+    rng = np.random.default_rng(ncols + pooled)
+    s = (rng.integers(0, 40, size=(rows, ncols)) / 40.0).astype(np.float32)  # many exact ties
+    s[::5, ::9] = -np.inf
+    pool = None
+    if pooled:
+        nb = (ncols + blk - 1) // blk
+        pool = np.stack([rng.permutation(200)[:nb] for _ in range(rows)]).astype(np.int32)
+        pool[::7, 3] = -1
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=None if pool is None else torch.from_numpy(pool).cuda(),
+                     blk=blk if pooled else 0)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    cols = np.arange(ncols)
+    for r in list(range(0, rows, 37)) + [rows - 1]:
+        if pooled:
+            pb = pool[r][cols // blk]
+            rec = np.where(pb < 0, -1, pb * blk + cols % blk)
+            ref = set(rec[_ref_topk(s[r], K, rec)].tolist())
+            got = g[r][g[r] >= 0]
+            assert set(got.tolist()) == ref and len(got) == len(ref), f"row {r}"
+        else:
+            ref = np.sort(_ref_topk(s[r], K))
+            got = g[r][g[r] >= 0]
+            assert np.array_equal(got, ref), f"row {r}"
+
+
 @pytest.mark.parametrize("blk,P,N", [(4, 8, 128), (64, 64, 65536), (8, 2048, 20000)])
 def test_block_pool_exact(blk, P, N):
     _case(f"block_pool blk={blk} P={P} N={N}")
