@@ -14,28 +14,25 @@
 // paths").
 //
 // attn_mfma_kernel (64 heads x 512 dims, bf16 queries, bf16 or e4m3 rows):
-//  * one workgroup = 8 waves per (query, split of the entry list); wave w
-//    owns heads 16*(w%4) .. +15 and channel half w/4 of the 512-dim latent,
-//    so each lane keeps only 64 fp32 accumulators and 32 query registers
-//    and two waves share every SIMD; the two halves of a head exchange
-//    their partial logits through LDS (2 KiB per wave per tile);
-//  * the valid selected records are first compacted into an LDS list, so
-//    -1 padding costs nothing;
-//  * entries are processed in tiles of 32 rows (32 KiB of bf16).  A tile is
-//    fetched with fully used 256-byte segments into registers one tile
-//    ahead, then written to LDS twice: row-major (padded to 1040 B per row)
-//    for S^T = X Q^T, and transposed in a group-major, XOR-swizzled layout
-//    for O^T += X^T P^T.  Both the transposing writes and the MFMA operand
-//    reads then touch each 16-byte bank slot exactly as often as the data
-//    volume requires;
-//  * S^T is computed with 16x16x32 bf16 MFMAs (entries on M, heads on N),
-//    so each lane holds 8 logits of ONE head: the online-softmax max and
-//    sum need only two cross-lane steps, and those 8 probabilities are
-//    exactly the B operand of the P.V MFMA (heads on N again), so P never
-//    leaves registers.  P is split into bf16 hi + lo parts (two MFMAs) so
-//    that rounding P to bf16 costs no accuracy;
-//  * e4m3 rows are converted exactly to bf16 while staging; their per-row
-//    scale multiplies the logit and the probability instead;
+//  * persistent: one workgroup of 4 waves per compute unit walks the work
+//    items, (query, split of the entry list) pairs; wave w owns heads
+//    16w .. 16w+15 over all 512 channels, so O stays in its 128 accumulation
+//    registers and no partial sums cross waves;
+//  * the valid selected records are compacted into an LDS list, so -1
+//    padding costs nothing, and a table of row addresses is built per item;
+//  * entries are processed in tiles of 32 rows, copied global -> LDS
+//    row-major (bf16 directly with global_load_lds; e4m3 converted exactly
+//    to bf16 in registers on the way) two tiles ahead of their use;
+//  * S^T = X Q^T with 16x16x32 bf16 MFMAs (entries on M, heads on N), so
+//    each lane holds 8 logits of ONE head, which are exactly the B operand
+//    of the P.V MFMA; O^T += X^T P^T reads X^T with the transposing LDS
+//    load.  P is split into bf16 hi + lo parts (two MFMAs) so that rounding
+//    P to bf16 costs no accuracy;
+//  * the P.V of tile t, the S^T of tile t+1 and its softmax form one
+//    branch-free MFMA stream per iteration; each head keeps a lazy
+//    reference maximum that moves (with a rescale of O and l) only when a
+//    tile exceeds it by a wide margin, checked once per tile;
+//  * e4m3 per-row scales multiply the logit and the probability;
 //  * with one split the workgroup finishes (sink, normalisation, inverse
 //    RoPE) itself; otherwise it writes (max, sum, unnormalised O) and
 //    attn_combine_kernel merges the splits.
@@ -127,6 +124,10 @@ __device__ __forceinline__ void row_copy16(const uint8_t* rp, uint32_t voff, uin
                  : "memory", "m0");
 }
 
+__device__ __forceinline__ float max8(const float (&d)[8]) {
+    return fmaxf(fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3])), fmaxf(fmaxf(d[4], d[5]), fmaxf(d[6], d[7])));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
@@ -160,7 +161,7 @@ struct __align__(16) AttnShared {
     float ezf[kScaled];                     // e4m3: logit factor sm * log2(e) * row scale
     float epf[kScaled];                     // e4m3: row scale (weights the probability)
     int32_t list_own[kListOwn];             // compacted valid record ids (e4m3)
-    float rope_cs[kMaxRope][2];
+    float rope_cs[kD / 2][2];               // (cos, sin) per channel pair; (1, 0) off the rotary channels
     double rope_inv[kMaxRope];              // base^(-2j/r), once per workgroup
     int cnt[kIdsPerThread][kWaves];         // valid ids per (chunk, wave)
     __device__ __forceinline__ int32_t* list() {
@@ -310,8 +311,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         }
         // rotary channels [r0, kD) get the inverse rotation (one split
         // only).  In the read-back layout a lane keeps the same 4 channels
-        // for all 16 rows, so it fetches its two rotations once per half.
-        const int r0 = p.nsplit == 1 ? kD - p.rope_dims : kD;
+        // for all 16 rows, so it fetches its two rotations once per half
+        // (the table holds (cos, sin) for every channel pair, (1, 0) below r0)
+        int r0 = p.nsplit == 1 ? kD - p.rope_dims : kD;
+        asm volatile("" : "+s"(r0));  // tested per half here, not hoisted out of the item loop
         static_assert(kWaves * 16 * kStagePitch <= 2 * kBuf, "staging fits the last two tile buffers");
         uint8_t* stage = &sh.xb[AttnShared<KVDT>::kNB - 2][0] + wave * 16 * kStagePitch;
 #pragma unroll
@@ -319,11 +322,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
             for (int u = 0; u < 16; ++u)
                 *reinterpret_cast<f32x4*>(stage + l16 * kStagePitch + 4 * (16 * u + 4 * g)) = acc[16 * half + u] * f;
-            const int c0 = 256 * half + 4 * lane;  // this lane's channels c0 .. c0+3
-            const bool rot0 = c0 >= r0, rot1 = c0 + 2 >= r0;
-            const int j0 = rot0 ? (c0 - r0) >> 1 : 0, j1 = rot1 ? (c0 + 2 - r0) >> 1 : 0;
-            const float cs0 = sh.rope_cs[j0][0], sn0 = sh.rope_cs[j0][1];
-            const float cs1 = sh.rope_cs[j1][0], sn1 = sh.rope_cs[j1][1];
+            const bool rot = 256 * half + 256 > r0;  // wave-uniform: this half holds rotary channels
+            // this lane's channels 256*half + 4*lane .. +3: pairs p0, p0 + 1
+            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sh.rope_cs[128 * half + 2 * lane][0]);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows visible to the wave
             f32x4 rows[16];  // all reads in flight at once
 #pragma unroll
@@ -331,11 +332,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 f32x4 v = rows[r];
-                const float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
-                v[0] = rot0 ? x0 * cs0 + y0 * sn0 : x0;
-                v[1] = rot0 ? -x0 * sn0 + y0 * cs0 : y0;
-                v[2] = rot1 ? x1 * cs1 + y1 * sn1 : x1;
-                v[3] = rot1 ? -x1 * sn1 + y1 * cs1 : y1;
+                if (rot) {
+                    const float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
+                    v[0] = x0 * cs[0] + y0 * cs[1];
+                    v[1] = y0 * cs[0] - x0 * cs[1];
+                    v[2] = x1 * cs[2] + y1 * cs[3];
+                    v[3] = y1 * cs[2] - x1 * cs[3];
+                }
                 *reinterpret_cast<f32x4*>(dst + r * kD + 256 * half + 4 * lane) = v;
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites
@@ -481,8 +484,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (p.nsplit == 1)
-            for (int i = tid; i < rd / 2; i += kThreads)
-                rope_cos_sin(t, sh.rope_inv[i], sh.rope_cs[i][0], sh.rope_cs[i][1]);
+            for (int i = tid; i < kD / 2; i += kThreads) {
+                const int j = i - (kD - rd) / 2;  // rotary pair index of channel pair i
+                float c = 1.f, sn = 0.f;
+                if (j >= 0) rope_cos_sin(t, sh.rope_inv[j], c, sn);
+                sh.rope_cs[i][0] = c;
+                sh.rope_cs[i][1] = sn;
+            }
 
         // tile `it` visible in LDS to every wave; the copies of the tile two
         // ahead go out.  The next item's inputs are fetched in tile 0, after
@@ -508,9 +516,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         // four steps of two k-step pairs each, which the P.V of the previous
         // tile interleaves with its MFMAs; the row chunks of pair i+2 are
         // read before the MFMAs of pair i (two pairs in flight hide the LDS
-        // latency).  qk_end turns the sums into z in log2 units (entries
-        // 16*mt + 4g + v of head h) and returns the head's tile max.  Padding
-        // entries repeat a real row, so they may take part in the max; only
+        // latency).  qk_end forms d = z - m for the lane's entries 16*mt +
+        // 4g + v of head h (z in log2 units, m the head's reference) and
+        // reports whether any of them exceeds the lazy threshold.  Padding
+        // entries repeat a real row, so they may take part in a maximum; only
         // their probabilities are dropped.
         struct Qk {
             f32x4 s[4];
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 q.s[3] = mfma16x16x32(as_bf16x8(q.ka[k][3]), qf[i + 1], q.s[3]);
             }
         };
-        auto qk_end = [&](int it, Qk& q, float (&z)[8]) -> float {
+        auto qk_end = [&](int it, Qk& q, float m, float (&d)[8]) -> bool {
             const f32x4 s0 = q.s[0] + q.s[2];
             const f32x4 s1 = q.s[1] + q.s[3];
             if constexpr (KVDT == DT_E4M3) {
@@ -551,36 +560,42 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    z[v] = s0[v] * f0[v];
-                    z[4 + v] = s1[v] * f1[v];
+                    d[v] = fmaf(s0[v], f0[v], -m);
+                    d[4 + v] = fmaf(s1[v], f1[v], -m);
                 }
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    z[v] = s0[v] * cz;
-                    z[4 + v] = s1[v] * cz;
+                    d[v] = fmaf(s0[v], cz, -m);
+                    d[4 + v] = fmaf(s1[v], cz, -m);
                 }
             }
-            const float tm =
-                fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-            return max4_rows(tm);
+            return max8(d) > kJump;
         };
-        // Softmax of tile `it` relative to m, in eight steps that the P.V of
-        // the previous tile interleaves with its MFMAs.  Steps 0-3: two
-        // probabilities each (padding entries dropped without a branch);
-        // step 4: their sum (and the e4m3 row scales); steps 4-7: one packed
-        // pair each of P = hi + lo in bf16 (hi is P rounded, lo the rounding
-        // error).
+        // Softmax of tile `it`, in eight steps that the P.V of the previous
+        // tile interleaves with its MFMAs.  Steps 0-3: two probabilities
+        // 2^(d - shift) each; step 4: their sum (and the e4m3 row scales);
+        // steps 4-7: one packed pair each of P = hi + lo in bf16 (hi is P
+        // rounded, lo the rounding error).  In the stream (MASK false) no
+        // entry is dropped and the shift is 0: tiles that hold padding
+        // entries, or in which some head passes the lazy threshold, are
+        // redone afterwards with MASK true.
         struct Soft {
             float pr[8];
             float psum;
             uint32_t phi[4], plo[4];
         };
-        auto soft_step = [&](int j, int it, const float (&z)[8], float m, Soft& s) {
+        auto soft_step = [&](int j, int it, const float (&d)[8], float shift, Soft& s, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
             if (j < 4) {
-                const int lim = nvalid - it * kTile;  // entries of this tile that are real
-                s.pr[j] = (4 * g + j < lim) ? __builtin_amdgcn_exp2f(z[j] - m) : 0.f;
-                s.pr[4 + j] = (16 + 4 * g + j < lim) ? __builtin_amdgcn_exp2f(z[4 + j] - m) : 0.f;
+                if constexpr (MASK) {
+                    const int lim = nvalid - it * kTile;  // entries of this tile that are real
+                    s.pr[j] = (4 * g + j < lim) ? __builtin_amdgcn_exp2f(d[j] - shift) : 0.f;
+                    s.pr[4 + j] = (16 + 4 * g + j < lim) ? __builtin_amdgcn_exp2f(d[4 + j] - shift) : 0.f;
+                } else {
+                    s.pr[j] = __builtin_amdgcn_exp2f(d[j]);
+                    s.pr[4 + j] = __builtin_amdgcn_exp2f(d[4 + j]);
+                }
                 // computed here, in the MFMA shadow: the results are only read
                 // after the loop's branch, past which the compiler would sink them
                 asm volatile("" : "+v"(s.pr[j]), "+v"(s.pr[4 + j]));
@@ -605,6 +620,24 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                                   s.pr[2 * i + 1] - __uint_as_float(hi & 0xFFFF0000u));
             asm volatile("" : "+v"(s.phi[i]), "+v"(s.plo[i]));
             if (j == 4) asm volatile("" : "+v"(s.psum));
+        };
+        // The exact softmax of tile `it` (first tile of an item, padded
+        // tiles, threshold passes): heads whose tile maximum exceeds the
+        // reference by more than kJump move their reference to it, rescaling
+        // O and l; padding entries are dropped.
+        auto soft_exact = [&](int it, const float (&d)[8], Soft& s) {
+            const float hm = max4_rows(max8(d));  // head's tile max relative to m_run
+            const bool jump = hm > kJump;
+            const float shift = jump ? hm : 0.f;
+            if (__any(jump)) {
+                const float sc = __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+                for (int u = 0; u < 32; ++u) acc[u] *= sc;
+                l_run *= sc;
+            }
+            m_run += shift;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) soft_step(j, it, d, shift, s, std::true_type{});
         };
         auto packed = [](const uint32_t (&w)[4]) { return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}); };
         // O^T += X^T P^T for tile `it`: channels 16*u + 4g + v, head h.  The
@@ -659,9 +692,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 __builtin_amdgcn_sched_barrier(0);
                 qk_step(q, j);
             }
-            m_run = qk_end(0, q, z);  // the first tile sets the reference
+            qk_end(0, q, 0.f, z);
+            // the first tile sets the reference: the head's maximum
+            const float hm = max4_rows(max8(z));
+            m_run = hm;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) soft_step(j, 0, z, m_run, s);
+            for (int v = 0; v < 8; ++v) z[v] -= hm;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) soft_step(j, 0, z, 0.f, s, std::true_type{});
             l_run = s.psum;
             bhi = packed(s.phi);
             blo = packed(s.plo);
@@ -694,9 +732,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             tile_ready(it + 1);
             Qk q;
             qk_begin(it + 1, q);
-            float zn[8];
-            float m_new = m_run;
-            bool jump = false;
+            float dn[8];
+            bool over = false;
             Soft s;
             tile_pv(it, bhi, blo, [&](int j) {
                 if constexpr (CP) row_copy16(rp[j], voff, cdst + j * kXPitch);
@@ -704,27 +741,18 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     qk_step(q, j);
                     return;
                 }
-                if (j == 4) {
-                    const float tmn = qk_end(it + 1, q, zn);
-                    jump = tmn > m_run + kJump;
-                    m_new = jump ? tmn : m_run;
-                }
-                soft_step(2 * (j - 4), it + 1, zn, m_new, s);
-                soft_step(2 * (j - 4) + 1, it + 1, zn, m_new, s);
+                if (j == 4) over = qk_end(it + 1, q, m_run, dn);
+                soft_step(2 * (j - 4), it + 1, dn, 0.f, s, std::false_type{});
+                soft_step(2 * (j - 4) + 1, it + 1, dn, 0.f, s, std::false_type{});
             });
-            if (__any(jump)) {  // rare: the reference moves; O and l follow it
-                const float sc = jump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-#pragma unroll
-                for (int u = 0; u < 32; ++u) acc[u] *= sc;
-                l_run *= sc;
-            }
+            // rare: a head passes the threshold, or the tile holds padding
+            if (__any(over) || nvalid - (it + 1) * kTile < kTile) soft_exact(it + 1, dn, s);
             l_run += s.psum;
             // O stays in the accumulation registers across iterations (else
             // the compiler keeps it in VGPRs and copies it in and out of the
             // MFMA accumulators every tile)
 #pragma unroll
             for (int u = 0; u < 32; ++u) asm volatile("" : "+a"(acc[u]));
-            m_run = m_new;
             bhi = packed(s.phi);
             blo = packed(s.plo);
         };
