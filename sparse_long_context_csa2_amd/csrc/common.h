@@ -133,6 +133,11 @@ __device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
 }
 
 // max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+// max(x, 0) as one signed-integer max of the bits: a negative float has the
+// sign bit set, so it compares below 0 (fmaxf on a matrix-unit result costs
+// an extra canonicalising max)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ float max4_rows(float x) {
     float a, b;
     pair_xor16(x, a, b);

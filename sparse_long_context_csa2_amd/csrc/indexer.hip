@@ -17,7 +17,8 @@
 //    a lane holds 8 heads of one record, two xor-shuffles finish the sum.
 //    Decode rows (one query token) give each wave its own record tiles.
 //  * idx_prefill_kernel -- many tokens of one sequence (no pool): 32x32x16
-//    MFMAs over LDS-staged key tiles shared by a workgroup's 8 tokens.
+//    MFMAs, one token per wave with its query in registers, key tiles
+//    streamed through LDS and shared by the workgroup's 8 tokens.
 //  * idx_generic_kernel -- any head count/dim and dtype, one thread per
 //    (row, column), fp32 FMA; used for small shapes such as the toy.
 #include <type_traits>
@@ -43,6 +44,10 @@ struct IdxP {
     float* out;
     int tiles_per_block;
 };
+
+// LDS hand-off barrier: this wave's LDS accesses are complete, then all
+// waves meet (global loads in flight are not waited for)
+__device__ __forceinline__ void lds_sync_all() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int visible_count(int64_t t, int m, int nrec) {
     // records s with m*s + m - 1 <= t  <=>  s < floor((t + 1) / m)
@@ -171,8 +176,8 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
             for (int v = 0; v < 4; ++v) {
                 float d0 = acc0[v], d1 = acc1[v];
                 if (KDT == DT_E4M3) { d0 *= T.kscale; d1 *= T.kscale; }
-                part += wv[0][v] * fmaxf(d0, 0.f);
-                part += wv[1][v] * fmaxf(d1, 0.f);
+                part += wv[0][v] * relu(d0);
+                part += wv[1][v] * relu(d1);
             }
             part += shfl_xor_f(part, 16);
             part += shfl_xor_f(part, 32);
@@ -208,171 +213,291 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
 
 // Prefill scoring: many query tokens of one sequence against the records
 // they may see -- a causal GEMM (tokens x heads) x 128 x records with a
-// ReLU and weighted head-sum epilogue.  Records are stationary: a
-// workgroup owns kP2Rec consecutive records, converts their keys to bf16
-// in LDS once, and its waves stream query tokens past them, each token's
-// query fragments read straight from global memory by the one wave that
-// scores it.  32x32x16 MFMAs: M = the 32 heads of the token, N = 32
-// records, K = 128 dims in 8 k-steps.  Lane group kg takes dims
-// 64 kg + 8 ks .. +7 at k-step ks in both operands, so a lane's query
-// fragments are 128 contiguous bytes of one head row.  Records come in
-// pairs of 32-record sets: after the epilogue one lane swap leaves lane l
-// holding the score of record 64 sp + l, and a wave stores 256 contiguous
-// bytes.  Sets that the token cannot see at all are skipped.
-constexpr int kP2Rec = 256;            // records per workgroup
-constexpr int kP2TokW = 8;             // tokens per wave
-constexpr int kP2Tok = 4 * kP2TokW;    // tokens per workgroup
-constexpr int kP2Pitch = kDi * 2 + 16; // bytes per LDS key row: conflict-free operand reads
+// ReLU and weighted head-sum epilogue.
+//
+// Tokens are stationary: a workgroup of 8 waves takes a block of 8
+// consecutive tokens of one sequence, one token per wave, whose query
+// fragments stay in registers, and streams the key rows the block can see
+// through LDS in tiles of 64 records.  Blocks are numbered by position, and
+// workgroup w takes blocks nb-1-w and w: under causal visibility every
+// workgroup then has about the same number of tiles.  32x32x16 MFMAs:
+// M = the 32 heads of the token, N = 32 records, K = 128 dims in 8 k-steps.
+// Lane group kg takes dims 64 kg + 8 ks .. +7 at k-step ks in both
+// operands.  After the epilogue one lane swap leaves lane l holding the
+// score of record 64 k + l of tile k; a wave keeps eight tiles' scores in
+// registers and then stores them.
+//
+// Memory: the block's queries and head weights, and the key tiles, are
+// copied global -> LDS with global_load_lds (e4m3 key rows go through
+// registers and are converted exactly to bf16); the second block's queries
+// are copied while the first block runs.  Tiles come in periods of two, one
+// barrier each, the next period's copies in flight during the current one.
+// In LDS a 256-byte row (one head's query, one record's key) keeps its
+// 16-byte chunk c at slot c ^ (r mod 16), so the 16 rows that one phase of
+// an operand read touches fill all banks.
+constexpr int kPWaves = 8;               // waves per workgroup = tokens per block
+constexpr int kPTile = 64;               // records per tile
+constexpr int kPRing = 4;                // tile buffers: two periods of two tiles
+constexpr int kPRowB = kDi * 2;          // bytes per LDS row (bf16)
+constexpr int kPChunk = 8;               // tiles whose scores are stored together
+constexpr int kPQBytes = kHi * kPRowB;   // one token's queries
+
+__device__ __forceinline__ uint32_t lds_u32(const void* ptr) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint8_t*)(ptr)));
+}
+
+// One 1 KiB global -> LDS copy: lane l moves the 16 bytes at base + off to
+// LDS byte address lds + 16 l (gfx950 global_load_lds_dwordx4, LDS address
+// in M0).  Completion is awaited with explicit vmcnt waits.
+__device__ __forceinline__ void copy_lds16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
 
 template <int KDT>
-__global__ __launch_bounds__(256, 2) void idx_prefill_kernel(IdxP p) {
-    __shared__ __align__(16) uint8_t kl[kP2Rec * kP2Pitch];
-    __shared__ float ksl[kP2Rec];
+__global__ __launch_bounds__(kPWaves * 64, 1) void idx_prefill_kernel(IdxP p, int nb) {
+    __shared__ __align__(16) uint8_t kt[kPRing][kPTile * kPRowB];
+    __shared__ __align__(16) uint8_t qs[kPWaves][kPQBytes];
+    __shared__ __align__(16) float wsh[kPWaves][kHi];
+    __shared__ float kst[kPRing][kPTile];  // e4m3 row scales
     constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
-    constexpr int kPairs = kP2Rec / 64;  // 64-record set pairs of the group
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;   // record within a set (B and C column), head (A row)
     const int kg = lane >> 5;  // k group
-    // Workgroup L runs on XCD L % 8 (round-robin dispatch).  The record
-    // groups of one token block get ids that are equal mod 8 and adjacent in
-    // that XCD's order, so the block's query rows are read into one L2;
-    // later token blocks (more visible records) come first.
-    const int ntb = (p.Tq + kP2Tok - 1) / kP2Tok;
-    const int nblk = p.B * ntb;
-    const int ngr = (p.ncols + kP2Rec - 1) / kP2Rec;
-    const int L = static_cast<int>(blockIdx.x);
-    const int mi = L / 8;
-    const int tbi = (mi / ngr) * 8 + L % 8;
-    if (tbi >= nblk) return;  // padding of the id space to a multiple of 8 blocks
-    const int blk = nblk - 1 - tbi;
-    const int b = blk / ntb;
-    const int t0 = (blk % ntb) * kP2Tok;
-    const int R0 = (mi % ngr) * kP2Rec;
-    const int nr = min(kP2Rec, p.ncols - R0);  // columns of this group
-    const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
-    const size_t row0 = static_cast<size_t>(b) * p.Tq;
+    const int sw = j & 15;     // chunk swizzle of rows j and 32 + j
+    const int w0 = static_cast<int>(blockIdx.x);
+    // a heavy block, then a light one (whose queries arrive meanwhile)
+    const int npass = nb - 1 - w0 > w0 ? 2 : 1;
+    const int jbs[2] = {nb - 1 - w0, w0};
 
-    // this wave's tokens: visibility (lane i holds token i's), and the
-    // first token's query fragments and head weights
-    const int tw0 = t0 + kP2TokW * wave;
-    const int tw1 = min(tw0 + kP2TokW, p.Tq);
-    const int vis_l = (lane < tw1 - tw0) ? visible_count(p.q_pos[row0 + tw0 + lane], p.m, nrec) : 0;
-    struct Tok {
-        bf16x8 a[8];
-        f32x4 w[4];
-    };
-    auto tload = [&](int t, Tok& x) {
-        const u32x4* qh = reinterpret_cast<const u32x4*>(p.q + ((row0 + t) * kHi + j) * kDi + 64 * kg);
+    // queries of block jb -> LDS (wave w: token t0 + w, eight 4-row
+    // copies), and wave 0 the eight tokens' head weights (one copy)
+    auto qcopy = [&](int jb) {
+        const int b = jb % p.B;
+        const int t0 = (jb / p.B) * kPWaves;
+        const size_t row0 = static_cast<size_t>(b) * p.Tq;
+        const int tq = min(t0 + wave, p.Tq - 1);  // past the end: a valid row, never stored
+        const uint16_t* qrow = p.q + (row0 + tq) * kHi * kDi;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) x.a[ks] = as_bf16x8(qh[ks]);
-        // weights of this lane's 16 heads: 8 (v / 4) + 4 kg + v % 4
-        const float* wr = p.w + (row0 + t) * kHi + 4 * kg;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) x.w[q4] = *reinterpret_cast<const f32x4*>(wr + 8 * q4);
-    };
-    Tok cur;
-    if (tw0 < tw1) tload(tw0, cur);
-
-    // keys of the group -> bf16 rows in LDS (records past N are zero rows,
-    // masked below like every record the token cannot see)
-    {
-        typedef typename std::conditional<KDT == DT_BF16, u32x4, u32x2>::type Raw;
-        constexpr int kChunkBytes = (KDT == DT_BF16) ? 16 : 8;  // 8 dims
-        const uint8_t* kb = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
-        // all loads first and unconditional (a clamped row, zeroed after):
-        // a branch around each load would serialise them
-        Raw raw[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c = i * 256 + tid;  // 16 chunks per record
-            const int rec = min(R0 + (c >> 4), p.N - 1);
-            raw[i] = *reinterpret_cast<const Raw*>(kb + static_cast<size_t>(rec) * kRowBytes + kChunkBytes * (c & 15));
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            copy_lds16(qrow, static_cast<uint32_t>(r * kPRowB + 16 * ((lane & 15) ^ (r & 15))),
+                       lds_u32(&qs[wave][0]) + i * 4 * kPRowB);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c = i * 256 + tid;
-            u32x4 v;
-            if constexpr (KDT == DT_BF16) v = raw[i];
-            else v = e4m3x8_to_bf16x8(raw[i]);
-            if (R0 + (c >> 4) >= p.N) v = u32x4{0, 0, 0, 0};
-            *reinterpret_cast<u32x4*>(kl + (c >> 4) * kP2Pitch + 16 * (c & 15)) = v;
+        if (wave == 0) {
+            const int tw = min(t0 + (lane >> 3), p.Tq - 1) - t0;
+            copy_lds16(p.w + (row0 + t0) * kHi, static_cast<uint32_t>((tw * kHi + 4 * (lane & 7)) * 4), lds_u32(&wsh[0][0]));
         }
-        if constexpr (KDT == DT_E4M3)
-            ksl[tid] = R0 + tid < p.N ? p.ks[static_cast<size_t>(b) * p.N + R0 + tid] : 0.f;
-    }
-    __syncthreads();
+    };
+    qcopy(jbs[0]);
 
-    // Set pairs 0 .. NP-1 of one token in one branch-free block (their
-    // MFMAs, operand reads and epilogues interleave); pairs past NP are
-    // out of the token's sight and score -inf.
-    float sc[kP2TokW][kPairs];
-    auto score_pairs = [&](auto np_tag, const Tok& x, int vis, float (&out)[kPairs]) {
-        constexpr int NP = decltype(np_tag)::value;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            if (npass < 2) break;
+            lds_sync_all();  // every wave is done with the previous block's tiles
+        }
+        const int jb = jbs[pass];
+        const int b = jb % p.B;
+        const int t0 = (jb / p.B) * kPWaves;
+        const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+        const size_t row0 = static_cast<size_t>(b) * p.Tq;
+        // visibility: lane i (mod 8) holds token t0 + i's; the block's tiles
+        // cover the most that any of its tokens sees
+        const int ti = t0 + (lane & 7);
+        const int vis_l = ti < p.Tq ? visible_count(p.q_pos[row0 + ti], p.m, nrec) : 0;
+        int vmax = vis_l;
+        vmax = max(vmax, __shfl_xor(vmax, 1));
+        vmax = max(vmax, __shfl_xor(vmax, 2));
+        vmax = max(vmax, __shfl_xor(vmax, 4));
+        vmax = __builtin_amdgcn_readfirstlane(vmax);
+        const int nt = (min(vmax, p.ncols) + kPTile - 1) / kPTile;
+        const int t = t0 + wave;
+        const bool live = t < p.Tq;
+        const int vis = __builtin_amdgcn_readlane(vis_l, wave);
+        const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+
+        // bf16 key tile k -> buffer k % kPRing: wave w copies rows 8w .. 8w+7
+        // (two 4-row copies; lane l takes row 4i + l/16, chunk slot l % 16)
+        auto issue = [&](int k) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * wave + ii;
+                const int r = 4 * i + (lane >> 4);
+                const int rec0 = k * kPTile;
+                const int rr = min(rec0 + r, p.N - 1) - rec0;  // rows past N repeat the last (masked)
+                copy_lds16(kbase + static_cast<size_t>(rec0) * kRowBytes,
+                           static_cast<uint32_t>(rr * kRowBytes + 16 * ((lane & 15) ^ (r & 15))),
+                           lds_u32(&kt[k % kPRing][0]) + i * 4 * kPRowB);
+            }
+        };
+        // e4m3 key tiles: thread tid stages 16 dims (two chunks) of row
+        // tid / 8, threads 0..63 the row scales; even and odd tiles have a
+        // register set each
+        u32x4 eraw[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+        float esc[2] = {0.f, 0.f};
+        auto eload = [&](int k, int par) {
+            const int r = tid >> 3;
+            const int rec = min(k * kPTile + r, p.N - 1);
+            eraw[par] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(rec) * kRowBytes + 16 * (tid & 7));
+            if (tid < kPTile) esc[par] = p.ks[static_cast<size_t>(b) * p.N + min(k * kPTile + tid, p.N - 1)];
+        };
+        auto eland = [&](int k, int par) {
+            const int r = tid >> 3;
+            const int c = 2 * (tid & 7);
+            uint8_t* row = &kt[k % kPRing][r * kPRowB];
+            *reinterpret_cast<u32x4*>(row + 16 * (c ^ (r & 15))) = e4m3x8_to_bf16x8(u32x2{eraw[par][0], eraw[par][1]});
+            *reinterpret_cast<u32x4*>(row + 16 * ((c + 1) ^ (r & 15))) = e4m3x8_to_bf16x8(u32x2{eraw[par][2], eraw[par][3]});
+            if (tid < kPTile) kst[k % kPRing][tid] = esc[par];
+        };
+        // Period of tiles k, k+1 (k even, > 0): its tiles are visible to
+        // every wave after the barrier; the next period's tiles go out
+        // into the buffers of the previous period.
+        auto period = [&](int k) {
+            if constexpr (KDT == DT_BF16) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_sync_all();
+                if (k + 2 < nt) issue(k + 2);
+                if (k + 3 < nt) issue(k + 3);
+            } else {
+                lds_sync_all();
+                if (k + 2 < nt) eland(k + 2, 0);
+                if (k + 3 < nt) eland(k + 3, 1);
+                if (k + 4 < nt) eload(k + 4, 0);
+                if (k + 5 < nt) eload(k + 5, 1);
+            }
+        };
+
+        // Period 0: tiles 0, 1 and the queries land; the fragments move to
+        // registers; the next block's queries and the tiles of period 1 go out.
+        if constexpr (KDT == DT_BF16) {
+            if (nt > 0) issue(0);
+            if (nt > 1) issue(1);
+        } else {
+            if (nt > 0) eload(0, 0);
+            if (nt > 1) eload(1, 1);
+            if (nt > 0) eland(0, 0);
+            if (nt > 1) eland(1, 1);
+            if (nt > 2) eload(2, 0);
+            if (nt > 3) eload(3, 1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_sync_all();
+        bf16x8 qa[8];
         float wv[16];
+        {
+            const uint8_t* qr = &qs[wave][j * kPRowB];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) wv[v] = x.w[v / 4][v % 4];
+            for (int ks = 0; ks < 8; ++ks) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * ((8 * kg + ks) ^ sw)));
+            // weights of this lane's 16 heads: 8 (v / 4) + 4 kg + v % 4
 #pragma unroll
-        for (int sp = 0; sp < kPairs; ++sp) {
-            out[sp] = -__builtin_huge_valf();
-            if (sp < NP) {  // folds: sp is unrolled, NP a constant
-                const int rb = 64 * sp;
-                const uint8_t* k0 = kl + (rb + j) * kP2Pitch + 128 * kg;
-                const uint8_t* k1 = k0 + 32 * kP2Pitch;
-                f32x16 c0, c1;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wsh[wave][8 * q4 + 4 * kg]);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) c0[v] = c1[v] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(k0 + 16 * ks));
-                    const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(k1 + 16 * ks));
-                    c0 = mfma32x32x16(x.a[ks], b0, c0);
-                    c1 = mfma32x32x16(x.a[ks], b1, c1);
-                }
-                float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    s0 = fmaf(wv[v], fmaxf(c0[v], 0.f), s0);
-                    s1 = fmaf(wv[v], fmaxf(c1[v], 0.f), s1);
-                }
-                // lanes 0..31 finish set 0 (records rb + l), lanes 32..63 set 1
-                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
-                float tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-                if constexpr (KDT == DT_E4M3) tot *= ksl[rb + lane];  // the row scale is >= 0: it commutes with the ReLU
-                if (R0 + rb + lane < vis) out[sp] = tot;
+                for (int e = 0; e < 4; ++e) wv[4 * q4 + e] = w4[e];
             }
         }
-    };
-    // Scores stay in registers until the wave's tokens are done: a store
-    // inside the loop would make every wait for the next token's loads wait
-    // for the stores as well.
-#pragma unroll
-    for (int i = 0; i < kP2TokW; ++i) {
-        const int t = tw0 + i;
-        if (t >= tw1) break;
-        Tok nxt;
-        if (t + 1 < tw1) tload(t + 1, nxt);
-        const int vis = __builtin_amdgcn_readlane(vis_l, i);
-        // set pairs holding a record the token sees (all of them hold columns)
-        const int np = min(max(vis - R0 + 63, 0) >> 6, (nr + 63) >> 6);
-        switch (np) {
-            case 0: score_pairs(std::integral_constant<int, 0>{}, cur, vis, sc[i]); break;
-            case 1: score_pairs(std::integral_constant<int, 1>{}, cur, vis, sc[i]); break;
-            case 2: score_pairs(std::integral_constant<int, 2>{}, cur, vis, sc[i]); break;
-            case 3: score_pairs(std::integral_constant<int, 3>{}, cur, vis, sc[i]); break;
-            default: score_pairs(std::integral_constant<int, 4>{}, cur, vis, sc[i]); break;
+        if (pass == 0 && npass == 2) {
+            lds_sync_all();  // every wave holds its fragments: the query buffer is free
+            qcopy(jbs[1]);
         }
-        cur = nxt;
-    }
+        if constexpr (KDT == DT_BF16) {
+            if (nt > 2) issue(2);
+            if (nt > 3) issue(3);
+        } else {
+            if (nt > 2) eland(2, 0);
+            if (nt > 3) eland(3, 1);
+            if (nt > 4) eload(4, 0);
+            if (nt > 5) eload(5, 1);
+        }
+
+        // epilogue of a tile's MFMA results: lane l gets the score of record
+        // 64k + l
+        auto epi = [&](int k, const f32x16 (&c)[2], float scl) -> float {
+            float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kP2TokW; ++i) {
-        const int t = tw0 + i;
-        if (t >= tw1) break;
-        float* orow = p.out + (row0 + t) * p.ncols + R0;
+            for (int v = 0; v < 16; ++v) {
+                s0[v & 3] = fmaf(wv[v], relu(c[0][v]), s0[v & 3]);
+                s1[v & 3] = fmaf(wv[v], relu(c[1][v]), s1[v & 3]);
+            }
+            const float a0 = (s0[0] + s0[1]) + (s0[2] + s0[3]);
+            const float a1 = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+            // lanes 0..31 finish set 0 (records 64k + l), lanes 32..63 set 1
+            const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+            float tot = __uint_as_float(rs[0]) + __uint_as_float(rs[1]);
+            if constexpr (KDT == DT_E4M3) tot *= scl;  // the row scale is >= 0: it commutes with the ReLU
+            return k * kPTile + lane < vis ? tot : -__builtin_huge_valf();
+        };
+        // MFMAs of tile k (set 0: rows j, set 1: rows 32 + j) with the
+        // epilogue of tile kp (results cp, row scale sp) spread between them:
+        // all operand reads first, then one MFMA and four VALU instructions at
+        // a time.  The row scale of tile k is read now, before the barrier
+        // that lets its buffer be refilled.
+        auto mma_epi = [&](int k, f32x16 (&c)[2], float& scl, int kp, const f32x16 (&cp)[2], float sp) -> float {
+            if constexpr (KDT == DT_E4M3) scl = kst[k % kPRing][lane];
+            const uint8_t* r0p = &kt[k % kPRing][j * kPRowB];
+            const uint8_t* r1p = r0p + 32 * kPRowB;
+            bf16x8 bop[8][2];
 #pragma unroll
-        for (int sp = 0; sp < kPairs; ++sp)
-            if (64 * sp + lane < nr) orow[64 * sp + lane] = sc[i][sp];
+            for (int ks = 0; ks < 8; ++ks) {
+                const int cs = 16 * ((8 * kg + ks) ^ sw);
+                bop[ks][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(r0p + cs));
+                bop[ks][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(r1p + cs));
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) c[0][v] = c[1][v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                c[0] = mfma32x32x16(qa[ks], bop[ks][0], c[0]);
+                c[1] = mfma32x32x16(qa[ks], bop[ks][1], c[1]);
+            }
+            const float e = epi(kp, cp, sp);
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // LDS reads
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+            }
+            return e;
+        };
+
+        // Tile k's MFMAs and tile k-1's epilogue form one block, so the
+        // epilogue's VALU work fills the matrix pipeline's shadow.
+        float* orow = p.out + (row0 + (live ? t : t0)) * p.ncols;
+        float sc[kPChunk];
+        auto flush = [&](int kb, int cnt) {  // scores of tiles kb .. kb+cnt-1
+            if (live) {
+#pragma unroll
+                for (int u = 0; u < kPChunk; ++u) {
+                    const int c = (kb + u) * kPTile + lane;
+                    if (u < cnt && c < p.ncols) orow[c] = sc[u];
+                }
+            }
+        };
+        f32x16 cc[2][2];
+        float cscl[2] = {1.f, 1.f};  // e4m3 row scale of the record each lane scores
+        for (int k0 = 0; k0 < nt; k0 += kPChunk) {
+#pragma unroll
+            for (int i = 0; i < kPChunk; ++i) {
+                const int k = k0 + i;
+                if (k < nt) {
+                    if ((i & 1) == 0 && k > 0) period(k);
+                    // (for k = 0 the epilogue runs on stale registers; unused)
+                    const float e = mma_epi(k, cc[i & 1], cscl[i & 1], k - 1, cc[(i + 1) & 1], cscl[(i + 1) & 1]);
+                    if (k > 0) sc[(i + kPChunk - 1) % kPChunk] = e;
+                    if (i == 0 && k > 0) flush(k0 - kPChunk, kPChunk);
+                    if (k == nt - 1) {
+                        sc[i] = epi(k, cc[i & 1], cscl[i & 1]);
+                        flush(k0, i + 1);
+                    }
+                }
+            }
+        }
+        // columns past the block's tiles: nothing there is visible
+        if (live)
+            for (int c = nt * kPTile + lane; c < p.ncols; c += 64) orow[c] = -__builtin_huge_valf();
     }
 }
 
@@ -451,8 +576,8 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
     if (index_scores_mfma_ok(a)) {
         const int ntiles = (a.ncols + 15) / 16;
         const int rows = a.B * a.Tq;
-        // Prefill-shaped work (many tokens of one sequence, no pool): waves
-        // share record tiles across 16 tokens.
+        // Prefill-shaped work (many tokens of one sequence, no pool): blocks of
+        // 8 tokens, two blocks (a light and a heavy one) per workgroup.
         if (!a.pool && a.Tq >= 16) {
             IdxP p;
             p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
@@ -465,12 +590,12 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
             p.pool = nullptr;
             p.out = a.scores;
             p.tiles_per_block = 0;
-            const int nblk8 = (a.B * ((a.Tq + kP2Tok - 1) / kP2Tok) + 7) / 8 * 8;
-            const dim3 grid(nblk8 * ((a.ncols + kP2Rec - 1) / kP2Rec));
+            const int nb = a.B * ((a.Tq + kPWaves - 1) / kPWaves);
+            const dim3 grid((nb + 1) / 2);
             if (a.k_dtype == DT_BF16)
-                hipLaunchKernelGGL(idx_prefill_kernel<DT_BF16>, grid, dim3(256), 0, st, p);
+                hipLaunchKernelGGL(idx_prefill_kernel<DT_BF16>, grid, dim3(kPWaves * 64), 0, st, p, nb);
             else
-                hipLaunchKernelGGL(idx_prefill_kernel<DT_E4M3>, grid, dim3(256), 0, st, p);
+                hipLaunchKernelGGL(idx_prefill_kernel<DT_E4M3>, grid, dim3(kPWaves * 64), 0, st, p, nb);
             return static_cast<int>(hipGetLastError());
         }
         // Decode rows: the largest tiles per block that still gives >= 1024
