@@ -774,64 +774,71 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     }
 }
 
-// Merges split partials: one workgroup per (query, group of 4 heads); each
-// thread owns 8 consecutive channels of one head.
+// Merges split partials: one workgroup per (query, pair of heads).  The
+// split weights w_s = 2^(m_s - a) / den (a the largest of the partial maxima
+// and the sink, den = 2^(sink - a) + sum_s l_s 2^(m_s - a)) are formed by one
+// half-wave per head, one lane per split; then each thread sums four
+// channels of one head over the splits, four splits' loads in flight at a
+// time, and applies the inverse rotation.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
     __shared__ float rope_cs[kMaxRope][2];
-    __shared__ float wts[4][kMaxSplits];
+    __shared__ float wts[2][kMaxSplits];
     const int qr = blockIdx.x;
-    const int h0 = 4 * blockIdx.y;
+    const int h0 = 2 * blockIdx.y;
+    const int tid = threadIdx.x;
+    const int ns = p.nsplit;
     const int64_t t = p.q_pos[qr];
     const int rd = p.rope_dims;
-    for (int i = threadIdx.x; i < rd / 2; i += 256) rope_angle(t, i, rd, p.rope_base, rope_cs[i][0], rope_cs[i][1]);
-    const int ns = p.nsplit;
-    // per-head split weights: w_s = e^{m_s - a} / den
-    if (threadIdx.x < 4) {
-        const int h = h0 + threadIdx.x;
-        const float* ml = p.part_ml + (static_cast<size_t>(qr) * ns * kH + h) * 2;
-        const float sk = p.sink[h] * kLog2e;  // partial maxima are in log2 units
-        float a = sk;
-        for (int s = 0; s < ns; ++s) a = fmaxf(a, ml[static_cast<size_t>(s) * kH * 2]);
-        float den = 0.f;
-        if (a != -__builtin_huge_valf()) {
-            den = __builtin_amdgcn_exp2f(sk - a);
-            for (int s = 0; s < ns; ++s) {
-                const float m = ml[static_cast<size_t>(s) * kH * 2];
-                if (m != -__builtin_huge_valf()) den += ml[static_cast<size_t>(s) * kH * 2 + 1] * __builtin_amdgcn_exp2f(m - a);
-            }
-        }
-        for (int s = 0; s < ns; ++s) {
-            const float m = ml[static_cast<size_t>(s) * kH * 2];
-            wts[threadIdx.x][s] = (den > 0.f && m != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m - a) / den : 0.f;
-        }
+    for (int i = tid; i < rd / 2; i += 256) rope_angle(t, i, rd, p.rope_base, rope_cs[i][0], rope_cs[i][1]);
+    if (tid < 64) {
+        const int hw = tid >> 5, s = tid & 31;
+        const int h = h0 + hw;
+        const float* ml = p.part_ml + ((static_cast<size_t>(qr) * ns + min(s, ns - 1)) * kH + h) * 2;
+        const float m = s < ns ? ml[0] : -__builtin_huge_valf();  // log2 units
+        const float l = s < ns ? ml[1] : 0.f;
+        const float sk = p.sink[h] * kLog2e;
+        float a = m;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+        a = fmaxf(a, sk);
+        const float e = (m != -__builtin_huge_valf() && a != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m - a) : 0.f;
+        float den = l * e;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) den += __shfl_xor(den, o);
+        if (a != -__builtin_huge_valf()) den += __builtin_amdgcn_exp2f(sk - a);
+        if (s < ns) wts[hw][s] = den > 0.f ? e / den : 0.f;
     }
     __syncthreads();
-    const int hl = threadIdx.x >> 6;
+    const int hl = tid >> 7;  // 128 threads per head
     const int h = h0 + hl;
-    const int d = 8 * (threadIdx.x & 63);
-    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-    for (int s = 0; s < ns; ++s) {
-        const float* po = p.part_o + ((static_cast<size_t>(qr) * ns + s) * kH + h) * kD + d;
-        const float wgt = wts[hl][s];
-        x0 += wgt * *reinterpret_cast<const f32x4*>(po);
-        x1 += wgt * *reinterpret_cast<const f32x4*>(po + 4);
+    const int d = 4 * (tid & 127);
+    const float* pb = p.part_o + (static_cast<size_t>(qr) * ns * kH + h) * kD + d;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+        f32x4 v[4];
+        float w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sc = min(s0 + i, ns - 1);  // past the last split: reread it with weight 0
+            v[i] = *reinterpret_cast<const f32x4*>(pb + static_cast<size_t>(sc) * kH * kD);
+            w[i] = s0 + i < ns ? wts[hl][sc] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x += w[i] * v[i];
     }
-    float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     const int r0 = kD - rd;
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
+    for (int i = 0; i < 4; i += 2) {
         const int dd = d + i;
         if (dd >= r0) {
             const int jp = (dd - r0) >> 1;
             const float cs = rope_cs[jp][0], sn = rope_cs[jp][1];
-            const float x = v[i], y = v[i + 1];
-            v[i] = x * cs + y * sn;
-            v[i + 1] = -x * sn + y * cs;
+            const float xa = x[i], ya = x[i + 1];
+            x[i] = xa * cs + ya * sn;
+            x[i + 1] = -xa * sn + ya * cs;
         }
     }
-    float* o = p.out + (static_cast<size_t>(qr) * kH + h) * kD + d;
-    *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    *reinterpret_cast<f32x4*>(p.out + (static_cast<size_t>(qr) * kH + h) * kD + d) = x;
 }
 
 // ---------------------------------------------------------------- generic
@@ -1030,7 +1037,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
             hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(kThreads), 0, st, p);
         int e = static_cast<int>(hipGetLastError());
         if (e || p.nsplit == 1) return e;
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(Q, kH / 4), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(Q, kH / 2), dim3(256), 0, st, p);
         return static_cast<int>(hipGetLastError());
     }
     AttnG p;
