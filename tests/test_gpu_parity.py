@@ -128,7 +128,7 @@ def _score_rows(rows, n, seed):
 
 
 @pytest.mark.parametrize("n,K", [(5, 8), (700, 8), (1024, 512), (1500, 300), (2048, 1), (2049, 2048), (4096, 100),
-                                 (16384, 512), (20000, 2048), (65536, 512)])
+                                 (4097, 2048), (12345, 700), (16384, 512), (16385, 64), (20000, 2048), (65536, 512)])
 def test_topk_exact(n, K):
     _case(f"topk rows=4 n={n} K={K}")
     s = _score_rows(4, n, n + K)
@@ -142,12 +142,15 @@ def test_topk_exact(n, K):
         assert np.all(g[r][len(ref):] == -1)
 
 
-def test_topk_pool_mapping_ties_by_record_id():
-    _case("topk with a pool column map")
-    P, blk, K = 6, 64, 100
+@pytest.mark.parametrize("P", [6, 100])
+def test_topk_pool_mapping_ties_by_record_id(P):
+    """Pool columns map to record ids out of column order; ties in score are
+    broken by record id (P=100: 6400 columns, one workgroup per row)."""
+    _case(f"topk with a pool column map, P={P}")
+    blk, K = 64, 100
     rng = np.random.default_rng(9)
     s = (rng.integers(0, 20, size=(3, P * blk)) / 20.0).astype(np.float32)
-    pool = np.stack([rng.permutation(40)[:P] for _ in range(3)]).astype(np.int32)
+    pool = np.stack([rng.permutation(max(40, 2 * P))[:P] for _ in range(3)]).astype(np.int32)
     pool[1, 2] = -1
     g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=torch.from_numpy(pool).cuda(), blk=blk)
     torch.cuda.synchronize()
