@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     v[2] = x1 * cs[2] + y1 * cs[3];
                     v[3] = y1 * cs[2] - x1 * cs[3];
                 }
-                *reinterpret_cast<f32x4*>(dst + r * kD + 256 * half + 4 * lane) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + r * kD + 256 * half + 4 * lane));
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites
         }

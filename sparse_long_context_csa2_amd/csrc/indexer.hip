@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     const int c0 = t_begin * 16;
     const int c1 = min(t_end * 16, p.ncols);
     float* orow = p.out + row * p.ncols;
-    for (int c = c0 + static_cast<int>(threadIdx.x); c < c1; c += 256) orow[c] = osc[c - c0];
+    for (int c = c0 + static_cast<int>(threadIdx.x); c < c1; c += 256) __builtin_nontemporal_store(osc[c - c0], &orow[c]);
 }
 
 // Prefill scoring: many query tokens of one sequence against the records
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void idx_prefill_kernel(IdxP p, in
 #pragma unroll
                 for (int u = 0; u < kPChunk; ++u) {
                     const int c = (kb + u) * kPTile + lane;
-                    if (u < cnt && c < p.ncols) orow[c] = sc[u];
+                    if (u < cnt && c < p.ncols) __builtin_nontemporal_store(sc[u], &orow[c]);
                 }
             }
         };
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void idx_prefill_kernel(IdxP p, in
         }
         // columns past the block's tiles: nothing there is visible
         if (live)
-            for (int c = nt * kPTile + lane; c < p.ncols; c += 64) orow[c] = -__builtin_huge_valf();
+            for (int c = nt * kPTile + lane; c < p.ncols; c += 64) __builtin_nontemporal_store(-__builtin_huge_valf(), &orow[c]);
     }
 }
 
