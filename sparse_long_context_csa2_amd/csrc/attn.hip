@@ -650,7 +650,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3);
             const uint8_t* tr1 = tr0 + 16 * kXPitch;
             typedef short s16x4 __attribute__((ext_vector_type(4)));
-            bf16x8 va[2][4];
+            // operands two channel groups ahead (bf16; e4m3 has no registers
+            // to spare and reads one group ahead)
+            constexpr int kVA = (KVDT == DT_BF16) ? 3 : 2;
+            bf16x8 va[kVA][4];
             auto vload = [&](int uh, bf16x8* d) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -664,10 +667,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 }
             };
             vload(0, va[0]);
+            if constexpr (kVA == 3) vload(4, va[1]);
 #pragma unroll
             for (int uh = 0; uh < 32; uh += 4) {
-                const int k = (uh / 4) & 1;
-                if (uh + 4 < 32) vload(uh + 4, va[k ^ 1]);
+                const int k = (uh / 4) % kVA;
+                if (uh + 4 * (kVA - 1) < 32) vload(uh + 4 * (kVA - 1), va[(k + kVA - 1) % kVA]);
                 __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], bhi, acc[uh + u]);
