@@ -502,7 +502,7 @@ constexpr int kBitWords = 8192;  // column bitmap of the final ordering: rows up
 // word w of the bitmap lives at w + w / 32: a thread's run of 32 words then
 // starts one bank further than its neighbour's
 __device__ __forceinline__ int bit_slot(int w) { return w + (w >> 5); }
-struct LongShared {
+struct __align__(16) LongShared {
     union {
         struct {
             int hist[kBins];
@@ -595,13 +595,14 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     // ---- last workgroup of this row: resolve the boundary bin ----
     const int ncand = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
     const int nsure = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
-    if (threadIdx.x == 0) sh.misc[0] = 0;  // final count
-    __syncthreads();
-    auto take_col = [&](int c, uint32_t key) {
-        const int slot = atomicAdd(&sh.misc[0], 1);
-        if (slot < K)
-            sh.u.fin.fin[slot] = p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
+    unsigned long long* fin = sh.u.fin.fin;
+    // fin[i] for the i-th chosen element: its column, or with sort_by_key
+    // its composite key.  The chosen-outright ones take fin[0 .. nsure) in
+    // list order, the chosen candidates follow, placed by block scans.
+    auto fin_val = [&](int c, uint32_t key) -> unsigned long long {
+        return p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
     };
+    int take = nsure;
     // The list reads below are issued all at once per thread (clamped
     // indices, unused results dropped): a loop that waits for each
     // device-scope load before the next would pay a memory round trip per
@@ -616,8 +617,10 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) kv[j] = p.sort_by_key && nsure > 0 ? key_of(p, prow, srow, cs[j]) : 0u;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            if (j * kNT + static_cast<int>(threadIdx.x) < nsure) take_col(cs[j], kv[j]);
+        for (int j = 0; j < kPer; ++j) {
+            const int i = j * kNT + static_cast<int>(threadIdx.x);
+            if (i < nsure) fin[i] = fin_val(cs[j], kv[j]);
+        }
     }
     if (b1 >= 0) {
         // every candidate shares the key's top 12 bits (bin b1)
@@ -653,8 +656,20 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 return true;
             };
             thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
-            for (int i = threadIdx.x; i < ncand; i += kNT)
-                if (composite(sh.u.fin.key[i], sh.u.fin.rec[i]) >= thr) take_col(sh.u.fin.col[i], sh.u.fin.key[i]);
+            bool f[kPer];
+            int nf = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = j * kNT + static_cast<int>(threadIdx.x);
+                f[j] = i < ncand && composite(ck[j], cr[j]) >= thr;
+                nf += f[j] ? 1 : 0;
+            }
+            int nt;
+            int at = nsure + block_excl_scan(nf, sh.scan, &nt);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if (f[j]) fin[at++] = fin_val(cc[j], ck[j]);
+            take += nt;
         } else {  // a crowded boundary bin: select from the row's list
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
                 key = ld_dev(gkey + i);
@@ -662,16 +677,25 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 return true;
             };
             thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
-            for (int i = threadIdx.x; i < ncand; i += kNT) {
-                const uint32_t k = ld_dev(gkey + i);
-                const int c = ld_dev(gcol + i);
-                if (composite(k, rec_of(p, prow, c)) >= thr) take_col(c, k);
+            for (int base = 0; base < ncand; base += kNT) {
+                const int i = base + static_cast<int>(threadIdx.x);
+                uint32_t k = 0u;
+                int c = 0;
+                bool f = false;
+                if (i < ncand) {
+                    k = ld_dev(gkey + i);
+                    c = ld_dev(gcol + i);
+                    f = composite(k, rec_of(p, prow, c)) >= thr;
+                }
+                int nt;
+                const int at = take + block_excl_scan(f ? 1 : 0, sh.scan, &nt);
+                if (f) fin[at] = fin_val(c, k);
+                take += nt;
             }
         }
     }
     __syncthreads();
-    const int take = min(sh.misc[0], K);
-    unsigned long long* fin = sh.u.fin.fin;
+    take = min(take, K);
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
     auto out_of = [&](unsigned long long v) -> int32_t {
         return p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(v)) : rec_of(p, prow, static_cast<int>(v));
@@ -682,7 +706,8 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         // thread writes the set bits of its run of words at its place
         // from one block scan of the popcounts
         const int nw = (p.ncols + 31) / 32;
-        for (int i = threadIdx.x; i < bit_slot(nw); i += kNT) sh.a.bits[i] = 0u;
+        const int nz = (bit_slot(nw) + 3) >> 2;  // 16-byte words; the array holds a multiple of 4
+        for (int i = threadIdx.x; i < nz; i += kNT) reinterpret_cast<uint4*>(sh.a.bits)[i] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
         for (int i = threadIdx.x; i < take; i += kNT) {
             const int c = static_cast<int>(fin[i]);
@@ -703,15 +728,22 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
         }
         int total;
         int pos = block_excl_scan(cntb, sh.scan, &total);
+        // columns in order into LDS (fin is free once marked), then one
+        // coalesced pass maps them to records and writes the row (a store
+        // per set bit would also wait, at each pool read, for the stores
+        // before it)
+        int* outc = reinterpret_cast<int*>(fin);
 #pragma unroll
         for (int k = 0; k < kWpt; ++k) {
             unsigned bw = wv[k];
             while (bw) {
                 const int bit = __ffs(static_cast<int>(bw)) - 1;
                 bw &= bw - 1u;
-                orow[pos++] = rec_of(p, prow, 32 * (w0 + k) + bit);
+                outc[pos++] = 32 * (w0 + k) + bit;
             }
         }
+        __syncthreads();
+        for (int i = threadIdx.x; i < take; i += kNT) orow[i] = rec_of(p, prow, outc[i]);
         return;
     }
     // otherwise a bitonic sort in LDS (log^2 stages, one block pass each)
