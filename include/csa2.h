@@ -20,7 +20,9 @@
  *   the shape given in brackets; pointers must be 16-byte aligned.
  * - Storage dtypes (csa2_dtype): CSA2_F32 = IEEE float32, CSA2_BF16 =
  *   bfloat16 (uint16 bit patterns), CSA2_E4M3 = OCP fp8 e4m3fn codes with
- *   one float32 scale per row (value = decode(code) * scale[row]).
+ *   one float32 scale per row (value = decode(code) * scale[row]).  Scales
+ *   are finite and >= 0, as max|x|/448 is; the indexer may apply a key
+ *   row's scale after the ReLU.
  * - Positions are 0-based absolute token positions (int64).  Record s of
  *   a cache compressed at ratio m covers tokens m*s .. m*s+m-1 and is
  *   visible to a query at t only if m*s+m-1 <= t and s < n_rec ("DeepSeek V4
