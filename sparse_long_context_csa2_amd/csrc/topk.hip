@@ -331,6 +331,7 @@ struct SmallShared {
         unsigned long long fin[kMaxK];
     };
     int cand[kCandCap];
+    int pool[CAP];                // the row's pool (block ids; P <= columns), when it has one
     int hist8[256];
     Scan scan;
     int misc[4];
@@ -345,11 +346,21 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
     const float* srow = p.scores + static_cast<size_t>(row) * n;
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    // The row's pool goes to LDS first: every record id below is then an
+    // LDS read (a global read would wait, at each use, for the stores and
+    // loads issued before it).
+    const int32_t* lpool = nullptr;
+    if (prow) {
+        for (int i = threadIdx.x; i < p.P; i += kNT) sh.pool[i] = prow[i];
+        __syncthreads();
+        lpool = sh.pool;
+    }
+    auto recl = [&](int c) -> int { return rec_of(p, lpool, c); };
 
     int nvalid = 0;
     for (int c0 = 0; c0 < n; c0 += 4 * kNT) {  // four keys per thread per round, loads issued together
         uint32_t kk[4];
-        load_keys(p, prow, srow, c0, n, kk);
+        load_keys(p, lpool, srow, c0, n, kk);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = c0 + i * kNT + static_cast<int>(threadIdx.x);
@@ -387,7 +398,7 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
                 const int c = sh.cand[i];
                 key = sh.keys[c];
-                rec = rec_of(p, prow, c);
+                rec = recl(c);
                 return true;
             };
             thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
@@ -395,7 +406,7 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
             auto src = [&](int c, uint32_t& key, int& rec) -> bool {
                 key = sh.keys[c];
                 if (!key || static_cast<int>(key >> kBinShift) != bstar) return false;
-                rec = rec_of(p, prow, c);
+                rec = recl(c);
                 return true;
             };
             thr = radix_select(src, n, need, sh.hist8, sh.scan);
@@ -406,28 +417,32 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
         if (!k) return false;
         const int b = static_cast<int>(k >> kBinShift);
         if (b != bstar) return b > bstar;
-        return composite(k, rec_of(p, prow, c)) >= thr;
+        return composite(k, recl(c)) >= thr;
     };
     const int take = nvalid < K ? nvalid : K;
 
     if (!p.sort_by_key) {
         // ordered compaction: each thread owns a contiguous run of columns
+        // and places its chosen records in LDS (the histogram's space, dead
+        // by now); one coalesced pass then writes the row
         const int per = (n + kNT - 1) / kNT;
         const int c0 = threadIdx.x * per, c1 = min(n, c0 + per);
         int cnt = 0;
         for (int c = c0; c < c1; ++c) cnt += chosen(c);
         int tot;
         int pos = block_excl_scan(cnt, sh.scan, &tot);
+        int* outr = sh.hist;
         for (int c = c0; c < c1; ++c)
-            if (chosen(c) && pos < K) orow[pos++] = rec_of(p, prow, c);
-        for (int i = take + threadIdx.x; i < K; i += kNT) orow[i] = -1;
+            if (chosen(c) && pos < K) outr[pos++] = recl(c);
+        __syncthreads();
+        for (int i = threadIdx.x; i < K; i += kNT) orow[i] = i < take ? outr[i] : -1;
     } else {
         if (threadIdx.x == 0) sh.misc[1] = 0;
         __syncthreads();
         for (int c = threadIdx.x; c < n; c += kNT) {
             if (chosen(c)) {
                 const int slot = atomicAdd(&sh.misc[1], 1);
-                if (slot < K) sh.fin[slot] = composite(sh.keys[c], rec_of(p, prow, c));
+                if (slot < K) sh.fin[slot] = composite(sh.keys[c], recl(c));
             }
         }
         __syncthreads();

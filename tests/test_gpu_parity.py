@@ -164,6 +164,35 @@ def test_topk_pool_mapping_ties_by_record_id(P):
         assert set(got.tolist()) == ref and len(got) == len(ref)
 
 
+@pytest.mark.parametrize("blk,K", [(64, 300), (1, 512), (16, 2048)])
+def test_topk_pool_rows_one_workgroup(blk, K):
+    """Pooled rows of 4096 columns and fewer than 1024 rows: one workgroup
+    per row with the row's pool held on chip (P = 4096 / blk, so blk=1 gives
+    the largest pool); exact ties, -inf scores and -1 pool blocks."""
+    _case(f"topk pooled 4096-column rows, blk={blk} K={K}")
+    rows, ncols = 5, 4096
+    P = ncols // blk
+    rng = np.random.default_rng(blk * 7 + K)
+    s = (rng.integers(0, 30, size=(rows, ncols)) / 30.0).astype(np.float32)
+    s[1, ::7] = -np.inf
+    pool = np.stack([rng.permutation(2 * P + 7)[:P] for _ in range(rows)]).astype(np.int32)
+    pool[2, ::5] = -1
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=torch.from_numpy(pool).cuda(), blk=blk)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    cols = np.arange(ncols)
+    for r in range(rows):
+        pb = pool[r][cols // blk]
+        rec = np.where(pb < 0, -1, pb * blk + cols % blk)
+        ref = rec[_ref_topk(s[r], K, rec)]
+        got = g[r][g[r] >= 0]
+        assert set(got.tolist()) == set(ref.tolist()) and len(got) == len(ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1), f"row {r}"
+        # column order: the chosen records appear in the order of their columns
+        col_of = {int(v): i for i, v in enumerate(rec) if v >= 0}
+        assert all(col_of[int(a)] < col_of[int(b)] for a, b in zip(got[:-1], got[1:])), f"row {r}"
+
+
 @pytest.mark.parametrize("pooled", [False, True])
 @pytest.mark.parametrize("ncols", [1536, 4096])
 def test_topk_many_rows(pooled, ncols):
