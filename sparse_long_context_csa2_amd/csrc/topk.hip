@@ -323,6 +323,45 @@ __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
 
 // ---------------------------------------------------------------- rows <= 4096
 
+// Ordered compaction of a block's flagged columns, taken in rounds: thread
+// t holds the flag of column r * kNT + t in round r.  Each wave counts a
+// round with one ballot; one wave scans the R * kNW counts in (round, wave)
+// order; emit(r, pos) then gets each flagged column's place in column
+// order.  Strided columns keep the LDS reads around it free of bank
+// conflicts, and no counter is shared.  Returns the number flagged.
+// cnt needs 2 * R * kNW + 1 ints, and R * kNW <= 64.
+template <int R, class Emit>
+__device__ int block_compact(const bool (&flag)[R], int* cnt, Emit emit) {
+    static_assert(R * kNW <= 64, "one wave scans the counts");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long bal[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        bal[r] = __ballot(flag[r]);
+        if (lane == 0) cnt[r * kNW + wave] = __popcll(bal[r]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int v = lane < R * kNW ? cnt[lane] : 0;
+        int x = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, kWave);
+            if (lane >= o) x += y;
+        }
+        if (lane < R * kNW) cnt[R * kNW + lane] = x - v;
+        if (lane == 63) cnt[2 * R * kNW] = x;  // the total
+    }
+    __syncthreads();
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (flag[r]) emit(r, cnt[R * kNW + r * kNW + wave] + __popcll(bal[r] & lt));
+    const int total = cnt[2 * R * kNW];
+    __syncthreads();  // cnt may be reused
+    return total;
+}
+
 template <int CAP>
 struct SmallShared {
     uint32_t keys[CAP];
@@ -333,6 +372,7 @@ struct SmallShared {
     int cand[kCandCap];
     int pool[CAP];                // the row's pool (block ids; P <= columns), when it has one
     int hist8[256];
+    int ccnt[2 * (CAP / kNT) * kNW + 1];
     Scan scan;
     int misc[4];
 };
@@ -383,17 +423,19 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
         __syncthreads();
         int need;
         bstar = find_from_top<kBins / kNT>(sh.hist, K, sh.scan, &need);
-        if (threadIdx.x == 0) sh.misc[0] = 0;
-        __syncthreads();
-        for (int c = threadIdx.x; c < n; c += kNT) {
-            const uint32_t k = sh.keys[c];
-            if (k && static_cast<int>(k >> kBinShift) == bstar) {
-                const int slot = atomicAdd(&sh.misc[0], 1);
-                if (slot < kCandCap) sh.cand[slot] = c;
-            }
+        constexpr int kR = CAP / kNT;
+        bool inb[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int c = r * kNT + static_cast<int>(threadIdx.x);
+            const uint32_t k = c < n ? sh.keys[c] : 0u;
+            inb[r] = k && static_cast<int>(k >> kBinShift) == bstar;
         }
-        __syncthreads();
-        const int ncand = sh.misc[0];
+        const int ncand = block_compact(inb, sh.ccnt, [&](int r, int pos) {
+            if (pos < kCandCap) sh.cand[pos] = r * kNT + static_cast<int>(threadIdx.x);
+        });
+        // every candidate shares the key's top 12 bits (bin bstar)
+        const unsigned long long known = static_cast<unsigned long long>(static_cast<uint32_t>(bstar) << kBinShift) << 32;
         if (ncand <= kCandCap) {
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
                 const int c = sh.cand[i];
@@ -401,7 +443,7 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
                 rec = recl(c);
                 return true;
             };
-            thr = radix_select(src, ncand, need, sh.hist8, sh.scan);
+            thr = radix_select(src, ncand, need, sh.hist8, sh.scan, 48, known);
         } else {
             auto src = [&](int c, uint32_t& key, int& rec) -> bool {
                 key = sh.keys[c];
@@ -409,7 +451,7 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
                 rec = recl(c);
                 return true;
             };
-            thr = radix_select(src, n, need, sh.hist8, sh.scan);
+            thr = radix_select(src, n, need, sh.hist8, sh.scan, 48, known);
         }
     }
     auto chosen = [&](int c) -> bool {
@@ -422,19 +464,20 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
     const int take = nvalid < K ? nvalid : K;
 
     if (!p.sort_by_key) {
-        // ordered compaction: each thread owns a contiguous run of columns
-        // and places its chosen records in LDS (the histogram's space, dead
-        // by now); one coalesced pass then writes the row
-        const int per = (n + kNT - 1) / kNT;
-        const int c0 = threadIdx.x * per, c1 = min(n, c0 + per);
-        int cnt = 0;
-        for (int c = c0; c < c1; ++c) cnt += chosen(c);
-        int tot;
-        int pos = block_excl_scan(cnt, sh.scan, &tot);
+        // ordered compaction of the chosen records into LDS (the
+        // histogram's space, dead by now); one coalesced pass then writes
+        // the row
+        constexpr int kR = CAP / kNT;
+        bool ch[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int c = r * kNT + static_cast<int>(threadIdx.x);
+            ch[r] = c < n && chosen(c);
+        }
         int* outr = sh.hist;
-        for (int c = c0; c < c1; ++c)
-            if (chosen(c) && pos < K) outr[pos++] = recl(c);
-        __syncthreads();
+        block_compact(ch, sh.ccnt, [&](int r, int pos) {
+            if (pos < K) outr[pos] = recl(r * kNT + static_cast<int>(threadIdx.x));
+        });
         for (int i = threadIdx.x; i < K; i += kNT) orow[i] = i < take ? outr[i] : -1;
     } else {
         if (threadIdx.x == 0) sh.misc[1] = 0;
