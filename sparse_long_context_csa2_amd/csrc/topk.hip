@@ -388,24 +388,34 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
     // The row's pool goes to LDS first: every record id below is then an
     // LDS read (a global read would wait, at each use, for the stores and
-    // loads issued before it).
-    const int32_t* lpool = nullptr;
-    if (prow) {
+    // loads issued before it).  Column c's block c / blk comes from one
+    // multiply by ceil(2^32 / blk), exact while c * blk < 2^32 (here both
+    // are at most 4096), not from an integer division per use.
+    const bool pooled = prow != nullptr;
+    if (pooled) {
         for (int i = threadIdx.x; i < p.P; i += kNT) sh.pool[i] = prow[i];
         __syncthreads();
-        lpool = sh.pool;
     }
-    auto recl = [&](int c) -> int { return rec_of(p, lpool, c); };
+    const unsigned long long bmul = pooled ? ((1ull << 32) + p.blk - 1) / p.blk : 0ull;
+    auto recl = [&](int c) -> int {
+        if (!pooled) return c;
+        const int q = static_cast<int>((static_cast<unsigned long long>(c) * bmul) >> 32);
+        const int pb = sh.pool[q];
+        return pb < 0 ? -1 : pb * p.blk + (c - q * p.blk);
+    };
 
     int nvalid = 0;
     for (int c0 = 0; c0 < n; c0 += 4 * kNT) {  // four keys per thread per round, loads issued together
-        uint32_t kk[4];
-        load_keys(p, lpool, srow, c0, n, kk);
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = srow[min(c0 + i * kNT + static_cast<int>(threadIdx.x), n - 1)];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = c0 + i * kNT + static_cast<int>(threadIdx.x);
-            if (c < n) sh.keys[c] = kk[i];
-            nvalid += kk[i] != 0u;
+            uint32_t k = score_key(sv[i]);
+            if (c >= n || (k != 0u && recl(c) < 0)) k = 0u;
+            if (c < n) sh.keys[c] = k;
+            nvalid += k != 0u;
         }
     }
     for (int i = threadIdx.x; i < kBins; i += kNT) sh.hist[i] = 0;
