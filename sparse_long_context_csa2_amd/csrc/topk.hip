@@ -226,6 +226,17 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 // by a second binary search over record ids with one.  Column order comes
 // from ballot prefixes; score order (K <= 64) from a bitonic sort across
 // the wave's lanes.
+__device__ __forceinline__ uint32_t warp_min_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+    return v;
+}
+__device__ __forceinline__ uint32_t warp_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+    return v;
+}
+
 template <int KPL, bool POOL>
 __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
     __shared__ unsigned long long slot[kNW][64];
@@ -266,11 +277,28 @@ __global__ __launch_bounds__(kNT) void topk_wave_kernel(TopkP p) {
     uint32_t kstar = 1u;  // with nvalid <= K every valid key is chosen
     int need_tie = KPL * 64;
     if (nvalid > K) {
-        // largest x with count(key >= x) >= K
-        uint32_t x = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
+        // Largest x with count(key >= x) >= K.  The K-th key lies between
+        // the smallest and the largest valid key, so the bits above their
+        // highest differing bit are known; and once a probe counts exactly
+        // K keys at or above it, those K keys are the selection (every key
+        // equal to the probe is then needed), so the search can stop.
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            if (kk[i]) lo = min(lo, kk[i]);
+            hi = max(hi, kk[i]);
+        }
+        lo = warp_min_u32(lo);
+        hi = warp_max_u32(hi);
+        const uint32_t diff = lo ^ hi;
+        const int top = diff ? 31 - __builtin_clz(diff) : -1;
+        uint32_t x = top >= 0 ? (hi & ~((2u << top) - 1u)) : hi;  // the common prefix (<= lo)
+        if (top == 31) x = 0u;
+        for (int bit = top; bit >= 0; --bit) {
             const uint32_t cand = x | (1u << bit);
-            if (count_ge(cand) >= K) x = cand;
+            const int c = count_ge(cand);
+            if (c >= K) x = cand;
+            if (c == K) break;
         }
         kstar = x;
         need_tie = K - (kstar == 0xFFFFFFFFu ? 0 : count_ge(kstar + 1u));  // keys equal to k* still needed

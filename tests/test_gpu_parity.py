@@ -164,6 +164,34 @@ def test_topk_pool_mapping_ties_by_record_id(P):
         assert set(got.tolist()) == ref and len(got) == len(ref)
 
 
+@pytest.mark.parametrize("pooled", [False, True])
+def test_topk_wave_rows_few_distinct_scores(pooled):
+    """One wave per row when the valid scores take one or two values: the
+    search for the K-th key then starts with nothing (or one bit) left to
+    decide, and the ties are broken by record id."""
+    _case(f"topk wave rows with one or two distinct scores, pooled={pooled}")
+    rows, ncols, K, blk = 4, 512, 100, 16
+    s = np.full((rows, ncols), 0.25, dtype=np.float32)
+    s[1, ::3] = 0.5                    # two values
+    s[2, 200:] = -np.inf               # one value, then nothing selectable
+    s[3, :] = np.float32(3e-39)        # one subnormal value
+    rng = np.random.default_rng(5)
+    pool = None
+    cols = np.arange(ncols)
+    if pooled:
+        pool = np.stack([rng.permutation(100)[:ncols // blk] for _ in range(rows)]).astype(np.int32)
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=None if pool is None else torch.from_numpy(pool).cuda(),
+                     blk=blk if pooled else 0)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(rows):
+        rec = pool[r][cols // blk] * blk + cols % blk if pooled else cols
+        ref = rec[_ref_topk(s[r], K, rec)]
+        got = g[r][g[r] >= 0]
+        assert set(got.tolist()) == set(ref.tolist()) and len(got) == len(ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1), f"row {r}"
+
+
 @pytest.mark.parametrize("blk,K", [(64, 300), (1, 512), (16, 2048)])
 def test_topk_pool_rows_one_workgroup(blk, K):
     """Pooled rows of 4096 columns and fewer than 1024 rows: one workgroup
