@@ -23,10 +23,12 @@
 // row with the keys cached in LDS.
 // Longer rows: the row is split into 4096-column chunks over many
 // workgroups.  A histogram kernel accumulates the row histogram (LDS-
-// private per workgroup, merged with global atomics); a select kernel then
-// classifies each chunk -- keys above the boundary bin are chosen
-// outright, keys inside it are candidates -- places both lists with one
-// block scan and appends them to the row's with one atomic.  The last
+// private per workgroup, merged with global atomics after a kernel that
+// clears it; rows of at most four chunks instead keep each chunk's
+// histogram, which the select kernel sums, and need no clearing).  A
+// select kernel then classifies each chunk -- keys above the boundary bin
+// are chosen outright, keys inside it are candidates -- places both lists
+// with one block scan and appends them to the row's with one atomic.  The last
 // workgroup to finish a row (atomic ticket) resolves the boundary bin
 // exactly and writes the row, sorted in LDS.  Output ids are sorted by
 // column, so results are deterministic whatever the order in which
@@ -50,6 +52,7 @@ constexpr int kSmallCols = 4096;     // short rows: one workgroup per row
 constexpr int kChunk = 4096;         // columns per workgroup on long rows
 constexpr int kCandCap = 2048;       // boundary candidates held in LDS
 constexpr int kMaxK = 2048;
+constexpr int kFewChunks = 4;        // rows of up to this many chunks keep per-chunk histograms
 
 struct TopkP {
     int rows, ncols, K, P, blk, nchunks;
@@ -58,7 +61,8 @@ struct TopkP {
     int32_t* idx;
     int sort_by_key;
     // long-row workspace
-    int* ghist;      // [rows][kBins]: histogram of the keys' top 12 bits
+    int* ghist;      // [rows][kBins]: histogram of the keys' top 12 bits; with at most
+                     // kFewChunks chunks per row, [rows][nchunks][kBins]: each chunk's own
     int* cnt;        // [rows][4]: candidate count, chosen count (one 64-bit word), finished chunks
     int* sure;       // [rows][K]: columns chosen outright
     uint32_t* ckey;  // [rows][ncols]: boundary-bin candidates (key, column)
@@ -589,6 +593,14 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
     for (int i = 0; i < kChunk / kNT; ++i)
         if (kk[i]) atomicAdd(&hist[kk[i] >> kBinShift], 1);
     __syncthreads();
+    if (p.nchunks <= kFewChunks) {
+        // the chunk's own histogram (the select kernel sums the row's few);
+        // the row's counters are cleared here, before the select kernel runs
+        int* g = p.ghist + (static_cast<size_t>(row) * p.nchunks + blockIdx.x) * kBins;
+        for (int i = threadIdx.x; i < kBins; i += kNT) g[i] = hist[i];
+        if (blockIdx.x == 0 && threadIdx.x < 4) p.cnt[row * 4 + threadIdx.x] = 0;
+        return;
+    }
     int* g = p.ghist + static_cast<size_t>(row) * kBins;
     for (int i = threadIdx.x; i < kBins; i += kNT)
         if (hist[i]) atomicAdd(&g[i], hist[i]);
@@ -634,7 +646,23 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     // the chunk's keys and the row histogram, all loads in flight at once
     uint32_t kk[kChunk / kNT];
     load_keys(p, prow, srow, c0, c1, kk);
-    {
+    if (p.nchunks <= kFewChunks) {
+        // the row histogram is the sum of its chunks' (all loads in flight at once)
+        const int* g = p.ghist + static_cast<size_t>(row) * p.nchunks * kBins;
+        int hv[kFewChunks][kBins / kNT];
+#pragma unroll
+        for (int c = 0; c < kFewChunks; ++c)
+#pragma unroll
+            for (int j = 0; j < kBins / kNT; ++j)
+                hv[c][j] = g[static_cast<size_t>(min(c, p.nchunks - 1)) * kBins + j * kNT + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < kBins / kNT; ++j) {
+            int t = 0;
+#pragma unroll
+            for (int c = 0; c < kFewChunks; ++c) t += c < p.nchunks ? hv[c][j] : 0;
+            sh.a.h.hist[j * kNT + threadIdx.x] = t;
+        }
+    } else {
         const int* g = p.ghist + static_cast<size_t>(row) * kBins;
         int hv[kBins / kNT];
 #pragma unroll
@@ -892,8 +920,9 @@ struct LongLayout {
 LongLayout long_layout(int rows, int ncols, int K) {
     LongLayout L;
     size_t off = 0;
+    const size_t nchk = (static_cast<size_t>(ncols) + kChunk - 1) / kChunk;
     L.hist = off;
-    off += align256(static_cast<size_t>(rows) * kBins * sizeof(int));
+    off += align256(static_cast<size_t>(rows) * (nchk <= kFewChunks ? nchk : 1) * kBins * sizeof(int));
     L.cnt = off;
     off += align256(static_cast<size_t>(rows) * 4 * sizeof(int));
     L.sure = off;
@@ -934,7 +963,7 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
     p.ckey = reinterpret_cast<uint32_t*>(base + L.ckey);
     p.ccol = reinterpret_cast<int*>(base + L.ccol);
     p.nchunks = (p.ncols + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL(topk_zero_kernel, dim3(p.rows), dim3(kNT), 0, st, p);
+    if (p.nchunks > kFewChunks) hipLaunchKernelGGL(topk_zero_kernel, dim3(p.rows), dim3(kNT), 0, st, p);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
     hipLaunchKernelGGL(topk_select_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
     return static_cast<int>(hipGetLastError());
