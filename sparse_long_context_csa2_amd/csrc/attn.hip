@@ -791,6 +791,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
     const int h0 = 2 * blockIdx.y;
     const int tid = threadIdx.x;
     const int ns = p.nsplit;
+    // this thread's channels of the first kPre splits load first: their
+    // latency then overlaps the split weights and the rotary table
+    const int hl = tid >> 7;  // 128 threads per head
+    const int h = h0 + hl;
+    const int d = 4 * (tid & 127);
+    const float* pb = p.part_o + (static_cast<size_t>(qr) * ns * kH + h) * kD + d;
+    constexpr int kPre = 16;
+    f32x4 v0[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (i < ns) v0[i] = *reinterpret_cast<const f32x4*>(pb + static_cast<size_t>(i) * kH * kD);
     const int64_t t = p.q_pos[qr];
     const int rd = p.rope_dims;
     for (int i = tid; i < rd / 2; i += 256) rope_angle(t, i, rd, p.rope_base, rope_cs[i][0], rope_cs[i][1]);
@@ -813,12 +824,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
         if (s < ns) wts[hw][s] = den > 0.f ? e / den : 0.f;
     }
     __syncthreads();
-    const int hl = tid >> 7;  // 128 threads per head
-    const int h = h0 + hl;
-    const int d = 4 * (tid & 127);
-    const float* pb = p.part_o + (static_cast<size_t>(qr) * ns * kH + h) * kD + d;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ns; s0 += 4) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (i < ns) x += wts[hl][i] * v0[i];
+    for (int s0 = kPre; s0 < ns; s0 += 4) {
         f32x4 v[4];
         float w[4];
 #pragma unroll
