@@ -1,20 +1,26 @@
 """Benchmark of the CSA2 layer on one MI355X.
 
-Default workload: the Flash-shape prefill layer (1 sequence of 4096 query
-tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x 512
-latent with 64 rotary dims, window 128, bf16).  ``--workload`` selects one of
-the decode workloads instead.
+The default run measures the Flash-shape prefill layer (1 sequence of 4096
+query tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x
+512 latent with 64 rotary dims, window 128, bf16) as ``value``, and the
+three decode workloads (Full decode at 64K context, hierarchical
+Full/Reindex/Reuse decode at 256K, fp8 decode at 1M) in the same run, each
+reported in its own object under ``workloads``.  ``--workload`` picks
+another primary workload; ``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
 every layer of its sharing group, indexer scores (Full / Reindex), block
 pool (when the Full layer builds one), Top-K and sparse attention -- the
 same entry points, in the same order, that csa2_layer enqueues.  HIP
-events on the launch stream bracket each call, so each kernel's average
-duration over the timed steps is measured live; the dominant kernel's
-roofline is reported from it.  Inputs are resident in HBM before timing.
+events recorded on the launch stream bracket each call, so each kernel's
+average duration over the timed steps is measured live; the dominant
+kernel's roofline is reported from it.  Decode workloads are also timed as
+one captured HIP graph per step (the same launches replayed without host
+gaps).  Inputs are resident in HBM before timing, and decode steps rotate
+two cache copies so that the caches are not served from the 256 MB MALL.
 
 One JSON line is printed.  The fp64 CPU oracle is also timed on a bounded
-sample of the same workload (``cpu_baseline``).
+sample of each workload (``cpu_baseline``).
 """
 
 from __future__ import annotations
@@ -43,10 +49,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--only", action="store_true", help="measure the primary workload only")
+    ap.add_argument("--extra", default="C3,C4,C5", help="further workloads measured in the same run")
+    ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra-cpu-seconds", type=float, default=8.0)
     return ap.parse_args()
 
 
@@ -106,12 +116,13 @@ def kernel_work(wl, inp):
 # --------------------------------------------------------------- the timed step
 
 class Step:
-    """Enqueues the hot path of one workload through the ABI's entry points,
-    recording a HIP event between calls."""
+    """Enqueues the hot path of one workload through the ABI's entry points
+    on one stream, optionally recording a HIP event between calls."""
 
-    def __init__(self, grp, torch):
+    def __init__(self, grp, torch, stream=None):
         from sparse_long_context_csa2_amd import binding as Bd
         self.Bd, self.torch, self.grp = Bd, torch, grp
+        self.stream = stream  # torch stream the calls are enqueued on (None: current)
         wl = grp.wl
         self.calls = []  # (name, fn(copy) -> prepared call)
         self.prepared = None
@@ -123,6 +134,9 @@ class Step:
             self.scores_pool = torch.empty((wl.B, wl.Tq, wl.P * wl.blk), dtype=torch.float32, device=dev)
         nbp = Bd.lib().csa2_block_pool_workspace_bytes(rows, wl.N, wl.blk) if wl.P else 0
         self.pool_ws = torch.empty(max(nbp, 256), dtype=torch.uint8, device=dev)
+        ntk = max(Bd.lib().csa2_topk_workspace_bytes(rows, wl.N, wl.K),
+                  Bd.lib().csa2_topk_workspace_bytes(rows, wl.P * wl.blk, wl.K) if wl.P else 0)
+        self.topk_ws = torch.empty(max(ntk, 256), dtype=torch.uint8, device=dev)
         na = Bd.lib().csa2_sparse_attn_workspace_bytes(wl.B, wl.Tq, wl.H, wl.D, wl.K, wl.W)
         self.attn_ws = torch.empty(max(na, 256), dtype=torch.uint8, device=dev)
         for li, lay in enumerate(grp.layers):
@@ -145,21 +159,22 @@ class Step:
             out = self.scores_full if pool is None else self.scores_pool
             return Bd.csa2_index_scores(lay["q_idx"], lay["w"], sh["k_idx"], sh["k_scale"], lay["q_pos"], sh["m"],
                                         n_rec=sh["n_rec"], pool=pool, blk=lay["blk"] if pool is not None else 0,
-                                        out=out, prepare=True)
+                                        out=out, stream=self.stream, prepare=True)
         return f
 
     def _pool(self, lay):
         def f(copy):
             return self.Bd.csa2_block_pool(self.scores_full, lay["blk"], lay["P"], out=self.grp.pool,
-                                           ws=self.pool_ws, prepare=True)
+                                           ws=self.pool_ws, stream=self.stream, prepare=True)
         return f
 
     def _topk(self, lay, li, pooled):
         def f(copy):
             if pooled:
                 return self.Bd.csa2_topk(self.scores_pool, lay["K"], pool=self.grp.pool, blk=lay["blk"],
-                                         out=self.grp.idx[li], prepare=True)
-            return self.Bd.csa2_topk(self.scores_full, lay["K"], out=self.grp.idx[li], prepare=True)
+                                         out=self.grp.idx[li], ws=self.topk_ws, stream=self.stream, prepare=True)
+            return self.Bd.csa2_topk(self.scores_full, lay["K"], out=self.grp.idx[li], ws=self.topk_ws,
+                                     stream=self.stream, prepare=True)
         return f
 
     def _attn(self, lay, li):
@@ -168,7 +183,7 @@ class Step:
             return self.Bd.csa2_sparse_attn(lay["q"], sh["kv"], sh["kv_scale"], self.grp.idx[li], lay["swa"],
                                             lay["swa_scale"], lay["W"], lay["q_pos"], lay["sink"], lay["rope_dims"],
                                             lay["rope_base"], lay["sm_scale"], out=lay["out"], ws=self.attn_ws,
-                                            prepare=True)
+                                            stream=self.stream, prepare=True)
         return f
 
     def run(self, copy, events=None):
@@ -178,23 +193,30 @@ class Step:
             self.prepared = [[fn(c) for c in range(len(self.grp.shared))] for _, fn in self.calls]
         for i, calls in enumerate(self.prepared):
             if events is not None:
-                events[i].record()
+                events[i].record(self.stream)
             calls[copy]()
         if events is not None:
-            events[len(self.calls)].record()
+            events[len(self.calls)].record(self.stream)
 
 
 # --------------------------------------------------------------- CPU baseline
+
+def cpu_threads():
+    """(host cores this process may run on, BLAS threads numpy uses)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        blas = 1
+    return cores, blas
+
 
 def cpu_baseline(inp, seconds):
     """The fp64 oracle, as it stands, on a bounded sample of query rows of
     the same workload (spread over the batch and the sequence)."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing
-        threads = 1
+    cores, blas = cpu_threads()
     wl = inp["wl"]
     rows = [(b, t) for t in range(wl.Tq) for b in range(wl.B)]
     rng = np.random.default_rng(0)
@@ -209,7 +231,8 @@ def cpu_baseline(inp, seconds):
         if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done / dt, 2), "unit": "query-tokens/s", "cores": min(cores, blas), "kind": "oracle",
+            "affinity_cores": cores, "blas_threads": blas,
             "sample": f"{done} of {len(rows)} query rows of the same workload (random order), "
                       f"{len(lays)} layer(s) each, fp64 NumPy, {dt:.1f} s"}
 
@@ -229,6 +252,116 @@ def traffic_for(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
+# --------------------------------------------------------------- one workload
+
+def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
+    """Times `steps` steps of workload `key` and returns its report."""
+    from sparse_long_context_csa2_amd import runner as R
+    from sparse_long_context_csa2_amd import workloads as WL
+
+    wl = WL.CONFIGS[key]
+    inp = WL.make_inputs(wl)
+    decode = wl.decode_pos is not None
+    copies = copies or (2 if decode else 1)
+    grp = R.DeviceGroup(inp, device="cuda:0", copies=copies)
+    stream = torch.cuda.Stream()
+    step = Step(grp, torch, stream)
+    ncalls = len(step.calls)
+
+    for i in range(warmup):
+        step.run(i % copies)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step.run(s % copies, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {}
+    for s in range(steps):
+        for i, (name, _) in enumerate(step.calls):
+            per_call.setdefault(name, []).append(evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3)
+    step_s = [evs[s][0].elapsed_time(evs[s][ncalls]) * 1e-3 for s in range(steps)]
+    ms_eager = 1e3 * float(np.mean(step_s))
+    tokens = wl.B * wl.Tq
+
+    ms_graph = None
+    if graph:
+        # one graph per cache copy, each replaying the whole step's launches
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step.run(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for s in range(steps):
+                graphs[s % copies].replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / steps
+        del graphs
+    ms_per_step = ms_graph if ms_graph is not None else ms_eager
+    value = tokens / (ms_per_step * 1e-3)
+
+    work = kernel_work(wl, inp)
+    kern = {}
+    for name, ts in per_call.items():
+        ntimes = sum(1 for n, _ in step.calls if n == name)
+        avg = float(np.mean(ts))
+        kern[name] = {"avg_us": round(avg * 1e6, 2), "calls_per_step": ntimes}
+        if name in work:
+            w = work[name]
+            kern[name]["GB_s"] = round(w["bytes"] / avg / 1e9, 1)
+            kern[name]["TFLOP_s"] = round(w["flops"] / avg / 1e12, 2)
+    # dominant kernel: the largest share of the step
+    dom = max(per_call, key=lambda n: float(np.sum(per_call[n])))
+    w = work.get(dom)
+    avg = float(np.mean(per_call[dom]))
+    t_hbm = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = w["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        ach, peak, unit, bound = w["flops"] / avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = w["bytes"] / avg / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic_for(key, dom), "kernel": dom,
+            "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"], "avg_us": round(avg * 1e6, 2)}
+
+    # the method's required HBM bytes per step (keys scanned, queries, head
+    # weights, gathered and window rows, outputs; no intermediates) against
+    # the step time, and the same for the scan and gather calls alone
+    step_bytes = sum(work[n]["bytes"] for n, _ in step.calls if n in ("index_full", "index_pool", "attn"))
+    sg_time = sum(float(np.sum(per_call[n])) for n in per_call if n in ("index_full", "index_pool", "attn")) / steps
+    hbm = {"step_bytes": step_bytes,
+           "step_frac": round(step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+           "index_and_gather_frac": round(step_bytes / sg_time / (HBM_PEAK_GBS * 1e9), 4)}
+
+    cpu = cpu_baseline(inp, cpu_seconds) if cpu_seconds > 0 else None
+    rep = {
+        "workload": wl.name, "value": round(value, 1), "unit": "query-tokens/s",
+        "ms_per_step": round(ms_per_step, 4), "eager_ms_per_step": round(ms_eager, 4),
+        "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 4),
+        "steps": steps, "warmup": warmup,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[wl.kv_dtype],
+        "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
+                   "H": wl.H, "D": wl.D, "K": wl.K, "W": wl.W, "blk": wl.blk, "P": wl.P,
+                   "layers": list(wl.modes), "cache_copies": copies},
+        "roofline": roof, "hbm": hbm, "cpu_baseline": cpu, "kernels": kern, "wall_s": round(wall, 3),
+    }
+    del step, grp, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rep
+
+
 # --------------------------------------------------------------- main
 
 def main():
@@ -239,102 +372,39 @@ def main():
         sys.exit(2)
     import torch
 
-    from sparse_long_context_csa2_amd import runner as R
     from sparse_long_context_csa2_amd import workloads as WL
 
-    wl = WL.CONFIGS[args.workload]
-    inp = WL.make_inputs(wl)
-    decode = wl.decode_pos is not None
-    copies = args.copies or (2 if decode else 1)
-    grp = R.DeviceGroup(inp, device="cuda:0", copies=copies)
-    step = Step(grp, torch)
-    ncalls = len(step.calls)
-
-    for i in range(args.warmup):
-        step.run(i % copies)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step.run(s % copies, evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = {}
-    for s in range(args.steps):
-        for i, (name, _) in enumerate(step.calls):
-            per_call.setdefault(name, []).append(evs[s][i].elapsed_time(evs[s][i + 1]) * 1e-3)
-    step_s = [evs[s][0].elapsed_time(evs[s][ncalls]) * 1e-3 for s in range(args.steps)]
-    ms_per_step = 1e3 * float(np.mean(step_s))
-    tokens = wl.B * wl.Tq
-    value = tokens / (ms_per_step * 1e-3)
-
-    # csa2_layer itself, same work, for reference
-    for i in range(2):
-        grp.run(i % copies)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s in range(args.steps):
-        grp.run(s % copies)
-    e1.record()
-    torch.cuda.synchronize()
-    layer_ms = e0.elapsed_time(e1) / args.steps
-
-    work = kernel_work(wl, inp)
-    kern = {}
-    for name, ts in per_call.items():
-        key = "attn" if name == "attn" else name
-        ntimes = sum(1 for n, _ in step.calls if n == name)
-        avg = float(np.mean(ts))
-        kern[name] = {"avg_us": round(avg * 1e6, 2), "calls_per_step": ntimes}
-        if key in work:
-            w = work[key]
-            kern[name]["GB_s"] = round(w["bytes"] / avg / 1e9, 1)
-            kern[name]["TFLOP_s"] = round(w["flops"] / avg / 1e12, 2)
-    # dominant kernel: the largest share of the step
-    dom = max(per_call, key=lambda n: float(np.sum(per_call[n])))
-    w = work.get(dom)
-    avg = float(np.mean(per_call[dom]))
-    if w is not None:
-        t_hbm = w["bytes"] / (HBM_PEAK_GBS * 1e9)
-        t_mfma = w["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-        if t_mfma > t_hbm:
-            ach, peak, unit, bound = w["flops"] / avg / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
-        else:
-            ach, peak, unit, bound = w["bytes"] / avg / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-        roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": traffic_for(args.workload, dom), "kernel": dom,
-                "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"], "avg_us": round(avg * 1e6, 2)}
-    else:
-        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": None,
-                "traffic": None, "kernel": dom}
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+    prim = measure(args.workload, args.steps, args.warmup, args.copies,
+                   0 if args.no_cpu else args.cpu_seconds, torch,
+                   graph=WL.CONFIGS[args.workload].decode_pos is not None)
+    extra = {}
+    if not args.only:
+        for key in [k for k in args.extra.split(",") if k and k != args.workload]:
+            print(f"[bench] {key}", file=sys.stderr, flush=True)
+            rep = measure(key, args.extra_steps, args.warmup, 0, 0 if args.no_cpu else args.extra_cpu_seconds,
+                          torch, graph=WL.CONFIGS[key].decode_pos is not None)
+            extra[key] = rep
 
     line = {
         "metric": "CSA2 layer query-tokens/s (prefill & decode) + % of HBM/MFMA peak, 1 GPU",
-        "value": round(value, 1),
+        "value": prim["value"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": prim["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[wl.kv_dtype],
+        "dtype": prim["dtype"],
         "data": "synthetic (seeded N(0,1/d) inputs of the workload's shapes)",
-        "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
-                   "H": wl.H, "D": wl.D, "K": wl.K, "W": wl.W, "blk": wl.blk, "P": wl.P,
-                   "layers": list(wl.modes), "cache_copies": copies},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "kernels": kern,
-        "layer_api_ms_per_step": round(layer_ms, 4),
-        "wall_s": round(wall, 3),
+        "config": prim["config"],
+        "roofline": prim["roofline"],
+        "cpu_baseline": prim["cpu_baseline"],
+        "kernels": prim["kernels"],
+        "hbm": prim["hbm"],
+        "eager_ms_per_step": prim["eager_ms_per_step"],
+        "workloads": extra,
     }
     print(json.dumps(line))
 

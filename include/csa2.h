@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every tensor pointer is a DEVICE pointer to a dense row-major array with
- *   the shape given in brackets; pointers must be 16-byte aligned.
+ *   the shape given in brackets; pointers must be 16-byte aligned and
+ *   workspaces 256-byte aligned (a misaligned one is refused with
+ *   CSA2_EINVAL before anything is enqueued).
  * - Storage dtypes (csa2_dtype): CSA2_F32 = IEEE float32, CSA2_BF16 =
  *   bfloat16 (uint16 bit patterns), CSA2_E4M3 = OCP fp8 e4m3fn codes with
  *   one float32 scale per row (value = decode(code) * scale[row]).  Scales

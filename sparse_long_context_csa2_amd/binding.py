@@ -140,12 +140,28 @@ def _stream(stream) -> Optional[int]:
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
-def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+def _torch_stream(stream, device):
+    """The torch stream a call is enqueued on (a raw handle is wrapped)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
+
+
+def _empty(shape, dtype, device, stream) -> torch.Tensor:
+    """A temporary or output buffer allocated on the stream the kernels run
+    on, so that torch's caching allocator orders its reuse after them."""
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor], stream=None) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return ws
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty(nbytes, torch.uint8, device, stream)
 
 
 def csa2_index_scores(q_idx, w, k_idx, k_scale, q_pos, m: int, n_rec=None, pool=None, blk: int = 0,
@@ -158,7 +174,7 @@ def csa2_index_scores(q_idx, w, k_idx, k_scale, q_pos, m: int, n_rec=None, pool=
     P = 0 if pool is None else pool.shape[-1]
     ncols = N if pool is None else P * blk
     if out is None:
-        out = torch.empty((B, Tq, ncols), dtype=torch.float32, device=q_idx.device)
+        out = _empty((B, Tq, ncols), torch.float32, q_idx.device, stream)
     return _call(lib().csa2_index_scores,
                  (B, Tq, N, Hi, Di, m, _p(q_idx), dtype_code(q_idx), _p(w), _p(k_idx), _p(k_scale),
                   dtype_code(k_idx), _p(q_pos), _p(n_rec), _p(pool), P, blk if pool is not None else 0, _p(out),
@@ -170,9 +186,9 @@ def csa2_block_pool(scores, blk: int, P: int, out=None, ws=None, stream=None, pr
     N = scores.shape[-1]
     rows = scores.numel() // N
     if out is None:
-        out = torch.empty(scores.shape[:-1] + (P,), dtype=torch.int32, device=scores.device)
+        out = _empty(scores.shape[:-1] + (P,), torch.int32, scores.device, stream)
     nb = lib().csa2_block_pool_workspace_bytes(rows, N, blk)
-    ws = _ws(nb, scores.device, ws)
+    ws = _ws(nb, scores.device, ws, stream)
     return _call(lib().csa2_block_pool, (rows, N, blk, P, _p(scores), _p(out), _p(ws), nb, _stream(stream)), out,
                  prepare, (ws,))
 
@@ -184,9 +200,9 @@ def csa2_topk(scores, K: int, pool=None, blk: int = 0, out=None, ws=None, stream
     rows = scores.numel() // ncols
     P = 0 if pool is None else pool.shape[-1]
     if out is None:
-        out = torch.empty(scores.shape[:-1] + (K,), dtype=torch.int32, device=scores.device)
+        out = _empty(scores.shape[:-1] + (K,), torch.int32, scores.device, stream)
     nb = lib().csa2_topk_workspace_bytes(rows, ncols, K)
-    ws = _ws(nb, scores.device, ws)
+    ws = _ws(nb, scores.device, ws, stream)
     return _call(lib().csa2_topk, (rows, ncols, K, _p(scores), _p(pool), P, blk if pool is not None else 0, _p(out),
                                    _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
@@ -200,9 +216,9 @@ def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, 
     S = swa.shape[1]
     K = 0 if idx is None else idx.shape[-1]
     if out is None:
-        out = torch.empty((B, Tq, H, D), dtype=torch.float32, device=q.device)
+        out = _empty((B, Tq, H, D), torch.float32, q.device, stream)
     nb = lib().csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W)
-    ws = _ws(nb, q.device, ws)
+    ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_sparse_attn,
                  (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(idx), _p(swa),
                   _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "launch.h"
@@ -38,6 +39,22 @@ bool dtype_ok(int dt) { return dt == CSA2_F32 || dt == CSA2_BF16 || dt == CSA2_E
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Tensor pointers must be 16-byte aligned (the kernels use 16-byte vector
+// loads and stores and copy rows straight into LDS); workspaces 256-byte
+// aligned (they are carved into 256-byte aligned parts).
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+int check_align(const char* who, std::initializer_list<const void*> ptrs, const void* ws) {
+    int i = 0;
+    for (const void* p : ptrs) {
+        if (p && misaligned(p, 16))
+            return fail(CSA2_EINVAL, "%s: pointer argument %d (%p) is not 16-byte aligned", who, i, p);
+        ++i;
+    }
+    if (ws && misaligned(ws, 256)) return fail(CSA2_EINVAL, "%s: workspace %p is not 256-byte aligned", who, ws);
+    return CSA2_OK;
+}
+
 int check_scale(const char* name, int dt, const void* scale) {
     if (!dtype_ok(dt)) return fail(CSA2_EINVAL, "%s: unknown dtype %d", name, dt);
     if (dt == CSA2_E4M3 && !scale) return fail(CSA2_EINVAL, "%s: e4m3 storage needs a per-row scale", name);
@@ -56,7 +73,10 @@ int validate_index(const csa2::IndexArgs& a) {
     if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
         return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
                     "index_scores: queries must be f32 or bf16");
-    int e = check_scale("index_scores keys", a.k_dtype, a.k_scale);
+    int e = check_align("index_scores", {a.q_idx, a.w, a.k_idx, a.k_scale, a.q_pos, a.n_rec, a.pool, a.scores},
+                        nullptr);
+    if (e) return e;
+    e = check_scale("index_scores keys", a.k_dtype, a.k_scale);
     if (e) return e;
     if (a.pool) {
         if (a.P < 1 || a.blk < 1) return fail(CSA2_EINVAL, "index_scores: pool needs P >= 1 and blk >= 1");
@@ -86,7 +106,10 @@ int validate_attn(const csa2::AttnArgs& a) {
     if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
         return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
                     "sparse_attn: queries must be f32 or bf16");
-    int e = check_scale("sparse_attn kv", a.kv_dtype, a.kv_scale);
+    int e = check_align("sparse_attn",
+                        {a.q, a.kv, a.kv_scale, a.idx, a.swa, a.swa_scale, a.q_pos, a.sink, a.out}, a.ws);
+    if (e) return e;
+    e = check_scale("sparse_attn kv", a.kv_dtype, a.kv_scale);
     if (e) return e;
     e = check_scale("sparse_attn swa", a.swa_dtype, a.swa_scale);
     if (e) return e;
@@ -135,6 +158,7 @@ int csa2_block_pool(int rows, int N, int blk, int P, const float* scores, int32_
         return fail(CSA2_EINVAL, "block_pool: sizes must be >= 1 (rows=%d N=%d blk=%d P=%d)", rows, N, blk, P);
     if (P > CSA2_MAX_K) return fail(CSA2_EINVAL, "block_pool: P=%d above %d", P, CSA2_MAX_K);
     if (!scores || !pool) return fail(CSA2_EINVAL, "block_pool: null required pointer");
+    if (int e = check_align("block_pool", {scores, pool}, ws)) return e;
     const size_t need = csa2::block_pool_ws_bytes(rows, N, blk);
     if (ws_bytes < need || (need && !ws))
         return fail(CSA2_EWORKSPACE, "block_pool: workspace %zu bytes, need %zu", ws_bytes, need);
@@ -153,6 +177,7 @@ int csa2_topk(int rows, int ncols, int K, const float* scores, const int32_t* po
         return fail(CSA2_EINVAL, "topk: sizes must be >= 1 (rows=%d ncols=%d K=%d)", rows, ncols, K);
     if (K > CSA2_MAX_K) return fail(CSA2_EINVAL, "topk: K=%d above %d", K, CSA2_MAX_K);
     if (!scores || !idx) return fail(CSA2_EINVAL, "topk: null required pointer");
+    if (int e = check_align("topk", {scores, pool, idx}, ws)) return e;
     if (pool) {
         if (P < 1 || blk < 1 || static_cast<long long>(P) * blk != ncols)
             return fail(CSA2_EINVAL, "topk: pool mapping needs P*blk == ncols (P=%d blk=%d ncols=%d)", P, blk,
@@ -219,6 +244,7 @@ static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
         return fail(CSA2_EINVAL, "layer: sizes must be >= 1 (B=%d Tq=%d N=%d m=%d)", d->B, d->Tq, d->N, d->m);
     if (d->K < 1 || d->K > CSA2_MAX_K) return fail(CSA2_EINVAL, "layer: K=%d outside 1..%d", d->K, CSA2_MAX_K);
     if (!d->idx_inout) return fail(CSA2_EINVAL, "layer: idx_inout is required");
+    if (int e = check_align("layer", {d->idx_inout, d->pool_inout}, d->ws)) return e;
     pl.rows = d->B * d->Tq;
     pl.ncols = d->N;
     const bool scores_needed = d->mode != CSA2_REUSE;

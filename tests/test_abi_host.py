@@ -142,3 +142,35 @@ def test_layer_validation_and_workspace(L):
     d.K, d.mode, d.pool_inout, d.P, d.blk = 512, 1, FAKE, 64, 64
     assert L.csa2_workspace_bytes(ctypes.byref(d)) >= 2 * 64 * 64 * 4
     assert L.csa2_layer(None, None) == B.CSA2_EINVAL
+
+
+def test_misaligned_pointers_are_refused(L):
+    """Every tensor pointer must be 16-byte aligned and every workspace
+    256-byte aligned; a misaligned one is refused before any launch."""
+    f = L.csa2_index_scores
+    assert f(1, 1, 8, 4, 16, 1, FAKE + 8, 0, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE, None, 0,
+             None) == B.CSA2_EINVAL
+    assert "16-byte" in L.csa2_status_str(B.CSA2_EINVAL).decode()
+    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, FAKE, FAKE, None, 0, FAKE + 4, None, None, 0, 0, FAKE, None, 0,
+             None) == B.CSA2_EINVAL
+    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE + 2, None, 0,
+             None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 2, FAKE, None, 0, 0, FAKE + 4, FAKE, 1 << 20, None) == B.CSA2_EINVAL
+    assert L.csa2_topk(1, 8, 2, FAKE, None, 0, 0, FAKE, FAKE + 16, 1 << 20, None) == B.CSA2_EINVAL
+    assert "256-byte" in L.csa2_status_str(B.CSA2_EINVAL).decode()
+    assert L.csa2_block_pool(3, 64, 4, 2, FAKE + 8, FAKE, FAKE, 1 << 20, None) == B.CSA2_EINVAL
+    assert _attn(L, out=FAKE + 8) == B.CSA2_EINVAL
+    assert _attn(L, kv=FAKE + 2) == B.CSA2_EINVAL
+    assert _attn(L, K=512, ws=FAKE + 128, wsb=1 << 30) == B.CSA2_EINVAL
+    d = B.LayerDesc()
+    d.mode, d.B, d.Tq, d.N, d.m = 0, 2, 1, 1000, 4
+    d.k_idx, d.k_dtype, d.kv, d.kv_dtype = FAKE, 1, FAKE, 1
+    d.Hi, d.Di, d.q_idx, d.q_idx_dtype, d.w = 32, 128, FAKE, 1, FAKE
+    d.H, d.D, d.q, d.q_dtype = 64, 512, FAKE, 1
+    d.swa, d.swa_dtype, d.S, d.W = FAKE, 1, 128, 128
+    d.sink, d.rope_dims, d.rope_base, d.q_pos = FAKE, 64, 10000.0, FAKE
+    d.K, d.idx_inout, d.out = 512, FAKE, FAKE
+    d.ws, d.ws_bytes = FAKE + 64, 1 << 30
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
+    d.ws, d.q = FAKE, FAKE + 8
+    assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL

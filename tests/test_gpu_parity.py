@@ -298,12 +298,11 @@ def test_sparse_attn_mfma(kdt, Tq):
                               _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    tol = PR.ATTN_TOL[kdt]
     worst = 0.0
     for b in range(2):
         for ti in (list(range(Tq)) if Tq < 10 else [0, 1, 77, Tq - 1]):
-            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
-            worst = max(worst, PR.check_attn(out[b, ti], ref, tol, f"b={b} t={ti}"))
+            err, _ = PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], kdt, f"b={b} t={ti}")
+            worst = max(worst, err)
     print(f"max abs err {worst:.3g}")
 
 
@@ -320,9 +319,9 @@ def test_sparse_attn_sharp_logits(kdt):
     out = out.cpu().numpy()
     for b in range(2):
         for ti in range(3):
-            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
-            # unit-scale rows: hold bf16 to the stated 2e-3, e4m3 to 5e-2
-            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+            # unit-scale rows: the bound is the contract's 2e-3 itself
+            err, tol = PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], kdt, f"b={b} t={ti}")
+            assert tol > 0.9 * PR.ATTN_TOL[kdt]
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
@@ -363,22 +362,22 @@ def test_sparse_attn_late_dominant_entry(kdt, Tq):
     assert np.all(np.isfinite(out))
     for b in range(2):
         for ti in (list(range(Tq)) if Tq < 10 else [0, 1, 77, Tq - 1]):
-            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
-            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+            PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], kdt, f"b={b} t={ti}")
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
-@pytest.mark.parametrize("Tq", [64, 150])
-def test_sparse_attn_rising_maximum(kdt, Tq):
-    """Logits climb in steps across the tiles of one item: tile 0 near 0,
-    tile 1 about 63.3 log2 units higher, tile 2 about 64.8 (a kernel that
-    lets its reference maximum lag by up to 64 units moves it only at tile
-    2, while tile 1's terms still weigh about 2^-1.5 each against tile 2's).
-    Every term must keep its weight when the maximum moves: dropping tiles 0
-    and 1 would move the output by about 8e-2.  Tq=64 runs the split path
-    (two splits of three tiles), Tq=150 the single-launch path."""
-    _case(f"sparse_attn rising maximum {kdt} Tq={Tq}")
-    wl, inp, idx = _rising_case(kdt, Tq)
+@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 150)])
+def test_sparse_attn_rising_maximum(kdt, B, Tq):
+    """Logits climb in steps across the 32-entry tiles of one query: tile 0
+    near 0, tile 1 about 63.3 log2 units higher, tile 2 about 64.8 (a kernel
+    that lets its reference maximum lag by up to 64 units moves it only at
+    tile 2, while tile 1's terms still weigh about 2^-1.5 each against tile
+    2's).  Every term must keep its weight when the maximum moves: dropping
+    tiles 0 and 1 would move the output by about 8e-2.  One query alone
+    (B=1, Tq=1) has its entries spread over several parts whose maxima
+    differ by ~65 units; 300 queries keep each query's entries together."""
+    _case(f"sparse_attn rising maximum {kdt} B={B} Tq={Tq}")
+    wl, inp, idx = _rising_case(kdt, Tq, B)
     sh, lay = inp["shared"], inp["layers"][0]
     out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
                               _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
@@ -386,13 +385,12 @@ def test_sparse_attn_rising_maximum(kdt, Tq):
     out = out.cpu().numpy()
     assert np.all(np.isfinite(out))
     for b in range(wl.B):
-        for ti in [0, 1, Tq // 2, Tq - 1]:
-            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
-            PR.check_attn(out[b, ti], ref, PR.ATTN_TOL[kdt], f"b={b} t={ti}")
+        for ti in sorted({0, 1, Tq // 2, Tq - 1} & set(range(Tq))):
+            PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], kdt, f"b={b} t={ti}")
 
 
-def _rising_case(kdt, Tq):
-    wl = _small(B=2, Tq=Tq, N=300, K=128, W=24, swa_slots=32, decode_pos=5000, k_dtype=kdt, kv_dtype=kdt,
+def _rising_case(kdt, Tq, B=2):
+    wl = _small(B=B, Tq=Tq, N=300, K=128, W=24, swa_slots=32, decode_pos=5000, k_dtype=kdt, kv_dtype=kdt,
                 swa_dtype=kdt)
     inp = WL.make_inputs(wl)
     sh, lay = inp["shared"], inp["layers"][0]
@@ -431,6 +429,35 @@ def _rising_case(kdt, Tq):
     return wl, inp, idx
 
 
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("B,K,W", [(1, 512, 128), (1, 2048, 128), (4, 1920, 128), (3, 2048, 256)])
+def test_sparse_attn_few_queries_long_lists(kdt, B, K, W):
+    """Few decode queries with long entry lists (up to 2048 selected records
+    plus a 256-row window): the work of one query is spread over many parts
+    that are merged at the end.  Unit-scale rows and queries, so the bound
+    is the contract's 2e-3 itself; some ids are -1 or out of range."""
+    _case(f"sparse_attn few queries B={B} K={K} W={W} {kdt}")
+    N = 4096
+    wl = _small(B=B, Tq=1, N=N, K=K, W=W, swa_slots=W + 8, decode_pos=5 * N, k_dtype=kdt, kv_dtype=kdt,
+                swa_dtype=kdt, q_std=1.0, kv_std=1.0)
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    rng = np.random.default_rng(K + W + B)
+    idx = np.stack([rng.permutation(N)[:K] for _ in range(B)])[:, None, :].astype(np.int32)
+    idx[0, 0, K // 3] = -1
+    idx[-1, 0, 7] = N + 5
+    if B > 1:
+        idx[1, 0, K - 40:] = -1
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b in range(B):
+        err, tol = PR.check_attn_query(out[b, 0], sh, lay, b, 0, idx[b, 0], kdt, f"b={b}")
+        assert tol > 0.9 * PR.ATTN_TOL[kdt]
+
+
 @pytest.mark.parametrize("H,D,dt", [(2, 16, "f32"), (3, 48, "bf16")])
 def test_sparse_attn_generic(H, D, dt):
     _case(f"sparse_attn generic H={H} D={D} {dt}")
@@ -446,8 +473,11 @@ def test_sparse_attn_generic(H, D, dt):
     out = out.cpu().numpy()
     for b in range(2):
         for ti in range(5):
-            ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
-            PR.check_attn(out[b, ti], ref, 1e-4 if dt == "f32" else PR.ATTN_TOL[dt], f"b={b} t={ti}")
+            if dt == "f32":
+                ref = PR.oracle_attention(sh, lay, b, ti, idx[b, ti])
+                PR.check_attn(out[b, ti], ref, 1e-4, f"b={b} t={ti}")
+            else:
+                PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], dt, f"b={b} t={ti}")
 
 
 # ------------------------------------------------------------------ layers
@@ -475,8 +505,7 @@ def _check_group(inp, grp, rows):
                 PR.check_topk(ids, r["cand"], r["scores"], lay["K"], where)
             else:
                 assert np.array_equal(ids, prev), where
-            ref = PR.oracle_attention(sh, lay, b, ti, ids)
-            PR.check_attn(outs[li][b, ti], ref, PR.ATTN_TOL[inp["wl"].kv_dtype], where)
+            PR.check_attn_query(outs[li][b, ti], sh, lay, b, ti, ids, inp["wl"].kv_dtype, where)
             prev = ids
 
 

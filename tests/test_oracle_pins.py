@@ -154,6 +154,33 @@ def test_mask_then_select_printed_example():
     assert list(O.top_k(s[vis], vis, g["k"])) == g["selected_after_mask"]
 
 
+def test_window_positions_printed_example():
+    """The page's window-2 example: the query at position 4 sees positions 3
+    and 4 (the previous token and itself); an off-by-one window ([2, 3] or
+    [2, 3, 4]) fails.  Truncation at position 0 keeps only real positions."""
+    g = golden("window_positions.json")
+    for ex in g["examples"]:
+        assert O.window_positions(ex["t"], ex["W"]).tolist() == ex["positions"]
+    assert O.window_positions(0, 128).tolist() == [0]
+    assert O.window_positions(3, 128).tolist() == [0, 1, 2, 3]
+    assert len(O.window_positions(10 ** 6, 128)) == 128
+    assert O.window_positions(10 ** 6, 128)[-1] == 10 ** 6
+
+
+def test_hca_toy_visibility_printed_example():
+    """HCA toy: 8 tokens at compression 4 give 2 entries; the query p sees
+    entry 0 only (entry 1 holds future tokens), under either position the
+    page gives p; at Flash scale 1,048,576 / 128 = 8192 entries plus the
+    128-row window make 8320 entries per query."""
+    g = golden("hca_toy_visibility.json")
+    for q in g["queries"]:
+        assert O.visible_records(g["n_entries"], g["m"], q["t"]).tolist() == q["visible"]
+    f = g["flash_entries_per_query"]
+    vis = O.visible_records(f["context"] // f["m"], f["m"], f["context"])
+    assert len(vis) == f["compressed"]
+    assert len(vis) + len(O.window_positions(f["context"], f["window"])) == f["total"]
+
+
 def test_visibility_closed_form():
     # m = 4: record s visible iff 4s+3 <= t, i.e. floor((t+1)/4) records
     for t in range(0, 40):
