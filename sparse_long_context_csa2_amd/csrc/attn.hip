@@ -15,9 +15,14 @@
 //
 // attn_mfma_kernel (64 heads x 512 dims, bf16 queries, bf16 or e4m3 rows):
 //  * persistent: one workgroup of 4 waves per compute unit walks the work
-//    items, (query, split of the entry list) pairs; wave w owns heads
-//    16w .. 16w+15 over all 512 channels, so O stays in its 128 accumulation
-//    registers and no partial sums cross waves;
+//    items.  With many queries (prefill) an item is a query: wave w owns
+//    heads 16w .. 16w+15 over all 512 channels, so O stays in its 128
+//    accumulation registers and no partial sums cross waves.  With few
+//    queries (decode) an item is one group of 16 heads of a query (or of a
+//    split of its entries): every wave forms the same logits for those
+//    heads and owns 128 channels of their output, and the four head groups
+//    of a query run on one XCD, so the rows they all gather come from HBM
+//    once and from that XCD's L2 for the other three;
 //  * the valid selected records are compacted into an LDS list, so -1
 //    padding costs nothing, and a table of row addresses is built per item;
 //  * entries are processed in tiles of 32 rows, copied global -> LDS
@@ -35,7 +40,8 @@
 //  * e4m3 per-row scales multiply the logit and the probability;
 //  * with one split the workgroup finishes (sink, normalisation, inverse
 //    RoPE) itself; otherwise it writes (max, sum, unnormalised O) and
-//    attn_combine_kernel merges the splits.
+//    attn_combine_kernel merges the splits.  Splits are used only while the
+//    items alone would leave most compute units idle.
 // attn_generic_kernel: any head count and dim (one workgroup per query and
 // head, fp32 throughout); used for small shapes such as the toy.
 #include <stdint.h>
@@ -61,6 +67,7 @@ constexpr int kMayCross = 0x0002 | 0x0004 | 0x0400;  // log2 units: largest prob
 
 struct AttnP {
     int B, Tq, N, K, S, W, nsplit, per_split;
+    int n_items;              // work items (decode layout: padded, see decode_item)
     const uint16_t* q;        // bf16 [B][Tq][64][512]
     const uint8_t* kv;        // rows, bf16 or e4m3
     const float* kv_scale;
@@ -214,13 +221,34 @@ __device__ __forceinline__ int item_of(int round, int g, int G) {
 // While an item runs, the next item's index slice, position and query
 // fragments are loaded into registers, so an item starts without waiting
 // for global memory.
-template <int KVDT>
+// Decode layout: item i of a grid whose size is a multiple of 8 runs on XCD
+// i mod 8 (workgroups are dispatched to the 8 XCDs in turn); the four head
+// groups of one (query, split) get items on the same XCD, in the same
+// round, so the rows they all gather are fetched from HBM once and read
+// from that XCD's L2 by the other three.
+struct DecItem {
+    int qs, hg;  // (query, split) index and head group
+};
+__device__ __forceinline__ DecItem decode_item(int i) {
+    const int k = i >> 3;
+    return DecItem{8 * (k >> 2) + (i & 7), k & 3};
+}
+
+template <int KVDT, int NHG>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     __shared__ AttnShared<KVDT> sh;
     constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
+    // NHG = 64: wave w owns heads 16w .. 16w+15 over all 512 channels.
+    // NHG = 16 (decode): the workgroup owns one group of 16 heads; every
+    // wave computes the same logits and softmax for them and owns channels
+    // 128w .. 128w+127 of their P.V (O is then 32 registers).
+    constexpr bool kDec = NHG == 16;
+    constexpr int kU = kDec ? 8 : 32;      // 16-channel blocks of O per wave
+    constexpr int kUG = kU / 8;            // blocks per channel group of the MFMA stream
+    static_assert(NHG == 16 || NHG == 64, "head groups of 16 or 64");
     // An operand in an accumulation register tells the compiler that this
     // kernel uses them, so it selects the MFMA form whose accumulator lives
-    // in AGPRs: the 128 accumulators then stay there across the tile loop
+    // in AGPRs: the accumulators then stay there across the tile loop
     // instead of being copied to and from VGPRs on every iteration.
     asm volatile("" ::"a"(0.f));
     const int tid = threadIdx.x;
@@ -228,15 +256,27 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g = lane >> 4;
-    const int h = 16 * wave + l16;
+    const int ch0 = kDec ? 128 * wave : 0;  // first channel of the wave's O
     const int Q = p.B * p.Tq;
-    const int n_items = Q * p.nsplit;
+    const int n_items = p.n_items;
     const int G = gridDim.x;
     const float cz = p.sm * kLog2e;
     const int nids = (p.K + kThreads - 1) / kThreads;  // index chunks per thread
     const uint32_t voff = 16u * lane;
 
-    auto query_of = [&](int item) { return p.nsplit == 1 ? Q - 1 - item : item / p.nsplit; };
+    auto item_ok = [&](int item) { return !kDec || decode_item(item).qs < Q * p.nsplit; };
+    auto query_of = [&](int item) {
+        if constexpr (kDec) return decode_item(item).qs / p.nsplit;
+        return p.nsplit == 1 ? Q - 1 - item : item / p.nsplit;
+    };
+    auto split_of = [&](int item) {
+        if constexpr (kDec) return decode_item(item).qs % p.nsplit;
+        return p.nsplit == 1 ? 0 : item % p.nsplit;
+    };
+    auto head_of = [&](int item) {  // this lane's head
+        if constexpr (kDec) return 16 * decode_item(item).hg + l16;
+        return 16 * wave + l16;
+    };
     auto fetch = [&](int item, ItemFetch& f) {
         const int qr = query_of(item);
         const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
@@ -248,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         f.t = p.q_pos[qr];
     };
     auto fetch_q = [&](int item, ItemFetch& f) {
-        const uint16_t* qh = p.q + (static_cast<size_t>(query_of(item)) * kH + h) * kD;
+        const uint16_t* qh = p.q + (static_cast<size_t>(query_of(item)) * kH + head_of(item)) * kD;
 #pragma unroll
         for (int i = 0; i < 16; ++i) f.q[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * i + g)));
     };
@@ -256,17 +296,18 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     // the pow() is far costlier than the per-item angle, so it runs once
     for (int i = tid; i < p.rope_dims / 2; i += kThreads) sh.rope_inv[i] = rope_inv_freq(i, p.rope_dims, p.rope_base);
 
-    const float sk = p.sink[h] * kLog2e;  // the head's sink logit, log2 units
     ItemFetch nx;
     const int R = (n_items + G - 1) / G;  // rounds
-    const int rot = static_cast<int>(blockIdx.x) % R;
+    // decode: rounds in order, item r*G + g (G is a multiple of 8, so a
+    // workgroup stays on its XCD's share of the items)
+    const int rot = kDec ? 0 : static_cast<int>(blockIdx.x) % R;
     int k_next = 0;  // position in this workgroup's round order
     auto next_item = [&]() -> int {
         while (k_next < R) {
             const int r = k_next + rot < R ? k_next + rot : k_next + rot - R;
             ++k_next;
-            const int it = item_of(r, blockIdx.x, G);
-            if (it < n_items) return it;  // only the last round is partial
+            const int it = kDec ? r * G + static_cast<int>(blockIdx.x) : item_of(r, blockIdx.x, G);
+            if (it < n_items && item_ok(it)) return it;  // only the last round is partial
         }
         return n_items;
     };
@@ -278,20 +319,22 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 
     // Output of an item.  It runs once the next item's first tile copies
     // are in flight (its stores then drain while those copies land), so O,
-    // m and l persist across items.  O leaves through LDS: each wave stages
-    // its 16 heads, 256 channels at a time, in the last two tile buffers (the
-    // next item's first copies target the first two; rows padded so the
-    // lanes of one write pass hit distinct banks), and every global store
-    // then writes 1 KB of one head's row.  The wave's 16 output rows are
-    // contiguous in both the final output and the split partials.
-    f32x4 acc[32];
+    // m and l persist across items.  O leaves through LDS, staged in the
+    // last two tile buffers (the next item's first copies target the first
+    // two; rows padded so the lanes of one write pass hit distinct banks),
+    // so that every global store writes whole runs of one head's row: 1 KB
+    // (NHG = 64: each wave stages its 16 heads, 256 channels at a time) or
+    // 512 B (decode: each wave stages its 128 channels of the 16 heads).
+    f32x4 acc[kU];
     float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
     float l_run = 0.f;                     // this lane's share of the running sum
-    int prev_qr = -1, prev_split = 0;      // the item whose output is pending
-    auto finish = [&](int qr_f, int split_f) {
+    int prev_qr = -1, prev_split = 0, prev_h = 0;  // the item whose output is pending
+    auto finish = [&](int qr_f, int split_f, int h_f) {
+        const int hb = h_f - l16;  // first head of the wave's 16
         float f = 1.f;  // normalisation (one split) or none (partials)
         float* dst;
         if (p.nsplit == 1) {
+            const float sk = p.sink[h_f] * kLog2e;  // the head's sink logit, log2 units
             const float a = fmaxf(m_run, sk);
             f = 0.f;
             if (a != -__builtin_huge_valf()) {
@@ -300,23 +343,54 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 const float den = l_run * em + es;
                 f = den > 0.f ? em / den : 0.f;
             }
-            dst = p.out + (static_cast<size_t>(qr_f) * kH + 16 * wave) * kD;
+            dst = p.out + (static_cast<size_t>(qr_f) * kH + hb) * kD;
         } else {
-            const size_t slot0 = (static_cast<size_t>(qr_f) * p.nsplit + split_f) * kH + 16 * wave;
+            const size_t slot0 = (static_cast<size_t>(qr_f) * p.nsplit + split_f) * kH + hb;
             dst = p.part_o + slot0 * kD;
-            if (g == 0) {
+            if (g == 0 && (!kDec || wave == 0)) {  // decode: every wave holds the same m and l
                 p.part_ml[2 * (slot0 + l16)] = m_run;  // log2 units
                 p.part_ml[2 * (slot0 + l16) + 1] = l_run;
             }
         }
         // rotary channels [r0, kD) get the inverse rotation (one split
         // only).  In the read-back layout a lane keeps the same 4 channels
-        // for all 16 rows, so it fetches its two rotations once per half
+        // for all rows it stores, so it fetches its rotations once per pass
         // (the table holds (cos, sin) for every channel pair, (1, 0) below r0)
         int r0 = p.nsplit == 1 ? kD - p.rope_dims : kD;
-        asm volatile("" : "+s"(r0));  // tested per half here, not hoisted out of the item loop
+        asm volatile("" : "+s"(r0));  // tested per pass here, not hoisted out of the item loop
         static_assert(kWaves * 16 * kStagePitch <= 2 * kBuf, "staging fits the last two tile buffers");
         uint8_t* stage = &sh.xb[AttnShared<KVDT>::kNB - 2][0] + wave * 16 * kStagePitch;
+        if constexpr (kDec) {
+            // channels ch0 .. ch0+127 of 16 heads: lane (head l16, group g)
+            // holds channels 16u + 4g + v; read back, lane l takes 4
+            // channels of two heads per pass (2 x 512 B per store)
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                *reinterpret_cast<f32x4*>(stage + l16 * kStagePitch + 4 * (16 * u + 4 * g)) = acc[u] * f;
+            const int c = 4 * (lane & 31);  // channel offset within the wave's 128
+            const bool rot = ch0 + 128 > r0;
+            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sh.rope_cs[(ch0 + c) / 2][0]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows visible to the wave
+            f32x4 rows[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                rows[r] = *reinterpret_cast<const f32x4*>(stage + (2 * r + (lane >> 5)) * kStagePitch + 4 * c);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                f32x4 v = rows[r];
+                if (rot) {
+                    const float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
+                    v[0] = x0 * cs[0] + y0 * cs[1];
+                    v[1] = y0 * cs[0] - x0 * cs[1];
+                    v[2] = x1 * cs[2] + y1 * cs[3];
+                    v[3] = y1 * cs[2] - x1 * cs[3];
+                }
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<f32x4*>(dst + (2 * r + (lane >> 5)) * kD + ch0 + c));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            return;
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -348,7 +422,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 
     while (item < n_items) {
         const int qr = query_of(item);
-        const int split = p.nsplit == 1 ? 0 : item % p.nsplit;
+        const int split = split_of(item);
+        const int hh = head_of(item);
         const int b = qr / p.Tq;
         const int64_t t = nx.t;
         const int rd = p.rope_dims;
@@ -476,13 +551,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             if (ntile > 1) issue(1, 1);
         }
         if (prev_qr >= 0) {
-            finish(prev_qr, prev_split);
+            finish(prev_qr, prev_split, prev_h);
             lds_sync();  // every wave is done with the previous item's rope table
         }
         m_run = -__builtin_huge_valf();
         l_run = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kU; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (p.nsplit == 1)
             for (int i = tid; i < kD / 2; i += kThreads) {
                 const int j = i - (kD - rd) / 2;  // rotary pair index of channel pair i
@@ -632,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             if (__any(jump)) {
                 const float sc = __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
-                for (int u = 0; u < 32; ++u) acc[u] *= sc;
+                for (int u = 0; u < kU; ++u) acc[u] *= sc;
                 l_run *= sc;
             }
             m_run += shift;
@@ -640,23 +715,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             for (int j = 0; j < 8; ++j) soft_step(j, it, d, shift, s, std::true_type{});
         };
         auto packed = [](const uint32_t (&w)[4]) { return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}); };
-        // O^T += X^T P^T for tile `it`: channels 16*u + 4g + v, head h.  The
-        // transposing read: lane s of group g -> row 4g + s/4 (and 16 + ...),
-        // channels d0 + 4(s%4) .. +3; the operands of channel group k+1 are
-        // read before the MFMAs of group k.  side(step) runs between the
-        // MFMAs of each of the eight channel groups.
+        // O^T += X^T P^T for tile `it`: channels ch0 + 16*u + 4g + v, head h.
+        // The transposing read: lane s of group g -> row 4g + s/4 (and 16 +
+        // ...), channels d0 + 4(s%4) .. +3; the operands of channel group
+        // k+1 are read before the MFMAs of group k.  side(step) runs between
+        // the MFMAs of each of the eight channel groups (kUG blocks each).
         auto tile_pv = [&](int it, const bf16x8& bhi, const bf16x8& blo, auto&& side) {
             const uint8_t* xb = sh.xb[it % NB];
-            const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3);
+            const uint8_t* tr0 = xb + (4 * g + (l16 >> 2)) * kXPitch + 8 * (l16 & 3) + 2 * ch0;
             const uint8_t* tr1 = tr0 + 16 * kXPitch;
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             // operands two channel groups ahead (bf16; e4m3 has no registers
             // to spare and reads one group ahead)
-            constexpr int kVA = (KVDT == DT_BF16) ? 3 : 2;
-            bf16x8 va[kVA][4];
+            constexpr int kVA = (KVDT == DT_BF16 || kDec) ? 3 : 2;
+            bf16x8 va[kVA][kUG];
             auto vload = [&](int uh, bf16x8* d) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kUG; ++u) {
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4*)(tr0 + 32 * (uh + u)));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -667,17 +742,17 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 }
             };
             vload(0, va[0]);
-            if constexpr (kVA == 3) vload(4, va[1]);
+            if constexpr (kVA == 3) vload(kUG, va[1]);
 #pragma unroll
-            for (int uh = 0; uh < 32; uh += 4) {
-                const int k = (uh / 4) % kVA;
-                if (uh + 4 * (kVA - 1) < 32) vload(uh + 4 * (kVA - 1), va[(k + kVA - 1) % kVA]);
+            for (int uh = 0; uh < kU; uh += kUG) {
+                const int k = (uh / kUG) % kVA;
+                if (uh + kUG * (kVA - 1) < kU) vload(uh + kUG * (kVA - 1), va[(k + kVA - 1) % kVA]);
                 __builtin_amdgcn_sched_barrier(0);  // the reads above stay ahead
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], bhi, acc[uh + u]);
-                side(uh / 4);
+                for (int u = 0; u < kUG; ++u) acc[uh + u] = mfma16x16x32(va[k][u], bhi, acc[uh + u]);
+                side(uh / kUG);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[uh + u] = mfma16x16x32(va[k][u], blo, acc[uh + u]);
+                for (int u = 0; u < kUG; ++u) acc[uh + u] = mfma16x16x32(va[k][u], blo, acc[uh + u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -756,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             // the compiler keeps it in VGPRs and copies it in and out of the
             // MFMA accumulators every tile)
 #pragma unroll
-            for (int u = 0; u < 32; ++u) asm volatile("" : "+a"(acc[u]));
+            for (int u = 0; u < kU; ++u) asm volatile("" : "+a"(acc[u]));
             bhi = packed(s.phi);
             blo = packed(s.plo);
         };
@@ -770,11 +845,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
         prev_qr = qr;
         prev_split = split;
+        prev_h = hh;
         item = nxt;
     }
     if (prev_qr >= 0) {
         lds_sync();  // the last item's tiles are no longer read
-        finish(prev_qr, prev_split);
+        finish(prev_qr, prev_split, prev_h);
     }
 }
 
@@ -976,15 +1052,25 @@ int num_cus() {
     return n;
 }
 
-// Entry splits per query: about 128 work items in all.  Every split writes a
-// full fp32 partial O (128 KiB) that the combine reads back, so for few
-// queries half the compute units with longer items beat all of them with
-// short ones (measured on decode shapes: 8 and 16 queries run 25% and 7%
-// faster than with 256 items, 64 queries the same).
+// MI355X compute units.  The layout and split choices below depend only on
+// the shapes (so the workspace size does too); the grid uses the count the
+// device reports.
+constexpr int kCUs = 256;
+
+// Decode layout (one 16-head group per item) when the queries' four head
+// groups fit on the chip at once; otherwise 64 heads per item.
+bool decode_layout(int Q) { return 4 * Q <= kCUs; }
+
+// Entry splits per query.  Every split writes an fp32 partial O of its
+// heads that attn_combine_kernel reads back, so splits are used only while
+// the items would otherwise leave most compute units idle: about 128 items
+// in all (decode layout: four per split), none once the queries alone give
+// that many.
 int choose_splits(int Q, int K, int W, int& per) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
-    int ns = (128 + Q - 1) / Q;
+    const int per_split_items = decode_layout(Q) ? 4 : 1;
+    int ns = (128 + per_split_items * Q - 1) / (per_split_items * Q);
     if (ns > ntiles) ns = ntiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
@@ -1032,6 +1118,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         p.rope_dims = a.rope_dims;
         p.rope_base = a.rope_base;
         p.out = a.out;
+        const bool dec = decode_layout(Q);
         p.nsplit = choose_splits(Q, a.K, a.W, p.per_split);
         p.part_o = nullptr;
         p.part_ml = nullptr;
@@ -1042,13 +1129,24 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
                                                  ((o + 255) & ~static_cast<size_t>(255)));
         }
         // persistent: one workgroup per compute unit (the LDS footprint
-        // allows one), each walking its share of the work items
-        const int n_items = Q * p.nsplit;
-        const dim3 grid(n_items < num_cus() ? n_items : num_cus());
-        if (a.kv_dtype == DT_BF16)
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_BF16>, grid, dim3(kThreads), 0, st, p);
-        else
-            hipLaunchKernelGGL(attn_mfma_kernel<DT_E4M3>, grid, dim3(kThreads), 0, st, p);
+        // allows one), each walking its share of the work items.  Decode
+        // items come in blocks of 32 (8 XCDs x 4 head groups) and the grid
+        // is a multiple of 8, so every workgroup keeps to one XCD's items.
+        const int qs = Q * p.nsplit;
+        p.n_items = dec ? 32 * ((qs + 7) / 8) : qs;
+        const int cus = dec ? (num_cus() / 8) * 8 : num_cus();
+        const dim3 grid(p.n_items < cus ? p.n_items : cus);
+        if (dec) {
+            if (a.kv_dtype == DT_BF16)
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_BF16, 16>), grid, dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_E4M3, 16>), grid, dim3(kThreads), 0, st, p);
+        } else {
+            if (a.kv_dtype == DT_BF16)
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_BF16, 64>), grid, dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_E4M3, 64>), grid, dim3(kThreads), 0, st, p);
+        }
         int e = static_cast<int>(hipGetLastError());
         if (e || p.nsplit == 1) return e;
         hipLaunchKernelGGL(attn_combine_kernel, dim3(Q, kH / 2), dim3(256), 0, st, p);

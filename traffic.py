@@ -8,7 +8,7 @@ Two counter passes and a summary (from the repository root)::
 
 ``run`` executes the workload's step once (the same calls, in the same
 order, as ``bench.py``), then each distinct ABI call of the step on its own
-``STEPS`` times, each group preceded by a small fill kernel that marks where
+``STEPS`` times, each group preceded by a small bitwise-not kernel that marks where
 it starts, and finally an elementwise copy of a known size.  ``summarize``
 scales each counter by what it reads for that copy (the copy reads and
 writes exactly COPY_BYTES), splits the dispatches at the markers, and writes
@@ -30,7 +30,7 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 STEPS = 4
 COPY_BYTES = 256 << 20
-MARK = "FillFunctor"   # kernel-name fragment of the group markers
+MARK = "bitwise_not"   # kernel-name fragment of the group markers
 COPY = "MulFunctor"    # kernel-name fragment of the reference copy
 
 # source file of each ABI call's kernels
@@ -54,12 +54,12 @@ def _run(workload: str) -> None:
     step.run(0)
     torch.cuda.synchronize()
     names = []
-    mark = torch.zeros(64, dtype=torch.float32, device="cuda:0")
+    mark = torch.zeros(64, dtype=torch.int32, device="cuda:0")
     for i, (name, _) in enumerate(step.calls):
         if name in names:
             continue
         names.append(name)
-        mark.fill_(float(len(names)))
+        torch.bitwise_not(mark, out=mark)  # marks the start of this call's group
         for s in range(STEPS):
             step.prepared[i][s % copies]()
         torch.cuda.synchronize()
@@ -107,7 +107,9 @@ def _per_kernel(rows, counter: str):
 def _groups(disp, ncalls):
     """Dispatches of each marked group (the step run before the first
     marker and everything after the copy are dropped)."""
-    marks = [i for i, (name, _) in enumerate(disp) if MARK in name]
+    copy_at = max(i for i, (name, _) in enumerate(disp) if COPY in name)
+    # the last ncalls markers before the copy (set-up fills come earlier)
+    marks = [i for i, (name, _) in enumerate(disp) if MARK in name and i < copy_at][-ncalls:]
     if len(marks) != ncalls:
         raise SystemExit(f"expected {ncalls} markers, found {len(marks)}")
     ends = marks[1:] + [next(i for i, (name, _) in enumerate(disp) if COPY in name and i > marks[-1])]
