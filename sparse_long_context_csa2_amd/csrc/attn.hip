@@ -1062,15 +1062,18 @@ constexpr int kCUs = 256;
 bool decode_layout(int Q) { return 4 * Q <= kCUs; }
 
 // Entry splits per query.  Every split writes an fp32 partial O of its
-// heads that attn_combine_kernel reads back, so splits are used only while
-// the items would otherwise leave most compute units idle: about 128 items
-// in all (decode layout: four per split), none once the queries alone give
-// that many.
+// heads that attn_combine_kernel reads back, so splits are used only in
+// the decode layout, while its items would otherwise leave most compute
+// units idle: about 128 items in all (four per split).  The partials then
+// never exceed 62 splits' worth (7.8 MiB).
 int choose_splits(int Q, int K, int W, int& per) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
-    const int per_split_items = decode_layout(Q) ? 4 : 1;
-    int ns = (128 + per_split_items * Q - 1) / (per_split_items * Q);
+    if (!decode_layout(Q)) {
+        per = ntiles * kTile;
+        return 1;
+    }
+    int ns = (128 + 4 * Q - 1) / (4 * Q);
     if (ns > ntiles) ns = ntiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
