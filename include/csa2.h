@@ -32,8 +32,9 @@
  *   tokens into 4 KV entries?": an entry is visible only if all its tokens
  *   are at or before the query).
  * - The caller owns every buffer.  The library never allocates, frees or
- *   synchronises, keeps no pointer after returning and has no global
- *   state; calls on different streams are independent.  `stream` is a
+ *   synchronises, keeps no pointer after returning and has no global state
+ *   (except the static scratch of csa2_sparse_attn_noalloc); calls on
+ *   different streams are independent.  `stream` is a
  *   hipStream_t passed as void* (NULL = the default stream).  Work is only
  *   enqueued: results are ready after the caller synchronises the stream.
  * - `ws`/`ws_bytes` is a caller-provided device workspace of at least the
@@ -201,6 +202,30 @@ int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K,
                      float sm_scale, int rope_dims, float rope_base,
                      float* out, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int W);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn_noalloc -- csa2_sparse_attn without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as csa2_sparse_attn.
+ *
+ * It allocates nothing: when a shape needs scratch (the split partials of
+ * decode shapes with fewer than 32 queries), it uses a 6 MiB array that
+ * the library holds in each GPU's memory for the life of the process.
+ * Shapes needing more (up to 7.8 MiB, 24-31 queries with long entry lists)
+ * return CSA2_EWORKSPACE; csa2_sparse_attn_workspace_bytes gives the
+ * need.  All calls on one GPU share that array, so calls that overlap on
+ * one GPU (other streams, other threads) race; calls on different GPUs do
+ * not.  The first call on a device looks the array up (no allocation).
+ * ------------------------------------------------------------------------ */
+int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K,
+                             const void* q, int q_dtype,
+                             const void* kv, const float* kv_scale, int kv_dtype,
+                             const int32_t* idx,
+                             const void* swa, const float* swa_scale, int swa_dtype,
+                             int S, int W, const int64_t* q_pos, const float* sink,
+                             float sm_scale, int rope_dims, float rope_base,
+                             float* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa2_layer -- one CSA2 layer in one of the three sharing modes

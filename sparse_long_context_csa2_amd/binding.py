@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_topk_workspace_bytes.restype = s
         L.csa2_sparse_attn.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f, v, v,
                                        s, v]
+        L.csa2_sparse_attn_noalloc.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f,
+                                               v, v]
         L.csa2_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.csa2_sparse_attn_workspace_bytes.restype = s
         L.csa2_layer.argtypes = [ctypes.POINTER(LayerDesc), v]

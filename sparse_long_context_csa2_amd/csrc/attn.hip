@@ -48,6 +48,8 @@
 
 #include <type_traits>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -1084,6 +1086,39 @@ int choose_splits(int Q, int K, int W, int& per) {
 }
 
 }  // namespace
+
+// Device-resident scratch of the allocation-free attention entry point: the
+// split partials (fp32 O, then (max, sum) per head) of one call.  Each GPU
+// holds its own copy for the life of the process; calls on one GPU share
+// it, so they must not overlap.  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per
+// device (sparse_attn_scratch below), and only that address is ever passed
+// to a kernel.
+constexpr size_t kScratchBytes = size_t(6) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+size_t sparse_attn_scratch_bytes() { return kScratchBytes; }
+
+void* sparse_attn_scratch(int& err) {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices];
+    int dev = 0;
+    err = static_cast<int>(hipGetDevice(&dev));
+    if (err) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        err = static_cast<int>(hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        err = static_cast<int>(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (err) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
 
 bool sparse_attn_mfma_ok(const AttnArgs& a) {
     return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && a.K <= kMaxKList && a.W <= kMaxWin &&

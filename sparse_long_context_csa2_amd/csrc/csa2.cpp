@@ -229,6 +229,32 @@ int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K, const void* q, i
     return e ? hip_fail(e, "sparse_attn launch") : CSA2_OK;
 }
 
+int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K, const void* q, int q_dtype,
+                             const void* kv, const float* kv_scale, int kv_dtype, const int32_t* idx,
+                             const void* swa, const float* swa_scale, int swa_dtype, int S, int W,
+                             const int64_t* q_pos, const float* sink, float sm_scale, int rope_dims,
+                             float rope_base, float* out, void* stream) {
+    csa2::AttnArgs a;
+    fill_attn(a, B, Tq, H, D, N, K, q, q_dtype, kv, kv_scale, kv_dtype, idx, swa, swa_scale, swa_dtype, S, W,
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, nullptr, 0);
+    int e = validate_attn(a);
+    if (e) return e;
+    const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
+    const size_t have = csa2::sparse_attn_scratch_bytes();
+    if (need > have)
+        return fail(CSA2_EWORKSPACE,
+                    "sparse_attn_noalloc: this shape needs %zu bytes of scratch, above the static %zu "
+                    "(use csa2_sparse_attn with a workspace)", need, have);
+    if (need) {
+        int herr = 0;
+        a.ws = csa2::sparse_attn_scratch(herr);
+        if (!a.ws) return hip_fail(herr, "sparse_attn_noalloc: scratch address");
+        a.ws_bytes = have;
+    }
+    e = csa2::launch_sparse_attn(a, stream);
+    return e ? hip_fail(e, "sparse_attn_noalloc launch") : CSA2_OK;
+}
+
 // ---------------------------------------------------------------- layer
 
 struct LayerPlan {

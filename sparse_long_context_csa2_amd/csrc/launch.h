@@ -68,5 +68,10 @@ struct AttnArgs {
 bool sparse_attn_mfma_ok(const AttnArgs& a);
 size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W);
 int launch_sparse_attn(const AttnArgs& a, void* stream);
+// The allocation-free entry point's static scratch: its size, and its
+// address on the current device (looked up on the first call per device;
+// err is a hipError_t value, 0 on success).
+size_t sparse_attn_scratch_bytes();
+void* sparse_attn_scratch(int& err);
 
 }  // namespace csa2

@@ -174,3 +174,30 @@ def test_misaligned_pointers_are_refused(L):
     assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
     d.ws, d.q = FAKE, FAKE + 8
     assert L.csa2_layer(ctypes.byref(d), None) == B.CSA2_EINVAL
+
+
+def _attn_noalloc(L, **kw):
+    a = dict(B=1, Tq=1, H=64, D=512, N=100, K=16, q=FAKE, qdt=1, kv=FAKE, kvs=None, kvdt=1, idx=FAKE,
+             swa=FAKE, swas=None, swadt=1, S=128, W=128, pos=FAKE, sink=FAKE, sm=0.0, r=64, base=10000.0,
+             out=FAKE)
+    a.update(kw)
+    return L.csa2_sparse_attn_noalloc(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["K"], a["q"], a["qdt"], a["kv"],
+                                      a["kvs"], a["kvdt"], a["idx"], a["swa"], a["swas"], a["swadt"], a["S"],
+                                      a["W"], a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"], None)
+
+
+def test_sparse_attn_noalloc_validation(L):
+    """The allocation-free entry point validates like csa2_sparse_attn and
+    refuses, before touching any device, a shape whose split partials need
+    more than its 6 MiB static scratch (24 queries x 640 entries need
+    6.02 MiB)."""
+    assert _attn_noalloc(L, W=129) == B.CSA2_EINVAL
+    assert _attn_noalloc(L, out=FAKE + 8) == B.CSA2_EINVAL
+    assert _attn_noalloc(L, kvdt=2) == B.CSA2_EINVAL
+    need = L.csa2_sparse_attn_workspace_bytes(24, 1, 64, 512, 512, 128)
+    assert need > 6 << 20
+    assert _attn_noalloc(L, B=24, K=512) == B.CSA2_EWORKSPACE
+    assert "static" in L.csa2_status_str(B.CSA2_EWORKSPACE).decode()
+    # the decode shapes of the benchmark fit
+    for Q in (8, 16, 64):
+        assert L.csa2_sparse_attn_workspace_bytes(Q, 1, 64, 512, 512, 128) <= 6 << 20
