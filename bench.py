@@ -4,8 +4,9 @@ The default run measures the Flash-shape prefill layer (1 sequence of 4096
 query tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x
 512 latent with 64 rotary dims, window 128, bf16) as ``value``, and the
 three decode workloads (Full decode at 64K context, hierarchical
-Full/Reindex/Reuse decode at 256K, fp8 decode at 1M) in the same run, each
-reported in its own object under ``workloads``.  ``--workload`` picks
+Full/Reindex/Reuse decode at 256K, fp8 decode at 1M) and the heavily
+compressed (HCA) decode at 1M in the same run, each reported in its own
+object under ``workloads``.  ``--workload`` picks
 another primary workload; ``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
@@ -48,9 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
-    ap.add_argument("--extra", default="C3,C4,C5", help="further workloads measured in the same run")
+    ap.add_argument("--extra", default="C3,C4,C5,C6", help="further workloads measured in the same run")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
@@ -69,7 +70,7 @@ def entries_per_query(wl, inp):
     n_rec = np.full(wl.B, wl.N) if wl.n_rec is None else np.asarray(wl.n_rec)
     t = q_pos.astype(np.int64)
     vis = np.minimum(n_rec[:, None], (t + 1) // wl.m)
-    sel = np.minimum(wl.K, vis)
+    sel = vis if wl.modes == ("hca",) else np.minimum(wl.K, vis)  # HCA attends to every visible record
     win = np.minimum(wl.W, t + 1)
     return sel, win, vis
 
@@ -107,6 +108,7 @@ def kernel_work(wl, inp):
     # Selection steps: their own inputs and outputs (scores are an
     # intermediate of the layer, but they are what these kernels stream).
     work["topk_full"] = dict(bytes=rows * (wl.N * 4 + wl.K * 4), flops=0.0)
+    work["attn_dense"] = work["attn"]
     if wl.P:
         work["block_pool"] = dict(bytes=rows * (wl.N * 4 + wl.P * 4), flops=0.0)
         work["topk_pool"] = dict(bytes=rows * (wl.P * wl.blk * 4 + wl.P * 4 + wl.K * 4), flops=0.0)
@@ -137,7 +139,8 @@ class Step:
         ntk = max(Bd.lib().csa2_topk_workspace_bytes(rows, wl.N, wl.K),
                   Bd.lib().csa2_topk_workspace_bytes(rows, wl.P * wl.blk, wl.K) if wl.P else 0)
         self.topk_ws = torch.empty(max(ntk, 256), dtype=torch.uint8, device=dev)
-        na = Bd.lib().csa2_sparse_attn_workspace_bytes(wl.B, wl.Tq, wl.H, wl.D, wl.K, wl.W)
+        na = max(Bd.lib().csa2_sparse_attn_workspace_bytes(wl.B, wl.Tq, wl.H, wl.D, wl.K, wl.W),
+                 Bd.lib().csa2_dense_attn_workspace_bytes(wl.B, wl.Tq, wl.H, wl.D, wl.N, wl.W))
         self.attn_ws = torch.empty(max(na, 256), dtype=torch.uint8, device=dev)
         for li, lay in enumerate(grp.layers):
             mode = lay["mode"]
@@ -149,7 +152,10 @@ class Step:
             elif mode == "reindex":
                 self.calls.append(("index_pool", self._index(lay, grp.pool)))
                 self.calls.append(("topk_pool", self._topk(lay, li, pooled=True)))
-            self.calls.append(("attn", self._attn(lay, li)))
+            if mode == "hca":
+                self.calls.append(("attn_dense", self._dense(lay)))
+            else:
+                self.calls.append(("attn", self._attn(lay, li)))
 
     def _index(self, lay, pool):
         Bd, grp = self.Bd, self.grp
@@ -184,6 +190,16 @@ class Step:
                                             lay["swa_scale"], lay["W"], lay["q_pos"], lay["sink"], lay["rope_dims"],
                                             lay["rope_base"], lay["sm_scale"], out=lay["out"], ws=self.attn_ws,
                                             stream=self.stream, prepare=True)
+        return f
+
+    def _dense(self, lay):
+        def f(copy):
+            sh = self.grp.shared[copy]
+            return self.Bd.csa2_dense_attn(lay["q"], sh["kv"], sh["kv_scale"], lay["swa"], lay["swa_scale"],
+                                           lay["W"], lay["q_pos"], lay["sink"], lay["rope_dims"], sh["m"],
+                                           n_rec=sh["n_rec"], rope_base=lay["rope_base"],
+                                           sm_scale=lay["sm_scale"], out=lay["out"], ws=self.attn_ws,
+                                           stream=self.stream, prepare=True)
         return f
 
     def run(self, copy, events=None):
@@ -338,8 +354,9 @@ def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
     # the method's required HBM bytes per step (keys scanned, queries, head
     # weights, gathered and window rows, outputs; no intermediates) against
     # the step time, and the same for the scan and gather calls alone
-    step_bytes = sum(work[n]["bytes"] for n, _ in step.calls if n in ("index_full", "index_pool", "attn"))
-    sg_time = sum(float(np.sum(per_call[n])) for n in per_call if n in ("index_full", "index_pool", "attn")) / steps
+    scan_gather = ("index_full", "index_pool", "attn", "attn_dense")
+    step_bytes = sum(work[n]["bytes"] for n, _ in step.calls if n in scan_gather)
+    sg_time = sum(float(np.sum(per_call[n])) for n in per_call if n in scan_gather) / steps
     hbm = {"step_bytes": step_bytes,
            "step_frac": round(step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
            "index_and_gather_frac": round(step_bytes / sg_time / (HBM_PEAK_GBS * 1e9), 4)}

@@ -64,7 +64,7 @@ extern "C" {
 #define CSA2_EHIP (-4)         /* a HIP launch failed */
 
 typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_E4M3 = 2 } csa2_dtype;
-typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2, CSA2_HCA = 3 } csa2_mode;
 
 /* Largest K accepted by csa2_topk and csa2_layer. */
 #define CSA2_MAX_K 2048
@@ -204,6 +204,38 @@ int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K,
 size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int W);
 
 /* ------------------------------------------------------------------------
+ * csa2_dense_attn -- heavily compressed attention (HCA): the same shared-
+ * latent MQA, window, sink and inverse output RoPE as csa2_sparse_attn,
+ * with no indexer and no selection: every visible compressed record is an
+ * entry ("DeepSeek V4 Inside: One Token Through Every Block", section
+ * "What does HCA change?": dense attention over the n/m' compressed
+ * entries plus the window; 8192 + 128 entries per query at 1,048,576
+ * tokens and m' = 128).
+ *
+ * For query (b,t) at position p = q_pos[b,t] the entries are the records
+ * s = 0 .. v-1 with v = min(n_rec[b], floor((p+1)/m)) (record s covers
+ * tokens m*s .. m*s+m-1 and is visible once all of them are <= p), then the
+ * window rows as in csa2_sparse_attn.
+ *
+ * Inputs: as csa2_sparse_attn, without idx/K, plus
+ *   m          compression ratio of the records (>= 1)
+ *   n_rec      [B] int32 records written per sequence (<= N), or NULL for N
+ *   N          records per sequence in kv; N + W <= 73728 for the 64x512
+ *              kernels
+ * Output
+ *   out        [B][Tq][H][D] float32
+ * Workspace: csa2_dense_attn_workspace_bytes(B, Tq, H, D, N, W).
+ * ------------------------------------------------------------------------ */
+int csa2_dense_attn(int B, int Tq, int H, int D, int N, int m, const int32_t* n_rec,
+                    const void* q, int q_dtype,
+                    const void* kv, const float* kv_scale, int kv_dtype,
+                    const void* swa, const float* swa_scale, int swa_dtype,
+                    int S, int W, const int64_t* q_pos, const float* sink,
+                    float sm_scale, int rope_dims, float rope_base,
+                    float* out, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_dense_attn_workspace_bytes(int B, int Tq, int H, int D, int N, int W);
+
+/* ------------------------------------------------------------------------
  * csa2_sparse_attn_noalloc -- csa2_sparse_attn without a workspace
  * argument, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid
@@ -243,6 +275,10 @@ int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K,
  *   REUSE    runs no indexer; attends over the index set in idx_inout (left
  *            by the preceding Full or Reindex layer) with this layer's own
  *            query, window rows and sink.
+ *   HCA      a heavily compressed attention layer: no indexer and no
+ *            selection; csa2_dense_attn over every visible record of kv
+ *            at ratio m (K, idx_inout, blk, P, pool_inout and the indexer
+ *            fields are ignored).
  *
  * Every mode computes a fresh output with the layer's own query.
  * ------------------------------------------------------------------------ */

@@ -281,7 +281,7 @@ def attend(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, sm: float) -> np.n
 # One query of one layer, and a sharing group of layers
 # --------------------------------------------------------------------------
 
-FULL, REINDEX, REUSE = "full", "reindex", "reuse"
+FULL, REINDEX, REUSE, HCA = "full", "reindex", "reuse", "hca"
 
 
 def _n_rec(shared: Dict, b: int) -> int:
@@ -300,8 +300,10 @@ def layer_query(shared: Dict, layer: Dict, b: int, ti: int, mode: str,
     Modes follow [EXPL] section 2's table: Full builds keys and takes a fresh
     Top-K, Reindex reuses keys but takes a fresh Top-K (restricted to the
     pool when one is given, [EXPL] section 3), Reuse keeps the preceding
-    Top-K list and runs no indexer.  Every mode computes a fresh output with
-    the layer's own query, local rows and sink.
+    Top-K list and runs no indexer.  HCA (a heavily compressed attention
+    layer, [INSIDE] "What does HCA change?") has no indexer and attends to
+    every visible record.  Every mode computes a fresh output with the
+    layer's own query, local rows and sink.
 
     ``shared``: N, m, k_idx [B][N][Di] (+ k_scale [B][N]), kv [B][N][D]
     (+ kv_scale), optional n_rec [B].
@@ -323,6 +325,11 @@ def layer_query(shared: Dict, layer: Dict, b: int, ti: int, mode: str,
         if prev_sel is None:
             raise ValueError("Reuse needs the preceding index set")
         sel = np.asarray(prev_sel, dtype=np.int64)
+    elif mode == HCA:
+        # heavily compressed attention: no indexer, every visible compressed
+        # entry is attended ([INSIDE] "What does HCA change?": dense
+        # attention over the n/m' entries, the future entry excluded)
+        sel = vis
     else:
         if mode == FULL:
             cand = vis

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EHIP = 0, -1, -2, -3, -4
 F32, BF16, E4M3 = 0, 1, 2
-FULL, REINDEX, REUSE = 0, 1, 2
-MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE}
+FULL, REINDEX, REUSE, HCA = 0, 1, 2, 3
+MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE, "hca": HCA}
 MAX_K = 2048
 
 _c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn_noalloc.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f,
                                                v, v]
         L.csa2_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.csa2_dense_attn.argtypes = [i, i, i, i, i, i, v, v, i, v, v, i, v, v, i, i, i, v, v, f, i, f, v, v, s, v]
+        L.csa2_dense_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.csa2_dense_attn_workspace_bytes.restype = s
         L.csa2_sparse_attn_workspace_bytes.restype = s
         L.csa2_layer.argtypes = [ctypes.POINTER(LayerDesc), v]
         L.csa2_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
@@ -223,6 +226,24 @@ def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, 
     ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_sparse_attn,
                  (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(idx), _p(swa),
+                  _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,
+                  float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
+
+
+def csa2_dense_attn(q, kv, kv_scale, swa, swa_scale, W: int, q_pos, sink, rope_dims: int, m: int, n_rec=None,
+                    rope_base: float = 10000.0, sm_scale: float = 0.0, out=None, ws=None, stream=None,
+                    prepare: bool = False) -> torch.Tensor:
+    """HCA attention output [B][Tq][H][D] float32 over every visible record
+    of kv at compression m; see csa2.h."""
+    B, Tq, H, D = q.shape
+    N = kv.shape[1]
+    S = swa.shape[1]
+    if out is None:
+        out = _empty((B, Tq, H, D), torch.float32, q.device, stream)
+    nb = lib().csa2_dense_attn_workspace_bytes(B, Tq, H, D, N, W)
+    ws = _ws(nb, q.device, ws, stream)
+    return _call(lib().csa2_dense_attn,
+                 (B, Tq, H, D, N, m, _p(n_rec), _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(swa),
                   _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,
                   float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 

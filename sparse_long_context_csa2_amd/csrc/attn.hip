@@ -44,6 +44,11 @@
 //    items alone would leave most compute units idle.
 // attn_generic_kernel: any head count and dim (one workgroup per query and
 // head, fp32 throughout); used for small shapes such as the toy.
+//
+// Dense mode (heavily compressed attention, "DeepSeek V4 Inside", section
+// "What does HCA change?": no indexer, dense attention over every visible
+// compressed entry plus the window): no index list; the selected records
+// of a query are all records s < min(n_rec, (t+1)/m), in id order.
 #include <stdint.h>
 
 #include <type_traits>
@@ -70,6 +75,8 @@ constexpr int kMayCross = 0x0002 | 0x0004 | 0x0400;  // log2 units: largest prob
 struct AttnP {
     int B, Tq, N, K, S, W, nsplit, per_split;
     int n_items;              // work items (decode layout: padded, see decode_item)
+    int dense_m;              // > 0: dense mode, every record visible at compression dense_m (no idx)
+    const int32_t* n_rec;     // dense mode: [B] records written per sequence, or null for N
     const uint16_t* q;        // bf16 [B][Tq][64][512]
     const uint8_t* kv;        // rows, bf16 or e4m3
     const float* kv_scale;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     const int n_items = p.n_items;
     const int G = gridDim.x;
     const float cz = p.sm * kLog2e;
-    const int nids = (p.K + kThreads - 1) / kThreads;  // index chunks per thread
+    const int nids = p.dense_m ? 0 : (p.K + kThreads - 1) / kThreads;  // index chunks per thread
     const uint32_t voff = 16u * lane;
 
     auto item_ok = [&](int item) { return !kDec || decode_item(item).qs < Q * p.nsplit; };
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     };
     auto fetch = [&](int item, ItemFetch& f) {
         const int qr = query_of(item);
-        const int32_t* irow = p.idx + static_cast<size_t>(qr) * p.K;
+        const int32_t* irow = nids ? p.idx + static_cast<size_t>(qr) * p.K : nullptr;
 #pragma unroll
         for (int j = 0; j < kIdsPerThread; ++j) {
             const int c = j * kThreads + tid;
@@ -459,6 +466,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             }
         }
         nsel = __builtin_amdgcn_readfirstlane(nsel);
+        if (p.dense_m) {  // dense: every visible record, in id order
+            const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+            const int64_t v = t < 0 ? 0 : (t + 1) / p.dense_m;
+            nsel = static_cast<int>(v < nrec ? v : nrec);
+        }
         const int nwin = t < 0 ? 0 : static_cast<int>(t + 1 < p.W ? t + 1 : p.W);
         const int slot0 = static_cast<int>((t - nwin + 1) % p.S);  // ring slot of the first window row
         const int E = nsel + nwin;
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             const uint8_t* rp;
             float sc = 1.f;
             if (ge < nsel) {
-                const size_t r = static_cast<size_t>(b) * p.N + sh.list()[ge];
+                const size_t r = static_cast<size_t>(b) * p.N + (p.dense_m ? ge : sh.list()[ge]);
                 if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
                 rp = p.kv + r * kRowBytes;
             } else {
@@ -937,6 +949,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
 
 struct AttnG {
     int B, Tq, H, D, N, K, S, W, qdt, kvdt, swadt;
+    int dense_m;            // > 0: dense mode (K = N, entry j < visible count is record j)
+    const int32_t* n_rec;
     const void* q;
     const void* kv;
     const float* kv_scale;
@@ -982,9 +996,15 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnG p) {
     const int64_t win0 = t - nwin + 1;
     const int E = p.K + nwin;
     __syncthreads();
+    int nvis = 0;  // dense mode: visible records
+    if (p.dense_m) {
+        const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+        const int64_t v = t < 0 ? 0 : (t + 1) / p.dense_m;
+        nvis = static_cast<int>(v < nrec ? v : nrec);
+    }
     auto entry = [&](int j, const void*& base, size_t& off, float& sc, int& dt) -> bool {
         if (j < p.K) {
-            const int rec = p.idx[static_cast<size_t>(qr) * p.K + j];
+            const int rec = p.dense_m ? (j < nvis ? j : -1) : p.idx[static_cast<size_t>(qr) * p.K + j];
             if (rec < 0 || rec >= p.N) return false;
             const size_t r = static_cast<size_t>(b) * p.N + rec;
             base = p.kv; off = r * D; dt = p.kvdt;
@@ -1066,16 +1086,21 @@ bool decode_layout(int Q) { return 4 * Q <= kCUs; }
 // Entry splits per query.  Every split writes an fp32 partial O of its
 // heads that attn_combine_kernel reads back, so splits are used only in
 // the decode layout, while its items would otherwise leave most compute
-// units idle: about 128 items in all (four per split).  The partials then
-// never exceed 62 splits' worth (7.8 MiB).
-int choose_splits(int Q, int K, int W, int& per) {
+// units idle: about 128 items in all (four per split; 256 in dense mode,
+// whose lists are long), and wherever a split would hold more entries than
+// the entry table (kMaxEnt).  Sparse shapes then never need more than 62
+// splits' worth of partials (7.8 MiB).  K is the longest list of records
+// (dense mode: N).
+int choose_splits(int Q, int K, int W, bool dense, int& per) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
-    if (!decode_layout(Q)) {
-        per = ntiles * kTile;
-        return 1;
+    const int need = (ntiles * kTile + kMaxEnt - 1) / kMaxEnt;  // splits the entry table needs
+    int ns = need;
+    if (decode_layout(Q)) {
+        const int target = dense ? 256 : 128;
+        const int want = (target + 4 * Q - 1) / (4 * Q);
+        if (want > ns) ns = want;
     }
-    int ns = (128 + 4 * Q - 1) / (4 * Q);
     if (ns > ntiles) ns = ntiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
@@ -1121,16 +1146,28 @@ void* sparse_attn_scratch(int& err) {
 }
 
 bool sparse_attn_mfma_ok(const AttnArgs& a) {
-    return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && a.K <= kMaxKList && a.W <= kMaxWin &&
-           (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_E4M3) && a.swa_dtype == a.kv_dtype &&
-           a.rope_dims <= kD;
+    const int klist = a.dense_m ? a.N : a.K;  // longest list of records
+    return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && (a.dense_m ? 1 : a.K <= kMaxKList) &&
+           a.W <= kMaxWin && static_cast<long long>(klist) + a.W <= static_cast<long long>(kMaxSplits) * kMaxEnt &&
+           (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_E4M3) && a.swa_dtype == a.kv_dtype && a.rope_dims <= kD;
+}
+
+size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W) {
+    if (H != kH || D != kD) return 0;
+    int per;
+    const int Q = B * Tq;
+    const int ns = choose_splits(Q, N, W, true, per);
+    if (ns == 1) return 0;
+    const size_t o = static_cast<size_t>(Q) * ns * kH * kD * sizeof(float);
+    const size_t ml = static_cast<size_t>(Q) * ns * kH * 2 * sizeof(float);
+    return ((o + 255) & ~static_cast<size_t>(255)) + ((ml + 255) & ~static_cast<size_t>(255));
 }
 
 size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W) {
     if (H != kH || D != kD) return 0;
     int per;
     const int Q = B * Tq;
-    const int ns = choose_splits(Q, K, W, per);
+    const int ns = choose_splits(Q, K, W, false, per);
     if (ns == 1) return 0;
     const size_t o = static_cast<size_t>(Q) * ns * kH * kD * sizeof(float);
     const size_t ml = static_cast<size_t>(Q) * ns * kH * 2 * sizeof(float);
@@ -1157,7 +1194,9 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         p.rope_base = a.rope_base;
         p.out = a.out;
         const bool dec = decode_layout(Q);
-        p.nsplit = choose_splits(Q, a.K, a.W, p.per_split);
+        p.dense_m = a.dense_m;
+        p.n_rec = a.n_rec;
+        p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, a.dense_m > 0, p.per_split);
         p.part_o = nullptr;
         p.part_ml = nullptr;
         if (p.nsplit > 1) {
@@ -1196,7 +1235,9 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
     p.q = a.q; p.kv = a.kv; p.kv_scale = a.kv_scale; p.idx = a.idx; p.swa = a.swa;
     p.swa_scale = a.swa_scale; p.q_pos = a.q_pos; p.sink = a.sink; p.sm = sm;
     p.rope_dims = a.rope_dims; p.rope_base = a.rope_base; p.out = a.out;
-    const size_t lds = (2 * static_cast<size_t>(a.D) + a.K + a.W) * sizeof(float);
+    p.dense_m = a.dense_m; p.n_rec = a.n_rec;
+    if (a.dense_m) p.K = a.N;  // entry j < N is record j when visible
+    const size_t lds = (2 * static_cast<size_t>(a.D) + p.K + a.W) * sizeof(float);
     hipLaunchKernelGGL(attn_generic_kernel, dim3(Q, a.H), dim3(256), lds, st, p);
     return static_cast<int>(hipGetLastError());
 }

@@ -118,9 +118,10 @@ int validate_attn(const csa2::AttnArgs& a) {
     if (!(a.rope_base > 0.f)) return fail(CSA2_EINVAL, "sparse_attn: rope_base must be > 0");
     if (!(a.sm_scale >= 0.f) || isinf(a.sm_scale)) return fail(CSA2_EINVAL, "sparse_attn: bad sm_scale");
     if (!csa2::sparse_attn_mfma_ok(a)) {
-        if (a.D > 1024 || 2LL * a.D + a.K + a.W > 16384)
-            return fail(CSA2_EUNSUPPORTED, "sparse_attn: no kernel for H=%d D=%d K=%d W=%d with these dtypes",
-                        a.H, a.D, a.K, a.W);
+        const long long klist = a.dense_m ? a.N : a.K;  // longest list of records
+        if (a.D > 1024 || 2LL * a.D + klist + a.W > 16384)
+            return fail(CSA2_EUNSUPPORTED, "sparse_attn: no kernel for H=%d D=%d K=%lld W=%d with these dtypes",
+                        a.H, a.D, klist, a.W);
     }
     return CSA2_OK;
 }
@@ -255,6 +256,31 @@ int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K, const vo
     return e ? hip_fail(e, "sparse_attn_noalloc launch") : CSA2_OK;
 }
 
+size_t csa2_dense_attn_workspace_bytes(int B, int Tq, int H, int D, int N, int W) {
+    if (B < 1 || Tq < 1 || H < 1 || D < 1 || N < 1 || W < 1) return 0;
+    return csa2::dense_attn_ws_bytes(B, Tq, H, D, N, W);
+}
+
+int csa2_dense_attn(int B, int Tq, int H, int D, int N, int m, const int32_t* n_rec, const void* q, int q_dtype,
+                    const void* kv, const float* kv_scale, int kv_dtype, const void* swa, const float* swa_scale,
+                    int swa_dtype, int S, int W, const int64_t* q_pos, const float* sink, float sm_scale,
+                    int rope_dims, float rope_base, float* out, void* ws, size_t ws_bytes, void* stream) {
+    if (m < 1) return fail(CSA2_EINVAL, "dense_attn: compression ratio m=%d must be >= 1", m);
+    if (int e = check_align("dense_attn", {n_rec}, nullptr)) return e;
+    csa2::AttnArgs a;
+    fill_attn(a, B, Tq, H, D, N, 0, q, q_dtype, kv, kv_scale, kv_dtype, nullptr, swa, swa_scale, swa_dtype, S, W,
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, ws, ws_bytes);
+    a.dense_m = m;
+    a.n_rec = n_rec;
+    int e = validate_attn(a);
+    if (e) return e;
+    const size_t need = csa2::dense_attn_ws_bytes(B, Tq, H, D, N, W);
+    if (ws_bytes < need || (need && !ws))
+        return fail(CSA2_EWORKSPACE, "dense_attn: workspace %zu bytes, need %zu", ws_bytes, need);
+    e = csa2::launch_sparse_attn(a, stream);
+    return e ? hip_fail(e, "dense_attn launch") : CSA2_OK;
+}
+
 // ---------------------------------------------------------------- layer
 
 struct LayerPlan {
@@ -264,15 +290,21 @@ struct LayerPlan {
 
 static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
     if (!d) return fail(CSA2_EINVAL, "layer: null descriptor");
-    if (d->mode != CSA2_FULL && d->mode != CSA2_REINDEX && d->mode != CSA2_REUSE)
+    if (d->mode != CSA2_FULL && d->mode != CSA2_REINDEX && d->mode != CSA2_REUSE && d->mode != CSA2_HCA)
         return fail(CSA2_EINVAL, "layer: unknown mode %d", d->mode);
     if (d->B < 1 || d->Tq < 1 || d->N < 1 || d->m < 1)
         return fail(CSA2_EINVAL, "layer: sizes must be >= 1 (B=%d Tq=%d N=%d m=%d)", d->B, d->Tq, d->N, d->m);
+    pl.rows = d->B * d->Tq;
+    pl.ncols = d->N;
+    if (d->mode == CSA2_HCA) {  // no selection: attention over every visible record
+        if (int e = check_align("layer", {d->n_rec}, d->ws)) return e;
+        pl.off_scores = pl.off_pool = pl.off_topk = pl.off_attn = 0;
+        pl.total = align256(csa2::dense_attn_ws_bytes(d->B, d->Tq, d->H, d->D, d->N, d->W));
+        return CSA2_OK;
+    }
     if (d->K < 1 || d->K > CSA2_MAX_K) return fail(CSA2_EINVAL, "layer: K=%d outside 1..%d", d->K, CSA2_MAX_K);
     if (!d->idx_inout) return fail(CSA2_EINVAL, "layer: idx_inout is required");
     if (int e = check_align("layer", {d->idx_inout, d->pool_inout}, d->ws)) return e;
-    pl.rows = d->B * d->Tq;
-    pl.ncols = d->N;
     const bool scores_needed = d->mode != CSA2_REUSE;
     if (d->mode == CSA2_FULL && d->pool_inout) {
         if (d->blk < 1 || d->P < 1 || d->P > CSA2_MAX_K)
@@ -306,6 +338,10 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     LayerPlan pl;
     int e = plan_layer(d, pl);
     if (e) return e;
+    if (d->mode == CSA2_HCA)
+        return csa2_dense_attn(d->B, d->Tq, d->H, d->D, d->N, d->m, d->n_rec, d->q, d->q_dtype, d->kv, d->kv_scale,
+                               d->kv_dtype, d->swa, d->swa_scale, d->swa_dtype, d->S, d->W, d->q_pos, d->sink,
+                               d->sm_scale, d->rope_dims, d->rope_base, d->out, d->ws, d->ws_bytes, stream);
     csa2::IndexArgs ia;
     const bool scoring = d->mode != CSA2_REUSE;
     const bool pooled = d->mode == CSA2_REINDEX && d->pool_inout;

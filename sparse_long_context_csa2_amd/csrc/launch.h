@@ -64,9 +64,12 @@ struct AttnArgs {
     float* out;
     void* ws;
     size_t ws_bytes;
+    int dense_m = 0;                // > 0: dense mode (no idx; all visible records at ratio dense_m)
+    const int32_t* n_rec = nullptr;  // dense mode: [B] or null (= N)
 };
 bool sparse_attn_mfma_ok(const AttnArgs& a);
 size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W);
+size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W);
 int launch_sparse_attn(const AttnArgs& a, void* stream);
 // The allocation-free entry point's static scratch: its size, and its
 // address on the current device (looked up on the first call per device;

@@ -4,7 +4,8 @@
 :mod:`.workloads`) to the GPU once, owns the per-layer index, pool, output
 and workspace buffers, and enqueues the layers with ``csa2_layer`` in
 order: a Full layer (optionally building the block pool), Reindex layers
-searching that pool, and Reuse layers reading the last index set.
+searching that pool, Reuse layers reading the last index set, and HCA
+layers attending to every visible record.
 """
 
 from __future__ import annotations
@@ -54,9 +55,9 @@ class DeviceGroup:
         self.idx: List[torch.Tensor] = []
         cur = None
         for d in self.layers:
-            if d["mode"] != "reuse":
+            if d["mode"] in ("full", "reindex"):
                 cur = torch.full((B, Tq, d["K"]), -1, dtype=torch.int32, device=device)
-            self.idx.append(cur)
+            self.idx.append(cur if d["mode"] != "hca" else None)
         self.pool = None
         if any(d["build_pool"] for d in self.layers):
             self.pool = torch.full((B, Tq, wl.P), -1, dtype=torch.int32, device=device)
@@ -83,5 +84,5 @@ class DeviceGroup:
     def outputs(self) -> List[np.ndarray]:
         return [d["out"].cpu().numpy() for d in self.layers]
 
-    def index_sets(self) -> List[np.ndarray]:
-        return [i.cpu().numpy() for i in self.idx]
+    def index_sets(self) -> List[Optional[np.ndarray]]:
+        return [None if i is None else i.cpu().numpy() for i in self.idx]

@@ -160,6 +160,11 @@ CONFIGS: Dict[str, Workload] = {
         k_dtype="e4m3", kv_dtype="e4m3", swa_dtype="e4m3",
         description="long-context decode: B=8, context 1,048,576 (N=262,144); "
                     "keys, latent and window in e4m3 with an fp32 scale per row"),
+    "C6": Workload(
+        name="C6-hca-decode-bf16", seed=5, B=8, Tq=1, N=8192, m=128, Hi=32, Di=128, H=64, D=512,
+        rope_dims=64, W=128, K=0, decode_pos=1048576, modes=("hca",),
+        description="heavily compressed attention decode: B=8, context 1,048,576 at m'=128 "
+                    "(N=8,192 records, all visible), no indexer, SWA 128 plus sink, bf16"),
 }
 
 _NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}

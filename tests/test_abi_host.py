@@ -201,3 +201,25 @@ def test_sparse_attn_noalloc_validation(L):
     # the decode shapes of the benchmark fit
     for Q in (8, 16, 64):
         assert L.csa2_sparse_attn_workspace_bytes(Q, 1, 64, 512, 512, 128) <= 6 << 20
+
+
+def test_dense_attn_validation(L):
+    """csa2_dense_attn (HCA): the attention checks plus m >= 1; its
+    workspace grows with the record count, since a long dense list is
+    split across compute units."""
+    def call(**kw):
+        a = dict(B=1, Tq=1, H=64, D=512, N=8192, m=128, nrec=None, q=FAKE, qdt=1, kv=FAKE, kvs=None, kvdt=1,
+                 swa=FAKE, swas=None, swadt=1, S=128, W=128, pos=FAKE, sink=FAKE, out=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return L.csa2_dense_attn(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["m"], a["nrec"], a["q"], a["qdt"],
+                                 a["kv"], a["kvs"], a["kvdt"], a["swa"], a["swas"], a["swadt"], a["S"], a["W"],
+                                 a["pos"], a["sink"], 0.0, 64, 10000.0, a["out"], a["ws"], a["wsb"], None)
+    assert call(m=0) == B.CSA2_EINVAL
+    assert call(W=129) == B.CSA2_EINVAL
+    assert call(nrec=FAKE + 4) == B.CSA2_EINVAL
+    assert call(kvdt=2) == B.CSA2_EINVAL
+    need = L.csa2_dense_attn_workspace_bytes(8, 1, 64, 512, 8192, 128)
+    assert need >= 8 * 8 * 64 * 512 * 4  # 8 queries x 8 splits of fp32 partials
+    assert call(B=8) == B.CSA2_EWORKSPACE
+    assert L.csa2_dense_attn_workspace_bytes(8, 1, 64, 512, 10, 8) == 0  # one tile: no split
+    assert call(H=3, D=2048, qdt=0, kvdt=0, swadt=0) == B.CSA2_EUNSUPPORTED

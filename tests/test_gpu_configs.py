@@ -26,6 +26,7 @@ SAMPLES = {
     "C3": [(0, 0), (17, 0), (63, 0)],
     "C4": [(0, 0), (9, 0), (15, 0)],
     "C5": [(0, 0), (7, 0)],
+    "C6": [(0, 0), (3, 0), (7, 0)],
 }
 # rows whose whole score row is compared (a full C2 row costs the oracle
 # 1024 columns; a C5 row 262,144)
@@ -35,6 +36,7 @@ SCORE_ROWS = {
     "C3": [(0, 0), (17, 0), (63, 0)],
     "C4": [(0, 0), (9, 0), (15, 0)],
     "C5": [(0, 0), (7, 0)],
+    "C6": [],
 }
 # unit-scale variants: rows and queries ~ N(0, 1), the scale the contract's
 # attention bounds are stated for
@@ -76,7 +78,7 @@ def _device_scores(grp, li, pooled):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C3u", "C5u"])
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C6", "C3u", "C5u"])
 def test_config_full_size(cfg):
     print(f"[case] full-size {cfg}", flush=True)
     wl, base = _workload(cfg)
@@ -89,13 +91,14 @@ def test_config_full_size(cfg):
     pool = None if grp.pool is None else grp.pool.cpu().numpy()
     for o in outs:
         assert np.isfinite(o).all()
-    _row_properties(inp, idxs[0], wl.K)
+    if idxs[0] is not None:
+        _row_properties(inp, idxs[0], wl.K)
     sh, lays = inp["shared"], inp["layers"]
 
     # whole score rows, element by element
     worst_rel = 0.0
     for li, lay in enumerate(lays):
-        if lay["mode"] == "reuse":
+        if lay["mode"] in ("reuse", "hca"):
             continue
         pooled = lay["mode"] == "reindex"
         g = _device_scores(grp, li, pooled)
@@ -111,7 +114,7 @@ def test_config_full_size(cfg):
         prev = None
         for li, lay in enumerate(lays):
             where = f"{cfg} layer {li} ({lay['mode']}) b={b} t={ti}"
-            ids = idxs[li][b, ti]
+            ids = None if idxs[li] is None else idxs[li][b, ti]
             if lay["mode"] == "full":
                 r = O.layer_query(sh, lay, b, ti, O.FULL, build_pool=lay["build_pool"])
                 nd += PR.check_topk(ids, r["cand"], r["scores"], lay["K"], where)
@@ -127,6 +130,9 @@ def test_config_full_size(cfg):
                 gp = pool[b, ti]
                 r = O.layer_query(sh, lay, b, ti, O.REINDEX, pool_in=gp[gp >= 0])
                 nd += PR.check_topk(ids, r["cand"], r["scores"], lay["K"], where)
+            elif lay["mode"] == "hca":  # every visible record
+                t = int(lay["q_pos"][b, ti])
+                ids = np.arange(min(wl.N, (t + 1) // wl.m))
             else:
                 assert np.array_equal(ids, prev), where
             err, tol = PR.check_attn_query(outs[li][b, ti], sh, lay, b, ti, ids, wl.kv_dtype, where)

@@ -480,6 +480,75 @@ def test_sparse_attn_generic(H, D, dt):
                 PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], dt, f"b={b} t={ti}")
 
 
+# ------------------------------------------------------------------ dense (HCA)
+
+def _visible(inp, b, ti):
+    sh, lay = inp["shared"], inp["layers"][0]
+    nrec = sh["N"] if sh["n_rec"] is None else int(sh["n_rec"][b])
+    return np.arange(min(nrec, (int(lay["q_pos"][b, ti]) + 1) // sh["m"]), dtype=np.int64)
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("B,Tq,N,W,n_rec,unit", [(3, 1, 3000, 128, (3000, 1777, 5), False),
+                                                   (1, 1, 20000, 128, None, True),
+                                                   (2, 150, 60, 16, (60, 33), False)])
+def test_dense_attn(kdt, B, Tq, N, W, n_rec, unit):
+    """HCA attention over every visible record: decode rows with ragged
+    record counts (a long list split over many compute units; 20,000
+    unit-scale records in 32 splits) and prefill rows where visibility grows
+    with the position (records still holding future tokens excluded)."""
+    _case(f"dense_attn {kdt} B={B} Tq={Tq} N={N} W={W} n_rec={n_rec} unit={unit}")
+    kw = dict(q_std=1.0, kv_std=1.0) if unit else {}
+    if n_rec is not None:
+        kw["n_rec"] = n_rec
+    decode = Tq == 1
+    wl = _small(B=B, Tq=Tq, N=N, K=0, W=W, swa_slots=W + 3 if decode else 0, decode_pos=4 * N + 9 if decode else None,
+                k_dtype=kdt, kv_dtype=kdt, swa_dtype=kdt, modes=("hca",), **kw)
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_dense_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(lay["swa"]),
+                             _dev(lay["swa_scale"]), W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims, sh["m"],
+                             n_rec=_dev(sh["n_rec"]))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rows = [(b, ti) for b in range(B) for ti in (range(Tq) if Tq < 10 else (0, 2, 3, 4, 77, Tq - 1))]
+    worst = 0.0
+    for b, ti in rows:
+        err, tol = PR.check_attn_query(out[b, ti], sh, lay, b, ti, _visible(inp, b, ti), kdt, f"b={b} t={ti}")
+        worst = max(worst, err / tol)
+        if unit:
+            assert tol > 0.9 * PR.ATTN_TOL[kdt]
+    print(f"worst err / bound {worst:.3g}")
+
+
+def test_dense_attn_generic_and_layer_mode():
+    """Dense mode on the generic kernel (2 heads x 16, fp32) and the HCA
+    mode of csa2_layer (64 x 512 bf16, through DeviceGroup)."""
+    _case("dense_attn generic kernel; csa2_layer HCA mode")
+    wl = _small(B=2, Tq=40, N=12, K=0, H=2, D=16, rope_dims=4, W=6, decode_pos=None, q_dtype="f32",
+                kv_dtype="f32", swa_dtype="f32", q_std=1.0, kv_std=1.0, modes=("hca",), n_rec=(12, 7))
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_dense_attn(_dev(lay["q"]), _dev(sh["kv"]), None, _dev(lay["swa"]), None, wl.W, _dev(lay["q_pos"]),
+                             _dev(lay["sink"]), wl.rope_dims, sh["m"], n_rec=_dev(sh["n_rec"]))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(2):
+        for ti in range(40):
+            ref = PR.oracle_attention(sh, lay, b, ti, _visible(inp, b, ti))
+            PR.check_attn(out[b, ti], ref, 1e-4, f"generic b={b} t={ti}")
+    wl = _small(B=3, Tq=1, N=2000, K=0, W=64, decode_pos=4 * 1500, modes=("hca",), n_rec=(2000, 1200, 3))
+    inp = WL.make_inputs(wl)
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    out = grp.outputs()[0]
+    for b in range(3):
+        PR.check_attn_query(out[b, 0], inp["shared"], inp["layers"][0], b, 0, _visible(inp, b, 0), "bf16",
+                            f"layer b={b}")
+
+
 # ------------------------------------------------------------------ layers
 
 def _check_group(inp, grp, rows):

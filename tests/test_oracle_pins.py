@@ -347,6 +347,25 @@ def test_layer_equals_dense_softmax_when_everything_is_selected(kv_dtype):
             assert np.allclose(r["out"], ref, atol=1e-12), (b, ti)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
+def test_hca_layer_is_dense_softmax_over_visible_records(kv_dtype):
+    """An HCA layer (no indexer) attends to every visible compressed record
+    plus the window: it equals one torch fp64 softmax over exactly those
+    rows and a sink key, whatever K says; records still holding future
+    tokens are left out (t = 0..2 see no record at m = 4)."""
+    wl = WL.Workload(name="hca", seed=12, B=2, Tq=30, N=9, m=4, Hi=3, Di=8, H=3, D=12,
+                     rope_dims=4, W=5, K=0, q_idx_dtype="f32", k_dtype=kv_dtype, q_dtype="f32",
+                     kv_dtype=kv_dtype, swa_dtype=kv_dtype, q_std=1.0, kv_std=1.0, modes=("hca",),
+                     n_rec=(9, 4))
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    for b in range(2):
+        for ti in range(30):
+            r = O.layer_query(sh, lay, b, ti, O.HCA)
+            assert r["sel"].tolist() == [s for s in range(wl.n_rec[b]) if 4 * s + 3 <= ti]
+            assert np.allclose(r["out"], _dense_reference(sh, lay, b, ti), atol=1e-12), (b, ti)
+
+
 def test_c1_hierarchy_invariant_and_counts():
     """K <= P: Top-K over the pool equals Top-K over all visible records (a
     block holding a global top-K record has a max at least the K-th score,

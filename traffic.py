@@ -34,7 +34,7 @@ MARK = "bitwise_not"   # kernel-name fragment of the group markers
 COPY = "MulFunctor"    # kernel-name fragment of the reference copy
 
 # source file of each ABI call's kernels
-SOURCE = {"attn": "attn.hip", "index_full": "indexer.hip", "index_pool": "indexer.hip",
+SOURCE = {"attn": "attn.hip", "attn_dense": "attn.hip", "index_full": "indexer.hip", "index_pool": "indexer.hip",
           "topk_full": "topk.hip", "topk_pool": "topk.hip", "block_pool": "topk.hip"}
 
 
@@ -81,7 +81,8 @@ def _calls_of(workload: str):
     for mode in WL.CONFIGS[workload].modes:
         m = mode.split("+")[0]
         seq = {"full": ["index_full"] + (["block_pool"] if mode.endswith("+pool") else []) + ["topk_full"],
-               "reindex": ["index_pool", "topk_pool"], "reuse": []}[m] + ["attn"]
+               "reindex": ["index_pool", "topk_pool"], "reuse": [], "hca": []}[m] + \
+            (["attn_dense"] if m == "hca" else ["attn"])
         names += [n for n in seq if n not in names]
     return names
 
