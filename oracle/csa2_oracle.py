@@ -94,15 +94,92 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def dequant(arr: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
+def _e2m1_value(code: int) -> float:
+    """Value of one four-bit E2M1 code: sign bit 3, two exponent bits (bias
+    1), one mantissa bit; exponent 0 is subnormal (0 or 0.5).  The eight
+    magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([COURSE] "How DeepSeek stores
+    its main KV cache in four-bit numbers", "Which values can E2M1
+    represent?"); +0 and -0 are two codes of one value."""
+    s = -1.0 if code & 8 else 1.0
+    e = (code >> 1) & 3
+    mant = code & 1
+    if e == 0:
+        return s * 0.5 * mant
+    return s * (1.0 + 0.5 * mant) * 2.0 ** (e - 1)
+
+
+_E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Four-bit E2M1 codes (one per element, 0..15) -> float64 (exact)."""
+    return _E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """Two four-bit codes per byte -> one code per element: element 2j is
+    the low nibble of byte j, element 2j+1 the high nibble ([COURSE] FP4
+    lesson: two four-bit values fit inside one byte)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """E8M0 block-scale bytes -> float64: 2^(code - 127); 255 is NaN (the
+    shared scale of the OCP microscaling formats, MXFP4 included)."""
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+# FP4 main-KV row: each group of 16 channels holds 16 E2M1 codes and one E4M3
+# scale: 16*4 + 8 = 72 bits, so a 512-channel row takes 288 bytes ([EXPL] §7
+# "FP4 global KV").  Row layout here: the D/2 code bytes, then the D/16 scale
+# bytes.
+FP4_GROUP = 16
+MX_BLOCK = 32
+
+
+def dequant_fp4_rows(rows: np.ndarray) -> np.ndarray:
+    """FP4 main-KV rows [..., D/2 + D/16] bytes -> values [..., D]: value =
+    E2M1 level x the group's E4M3 scale ([COURSE] FP4 lesson, "Give a block a
+    shared scale": reconstructed value = stored level x shared scale)."""
+    r = np.asarray(rows, dtype=np.uint8)
+    D = r.shape[-1] * 16 // 9
+    codes = unpack_fp4(r[..., : D // 2])
+    scale = decode_e4m3(r[..., D // 2:])
+    return decode_e2m1(codes) * np.repeat(scale, FP4_GROUP, axis=-1)
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 (OCP microscaling): packed E2M1 codes [..., n/2] and one E8M0
+    scale per 32 elements [..., n/32] -> values [..., n] (the indexer's
+    query and key format, [EXPL] §7 table)."""
+    v = decode_e2m1(unpack_fp4(codes))
+    return v * np.repeat(decode_e8m0(scales), MX_BLOCK, axis=-1)
+
+
+def dequant(arr: np.ndarray, scale: Optional[np.ndarray] = None, fmt: Optional[str] = None) -> np.ndarray:
     """Storage array -> float64 values.
 
     float32 and float64 arrays are upcast, uint16 arrays are bf16 bit
     patterns, uint8 arrays are e4m3 codes and then need ``scale``: one value
-    per row (the array's shape without its last axis).  Quantized cache rows
-    hold code*scale ([COURSE] FP4 lesson, "Quantize after RoPE": values are
-    dequantized before attention).
+    per row (the array's shape without its last axis).  ``fmt`` "fp4" reads
+    FP4 main-KV rows (dequant_fp4_rows, no separate scale); "mxfp4" reads
+    packed E2M1 codes with ``scale`` holding the E8M0 block scales.
+    Quantized cache rows hold level*scale ([COURSE] FP4 lesson, "Quantize
+    after RoPE": values are dequantized before attention).
     """
+    if fmt == "fp4":
+        if scale is not None:
+            raise ValueError("FP4 rows carry their scales inline")
+        return dequant_fp4_rows(arr)
+    if fmt == "mxfp4":
+        if scale is None:
+            raise ValueError("MXFP4 needs its E8M0 block scales")
+        return dequant_mxfp4(arr, scale)
     a = np.asarray(arr)
     if a.dtype == np.float32 or a.dtype == np.float64:
         out = a.astype(np.float64)
@@ -284,6 +361,18 @@ def attend(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, sm: float) -> np.n
 FULL, REINDEX, REUSE, HCA = "full", "reindex", "reuse", "hca"
 
 
+def _keys(shared: Dict, b: int, recs: np.ndarray) -> np.ndarray:
+    """Indexer key rows of sequence b, upcast (format from shared["k_format"])."""
+    ks = shared.get("k_scale")
+    return dequant(shared["k_idx"][b][recs], None if ks is None else ks[b][recs], shared.get("k_format"))
+
+
+def _queries(layer: Dict, b: int, ti: int) -> np.ndarray:
+    """Indexer queries [Hi][Di] of one token, upcast."""
+    qs = layer.get("q_idx_scale")
+    return dequant(layer["q_idx"][b, ti], None if qs is None else qs[b, ti], layer.get("q_idx_format"))
+
+
 def _n_rec(shared: Dict, b: int) -> int:
     n_rec = shared.get("n_rec")
     N = shared["N"]
@@ -337,9 +426,8 @@ def layer_query(shared: Dict, layer: Dict, b: int, ti: int, mode: str,
             cand = vis if pool_in is None else pool_records(pool_in, vis, int(layer["blk"]))
         else:
             raise ValueError(mode)
-        k_rows = dequant(shared["k_idx"][b][cand],
-                         None if shared.get("k_scale") is None else shared["k_scale"][b][cand])
-        q_i = dequant(layer["q_idx"][b, ti])
+        k_rows = _keys(shared, b, cand)
+        q_i = _queries(layer, b, ti)
         w = np.asarray(layer["w"][b, ti], dtype=np.float64)
         sc = index_scores(q_i, w, k_rows)
         res["cand"], res["scores"], res["n_scored"] = cand, sc, len(cand)
@@ -352,12 +440,14 @@ def layer_query(shared: Dict, layer: Dict, b: int, ti: int, mode: str,
 
     sel_valid = sel[(sel >= 0) & (sel < shared["N"])]
     glob = dequant(shared["kv"][b][sel_valid],
-                   None if shared.get("kv_scale") is None else shared["kv_scale"][b][sel_valid])
+                   None if shared.get("kv_scale") is None else shared["kv_scale"][b][sel_valid],
+                   shared.get("kv_format"))
     S = layer["swa"].shape[1]
     pos = window_positions(t, int(layer["W"]))
     slots = pos % S
     loc = dequant(layer["swa"][b][slots],
-                  None if layer.get("swa_scale") is None else layer["swa_scale"][b][slots])
+                  None if layer.get("swa_scale") is None else layer["swa_scale"][b][slots],
+                  layer.get("swa_format"))
     rows = np.concatenate([glob, loc], axis=0)
     q = dequant(layer["q"][b, ti])
     D = q.shape[-1]
@@ -398,10 +488,8 @@ def full_row_scores(shared: Dict, layer: Dict, b: int, ti: int) -> np.ndarray:
     vis = visible_records(_n_rec(shared, b), int(shared["m"]), t)
     row = np.full(N, NEG_INF, dtype=np.float64)
     if len(vis):
-        k_rows = dequant(shared["k_idx"][b][vis],
-                         None if shared.get("k_scale") is None else shared["k_scale"][b][vis])
-        row[vis] = index_scores(dequant(layer["q_idx"][b, ti]),
-                                np.asarray(layer["w"][b, ti], dtype=np.float64), k_rows)
+        row[vis] = index_scores(_queries(layer, b, ti), np.asarray(layer["w"][b, ti], dtype=np.float64),
+                                _keys(shared, b, vis))
     return row
 
 
@@ -427,9 +515,7 @@ def pool_row_scores(shared: Dict, layer: Dict, b: int, ti: int,
         recs.append(s)
     if cols:
         recs = np.asarray(recs, dtype=np.int64)
-        k_rows = dequant(shared["k_idx"][b][recs],
-                         None if shared.get("k_scale") is None else shared["k_scale"][b][recs])
-        row[np.asarray(cols)] = index_scores(dequant(layer["q_idx"][b, ti]),
+        row[np.asarray(cols)] = index_scores(_queries(layer, b, ti),
                                              np.asarray(layer["w"][b, ti], dtype=np.float64),
-                                             k_rows)
+                                             _keys(shared, b, recs))
     return row

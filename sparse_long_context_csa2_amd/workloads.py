@@ -75,6 +75,78 @@ def quantize_rows_e4m3(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return e4m3_encode(v), scale
 
 
+def _e4m3_decode_f32(codes: np.ndarray) -> np.ndarray:
+    """Value of e4m3fn codes as float32 (the quantizers need the stored
+    scale's value)."""
+    c = np.asarray(codes, dtype=np.int32)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float32)
+    v = np.where(e == 0, m / np.float32(8.0) * np.float32(2.0 ** -6),
+                 (np.float32(1.0) + m / np.float32(8.0)) * np.exp2((e - 7).astype(np.float32)))
+    return np.where(c & 0x80, -v, v).astype(np.float32)
+
+
+_E2M1_LEVELS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """float32 values -> four-bit E2M1 codes (one per element, 0..15): the
+    nearest of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the code
+    with an even mantissa bit, saturating at 6; bit 3 is the sign."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.minimum(np.abs(v), np.float32(6.0))
+    # distance to every level; argmin takes the lower code of an exact tie,
+    # which moves up one when that code is odd (its mantissa bit is set)
+    d = np.abs(a[..., None] - _E2M1_LEVELS)
+    code = np.argmin(d, axis=-1).astype(np.uint8)
+    tie = np.take_along_axis(d, code[..., None].astype(np.int64), -1)[..., 0]
+    nxt = np.minimum(code + 1, 7)
+    tie_up = (code % 2 == 1) & (np.take_along_axis(d, nxt[..., None].astype(np.int64), -1)[..., 0] == tie)
+    code = np.where(tie_up, nxt, code).astype(np.uint8)
+    return (code | (np.signbit(v).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+def pack_fp4(codes: np.ndarray) -> np.ndarray:
+    """One E2M1 code per element -> two per byte (element 2j in the low
+    nibble of byte j)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_rows_fp4(x: np.ndarray) -> np.ndarray:
+    """FP4 main-KV rows: every 16 channels share one E4M3 scale, the largest
+    magnitude of the group / 6 rounded to nearest even (an all-zero group has
+    scale 0 and codes 0); codes = E2M1(x / scale).  Row layout: the D/2 code
+    bytes, then the D/16 scale bytes (288 bytes for 512 channels)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // 16, 16))
+    amax = np.abs(g).max(axis=-1)
+    sc_code = e4m3_encode(amax / np.float32(6.0))
+    sc = _e4m3_decode_f32(sc_code)
+    safe = np.where(sc > 0, sc, np.float32(1.0))
+    v = np.where((sc > 0)[..., None], g / safe[..., None], np.float32(0.0))
+    codes = e2m1_encode(v).reshape(x.shape)
+    return np.concatenate([pack_fp4(codes), sc_code], axis=-1)
+
+
+def quantize_mxfp4(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """OCP MXFP4: blocks of 32 elements share an E8M0 scale 2^e with e =
+    floor(log2(max |x|)) - 2 (2 is E2M1's largest exponent), clamped to
+    [-127, 127]; elements = E2M1(x / 2^e), saturating.  Returns (packed
+    codes [..., n/2], scale bytes e + 127 [..., n/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    blk = x.reshape(x.shape[:-1] + (n // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, np.float32(1e-38)))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int32)
+    v = blk / np.exp2(e.astype(np.float32))[..., None]
+    codes = e2m1_encode(v).reshape(x.shape)
+    return pack_fp4(codes), (e + 127).astype(np.uint8)
+
+
 # --------------------------------------------------------------------------
 # Workload description
 # --------------------------------------------------------------------------
@@ -102,7 +174,8 @@ class Workload:
     rope_base: float = 10000.0
     # decode: all queries at position `decode_pos`; prefill: q_pos = 0..Tq-1
     decode_pos: Optional[int] = None
-    # storage dtypes: "f32" | "bf16" | "e4m3"
+    # storage dtypes: "f32" | "bf16" | "e4m3"; "fp4" (main KV rows: E2M1 + an
+    # E4M3 scale per 16 channels); "mxfp4" (indexer queries and keys)
     q_idx_dtype: str = "bf16"
     k_dtype: str = "bf16"
     q_dtype: str = "bf16"
@@ -167,7 +240,7 @@ CONFIGS: Dict[str, Workload] = {
                     "(N=8,192 records, all visible), no indexer, SWA 128 plus sink, bf16"),
 }
 
-_NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}
+_NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "fp4": np.uint8, "mxfp4": np.uint8}
 
 # --------------------------------------------------------------------------
 # Generation
@@ -193,14 +266,30 @@ def _normal_f32(ss: np.random.SeedSequence, shape, std: float) -> np.ndarray:
 
 
 def _store(x: np.ndarray, dtype: str):
-    """float32 draw -> (storage array, per-row scale or None)."""
+    """float32 draw -> (storage array, scale array or None)."""
     if dtype == "f32":
         return x, None
     if dtype == "bf16":
         return f32_to_bf16_bits(x), None
     if dtype == "e4m3":
         return quantize_rows_e4m3(x)
+    if dtype == "fp4":
+        return quantize_rows_fp4(x), None
+    if dtype == "mxfp4":
+        return quantize_mxfp4(x)
     raise ValueError(dtype)
+
+
+def stored_shape(row_shape, dtype: str):
+    """(storage shape, scale shape or None) of a [..., n] float tensor."""
+    *lead, n = row_shape
+    if dtype == "fp4":
+        return tuple(lead) + (n // 2 + n // 16,), None
+    if dtype == "mxfp4":
+        return tuple(lead) + (n // 2,), tuple(lead) + (n // 32,)
+    if dtype == "e4m3":
+        return tuple(row_shape), tuple(lead)
+    return tuple(row_shape), None
 
 
 def _batched_normal(ss: np.random.SeedSequence, B: int, row_shape, std: float, dtype: str,
@@ -209,8 +298,11 @@ def _batched_normal(ss: np.random.SeedSequence, B: int, row_shape, std: float, d
     stream per sequence) and store it.  ``only`` restricts the draw to some
     sequences (the others stay zero) for memory-bounded samples."""
     kids = ss.spawn(B)
-    out = np.zeros((B,) + tuple(row_shape), dtype=_NP_STORAGE[dtype])
-    scale = np.zeros((B,) + tuple(row_shape[:-1]), dtype=np.float32) if dtype == "e4m3" else None
+    shp, sshp = stored_shape(row_shape, dtype)
+    out = np.zeros((B,) + shp, dtype=_NP_STORAGE[dtype])
+    scale = None
+    if sshp is not None:
+        scale = np.zeros((B,) + sshp, dtype=np.float32 if dtype == "e4m3" else np.uint8)
     idx = range(B) if only is None else only
 
     def one(b):
@@ -243,7 +335,7 @@ def make_inputs(wl: Workload, only: Optional[List[int]] = None, q_gain: float = 
     kv, kv_scale = _batched_normal(kids[1], B, (N, wl.D), kv_std, wl.kv_dtype, only)
     n_rec = None if wl.n_rec is None else np.asarray(wl.n_rec, dtype=np.int32)
     shared = dict(N=N, m=wl.m, n_rec=n_rec, k_idx=k_idx, k_scale=k_scale,
-                  kv=kv, kv_scale=kv_scale)
+                  kv=kv, kv_scale=kv_scale, k_format=wl.k_dtype, kv_format=wl.kv_dtype)
 
     if wl.decode_pos is not None:
         q_pos = np.full((B, Tq), wl.decode_pos, dtype=np.int64)
@@ -256,8 +348,8 @@ def make_inputs(wl: Workload, only: Optional[List[int]] = None, q_gain: float = 
     for li, mode_s in enumerate(wl.modes):
         base = 2 + 5 * li
         mode = mode_s.split("+")[0]
-        q_idx, _ = _batched_normal(kids[base + 0], B, (Tq, wl.Hi, wl.Di), qk_std,
-                                   wl.q_idx_dtype, only)
+        q_idx, q_idx_scale = _batched_normal(kids[base + 0], B, (Tq, wl.Hi, wl.Di), qk_std,
+                                             wl.q_idx_dtype, only)
         wk = kids[base + 1].spawn(B)
         w = np.zeros((B, Tq, wl.Hi), dtype=np.float32)
         for b in (range(B) if only is None else only):
@@ -275,14 +367,16 @@ def make_inputs(wl: Workload, only: Optional[List[int]] = None, q_gain: float = 
         sink = g.standard_normal(size=wl.H).astype(np.float32)
         layers.append(dict(
             mode=mode, build_pool=mode_s.endswith("+pool"), q_pos=q_pos, q_idx=q_idx, w=w,
+            q_idx_scale=q_idx_scale, q_idx_format=wl.q_idx_dtype, swa_format=wl.swa_dtype,
             q=q, swa=swa, swa_scale=swa_scale, sink=sink, K=wl.K, W=wl.W, blk=wl.blk,
             P=wl.P, rope_dims=wl.rope_dims, rope_base=wl.rope_base, sm_scale=0.0))
     return {"shared": shared, "layers": layers, "wl": wl}
 
 
 def dtype_code(dtype: str) -> int:
-    """Storage dtype name -> the library's dtype code (0 f32, 1 bf16, 2 e4m3)."""
-    return {"f32": 0, "bf16": 1, "e4m3": 2}[dtype]
+    """Storage dtype name -> the library's dtype code (0 f32, 1 bf16, 2 e4m3,
+    3 fp4 main-KV rows, 4 mxfp4)."""
+    return {"f32": 0, "bf16": 1, "e4m3": 2, "fp4": 3, "mxfp4": 4}[dtype]
 
 
 def storage_dtype_name(arr: np.ndarray) -> str:

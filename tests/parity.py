@@ -81,11 +81,13 @@ def entry_rows(shared, layer, b, ti, ids):
     and its window rows), for the scale of the attention bound."""
     ids = np.asarray(ids, dtype=np.int64)
     ids = ids[(ids >= 0) & (ids < shared["N"])]
-    glob = O.dequant(shared["kv"][b][ids], None if shared.get("kv_scale") is None else shared["kv_scale"][b][ids])
+    glob = O.dequant(shared["kv"][b][ids], None if shared.get("kv_scale") is None else shared["kv_scale"][b][ids],
+                     shared.get("kv_format"))
     t = int(layer["q_pos"][b, ti])
     S = layer["swa"].shape[1]
     slots = O.window_positions(t, int(layer["W"])) % S
-    loc = O.dequant(layer["swa"][b][slots], None if layer.get("swa_scale") is None else layer["swa_scale"][b][slots])
+    loc = O.dequant(layer["swa"][b][slots], None if layer.get("swa_scale") is None else layer["swa_scale"][b][slots],
+                    layer.get("swa_format"))
     return np.concatenate([glob, loc], 0)
 
 

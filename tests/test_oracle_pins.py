@@ -278,6 +278,85 @@ def test_e4m3_decoder_all_codes_against_torch():
     assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
 
 
+def test_e2m1_levels_printed():
+    """The eight E2M1 magnitudes in code order are the page's list, codes
+    8-15 are their negatives, and the 16 codes hold 15 distinct values."""
+    g = golden("fp4_e2m1.json")
+    vals = O.decode_e2m1(np.arange(16))
+    assert vals[:8].tolist() == g["magnitudes"]
+    assert (vals[8:] == -vals[:8]).all()
+    assert len(set(vals.tolist())) == g["distinct_values"]  # +0 and -0 compare equal
+
+
+def test_fp4_group_scale_and_row_size_printed():
+    """A group of 16 levels times its E4M3 scale (the page's 0.5 and 2
+    turning level 3 into 1.5 and 6); 16 x 4 + 8 = 72 bits per group and 288
+    bytes per 512-channel row; the quantizer stores 3.2 (scale 1) as level
+    3, read back 3.0."""
+    g = golden("fp4_e2m1.json")
+    three = 5  # E2M1 code of 3.0 (exponent 2, mantissa 1)
+    assert O.decode_e2m1(np.array([three]))[0] == 3.0
+    for ex in g["scale_examples"]:
+        sc_code = WL.e4m3_encode(np.array([ex["scale"]], np.float32))
+        row = np.concatenate([np.full(8, three | (three << 4), np.uint8), sc_code])  # 16 channels
+        vals = O.dequant_fp4_rows(row[None, :])[0]
+        assert vals.shape == (16,)
+        assert np.all(vals == ex["value"])
+    grp = g["group"]
+    assert grp["channels"] * grp["value_bits"] + grp["scale_bits"] == grp["bits"]
+    assert grp["bits"] / grp["channels"] == grp["bits_per_channel"]
+    rows = WL.quantize_rows_fp4(np.ones((1, g["row"]["channels"]), np.float32))
+    assert rows.shape[-1] == g["row"]["bytes"] == g["row"]["channels"] * grp["bits"] // grp["channels"] // 8
+    assert O.dequant_fp4_rows(rows).shape[-1] == g["row"]["channels"]
+    ex = g["rounding_example"]
+    code = WL.e2m1_encode(np.array([ex["original"] / ex["scale"]], np.float32))
+    back = O.decode_e2m1(code)[0] * ex["scale"]
+    assert back == ex["read_back"] and abs((back - ex["original"]) - ex["error"]) < 1e-6
+
+
+def test_fp4_rows_brute_force():
+    """FP4 rows against a per-channel loop: channel c reads the nibble of
+    byte c/2 (low nibble for even c) and the scale byte D/2 + c/16."""
+    mags = golden("fp4_e2m1.json")["magnitudes"]
+    level = lambda nib: (-1.0 if nib & 8 else 1.0) * mags[nib & 7]
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 256, size=(4, 9 * 8), dtype=np.uint8)  # D = 128
+    rows[:, 64:] = rng.integers(0, 0x7F, size=(4, 8))  # finite scales
+    e4m3 = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.dequant_fp4_rows(rows)
+    for r in range(4):
+        for c in range(128):
+            nib = (int(rows[r, c // 2]) >> (4 * (c % 2))) & 0xF
+            assert got[r, c] == level(nib) * e4m3[rows[r, 64 + c // 16]]
+
+
+def test_mxfp4_against_torch_e8m0_and_brute_force():
+    """E8M0 scales against torch.float8_e8m0fnu (all 256 codes); MXFP4
+    values against a per-element loop (32-element blocks)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = O.decode_e8m0(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    rng = np.random.default_rng(4)
+    packed = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)  # 128 elements
+    sc = rng.integers(100, 150, size=(3, 4), dtype=np.uint8)
+    v = O.dequant_mxfp4(packed, sc)
+    mags = golden("fp4_e2m1.json")["magnitudes"]
+    for r in range(3):
+        for i in range(128):
+            nib = (int(packed[r, i // 2]) >> (4 * (i % 2))) & 0xF
+            lev = (-1.0 if nib & 8 else 1.0) * mags[nib & 7]
+            assert v[r, i] == lev * ref[sc[r, i // 32]]
+    # the quantizer's shared exponent keeps every block's largest element
+    # within E2M1's range (the largest magnitude of a block lands in [4, 8))
+    x = rng.standard_normal((5, 128)).astype(np.float32)
+    c, s = WL.quantize_mxfp4(x)
+    blk = np.abs(x.reshape(5, 4, 32)).max(-1) / O.decode_e8m0(s)
+    assert np.all((blk >= 4) & (blk < 8))
+
+
 def test_bf16_decoder_against_torch():
     rng = np.random.default_rng(6)
     bits = rng.integers(0, 65536, size=4096, dtype=np.uint32).astype(np.uint16)
@@ -312,11 +391,11 @@ def _dense_reference(shared, layer, b, ti):
     vis = O.visible_records(shared["N"] if shared["n_rec"] is None else int(shared["n_rec"][b]),
                             shared["m"], t)
     glob = O.dequant(shared["kv"][b][vis], None if shared["kv_scale"] is None
-                     else shared["kv_scale"][b][vis])
+                     else shared["kv_scale"][b][vis], shared.get("kv_format"))
     pos = np.arange(max(0, t - layer["W"] + 1), t + 1)
     S = layer["swa"].shape[1]
     loc = O.dequant(layer["swa"][b][pos % S], None if layer["swa_scale"] is None
-                    else layer["swa_scale"][b][pos % S])
+                    else layer["swa_scale"][b][pos % S], layer.get("swa_format"))
     x = torch.from_numpy(np.concatenate([glob, loc], 0))
     q = torch.from_numpy(O.dequant(layer["q"][b, ti]))
     H, D = q.shape
@@ -364,6 +443,31 @@ def test_hca_layer_is_dense_softmax_over_visible_records(kv_dtype):
             r = O.layer_query(sh, lay, b, ti, O.HCA)
             assert r["sel"].tolist() == [s for s in range(wl.n_rec[b]) if 4 * s + 3 <= ti]
             assert np.allclose(r["out"], _dense_reference(sh, lay, b, ti), atol=1e-12), (b, ti)
+
+
+def test_fp4_layer_equals_dense_softmax_when_everything_is_selected():
+    """The V4.1 storage formats through a whole layer: FP4 main-KV rows,
+    MXFP4 indexer queries and keys, FP8 window rows; with K covering every
+    visible record the layer is one torch fp64 softmax over the dequantized
+    rows (the indexer then only has to keep everything)."""
+    wl = WL.Workload(name="fp4", seed=13, B=2, Tq=24, N=6, m=4, Hi=3, Di=32, H=3, D=32,
+                     rope_dims=4, W=5, K=8, q_idx_dtype="mxfp4", k_dtype="mxfp4", q_dtype="f32",
+                     kv_dtype="fp4", swa_dtype="e4m3", q_std=1.0, kv_std=1.0, w_dist="uniform")
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    assert sh["kv"].shape[-1] == 32 // 2 + 32 // 16 and sh["k_idx"].shape[-1] == 16
+    for b in range(2):
+        for ti in range(24):
+            r = O.layer_query(sh, lay, b, ti, O.FULL)
+            assert np.allclose(r["out"], _dense_reference(sh, lay, b, ti), atol=1e-12), (b, ti)
+    # MXFP4 scores: the same as scoring the dequantized vectors directly
+    for ti in (5, 23):
+        q = O.dequant_mxfp4(lay["q_idx"][0, ti], lay["q_idx_scale"][0, ti])
+        k = O.dequant_mxfp4(sh["k_idx"][0], sh["k_scale"][0])
+        want = np.maximum(k @ q.T, 0) @ lay["w"][0, ti].astype(np.float64)
+        got = O.full_row_scores(sh, lay, 0, ti)
+        vis = np.isfinite(got)
+        assert np.allclose(got[vis], want[vis], rtol=1e-12, atol=0)
 
 
 def test_c1_hierarchy_invariant_and_counts():
