@@ -4,9 +4,10 @@ The default run measures the Flash-shape prefill layer (1 sequence of 4096
 query tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x
 512 latent with 64 rotary dims, window 128, bf16) as ``value``, and the
 three decode workloads (Full decode at 64K context, hierarchical
-Full/Reindex/Reuse decode at 256K, fp8 decode at 1M) and the heavily
-compressed (HCA) decode at 1M in the same run, each reported in its own
-object under ``workloads``.  ``--workload`` picks
+Full/Reindex/Reuse decode at 256K, fp8 decode at 1M, the heavily
+compressed (HCA) decode at 1M, and the 1M decode in the V4.1 cache formats
+(FP4 main KV, MXFP4 indexer, FP8 window)) in the same run, each reported
+in its own object under ``workloads``.  ``--workload`` picks
 another primary workload; ``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
@@ -49,9 +50,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
-    ap.add_argument("--extra", default="C3,C4,C5,C6", help="further workloads measured in the same run")
+    ap.add_argument("--extra", default="C3,C4,C5,C6,C7", help="further workloads measured in the same run")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
@@ -77,11 +78,13 @@ def entries_per_query(wl, inp):
 
 def kernel_work(wl, inp):
     """Algorithmic bytes and flops per call of each step phase."""
-    elt = {"f32": 4, "bf16": 2, "e4m3": 1}
-    kbytes = wl.Di * elt[wl.k_dtype] + (4 if wl.k_dtype == "e4m3" else 0)
-    rbytes = wl.D * elt[wl.kv_dtype] + (4 if wl.kv_dtype == "e4m3" else 0)
-    qi_bytes = wl.Hi * wl.Di * elt[wl.q_idx_dtype] + wl.Hi * 4
-    q_bytes = wl.H * wl.D * elt[wl.q_dtype]
+    def row_bytes(n, dt):  # one stored row of n elements, with its scales
+        return {"f32": 4 * n, "bf16": 2 * n, "e4m3": n + 4, "fp4": n // 2 + n // 16, "mxfp4": n // 2 + n // 32}[dt]
+    kbytes = row_bytes(wl.Di, wl.k_dtype)
+    rbytes = row_bytes(wl.D, wl.kv_dtype)
+    wbytes = row_bytes(wl.D, wl.swa_dtype)
+    qi_bytes = wl.Hi * row_bytes(wl.Di, wl.q_idx_dtype) + wl.Hi * 4
+    q_bytes = wl.H * row_bytes(wl.D, wl.q_dtype)
     out_bytes = wl.H * wl.D * 4
     sel, win, vis = entries_per_query(wl, inp)
     rows = wl.B * wl.Tq
@@ -102,8 +105,9 @@ def kernel_work(wl, inp):
     # need (a decode query's own set; a prefill sequence's records and window
     # rows are shared by its tokens and read once)
     t_max = inp["layers"][0]["q_pos"].max(axis=1) + 1
-    uniq = np.minimum(vis.max(axis=1), sel.sum(axis=1)) + np.minimum(np.minimum(wl.S, t_max), win.sum(axis=1))
-    work["attn"] = dict(bytes=int(uniq.sum()) * rbytes + rows * (q_bytes + out_bytes),
+    urec = np.minimum(vis.max(axis=1), sel.sum(axis=1))
+    uwin = np.minimum(np.minimum(wl.S, t_max), win.sum(axis=1))
+    work["attn"] = dict(bytes=int(urec.sum()) * rbytes + int(uwin.sum()) * wbytes + rows * (q_bytes + out_bytes),
                         flops=4.0 * wl.D * wl.H * ent)
     # Selection steps: their own inputs and outputs (scores are an
     # intermediate of the layer, but they are what these kernels stream).
@@ -165,7 +169,7 @@ class Step:
             out = self.scores_full if pool is None else self.scores_pool
             return Bd.csa2_index_scores(lay["q_idx"], lay["w"], sh["k_idx"], sh["k_scale"], lay["q_pos"], sh["m"],
                                         n_rec=sh["n_rec"], pool=pool, blk=lay["blk"] if pool is not None else 0,
-                                        out=out, stream=self.stream, prepare=True)
+                                        out=out, stream=self.stream, prepare=True, q_scale=lay["q_idx_scale"])
         return f
 
     def _pool(self, lay):
@@ -367,7 +371,7 @@ def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
         "ms_per_step": round(ms_per_step, 4), "eager_ms_per_step": round(ms_eager, 4),
         "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 4),
         "steps": steps, "warmup": warmup,
-        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16"}[wl.kv_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16", "fp4": "fp4+mxfp4+e4m3+bf16"}[wl.kv_dtype],
         "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
                    "H": wl.H, "D": wl.D, "K": wl.K, "W": wl.W, "blk": wl.blk, "P": wl.P,
                    "layers": list(wl.modes), "cache_copies": copies},

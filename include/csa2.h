@@ -25,6 +25,17 @@
  *   one float32 scale per row (value = decode(code) * scale[row]).  Scales
  *   are finite and >= 0, as max|x|/448 is; the indexer may apply a key
  *   row's scale after the ReLU.
+ *   CSA2_FP4 = the FP4 main-KV row ("DeepSeek-V4.1-Flash explained",
+ *   section 7: each group of 16 channels holds 16 four-bit E2M1 values and
+ *   one E4M3 scale, 72 bits, so a 512-channel row takes 288 bytes): a row
+ *   of D channels is D/2 code bytes (channel 2j in the low nibble of byte
+ *   j) followed by D/16 E4M3 scale bytes; value = E2M1(code) * scale of its
+ *   group; no separate scale array.  Attention rows only, with E4M3 window
+ *   rows (the local cache stays FP8).
+ *   CSA2_MXFP4 = OCP MXFP4 (the indexer's query and key format, same
+ *   section): packed E2M1 codes [..][n/2] in the tensor and one E8M0 scale
+ *   byte (2^(b-127)) per 32 elements [..][n/32] in its scale argument.
+ *   Indexer queries and keys only.
  * - Positions are 0-based absolute token positions (int64).  Record s of
  *   a cache compressed at ratio m covers tokens m*s .. m*s+m-1 and is
  *   visible to a query at t only if m*s+m-1 <= t and s < n_rec ("DeepSeek V4
@@ -63,7 +74,7 @@ extern "C" {
 #define CSA2_EWORKSPACE (-3)   /* workspace missing or too small */
 #define CSA2_EHIP (-4)         /* a HIP launch failed */
 
-typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_E4M3 = 2 } csa2_dtype;
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_E4M3 = 2, CSA2_FP4 = 3, CSA2_MXFP4 = 4 } csa2_dtype;
 typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2, CSA2_HCA = 3 } csa2_mode;
 
 /* Largest K accepted by csa2_topk and csa2_layer. */
@@ -85,10 +96,13 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2, CSA2_HCA = 3 } c
  *   N          records per sequence in k_idx (>= 1)
  *   Hi, Di     indexer heads and head dim (1..64, 1..256)
  *   m          compression ratio (>= 1): tokens per record
- *   q_idx      [B][Tq][Hi][Di]  q_dtype in {F32, BF16}
+ *   q_idx      [B][Tq][Hi][Di]  q_dtype in {F32, BF16, MXFP4}
+ *   q_scale    MXFP4 queries: [B][Tq][Hi][Di/32] E8M0 bytes; else NULL
  *   w          [B][Tq][Hi] float32 head weights
- *   k_idx      [B][N][Di]       k_dtype in {F32, BF16, E4M3}
- *   k_scale    [B][N] float32, required for E4M3 and NULL otherwise
+ *   k_idx      [B][N][Di]       k_dtype in {F32, BF16, E4M3, MXFP4}
+ *   k_scale    E4M3: [B][N] float32; MXFP4: [B][N][Di/32] E8M0 bytes;
+ *              NULL otherwise.  MXFP4 needs Hi = 32, Di = 128, and MXFP4
+ *              queries need MXFP4 keys.
  *   q_pos      [B][Tq] int64 absolute query positions
  *   n_rec      [B] int32 valid record counts (<= N), or NULL for N
  *   pool, P, blk
@@ -102,8 +116,8 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2, CSA2_HCA = 3 } c
  * Workspace: none (ws may be NULL).
  * ------------------------------------------------------------------------ */
 int csa2_index_scores(int B, int Tq, int N, int Hi, int Di, int m,
-                      const void* q_idx, int q_dtype, const float* w,
-                      const void* k_idx, const float* k_scale, int k_dtype,
+                      const void* q_idx, int q_dtype, const void* q_scale, const float* w,
+                      const void* k_idx, const void* k_scale, int k_dtype,
                       const int64_t* q_pos, const int32_t* n_rec,
                       const int32_t* pool, int P, int blk,
                       float* scores, void* ws, size_t ws_bytes, void* stream);
@@ -179,8 +193,10 @@ size_t csa2_topk_workspace_bytes(int rows, int ncols, int K);
  * Inputs
  *   B, Tq, H, D, N, K  sizes (K in 0..CSA2_MAX_K; K = 0 means window only)
  *   q          [B][Tq][H][D]  q_dtype in {F32, BF16}
- *   kv         [B][N][D]      kv_dtype in {F32, BF16, E4M3}; kv_scale [B][N]
- *                             for E4M3, NULL otherwise
+ *   kv         [B][N][D]      kv_dtype in {F32, BF16, E4M3, FP4}; kv_scale
+ *                             [B][N] for E4M3, NULL otherwise (FP4 rows are
+ *                             [B][N][D/2 + D/16] bytes with inline scales and
+ *                             need E4M3 window rows, H = 64, D = 512)
  *   idx        [B][Tq][K] int32 record ids (-1 or out of range = empty)
  *   swa        [B][S][D]      ring of local rows: position p lives in slot
  *                             p mod S; swa_dtype like kv; swa_scale [B][S]
@@ -289,15 +305,16 @@ typedef struct csa2_layer_desc {
     int N, m;            /* records per sequence, tokens per record */
     const int32_t* n_rec;           /* [B] or NULL (= N) */
     const void* k_idx;              /* [B][N][Di] indexer keys */
-    const float* k_scale;           /* [B][N] for E4M3, else NULL */
+    const void* k_scale;            /* E4M3: [B][N] float; MXFP4: [B][N][Di/32] E8M0; else NULL */
     int k_dtype;
-    const void* kv;                 /* [B][N][D] shared latent (K = V) */
+    const void* kv;                 /* [B][N][D] shared latent (K = V); FP4: [B][N][D/2 + D/16] */
     const float* kv_scale;          /* [B][N] for E4M3, else NULL */
     int kv_dtype;
     /* this layer's indexer */
     int Hi, Di;
     const void* q_idx;              /* [B][Tq][Hi][Di] */
     int q_idx_dtype;
+    const void* q_idx_scale;        /* MXFP4: [B][Tq][Hi][Di/32] E8M0; else NULL */
     const float* w;                 /* [B][Tq][Hi] */
     /* this layer's attention */
     int H, D;

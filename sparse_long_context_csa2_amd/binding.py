@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OK, CSA2_EINVAL, CSA2_EUNSUPPORTED, CSA2_EWORKSPACE, CSA2_EHIP = 0, -1, -2, -3, -4
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, FP4, MXFP4 = 0, 1, 2, 3, 4
 FULL, REINDEX, REUSE, HCA = 0, 1, 2, 3
 MODES = {"full": FULL, "reindex": REINDEX, "reuse": REUSE, "hca": HCA}
 MAX_K = 2048
@@ -35,7 +35,7 @@ class LayerDesc(ctypes.Structure):
         ("N", _c_int), ("m", _c_int), ("n_rec", _vp),
         ("k_idx", _vp), ("k_scale", _vp), ("k_dtype", _c_int),
         ("kv", _vp), ("kv_scale", _vp), ("kv_dtype", _c_int),
-        ("Hi", _c_int), ("Di", _c_int), ("q_idx", _vp), ("q_idx_dtype", _c_int), ("w", _vp),
+        ("Hi", _c_int), ("Di", _c_int), ("q_idx", _vp), ("q_idx_dtype", _c_int), ("q_idx_scale", _vp), ("w", _vp),
         ("H", _c_int), ("D", _c_int), ("q", _vp), ("q_dtype", _c_int),
         ("swa", _vp), ("swa_scale", _vp), ("swa_dtype", _c_int), ("S", _c_int), ("W", _c_int),
         ("sink", _vp), ("sm_scale", _c_float), ("rope_dims", _c_int), ("rope_base", _c_float),
@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
                                "`python sparse_long_context_csa2_amd/build.py`")
         L = ctypes.CDLL(LIB_PATH)
         i, s, v, f = _c_int, _c_size, _vp, _c_float
-        L.csa2_index_scores.argtypes = [i, i, i, i, i, i, v, i, v, v, v, i, v, v, v, i, i, v, v, s, v]
+        L.csa2_index_scores.argtypes = [i, i, i, i, i, i, v, i, v, v, v, v, i, v, v, v, i, i, v, v, s, v]
         L.csa2_block_pool.argtypes = [i, i, i, i, v, v, v, s, v]
         L.csa2_block_pool_workspace_bytes.argtypes = [i, i, i]
         L.csa2_block_pool_workspace_bytes.restype = s
@@ -119,7 +119,10 @@ def _call(cfunc, args, result, prepare: bool, keep=()):
     return result
 
 
-def dtype_code(t: Optional[torch.Tensor]) -> int:
+def dtype_code(t: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None) -> int:
+    """Library dtype code of a storage tensor.  Packed four-bit tensors
+    (torch.float4_e2m1fn_x2) are MXFP4 when an E8M0 scale tensor comes with
+    them and FP4 main-KV rows (inline E4M3 group scales) otherwise."""
     if t is None:
         return F32
     if t.dtype == torch.float32:
@@ -128,7 +131,14 @@ def dtype_code(t: Optional[torch.Tensor]) -> int:
         return BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return E4M3
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return MXFP4 if scale is not None else FP4
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _elems(t: torch.Tensor) -> int:
+    """Elements along the last axis (a packed four-bit byte holds two)."""
+    return 2 * t.shape[-1] if t.dtype == torch.float4_e2m1fn_x2 else t.shape[-1]
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -170,20 +180,22 @@ def _ws(nbytes: int, device, ws: Optional[torch.Tensor], stream=None) -> Optiona
 
 
 def csa2_index_scores(q_idx, w, k_idx, k_scale, q_pos, m: int, n_rec=None, pool=None, blk: int = 0,
-                      out=None, stream=None, prepare: bool = False) -> torch.Tensor:
+                      out=None, stream=None, prepare: bool = False, q_scale=None) -> torch.Tensor:
     """Scores [B][Tq][N] (or [B][Tq][P*blk] with a pool); see csa2.h.
-    With ``prepare`` the call is returned as a ``Prepared`` instead of
-    being enqueued (likewise for the other entry points)."""
-    B, Tq, Hi, Di = q_idx.shape
+    ``q_scale``: the E8M0 block scales of MXFP4 queries.  With ``prepare``
+    the call is returned as a ``Prepared`` instead of being enqueued
+    (likewise for the other entry points)."""
+    B, Tq, Hi = q_idx.shape[:3]
+    Di = _elems(q_idx)
     N = k_idx.shape[1]
     P = 0 if pool is None else pool.shape[-1]
     ncols = N if pool is None else P * blk
     if out is None:
         out = _empty((B, Tq, ncols), torch.float32, q_idx.device, stream)
     return _call(lib().csa2_index_scores,
-                 (B, Tq, N, Hi, Di, m, _p(q_idx), dtype_code(q_idx), _p(w), _p(k_idx), _p(k_scale),
-                  dtype_code(k_idx), _p(q_pos), _p(n_rec), _p(pool), P, blk if pool is not None else 0, _p(out),
-                  None, 0, _stream(stream)), out, prepare)
+                 (B, Tq, N, Hi, Di, m, _p(q_idx), dtype_code(q_idx, q_scale), _p(q_scale), _p(w), _p(k_idx),
+                  _p(k_scale), dtype_code(k_idx, k_scale), _p(q_pos), _p(n_rec), _p(pool), P,
+                  blk if pool is not None else 0, _p(out), None, 0, _stream(stream)), out, prepare)
 
 
 def csa2_block_pool(scores, blk: int, P: int, out=None, ws=None, stream=None, prepare: bool = False) -> torch.Tensor:
@@ -225,9 +237,9 @@ def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, 
     nb = lib().csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W)
     ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_sparse_attn,
-                 (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(idx), _p(swa),
-                  _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,
-                  float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
+                 (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv, kv_scale), _p(idx),
+                  _p(swa), _p(swa_scale), dtype_code(swa, swa_scale), S, W, _p(q_pos), _p(sink), float(sm_scale),
+                  rope_dims, float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
 
 def csa2_dense_attn(q, kv, kv_scale, swa, swa_scale, W: int, q_pos, sink, rope_dims: int, m: int, n_rec=None,
@@ -243,9 +255,9 @@ def csa2_dense_attn(q, kv, kv_scale, swa, swa_scale, W: int, q_pos, sink, rope_d
     nb = lib().csa2_dense_attn_workspace_bytes(B, Tq, H, D, N, W)
     ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_dense_attn,
-                 (B, Tq, H, D, N, m, _p(n_rec), _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv), _p(swa),
-                  _p(swa_scale), dtype_code(swa), S, W, _p(q_pos), _p(sink), float(sm_scale), rope_dims,
-                  float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
+                 (B, Tq, H, D, N, m, _p(n_rec), _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv, kv_scale),
+                  _p(swa), _p(swa_scale), dtype_code(swa, swa_scale), S, W, _p(q_pos), _p(sink), float(sm_scale),
+                  rope_dims, float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
 
 def make_layer_desc(mode: str, shared: dict, layer: dict, idx_inout, pool_inout, out, ws=None) -> LayerDesc:
@@ -264,16 +276,17 @@ def make_layer_desc(mode: str, shared: dict, layer: dict, idx_inout, pool_inout,
     d.N, d.m = kv.shape[1], int(shared["m"])
     d.n_rec = _p(shared.get("n_rec"))
     k_idx = shared["k_idx"]
-    d.k_idx, d.k_scale, d.k_dtype = _p(k_idx), _p(shared.get("k_scale")), dtype_code(k_idx)
-    d.kv, d.kv_scale, d.kv_dtype = _p(kv), _p(shared.get("kv_scale")), dtype_code(kv)
+    d.k_idx, d.k_scale, d.k_dtype = _p(k_idx), _p(shared.get("k_scale")), dtype_code(k_idx, shared.get("k_scale"))
+    d.kv, d.kv_scale, d.kv_dtype = _p(kv), _p(shared.get("kv_scale")), dtype_code(kv, shared.get("kv_scale"))
     q_idx = layer.get("q_idx")
     if q_idx is not None:
-        d.Hi, d.Di = q_idx.shape[2], q_idx.shape[3]
-        d.q_idx, d.q_idx_dtype, d.w = _p(q_idx), dtype_code(q_idx), _p(layer["w"])
+        qs = layer.get("q_idx_scale")
+        d.Hi, d.Di = q_idx.shape[2], _elems(q_idx)
+        d.q_idx, d.q_idx_dtype, d.q_idx_scale, d.w = _p(q_idx), dtype_code(q_idx, qs), _p(qs), _p(layer["w"])
     d.H, d.D, d.q, d.q_dtype = H, D, _p(q), dtype_code(q)
     swa = layer["swa"]
-    d.swa, d.swa_scale, d.swa_dtype, d.S, d.W = _p(swa), _p(layer.get("swa_scale")), dtype_code(swa), \
-        swa.shape[1], int(layer["W"])
+    d.swa, d.swa_scale, d.swa_dtype, d.S, d.W = _p(swa), _p(layer.get("swa_scale")), \
+        dtype_code(swa, layer.get("swa_scale")), swa.shape[1], int(layer["W"])
     d.sink, d.sm_scale = _p(layer["sink"]), float(layer.get("sm_scale", 0.0))
     d.rope_dims, d.rope_base = int(layer["rope_dims"]), float(layer["rope_base"])
     d.q_pos = _p(layer["q_pos"])

@@ -168,7 +168,7 @@ struct __align__(16) AttnShared {
     // tile buffers: P.V on tile t, S^T on t+1, copies of t+2 (and, for
     // bf16, t+3) in flight
     static constexpr int kNB = (KVDT == DT_BF16) ? 4 : 3;
-    static constexpr int kScaled = (KVDT == DT_E4M3) ? kMaxEnt : 4;
+    static constexpr int kScaled = (KVDT != DT_BF16) ? kMaxEnt : 4;
     // bf16 keeps the compacted id list in the last tile buffer: it is only
     // live while an item is set up, when no copy is in flight
     static constexpr int kListOwn = (KVDT == DT_BF16) ? 4 : kMaxKList;
@@ -246,7 +246,9 @@ __device__ __forceinline__ DecItem decode_item(int i) {
 template <int KVDT, int NHG>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     __shared__ AttnShared<KVDT> sh;
-    constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;
+    constexpr int kRowBytes = (KVDT == DT_BF16) ? kD * 2 : kD;  // window rows (e4m3 when records are fp4)
+    // record rows: fp4 holds D/2 code bytes then D/16 E4M3 group scales
+    constexpr int kGRowBytes = (KVDT == DT_FP4) ? kD / 2 + kD / 16 : kRowBytes;
     // NHG = 64: wave w owns heads 16w .. 16w+15 over all 512 channels.
     // NHG = 16 (decode): the workgroup owns one group of 16 heads; every
     // wave computes the same logits and softmax for them and owns channels
@@ -488,16 +490,16 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             if (ge < nsel) {
                 const size_t r = static_cast<size_t>(b) * p.N + (p.dense_m ? ge : sh.list()[ge]);
                 if constexpr (KVDT == DT_E4M3) sc = p.kv_scale[r];
-                rp = p.kv + r * kRowBytes;
+                rp = p.kv + r * kGRowBytes;
             } else {
                 int slot = slot0 + (ge - nsel);  // < 2S since the window has at most S rows
                 if (slot >= p.S) slot -= p.S;
                 const size_t r = static_cast<size_t>(b) * p.S + slot;
-                if constexpr (KVDT == DT_E4M3) sc = p.swa_scale[r];
+                if constexpr (KVDT != DT_BF16) sc = p.swa_scale[r];
                 rp = p.swa + r * kRowBytes;
             }
             sh.eptr[e] = reinterpret_cast<uint64_t>(rp);
-            if constexpr (KVDT == DT_E4M3) {
+            if constexpr (KVDT != DT_BF16) {
                 sh.ezf[e] = cz * sc;
                 sh.epf[e] = sc;
             }
@@ -506,9 +508,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 
         // Tile staging: wave w fills rows 8w .. 8w+7 of the tile.  bf16 rows
         // go straight from global memory into LDS; e4m3 rows are converted to
-        // bf16 in registers on the way (staged one tile ahead).
+        // bf16 in registers on the way (staged one tile ahead); so are fp4
+        // record rows (lane l: the code dword of channels 8l .. 8l+7 and the
+        // E4M3 scale of their group), whose window rows are e4m3.  Entry e of
+        // the item is a record while e < ng (padding repeats the last entry).
         typedef typename std::conditional<KVDT == DT_BF16, u32x4, u32x2>::type Raw;
         Raw stg[kRowsPerWave];
+        const int ng = max(0, min(nsel - j0, nvalid));
+        auto rec4 = [&](int e) { return KVDT == DT_FP4 && min(e, nvalid - 1) < ng; };
         auto issue = [&](int it, int k) {
             const u32x4* ep = reinterpret_cast<const u32x4*>(&sh.eptr[it * kTile + kRowsPerWave * wave]);
             if constexpr (KVDT == DT_BF16) {
@@ -531,18 +538,33 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     // against the LDS wait counter, so every LDS wait would
                     // wait for these staging loads as well
                     typedef const __attribute__((address_space(1))) Raw GRaw;
-                    stg[i] = *(GRaw*)(uniform_ptr(pa[0], pa[1]) + 8 * lane);
-                    stg[i + 1] = *(GRaw*)(uniform_ptr(pa[2], pa[3]) + 8 * lane);
+                    typedef const __attribute__((address_space(1))) uint32_t G32;
+                    typedef const __attribute__((address_space(1))) uint8_t G8;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const uint8_t* rp = uniform_ptr(pa[2 * h2], pa[2 * h2 + 1]);
+                        if (rec4(it * kTile + kRowsPerWave * wave + i + h2)) {  // wave-uniform
+                            stg[i + h2][0] = *(G32*)(rp + 4 * lane);
+                            stg[i + h2][1] = *(G8*)(rp + kD / 2 + (lane >> 1));
+                        } else {
+                            stg[i + h2] = *(GRaw*)(rp + 8 * lane);
+                        }
+                    }
                 }
             }
         };
-        auto land = [&](int k) {  // e4m3 only: staged registers -> LDS
-            if constexpr (KVDT == DT_E4M3) {
+        auto land = [&](int it, int k) {  // e4m3 and fp4: staged registers -> LDS
+            if constexpr (KVDT != DT_BF16) {
                 uint8_t* xb = sh.xb[k];
 #pragma unroll
-                for (int i = 0; i < kRowsPerWave; ++i)
-                    *reinterpret_cast<u32x4*>(xb + (kRowsPerWave * wave + i) * kXPitch + 16 * lane) =
-                        e4m3x8_to_bf16x8(stg[i]);
+                for (int i = 0; i < kRowsPerWave; ++i) {
+                    u32x4 v;
+                    if (rec4(it * kTile + kRowsPerWave * wave + i))
+                        v = fp4x8_to_bf16x8(stg[i][0], e4m3_to_f32(static_cast<uint8_t>(stg[i][1])));
+                    else
+                        v = e4m3x8_to_bf16x8(stg[i]);
+                    *reinterpret_cast<u32x4*>(xb + (kRowsPerWave * wave + i) * kXPitch + 16 * lane) = v;
+                }
             }
         };
 
@@ -595,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 // later copies go out from inside the MFMA stream (below)
                 if (it == 0 && it + 2 < ntile) issue(it + 2, (it + 2) % NB);
             } else {
-                land(buf);
+                land(it, buf);
                 if (it == 0 && nxt < n_items) fetch(nxt, nx);
                 if (it + 1 < ntile) issue(it + 1, (it + 1) % NB);
                 lds_sync();
@@ -644,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         auto qk_end = [&](int it, Qk& q, float m, float (&d)[8]) -> bool {
             const f32x4 s0 = q.s[0] + q.s[2];
             const f32x4 s1 = q.s[1] + q.s[3];
-            if constexpr (KVDT == DT_E4M3) {
+            if constexpr (KVDT != DT_BF16) {  // per-entry scales (fp4 records: 1)
                 const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 4 * g]);
                 const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.ezf[it * kTile + 16 + 4 * g]);
 #pragma unroll
@@ -692,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             }
             if (j == 4) {
                 s.psum = ((s.pr[0] + s.pr[1]) + (s.pr[2] + s.pr[3])) + ((s.pr[4] + s.pr[5]) + (s.pr[6] + s.pr[7]));
-                if constexpr (KVDT == DT_E4M3) {
+                if constexpr (KVDT != DT_BF16) {
                     const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 4 * g]);
                     const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sh.epf[it * kTile + 16 + 4 * g]);
 #pragma unroll
@@ -1149,7 +1171,9 @@ bool sparse_attn_mfma_ok(const AttnArgs& a) {
     const int klist = a.dense_m ? a.N : a.K;  // longest list of records
     return a.H == kH && a.D == kD && a.q_dtype == DT_BF16 && (a.dense_m ? 1 : a.K <= kMaxKList) &&
            a.W <= kMaxWin && static_cast<long long>(klist) + a.W <= static_cast<long long>(kMaxSplits) * kMaxEnt &&
-           (a.kv_dtype == DT_BF16 || a.kv_dtype == DT_E4M3) && a.swa_dtype == a.kv_dtype && a.rope_dims <= kD;
+           (((a.kv_dtype == DT_BF16 || a.kv_dtype == DT_E4M3) && a.swa_dtype == a.kv_dtype) ||
+            (a.kv_dtype == DT_FP4 && a.swa_dtype == DT_E4M3)) &&
+           a.rope_dims <= kD;
 }
 
 size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W) {
@@ -1216,13 +1240,17 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         if (dec) {
             if (a.kv_dtype == DT_BF16)
                 hipLaunchKernelGGL((attn_mfma_kernel<DT_BF16, 16>), grid, dim3(kThreads), 0, st, p);
-            else
+            else if (a.kv_dtype == DT_E4M3)
                 hipLaunchKernelGGL((attn_mfma_kernel<DT_E4M3, 16>), grid, dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_FP4, 16>), grid, dim3(kThreads), 0, st, p);
         } else {
             if (a.kv_dtype == DT_BF16)
                 hipLaunchKernelGGL((attn_mfma_kernel<DT_BF16, 64>), grid, dim3(kThreads), 0, st, p);
-            else
+            else if (a.kv_dtype == DT_E4M3)
                 hipLaunchKernelGGL((attn_mfma_kernel<DT_E4M3, 64>), grid, dim3(kThreads), 0, st, p);
+            else
+                hipLaunchKernelGGL((attn_mfma_kernel<DT_FP4, 64>), grid, dim3(kThreads), 0, st, p);
         }
         int e = static_cast<int>(hipGetLastError());
         if (e || p.nsplit == 1) return e;

@@ -7,7 +7,7 @@
 namespace csa2 {
 
 // Storage dtype codes (same values as the C ABI's csa2_dtype).
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2, DT_FP4 = 3, DT_MXFP4 = 4 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -60,6 +60,33 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
     r[2] = e4m3x2_to_bf16x2(c[1], false);
     r[3] = e4m3x2_to_bf16x2(c[1], true);
     return r;
+}
+
+// ---------------------------------------------------------------- fp4
+// Eight E2M1 codes (one dword; element 2j in the low nibble of byte j) times
+// a scale -> eight bf16.  Exact: a level (at most 2 significant bits) times
+// an E4M3 or power-of-two scale (at most 4) fits bf16's 8.  gfx950's
+// conversion applies only the exponent of its scale operand, so the levels
+// are converted with scale 1 and the scale multiplies in float32.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    u32x4 r;
+    r[0] = cvt_bf16x2(a[0] * scale, a[1] * scale);
+    r[1] = cvt_bf16x2(b[0] * scale, b[1] * scale);
+    r[2] = cvt_bf16x2(c[0] * scale, c[1] * scale);
+    r[3] = cvt_bf16x2(d[0] * scale, d[1] * scale);
+    return r;
+}
+
+// E8M0 block scale (OCP microscaling) -> float: 2^(code - 127); 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+    code &= 0xFFu;
+    if (code == 0xFFu) return __uint_as_float(0x7FC00000u);
+    return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint8_t code) {

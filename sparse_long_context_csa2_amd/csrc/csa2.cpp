@@ -35,7 +35,7 @@ int hip_fail(int err, const char* what) {
     return fail(CSA2_EHIP, "%s: HIP error %d", what, err);
 }
 
-bool dtype_ok(int dt) { return dt == CSA2_F32 || dt == CSA2_BF16 || dt == CSA2_E4M3; }
+bool dtype_ok(int dt) { return dt >= CSA2_F32 && dt <= CSA2_MXFP4; }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -55,10 +55,13 @@ int check_align(const char* who, std::initializer_list<const void*> ptrs, const 
     return CSA2_OK;
 }
 
+// e4m3 needs its per-row scales and MXFP4 its E8M0 block scales; FP4 rows
+// carry their scales inline, and f32/bf16 have none.
 int check_scale(const char* name, int dt, const void* scale) {
     if (!dtype_ok(dt)) return fail(CSA2_EINVAL, "%s: unknown dtype %d", name, dt);
-    if (dt == CSA2_E4M3 && !scale) return fail(CSA2_EINVAL, "%s: e4m3 storage needs a per-row scale", name);
-    if (dt != CSA2_E4M3 && scale) return fail(CSA2_EINVAL, "%s: scale given for a non-quantized tensor", name);
+    const bool needs = dt == CSA2_E4M3 || dt == CSA2_MXFP4;
+    if (needs && !scale) return fail(CSA2_EINVAL, "%s: dtype %d needs its scale array", name, dt);
+    if (!needs && scale) return fail(CSA2_EINVAL, "%s: scale array given for dtype %d, which has none", name, dt);
     return CSA2_OK;
 }
 
@@ -70,14 +73,22 @@ int validate_index(const csa2::IndexArgs& a) {
                     a.Tq, a.N, a.Hi, a.Di, a.m);
     if (!a.q_idx || !a.w || !a.k_idx || !a.q_pos || !a.scores)
         return fail(CSA2_EINVAL, "index_scores: null required pointer");
-    if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
+    if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16 && a.q_dtype != CSA2_MXFP4)
         return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
-                    "index_scores: queries must be f32 or bf16");
-    int e = check_align("index_scores", {a.q_idx, a.w, a.k_idx, a.k_scale, a.q_pos, a.n_rec, a.pool, a.scores},
-                        nullptr);
+                    "index_scores: queries must be f32, bf16 or mxfp4");
+    int e = check_align("index_scores",
+                        {a.q_idx, a.q_scale, a.w, a.k_idx, a.k_scale, a.q_pos, a.n_rec, a.pool, a.scores}, nullptr);
+    if (e) return e;
+    e = check_scale("index_scores queries", a.q_dtype, a.q_scale);
     if (e) return e;
     e = check_scale("index_scores keys", a.k_dtype, a.k_scale);
     if (e) return e;
+    if (a.k_dtype == CSA2_FP4)
+        return fail(CSA2_EUNSUPPORTED, "index_scores: FP4 main-KV rows are not an indexer key format (use mxfp4)");
+    if (a.q_dtype == CSA2_MXFP4 && a.k_dtype != CSA2_MXFP4)
+        return fail(CSA2_EUNSUPPORTED, "index_scores: mxfp4 queries need mxfp4 keys");
+    if ((a.q_dtype == CSA2_MXFP4 || a.k_dtype == CSA2_MXFP4) && !csa2::index_scores_mfma_ok(a))
+        return fail(CSA2_EUNSUPPORTED, "index_scores: mxfp4 needs Hi=32, Di=128 (got Hi=%d Di=%d)", a.Hi, a.Di);
     if (a.pool) {
         if (a.P < 1 || a.blk < 1) return fail(CSA2_EINVAL, "index_scores: pool needs P >= 1 and blk >= 1");
         if (static_cast<long long>(a.P) * a.blk > (1LL << 30))
@@ -113,6 +124,10 @@ int validate_attn(const csa2::AttnArgs& a) {
     if (e) return e;
     e = check_scale("sparse_attn swa", a.swa_dtype, a.swa_scale);
     if (e) return e;
+    if (a.kv_dtype == CSA2_MXFP4 || a.swa_dtype == CSA2_MXFP4 || a.swa_dtype == CSA2_FP4)
+        return fail(CSA2_EUNSUPPORTED, "sparse_attn: mxfp4 rows, and fp4 window rows, are not attention formats");
+    if (a.kv_dtype == CSA2_FP4 && (a.swa_dtype != CSA2_E4M3 || !csa2::sparse_attn_mfma_ok(a)))
+        return fail(CSA2_EUNSUPPORTED, "sparse_attn: fp4 records need e4m3 window rows and H=64, D=512");
     if (a.rope_dims < 0 || a.rope_dims > a.D || (a.rope_dims & 1))
         return fail(CSA2_EINVAL, "sparse_attn: rope_dims=%d must be even and <= D", a.rope_dims);
     if (!(a.rope_base > 0.f)) return fail(CSA2_EINVAL, "sparse_attn: rope_base must be > 0");
@@ -131,14 +146,14 @@ int validate_attn(const csa2::AttnArgs& a) {
 extern "C" {
 
 int csa2_index_scores(int B, int Tq, int N, int Hi, int Di, int m, const void* q_idx, int q_dtype,
-                      const float* w, const void* k_idx, const float* k_scale, int k_dtype,
+                      const void* q_scale, const float* w, const void* k_idx, const void* k_scale, int k_dtype,
                       const int64_t* q_pos, const int32_t* n_rec, const int32_t* pool, int P, int blk,
                       float* scores, void* ws, size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
     csa2::IndexArgs a;
     a.B = B; a.Tq = Tq; a.N = N; a.Hi = Hi; a.Di = Di; a.m = m;
-    a.q_idx = q_idx; a.q_dtype = q_dtype; a.w = w; a.k_idx = k_idx; a.k_scale = k_scale;
+    a.q_idx = q_idx; a.q_dtype = q_dtype; a.q_scale = q_scale; a.w = w; a.k_idx = k_idx; a.k_scale = k_scale;
     a.k_dtype = k_dtype; a.q_pos = q_pos; a.n_rec = n_rec; a.pool = pool; a.P = P; a.blk = blk;
     a.scores = scores;
     a.ncols = pool ? P * blk : N;
@@ -348,7 +363,8 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     float* scores = reinterpret_cast<float*>(static_cast<uint8_t*>(d->ws) + pl.off_scores);
     if (scoring) {
         ia.B = d->B; ia.Tq = d->Tq; ia.N = d->N; ia.Hi = d->Hi; ia.Di = d->Di; ia.m = d->m;
-        ia.q_idx = d->q_idx; ia.q_dtype = d->q_idx_dtype; ia.w = d->w; ia.k_idx = d->k_idx;
+        ia.q_idx = d->q_idx; ia.q_dtype = d->q_idx_dtype; ia.q_scale = d->q_idx_scale; ia.w = d->w;
+        ia.k_idx = d->k_idx;
         ia.k_scale = d->k_scale; ia.k_dtype = d->k_dtype; ia.q_pos = d->q_pos; ia.n_rec = d->n_rec;
         ia.pool = pooled ? d->pool_inout : nullptr;
         ia.P = pooled ? d->P : 0;

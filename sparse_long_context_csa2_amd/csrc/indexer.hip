@@ -34,10 +34,11 @@ constexpr int kDi = 128;
 
 struct IdxP {
     int B, Tq, N, m, ncols, P, blk;
-    const uint16_t* q;   // bf16 [B][Tq][32][128]
+    const uint16_t* q;   // bf16 [B][Tq][32][128], or MXFP4 codes [B][Tq][32][64]
+    const uint8_t* qsc;  // MXFP4 queries: E8M0 scales [B][Tq][32][4], else null
     const float* w;      // [B][Tq][32]
-    const uint8_t* k;    // key rows, bf16 or e4m3
-    const float* ks;     // e4m3 row scales [B][N]
+    const uint8_t* k;    // key rows: bf16, e4m3, or MXFP4 codes (64 bytes)
+    const void* ks;      // e4m3 row scales float [B][N]; MXFP4 E8M0 scales uint8 [B][N][4]
     const int64_t* q_pos;
     const int32_t* n_rec;
     const int32_t* pool;
@@ -60,6 +61,7 @@ __device__ __forceinline__ int visible_count(int64_t t, int m, int nrec) {
 template <int KDT>
 __device__ __forceinline__ int chunk8(int g, int ks) {
     if (KDT == DT_BF16) return g + 4 * ks;                 // one 16-byte load per k-step
+    if (KDT == DT_MXFP4) return 4 * g + ks;                // one 16-byte load (= one MX block) per row
     return 2 * (g + 4 * (ks >> 1)) + (ks & 1);             // one 16-byte load per two k-steps
 }
 
@@ -74,16 +76,24 @@ __device__ __forceinline__ u32x4 ld16_nt(const u32x4* p) { return __builtin_nont
 template <int KDT>
 __device__ __forceinline__ void load_key_raw(const uint8_t* row, int g, u32x4 (&raw)[4]) {
     const u32x4* p = reinterpret_cast<const u32x4*>(row);
+    if constexpr (KDT == DT_MXFP4) {  // dims 32g .. 32g+31: one MX block, 16 bytes
+        raw[0] = ld16_nt(p + g);
+        return;
+    }
     constexpr int kLoads = (KDT == DT_BF16) ? 4 : 2;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) raw[i] = ld16_nt(p + g + 4 * i);
 }
 
+// `scale`: the lane's MX block scale (MXFP4 keys; unused otherwise).
 template <int KDT>
-__device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], bf16x8 (&bk)[4]) {
+__device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], float scale, bf16x8 (&bk)[4]) {
     if constexpr (KDT == DT_BF16) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) bk[ks] = as_bf16x8(raw[ks]);
+    } else if constexpr (KDT == DT_MXFP4) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bk[ks] = as_bf16x8(fp4x8_to_bf16x8(raw[0][ks], scale));
     } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : (KDT == DT_MXFP4 ? kDi / 2 : kDi);
 
     const int b = blockIdx.y / p.Tq;
     const int tok = blockIdx.y % p.Tq;
@@ -121,10 +131,18 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     const int vis = visible_count(p.q_pos[row], p.m, nrec);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
+        if (KDT == DT_MXFP4 && p.qsc) {  // MXFP4 queries: the head's block g and its scale
+            const size_t hrow = row * kHi + 16 * mt + n;
+            const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + hrow * (kDi / 2) + 16 * g);
+            const float sc = e8m0_to_f32(p.qsc[hrow * (kDi / 32) + g]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qa[mt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * chunk8<KDT>(g, ks)));
+            for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(fp4x8_to_bf16x8(c[ks], sc));
+        } else {
+            const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[mt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * chunk8<KDT>(g, ks)));
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) wv[mt][v] = p.w[row * kHi + 16 * mt + 4 * g + v];
     }
@@ -140,6 +158,7 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
         bool any;
         u32x4 raw[4];
         float kscale;
+        uint32_t kblk;  // MXFP4: the row's four E8M0 block scales
     };
     auto fetch = [&](int ti, Tile& T) {
         const int c = ti * 16 + n;
@@ -155,16 +174,20 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
         const bool ld = T.rec >= 0 && T.rec < vis;
         T.any = __any(ld);
         T.kscale = 1.f;
+        T.kblk = 0;
         if (T.any) {
             load_key_raw<KDT>(kbase + static_cast<size_t>(ld ? T.rec : 0) * kRowBytes, g, T.raw);
-            if (KDT == DT_E4M3) T.kscale = ld ? p.ks[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+            if (KDT == DT_E4M3)
+                T.kscale = ld ? static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+            if (KDT == DT_MXFP4)
+                T.kblk = static_cast<const uint32_t*>(p.ks)[static_cast<size_t>(b) * p.N + (ld ? T.rec : 0)];
         }
     };
     auto score = [&](int ti, const Tile& T) {
         float val = -__builtin_huge_valf();
         if (T.any) {
             bf16x8 bk[4];
-            key_operands<KDT>(T.raw, bk);
+            key_operands<KDT>(T.raw, KDT == DT_MXFP4 ? e8m0_to_f32(T.kblk >> (8 * g)) : 1.f, bk);
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     // tiles wave, wave + 4, ... of the range, through a ring of kRing
     // tiles: kRing - 1 in flight ahead of the one being multiplied (e4m3
     // tiles carry half the bytes, so more of them)
-    constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;
+    constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;  // MXFP4 tiles: a quarter of the bytes
     Tile tt[kRing];
     const int ti0 = t_begin + wave;
 #pragma unroll
@@ -343,7 +366,8 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void idx_prefill_kernel(IdxP p, in
             const int r = tid >> 3;
             const int rec = min(k * kPTile + r, p.N - 1);
             eraw[par] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(rec) * kRowBytes + 16 * (tid & 7));
-            if (tid < kPTile) esc[par] = p.ks[static_cast<size_t>(b) * p.N + min(k * kPTile + tid, p.N - 1)];
+            if (tid < kPTile)
+                esc[par] = static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + min(k * kPTile + tid, p.N - 1)];
         };
         auto eland = [&](int k, int par) {
             const int r = tid >> 3;
@@ -551,6 +575,7 @@ int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     IdxP p;
     p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
     p.q = static_cast<const uint16_t*>(a.q_idx);
+    p.qsc = static_cast<const uint8_t*>(a.q_scale);
     p.w = a.w;
     p.k = static_cast<const uint8_t*>(a.k_idx);
     p.ks = a.k_scale;
@@ -568,8 +593,9 @@ int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
 }  // namespace
 
 bool index_scores_mfma_ok(const IndexArgs& a) {
-    return a.Hi == kHi && a.Di == kDi && a.q_dtype == DT_BF16 &&
-           (a.k_dtype == DT_BF16 || a.k_dtype == DT_E4M3);
+    if (a.Hi != kHi || a.Di != kDi) return false;
+    if (a.k_dtype == DT_MXFP4) return a.q_dtype == DT_BF16 || a.q_dtype == DT_MXFP4;
+    return a.q_dtype == DT_BF16 && (a.k_dtype == DT_BF16 || a.k_dtype == DT_E4M3);
 }
 
 int launch_index_scores(const IndexArgs& a, void* stream) {
@@ -579,10 +605,11 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
         const int rows = a.B * a.Tq;
         // Prefill-shaped work (many tokens of one sequence, no pool): blocks of
         // 8 tokens, two blocks (a light and a heavy one) per workgroup.
-        if (!a.pool && a.Tq >= 16) {
+        if (!a.pool && a.Tq >= 16 && a.k_dtype != DT_MXFP4) {
             IdxP p;
             p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
             p.q = static_cast<const uint16_t*>(a.q_idx);
+            p.qsc = nullptr;
             p.w = a.w;
             p.k = static_cast<const uint8_t*>(a.k_idx);
             p.ks = a.k_scale;
@@ -606,13 +633,15 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
         // slower again.)
         int tpb = kDecTpbMax;
         while (tpb > 4 && static_cast<long>(rows) * ((ntiles + tpb - 1) / tpb) < 512) tpb >>= 1;
+        if (a.k_dtype == DT_MXFP4) return launch_mfma<DT_MXFP4>(a, tpb, st);
         return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16>(a, tpb, st) : launch_mfma<DT_E4M3>(a, tpb, st);
     }
     IdxG p;
     p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.Hi = a.Hi; p.Di = a.Di; p.m = a.m; p.ncols = a.ncols;
     p.P = a.P; p.blk = a.blk; p.qdt = a.q_dtype; p.kdt = a.k_dtype;
-    p.q = a.q_idx; p.w = a.w; p.k = a.k_idx; p.ks = a.k_scale; p.q_pos = a.q_pos;
+    p.q = a.q_idx; p.w = a.w; p.k = a.k_idx; p.q_pos = a.q_pos;
     p.n_rec = a.n_rec; p.pool = a.pool; p.out = a.scores;
+    p.ks = static_cast<const float*>(a.k_scale);
     dim3 grid((a.ncols + 255) / 256, a.B * a.Tq);
     const size_t lds = (static_cast<size_t>(a.Hi) * a.Di + a.Hi) * sizeof(float);
     hipLaunchKernelGGL(idx_generic_kernel, grid, dim3(256), lds, st, p);

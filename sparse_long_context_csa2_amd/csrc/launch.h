@@ -12,9 +12,10 @@ struct IndexArgs {
     int B, Tq, N, Hi, Di, m;
     const void* q_idx;
     int q_dtype;
+    const void* q_scale;  // MXFP4 queries: E8M0 scales [B][Tq][Hi][Di/32], else null
     const float* w;
     const void* k_idx;
-    const float* k_scale;
+    const void* k_scale;  // e4m3: float [B][N]; MXFP4: E8M0 bytes [B][N][Di/32]; else null
     int k_dtype;
     const int64_t* q_pos;
     const int32_t* n_rec;

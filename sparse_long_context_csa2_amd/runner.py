@@ -18,15 +18,26 @@ import torch
 from . import binding as _b
 
 
-def to_device(arr, device="cuda") -> Optional[torch.Tensor]:
+def to_device(arr, device="cuda", fmt: Optional[str] = None) -> Optional[torch.Tensor]:
     """numpy storage array -> device tensor (uint16 bf16 bits become a
-    bfloat16 view, uint8 e4m3 codes stay uint8)."""
+    bfloat16 view, uint8 e4m3 codes stay uint8).  ``fmt`` "fp4" or "mxfp4"
+    tags packed four-bit codes as torch.float4_e2m1fn_x2, "e8m0" tags MX
+    block scales as torch.float8_e8m0fnu (views of the same bytes)."""
     if arr is None:
         return None
     a = np.ascontiguousarray(arr)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(a).to(device)
+    t = torch.from_numpy(a).to(device)
+    if fmt in ("fp4", "mxfp4"):
+        return t.view(torch.float4_e2m1fn_x2)
+    if fmt == "e8m0":
+        return t.view(torch.float8_e8m0fnu)
+    return t
+
+
+def _scale_fmt(fmt: Optional[str]) -> Optional[str]:
+    return "e8m0" if fmt == "mxfp4" else None
 
 
 class DeviceGroup:
@@ -35,9 +46,11 @@ class DeviceGroup:
         self.wl = wl
         self.device = device
         sh = inputs["shared"]
+        kf, vf = sh.get("k_format"), sh.get("kv_format")
         self.shared = [dict(m=sh["m"], n_rec=to_device(sh["n_rec"], device),
-                            k_idx=to_device(sh["k_idx"], device), k_scale=to_device(sh["k_scale"], device),
-                            kv=to_device(sh["kv"], device), kv_scale=to_device(sh["kv_scale"], device))]
+                            k_idx=to_device(sh["k_idx"], device, kf),
+                            k_scale=to_device(sh["k_scale"], device, _scale_fmt(kf)),
+                            kv=to_device(sh["kv"], device, vf), kv_scale=to_device(sh["kv_scale"], device))]
         # extra copies of the shared store let a benchmark rotate caches
         for _ in range(copies - 1):
             self.shared.append({k: (v.clone() if isinstance(v, torch.Tensor) else v)
@@ -47,8 +60,11 @@ class DeviceGroup:
         for lay in inputs["layers"]:
             d = {k: lay[k] for k in ("mode", "build_pool", "K", "W", "blk", "P", "rope_dims", "rope_base",
                                      "sm_scale")}
-            for k in ("q_idx", "w", "q", "swa", "swa_scale", "sink", "q_pos"):
+            for k in ("w", "q", "swa", "swa_scale", "sink", "q_pos"):
                 d[k] = to_device(lay[k], device)
+            qf = lay.get("q_idx_format")
+            d["q_idx"] = to_device(lay["q_idx"], device, qf)
+            d["q_idx_scale"] = to_device(lay.get("q_idx_scale"), device, _scale_fmt(qf))
             d["out"] = torch.empty((B, Tq, wl.H, wl.D), dtype=torch.float32, device=device)
             self.layers.append(d)
         # index sets: Full/Reindex write their own; Reuse reads the last one

@@ -86,7 +86,10 @@ def _e4m3_decode_f32(codes: np.ndarray) -> np.ndarray:
     return np.where(c & 0x80, -v, v).astype(np.float32)
 
 
-_E2M1_LEVELS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+# midpoints between neighbouring E2M1 magnitudes (0, 0.5, 1, 1.5, 2, 3, 4,
+# 6), and whether an exact tie there rounds up: it does when the lower code
+# is odd (mantissa bit set), so that ties go to the even code
+_E2M1_MIDS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False))
 
 
 def e2m1_encode(v: np.ndarray) -> np.ndarray:
@@ -94,16 +97,11 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
     nearest of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the code
     with an even mantissa bit, saturating at 6; bit 3 is the sign."""
     v = np.asarray(v, dtype=np.float32)
-    a = np.minimum(np.abs(v), np.float32(6.0))
-    # distance to every level; argmin takes the lower code of an exact tie,
-    # which moves up one when that code is odd (its mantissa bit is set)
-    d = np.abs(a[..., None] - _E2M1_LEVELS)
-    code = np.argmin(d, axis=-1).astype(np.uint8)
-    tie = np.take_along_axis(d, code[..., None].astype(np.int64), -1)[..., 0]
-    nxt = np.minimum(code + 1, 7)
-    tie_up = (code % 2 == 1) & (np.take_along_axis(d, nxt[..., None].astype(np.int64), -1)[..., 0] == tie)
-    code = np.where(tie_up, nxt, code).astype(np.uint8)
-    return (code | (np.signbit(v).astype(np.uint8) << 3)).astype(np.uint8)
+    a = np.abs(v)
+    code = np.zeros(v.shape, dtype=np.uint8)
+    for mid, up in _E2M1_MIDS:
+        code += (a >= np.float32(mid)) if up else (a > np.float32(mid))
+    return code | (np.signbit(v).astype(np.uint8) << 3)
 
 
 def pack_fp4(codes: np.ndarray) -> np.ndarray:
@@ -113,12 +111,28 @@ def pack_fp4(codes: np.ndarray) -> np.ndarray:
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
+def _by_rows(fn, x: np.ndarray, rows: int = 8192):
+    """Applies fn to chunks of rows of x (bounded temporaries)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1, x.shape[-1])
+    if flat.shape[0] <= rows:
+        return fn(x)
+    parts = [fn(flat[i:i + rows]) for i in range(0, flat.shape[0], rows)]
+    if isinstance(parts[0], tuple):
+        return tuple(np.concatenate([p[k] for p in parts]).reshape(x.shape[:-1] + (parts[0][k].shape[-1],))
+                     for k in range(len(parts[0])))
+    return np.concatenate(parts).reshape(x.shape[:-1] + (parts[0].shape[-1],))
+
+
 def quantize_rows_fp4(x: np.ndarray) -> np.ndarray:
     """FP4 main-KV rows: every 16 channels share one E4M3 scale, the largest
     magnitude of the group / 6 rounded to nearest even (an all-zero group has
     scale 0 and codes 0); codes = E2M1(x / scale).  Row layout: the D/2 code
     bytes, then the D/16 scale bytes (288 bytes for 512 channels)."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
+    return _by_rows(_fp4_rows, x)
+
+
+def _fp4_rows(x: np.ndarray) -> np.ndarray:
     D = x.shape[-1]
     g = x.reshape(x.shape[:-1] + (D // 16, 16))
     amax = np.abs(g).max(axis=-1)
@@ -135,7 +149,10 @@ def quantize_mxfp4(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     floor(log2(max |x|)) - 2 (2 is E2M1's largest exponent), clamped to
     [-127, 127]; elements = E2M1(x / 2^e), saturating.  Returns (packed
     codes [..., n/2], scale bytes e + 127 [..., n/32])."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
+    return _by_rows(_mxfp4_rows, x)
+
+
+def _mxfp4_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     n = x.shape[-1]
     blk = x.reshape(x.shape[:-1] + (n // 32, 32))
     amax = np.abs(blk).max(axis=-1)
@@ -238,6 +255,13 @@ CONFIGS: Dict[str, Workload] = {
         rope_dims=64, W=128, K=0, decode_pos=1048576, modes=("hca",),
         description="heavily compressed attention decode: B=8, context 1,048,576 at m'=128 "
                     "(N=8,192 records, all visible), no indexer, SWA 128 plus sink, bf16"),
+    "C7": Workload(
+        name="C7-long-decode-fp4", seed=6, B=8, Tq=1, N=262144, m=4, Hi=32, Di=128,
+        H=64, D=512, rope_dims=64, W=128, K=512, decode_pos=1048576,
+        q_idx_dtype="mxfp4", k_dtype="mxfp4", kv_dtype="fp4", swa_dtype="e4m3",
+        description="long-context decode in the V4.1 cache formats: B=8, context 1,048,576 "
+                    "(N=262,144); main KV FP4 (E2M1 + E4M3 scale per 16 channels, 288 B rows), "
+                    "indexer queries and keys MXFP4, window FP8"),
 }
 
 _NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "fp4": np.uint8, "mxfp4": np.uint8}

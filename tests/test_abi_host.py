@@ -54,7 +54,7 @@ def test_index_scores_validation(L):
         a = dict(ok)
         a.update(kw)
         return f(a["B"], a["Tq"], a["N"], a["Hi"], a["Di"], a["m"], kw.get("q", FAKE), kw.get("qdt", 0),
-                 kw.get("w", FAKE), kw.get("k", FAKE), kw.get("ks", None), kw.get("kdt", 0),
+                 kw.get("qs", None), kw.get("w", FAKE), kw.get("k", FAKE), kw.get("ks", None), kw.get("kdt", 0),
                  kw.get("pos", FAKE), None, kw.get("pool", None), kw.get("P", 0), kw.get("blk", 0),
                  kw.get("out", FAKE), None, 0, None)
 
@@ -65,7 +65,13 @@ def test_index_scores_validation(L):
     assert call(kdt=9) == B.CSA2_EINVAL
     assert call(kdt=2) == B.CSA2_EINVAL              # e4m3 without scale
     assert call(ks=FAKE) == B.CSA2_EINVAL            # scale for f32 keys
-    assert call(qdt=2) == B.CSA2_EUNSUPPORTED        # e4m3 queries
+    assert call(qdt=2, qs=FAKE) == B.CSA2_EUNSUPPORTED  # e4m3 queries
+    assert call(qdt=4) == B.CSA2_EINVAL              # mxfp4 queries without their scales
+    assert call(qdt=4, qs=FAKE, kdt=1) == B.CSA2_EUNSUPPORTED  # mxfp4 queries need mxfp4 keys
+    assert call(kdt=4) == B.CSA2_EINVAL              # mxfp4 keys without their scales
+    assert call(kdt=4, ks=FAKE) == B.CSA2_EUNSUPPORTED  # mxfp4 needs the 32 x 128 kernel
+    assert call(kdt=3) == B.CSA2_EUNSUPPORTED        # fp4 main-KV rows are no key format
+    assert call(kdt=3, ks=FAKE) == B.CSA2_EINVAL     # fp4 rows carry their scales inline
     assert call(Hi=65) == B.CSA2_EUNSUPPORTED
     assert call(pool=FAKE, P=0, blk=4) == B.CSA2_EINVAL
     assert call(P=2, blk=4) == B.CSA2_EINVAL         # P/blk without a pool
@@ -108,6 +114,10 @@ def test_sparse_attn_validation(L):
     assert _attn(L, kvdt=2) == B.CSA2_EINVAL           # e4m3 without scale
     assert _attn(L, kvs=FAKE) == B.CSA2_EINVAL         # scale for bf16
     assert _attn(L, qdt=2) == B.CSA2_EUNSUPPORTED
+    assert _attn(L, kvdt=3) == B.CSA2_EUNSUPPORTED    # fp4 records need e4m3 window rows
+    assert _attn(L, kvdt=3, kvs=FAKE, swadt=2, swas=FAKE) == B.CSA2_EINVAL  # fp4 scales are inline
+    assert _attn(L, kvdt=4, kvs=FAKE) == B.CSA2_EUNSUPPORTED  # mxfp4 is no attention row format
+    assert _attn(L, kvdt=3, swadt=2, swas=FAKE, H=2, D=16, qdt=0) == B.CSA2_EUNSUPPORTED  # 64 x 512 only
     assert _attn(L, H=3, D=2048, qdt=0, kvdt=0, swadt=0) == B.CSA2_EUNSUPPORTED
     # decode-shaped calls need split partials: an empty workspace is refused
     need = L.csa2_sparse_attn_workspace_bytes(1, 1, 64, 512, 512, 128)
@@ -148,12 +158,12 @@ def test_misaligned_pointers_are_refused(L):
     """Every tensor pointer must be 16-byte aligned and every workspace
     256-byte aligned; a misaligned one is refused before any launch."""
     f = L.csa2_index_scores
-    assert f(1, 1, 8, 4, 16, 1, FAKE + 8, 0, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE, None, 0,
+    assert f(1, 1, 8, 4, 16, 1, FAKE + 8, 0, None, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE, None, 0,
              None) == B.CSA2_EINVAL
     assert "16-byte" in L.csa2_status_str(B.CSA2_EINVAL).decode()
-    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, FAKE, FAKE, None, 0, FAKE + 4, None, None, 0, 0, FAKE, None, 0,
+    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, None, FAKE, FAKE, None, 0, FAKE + 4, None, None, 0, 0, FAKE, None, 0,
              None) == B.CSA2_EINVAL
-    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE + 2, None, 0,
+    assert f(1, 1, 8, 4, 16, 1, FAKE, 0, None, FAKE, FAKE, None, 0, FAKE, None, None, 0, 0, FAKE + 2, None, 0,
              None) == B.CSA2_EINVAL
     assert L.csa2_topk(1, 8, 2, FAKE, None, 0, 0, FAKE + 4, FAKE, 1 << 20, None) == B.CSA2_EINVAL
     assert L.csa2_topk(1, 8, 2, FAKE, None, 0, 0, FAKE, FAKE + 16, 1 << 20, None) == B.CSA2_EINVAL

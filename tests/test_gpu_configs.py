@@ -27,6 +27,7 @@ SAMPLES = {
     "C4": [(0, 0), (9, 0), (15, 0)],
     "C5": [(0, 0), (7, 0)],
     "C6": [(0, 0), (3, 0), (7, 0)],
+    "C7": [(0, 0), (7, 0)],
 }
 # rows whose whole score row is compared (a full C2 row costs the oracle
 # 1024 columns; a C5 row 262,144)
@@ -37,10 +38,11 @@ SCORE_ROWS = {
     "C4": [(0, 0), (9, 0), (15, 0)],
     "C5": [(0, 0), (7, 0)],
     "C6": [],
+    "C7": [(0, 0), (7, 0)],
 }
 # unit-scale variants: rows and queries ~ N(0, 1), the scale the contract's
 # attention bounds are stated for
-UNIT = {"C3u": "C3", "C5u": "C5"}
+UNIT = {"C3u": "C3", "C5u": "C5", "C7u": "C7"}
 
 
 def _workload(cfg):
@@ -73,12 +75,12 @@ def _device_scores(grp, li, pooled):
     sh, lay = grp.shared[0], grp.layers[li]
     out = Bd.csa2_index_scores(lay["q_idx"], lay["w"], sh["k_idx"], sh["k_scale"], lay["q_pos"], sh["m"],
                                n_rec=sh["n_rec"], pool=grp.pool if pooled else None,
-                               blk=lay["blk"] if pooled else 0)
+                               blk=lay["blk"] if pooled else 0, q_scale=lay["q_idx_scale"])
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C6", "C3u", "C5u"])
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C3u", "C5u", "C7u"])
 def test_config_full_size(cfg):
     print(f"[case] full-size {cfg}", flush=True)
     wl, base = _workload(cfg)

@@ -549,6 +549,111 @@ def test_dense_attn_generic_and_layer_mode():
                             f"layer b={b}")
 
 
+# ------------------------------------------------------------------ FP4 / MXFP4
+
+def _devf(inp, which, key):
+    """Device tensor of a storage array with its format tag."""
+    src = inp["shared"] if which == "shared" else inp["layers"][0]
+    fmt = {"k_idx": src.get("k_format"), "kv": src.get("kv_format"), "q_idx": src.get("q_idx_format")}.get(key)
+    if key == "k_scale":
+        fmt = "e8m0" if src.get("k_format") == "mxfp4" else None
+    if key == "q_idx_scale":
+        fmt = "e8m0" if src.get("q_idx_format") == "mxfp4" else None
+    return R.to_device(src.get(key), fmt=fmt)
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("Tq,N,pooled", [(2, 1000, False), (20, 333, False), (1, 2048, True)])
+def test_index_scores_mxfp4(qdt, Tq, N, pooled):
+    """MXFP4 indexer keys (E2M1 with an E8M0 scale per 32 dims), with bf16
+    or MXFP4 queries: decode rows with ragged record counts, a prefill-
+    shaped call (20 tokens, growing visibility) and pool mode."""
+    _case(f"index_scores mxfp4 keys, {qdt} queries, Tq={Tq} N={N} pooled={pooled}")
+    kw = dict(n_rec=(N, N // 2 + 1, 5)) if not pooled else {}
+    wl = _small(Tq=Tq, N=N, k_dtype="mxfp4", q_idx_dtype=qdt, decode_pos=None if Tq == 20 else 4 * N + 7, **kw)
+    inp = WL.make_inputs(wl)
+    if Tq == 20:
+        inp["layers"][0]["q_pos"][1] += 900
+    sh, lay = inp["shared"], inp["layers"][0]
+    pool, blk = None, 0
+    if pooled:
+        blk, P = 64, 6
+        rng = np.random.default_rng(9)
+        pool = rng.integers(0, N // blk, size=(wl.B, Tq, P)).astype(np.int32)
+        pool[:, :, -1] = -1
+    out = Bd.csa2_index_scores(_devf(inp, "layer", "q_idx"), _dev(lay["w"]), _devf(inp, "shared", "k_idx"),
+                               _devf(inp, "shared", "k_scale"), _dev(lay["q_pos"]), sh["m"], n_rec=_dev(sh["n_rec"]),
+                               pool=None if pool is None else _dev(pool), blk=blk,
+                               q_scale=_devf(inp, "layer", "q_idx_scale"))
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    for b in range(wl.B):
+        for ti in range(Tq):
+            if pooled:
+                o = O.pool_row_scores(sh, lay, b, ti, pool[b, ti], blk)
+            else:
+                o = O.full_row_scores(sh, lay, b, ti)
+            PR.check_scores(g[b, ti], o, f"b={b} t={ti}")
+
+
+@pytest.mark.parametrize("Tq,unit", [(3, False), (3, True), (150, False)])
+def test_sparse_attn_fp4_records(Tq, unit):
+    """FP4 main-KV records (288-byte rows: E2M1 codes and an E4M3 scale per
+    16 channels) gathered with FP8 window rows: decode (3 queries per
+    sequence, unit-scale rows too) and prefill layouts, with -1 and
+    out-of-range ids, a window-only query and window truncation at 0."""
+    _case(f"sparse_attn fp4 records + e4m3 window, Tq={Tq} unit={unit}")
+    kw = dict(q_std=1.0, kv_std=1.0) if unit else {}
+    wl = _small(B=2, Tq=Tq, N=300, K=48, W=24, swa_slots=32, decode_pos=5000, kv_dtype="fp4", swa_dtype="e4m3", **kw)
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    assert sh["kv"].shape[-1] == 288
+    rng = np.random.default_rng(Tq + 1)
+    idx = rng.integers(0, 300, size=(2, Tq, 48)).astype(np.int32)
+    idx[:, :, 40:] = -1
+    idx[0, 0, 5] = 300 + 7
+    idx[1, 0, :] = -1
+    lay["q_pos"][1, 0] = 3
+    out = Bd.csa2_sparse_attn(_dev(lay["q"]), _devf(inp, "shared", "kv"), None, _dev(idx), _dev(lay["swa"]),
+                              _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b in range(2):
+        for ti in (list(range(Tq)) if Tq < 10 else [0, 1, 77, Tq - 1]):
+            err, tol = PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], "fp4", f"b={b} t={ti}")
+            if unit:
+                assert tol > 0.9 * PR.ATTN_TOL["fp4"]
+
+
+def test_fp4_dense_and_layer_group():
+    """HCA over FP4 records, and a Full+pool / Reindex / Reuse group in the
+    V4.1 formats (MXFP4 indexer, FP4 records, FP8 window) through
+    csa2_layer."""
+    _case("dense_attn fp4; layer group in fp4/mxfp4/e4m3")
+    wl = _small(B=2, Tq=1, N=2000, K=0, W=64, decode_pos=4 * 1700, kv_dtype="fp4", swa_dtype="e4m3",
+                modes=("hca",), n_rec=(2000, 900))
+    inp = WL.make_inputs(wl)
+    sh, lay = inp["shared"], inp["layers"][0]
+    out = Bd.csa2_dense_attn(_dev(lay["q"]), _devf(inp, "shared", "kv"), None, _dev(lay["swa"]),
+                             _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims,
+                             sh["m"], n_rec=_dev(sh["n_rec"]))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(2):
+        PR.check_attn_query(out[b, 0], sh, lay, b, 0, _visible(inp, b, 0), "fp4", f"dense b={b}")
+    wl = _small(B=3, Tq=1, N=4096, blk=64, P=8, K=128, W=32, decode_pos=16400, q_idx_dtype="mxfp4",
+                k_dtype="mxfp4", kv_dtype="fp4", swa_dtype="e4m3",
+                modes=("full+pool", "reindex", "reindex", "reuse", "reuse"), n_rec=(4096, 3000, 4096))
+    inp = WL.make_inputs(wl)
+    for lay in inp["layers"][1:]:
+        lay["q_pos"] = inp["layers"][0]["q_pos"]
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    _check_group(inp, grp, [(b, 0) for b in range(3)])
+
+
 # ------------------------------------------------------------------ layers
 
 def _check_group(inp, grp, rows):
