@@ -111,7 +111,23 @@ __device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], float scale,
 // column runs at the end: no store sits between a prefetch and its wait.
 constexpr int kDecTpbMax = 128;  // tiles per workgroup, at most
 
-template <int KDT>
+// QMX (MXFP4 queries and keys): the scores come from gfx950's block-scaled
+// MFMA, v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1: one
+// instruction per 16 heads x 16 records covers all 128 dims, products are
+// exact and each lane's E8M0 scale applies to its 32 dims (lane l holds row
+// l % 16, dims 32 (l / 16) .. +31, element e in nibble e, low nibble first),
+// which is the stored MX block of that lane group; nothing is converted.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_mx4(const u32x4& a, int sa, const u32x4& b, int sb, f32x4 c) {
+    const i32x8 A = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
+                     0, 0, 0, 0};
+    const i32x8 Bv = {static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3]),
+                      0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+template <int KDT, bool QMX = false>
 __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     __shared__ float osc[kDecTpbMax * 16];
     const int lane = threadIdx.x & 63;
@@ -127,16 +143,16 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
 
     // A operands (the token's queries), head weights and visibility
     bf16x8 qa[2][4];
+    u32x4 qmx[2];  // QMX: the lane's 32 query codes (one MX block) per m-tile
+    int qmxs[2];   // QMX: their E8M0 scale
     float wv[2][4];
     const int vis = visible_count(p.q_pos[row], p.m, nrec);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        if (KDT == DT_MXFP4 && p.qsc) {  // MXFP4 queries: the head's block g and its scale
+        if constexpr (QMX) {  // MXFP4 queries: the head's block g and its scale
             const size_t hrow = row * kHi + 16 * mt + n;
-            const u32x4 c = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + hrow * (kDi / 2) + 16 * g);
-            const float sc = e8m0_to_f32(p.qsc[hrow * (kDi / 32) + g]);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qa[mt][ks] = as_bf16x8(fp4x8_to_bf16x8(c[ks], sc));
+            qmx[mt] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + hrow * (kDi / 2) + 16 * g);
+            qmxs[mt] = p.qsc[hrow * (kDi / 32) + g];
         } else {
             const uint16_t* qh = p.q + (row * kHi + 16 * mt + n) * kDi;
 #pragma unroll
@@ -186,13 +202,19 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     auto score = [&](int ti, const Tile& T) {
         float val = -__builtin_huge_valf();
         if (T.any) {
-            bf16x8 bk[4];
-            key_operands<KDT>(T.raw, KDT == DT_MXFP4 ? e8m0_to_f32(T.kblk >> (8 * g)) : 1.f, bk);
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (QMX) {
+                const int ksc = static_cast<int>((T.kblk >> (8 * g)) & 0xFFu);
+                acc0 = mfma_mx4(qmx[0], qmxs[0], T.raw[0], ksc, acc0);
+                acc1 = mfma_mx4(qmx[1], qmxs[1], T.raw[0], ksc, acc1);
+            } else {
+                bf16x8 bk[4];
+                key_operands<KDT>(T.raw, KDT == DT_MXFP4 ? e8m0_to_f32(T.kblk >> (8 * g)) : 1.f, bk);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                acc0 = mfma16x16x32(qa[0][ks], bk[ks], acc0);
-                acc1 = mfma16x16x32(qa[1][ks], bk[ks], acc1);
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc0 = mfma16x16x32(qa[0][ks], bk[ks], acc0);
+                    acc1 = mfma16x16x32(qa[1][ks], bk[ks], acc1);
+                }
             }
             // an e4m3 row's scale is >= 0, so it leaves the ReLU and is
             // applied once to the head sum: relu(s d) w = s w relu(d)
@@ -570,7 +592,7 @@ __global__ __launch_bounds__(256) void idx_generic_kernel(IdxG p) {
     p.out[row * p.ncols + c] = res;
 }
 
-template <int KDT>
+template <int KDT, bool QMX = false>
 int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     IdxP p;
     p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = a.P; p.blk = a.blk;
@@ -586,7 +608,7 @@ int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     p.tiles_per_block = tiles_per_block;
     const int ntiles = (a.ncols + 15) / 16;
     dim3 grid((ntiles + tiles_per_block - 1) / tiles_per_block, a.B * a.Tq);
-    hipLaunchKernelGGL(idx_mfma_kernel<KDT>, grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((idx_mfma_kernel<KDT, QMX>), grid, dim3(256), 0, st, p);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -633,7 +655,8 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
         // slower again.)
         int tpb = kDecTpbMax;
         while (tpb > 4 && static_cast<long>(rows) * ((ntiles + tpb - 1) / tpb) < 512) tpb >>= 1;
-        if (a.k_dtype == DT_MXFP4) return launch_mfma<DT_MXFP4>(a, tpb, st);
+        if (a.k_dtype == DT_MXFP4)
+            return a.q_dtype == DT_MXFP4 ? launch_mfma<DT_MXFP4, true>(a, tpb, st) : launch_mfma<DT_MXFP4>(a, tpb, st);
         return a.k_dtype == DT_BF16 ? launch_mfma<DT_BF16>(a, tpb, st) : launch_mfma<DT_E4M3>(a, tpb, st);
     }
     IdxG p;
