@@ -5,9 +5,10 @@ query tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x
 512 latent with 64 rotary dims, window 128, bf16) as ``value``, and the
 three decode workloads (Full decode at 64K context, hierarchical
 Full/Reindex/Reuse decode at 256K, fp8 decode at 1M, the heavily
-compressed (HCA) decode at 1M, and the 1M decode in the V4.1 cache formats
-(FP4 main KV, MXFP4 indexer, FP8 window)) in the same run, each reported
-in its own object under ``workloads``.  ``--workload`` picks
+compressed (HCA) decode at 1M, the 1M decode in the V4.1 cache formats
+(FP4 main KV, MXFP4 indexer, FP8 window), and a multi-query decode that
+verifies 5 positions per sequence) in the same run, each reported in its
+own object under ``workloads``.  ``--workload`` picks
 another primary workload; ``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
@@ -50,9 +51,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
-    ap.add_argument("--extra", default="C3,C4,C5,C6,C7", help="further workloads measured in the same run")
+    ap.add_argument("--extra", default="C3,C4,C5,C6,C7,C8", help="further workloads measured in the same run")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")

@@ -345,6 +345,20 @@ int csa2_layer(const csa2_layer_desc* desc, void* stream);
 /* Workspace csa2_layer needs for this descriptor (pointers are ignored). */
 size_t csa2_workspace_bytes(const csa2_layer_desc* desc);
 
+/* ------------------------------------------------------------------------
+ * csa2_group -- a sharing group in one call: layers[0 .. n_layers-1] in
+ * order on one stream, e.g. Full (building the pool) -> Reindex ->
+ * Reindex -> Reuse -> Reuse over one shared store ("DeepSeek-V4.1-Flash
+ * explained", section 2 mode table and section 3 "Hierarchical indexing:
+ * search broadly once").  Later layers read the idx_inout / pool_inout
+ * their predecessors write, so they must point at the same buffers.  All
+ * descriptors (and their workspaces, which layers of one group may share,
+ * since the layers run one after another) are validated before anything is
+ * enqueued.  The whole group is a fixed sequence of launches, so a caller
+ * can capture it in one HIP graph.
+ * ------------------------------------------------------------------------ */
+int csa2_group(const csa2_layer_desc* layers, int n_layers, void* stream);
+
 /* Static text for a status code; for the last error on the calling thread
  * it includes the detail recorded then. */
 const char* csa2_status_str(int status);

@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_dense_attn_workspace_bytes.restype = s
         L.csa2_sparse_attn_workspace_bytes.restype = s
         L.csa2_layer.argtypes = [ctypes.POINTER(LayerDesc), v]
+        L.csa2_group.argtypes = [ctypes.POINTER(LayerDesc), i, v]
         L.csa2_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.csa2_workspace_bytes.restype = s
         L.csa2_status_str.argtypes = [i]
@@ -306,6 +307,13 @@ def csa2_workspace_bytes(desc: LayerDesc) -> int:
 def csa2_layer(desc: LayerDesc, stream=None) -> None:
     """Enqueues one layer (see csa2.h); outputs land in the desc's buffers."""
     _check(lib().csa2_layer(ctypes.byref(desc), _stream(stream)))
+
+
+def csa2_group(descs, stream=None) -> None:
+    """Enqueues a sharing group (a sequence of layer descriptors) in one
+    call; see csa2.h."""
+    arr = (LayerDesc * len(descs))(*descs)
+    _check(lib().csa2_group(arr, len(descs), _stream(stream)))
 
 
 def version() -> str:

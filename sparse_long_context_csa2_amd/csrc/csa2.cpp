@@ -408,6 +408,24 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     return e ? hip_fail(e, "layer: sparse_attn launch") : CSA2_OK;
 }
 
+int csa2_group(const csa2_layer_desc* layers, int n_layers, void* stream) {
+    if (!layers || n_layers < 1) return fail(CSA2_EINVAL, "group: need at least one layer descriptor");
+    // every layer is validated before anything is enqueued
+    for (int i = 0; i < n_layers; ++i) {
+        LayerPlan pl;
+        int e = plan_layer(&layers[i], pl);
+        if (e) return e;
+        if (pl.total && (!layers[i].ws || layers[i].ws_bytes < pl.total))
+            return fail(CSA2_EWORKSPACE, "group: layer %d workspace %zu bytes, need %zu", i, layers[i].ws_bytes,
+                        pl.total);
+    }
+    for (int i = 0; i < n_layers; ++i) {
+        const int e = csa2_layer(&layers[i], stream);
+        if (e) return e;
+    }
+    return CSA2_OK;
+}
+
 const char* csa2_status_str(int status) {
     if (status != CSA2_OK && status == g_detail_code && !g_detail.empty()) return g_detail.c_str();
     switch (status) {

@@ -257,6 +257,128 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     for (int c = c0 + static_cast<int>(threadIdx.x); c < c1; c += 256) __builtin_nontemporal_store(osc[c - c0], &orow[c]);
 }
 
+// Multi-query decode scoring: several query tokens of one sequence (2 .. 8,
+// e.g. the positions a speculative draft asks the model to verify, "Create
+// DeepSeek from scratch", "How DSpark drafts and verifies several tokens")
+// against all its records, no pool.  A key tile is loaded once, into
+// registers as in idx_mfma_kernel, and multiplied against every token: the
+// M side of the products is Tq x 32 heads, so the keys cross HBM once per
+// sequence instead of once per token.  The tokens' queries sit in LDS (a
+// 256-byte head row keeps its 16-byte chunk c at slot c ^ (row mod 16), so
+// the 16 rows one operand read touches fill all banks) and their scores
+// collect in LDS until the workgroup's column run is done.
+constexpr int kMultiMax = 8;     // query tokens per sequence, at most
+constexpr int kMultiTpbMax = 64; // tiles per workgroup, at most
+
+template <int KDT>
+__global__ __launch_bounds__(256) void idx_multi_kernel(IdxP p) {
+    extern __shared__ __align__(16) uint8_t msh[];
+    const int Tq = p.Tq;
+    uint8_t* qsh = msh;                                          // [Tq][32 heads][256 B], swizzled
+    float* wsh = reinterpret_cast<float*>(msh + Tq * kHi * 256);  // [Tq][32]
+    float* osc = wsh + Tq * kHi;                                 // [Tq][tpb * 16]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    const int b = blockIdx.y;
+    const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
+    const int tpb = p.tiles_per_block;
+
+    // the tokens' queries and head weights into LDS
+    for (int c = tid; c < Tq * kHi * 16; c += 256) {
+        const int r = c >> 4, ch = c & 15;  // head row (token * 32 + head), chunk
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p.q + (static_cast<size_t>(b) * Tq * kHi + r) * kDi + 8 * ch);
+        *reinterpret_cast<u32x4*>(qsh + r * 256 + 16 * (ch ^ (r & 15))) = v;
+    }
+    for (int c = tid; c < Tq * kHi; c += 256) wsh[c] = p.w[static_cast<size_t>(b) * Tq * kHi + c];
+    __shared__ int vsh[kMultiMax];  // records each token may see
+    if (tid < kMultiMax) vsh[tid] = tid < Tq ? visible_count(p.q_pos[static_cast<size_t>(b) * Tq + tid], p.m, nrec) : 0;
+    __syncthreads();
+    int vmax = 0;
+    for (int t = 0; t < Tq; ++t) vmax = max(vmax, vsh[t]);
+
+    const int ntiles = (p.ncols + 15) / 16;
+    const int t_begin = blockIdx.x * tpb;
+    const int t_end = min(ntiles, t_begin + tpb);
+    const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+
+    struct Tile {
+        int rec;
+        bool any;
+        u32x4 raw[4];
+        float kscale;
+    };
+    auto fetch = [&](int ti, Tile& T) {
+        const int c = ti * 16 + n;
+        T.rec = c < p.ncols ? c : -1;
+        const bool ld = T.rec >= 0 && T.rec < vmax;
+        T.any = __any(ld);
+        T.kscale = 1.f;
+        if (T.any) {
+            load_key_raw<KDT>(kbase + static_cast<size_t>(ld ? T.rec : 0) * kRowBytes, g, T.raw);
+            if (KDT == DT_E4M3)
+                T.kscale = ld ? static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+        }
+    };
+    auto score = [&](int ti, const Tile& T) {
+        bf16x8 bk[4];
+        if (T.any) key_operands<KDT>(T.raw, 1.f, bk);
+        for (int t = 0; t < Tq; ++t) {
+            float val = -__builtin_huge_valf();
+            if (T.any) {
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+                const uint8_t* q0 = qsh + (t * kHi + n) * 256;       // head n (m-tile 0)
+                const uint8_t* q1 = q0 + 16 * 256;                    // head 16 + n
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int ch = chunk8<KDT>(g, ks) ^ n;           // rows n and 16 + n share the swizzle
+                    acc0 = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(q0 + 16 * ch)), bk[ks], acc0);
+                    acc1 = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(q1 + 16 * ch)), bk[ks], acc1);
+                }
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsh + t * kHi + 4 * g);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(wsh + t * kHi + 16 + 4 * g);
+                float part = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    part += w0[v] * relu(acc0[v]);
+                    part += w1[v] * relu(acc1[v]);
+                }
+                part += shfl_xor_f(part, 16);
+                part += shfl_xor_f(part, 32);
+                if (KDT == DT_E4M3) part *= T.kscale;
+                if (T.rec >= 0 && T.rec < vsh[t]) val = part;
+            }
+            if (g == 0) osc[t * tpb * 16 + (ti - t_begin) * 16 + n] = val;
+        }
+    };
+    constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;
+    Tile tt[kRing];
+    const int ti0 = t_begin + wave;
+#pragma unroll
+    for (int d = 0; d + 1 < kRing; ++d)
+        if (ti0 + 4 * d < t_end) fetch(ti0 + 4 * d, tt[d]);
+    for (int base = ti0; base < t_end; base += 4 * kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+            const int ti = base + 4 * d;
+            if (ti >= t_end) break;
+            const int tf = ti + 4 * (kRing - 1);
+            if (tf < t_end) fetch(tf, tt[(d + kRing - 1) % kRing]);
+            score(ti, tt[d]);
+        }
+    }
+    __syncthreads();
+    const int c0 = t_begin * 16;
+    const int c1 = min(t_end * 16, p.ncols);
+    for (int t = 0; t < Tq; ++t) {
+        float* orow = p.out + (static_cast<size_t>(b) * Tq + t) * p.ncols;
+        for (int c = c0 + tid; c < c1; c += 256) __builtin_nontemporal_store(osc[t * tpb * 16 + c - c0], &orow[c]);
+    }
+}
+
 // Prefill scoring: many query tokens of one sequence against the records
 // they may see -- a causal GEMM (tokens x heads) x 128 x records with a
 // ReLU and weighted head-sum epilogue.
@@ -646,6 +768,32 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
                 hipLaunchKernelGGL(idx_prefill_kernel<DT_BF16>, grid, dim3(kPWaves * 64), 0, st, p, nb);
             else
                 hipLaunchKernelGGL(idx_prefill_kernel<DT_E4M3>, grid, dim3(kPWaves * 64), 0, st, p, nb);
+            return static_cast<int>(hipGetLastError());
+        }
+        // Several decode tokens per sequence (and no pool): each key tile is
+        // read once for all of them.  Tiles per workgroup: the largest that
+        // still gives >= 512 workgroups.
+        if (!a.pool && a.Tq >= 2 && a.Tq <= kMultiMax && a.q_dtype == DT_BF16 && a.k_dtype != DT_MXFP4) {
+            int tpb = kMultiTpbMax;
+            while (tpb > 4 && static_cast<long>(a.B) * ((ntiles + tpb - 1) / tpb) < 512) tpb >>= 1;
+            IdxP p;
+            p.B = a.B; p.Tq = a.Tq; p.N = a.N; p.m = a.m; p.ncols = a.ncols; p.P = 0; p.blk = 0;
+            p.q = static_cast<const uint16_t*>(a.q_idx);
+            p.qsc = nullptr;
+            p.w = a.w;
+            p.k = static_cast<const uint8_t*>(a.k_idx);
+            p.ks = a.k_scale;
+            p.q_pos = a.q_pos;
+            p.n_rec = a.n_rec;
+            p.pool = nullptr;
+            p.out = a.scores;
+            p.tiles_per_block = tpb;
+            const size_t lds = static_cast<size_t>(a.Tq) * (kHi * 256 + kHi * 4 + tpb * 16 * 4);
+            const dim3 grid((ntiles + tpb - 1) / tpb, a.B);
+            if (a.k_dtype == DT_BF16)
+                hipLaunchKernelGGL(idx_multi_kernel<DT_BF16>, grid, dim3(256), lds, st, p);
+            else
+                hipLaunchKernelGGL(idx_multi_kernel<DT_E4M3>, grid, dim3(256), lds, st, p);
             return static_cast<int>(hipGetLastError());
         }
         // Decode rows: the largest tiles per block that still gives >= 512

@@ -94,8 +94,18 @@ class DeviceGroup:
                 desc.ws_bytes = self.ws.numel()
 
     def run(self, copy: int = 0, stream=None) -> None:
-        for desc in self.descs[copy]:
-            _b.csa2_layer(desc, stream)
+        """The whole group through one csa2_group call."""
+        _b.csa2_group(self.descs[copy], stream)
+
+    def capture(self, copy: int = 0) -> "torch.cuda.CUDAGraph":
+        """The group's launches captured as one HIP graph (replay() reruns
+        the whole group on the same buffers)."""
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            self.run(copy, s)
+        return g
 
     def outputs(self) -> List[np.ndarray]:
         return [d["out"].cpu().numpy() for d in self.layers]

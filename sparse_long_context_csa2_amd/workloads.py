@@ -262,6 +262,11 @@ CONFIGS: Dict[str, Workload] = {
         description="long-context decode in the V4.1 cache formats: B=8, context 1,048,576 "
                     "(N=262,144); main KV FP4 (E2M1 + E4M3 scale per 16 channels, 288 B rows), "
                     "indexer queries and keys MXFP4, window FP8"),
+    "C8": Workload(
+        name="C8-verify-decode-bf16", seed=7, B=16, Tq=5, N=16384, m=4, Hi=32, Di=128,
+        H=64, D=512, rope_dims=64, W=128, K=512, decode_pos=65536,
+        description="multi-query decode, Full mode: B=16 sequences at context 65,536 (N=16,384), "
+                    "5 query positions each (a verification pass over drafted tokens), bf16"),
 }
 
 _NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "fp4": np.uint8, "mxfp4": np.uint8}

@@ -233,3 +233,26 @@ def test_dense_attn_validation(L):
     assert call(B=8) == B.CSA2_EWORKSPACE
     assert L.csa2_dense_attn_workspace_bytes(8, 1, 64, 512, 10, 8) == 0  # one tile: no split
     assert call(H=3, D=2048, qdt=0, kvdt=0, swadt=0) == B.CSA2_EUNSUPPORTED
+
+
+def test_group_validates_every_layer_first(L):
+    """csa2_group refuses an empty group and, when any layer is invalid,
+    returns that layer's error before enqueuing any layer."""
+    d = B.LayerDesc()
+    d.mode, d.B, d.Tq, d.N, d.m = 2, 1, 1, 100, 4
+    d.kv, d.kv_dtype, d.H, d.D, d.q, d.q_dtype = FAKE, 1, 64, 512, FAKE, 1
+    d.swa, d.swa_dtype, d.S, d.W = FAKE, 1, 128, 128
+    d.sink, d.rope_dims, d.rope_base, d.q_pos = FAKE, 64, 10000.0, FAKE
+    d.K, d.idx_inout, d.out = 16, FAKE, FAKE
+    d.ws, d.ws_bytes = FAKE, 1 << 30
+    bad = B.LayerDesc()
+    ctypes.pointer(bad)[0] = d
+    bad.mode = 9
+    arr = (B.LayerDesc * 2)(d, bad)
+    assert L.csa2_group(arr, 2, None) == B.CSA2_EINVAL
+    assert "unknown mode" in L.csa2_status_str(B.CSA2_EINVAL).decode()
+    d.ws_bytes = 16
+    arr = (B.LayerDesc * 2)(d, d)
+    assert L.csa2_group(arr, 2, None) == B.CSA2_EWORKSPACE
+    assert L.csa2_group(arr, 0, None) == B.CSA2_EINVAL
+    assert L.csa2_group(None, 1, None) == B.CSA2_EINVAL

@@ -28,6 +28,7 @@ SAMPLES = {
     "C5": [(0, 0), (7, 0)],
     "C6": [(0, 0), (3, 0), (7, 0)],
     "C7": [(0, 0), (7, 0)],
+    "C8": [(0, 0), (0, 4), (9, 2), (15, 4)],
 }
 # rows whose whole score row is compared (a full C2 row costs the oracle
 # 1024 columns; a C5 row 262,144)
@@ -39,6 +40,7 @@ SCORE_ROWS = {
     "C5": [(0, 0), (7, 0)],
     "C6": [],
     "C7": [(0, 0), (7, 0)],
+    "C8": [(0, 0), (0, 4), (9, 2), (15, 4)],
 }
 # unit-scale variants: rows and queries ~ N(0, 1), the scale the contract's
 # attention bounds are stated for
@@ -80,7 +82,7 @@ def _device_scores(grp, li, pooled):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C3u", "C5u", "C7u"])
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8", "C3u", "C5u", "C7u"])
 def test_config_full_size(cfg):
     print(f"[case] full-size {cfg}", flush=True)
     wl, base = _workload(cfg)

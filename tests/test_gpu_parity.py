@@ -64,6 +64,25 @@ def test_index_scores_mfma_decode(kdt):
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("Tq", [3, 5, 8])
+def test_index_scores_multi_query(kdt, Tq):
+    """Several decode tokens per sequence (a verification pass over drafted
+    positions): each key tile is read once for all of them.  Ragged record
+    counts, tokens whose visibility ends inside a tile, 3000 records over
+    several workgroups' column runs."""
+    _case(f"index_scores multi-query decode, {kdt} keys, Tq={Tq}")
+    wl = _small(Tq=Tq, N=3000, k_dtype=kdt, n_rec=(3000, 1999, 7), decode_pos=4 * 3000 + 11)
+    inp = WL.make_inputs(wl)
+    q_pos = inp["layers"][0]["q_pos"]
+    q_pos[1] = 4 * 1500 + np.arange(Tq) * 3  # visibility grows inside a tile across the tokens
+    q_pos[2, 0] = 2                          # a token that sees nothing
+    g = _run_scores(inp)
+    for b in range(3):
+        for ti in range(Tq):
+            PR.check_scores(g[b, ti], O.full_row_scores(inp["shared"], inp["layers"][0], b, ti), f"b={b} t={ti}")
+
+
+@pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
 @pytest.mark.parametrize("Tq,N,n_rec", [(70, 40, None), (37, 700, None), (21, 301, None), (48, 600, (450, 600))])
 def test_index_scores_mfma_prefill(kdt, Tq, N, n_rec):
     """Ragged token groups; several 256-record groups (N=700); a row length
@@ -771,3 +790,32 @@ def test_prefill_row_equals_decode():
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(g1.index_sets()[0][0, 0]), np.sort(idx_p[0, t]))
         assert np.abs(g1.outputs()[0][0, 0] - out_p[0, t]).max() <= 1e-5
+
+
+def test_group_graph_replay():
+    """A sharing group (Full + pool, Reindex, Reuse) captured as one HIP
+    graph: every replay, with eager work and synchronisation between the
+    replays, reproduces the eager group's index sets and outputs exactly."""
+    _case("csa2_group captured in a HIP graph, replayed three times")
+    wl = _small(B=3, Tq=2, N=3000, blk=64, P=8, K=96, W=32, decode_pos=12100,
+                modes=("full+pool", "reindex", "reuse"))
+    inp = WL.make_inputs(wl)
+    grp = R.DeviceGroup(inp)
+    grp.run()
+    torch.cuda.synchronize()
+    want_o, want_i = grp.outputs(), grp.index_sets()
+    _check_group(inp, grp, [(0, 0), (2, 1)])
+    g = grp.capture()
+    for r in range(3):
+        for lay in grp.layers:
+            lay["out"].fill_(float("nan"))  # eager work between the replays
+        for t in grp.idx:
+            if t is not None:
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(grp.outputs(), want_o):
+            assert np.array_equal(a, b), f"replay {r}: outputs differ"
+        for a, b in zip(grp.index_sets(), want_i):
+            assert np.array_equal(a, b), f"replay {r}: index sets differ"
