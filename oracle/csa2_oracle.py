@@ -355,6 +355,66 @@ def attend(q: np.ndarray, rows: np.ndarray, sink: np.ndarray, sm: float) -> np.n
 
 
 # --------------------------------------------------------------------------
+# Record construction (the compressor and the cache write)
+# --------------------------------------------------------------------------
+
+
+def pool_block(c: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """One record from the m token rows of its block: each channel is a
+    softmax-weighted sum over the block's tokens, the weights coming from
+    that channel's gate logits ([COURSE] "How CSA2 compresses, shares, and
+    selects attention memory": above ratio 1, consecutive token
+    representations are pooled with learned, channel-wise softmax gates).
+    At ratio 1 there is no pooling: the record is the token's row.
+
+    c, z: [m][D] candidate latents and gate logits -> [D]."""
+    c = np.asarray(c, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    if c.shape[0] == 1:
+        return c[0].copy()
+    a = np.exp(z - z.max(axis=0, keepdims=True))
+    a /= a.sum(axis=0, keepdims=True)
+    return (a * c).sum(axis=0)
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain ([INSIDE] CSA section: RMSNorm on
+    the compressed KV head before its RoPE; [COURSE]: at ratio 1 the record
+    is a normalized projection)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / math.sqrt(float(np.mean(x * x)) + eps) * np.asarray(gain, dtype=np.float64)
+
+
+def compress_records(c: np.ndarray, z: np.ndarray, m: int, gain: np.ndarray, eps: float, t0: int,
+                     rope_dims: int, rope_base: float) -> np.ndarray:
+    """Records of one sequence from its token rows (before quantization).
+
+    Record s pools tokens m*s .. m*s+m-1 of the rows (absolute positions t0
+    + m*s ..; groups do not overlap, [EXPL] §2: CSA2 removes overlapping
+    compression groups), is RMS-normalized, then its last ``rope_dims``
+    channels are rotated to the position of its last token, t0 + m*s + m-1
+    (caches are written after RoPE, [COURSE] FP4 lesson "Quantize after
+    RoPE"; the record's position is a reading: the pages do not state it).
+
+    c, z: [n*m][D]; returns [n][D] float64."""
+    c = np.asarray(c, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    n = c.shape[0] // m
+    out = np.empty((n, c.shape[1]), dtype=np.float64)
+    for s in range(n):
+        x = rms_norm(pool_block(c[m * s:m * s + m], z[m * s:m * s + m]), gain, eps)
+        out[s] = rope_rotate(x, float(t0 + m * s + m - 1), rope_dims, rope_base)
+    return out
+
+
+def derive_index_keys(stored: np.ndarray, w_ik: np.ndarray) -> np.ndarray:
+    """Indexer keys from the stored main-KV rows: k = x_stored @ W_ik
+    ([EXPL] §2: CSA2 derives indexer keys from main KV).  ``stored`` holds
+    the dequantized cache rows, so the keys depend on the cache alone."""
+    return np.asarray(stored, dtype=np.float64) @ np.asarray(w_ik, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
 # One query of one layer, and a sharing group of layers
 # --------------------------------------------------------------------------
 

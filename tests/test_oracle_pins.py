@@ -555,3 +555,87 @@ def test_full_row_and_pool_row_scores_agree_with_layer():
                 assert prow[c] == row[s]
             else:
                 assert prow[c] == -np.inf
+
+
+# ---------------------------------------------------------------- compressor
+
+def _torch_records(c, z, m, gain, eps, t0, r, base):
+    """Records written with library routines: torch softmax over the block
+    (dim 0, per channel), torch RMSNorm, and the rotation as a complex
+    multiply of adjacent channel pairs by e^{i pos theta_j}."""
+    ct, zt = torch.from_numpy(c), torch.from_numpy(z)
+    n, D = c.shape[0] // m, c.shape[1]
+    out = []
+    for s_ in range(n):
+        blk_c, blk_z = ct[m * s_:m * s_ + m], zt[m * s_:m * s_ + m]
+        pooled = (torch.softmax(blk_z, dim=0) * blk_c).sum(0)
+        x = torch.nn.functional.rms_norm(pooled[None], (D,), weight=torch.from_numpy(gain), eps=eps)[0].numpy()
+        pos = t0 + m * s_ + m - 1
+        j = np.arange(r // 2)
+        tail = x[D - r:].reshape(r // 2, 2)
+        cz = (tail[:, 0] + 1j * tail[:, 1]) * np.exp(1j * pos * base ** (-2.0 * j / r))
+        out.append(np.concatenate([x[:D - r], np.stack([cz.real, cz.imag], -1).reshape(r)]))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_compressor_against_library_softmax_rmsnorm_and_rotation(m):
+    """Channel-wise softmax pooling over the m tokens of each block, RMSNorm
+    and the record's rotation, against torch routines and complex
+    rotation; at m = 1 there is no pooling (a normalized projection)."""
+    rng = np.random.default_rng(30 + m)
+    D, n = 48, 5
+    c = rng.standard_normal((n * m, D))
+    z = rng.standard_normal((n * m, D)) * 2
+    gain = rng.uniform(0.5, 1.5, D)
+    got = O.compress_records(c, z, m, gain, 1e-6, 4 * m, 8, 10000.0)
+    assert np.allclose(got, _torch_records(c, z, m, gain, 1e-6, 4 * m, 8, 10000.0), rtol=1e-12, atol=1e-12)
+
+
+def test_compressor_closed_forms():
+    """Equal gate logits average the block; a dominant gate copies its
+    token (per channel); shifting a channel's logits changes nothing;
+    scaling the tokens changes nothing after the norm; records use their
+    own block only; unrotating at the last token's position restores the
+    normalized record, whose RMS is the gain's."""
+    rng = np.random.default_rng(40)
+    m, D = 4, 32
+    c = rng.standard_normal((3 * m, D))
+    gain = np.full(D, 0.7)
+    eq = O.compress_records(c, np.zeros_like(c), m, gain, 0.0, 0, 0, 10000.0)
+    mean = c.reshape(3, m, D).mean(1)
+    assert np.allclose(eq, mean / np.sqrt((mean ** 2).mean(1, keepdims=True)) * 0.7)
+    z = np.zeros_like(c)
+    pick = rng.integers(0, m, size=(3, D))
+    for s_ in range(3):
+        z[m * s_ + pick[s_], np.arange(D)] = 800.0
+    dom = O.compress_records(c, z, m, gain, 0.0, 0, 0, 10000.0)
+    chosen = np.array([[c[m * s_ + pick[s_, d], d] for d in range(D)] for s_ in range(3)])
+    assert np.allclose(dom, chosen / np.sqrt((chosen ** 2).mean(1, keepdims=True)) * 0.7)
+    z2 = rng.standard_normal((3 * m, D))
+    base = O.compress_records(c, z2, m, gain, 0.0, 8, 6, 10000.0)
+    assert np.allclose(O.compress_records(c, z2 + rng.standard_normal(D), m, gain, 0.0, 8, 6, 10000.0), base)
+    assert np.allclose(O.compress_records(3.5 * c, z2, m, gain, 0.0, 8, 6, 10000.0), base)
+    c3 = c.copy()
+    c3[m:2 * m] += 5.0  # only record 1's tokens
+    r3 = O.compress_records(c3, z2, m, gain, 0.0, 8, 6, 10000.0)
+    assert np.allclose(r3[[0, 2]], base[[0, 2]]) and not np.allclose(r3[1], base[1])
+    for s_ in range(3):
+        un = O.inverse_rope(base[s_], 8 + m * s_ + m - 1, 6, 10000.0)
+        assert np.isclose(np.sqrt(np.mean(un ** 2)), 0.7)
+
+
+def test_index_keys_from_stored_rows():
+    """Indexer keys are the stored (dequantized) main-KV rows times W_ik:
+    against torch fp64 matmul on FP4 and e4m3 rows."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    w = rng.standard_normal((64, 16))
+    rows = WL.quantize_rows_fp4(x)
+    k = O.derive_index_keys(O.dequant(rows, None, "fp4"), w)
+    ref = (torch.from_numpy(O.dequant_fp4_rows(rows)) @ torch.from_numpy(w)).numpy()
+    assert np.allclose(k, ref, rtol=1e-13, atol=0)
+    codes, sc = WL.quantize_rows_e4m3(x)
+    k2 = O.derive_index_keys(O.dequant(codes, sc), w)
+    e4 = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64) * torch.from_numpy(sc.astype(np.float64))[:, None]
+    assert np.allclose(k2, (e4 @ torch.from_numpy(w)).numpy(), rtol=1e-13, atol=0)
