@@ -4,9 +4,10 @@
  * One CSA2 layer separates three operations: creating memory, selecting
  * positions and attending to those positions ("DeepSeek-V4.1-Flash
  * explained", section 2 "CSA2: share memory without copying the answer").
- * This library covers selection and attention over memory the caller has
- * already built:
+ * This library covers writing that memory (csa2_compress), selection and
+ * attention:
  *
+ *   csa2_compress      records and indexer keys from token rows
  *   csa2_index_scores  lightning-indexer scores with causal visibility
  *   csa2_block_pool    hierarchical block-max candidate pool
  *   csa2_topk          Top-K record addresses (lower record id wins ties)
@@ -344,6 +345,61 @@ int csa2_layer(const csa2_layer_desc* desc, void* stream);
 
 /* Workspace csa2_layer needs for this descriptor (pointers are ignored). */
 size_t csa2_workspace_bytes(const csa2_layer_desc* desc);
+
+/* ------------------------------------------------------------------------
+ * csa2_compress -- record construction and the cache write.
+ *
+ * Turns token rows into global records and their indexer keys ("Create
+ * DeepSeek from scratch", "How CSA2 compresses, shares, and selects
+ * attention memory": above ratio 1, consecutive token representations are
+ * pooled with learned, channel-wise softmax gates; at ratio 1 a normalized
+ * projection; "DeepSeek-V4.1-Flash explained", section 2: CSA2 removes
+ * overlapping compression groups and derives indexer keys from main KV).
+ * For record s of sequence b (token rows m*s .. m*s+m-1, absolute
+ * positions t0[b] + m*s ..):
+ *
+ *   x[d]  = sum_i softmax_i(z[i][d]) * c[i][d]       over the block's rows
+ *   x     = x / sqrt(mean_d x[d]^2 + eps) * gain
+ *   x     = RoPE of the last rope_dims channels at position t0[b]+m*s+m-1
+ *           (adjacent pairs, angle pos*rope_base^(-2j/r), as the output
+ *           rotation of csa2_sparse_attn undoes)
+ *   kv    = x stored in kv_dtype (quantized after RoPE, the FP4 lesson's
+ *           "Quantize after RoPE")
+ *   k_idx = (stored kv row, dequantized) @ W_ik, stored in k_dtype
+ *
+ * The token projections c = h W_c and z = h W_z are ordinary linear layers
+ * and are inputs here.  Quantizers round to nearest, ties to even,
+ * saturating: e4m3 rows take scale max|x|/448; FP4 groups of 16 take the
+ * E4M3 scale nearest max|x|/6; MXFP4 blocks of 32 take 2^(floor(log2
+ * max|x|) - 2).
+ *
+ * Inputs
+ *   B, T, m    sequences, token rows per sequence (a multiple of m), ratio
+ *   D, Di      latent width (128, 256, 512 or 1024) and key width (64, 128,
+ *              192 or 256)
+ *   c, z       [B][T][D] candidate latents and gate logits, in_dtype in
+ *              {F32, BF16}
+ *   t0         [B] int64 absolute position of token row 0 (a multiple of m;
+ *              its records go to cache rows t0/m, t0/m + 1, ...; rows at or
+ *              past N_out, or a negative t0, are not written)
+ *   gain       [D] float32; eps >= 0
+ *   w_ik       [D][Di] in w_dtype {F32, BF16}
+ *   N_out      records per sequence in the caches
+ * Outputs
+ *   kv         [B][N_out][D] in kv_dtype {F32, BF16, E4M3, FP4} (FP4:
+ *              [B][N_out][D/2 + D/16] bytes); kv_scale [B][N_out] for E4M3
+ *   k_idx      [B][N_out][Di] in k_dtype {F32, BF16, E4M3, MXFP4} (MXFP4:
+ *              [B][N_out][Di/2] bytes, Di = 128 or 256); k_scale [B][N_out]
+ *              float for E4M3, [B][N_out][Di/32] E8M0 bytes for MXFP4
+ * Workspace: none.
+ * ------------------------------------------------------------------------ */
+int csa2_compress(int B, int T, int D, int m, int Di,
+                  const void* c, const void* z, int in_dtype,
+                  const int64_t* t0, const float* gain, float eps,
+                  int rope_dims, float rope_base,
+                  const void* w_ik, int w_dtype, int N_out,
+                  void* kv, float* kv_scale, int kv_dtype,
+                  void* k_idx, void* k_scale, int k_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa2_group -- a sharing group in one call: layers[0 .. n_layers-1] in

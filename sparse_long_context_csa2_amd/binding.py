@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn_workspace_bytes.restype = s
         L.csa2_layer.argtypes = [ctypes.POINTER(LayerDesc), v]
         L.csa2_group.argtypes = [ctypes.POINTER(LayerDesc), i, v]
+        L.csa2_compress.argtypes = [i, i, i, i, i, v, v, i, v, v, f, i, f, v, i, i, v, v, i, v, v, i, v]
         L.csa2_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.csa2_workspace_bytes.restype = s
         L.csa2_status_str.argtypes = [i]
@@ -307,6 +308,21 @@ def csa2_workspace_bytes(desc: LayerDesc) -> int:
 def csa2_layer(desc: LayerDesc, stream=None) -> None:
     """Enqueues one layer (see csa2.h); outputs land in the desc's buffers."""
     _check(lib().csa2_layer(ctypes.byref(desc), _stream(stream)))
+
+
+def csa2_compress(c, z, t0, gain, w_ik, m: int, kv, k_idx, kv_scale=None, k_scale=None, rope_dims: int = 64,
+                  rope_base: float = 10000.0, eps: float = 1e-6, stream=None, prepare: bool = False):
+    """Records [B][N_out][..] and indexer keys from token rows c, z
+    [B][T][D]; see csa2.h.  The cache tensors' dtypes (with their scale
+    tensors) select the storage formats."""
+    B, T, D = c.shape
+    Di = _elems(k_idx)
+    N_out = kv.shape[1]
+    return _call(lib().csa2_compress,
+                 (B, T, D, m, Di, _p(c), _p(z), dtype_code(c), _p(t0), _p(gain), float(eps), rope_dims,
+                  float(rope_base), _p(w_ik), dtype_code(w_ik), N_out, _p(kv), _p(kv_scale),
+                  dtype_code(kv, kv_scale), _p(k_idx), _p(k_scale), dtype_code(k_idx, k_scale), _stream(stream)),
+                 (kv, k_idx), prepare)
 
 
 def csa2_group(descs, stream=None) -> None:

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
-SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "csa2.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "compress.hip", "csa2.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

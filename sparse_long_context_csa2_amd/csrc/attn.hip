@@ -99,25 +99,6 @@ constexpr int kMaxWin = 256;
 constexpr int kMaxEnt = kMaxKList + kMaxWin;  // entries of one split (multiple of kTile)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// cos/sin of the rotary angle t * base^(-2j/r): the angle is formed and
-// reduced modulo 2*pi in double precision (t reaches 2^20), the reduced
-// angle goes through single-precision sincos.
-__device__ __forceinline__ double rope_inv_freq(int j, int rd, float base) {
-    return pow(static_cast<double>(base), -2.0 * j / rd);
-}
-
-__device__ __forceinline__ void rope_cos_sin(int64_t t, double inv, float& c, float& s) {
-    const double th = static_cast<double>(t) * inv;
-    const double k = rint(th * 0.15915494309189533577);       // 1 / (2 pi)
-    double r = fma(-k, 6.283185307179586232, th);              // 2 pi, high part
-    r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi, low part
-    sincosf(static_cast<float>(r), &s, &c);
-}
-
-__device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base, float& c, float& s) {
-    rope_cos_sin(t, rope_inv_freq(j, rd, base), c, s);
-}
-
 // Barrier for LDS hand-offs: this wave's LDS accesses are complete, then
 // all waves meet.  Unlike __syncthreads() it does not wait for outstanding
 // global loads (the tile prefetches keep flowing across it); the asm is

@@ -105,6 +105,26 @@ __device__ __forceinline__ float load_elem(const void* base, size_t i, int dt) {
 
 __device__ __forceinline__ int dt_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }
 
+// ---------------------------------------------------------------- rotary
+// cos/sin of the rotary angle t * base^(-2j/r): the angle is formed and
+// reduced modulo 2*pi in double precision (t reaches 2^20), the reduced
+// angle goes through single-precision sincos.
+__device__ __forceinline__ double rope_inv_freq(int j, int rd, float base) {
+    return pow(static_cast<double>(base), -2.0 * j / rd);
+}
+
+__device__ __forceinline__ void rope_cos_sin(int64_t t, double inv, float& c, float& s) {
+    const double th = static_cast<double>(t) * inv;
+    const double k = rint(th * 0.15915494309189533577);       // 1 / (2 pi)
+    double r = fma(-k, 6.283185307179586232, th);              // 2 pi, high part
+    r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi, low part
+    sincosf(static_cast<float>(r), &s, &c);
+}
+
+__device__ __forceinline__ void rope_angle(int64_t t, int j, int rd, float base, float& c, float& s) {
+    rope_cos_sin(t, rope_inv_freq(j, rd, base), c, s);
+}
+
 // ---------------------------------------------------------------- ordering
 // Order-preserving float -> uint32 (larger float, larger key).  -inf and NaN
 // become 0, which marks "never selectable".

@@ -408,6 +408,42 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     return e ? hip_fail(e, "layer: sparse_attn launch") : CSA2_OK;
 }
 
+int csa2_compress(int B, int T, int D, int m, int Di, const void* c, const void* z, int in_dtype, const int64_t* t0,
+                  const float* gain, float eps, int rope_dims, float rope_base, const void* w_ik, int w_dtype,
+                  int N_out, void* kv, float* kv_scale, int kv_dtype, void* k_idx, void* k_scale, int k_dtype,
+                  void* stream) {
+    if (B < 1 || T < 1 || m < 1 || N_out < 1 || T % m)
+        return fail(CSA2_EINVAL, "compress: need B, T, m, N_out >= 1 and T a multiple of m (B=%d T=%d m=%d N_out=%d)",
+                    B, T, m, N_out);
+    if (!c || !z || !t0 || !gain || !w_ik || !kv || !k_idx)
+        return fail(CSA2_EINVAL, "compress: null required pointer");
+    if (int e = check_align("compress", {c, z, t0, gain, w_ik, kv, kv_scale, k_idx, k_scale}, nullptr)) return e;
+    if ((in_dtype != CSA2_F32 && in_dtype != CSA2_BF16) || (w_dtype != CSA2_F32 && w_dtype != CSA2_BF16))
+        return fail(dtype_ok(in_dtype) && dtype_ok(w_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
+                    "compress: token rows and W_ik must be f32 or bf16");
+    if (kv_dtype == CSA2_MXFP4 || k_dtype == CSA2_FP4)
+        return fail(CSA2_EUNSUPPORTED, "compress: records are f32/bf16/e4m3/fp4, keys f32/bf16/e4m3/mxfp4");
+    if (int e = check_scale("compress records", kv_dtype, kv_scale)) return e;
+    if (int e = check_scale("compress keys", k_dtype, k_scale)) return e;
+    if (D != 128 && D != 256 && D != 512 && D != 1024)
+        return fail(CSA2_EUNSUPPORTED, "compress: D=%d not in {128, 256, 512, 1024}", D);
+    if (Di < 64 || Di > 256 || Di % 64)
+        return fail(CSA2_EUNSUPPORTED, "compress: Di=%d must be 64, 128, 192 or 256", Di);
+    if (k_dtype == CSA2_MXFP4 && Di % 128)  // whole MX blocks and byte pairs per lane
+        return fail(CSA2_EUNSUPPORTED, "compress: mxfp4 keys need Di = 128 or 256 (got %d)", Di);
+    if (rope_dims < 0 || rope_dims > D || (rope_dims & 1))
+        return fail(CSA2_EINVAL, "compress: rope_dims=%d must be even and <= D", rope_dims);
+    if (!(rope_base > 0.f)) return fail(CSA2_EINVAL, "compress: rope_base must be > 0");
+    if (!(eps >= 0.f) || isinf(eps)) return fail(CSA2_EINVAL, "compress: bad eps");
+    csa2::CompressArgs a;
+    a.B = B; a.T = T; a.D = D; a.m = m; a.Di = Di; a.N_out = N_out;
+    a.c = c; a.z = z; a.in_dtype = in_dtype; a.t0 = t0; a.gain = gain; a.eps = eps;
+    a.rope_dims = rope_dims; a.rope_base = rope_base; a.w_ik = w_ik; a.w_dtype = w_dtype;
+    a.kv = kv; a.kv_scale = kv_scale; a.kv_dtype = kv_dtype; a.k_idx = k_idx; a.k_scale = k_scale; a.k_dtype = k_dtype;
+    const int e = csa2::launch_compress(a, stream);
+    return e ? hip_fail(e, "compress launch") : CSA2_OK;
+}
+
 int csa2_group(const csa2_layer_desc* layers, int n_layers, void* stream) {
     if (!layers || n_layers < 1) return fail(CSA2_EINVAL, "group: need at least one layer descriptor");
     // every layer is validated before anything is enqueued

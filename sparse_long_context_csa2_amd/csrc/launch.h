@@ -78,4 +78,25 @@ int launch_sparse_attn(const AttnArgs& a, void* stream);
 size_t sparse_attn_scratch_bytes();
 void* sparse_attn_scratch(int& err);
 
+struct CompressArgs {
+    int B, T, D, m, Di, N_out;
+    const void* c;
+    const void* z;
+    int in_dtype;
+    const int64_t* t0;
+    const float* gain;
+    float eps;
+    int rope_dims;
+    float rope_base;
+    const void* w_ik;
+    int w_dtype;
+    void* kv;
+    float* kv_scale;
+    int kv_dtype;
+    void* k_idx;
+    void* k_scale;
+    int k_dtype;
+};
+int launch_compress(const CompressArgs& a, void* stream);
+
 }  // namespace csa2

@@ -411,3 +411,47 @@ def dtype_code(dtype: str) -> int:
 def storage_dtype_name(arr: np.ndarray) -> str:
     return {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16",
             np.dtype(np.uint8): "e4m3"}[np.asarray(arr).dtype]
+
+
+# --------------------------------------------------------------------------
+# Record construction workloads (csa2_compress)
+# --------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class CompressWorkload:
+    """Token rows of B sequences turned into records and indexer keys."""
+
+    name: str
+    seed: int
+    B: int
+    T: int
+    m: int
+    D: int
+    Di: int
+    rope_dims: int
+    in_dtype: str = "bf16"
+    kv_dtype: str = "fp4"
+    k_dtype: str = "mxfp4"
+    description: str = ""
+
+
+COMPRESS: Dict[str, CompressWorkload] = {
+    "C9": CompressWorkload(
+        name="C9-compress-prefill-fp4", seed=8, B=16, T=4096, m=4, D=512, Di=128, rope_dims=64,
+        description="record construction for 16 sequences x 4096 tokens at m=4 (16,384 records): "
+                    "channel-wise softmax pooling, RMSNorm, RoPE, FP4 records and MXFP4 indexer keys"),
+}
+
+
+def make_compress_inputs(cw: CompressWorkload) -> Dict:
+    """Token rows c (candidate latents) and z (gate logits) ~ N(0, 1), gain ~
+    U(0.5, 1.5), W_ik ~ N(0, 1/D); sequences start at position 0."""
+    kids = np.random.SeedSequence(cw.seed).spawn(4)
+    c, _ = _batched_normal(kids[0], cw.B, (cw.T, cw.D), 1.0, cw.in_dtype)
+    z, _ = _batched_normal(kids[1], cw.B, (cw.T, cw.D), 1.0, cw.in_dtype)
+    g = np.random.Generator(np.random.PCG64(kids[2]))
+    gain = g.uniform(0.5, 1.5, size=cw.D).astype(np.float32)
+    w = (np.random.Generator(np.random.PCG64(kids[3])).standard_normal((cw.D, cw.Di)) /
+         math.sqrt(cw.D)).astype(np.float32)
+    return dict(c=c, z=z, gain=gain, w_ik=w, t0=np.zeros(cw.B, dtype=np.int64), cw=cw)

@@ -256,3 +256,30 @@ def test_group_validates_every_layer_first(L):
     assert L.csa2_group(arr, 2, None) == B.CSA2_EWORKSPACE
     assert L.csa2_group(arr, 0, None) == B.CSA2_EINVAL
     assert L.csa2_group(None, 1, None) == B.CSA2_EINVAL
+
+
+def test_compress_validation(L):
+    """csa2_compress: sizes, formats and scale arrays are checked on the
+    host before any launch."""
+    def call(**kw):
+        a = dict(B=1, T=8, D=512, m=4, Di=128, c=FAKE, z=FAKE, idt=1, t0=FAKE, gain=FAKE, eps=1e-6, r=64,
+                 base=10000.0, w=FAKE, wdt=1, N=16, kv=FAKE, kvs=None, kvdt=1, k=FAKE, ks=None, kdt=1)
+        a.update(kw)
+        return L.csa2_compress(a["B"], a["T"], a["D"], a["m"], a["Di"], a["c"], a["z"], a["idt"], a["t0"],
+                               a["gain"], a["eps"], a["r"], a["base"], a["w"], a["wdt"], a["N"], a["kv"], a["kvs"],
+                               a["kvdt"], a["k"], a["ks"], a["kdt"], None)
+    assert call(T=10) == B.CSA2_EINVAL                 # T not a multiple of m
+    assert call(m=0) == B.CSA2_EINVAL
+    assert call(c=None) == B.CSA2_EINVAL
+    assert call(z=FAKE + 8) == B.CSA2_EINVAL           # misaligned
+    assert call(D=96) == B.CSA2_EUNSUPPORTED
+    assert call(Di=100) == B.CSA2_EUNSUPPORTED
+    assert call(idt=2) == B.CSA2_EUNSUPPORTED          # e4m3 token rows
+    assert call(kvdt=2) == B.CSA2_EINVAL               # e4m3 records without their scales
+    assert call(kvdt=3, kvs=FAKE) == B.CSA2_EINVAL     # fp4 records carry their scales inline
+    assert call(kvdt=4, kvs=FAKE) == B.CSA2_EUNSUPPORTED
+    assert call(kdt=4) == B.CSA2_EINVAL                # mxfp4 keys without their scales
+    assert call(kdt=3) == B.CSA2_EUNSUPPORTED          # fp4 rows are no key format
+    assert call(kdt=4, ks=FAKE, Di=192) == B.CSA2_EUNSUPPORTED  # mxfp4 keys: Di = 128 or 256
+    assert call(r=63) == B.CSA2_EINVAL
+    assert call(eps=-1.0) == B.CSA2_EINVAL
