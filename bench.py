@@ -7,8 +7,9 @@ three decode workloads (Full decode at 64K context, hierarchical
 Full/Reindex/Reuse decode at 256K, fp8 decode at 1M, the heavily
 compressed (HCA) decode at 1M, the 1M decode in the V4.1 cache formats
 (FP4 main KV, MXFP4 indexer, FP8 window), and a multi-query decode that
-verifies 5 positions per sequence) in the same run, each reported in its
-own object under ``workloads``.  ``--workload`` picks
+verifies 5 positions per sequence) and record construction (16 x 4096
+token rows into FP4 records and MXFP4 keys) in the same run, each
+reported in its own object under ``workloads``.  ``--workload`` picks
 another primary workload; ``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
@@ -51,9 +52,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8", "C9"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
-    ap.add_argument("--extra", default="C3,C4,C5,C6,C7,C8", help="further workloads measured in the same run")
+    ap.add_argument("--extra", default="C3,C4,C5,C6,C7,C8,C9", help="further workloads measured in the same run")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
@@ -384,6 +385,94 @@ def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
     return rep
 
 
+# --------------------------------------------------------------- record construction
+
+def compress_work(cw):
+    """Algorithmic bytes and flops of one csa2_compress call: the token rows
+    c and z read once, gain and W_ik, the records and keys written once;
+    flops of the keys (2 D Di per record)."""
+    n = cw.B * (cw.T // cw.m)
+    ein = 4 if cw.in_dtype == "f32" else 2
+    rb = {"f32": 4 * cw.D, "bf16": 2 * cw.D, "e4m3": cw.D + 4, "fp4": cw.D // 2 + cw.D // 16}[cw.kv_dtype]
+    kb = {"f32": 4 * cw.Di, "bf16": 2 * cw.Di, "e4m3": cw.Di + 4, "mxfp4": cw.Di // 2 + cw.Di // 32}[cw.k_dtype]
+    return dict(bytes=2 * cw.B * cw.T * cw.D * ein + 4 * cw.D + 4 * cw.D * cw.Di + n * (rb + kb),
+                flops=2.0 * cw.D * cw.Di * n)
+
+
+def cpu_baseline_compress(inp, seconds):
+    """The oracle's record construction (pooling, RMSNorm, RoPE in fp64, keys
+    from the records) on a bounded sample: blocks of 64 records, one
+    sequence after another."""
+    import oracle as O
+    cores, blas = cpu_threads()
+    cw = inp["cw"]
+    n = cw.T // cw.m
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(cw.B):
+        for s0 in range(0, n, 64):
+            tok = slice(s0 * cw.m, (s0 + 64) * cw.m)
+            x = O.compress_records(O.dequant(inp["c"][b][tok]), O.dequant(inp["z"][b][tok]), cw.m, inp["gain"],
+                                   1e-6, int(inp["t0"][b]) + s0 * cw.m, cw.rope_dims, 10000.0)
+            O.derive_index_keys(x, inp["w_ik"])
+            done += x.shape[0] * cw.m
+            if time.perf_counter() - t0 > seconds:
+                break
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": min(cores, blas), "kind": "oracle",
+            "affinity_cores": cores, "blas_threads": blas,
+            "sample": f"{done} of {cw.B * cw.T} token rows (blocks of 64 records, in order), fp64 NumPy, "
+                      f"records before quantization and keys from them, {dt:.1f} s"}
+
+
+def measure_compress(key, steps, warmup, cpu_seconds, torch):
+    """Times `steps` csa2_compress calls of workload `key` (HIP events on the
+    launch stream) and returns its report."""
+    from sparse_long_context_csa2_amd import runner as R
+    from sparse_long_context_csa2_amd import workloads as WL
+
+    cw = WL.COMPRESS[key]
+    inp = WL.make_compress_inputs(cw)
+    dc = R.DeviceCompress(inp, device="cuda:0")
+    stream = torch.cuda.Stream()
+    for _ in range(warmup):
+        dc.run(stream)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for s in range(steps):
+            dc.run(stream)
+            evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ts = [evs[s].elapsed_time(evs[s + 1]) * 1e-3 for s in range(steps)]
+    avg = float(np.mean(ts))
+    w = compress_work(cw)
+    ach = w["bytes"] / avg / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, "compress"), "kernel": "compress",
+            "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"], "avg_us": round(avg * 1e6, 2)}
+    cpu = cpu_baseline_compress(inp, cpu_seconds) if cpu_seconds > 0 else None
+    rep = {
+        "workload": cw.name, "value": round(cw.B * cw.T / avg, 1), "unit": "tokens/s",
+        "ms_per_step": round(avg * 1e3, 4), "steps": steps, "warmup": warmup,
+        "dtype": f"{cw.in_dtype}->{cw.kv_dtype}+{cw.k_dtype}",
+        "config": {"workload": cw.name, "B": cw.B, "T": cw.T, "m": cw.m, "D": cw.D, "Di": cw.Di,
+                   "rope_dims": cw.rope_dims, "records": cw.B * (cw.T // cw.m)},
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernels": {"compress": {"avg_us": round(avg * 1e6, 2), "calls_per_step": 1, "GB_s": round(ach, 1)}},
+        "wall_s": round(wall, 3),
+    }
+    del dc, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rep
+
+
 # --------------------------------------------------------------- main
 
 def main():
@@ -396,21 +485,28 @@ def main():
 
     from sparse_long_context_csa2_amd import workloads as WL
 
-    prim = measure(args.workload, args.steps, args.warmup, args.copies,
-                   0 if args.no_cpu else args.cpu_seconds, torch,
-                   graph=WL.CONFIGS[args.workload].decode_pos is not None)
+    if args.workload in WL.COMPRESS:
+        prim = measure_compress(args.workload, args.steps, args.warmup, 0 if args.no_cpu else args.cpu_seconds, torch)
+    else:
+        prim = measure(args.workload, args.steps, args.warmup, args.copies,
+                       0 if args.no_cpu else args.cpu_seconds, torch,
+                       graph=WL.CONFIGS[args.workload].decode_pos is not None)
     extra = {}
     if not args.only:
         for key in [k for k in args.extra.split(",") if k and k != args.workload]:
             print(f"[bench] {key}", file=sys.stderr, flush=True)
-            rep = measure(key, args.extra_steps, args.warmup, 0, 0 if args.no_cpu else args.extra_cpu_seconds,
-                          torch, graph=WL.CONFIGS[key].decode_pos is not None)
+            cpu_s = 0 if args.no_cpu else args.extra_cpu_seconds
+            if key in WL.COMPRESS:
+                rep = measure_compress(key, args.extra_steps, args.warmup, cpu_s, torch)
+            else:
+                rep = measure(key, args.extra_steps, args.warmup, 0, cpu_s, torch,
+                              graph=WL.CONFIGS[key].decode_pos is not None)
             extra[key] = rep
 
     line = {
         "metric": "CSA2 layer query-tokens/s (prefill & decode) + % of HBM/MFMA peak, 1 GPU",
         "value": prim["value"],
-        "unit": "query-tokens/s",
+        "unit": prim["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -424,8 +520,8 @@ def main():
         "roofline": prim["roofline"],
         "cpu_baseline": prim["cpu_baseline"],
         "kernels": prim["kernels"],
-        "hbm": prim["hbm"],
-        "eager_ms_per_step": prim["eager_ms_per_step"],
+        "hbm": prim.get("hbm"),
+        "eager_ms_per_step": prim.get("eager_ms_per_step"),
         "workloads": extra,
     }
     print(json.dumps(line))

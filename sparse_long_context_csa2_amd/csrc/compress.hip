@@ -13,16 +13,28 @@
 // (dequantized) row: k = x_stored W_ik ("explained", section 2: CSA2
 // derives indexer keys from main KV), then quantized into the key cache.
 //
-// compress_kernel: one workgroup of 4 waves per 16 records of one
-// sequence.  A wave builds one record at a time: lane l owns channels
-// CPL*l .. CPL*l+CPL-1 (so rotary pairs and FP4 groups of 16 channels stay
-// within one lane or a few neighbouring lanes), runs an online softmax over
-// the block's tokens, reduces the row's mean square across the wave,
-// rotates, quantizes and stores the row, and keeps the stored row's values
-// in LDS.  The 16 rows' keys are then formed in float32 (each thread owns
-// one key dimension of 8 records; W_ik is read once per workgroup) and
-// quantized per record.
+// Two kernels on the caller's stream:
+//
+// pool_kernel streams the token rows (the HBM-bound part).  A wave builds
+// one record at a time, four per wave: lane l owns channels CPL*l ..
+// CPL*l+CPL-1 and loads them with 16-byte loads, four tokens at once; the
+// softmax runs over each group of four tokens with one exponential per
+// token and channel; the row's mean square is a wave reduction; the
+// rotary angles are computed one pair per lane (angle in double precision
+// from a per-workgroup table of inverse frequencies) and shuffled to the
+// lanes that own the pairs; the quantized row is written with one packed
+// store per lane.
+//
+// keys_kernel forms the keys as a matrix product on the matrix cores: 64
+// records (rows, read back from the cache just written, dequantized
+// exactly to bf16) times W_ik.  W_ik is split into bf16 high and low parts
+// (w = hi + lo to 2^-16 relative), float32 record rows likewise, so the
+// bf16 products accumulate in float32 to about float32 accuracy.  W_ik is
+// staged transposed in LDS 64 input channels at a time; the keys go
+// through LDS once more to be quantized one record per wave.
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -30,8 +42,12 @@
 namespace csa2 {
 namespace {
 
-constexpr int kRecPerWG = 16;
-constexpr int kCThreads = 256;
+constexpr int kPoolWaves = 4;
+constexpr int kPoolRecPerWave = 4;
+constexpr int kPoolRecPerWG = kPoolWaves * kPoolRecPerWave;
+constexpr int kMaxRopePairs = 512;  // rope_dims <= D <= 1024
+constexpr int kKeyRows = 64;        // records per keys workgroup (4 waves x 16 rows)
+constexpr int kWPitch = 72;         // bf16 per staged W_ik^T row: 64 channels + 8 (bank spread)
 
 struct CompP {
     int B, T, D, m, Di, N_out;
@@ -53,238 +69,556 @@ struct CompP {
     int k_dt;
 };
 
-__device__ __forceinline__ float ld_in(const uint8_t* base, size_t i, int dt) {
-    return dt == DT_F32 ? reinterpret_cast<const float*>(base)[i]
-                        : bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
-}
-
-// Nearest e4m3fn code of v (ties to even, saturating at +-448).
+// Nearest e4m3fn code of v (ties to even, saturating at +-448).  gfx950's
+// conversion rounds to nearest even but turns magnitudes from 464 up into
+// NaN, so the input is clamped to the largest finite value first; with
+// that it agrees with a comparison encoder on every e4m3 midpoint, its
+// float neighbours and the saturation range.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fminf(fabsf(v), 448.f);
-    uint32_t mag;
-    if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (rintf rounds ties to even)
-        mag = static_cast<uint32_t>(rintf(a * 512.f));
-    } else {               // keep 3 mantissa bits of the float, ties to even
-        uint32_t u = __float_as_uint(a);
-        u += 0x7FFFFu + ((u >> 20) & 1u);
-        mag = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
+    const float c = fminf(fmaxf(v, -448.f), 448.f);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// Two e4m3 codes (a in the low byte).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, -448.f), 448.f), fminf(fmaxf(b, -448.f), 448.f), 0,
+                                           false) & 0xFFFFu;
+}
+
+// Nearest E2M1 codes of a, b (ties to even, saturating at 6; a in the low
+// nibble) in byte `sel` of `old`: gfx950's conversion with unit scale,
+// which matches a comparison encoder on every midpoint of the E2M1 levels,
+// their float neighbours and the saturation range.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_encode2(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Reductions over aligned groups of N neighbouring lanes (N a power of
+// two up to 64) with DPP moves and gfx950's permlane swaps, no LDS round
+// trip: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes l ^ 1 and l ^ 2; after
+// those, row_half_mirror (l <-> 7 - l within 8 lanes) and row_mirror
+// (l <-> 15 - l within 16) meet the other quad and the other half.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+    if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
+    if constexpr (N >= 32) {
+        float x, y;
+        pair_xor16(v, x, y);
+        v = fmaxf(x, y);
     }
-    return sign | (mag < 0x7Eu ? mag : 0x7Eu);
+    if constexpr (N >= 64) {
+        float x, y;
+        pair_xor32(v, x, y);
+        v = fmaxf(x, y);
+    }
+    return v;
 }
 
-// Nearest E2M1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to
-// the even code; saturating at 6).  A tie at a midpoint goes up exactly
-// when the lower code is odd.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-    const float a = fabsf(v);
-    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return sum4_rows(v);
 }
 
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-    const float lv[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
-    const float x = lv[code & 7u];
-    return (code & 8u) ? -x : x;
+// ---------------------------------------------------------------- loads / stores
+
+// CPL channels of one token row, raw (bf16 pairs or float32 words).
+template <int CPL, bool BF>
+struct RawCh {
+    uint32_t w[BF ? CPL / 2 : CPL];
+};
+
+template <int CPL, bool BF>
+__device__ __forceinline__ void load_raw(const uint8_t* base, size_t elem, RawCh<CPL, BF>& r) {
+    constexpr int NW = BF ? CPL / 2 : CPL;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(base + elem * (BF ? 2 : 4));
+    if constexpr (NW >= 4) {
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k) {
+            const u32x4 v = reinterpret_cast<const u32x4*>(q)[k];
+            r.w[4 * k] = v[0];
+            r.w[4 * k + 1] = v[1];
+            r.w[4 * k + 2] = v[2];
+            r.w[4 * k + 3] = v[3];
+        }
+    } else if constexpr (NW == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(q);
+        r.w[0] = v[0];
+        r.w[1] = v[1];
+    } else {
+        r.w[0] = q[0];
+    }
 }
 
-// Largest |x| over aligned groups of `lanes` neighbouring lanes (a power of 2).
-__device__ __forceinline__ float group_max(float a, int lanes) {
-    for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, shfl_xor_f(a, o));
-    return a;
+template <int CPL, bool BF>
+__device__ __forceinline__ float raw_at(const RawCh<CPL, BF>& r, int j) {
+    if constexpr (BF) return __uint_as_float((j & 1) ? (r.w[j >> 1] & 0xFFFF0000u) : (r.w[j >> 1] << 16));
+    else return __uint_as_float(r.w[j]);
 }
 
-template <int CPL>
-__global__ __launch_bounds__(kCThreads) void compress_kernel(CompP p) {
-    extern __shared__ __align__(16) float csh[];
-    float* xs = csh;                               // [16][D] stored rows' values
-    float* ks = csh + kRecPerWG * p.D;             // [16][Di] keys before quantization
+// NB bytes (a power of two, the packed words w) to a naturally aligned address.
+template <int NB>
+__device__ __forceinline__ void st_bytes(uint8_t* dst, const uint32_t* w) {
+    if constexpr (NB == 1) {
+        *dst = static_cast<uint8_t>(w[0]);
+    } else if constexpr (NB == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
+    } else if constexpr (NB == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = w[0];
+    } else if constexpr (NB == 8) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < NB / 16; ++k)
+            reinterpret_cast<u32x4*>(dst)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    }
+}
+
+// ---------------------------------------------------------------- records
+
+template <int CPL, bool BF>
+__global__ __launch_bounds__(kPoolWaves * 64) void pool_kernel(CompP p) {
+    __shared__ double inv_sh[kMaxRopePairs];
+    constexpr int D = CPL * 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int b = blockIdx.y;
+    const int64_t t0 = p.t0[b];
+    if (t0 < 0) return;  // nothing of this sequence is written (workgroup-uniform)
+    const int64_t s0 = t0 / p.m;
+    const int n_rec = p.T / p.m;
+    const int npairs = p.rope_dims / 2;
+    const int r0 = D - p.rope_dims;
+    const int d0 = CPL * lane;
+    for (int j = tid; j < npairs; j += kPoolWaves * 64) inv_sh[j] = rope_inv_freq(j, p.rope_dims, p.rope_base);
+    __syncthreads();
+    float gain[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) gain[j] = p.gain[d0 + j];
+
+    for (int k = 0; k < kPoolRecPerWave; ++k) {
+        const int s = blockIdx.x * kPoolRecPerWG + k * kPoolWaves + wave;
+        if (s >= n_rec || s0 + s >= p.N_out) break;  // wave-uniform; s grows with k
+        // ---- channel-wise softmax pooling over the block's m tokens, four at a time
+        float mx[CPL], sm[CPL], ac[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            mx[j] = -__builtin_huge_valf();
+            sm[j] = 0.f;
+            ac[j] = 0.f;
+        }
+        const size_t row0 = (static_cast<size_t>(b) * p.T + static_cast<size_t>(s) * p.m) * D + d0;
+        // weights 2^(z log2(e) - max log2(e)); the running sums are rescaled
+        // when a later group of tokens raises the maximum
+        constexpr float kL2E = 1.4426950408889634f;
+        auto tokens = [&](int i0, auto nt_c, auto first_c) {
+            constexpr int NT = decltype(nt_c)::value;
+            constexpr bool kFirst = decltype(first_c)::value;
+            RawCh<CPL, BF> cr[NT], zr[NT];
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                load_raw(p.c, row0 + static_cast<size_t>(i0 + u) * D, cr[u]);
+                load_raw(p.z, row0 + static_cast<size_t>(i0 + u) * D, zr[u]);
+            }
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                float nm = mx[j];
+#pragma unroll
+                for (int u = 0; u < NT; ++u) nm = fmaxf(nm, raw_at(zr[u], j));
+                const float nml = nm * kL2E;
+                float sa = 0.f, aa = 0.f;
+                if constexpr (!kFirst) {
+                    const float sc = __builtin_amdgcn_exp2f(fmaf(mx[j], kL2E, -nml));
+                    sa = sm[j] * sc;
+                    aa = ac[j] * sc;
+                }
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(raw_at(zr[u], j), kL2E, -nml));
+                    sa += e;
+                    aa = fmaf(e, raw_at(cr[u], j), aa);
+                }
+                mx[j] = nm;
+                sm[j] = sa;
+                ac[j] = aa;
+            }
+        };
+        using Four = std::integral_constant<int, 4>;
+        using One = std::integral_constant<int, 1>;
+        int i0 = 0;
+        if (p.m >= 4) {
+            tokens(0, Four{}, std::true_type{});
+            for (i0 = 4; i0 + 4 <= p.m; i0 += 4) tokens(i0, Four{}, std::false_type{});
+        } else {
+            tokens(0, One{}, std::true_type{});
+            i0 = 1;
+        }
+        for (; i0 < p.m; ++i0) tokens(i0, One{}, std::false_type{});
+        // ---- RMSNorm
+        float x[CPL];
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            x[j] = ac[j] * __builtin_amdgcn_rcpf(sm[j]);
+            ss = fmaf(x[j], x[j], ss);
+        }
+        ss = wave_sum(ss);
+        const float rn = rsqrtf(ss / static_cast<float>(D) + p.eps);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) x[j] *= rn * gain[j];
+        // ---- RoPE at the block's last token: lane l computes pair 64*q + l,
+        // the owners of each pair's two channels fetch its cos / sin
+        const int64_t pos = t0 + static_cast<int64_t>(s) * p.m + p.m - 1;
+        for (int q = 0; 64 * q < npairs; ++q) {
+            float cs = 1.f, sn = 0.f;
+            if (64 * q + lane < npairs) rope_cos_sin(pos, inv_sh[64 * q + lane], cs, sn);
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2) {
+                const int src = ((d0 + j - r0) >> 1) - 64 * q;  // lane holding this pair's angle now
+                const float c2 = __shfl(cs, src & 63, kWave);
+                const float s2 = __shfl(sn, src & 63, kWave);
+                if (d0 + j >= r0 && src >= 0 && src < 64) {
+                    const float a = x[j], bb = x[j + 1];
+                    x[j] = a * c2 - bb * s2;
+                    x[j + 1] = a * s2 + bb * c2;
+                }
+            }
+        }
+        // ---- quantize and store the cache row
+        const size_t ci = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + s);
+        if (p.kv_dt == DT_F32) {
+            uint32_t w[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) w[j] = __float_as_uint(x[j]);
+            st_bytes<4 * CPL>(p.kv + (ci * D + d0) * 4, w);
+        } else if (p.kv_dt == DT_BF16) {
+            uint32_t w[CPL / 2];
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2) w[j / 2] = pack_bf16x2(x[j], x[j + 1]);
+            st_bytes<2 * CPL>(p.kv + (ci * D + d0) * 2, w);
+        } else if (p.kv_dt == DT_E4M3) {  // one scale per row: max|x| / 448
+            float am = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) am = fmaxf(am, fabsf(x[j]));
+            am = lanes_max<64>(am);
+            const float scl = am / 448.f;
+            const float inv = scl > 0.f ? 1.f / scl : 0.f;
+            uint32_t w[(CPL + 3) / 4] = {};
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2) w[j / 4] |= e4m3_encode2(x[j] * inv, x[j + 1] * inv) << (8 * (j % 4));
+            st_bytes<CPL>(p.kv + ci * D + d0, w);
+            if (lane == 0) p.kv_scale[ci] = scl;
+        } else {  // FP4 row: E2M1 codes, one E4M3 scale (nearest max|x| / 6) per 16 channels
+            uint8_t* row = p.kv + ci * (D / 2 + D / 16);
+            uint32_t w[(CPL + 7) / 8] = {};
+#pragma unroll
+            for (int gi = 0; gi < (CPL >= 16 ? CPL / 16 : 1); ++gi) {
+                constexpr int kGN = CPL >= 16 ? 16 : CPL;  // channels of the group in this lane
+                float ga = 0.f;
+#pragma unroll
+                for (int j = 0; j < kGN; ++j) ga = fmaxf(ga, fabsf(x[kGN * gi + j]));
+                if constexpr (CPL < 16) ga = lanes_max<16 / CPL>(ga);
+                const uint32_t scode = e4m3_encode(ga / 6.f);
+                const float scl = e4m3_to_f32(static_cast<uint8_t>(scode));
+                const float inv = scl > 0.f ? 1.f / scl : 0.f;
+#pragma unroll
+                for (int j = 0; j < kGN; j += 8) {  // up to 8 codes per word, 2 per conversion
+                    const int jj = kGN * gi + j;
+                    uint32_t wd = 0u;
+                    wd = e2m1_encode2<0>(wd, x[jj] * inv, x[jj + 1] * inv);
+                    if constexpr (kGN >= 4) wd = e2m1_encode2<1>(wd, x[jj + 2] * inv, x[jj + 3] * inv);
+                    if constexpr (kGN >= 8) {
+                        wd = e2m1_encode2<2>(wd, x[jj + 4] * inv, x[jj + 5] * inv);
+                        wd = e2m1_encode2<3>(wd, x[jj + 6] * inv, x[jj + 7] * inv);
+                    }
+                    w[jj / 8] = wd;
+                }
+                const int ch = d0 + kGN * gi;
+                if (ch % 16 == 0) row[D / 2 + ch / 16] = static_cast<uint8_t>(scode);
+            }
+            st_bytes<CPL / 2>(row + d0 / 2, w);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- keys
+
+// Raw A-operand data of one lane for one 64-channel chunk: its record's
+// channels gw*g + 16c .. +15 in the stored format.
+template <int RDT>
+struct RawA {
+    uint32_t w[RDT == DT_F32 ? 16 : (RDT == DT_BF16 ? 8 : (RDT == DT_E4M3 ? 4 : 3))];
+};
+
+template <int RDT>
+__device__ __forceinline__ void load_a(const CompP& p, size_t ci, int ch, bool rv, RawA<RDT>& a) {
+    constexpr int NW = sizeof(a.w) / 4;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) a.w[i] = 0u;
+    if (!rv) return;
+    const int D = p.D;
+    if constexpr (RDT == DT_FP4) {
+        const uint8_t* row = p.kv + ci * (D / 2 + D / 16);
+        const u32x2 codes = *reinterpret_cast<const u32x2*>(row + ch / 2);
+        a.w[0] = codes[0];
+        a.w[1] = codes[1];
+        a.w[2] = row[D / 2 + ch / 16];
+    } else {
+        constexpr int EB = RDT == DT_F32 ? 4 : (RDT == DT_BF16 ? 2 : 1);
+        const u32x4* q = reinterpret_cast<const u32x4*>(p.kv + (ci * D + ch) * EB);
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k) {
+            const u32x4 v = q[k];
+            a.w[4 * k] = v[0];
+            a.w[4 * k + 1] = v[1];
+            a.w[4 * k + 2] = v[2];
+            a.w[4 * k + 3] = v[3];
+        }
+    }
+}
+
+// The chunk's two k-steps as bf16 operands (hi; lo only for float32 rows).
+template <int RDT>
+__device__ __forceinline__ void a_operands(const RawA<RDT>& a, bf16x8 (&ah)[2], bf16x8 (&al)[2]) {
+    if constexpr (RDT == DT_FP4) {
+        const float scl = e4m3_to_f32(static_cast<uint8_t>(a.w[2]));
+        ah[0] = as_bf16x8(fp4x8_to_bf16x8(a.w[0], scl));
+        ah[1] = as_bf16x8(fp4x8_to_bf16x8(a.w[1], scl));
+    } else if constexpr (RDT == DT_E4M3) {  // codes; the row scale multiplies the keys
+        ah[0] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{a.w[0], a.w[1]}));
+        ah[1] = as_bf16x8(e4m3x8_to_bf16x8(u32x2{a.w[2], a.w[3]}));
+    } else if constexpr (RDT == DT_BF16) {
+        ah[0] = as_bf16x8(u32x4{a.w[0], a.w[1], a.w[2], a.w[3]});
+        ah[1] = as_bf16x8(u32x4{a.w[4], a.w[5], a.w[6], a.w[7]});
+    } else {  // float32 rows: x = hi + lo
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = __uint_as_float(a.w[8 * h + 2 * e]), x1 = __uint_as_float(a.w[8 * h + 2 * e + 1]);
+                hi[e] = cvt_bf16x2(x0, x1);
+                lo[e] = cvt_bf16x2(x0 - __uint_as_float(hi[e] << 16), x1 - __uint_as_float(hi[e] & 0xFFFF0000u));
+            }
+            ah[h] = as_bf16x8(hi);
+            al[h] = as_bf16x8(lo);
+        }
+    }
+}
+
+// Records written for sequence b: local ids 0 .. n_w-1 (cache rows s0 + s).
+// One workgroup: 64 records x all Di keys; wave w takes records
+// 32*(w & 1) .. +31 (two 16-row operand tiles) and key columns of half
+// (w >> 1), so each B operand read from LDS feeds two products.  Per
+// 64-channel chunk c, W_ik rows gw*g' + 16c + i (g' = 0..3, i = 0..15) sit
+// transposed in LDS column 16g' + i, high and low bf16 parts,
+// double-buffered: the next chunk's W_ik and record data are loaded into
+// registers before this chunk's products, so one barrier per chunk
+// separates a buffer's writes from its reads.
+template <int RDT, int NT, bool WF32>
+__global__ __launch_bounds__(256) void keys_kernel(CompP p) {
+    extern __shared__ __align__(16) uint8_t ksh[];
+    constexpr int Di = NT * 16;
+    constexpr int NH = NT / 2;                            // column tiles per wave
+    constexpr int kBuf = 2 * Di * kWPitch;                // bf16 per buffer: hi then lo
+    uint16_t* wsh = reinterpret_cast<uint16_t*>(ksh);      // [2 buffers][hi, lo][Di][kWPitch]
+    float* kout = reinterpret_cast<float*>(ksh);           // [64][Di + 4] keys, after the last chunk
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int b = blockIdx.y;
     const int D = p.D;
-    const int n_rec = p.T / p.m;
-    const int s_begin = blockIdx.x * kRecPerWG;
     const int64_t t0 = p.t0[b];
-    const int64_t s0 = t0 >= 0 ? t0 / p.m : -1;    // cache row of the first record
-    const int r0 = D - p.rope_dims;
-    const int d0 = CPL * lane;
+    if (t0 < 0) return;
+    const int64_t s0 = t0 / p.m;
+    const int n_rec = p.T / p.m;
+    const int n_w = static_cast<int>(min(static_cast<int64_t>(n_rec), static_cast<int64_t>(p.N_out) - s0));
+    const int s_base = blockIdx.x * kKeyRows;
+    if (s_base >= n_w) return;  // workgroup-uniform
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int rbase = 32 * (wave & 1);  // first of this wave's rows within the workgroup
+    const int t_lo = NH * (wave >> 1);  // first of this wave's column tiles
+    bool rv[2];
+    size_t ci[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int s = s_base + rbase + 16 * a + r;  // this lane's record in operand tile a
+        rv[a] = s < n_w;
+        ci[a] = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + (rv[a] ? s : 0));
+    }
+    const int gw = D / 4;  // channels of each lane group
+    const int nch = D / 64;
 
-    // ---- records: pool, normalize, rotate, quantize, store ----
-    for (int rr = wave; rr < kRecPerWG; rr += 4) {
-        const int s = s_begin + rr;
-        if (s >= n_rec) break;  // wave-uniform
-        float mx[CPL], sum[CPL], acc[CPL];
+    // W_ik staging: item (dq, jq) = 4 consecutive staged columns 4dq .. 4dq+3
+    // (one 16-row run of W_ik) x keys 4jq .. 4jq+3; Di / 64 items per thread
+    constexpr int kWI = Di / 64;
+    f32x4 wr[kWI][4];
+    auto load_w = [&](int c) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            mx[j] = -__builtin_huge_valf();
-            sum[j] = 0.f;
-            acc[j] = 0.f;
-        }
-#pragma unroll 4
-        for (int i = 0; i < p.m; ++i) {  // online softmax over the block's tokens
-            const size_t row = (static_cast<size_t>(b) * p.T + static_cast<size_t>(s) * p.m + i) * D + d0;
+        for (int it = 0; it < kWI; ++it) {
+            const int idx = tid + 256 * it;
+            const int dq = idx & 15, jq = idx >> 4;
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const float cv = ld_in(p.c, row + j, p.in_dt);
-                const float zv = ld_in(p.z, row + j, p.in_dt);
-                const float nm = fmaxf(mx[j], zv);
-                const float sc = __expf(mx[j] - nm);
-                const float e = __expf(zv - nm);
-                sum[j] = sum[j] * sc + e;
-                acc[j] = acc[j] * sc + e * cv;
-                mx[j] = nm;
-            }
-        }
-        float x[CPL];
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            x[j] = acc[j] / sum[j];
-            ss += x[j] * x[j];
-        }
-        ss = warp_sum(ss);
-        const float inv = rsqrtf(ss / static_cast<float>(D) + p.eps);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) x[j] *= inv * p.gain[d0 + j];
-        // forward rotation of the rotary pairs to the record's position
-        const int64_t pos = t0 + static_cast<int64_t>(s) * p.m + p.m - 1;
-#pragma unroll
-        for (int j = 0; j < CPL; j += 2) {
-            const int d = d0 + j;
-            if (d >= r0) {
-                float cs, sn;
-                rope_angle(pos, (d - r0) >> 1, p.rope_dims, p.rope_base, cs, sn);
-                const float a = x[j], bb = x[j + 1];
-                x[j] = a * cs - bb * sn;
-                x[j + 1] = a * sn + bb * cs;
-            }
-        }
-        // quantize into the cache row; xs keeps the stored values
-        const int64_t crow = s0 + s;
-        const bool in_cache = s0 >= 0 && crow < p.N_out;
-        const size_t ci = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(crow);
-        float xq[CPL];
-        if (p.kv_dt == DT_F32 || p.kv_dt == DT_BF16) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                if (p.kv_dt == DT_BF16) {
-                    const uint32_t hb = f32_to_bf16_rne(x[j]);
-                    xq[j] = __uint_as_float(hb << 16);
-                    if (in_cache) reinterpret_cast<uint16_t*>(p.kv)[ci * D + d0 + j] = static_cast<uint16_t>(hb);
+            for (int i = 0; i < 4; ++i) {
+                const int dl = 4 * dq + i;
+                const size_t d = static_cast<size_t>(gw * (dl >> 4) + 16 * c + (dl & 15));
+                if constexpr (WF32) {
+                    wr[it][i] = *reinterpret_cast<const f32x4*>(p.w + (d * Di + 4 * jq) * 4);
                 } else {
-                    xq[j] = x[j];
-                    if (in_cache) reinterpret_cast<float*>(p.kv)[ci * D + d0 + j] = x[j];
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(p.w + (d * Di + 4 * jq) * 2);
+                    wr[it][i] = f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                                      __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
                 }
-            }
-        } else if (p.kv_dt == DT_E4M3) {  // one scale per row: max|x| / 448
-            float am = 0.f;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) am = fmaxf(am, fabsf(x[j]));
-            am = warp_max(am);
-            const float scl = am / 448.f;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const uint32_t code = scl > 0.f ? e4m3_encode(x[j] / scl) : 0u;
-                xq[j] = e4m3_to_f32(static_cast<uint8_t>(code)) * scl;
-                if (in_cache) p.kv[ci * D + d0 + j] = static_cast<uint8_t>(code);
-            }
-            if (in_cache && lane == 0) p.kv_scale[ci] = scl;
-        } else {  // FP4 row: E2M1 codes, one E4M3 scale (max|x| / 6) per 16 channels
-            constexpr int kGL = CPL >= 16 ? 1 : 16 / CPL;  // lanes per group
-            float am = 0.f;
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) am = fmaxf(am, fabsf(x[j]));
-            const size_t rb = static_cast<size_t>(D) / 2 + D / 16;  // row bytes
-            uint8_t* row = p.kv + ci * rb;
-#pragma unroll
-            for (int gsub = 0; gsub < (CPL >= 16 ? CPL / 16 : 1); ++gsub) {
-                float ga = 0.f;
-                if constexpr (CPL >= 16) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) ga = fmaxf(ga, fabsf(x[16 * gsub + j]));
-                } else {
-                    ga = group_max(am, kGL);
-                }
-                const uint32_t scode = e4m3_encode(ga / 6.f);
-                const float scl = e4m3_to_f32(static_cast<uint8_t>(scode));
-                const int jb = CPL >= 16 ? 16 * gsub : 0;
-                const int je = CPL >= 16 ? jb + 16 : CPL;
-                for (int j = jb; j < je; j += 2) {
-                    const uint32_t c0 = scl > 0.f ? e2m1_encode(x[j] / scl) : 0u;
-                    const uint32_t c1 = scl > 0.f ? e2m1_encode(x[j + 1] / scl) : 0u;
-                    xq[j] = e2m1_value(c0) * scl;
-                    xq[j + 1] = e2m1_value(c1) * scl;
-                    if (in_cache) row[(d0 + j) / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
-                }
-                const int grp = (d0 + jb) / 16;
-                if (in_cache && (d0 + jb) % 16 == 0) row[D / 2 + grp] = static_cast<uint8_t>(scode);
             }
         }
+    };
+    auto store_w = [&](int buf) {
+        uint16_t* hi = wsh + buf * kBuf;
+        uint16_t* lo = hi + Di * kWPitch;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) xs[rr * D + d0 + j] = xq[j];
+        for (int it = 0; it < kWI; ++it) {
+            const int idx = tid + 256 * it;
+            const int dq = idx & 15, jq = idx >> 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int off = (4 * jq + e) * kWPitch + 4 * dq;
+                uint32_t h[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) h[i] = cvt_bf16x2(wr[it][2 * i][e], wr[it][2 * i + 1][e]);
+                *reinterpret_cast<u32x2*>(hi + off) = u32x2{h[0], h[1]};
+                if constexpr (WF32) {  // low parts: w - hi, exact in float32, rounded to bf16
+                    uint32_t l[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        l[i] = cvt_bf16x2(wr[it][2 * i][e] - __uint_as_float(h[i] << 16),
+                                          wr[it][2 * i + 1][e] - __uint_as_float(h[i] & 0xFFFF0000u));
+                    *reinterpret_cast<u32x2*>(lo + off) = u32x2{l[0], l[1]};
+                }
+            }
+        }
+    };
+
+    f32x4 acc[2][NH];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < NH; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    RawA<RDT> araw[2];
+    load_w(0);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) load_a<RDT>(p, ci[a], gw * g, rv[a], araw[a]);
+    store_w(0);
+    for (int c = 0; c < nch; ++c) {
+        bf16x8 ah[2][2], al[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) a_operands<RDT>(araw[a], ah[a], al[a]);
+        if (c + 1 < nch) {
+            load_w(c + 1);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) load_a<RDT>(p, ci[a], gw * g + 16 * (c + 1), rv[a], araw[a]);
+        }
+        __syncthreads();  // buffer c % 2 written by every wave; buffer (c + 1) % 2 no longer read
+        const uint16_t* hi = wsh + (c & 1) * kBuf;
+        const uint16_t* lo = hi + Di * kWPitch;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+            for (int t = 0; t < NH; ++t) {
+                const int off = (16 * (t_lo + t) + r) * kWPitch + 16 * g + 8 * q;
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(hi + off);
+                bf16x8 bl;
+                if constexpr (WF32) bl = *reinterpret_cast<const bf16x8*>(lo + off);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    acc[a][t] = mfma16x16x32(ah[a][q], bh, acc[a][t]);
+                    if constexpr (WF32) acc[a][t] = mfma16x16x32(ah[a][q], bl, acc[a][t]);
+                    if constexpr (RDT == DT_F32) acc[a][t] = mfma16x16x32(al[a][q], bh, acc[a][t]);
+                }
+            }
+        }
+        if (c + 1 < nch) store_w((c + 1) & 1);
+    }
+    // keys of rows rbase + 16a + 4g + v, columns 16(t_lo + t) + r -> LDS
+    constexpr int kp = Di + 4;
+    float rs[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            rs[a][v] = 1.f;
+            if constexpr (RDT == DT_E4M3) {
+                const int sv = s_base + rbase + 16 * a + 4 * g + v;
+                rs[a][v] = sv < n_w ? p.kv_scale[static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + sv)]
+                                    : 0.f;
+            }
+        }
     }
     __syncthreads();
-
-    // ---- keys: k = x_stored W_ik, float32 ----
-    const int nr = min(kRecPerWG, n_rec - s_begin);
-    for (int j = tid % p.Di, half = tid / p.Di; half * 8 < kRecPerWG; half += kCThreads / p.Di) {
-        if (tid >= (kCThreads / p.Di) * p.Di) break;
-        float a[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) a[r] = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < D; ++d) {
-            const float w = ld_in(p.w, static_cast<size_t>(d) * p.Di + j, p.w_dt);
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int r = 0; r < 8; ++r) a[r] = fmaf(xs[(half * 8 + r) * D + d], w, a[r]);
-        }
+        for (int t = 0; t < NH; ++t)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) ks[(half * 8 + r) * p.Di + j] = a[r];
-    }
+            for (int v = 0; v < 4; ++v)
+                kout[(rbase + 16 * a + 4 * g + v) * kp + 16 * (t_lo + t) + r] = acc[a][t][v] * rs[a][v];
     __syncthreads();
 
-    // ---- quantize the keys: one wave per record ----
-    const int kpl = p.Di / 64;  // key dims per lane (Di is a multiple of 64, <= 256)
-    for (int rr = wave; rr < nr; rr += 4) {
-        const int64_t crow = s0 + s_begin + rr;
-        if (s0 < 0 || crow >= p.N_out) continue;
-        const size_t ci = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(crow);
-        float v[4];
-        for (int j = 0; j < kpl; ++j) v[j] = ks[rr * p.Di + kpl * lane + j];
+    // ---- quantize the keys: one wave per record, lane l owns dims kpl*l ..
+    constexpr int kpl = Di / 64;
+    for (int rr = wave; rr < kKeyRows; rr += 4) {
+        const int sr = s_base + rr;
+        if (sr >= n_w) break;
+        const size_t cr = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + sr);
+        float v[kpl];
+#pragma unroll
+        for (int j = 0; j < kpl; ++j) v[j] = kout[rr * kp + kpl * lane + j];
         const int kd = kpl * lane;
         if (p.k_dt == DT_F32) {
-            for (int j = 0; j < kpl; ++j) reinterpret_cast<float*>(p.k)[ci * p.Di + kd + j] = v[j];
+#pragma unroll
+            for (int j = 0; j < kpl; ++j) reinterpret_cast<float*>(p.k)[cr * Di + kd + j] = v[j];
         } else if (p.k_dt == DT_BF16) {
+#pragma unroll
             for (int j = 0; j < kpl; ++j)
-                reinterpret_cast<uint16_t*>(p.k)[ci * p.Di + kd + j] = static_cast<uint16_t>(f32_to_bf16_rne(v[j]));
+                reinterpret_cast<uint16_t*>(p.k)[cr * Di + kd + j] = static_cast<uint16_t>(f32_to_bf16_rne(v[j]));
         } else if (p.k_dt == DT_E4M3) {
             float am = 0.f;
+#pragma unroll
             for (int j = 0; j < kpl; ++j) am = fmaxf(am, fabsf(v[j]));
-            am = warp_max(am);
+            am = lanes_max<64>(am);
             const float scl = am / 448.f;
-            for (int j = 0; j < kpl; ++j)
-                p.k[ci * p.Di + kd + j] = static_cast<uint8_t>(scl > 0.f ? e4m3_encode(v[j] / scl) : 0u);
-            if (lane == 0) reinterpret_cast<float*>(p.k_scale)[ci] = scl;
-        } else {  // MXFP4: blocks of 32 dims share 2^e, e = floor(log2 max|x|) - 2
+            const float inv = scl > 0.f ? 1.f / scl : 0.f;
+#pragma unroll
+            for (int j = 0; j < kpl; ++j) p.k[cr * Di + kd + j] = static_cast<uint8_t>(e4m3_encode(v[j] * inv));
+            if (lane == 0) reinterpret_cast<float*>(p.k_scale)[cr] = scl;
+        } else if constexpr (kpl % 2 == 0) {  // MXFP4: blocks of 32 dims share 2^e, e = floor(log2 max|x|) - 2
             float am = 0.f;
+#pragma unroll
             for (int j = 0; j < kpl; ++j) am = fmaxf(am, fabsf(v[j]));
-            am = group_max(am, 32 / kpl);
+            am = lanes_max<32 / kpl>(am);
             int e = -127;
             if (am > 0.f) {
                 const int be = static_cast<int>((__float_as_uint(am) >> 23) & 0xFFu);
                 e = (be == 0 ? -127 : be - 127) - 2;
                 e = e < -127 ? -127 : (e > 127 ? 127 : e);
             }
-            const float inv = ldexpf(1.f, -e);
-            uint8_t* krow = p.k + ci * (p.Di / 2);
-            for (int j = 0; j < kpl; j += 2) {
-                const uint32_t c0 = e2m1_encode(v[j] * inv);
-                const uint32_t c1 = e2m1_encode(v[j + 1] * inv);
-                krow[(kd + j) / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
-            }
-            if (kd % 32 == 0) p.k_scale[ci * (p.Di / 32) + kd / 32] = static_cast<uint8_t>(e + 127);
+            const float inv = __builtin_amdgcn_ldexpf(1.f, -e);
+            uint32_t w[1] = {e2m1_encode2<0>(0u, v[0] * inv, v[1] * inv)};
+            if constexpr (kpl == 4) w[0] = e2m1_encode2<1>(w[0], v[2] * inv, v[3] * inv);
+            st_bytes<kpl / 2>(p.k + cr * (Di / 2) + kd / 2, w);
+            if (kd % 32 == 0) p.k_scale[cr * (Di / 32) + kd / 32] = static_cast<uint8_t>(e + 127);
         }
     }
 }
@@ -311,15 +645,46 @@ int launch_compress(const CompressArgs& a, void* stream) {
     p.k_scale = static_cast<uint8_t*>(a.k_scale);
     p.k_dt = a.k_dtype;
     const int n_rec = a.T / a.m;
-    const dim3 grid((n_rec + kRecPerWG - 1) / kRecPerWG, a.B);
-    const size_t lds = static_cast<size_t>(kRecPerWG) * (a.D + a.Di) * sizeof(float);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 pgrid((n_rec + kPoolRecPerWG - 1) / kPoolRecPerWG, a.B);
+    const dim3 pblk(kPoolWaves * 64);
+    const bool bf = a.in_dtype == DT_BF16;
+#define CSA2_POOL(C)                                                                     \
+    if (bf) hipLaunchKernelGGL((pool_kernel<C, true>), pgrid, pblk, 0, st, p);            \
+    else hipLaunchKernelGGL((pool_kernel<C, false>), pgrid, pblk, 0, st, p);
     switch (a.D / 64) {
-        case 2: hipLaunchKernelGGL(compress_kernel<2>, grid, dim3(kCThreads), lds, st, p); break;
-        case 4: hipLaunchKernelGGL(compress_kernel<4>, grid, dim3(kCThreads), lds, st, p); break;
-        case 8: hipLaunchKernelGGL(compress_kernel<8>, grid, dim3(kCThreads), lds, st, p); break;
-        default: hipLaunchKernelGGL(compress_kernel<16>, grid, dim3(kCThreads), lds, st, p); break;
+        case 2: CSA2_POOL(2) break;
+        case 4: CSA2_POOL(4) break;
+        case 8: CSA2_POOL(8) break;
+        default: CSA2_POOL(16) break;
     }
+#undef CSA2_POOL
+    if (int e = static_cast<int>(hipGetLastError())) return e;
+    const dim3 kgrid((n_rec + kKeyRows - 1) / kKeyRows, a.B);
+    const size_t wbytes = static_cast<size_t>(4) * a.Di * kWPitch * sizeof(uint16_t);
+    const size_t obytes = static_cast<size_t>(kKeyRows) * (a.Di + 4) * sizeof(float);
+    const size_t lds = wbytes > obytes ? wbytes : obytes;
+#define CSA2_KEYS_W(R, W)                                                                             \
+    switch (a.Di / 16) {                                                                              \
+        case 4: hipLaunchKernelGGL((keys_kernel<R, 4, W>), kgrid, dim3(256), lds, st, p); break;      \
+        case 8: hipLaunchKernelGGL((keys_kernel<R, 8, W>), kgrid, dim3(256), lds, st, p); break;      \
+        case 12: hipLaunchKernelGGL((keys_kernel<R, 12, W>), kgrid, dim3(256), lds, st, p); break;    \
+        default: hipLaunchKernelGGL((keys_kernel<R, 16, W>), kgrid, dim3(256), lds, st, p); break;    \
+    }
+#define CSA2_KEYS(R)                  \
+    if (a.w_dtype == DT_F32) {        \
+        CSA2_KEYS_W(R, true)          \
+    } else {                          \
+        CSA2_KEYS_W(R, false)         \
+    }
+    switch (a.kv_dtype) {
+        case DT_F32: CSA2_KEYS(DT_F32) break;
+        case DT_BF16: CSA2_KEYS(DT_BF16) break;
+        case DT_E4M3: CSA2_KEYS(DT_E4M3) break;
+        default: CSA2_KEYS(DT_FP4) break;
+    }
+#undef CSA2_KEYS
+#undef CSA2_KEYS_W
     return static_cast<int>(hipGetLastError());
 }
 

@@ -5,7 +5,8 @@
 and workspace buffers, and enqueues the layers with ``csa2_layer`` in
 order: a Full layer (optionally building the block pool), Reindex layers
 searching that pool, Reuse layers reading the last index set, and HCA
-layers attending to every visible record.
+layers attending to every visible record.  ``DeviceCompress`` does the
+same for record construction (csa2_compress).
 """
 
 from __future__ import annotations
@@ -112,3 +113,55 @@ class DeviceGroup:
 
     def index_sets(self) -> List[Optional[np.ndarray]]:
         return [None if i is None else i.cpu().numpy() for i in self.idx]
+
+
+class DeviceCompress:
+    """One record-construction workload on a device: token rows, gain and
+    W_ik uploaded once, record and key caches (with their scales) allocated
+    in the workload's formats."""
+
+    _NP = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "fp4": np.uint8, "mxfp4": np.uint8}
+
+    def __init__(self, inputs: Dict, device: str = "cuda"):
+        cw = inputs["cw"]
+        self.cw = cw
+        B, n, D, Di = cw.B, cw.T // cw.m, cw.D, cw.Di
+        self.n_out = n
+        self.c = to_device(inputs["c"], device)
+        self.z = to_device(inputs["z"], device)
+        self.t0 = to_device(inputs["t0"], device)
+        self.gain = to_device(inputs["gain"], device)
+        self.w = to_device(inputs["w_ik"], device)
+        kv_w = D // 2 + D // 16 if cw.kv_dtype == "fp4" else D
+        k_w = Di // 2 if cw.k_dtype == "mxfp4" else Di
+        self.kv = to_device(np.zeros((B, n, kv_w), self._NP[cw.kv_dtype]), device,
+                            "fp4" if cw.kv_dtype == "fp4" else None)
+        self.k = to_device(np.zeros((B, n, k_w), self._NP[cw.k_dtype]), device,
+                           "mxfp4" if cw.k_dtype == "mxfp4" else None)
+        self.kv_scale = torch.zeros((B, n), dtype=torch.float32, device=device) if cw.kv_dtype == "e4m3" else None
+        self.k_scale = None
+        if cw.k_dtype == "e4m3":
+            self.k_scale = torch.zeros((B, n), dtype=torch.float32, device=device)
+        elif cw.k_dtype == "mxfp4":
+            self.k_scale = torch.zeros((B, n, Di // 32), dtype=torch.uint8, device=device).view(torch.float8_e8m0fnu)
+
+    def run(self, stream=None) -> None:
+        cw = self.cw
+        _b.csa2_compress(self.c, self.z, self.t0, self.gain, self.w, cw.m, self.kv, self.k,
+                        kv_scale=self.kv_scale, k_scale=self.k_scale, rope_dims=cw.rope_dims, stream=stream)
+
+    def fetch(self):
+        """(records, record scales, keys, key scales) as numpy storage arrays."""
+        cw = self.cw
+
+        def raw(t, fmt):
+            if t is None:
+                return None
+            if fmt == "f32":
+                return t.cpu().numpy()
+            return t.view(torch.uint8).cpu().numpy().view(self._NP[fmt])
+
+        ks = None if self.k_scale is None else (
+            self.k_scale.view(torch.uint8).cpu().numpy() if cw.k_dtype == "mxfp4" else self.k_scale.cpu().numpy())
+        return (raw(self.kv, cw.kv_dtype), None if self.kv_scale is None else self.kv_scale.cpu().numpy(),
+                raw(self.k, cw.k_dtype), ks)

@@ -110,3 +110,100 @@ def check_attn_query(gpu_out, shared, layer, b, ti, ids, kv_dtype, where=""):
     ref = oracle_attention(shared, layer, b, ti, ids)
     tol = attn_tol(kv_dtype, entry_rows(shared, layer, b, ti, ids))
     return check_attn(gpu_out, ref, tol, where), tol
+
+
+# ------------------------------------------------------------------ record construction
+
+def e4m3_half_step(v):
+    """Half the spacing of e4m3 values around |v| (subnormal spacing 2^-9)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 0.5 * np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+
+
+def bf16_half_ulp(v):
+    return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 8)
+
+
+def e2m1_half_step(v):
+    a = np.abs(v)
+    return 0.5 * np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+
+
+def check_rounding(got, exact, scale, half_step, where, sat=None):
+    """Every stored value is a nearest rounding of the exact one (within
+    half a step of the format at that magnitude, plus float32 noise);
+    values beyond the format's range saturate."""
+    g = np.asarray(got, np.float64)
+    x = np.asarray(exact, np.float64)
+    v = x / scale
+    tol = half_step(v) * scale * (1 + 1e-3) + 1e-6 * np.abs(x) + 1e-30
+    if sat is not None:
+        over = np.abs(v) > sat
+        tol = np.where(over, np.abs(x) - sat * scale + tol, tol)
+    bad = np.abs(g - x) > tol
+    assert not bad.any(), f"{where}: {bad.sum()} values off, worst {np.abs(g - x)[bad].max():.3g}"
+
+
+def check_compressed(kv_rows, kv_scale, k_rows, k_scale, x, w, kvf, kf, where=""):
+    """Stored records and keys of n records against the oracle's exact
+    records x [n][D] (before quantization) and W_ik w [D][Di].
+
+    float32 records match element by element; quantized ones (scales
+    included) are nearest roundings of x.  The keys are held to the exact
+    keys x @ W_ik, moved by at most what the record rounding (eb, bounded
+    from the oracle's values alone) and float32 accumulation allow, plus
+    their own format's rounding."""
+    n, D = x.shape
+    Di = w.shape[1]
+    w64 = np.asarray(w, np.float64)
+    # eb: how far a correct storage of x may lie from x
+    if kvf == "f32":
+        got = np.asarray(kv_rows, np.float64)
+        eb = np.full_like(x, 2e-5 * np.abs(x).max())
+        assert np.all(np.abs(got - x) <= eb), f"{where} f32 records"
+    elif kvf == "bf16":
+        eb = bf16_half_ulp(x) * (1 + 1e-3) + 1e-6 * np.abs(x)
+        check_rounding(O.dequant(kv_rows), x, 1.0, bf16_half_ulp, f"{where} bf16 records")
+    elif kvf == "e4m3":
+        so = np.abs(x).max(1) / 448
+        assert np.allclose(kv_scale, so, rtol=1e-5), f"{where} e4m3 record scales"
+        eb = e4m3_half_step(x / so[:, None]) * so[:, None] * (1 + 1e-3) + 1e-6 * np.abs(x)
+        check_rounding(O.dequant(kv_rows, kv_scale), x, so[:, None], e4m3_half_step, f"{where} e4m3 records")
+    else:
+        go = np.repeat(np.abs(x.reshape(n, D // 16, 16)).max(-1) / 6, 16, -1)  # exact group scales
+        hs = e4m3_half_step(go) * (1 + 1e-3) + 1e-7 * go
+        gs = np.repeat(O.decode_e4m3(kv_rows[:, D // 2:]), 16, -1)   # the stored ones
+        assert np.all(np.abs(gs - go) <= hs), f"{where} fp4 group scales"
+        # any scale within [go - hs, go + hs] may have been chosen: the largest steps
+        # and the earliest saturation bound the element error
+        eb = e2m1_half_step(x / (go - hs)) * (go + hs) * (1 + 1e-3) + np.maximum(0, np.abs(x) - 6 * (go - hs))
+        err = np.abs(O.dequant(kv_rows, None, "fp4") - x)
+        assert np.all(err <= eb + 1e-6 * np.abs(x)), f"{where} fp4 records: worst {(err - eb).max():.3g} over"
+    kexact = x @ w64
+    kb = eb @ np.abs(w64) + 1e-5 * (np.abs(x) @ np.abs(w64))
+    if kf == "f32":
+        assert np.all(np.abs(k_rows - kexact) <= kb), f"{where} f32 keys"
+    elif kf == "bf16":
+        err = np.abs(O.dequant(k_rows) - kexact)
+        assert np.all(err <= kb + bf16_half_ulp(kexact + np.sign(kexact) * kb) * (1 + 1e-3)), f"{where} bf16 keys"
+    elif kf == "e4m3":
+        so = np.abs(kexact).max(1) / 448
+        sk = kb.max(1) / 448
+        assert np.all(np.abs(k_scale - so) <= sk + 1e-5 * so), f"{where} e4m3 key scales"
+        smax = (so + sk + 1e-5 * so)[:, None]
+        err = np.abs(O.dequant(k_rows, k_scale) - kexact)
+        assert np.all(err <= kb + e4m3_half_step((np.abs(kexact) + kb) / smax) * smax * (1 + 1e-3)), \
+            f"{where} e4m3 keys"
+    else:
+        sc = O.decode_e8m0(k_scale)
+        amax = np.abs(kexact.reshape(n, Di // 32, 32)).max(-1)
+        amb = kb.reshape(n, Di // 32, 32).max(-1)
+        lo = 2.0 ** (np.floor(np.log2(np.maximum(amax - amb, 1e-30))) - 2)
+        hi = 2.0 ** (np.floor(np.log2(amax + amb)) - 2)
+        assert np.all((sc >= lo) & (sc <= hi)), f"{where} mxfp4 block scales"
+        s32 = np.repeat(sc, 32, -1)
+        err = np.abs(O.dequant_mxfp4(k_rows, k_scale) - kexact)
+        bound = kb + e2m1_half_step((np.abs(kexact) + kb) / s32) * s32 * (1 + 1e-3) + \
+            np.maximum(0, np.abs(kexact) + kb - 6 * s32)
+        assert np.all(err <= bound), f"{where} mxfp4 keys"

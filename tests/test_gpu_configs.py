@@ -1,4 +1,4 @@
-"""The five workloads at full size, in the launch configuration the
+"""The workloads at full size, in the launch configuration the
 benchmark times (one csa2_layer call per layer through DeviceGroup), plus
 unit-scale variants of the two decode shapes.
 
@@ -144,3 +144,27 @@ def test_config_full_size(cfg):
             prev = ids
     print(f"{cfg}: worst score rel err {worst_rel:.3g}, worst attention err / bound {worst:.3g}, "
           f"boundary set differences {nd}")
+
+
+def test_compress_full_size():
+    """Record construction at full size (16 sequences x 4096 tokens, m = 4,
+    FP4 records and MXFP4 keys), in the launch the benchmark times: sampled
+    records of three sequences (the first, middle and last 64 of each)
+    against the oracle's exact records and keys."""
+    print("[case] full-size C9 compress", flush=True)
+    cw = WL.COMPRESS["C9"]
+    inp = WL.make_compress_inputs(cw)
+    dc = R.DeviceCompress(inp)
+    dc.run()
+    torch.cuda.synchronize()
+    kv, kvs, k, ks = dc.fetch()
+    n = cw.T // cw.m
+    for b in (0, 7, 15):
+        for s0 in (0, n // 2 - 32, n - 64):
+            rows = slice(s0, s0 + 64)
+            tok = slice(s0 * cw.m, (s0 + 64) * cw.m)
+            x = O.compress_records(O.dequant(inp["c"][b][tok]), O.dequant(inp["z"][b][tok]), cw.m, inp["gain"],
+                                   1e-6, int(inp["t0"][b]) + s0 * cw.m, cw.rope_dims, 10000.0)
+            PR.check_compressed(kv[b][rows], None if kvs is None else kvs[b][rows], k[b][rows],
+                                None if ks is None else ks[b][rows], x, inp["w_ik"], cw.kv_dtype, cw.k_dtype,
+                                f"C9 b={b} records {s0}..{s0 + 63}")

@@ -823,37 +823,6 @@ def test_group_graph_replay():
 
 # ------------------------------------------------------------------ record construction
 
-def _e4m3_half_step(v):
-    """Half the spacing of e4m3 values around |v| (subnormal spacing 2^-9)."""
-    a = np.abs(v)
-    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
-    return 0.5 * np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
-
-
-def _bf16_half_ulp(v):
-    return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 8)
-
-
-def _e2m1_half_step(v):
-    a = np.abs(v)
-    return 0.5 * np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
-
-
-def _check_rounding(got, exact, scale, half_step, where, sat=None):
-    """Every stored value is a nearest rounding of the exact one (within
-    half a step of the format at that magnitude, plus float32 noise);
-    values beyond the format's range saturate."""
-    g = np.asarray(got, np.float64)
-    x = np.asarray(exact, np.float64)
-    v = x / scale
-    tol = half_step(v) * scale * (1 + 1e-3) + 1e-6 * np.abs(x) + 1e-30
-    if sat is not None:
-        over = np.abs(v) > sat
-        tol = np.where(over, np.abs(x) - sat * scale + tol, tol)
-    bad = np.abs(g - x) > tol
-    assert not bad.any(), f"{where}: {bad.sum()} values off, worst {np.abs(g - x)[bad].max():.3g}"
-
-
 @pytest.mark.parametrize("D,Di,T,m,idt,fmts", [
     (512, 128, 64, 4, "bf16", ("f32", "f32")),
     (512, 128, 40, 4, "bf16", ("bf16", "bf16")),
@@ -906,7 +875,6 @@ def test_compress_records_and_keys(D, Di, T, m, idt, fmts):
     k_g = kk.view(torch.uint8).cpu().numpy().view(npdt[kf]) if kf != "f32" else kk.cpu().numpy()
     kvs_g = None if kvs is None else kvs.cpu().numpy()
     ks_g = None if ks is None else ks.view(torch.uint8).cpu().numpy() if kf == "mxfp4" else ks.cpu().numpy()
-    w64 = w.astype(np.float64)
     for b in range(B):
         rows = slice(t0[b] // m, t0[b] // m + n)
         # untouched rows
@@ -914,56 +882,5 @@ def test_compress_records_and_keys(D, Di, T, m, idt, fmts):
         other[rows] = False
         assert np.array_equal(kv_g[b][other], kv0[b][other]) and np.array_equal(k_g[b][other], k0[b][other])
         x = O.compress_records(O.dequant(c_st[b]), O.dequant(z_st[b]), m, gain, eps, int(t0[b]), r, 10000.0)
-        # eb: how far a correct storage of x may lie from x (from the oracle's values only)
-        if kvf == "f32":
-            got = kv_g[b][rows].astype(np.float64)
-            eb = np.full_like(x, 2e-5 * np.abs(x).max())
-            assert np.all(np.abs(got - x) <= eb)
-        elif kvf == "bf16":
-            eb = _bf16_half_ulp(x) * (1 + 1e-3) + 1e-6 * np.abs(x)
-            _check_rounding(O.dequant(kv_g[b][rows]), x, 1.0, _bf16_half_ulp, f"b={b} bf16 records")
-        elif kvf == "e4m3":
-            so = np.abs(x).max(1) / 448
-            assert np.allclose(kvs_g[b][rows], so, rtol=1e-5)
-            eb = _e4m3_half_step(x / so[:, None]) * so[:, None] * (1 + 1e-3) + 1e-6 * np.abs(x)
-            _check_rounding(O.dequant(kv_g[b][rows], kvs_g[b][rows]), x, so[:, None], _e4m3_half_step,
-                            f"b={b} e4m3 records")
-        else:
-            go = np.repeat(np.abs(x.reshape(n, D // 16, 16)).max(-1) / 6, 16, -1)  # exact group scales
-            hs = _e4m3_half_step(go) * (1 + 1e-3) + 1e-7 * go
-            gs = np.repeat(O.decode_e4m3(kv_g[b][rows][:, D // 2:]), 16, -1)   # the stored ones
-            assert np.all(np.abs(gs - go) <= hs), f"b={b} fp4 group scales"
-            # any scale within [go - hs, go + hs] may have been chosen: the largest steps
-            # and the earliest saturation bound the element error
-            eb = _e2m1_half_step(x / (go - hs)) * (go + hs) * (1 + 1e-3) + np.maximum(0, np.abs(x) - 6 * (go - hs))
-            err = np.abs(O.dequant(kv_g[b][rows], None, "fp4") - x)
-            assert np.all(err <= eb + 1e-6 * np.abs(x)), f"b={b} fp4 records: worst {(err - eb).max():.3g} over"
-        # keys: the exact keys of the exact records, and how far the record
-        # rounding and float32 accumulation may move them
-        kexact = x @ w64
-        kb = eb @ np.abs(w64) + 1e-5 * (np.abs(x) @ np.abs(w64))
-        if kf == "f32":
-            assert np.all(np.abs(k_g[b][rows] - kexact) <= kb)
-        elif kf == "bf16":
-            err = np.abs(O.dequant(k_g[b][rows]) - kexact)
-            assert np.all(err <= kb + _bf16_half_ulp(kexact + np.sign(kexact) * kb) * (1 + 1e-3)), f"b={b} bf16 keys"
-        elif kf == "e4m3":
-            so = np.abs(kexact).max(1) / 448
-            sk = kb.max(1) / 448
-            assert np.all(np.abs(ks_g[b][rows] - so) <= sk + 1e-5 * so), f"b={b} e4m3 key scales"
-            smax = (so + sk + 1e-5 * so)[:, None]
-            err = np.abs(O.dequant(k_g[b][rows], ks_g[b][rows]) - kexact)
-            assert np.all(err <= kb + _e4m3_half_step((np.abs(kexact) + kb) / smax) * smax * (1 + 1e-3)), \
-                f"b={b} e4m3 keys"
-        else:
-            sc = O.decode_e8m0(ks_g[b][rows])
-            amax = np.abs(kexact.reshape(n, Di // 32, 32)).max(-1)
-            amb = kb.reshape(n, Di // 32, 32).max(-1)
-            lo = 2.0 ** (np.floor(np.log2(np.maximum(amax - amb, 1e-30))) - 2)
-            hi = 2.0 ** (np.floor(np.log2(amax + amb)) - 2)
-            assert np.all((sc >= lo) & (sc <= hi)), f"b={b} mxfp4 block scales"
-            s32 = np.repeat(sc, 32, -1)
-            err = np.abs(O.dequant_mxfp4(k_g[b][rows], ks_g[b][rows]) - kexact)
-            bound = kb + _e2m1_half_step((np.abs(kexact) + kb) / s32) * s32 * (1 + 1e-3) + \
-                np.maximum(0, np.abs(kexact) + kb - 6 * s32)
-            assert np.all(err <= bound), f"b={b} mxfp4 keys"
+        PR.check_compressed(kv_g[b][rows], None if kvs_g is None else kvs_g[b][rows], k_g[b][rows],
+                            None if ks_g is None else ks_g[b][rows], x, w, kvf, kf, f"b={b}")
