@@ -2,15 +2,16 @@
 
 The default run measures the Flash-shape prefill layer (1 sequence of 4096
 query tokens, m = 4 so 1024 records, indexer 32 x 128, Top-512, 64 heads x
-512 latent with 64 rotary dims, window 128, bf16) as ``value``, and the
-three decode workloads (Full decode at 64K context, hierarchical
-Full/Reindex/Reuse decode at 256K, fp8 decode at 1M, the heavily
-compressed (HCA) decode at 1M, the 1M decode in the V4.1 cache formats
-(FP4 main KV, MXFP4 indexer, FP8 window), and a multi-query decode that
-verifies 5 positions per sequence) and record construction (16 x 4096
-token rows into FP4 records and MXFP4 keys) in the same run, each
-reported in its own object under ``workloads``.  ``--workload`` picks
-another primary workload; ``--only`` skips the others.
+512 latent with 64 rotary dims, window 128, bf16, float32 output) as
+``value``.  The same run measures, each in its own object under
+``workloads``: that prefill layer with a bf16 output; the decode workloads
+(Full decode at 64K context, hierarchical Full/Reindex/Reuse decode at
+256K, fp8 decode at 1M, heavily compressed (HCA) decode at 1M, the 1M
+decode in the V4.1 cache formats (FP4 main KV, MXFP4 indexer, FP8
+window), and a multi-query decode that verifies 5 positions per
+sequence); and record construction (16 x 4096 token rows into FP4
+records and MXFP4 keys).  ``--workload`` picks another primary workload;
+``--only`` skips the others.
 
 A step is one pass of the whole hot path over the workload's batch: for
 every layer of its sharing group, indexer scores (Full / Reindex), block
@@ -54,7 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8", "C9"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
-    ap.add_argument("--extra", default="C3,C4,C5,C6,C7,C8,C9", help="further workloads measured in the same run")
+    ap.add_argument("--extra", default="C2b,C3,C4,C5,C6,C7,C8,C9", help="further workloads measured in the same run")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated between steps (0: 2 for decode, 1 for prefill)")
@@ -78,7 +79,7 @@ def entries_per_query(wl, inp):
     return sel, win, vis
 
 
-def kernel_work(wl, inp):
+def kernel_work(wl, inp, out_bf16=False):
     """Algorithmic bytes and flops per call of each step phase."""
     def row_bytes(n, dt):  # one stored row of n elements, with its scales
         return {"f32": 4 * n, "bf16": 2 * n, "e4m3": n + 4, "fp4": n // 2 + n // 16, "mxfp4": n // 2 + n // 32}[dt]
@@ -87,7 +88,7 @@ def kernel_work(wl, inp):
     wbytes = row_bytes(wl.D, wl.swa_dtype)
     qi_bytes = wl.Hi * row_bytes(wl.Di, wl.q_idx_dtype) + wl.Hi * 4
     q_bytes = wl.H * row_bytes(wl.D, wl.q_dtype)
-    out_bytes = wl.H * wl.D * 4
+    out_bytes = wl.H * wl.D * (2 if out_bf16 else 4)
     sel, win, vis = entries_per_query(wl, inp)
     rows = wl.B * wl.Tq
     work = {}
@@ -276,16 +277,22 @@ def traffic_for(workload, kernel):
 
 # --------------------------------------------------------------- one workload
 
+# workload variants: (base workload, attention output dtype)
+VARIANTS = {"C2b": ("C2", "bf16")}
+
+
 def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
     """Times `steps` steps of workload `key` and returns its report."""
     from sparse_long_context_csa2_amd import runner as R
     from sparse_long_context_csa2_amd import workloads as WL
 
-    wl = WL.CONFIGS[key]
+    base, odt = VARIANTS.get(key, (key, "f32"))
+    wl = WL.CONFIGS[base]
     inp = WL.make_inputs(wl)
     decode = wl.decode_pos is not None
     copies = copies or (2 if decode else 1)
-    grp = R.DeviceGroup(inp, device="cuda:0", copies=copies)
+    grp = R.DeviceGroup(inp, device="cuda:0", copies=copies,
+                        out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
     stream = torch.cuda.Stream()
     step = Step(grp, torch, stream)
     ncalls = len(step.calls)
@@ -333,7 +340,7 @@ def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
     ms_per_step = ms_graph if ms_graph is not None else ms_eager
     value = tokens / (ms_per_step * 1e-3)
 
-    work = kernel_work(wl, inp)
+    work = kernel_work(wl, inp, out_bf16=odt == "bf16")
     kern = {}
     for name, ts in per_call.items():
         ntimes = sum(1 for n, _ in step.calls if n == name)
@@ -369,12 +376,13 @@ def measure(key, steps, warmup, copies, cpu_seconds, torch, graph=False):
 
     cpu = cpu_baseline(inp, cpu_seconds) if cpu_seconds > 0 else None
     rep = {
-        "workload": wl.name, "value": round(value, 1), "unit": "query-tokens/s",
+        "workload": wl.name + ("-bf16-out" if odt == "bf16" else ""), "value": round(value, 1),
+        "unit": "query-tokens/s", "output_dtype": odt,
         "ms_per_step": round(ms_per_step, 4), "eager_ms_per_step": round(ms_eager, 4),
         "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 4),
         "steps": steps, "warmup": warmup,
         "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3+bf16", "fp4": "fp4+mxfp4+e4m3+bf16"}[wl.kv_dtype],
-        "config": {"workload": wl.name, "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
+        "config": {"workload": wl.name + ("-bf16-out" if odt == "bf16" else ""), "B": wl.B, "Tq": wl.Tq, "N": wl.N, "m": wl.m, "Hi": wl.Hi, "Di": wl.Di,
                    "H": wl.H, "D": wl.D, "K": wl.K, "W": wl.W, "blk": wl.blk, "P": wl.P,
                    "layers": list(wl.modes), "cache_copies": copies},
         "roofline": roof, "hbm": hbm, "cpu_baseline": cpu, "kernels": kern, "wall_s": round(wall, 3),
@@ -499,8 +507,9 @@ def main():
             if key in WL.COMPRESS:
                 rep = measure_compress(key, args.extra_steps, args.warmup, cpu_s, torch)
             else:
-                rep = measure(key, args.extra_steps, args.warmup, 0, cpu_s, torch,
-                              graph=WL.CONFIGS[key].decode_pos is not None)
+                base = VARIANTS.get(key, (key,))[0]
+                rep = measure(key, args.extra_steps, args.warmup, 0, 0 if key in VARIANTS else cpu_s, torch,
+                              graph=WL.CONFIGS[base].decode_pos is not None)
             extra[key] = rep
 
     line = {

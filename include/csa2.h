@@ -207,7 +207,9 @@ size_t csa2_topk_workspace_bytes(int rows, int ncols, int K);
  *   sm_scale   logit scale; 0 means 1/sqrt(D)
  *   rope_dims  even, 0..D; rope_base > 0
  * Output
- *   out        [B][Tq][H][D] float32
+ *   out        [B][Tq][H][D] in out_dtype: CSA2_F32, or CSA2_BF16 (the
+ *              float32 result rounded to nearest even; half the bytes of
+ *              the largest write of a prefill step)
  * Workspace: csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W).
  * ------------------------------------------------------------------------ */
 int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K,
@@ -217,7 +219,7 @@ int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K,
                      const void* swa, const float* swa_scale, int swa_dtype,
                      int S, int W, const int64_t* q_pos, const float* sink,
                      float sm_scale, int rope_dims, float rope_base,
-                     float* out, void* ws, size_t ws_bytes, void* stream);
+                     void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int W);
 
 /* ------------------------------------------------------------------------
@@ -240,7 +242,7 @@ size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int 
  *   N          records per sequence in kv; N + W <= 73728 for the 64x512
  *              kernels
  * Output
- *   out        [B][Tq][H][D] float32
+ *   out        [B][Tq][H][D] in out_dtype (CSA2_F32 or CSA2_BF16)
  * Workspace: csa2_dense_attn_workspace_bytes(B, Tq, H, D, N, W).
  * ------------------------------------------------------------------------ */
 int csa2_dense_attn(int B, int Tq, int H, int D, int N, int m, const int32_t* n_rec,
@@ -249,7 +251,7 @@ int csa2_dense_attn(int B, int Tq, int H, int D, int N, int m, const int32_t* n_
                     const void* swa, const float* swa_scale, int swa_dtype,
                     int S, int W, const int64_t* q_pos, const float* sink,
                     float sm_scale, int rope_dims, float rope_base,
-                    float* out, void* ws, size_t ws_bytes, void* stream);
+                    void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_dense_attn_workspace_bytes(int B, int Tq, int H, int D, int N, int W);
 
 /* ------------------------------------------------------------------------
@@ -274,7 +276,7 @@ int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K,
                              const void* swa, const float* swa_scale, int swa_dtype,
                              int S, int W, const int64_t* q_pos, const float* sink,
                              float sm_scale, int rope_dims, float rope_base,
-                             float* out, void* stream);
+                             void* out, int out_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa2_layer -- one CSA2 layer in one of the three sharing modes
@@ -336,9 +338,10 @@ typedef struct csa2_layer_desc {
     int blk, P;
     int32_t* pool_inout;            /* [B][Tq][P] or NULL */
     /* output and scratch */
-    float* out;                     /* [B][Tq][H][D] */
+    void* out;                      /* [B][Tq][H][D] in out_dtype */
     void* ws;
     size_t ws_bytes;
+    int out_dtype;                  /* CSA2_F32 (0, the default) or CSA2_BF16 */
 } csa2_layer_desc;
 
 int csa2_layer(const csa2_layer_desc* desc, void* stream);

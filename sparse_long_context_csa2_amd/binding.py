@@ -41,7 +41,7 @@ class LayerDesc(ctypes.Structure):
         ("sink", _vp), ("sm_scale", _c_float), ("rope_dims", _c_int), ("rope_base", _c_float),
         ("q_pos", _vp),
         ("K", _c_int), ("idx_inout", _vp), ("blk", _c_int), ("P", _c_int), ("pool_inout", _vp),
-        ("out", _vp), ("ws", _vp), ("ws_bytes", _c_size),
+        ("out", _vp), ("ws", _vp), ("ws_bytes", _c_size), ("out_dtype", _c_int),
     ]
 
 
@@ -70,12 +70,13 @@ def lib() -> ctypes.CDLL:
         L.csa2_topk.argtypes = [i, i, i, v, v, i, i, v, v, s, v]
         L.csa2_topk_workspace_bytes.argtypes = [i, i, i]
         L.csa2_topk_workspace_bytes.restype = s
-        L.csa2_sparse_attn.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f, v, v,
-                                       s, v]
+        L.csa2_sparse_attn.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f, v, i,
+                                       v, s, v]
         L.csa2_sparse_attn_noalloc.argtypes = [i, i, i, i, i, i, v, i, v, v, i, v, v, v, i, i, i, v, v, f, i, f,
-                                               v, v]
+                                               v, i, v]
         L.csa2_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
-        L.csa2_dense_attn.argtypes = [i, i, i, i, i, i, v, v, i, v, v, i, v, v, i, i, i, v, v, f, i, f, v, v, s, v]
+        L.csa2_dense_attn.argtypes = [i, i, i, i, i, i, v, v, i, v, v, i, v, v, i, i, i, v, v, f, i, f, v, i, v, s,
+                                      v]
         L.csa2_dense_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.csa2_dense_attn_workspace_bytes.restype = s
         L.csa2_sparse_attn_workspace_bytes.restype = s
@@ -226,40 +227,52 @@ def csa2_topk(scores, K: int, pool=None, blk: int = 0, out=None, ws=None, stream
                                    _p(ws), nb, _stream(stream)), out, prepare, (ws,))
 
 
+def _out_code(out: torch.Tensor) -> int:
+    """Output dtype code: float32 or bfloat16 tensors."""
+    if out.dtype == torch.float32:
+        return F32
+    if out.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"attention output must be float32 or bfloat16, got {out.dtype}")
+
+
 def csa2_sparse_attn(q, kv, kv_scale, idx, swa, swa_scale, W: int, q_pos, sink, rope_dims: int,
                      rope_base: float = 10000.0, sm_scale: float = 0.0, out=None, ws=None,
-                     stream=None, prepare: bool = False) -> torch.Tensor:
-    """Attention output [B][Tq][H][D] float32; see csa2.h."""
+                     stream=None, prepare: bool = False, out_dtype=torch.float32) -> torch.Tensor:
+    """Attention output [B][Tq][H][D] (float32, or bfloat16 rounded to
+    nearest even: the dtype of ``out`` or ``out_dtype``); see csa2.h."""
     B, Tq, H, D = q.shape
     N = kv.shape[1]
     S = swa.shape[1]
     K = 0 if idx is None else idx.shape[-1]
     if out is None:
-        out = _empty((B, Tq, H, D), torch.float32, q.device, stream)
+        out = _empty((B, Tq, H, D), out_dtype, q.device, stream)
     nb = lib().csa2_sparse_attn_workspace_bytes(B, Tq, H, D, K, W)
     ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_sparse_attn,
                  (B, Tq, H, D, N, K, _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv, kv_scale), _p(idx),
                   _p(swa), _p(swa_scale), dtype_code(swa, swa_scale), S, W, _p(q_pos), _p(sink), float(sm_scale),
-                  rope_dims, float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
+                  rope_dims, float(rope_base), _p(out), _out_code(out), _p(ws), nb, _stream(stream)), out, prepare,
+                 (ws,))
 
 
 def csa2_dense_attn(q, kv, kv_scale, swa, swa_scale, W: int, q_pos, sink, rope_dims: int, m: int, n_rec=None,
                     rope_base: float = 10000.0, sm_scale: float = 0.0, out=None, ws=None, stream=None,
-                    prepare: bool = False) -> torch.Tensor:
-    """HCA attention output [B][Tq][H][D] float32 over every visible record
-    of kv at compression m; see csa2.h."""
+                    prepare: bool = False, out_dtype=torch.float32) -> torch.Tensor:
+    """HCA attention output [B][Tq][H][D] (float32 or bfloat16) over every
+    visible record of kv at compression m; see csa2.h."""
     B, Tq, H, D = q.shape
     N = kv.shape[1]
     S = swa.shape[1]
     if out is None:
-        out = _empty((B, Tq, H, D), torch.float32, q.device, stream)
+        out = _empty((B, Tq, H, D), out_dtype, q.device, stream)
     nb = lib().csa2_dense_attn_workspace_bytes(B, Tq, H, D, N, W)
     ws = _ws(nb, q.device, ws, stream)
     return _call(lib().csa2_dense_attn,
                  (B, Tq, H, D, N, m, _p(n_rec), _p(q), dtype_code(q), _p(kv), _p(kv_scale), dtype_code(kv, kv_scale),
                   _p(swa), _p(swa_scale), dtype_code(swa, swa_scale), S, W, _p(q_pos), _p(sink), float(sm_scale),
-                  rope_dims, float(rope_base), _p(out), _p(ws), nb, _stream(stream)), out, prepare, (ws,))
+                  rope_dims, float(rope_base), _p(out), _out_code(out), _p(ws), nb, _stream(stream)), out, prepare,
+                 (ws,))
 
 
 def make_layer_desc(mode: str, shared: dict, layer: dict, idx_inout, pool_inout, out, ws=None) -> LayerDesc:
@@ -296,6 +309,7 @@ def make_layer_desc(mode: str, shared: dict, layer: dict, idx_inout, pool_inout,
     d.blk, d.P = int(layer.get("blk", 0) or 0), int(layer.get("P", 0) or 0)
     d.pool_inout = _p(pool_inout)
     d.out = _p(out)
+    d.out_dtype = F32 if out is None else _out_code(out)
     d.ws = _p(ws)
     d.ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     return d

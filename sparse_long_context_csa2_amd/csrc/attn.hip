@@ -88,7 +88,8 @@ struct AttnP {
     float sm;
     int rope_dims;
     float rope_base;
-    float* out;               // [B][Tq][64][512]
+    void* out;                // [B][Tq][64][512], float32 or bf16 (out_bf16)
+    int out_bf16;
     float* part_o;            // [Q][nsplit][64][512]
     float* part_ml;           // [Q][nsplit][64][2]
 };
@@ -98,6 +99,17 @@ constexpr int kBuf = kTile * kXPitch;   // one tile buffer
 constexpr int kMaxWin = 256;
 constexpr int kMaxEnt = kMaxKList + kMaxWin;  // entries of one split (multiple of kTile)
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Four output channels at element e of the output: float32, or bf16
+// rounded to nearest even (8 bytes; e is a multiple of 4).
+__device__ __forceinline__ void store_out4(void* out, size_t e, f32x4 v, bool bf16) {
+    if (bf16) {
+        const u32x2 w = {cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e));
+    } else {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
+    }
+}
 
 // Barrier for LDS hand-offs: this wave's LDS accesses are complete, then
 // all waves meet.  Unlike __syncthreads() it does not wait for outstanding
@@ -324,7 +336,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     auto finish = [&](int qr_f, int split_f, int h_f) {
         const int hb = h_f - l16;  // first head of the wave's 16
         float f = 1.f;  // normalisation (one split) or none (partials)
-        float* dst;
+        void* dst;      // output (one split) or the split's partials, as elements from dst0
+        size_t dst0;
+        bool obf = false;
         if (p.nsplit == 1) {
             const float sk = p.sink[h_f] * kLog2e;  // the head's sink logit, log2 units
             const float a = fmaxf(m_run, sk);
@@ -335,10 +349,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 const float den = l_run * em + es;
                 f = den > 0.f ? em / den : 0.f;
             }
-            dst = p.out + (static_cast<size_t>(qr_f) * kH + hb) * kD;
+            dst = p.out;
+            dst0 = (static_cast<size_t>(qr_f) * kH + hb) * kD;
+            obf = p.out_bf16;
         } else {
             const size_t slot0 = (static_cast<size_t>(qr_f) * p.nsplit + split_f) * kH + hb;
-            dst = p.part_o + slot0 * kD;
+            dst = p.part_o;
+            dst0 = slot0 * kD;
             if (g == 0 && (!kDec || wave == 0)) {  // decode: every wave holds the same m and l
                 p.part_ml[2 * (slot0 + l16)] = m_run;  // log2 units
                 p.part_ml[2 * (slot0 + l16) + 1] = l_run;
@@ -377,8 +394,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     v[2] = x1 * cs[2] + y1 * cs[3];
                     v[3] = y1 * cs[2] - x1 * cs[3];
                 }
-                __builtin_nontemporal_store(
-                    v, reinterpret_cast<f32x4*>(dst + (2 * r + (lane >> 5)) * kD + ch0 + c));
+                store_out4(dst, dst0 + (2 * r + (lane >> 5)) * kD + ch0 + c, v, obf);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             return;
@@ -405,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                     v[2] = x1 * cs[2] + y1 * cs[3];
                     v[3] = y1 * cs[2] - x1 * cs[3];
                 }
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + r * kD + 256 * half + 4 * lane));
+                store_out4(dst, dst0 + r * kD + 256 * half + 4 * lane, v, obf);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites
         }
@@ -945,7 +961,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
             x[i + 1] = -xa * sn + ya * cs;
         }
     }
-    *reinterpret_cast<f32x4*>(p.out + (static_cast<size_t>(qr) * kH + h) * kD + d) = x;
+    store_out4(p.out, (static_cast<size_t>(qr) * kH + h) * kD + d, x, p.out_bf16);
 }
 
 // ---------------------------------------------------------------- generic
@@ -965,7 +981,8 @@ struct AttnG {
     float sm;
     int rope_dims;
     float rope_base;
-    float* out;
+    void* out;
+    int out_bf16;
 };
 
 __device__ float block_reduce(float v, float* red, bool is_max) {
@@ -1055,17 +1072,19 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnG p) {
     }
     __syncthreads();
     const int rd = p.rope_dims, r0 = D - rd;
-    float* orow = p.out + qoff;
     for (int i = threadIdx.x; i < D; i += blockDim.x) {
-        if (i < r0) {
-            orow[i] = ctx[i];
-        } else {
+        float o = ctx[i];
+        if (i >= r0) {
             const int jp = (i - r0) >> 1;
             float cs, sn;
             rope_angle(t, jp, rd, p.rope_base, cs, sn);
             const float x = ctx[r0 + 2 * jp], y = ctx[r0 + 2 * jp + 1];
-            orow[i] = ((i - r0) & 1) ? (-x * sn + y * cs) : (x * cs + y * sn);
+            o = ((i - r0) & 1) ? (-x * sn + y * cs) : (x * cs + y * sn);
         }
+        if (p.out_bf16)
+            static_cast<uint16_t*>(p.out)[qoff + i] = static_cast<uint16_t>(f32_to_bf16_rne(o));
+        else
+            static_cast<float*>(p.out)[qoff + i] = o;
     }
 }
 
@@ -1198,6 +1217,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         p.rope_dims = a.rope_dims;
         p.rope_base = a.rope_base;
         p.out = a.out;
+        p.out_bf16 = a.out_dtype == DT_BF16;
         const bool dec = decode_layout(Q);
         p.dense_m = a.dense_m;
         p.n_rec = a.n_rec;
@@ -1244,6 +1264,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
     p.q = a.q; p.kv = a.kv; p.kv_scale = a.kv_scale; p.idx = a.idx; p.swa = a.swa;
     p.swa_scale = a.swa_scale; p.q_pos = a.q_pos; p.sink = a.sink; p.sm = sm;
     p.rope_dims = a.rope_dims; p.rope_base = a.rope_base; p.out = a.out;
+    p.out_bf16 = a.out_dtype == DT_BF16;
     p.dense_m = a.dense_m; p.n_rec = a.n_rec;
     if (a.dense_m) p.K = a.N;  // entry j < N is record j when visible
     const size_t lds = (2 * static_cast<size_t>(a.D) + p.K + a.W) * sizeof(float);

@@ -117,6 +117,9 @@ int validate_attn(const csa2::AttnArgs& a) {
     if (a.q_dtype != CSA2_F32 && a.q_dtype != CSA2_BF16)
         return fail(dtype_ok(a.q_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
                     "sparse_attn: queries must be f32 or bf16");
+    if (a.out_dtype != CSA2_F32 && a.out_dtype != CSA2_BF16)
+        return fail(dtype_ok(a.out_dtype) ? CSA2_EUNSUPPORTED : CSA2_EINVAL,
+                    "sparse_attn: the output must be f32 or bf16 (out_dtype=%d)", a.out_dtype);
     int e = check_align("sparse_attn",
                         {a.q, a.kv, a.kv_scale, a.idx, a.swa, a.swa_scale, a.q_pos, a.sink, a.out}, a.ws);
     if (e) return e;
@@ -219,23 +222,23 @@ size_t csa2_sparse_attn_workspace_bytes(int B, int Tq, int H, int D, int K, int 
 static void fill_attn(csa2::AttnArgs& a, int B, int Tq, int H, int D, int N, int K, const void* q, int q_dtype,
                       const void* kv, const float* kv_scale, int kv_dtype, const int32_t* idx, const void* swa,
                       const float* swa_scale, int swa_dtype, int S, int W, const int64_t* q_pos,
-                      const float* sink, float sm_scale, int rope_dims, float rope_base, float* out, void* ws,
-                      size_t ws_bytes) {
+                      const float* sink, float sm_scale, int rope_dims, float rope_base, void* out,
+                      int out_dtype, void* ws, size_t ws_bytes) {
     a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.N = N; a.K = K;
     a.q = q; a.q_dtype = q_dtype; a.kv = kv; a.kv_scale = kv_scale; a.kv_dtype = kv_dtype; a.idx = idx;
     a.swa = swa; a.swa_scale = swa_scale; a.swa_dtype = swa_dtype; a.S = S; a.W = W; a.q_pos = q_pos;
     a.sink = sink; a.sm_scale = sm_scale; a.rope_dims = rope_dims; a.rope_base = rope_base; a.out = out;
-    a.ws = ws; a.ws_bytes = ws_bytes;
+    a.out_dtype = out_dtype; a.ws = ws; a.ws_bytes = ws_bytes;
 }
 
 int csa2_sparse_attn(int B, int Tq, int H, int D, int N, int K, const void* q, int q_dtype, const void* kv,
                      const float* kv_scale, int kv_dtype, const int32_t* idx, const void* swa,
                      const float* swa_scale, int swa_dtype, int S, int W, const int64_t* q_pos, const float* sink,
-                     float sm_scale, int rope_dims, float rope_base, float* out, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     float sm_scale, int rope_dims, float rope_base, void* out, int out_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
     csa2::AttnArgs a;
     fill_attn(a, B, Tq, H, D, N, K, q, q_dtype, kv, kv_scale, kv_dtype, idx, swa, swa_scale, swa_dtype, S, W,
-              q_pos, sink, sm_scale, rope_dims, rope_base, out, ws, ws_bytes);
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, out_dtype, ws, ws_bytes);
     int e = validate_attn(a);
     if (e) return e;
     const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
@@ -249,10 +252,10 @@ int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K, const vo
                              const void* kv, const float* kv_scale, int kv_dtype, const int32_t* idx,
                              const void* swa, const float* swa_scale, int swa_dtype, int S, int W,
                              const int64_t* q_pos, const float* sink, float sm_scale, int rope_dims,
-                             float rope_base, float* out, void* stream) {
+                             float rope_base, void* out, int out_dtype, void* stream) {
     csa2::AttnArgs a;
     fill_attn(a, B, Tq, H, D, N, K, q, q_dtype, kv, kv_scale, kv_dtype, idx, swa, swa_scale, swa_dtype, S, W,
-              q_pos, sink, sm_scale, rope_dims, rope_base, out, nullptr, 0);
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, out_dtype, nullptr, 0);
     int e = validate_attn(a);
     if (e) return e;
     const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
@@ -279,12 +282,13 @@ size_t csa2_dense_attn_workspace_bytes(int B, int Tq, int H, int D, int N, int W
 int csa2_dense_attn(int B, int Tq, int H, int D, int N, int m, const int32_t* n_rec, const void* q, int q_dtype,
                     const void* kv, const float* kv_scale, int kv_dtype, const void* swa, const float* swa_scale,
                     int swa_dtype, int S, int W, const int64_t* q_pos, const float* sink, float sm_scale,
-                    int rope_dims, float rope_base, float* out, void* ws, size_t ws_bytes, void* stream) {
+                    int rope_dims, float rope_base, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                    void* stream) {
     if (m < 1) return fail(CSA2_EINVAL, "dense_attn: compression ratio m=%d must be >= 1", m);
     if (int e = check_align("dense_attn", {n_rec}, nullptr)) return e;
     csa2::AttnArgs a;
     fill_attn(a, B, Tq, H, D, N, 0, q, q_dtype, kv, kv_scale, kv_dtype, nullptr, swa, swa_scale, swa_dtype, S, W,
-              q_pos, sink, sm_scale, rope_dims, rope_base, out, ws, ws_bytes);
+              q_pos, sink, sm_scale, rope_dims, rope_base, out, out_dtype, ws, ws_bytes);
     a.dense_m = m;
     a.n_rec = n_rec;
     int e = validate_attn(a);
@@ -356,7 +360,8 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     if (d->mode == CSA2_HCA)
         return csa2_dense_attn(d->B, d->Tq, d->H, d->D, d->N, d->m, d->n_rec, d->q, d->q_dtype, d->kv, d->kv_scale,
                                d->kv_dtype, d->swa, d->swa_scale, d->swa_dtype, d->S, d->W, d->q_pos, d->sink,
-                               d->sm_scale, d->rope_dims, d->rope_base, d->out, d->ws, d->ws_bytes, stream);
+                               d->sm_scale, d->rope_dims, d->rope_base, d->out, d->out_dtype, d->ws, d->ws_bytes,
+                               stream);
     csa2::IndexArgs ia;
     const bool scoring = d->mode != CSA2_REUSE;
     const bool pooled = d->mode == CSA2_REINDEX && d->pool_inout;
@@ -377,7 +382,7 @@ int csa2_layer(const csa2_layer_desc* d, void* stream) {
     csa2::AttnArgs aa;
     fill_attn(aa, d->B, d->Tq, d->H, d->D, d->N, d->K, d->q, d->q_dtype, d->kv, d->kv_scale, d->kv_dtype,
               d->idx_inout, d->swa, d->swa_scale, d->swa_dtype, d->S, d->W, d->q_pos, d->sink, d->sm_scale,
-              d->rope_dims, d->rope_base, d->out, static_cast<uint8_t*>(d->ws) + pl.off_attn,
+              d->rope_dims, d->rope_base, d->out, d->out_dtype, static_cast<uint8_t*>(d->ws) + pl.off_attn,
               d->ws_bytes > pl.off_attn ? d->ws_bytes - pl.off_attn : 0);
     e = validate_attn(aa);
     if (e) return e;

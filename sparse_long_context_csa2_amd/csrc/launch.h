@@ -62,7 +62,8 @@ struct AttnArgs {
     float sm_scale;
     int rope_dims;
     float rope_base;
-    float* out;
+    void* out;
+    int out_dtype;  // DT_F32 or DT_BF16
     void* ws;
     size_t ws_bytes;
     int dense_m = 0;                // > 0: dense mode (no idx; all visible records at ratio dense_m)

@@ -42,7 +42,7 @@ def _scale_fmt(fmt: Optional[str]) -> Optional[str]:
 
 
 class DeviceGroup:
-    def __init__(self, inputs: Dict, device: str = "cuda", copies: int = 1):
+    def __init__(self, inputs: Dict, device: str = "cuda", copies: int = 1, out_dtype=torch.float32):
         wl = inputs["wl"]
         self.wl = wl
         self.device = device
@@ -66,7 +66,7 @@ class DeviceGroup:
             qf = lay.get("q_idx_format")
             d["q_idx"] = to_device(lay["q_idx"], device, qf)
             d["q_idx_scale"] = to_device(lay.get("q_idx_scale"), device, _scale_fmt(qf))
-            d["out"] = torch.empty((B, Tq, wl.H, wl.D), dtype=torch.float32, device=device)
+            d["out"] = torch.empty((B, Tq, wl.H, wl.D), dtype=out_dtype, device=device)
             self.layers.append(d)
         # index sets: Full/Reindex write their own; Reuse reads the last one
         self.idx: List[torch.Tensor] = []
@@ -109,7 +109,7 @@ class DeviceGroup:
         return g
 
     def outputs(self) -> List[np.ndarray]:
-        return [d["out"].cpu().numpy() for d in self.layers]
+        return [d["out"].float().cpu().numpy() for d in self.layers]
 
     def index_sets(self) -> List[Optional[np.ndarray]]:
         return [None if i is None else i.cpu().numpy() for i in self.idx]

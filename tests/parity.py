@@ -104,12 +104,18 @@ def check_attn(gpu_out, ora_out, tol, where=""):
     return float(err)
 
 
-def check_attn_query(gpu_out, shared, layer, b, ti, ids, kv_dtype, where=""):
-    """Oracle attention on the GPU's index set, held to attn_tol; returns
-    (error, bound)."""
+def check_attn_query(gpu_out, shared, layer, b, ti, ids, kv_dtype, where="", out_bf16=False):
+    """Oracle attention on the GPU's index set, held to attn_tol (plus, for
+    a bf16 output, the rounding of the exact value to bf16: half a unit in
+    the last place of the slightly larger magnitude); returns (error, bound)."""
     ref = oracle_attention(shared, layer, b, ti, ids)
     tol = attn_tol(kv_dtype, entry_rows(shared, layer, b, ti, ids))
-    return check_attn(gpu_out, ref, tol, where), tol
+    if not out_bf16:
+        return check_attn(gpu_out, ref, tol, where), tol
+    err = np.abs(np.asarray(gpu_out, dtype=np.float64) - ref)
+    bound = tol + bf16_half_ulp(np.abs(ref) + tol) * (1 + 1e-6)
+    assert np.all(err <= bound), f"{where}: bf16 output off by {(err - bound).max():.3g} beyond its bound"
+    return float(err.max()), tol
 
 
 # ------------------------------------------------------------------ record construction

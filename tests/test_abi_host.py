@@ -100,7 +100,8 @@ def _attn(L, **kw):
     a.update(kw)
     return L.csa2_sparse_attn(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["K"], a["q"], a["qdt"], a["kv"],
                               a["kvs"], a["kvdt"], a["idx"], a["swa"], a["swas"], a["swadt"], a["S"], a["W"],
-                              a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"], a["ws"], a["wsb"], None)
+                              a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"], a.get("odt", 0), a["ws"],
+                              a["wsb"], None)
 
 
 def test_sparse_attn_validation(L):
@@ -119,6 +120,9 @@ def test_sparse_attn_validation(L):
     assert _attn(L, kvdt=4, kvs=FAKE) == B.CSA2_EUNSUPPORTED  # mxfp4 is no attention row format
     assert _attn(L, kvdt=3, swadt=2, swas=FAKE, H=2, D=16, qdt=0) == B.CSA2_EUNSUPPORTED  # 64 x 512 only
     assert _attn(L, H=3, D=2048, qdt=0, kvdt=0, swadt=0) == B.CSA2_EUNSUPPORTED
+    assert _attn(L, odt=2) == B.CSA2_EUNSUPPORTED      # outputs are f32 or bf16
+    assert _attn(L, odt=9) == B.CSA2_EINVAL
+    assert _attn_noalloc(L, odt=3) == B.CSA2_EUNSUPPORTED
     # decode-shaped calls need split partials: an empty workspace is refused
     need = L.csa2_sparse_attn_workspace_bytes(1, 1, 64, 512, 512, 128)
     assert need > 0
@@ -193,7 +197,8 @@ def _attn_noalloc(L, **kw):
     a.update(kw)
     return L.csa2_sparse_attn_noalloc(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["K"], a["q"], a["qdt"], a["kv"],
                                       a["kvs"], a["kvdt"], a["idx"], a["swa"], a["swas"], a["swadt"], a["S"],
-                                      a["W"], a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"], None)
+                                      a["W"], a["pos"], a["sink"], a["sm"], a["r"], a["base"], a["out"],
+                                      a.get("odt", 0), None)
 
 
 def test_sparse_attn_noalloc_validation(L):
@@ -223,7 +228,8 @@ def test_dense_attn_validation(L):
         a.update(kw)
         return L.csa2_dense_attn(a["B"], a["Tq"], a["H"], a["D"], a["N"], a["m"], a["nrec"], a["q"], a["qdt"],
                                  a["kv"], a["kvs"], a["kvdt"], a["swa"], a["swas"], a["swadt"], a["S"], a["W"],
-                                 a["pos"], a["sink"], 0.0, 64, 10000.0, a["out"], a["ws"], a["wsb"], None)
+                                 a["pos"], a["sink"], 0.0, 64, 10000.0, a["out"], a.get("odt", 0), a["ws"],
+                                 a["wsb"], None)
     assert call(m=0) == B.CSA2_EINVAL
     assert call(W=129) == B.CSA2_EINVAL
     assert call(nrec=FAKE + 4) == B.CSA2_EINVAL

@@ -499,6 +499,58 @@ def test_sparse_attn_generic(H, D, dt):
                 PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], dt, f"b={b} t={ti}")
 
 
+def _bf16_to_f32(t):
+    """bfloat16 tensor -> float32 numpy (exact)."""
+    return t.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("path", ["prefill", "decode", "split", "generic", "dense"])
+def test_attn_bf16_output(path):
+    """The bf16 output option: every output is the float32 output of the
+    same call rounded to nearest even (bit for bit), and within the
+    oracle's bound plus that rounding.  Covers the prefill layout, the
+    decode layout with one part and with merged parts, the generic kernel
+    and dense (HCA) attention."""
+    _case(f"attention bf16 output, {path} path")
+    if path in ("prefill", "decode"):
+        wl, inp, idx = _attn_case("bf16", 150 if path == "prefill" else 3, q_std=1.0, kv_std=1.0)
+    elif path == "split":
+        N = 4096
+        wl = _small(B=1, Tq=1, N=N, K=512, W=128, swa_slots=136, decode_pos=5 * N, q_std=1.0, kv_std=1.0)
+        inp = WL.make_inputs(wl)
+        idx = np.random.default_rng(1).permutation(N)[:512][None, None, :].astype(np.int32)
+    elif path == "generic":
+        wl = _small(B=2, Tq=5, N=50, K=12, H=3, D=48, rope_dims=4, W=6, swa_slots=8, decode_pos=60,
+                    q_std=1.0, kv_std=1.0)
+        inp = WL.make_inputs(wl)
+        idx = np.random.default_rng(3).integers(-1, 50, size=(2, 5, 12)).astype(np.int32)
+    else:
+        wl = _small(B=2, Tq=1, N=3000, K=0, W=128, swa_slots=136, decode_pos=4 * 3000 + 100, q_std=1.0, kv_std=1.0)
+        inp = WL.make_inputs(wl)
+        idx = None
+    sh, lay = inp["shared"], inp["layers"][0]
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        if path == "dense":
+            outs[dt] = Bd.csa2_dense_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(lay["swa"]),
+                                          _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]),
+                                          wl.rope_dims, wl.m, out_dtype=dt)
+        else:
+            outs[dt] = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx),
+                                           _dev(lay["swa"]), _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]),
+                                           _dev(lay["sink"]), wl.rope_dims, out_dtype=dt)
+    torch.cuda.synchronize()
+    assert outs[torch.bfloat16].dtype == torch.bfloat16
+    want = outs[torch.float32].to(torch.bfloat16)  # round to nearest even
+    assert torch.equal(outs[torch.bfloat16].view(torch.int16).cpu(), want.view(torch.int16).cpu())
+    ob = _bf16_to_f32(outs[torch.bfloat16])
+    B, Tq = ob.shape[:2]
+    for b in range(B):
+        for ti in ([0, 1, Tq - 1] if Tq > 3 else range(Tq)):
+            ids = np.arange(min(wl.N, (int(lay["q_pos"][b, ti]) + 1) // wl.m)) if idx is None else idx[b, ti]
+            PR.check_attn_query(ob[b, ti], sh, lay, b, ti, ids, wl.kv_dtype, f"b={b} t={ti}", out_bf16=True)
+
+
 # ------------------------------------------------------------------ dense (HCA)
 
 def _visible(inp, b, ti):

@@ -37,7 +37,8 @@ def _noalloc(L, q, kv, kv_scale, idx, swa, swa_scale, W, q_pos, sink, out):
     return L.csa2_sparse_attn_noalloc(B, Tq, H, D, kv.shape[1], idx.shape[-1], p(q), Bd.dtype_code(q), p(kv),
                                       p(kv_scale), Bd.dtype_code(kv), p(idx), p(swa), p(swa_scale),
                                       Bd.dtype_code(swa), swa.shape[1], W, p(q_pos), p(sink), 0.0, 64, 10000.0,
-                                      p(out), torch.cuda.current_stream().cuda_stream)
+                                      p(out), Bd.F32 if out.dtype == torch.float32 else Bd.BF16,
+                                      torch.cuda.current_stream().cuda_stream)
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
