@@ -35,7 +35,7 @@ COPY = "MulFunctor"    # kernel-name fragment of the reference copy
 
 # source file of each ABI call's kernels
 SOURCE = {"attn": "attn.hip", "attn_dense": "attn.hip", "index_full": "indexer.hip", "index_pool": "indexer.hip",
-          "topk_full": "topk.hip", "topk_pool": "topk.hip", "block_pool": "topk.hip"}
+          "topk_full": "topk.hip", "topk_pool": "topk.hip", "block_pool": "topk.hip", "compress": "compress.hip"}
 
 
 def _run(workload: str) -> None:
@@ -47,6 +47,19 @@ def _run(workload: str) -> None:
     from sparse_long_context_csa2_amd import runner as R
     from sparse_long_context_csa2_amd import workloads as WL
 
+    if workload in WL.COMPRESS:  # record construction: one call per step
+        dc = R.DeviceCompress(WL.make_compress_inputs(WL.COMPRESS[workload]), device="cuda:0")
+        dc.run()
+        torch.cuda.synchronize()
+        mark = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+        torch.bitwise_not(mark, out=mark)
+        for s in range(STEPS):
+            dc.run()
+        torch.bitwise_not(mark, out=mark)  # closes the group
+        torch.cuda.synchronize()
+        _copy(torch)
+        print(json.dumps({"workload": workload, "steps": STEPS, "calls": ["compress"], "copy_bytes": COPY_BYTES}))
+        return
     wl = WL.CONFIGS[workload]
     copies = 2 if wl.decode_pos is not None else 1  # as bench.py: decode rotates two cache copies
     grp = R.DeviceGroup(WL.make_inputs(wl), device="cuda:0", copies=copies)
@@ -63,11 +76,18 @@ def _run(workload: str) -> None:
         for s in range(STEPS):
             step.prepared[i][s % copies]()
         torch.cuda.synchronize()
+    torch.bitwise_not(mark, out=mark)  # closes the last group
+    torch.cuda.synchronize()
+    _copy(torch)
+    print(json.dumps({"workload": workload, "steps": STEPS, "calls": names, "copy_bytes": COPY_BYTES}))
+
+
+def _copy(torch) -> None:
+    """The reference copy: reads and writes COPY_BYTES."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    torch.mul(src, 1.0, out=dst)  # the reference: reads and writes COPY_BYTES
+    torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"workload": workload, "steps": STEPS, "calls": names, "copy_bytes": COPY_BYTES}))
 
 
 def _calls_of(workload: str):
@@ -77,6 +97,8 @@ def _calls_of(workload: str):
         sys.path.insert(0, ROOT)
     from sparse_long_context_csa2_amd import workloads as WL
 
+    if workload in WL.COMPRESS:
+        return ["compress"]
     names = []
     for mode in WL.CONFIGS[workload].modes:
         m = mode.split("+")[0]
@@ -85,6 +107,19 @@ def _calls_of(workload: str):
             (["attn_dense"] if m == "hca" else ["attn"])
         names += [n for n in seq if n not in names]
     return names
+
+
+def _algorithmic(workload: str):
+    """Algorithmic bytes per call (bench.py's accounting)."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    from sparse_long_context_csa2_amd import workloads as WL
+
+    if workload in WL.COMPRESS:
+        return {"compress": bench.compress_work(WL.COMPRESS[workload])["bytes"]}
+    wl = WL.CONFIGS[workload]
+    return {k: v["bytes"] for k, v in bench.kernel_work(wl, WL.make_inputs(wl)).items()}
 
 
 def _rows(d: str):
@@ -106,15 +141,14 @@ def _per_kernel(rows, counter: str):
 
 
 def _groups(disp, ncalls):
-    """Dispatches of each marked group (the step run before the first
-    marker and everything after the copy are dropped)."""
+    """Dispatches between consecutive markers (the step run before the
+    first marker and the reference copy after the last are dropped)."""
     copy_at = max(i for i, (name, _) in enumerate(disp) if COPY in name)
-    # the last ncalls markers before the copy (set-up fills come earlier)
-    marks = [i for i, (name, _) in enumerate(disp) if MARK in name and i < copy_at][-ncalls:]
-    if len(marks) != ncalls:
-        raise SystemExit(f"expected {ncalls} markers, found {len(marks)}")
-    ends = marks[1:] + [next(i for i, (name, _) in enumerate(disp) if COPY in name and i > marks[-1])]
-    return [disp[a + 1:b] for a, b in zip(marks, ends)]
+    # the last ncalls + 1 markers before the copy (set-up fills come earlier)
+    marks = [i for i, (name, _) in enumerate(disp) if MARK in name and i < copy_at][-(ncalls + 1):]
+    if len(marks) != ncalls + 1:
+        raise SystemExit(f"expected {ncalls + 1} markers, found {len(marks)}")
+    return [disp[a + 1:b] for a, b in zip(marks[:-1], marks[1:])]
 
 
 def _summarize(workload: str, fetch_dir: str, write_dir: str, calls) -> None:
@@ -136,13 +170,16 @@ def _summarize(workload: str, fetch_dir: str, write_dir: str, calls) -> None:
              f"{COPY_BYTES >> 20} MiB: FETCH_SIZE {res['FETCH_SIZE'][2]:.0f} KiB (factor {res['FETCH_SIZE'][1]:.4f}), "
              f"WRITE_SIZE {res['WRITE_SIZE'][2]:.0f} KiB (factor {res['WRITE_SIZE'][1]:.4f}).", "",
              f"Each call ran {STEPS} times on its own; figures are per call.", "",
-             "| call | kernels | fetch MB/call | write MB/call | HBM bytes/call |", "|---|---|---|---|---|"]
+             "| call | kernels | fetch MB/call | write MB/call | HBM bytes/call | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    algo = _algorithmic(workload)
     for gi, call in enumerate(calls):
         tot, kern = {}, set()
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             groups, scale, _ = res[counter]
             tot[counter] = sum(v for _, v in groups[gi]) * scale * 1024.0 / STEPS
-            kern |= {name.split("(")[0].replace("void ", "") for name, _ in groups[gi]}
+            kern |= {name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("csa2::", "")
+                     for name, _ in groups[gi]}
         per = tot["FETCH_SIZE"] + tot["WRITE_SIZE"]
         src = SOURCE[call]
         src_path = os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", src)
@@ -153,9 +190,13 @@ def _summarize(workload: str, fetch_dir: str, write_dir: str, calls) -> None:
                "write_bytes_per_launch": round(tot["WRITE_SIZE"]),
                "bytes_per_launch": round(per),
                "fetch_scale": res["FETCH_SIZE"][1], "write_scale": res["WRITE_SIZE"][1]}
+        a = algo.get(call)
+        rec["algorithmic_bytes"] = a
         json.dump(rec, open(os.path.join(out_dir, f"traffic_{call}_{workload}.json"), "w"), indent=1)
         lines.append(f"| {call} | {', '.join(sorted(kern))} | {tot['FETCH_SIZE'] / 1e6:.2f} | "
-                     f"{tot['WRITE_SIZE'] / 1e6:.2f} | {per:.4g} |")
+                     f"{tot['WRITE_SIZE'] / 1e6:.2f} | {per:.4g} | {a if a else '-'} | "
+                     f"{per / a:.2f} |" if a else f"| {call} | {', '.join(sorted(kern))} | "
+                     f"{tot['FETCH_SIZE'] / 1e6:.2f} | {tot['WRITE_SIZE'] / 1e6:.2f} | {per:.4g} | - | - |")
     open(os.path.join(out_dir, f"traffic_{workload}.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
