@@ -553,6 +553,230 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
     }
 }
 
+// ---------------------------------------------------------------- rows up to 16384 columns, one workgroup each
+
+// One workgroup of 1024 threads per row, the row's keys in registers:
+// thread t owns the KPT consecutive columns KPT*t .. KPT*t+KPT-1.  One LDS
+// histogram of the top 12 key bits finds the boundary bin; an exact radix
+// select over the composite keys of that bin runs straight over the
+// registers (8-bit digits below the bin's 12 known bits, each pass one LDS
+// histogram and one scan, stopping once a digit class holds exactly the
+// elements still needed); the chosen columns leave in column order through
+// one block scan of per-thread counts.  No candidate list, no workspace and
+// one launch: for the few long rows of decode this replaces a chain of
+// kernels that hand lists from workgroup to workgroup.
+constexpr int kRT = 1024;
+constexpr int kRW = kRT / kWave;
+constexpr int kRowCols = kRT * 16;  // columns per row at most (16 keys per thread fit the registers)
+
+struct RowScan {
+    int wave_tot[kRW];
+    int res[3];
+    uint32_t lo[kRW], hi[kRW];
+};
+
+__device__ int row_excl_scan(int v, RowScan& s, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) s.wave_tot[wave] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kRW; ++i) {
+        const int w = s.wave_tot[i];
+        off += i < wave ? w : 0;
+        tot += w;
+    }
+    *total = tot;
+    return off + x - v;
+}
+
+// Scanning nb = 4 * kRT (PER = 4) or 256 (PER = 0: threads below 256 hold
+// one bin each) bins from the top, the bin where the running count first
+// reaches `need`: returns it (-1 if the total is below need) and the number
+// still needed from it, and that bin's count.
+template <int PER>
+__device__ int row_find(const int* hist, int need, RowScan& s, int* rest, int* bin_count) {
+    constexpr int P = PER ? PER : 1;
+    constexpr int NB = PER ? kRT * PER : 256;
+    int loc[P];
+    int sum = 0;
+    const int t = threadIdx.x;
+    const int top = NB - 1 - t * P;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        loc[j] = (PER || t < NB) ? hist[top - j] : 0;
+        sum += loc[j];
+    }
+    int total;
+    const int excl = row_excl_scan(sum, s, &total);
+    if (t == 0) { s.res[0] = -1; s.res[1] = 0; s.res[2] = 0; }
+    __syncthreads();
+    if (excl < need && excl + sum >= need) {
+        int acc = excl;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (acc + loc[j] >= need) {
+                s.res[0] = top - j;
+                s.res[1] = need - acc;
+                s.res[2] = loc[j];
+                break;
+            }
+            acc += loc[j];
+        }
+    }
+    __syncthreads();
+    const int bin = s.res[0];
+    *rest = s.res[1];
+    *bin_count = s.res[2];
+    __syncthreads();
+    return bin;
+}
+
+struct __align__(16) RowShared {
+    int hist[kBins];
+    int hist8[256];
+    int pool[kRowCols / 4];  // the row's pool (blocks of at least 4 records)
+    RowScan scan;
+};
+
+template <int KPT, bool POOL>
+__global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
+    __shared__ RowShared sh;
+    const int row = blockIdx.x;
+    const int n = p.ncols;
+    const int K = p.K;
+    const int t = threadIdx.x;
+    const float* srow = p.scores + static_cast<size_t>(row) * n;
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    if constexpr (POOL) {
+        const int32_t* prow = p.pool + static_cast<size_t>(row) * p.P;
+        for (int i = t; i < p.P; i += kRT) sh.pool[i] = prow[i];
+    }
+    for (int i = t; i < kBins; i += kRT) sh.hist[i] = 0;
+    const int lane = t & 63, wave = t >> 6;
+    // the thread's scores, all loads in flight at once
+    const int c0 = KPT * t;
+    uint32_t kk[KPT];  // scores' bits, then keys
+    if ((n & 3) == 0 && c0 + KPT <= n) {  // whole and 16-byte aligned (the row base is)
+#pragma unroll
+        for (int i = 0; i < KPT; i += 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(srow + c0 + i);
+            kk[i] = v[0]; kk[i + 1] = v[1]; kk[i + 2] = v[2]; kk[i + 3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) kk[i] = __float_as_uint(srow[min(c0 + i, n - 1)]);
+    }
+    __syncthreads();  // pool and cleared histogram visible
+    auto rec_of_col = [&](int c) -> int {
+        if constexpr (!POOL) return c;
+        const int q = c / p.blk;
+        const int pb = sh.pool[q];
+        return pb < 0 ? -1 : pb * p.blk + (c - q * p.blk);
+    };
+    int nv = 0;
+    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int c = c0 + i;
+        uint32_t k = score_key(__uint_as_float(kk[i]));
+        if (c >= n || (POOL && k != 0u && rec_of_col(c) < 0)) k = 0u;
+        kk[i] = k;
+        nv += k != 0u;
+        if (k) klo = min(klo, k);
+        khi = max(khi, k);
+    }
+    // The row's valid keys share every bit above the highest bit in which
+    // its smallest and largest differ; the histogram takes the 12 bits
+    // below that common prefix, so the keys spread over the bins (the top
+    // 12 bits would put most of a row into a few bins, whose LDS atomics
+    // serialise).
+    for (int o = 32; o > 0; o >>= 1) {
+        klo = min(klo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(klo), o, kWave)));
+        khi = max(khi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(khi), o, kWave)));
+    }
+    if (lane == 0) {
+        sh.scan.lo[wave] = klo;
+        sh.scan.hi[wave] = khi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) {
+        klo = min(klo, sh.scan.lo[w]);
+        khi = max(khi, sh.scan.hi[w]);
+    }
+    const uint32_t diff = klo ^ khi;
+    const int top = (diff && klo <= khi) ? 31 - __builtin_clz(diff) : -1;
+    const int bsh = top > 11 ? top - 11 : 0;                                 // bin = (key >> bsh) & 4095
+    // the shared high bits (all of them when every valid key is equal)
+    const uint32_t common = top < 0 ? khi : (top >= 31 ? 0u : (khi & ~((2u << top) - 1u)));
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (kk[i]) atomicAdd(&sh.hist[(kk[i] >> bsh) & (kBins - 1)], 1);
+    int nvalid;
+    row_excl_scan(nv, sh.scan, &nvalid);  // barriers inside: the histogram is complete
+
+    int b1 = -1;
+    unsigned long long thr = 0ull;
+    if (nvalid > K) {
+        int need, bc;
+        b1 = row_find<4>(sh.hist, K, sh.scan, &need, &bc);
+        // radix select of the `need` largest composite keys of bin b1, over
+        // the registers; the common prefix and the bin fix the composite's
+        // bits from 32 + bsh up
+        const uint32_t kb = common | (static_cast<uint32_t>(b1) << bsh);  // the bin's key bits
+        unsigned long long prefix = static_cast<unsigned long long>(kb) << 32;
+        unsigned long long mask = ~0ull << (32 + bsh);
+        auto in_bin = [&](uint32_t k) { return k && (k >> bsh) == (kb >> bsh); };
+        for (int shift = 32 + bsh - 8;; shift -= 8) {
+            const int sh8 = shift > 0 ? shift : 0;
+            if (t < 256) sh.hist8[t] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                if (in_bin(kk[i])) {
+                    const unsigned long long ck = composite(kk[i], rec_of_col(c0 + i));
+                    if ((ck & mask) == prefix) atomicAdd(&sh.hist8[(ck >> sh8) & 255], 1);
+                }
+            }
+            __syncthreads();
+            int rest, cnt_d;
+            const int d = row_find<0>(sh.hist8, need, sh.scan, &rest, &cnt_d);
+            prefix |= static_cast<unsigned long long>(d) << sh8;
+            mask |= 255ull << sh8;
+            need = rest;
+            if (cnt_d == rest || sh8 == 0) break;  // the whole class is chosen, or the key is exact
+        }
+        thr = prefix;
+    }
+    // chosen columns, in column order: keys above the bin, and the bin's
+    // keys whose composite reaches the threshold
+    const uint32_t kbin = b1 >= 0 ? (common | (static_cast<uint32_t>(b1) << bsh)) >> bsh : 0u;
+    auto chosen = [&](int i) -> bool {
+        const uint32_t k = kk[i];
+        if (!k) return false;
+        if (b1 < 0) return true;
+        const uint32_t b = k >> bsh;
+        return b > kbin || (b == kbin && composite(k, rec_of_col(c0 + i)) >= thr);
+    };
+    int nc = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) nc += chosen(i);
+    int take;
+    int pos = row_excl_scan(nc, sh.scan, &take);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (chosen(i) && pos < K) orow[pos++] = rec_of_col(c0 + i);
+    for (int i = take + t; i < K; i += kRT) orow[i] = -1;
+}
+
 // ---------------------------------------------------------------- long rows
 
 // The row lists that the workgroups of a row hand to its last workgroup
@@ -949,6 +1173,19 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
             else if (p.ncols <= 64 * 32) hipLaunchKernelGGL((topk_wave_kernel<32, false>), grid, dim3(kNT), 0, st, p);
             else hipLaunchKernelGGL((topk_wave_kernel<64, false>), grid, dim3(kNT), 0, st, p);
         }
+        return static_cast<int>(hipGetLastError());
+    }
+    if (!p.sort_by_key && p.ncols <= kRowCols && (!p.pool || p.blk >= 4)) {
+        // rows up to 16384 columns (record ids or pooled): one workgroup each
+#define CSA2_ROW(KPT)                                                                                    \
+    if (p.pool) hipLaunchKernelGGL((topk_row_kernel<KPT, true>), dim3(p.rows), dim3(kRT), 0, st, p);     \
+    else hipLaunchKernelGGL((topk_row_kernel<KPT, false>), dim3(p.rows), dim3(kRT), 0, st, p);
+        if (p.ncols <= 4 * kRT) {
+            CSA2_ROW(4)
+        } else {
+            CSA2_ROW(16)
+        }
+#undef CSA2_ROW
         return static_cast<int>(hipGetLastError());
     }
     if (p.ncols <= kSmallCols) {
