@@ -95,41 +95,15 @@ __device__ __forceinline__ uint32_t e2m1_encode2(uint32_t old, float a, float b)
 }
 
 // Reductions over aligned groups of N neighbouring lanes (N a power of
-// two up to 64) with DPP moves and gfx950's permlane swaps, no LDS round
-// trip: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes l ^ 1 and l ^ 2; after
-// those, row_half_mirror (l <-> 7 - l within 8 lanes) and row_mirror
-// (l <-> 15 - l within 16) meet the other quad and the other half.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
+// two up to 64), with xor shuffles.
 template <int N>
 __device__ __forceinline__ float lanes_max(float v) {
-    if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
-    if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
-    if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
-    if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
-    if constexpr (N >= 32) {
-        float x, y;
-        pair_xor16(v, x, y);
-        v = fmaxf(x, y);
-    }
-    if constexpr (N >= 64) {
-        float x, y;
-        pair_xor32(v, x, y);
-        v = fmaxf(x, y);
-    }
+#pragma unroll
+    for (int o = 1; o < N; o <<= 1) v = fmaxf(v, shfl_xor_f(v, o));
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    v += dpp<0x141>(v);
-    v += dpp<0x140>(v);
-    return sum4_rows(v);
-}
+__device__ __forceinline__ float wave_sum(float v) { return warp_sum(v); }
 
 // ---------------------------------------------------------------- loads / stores
 
