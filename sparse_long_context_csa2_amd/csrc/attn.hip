@@ -187,8 +187,36 @@ struct __align__(16) AttnShared {
 struct ItemFetch {
     int ids[kIdsPerThread];
     int64_t t;
+    float sink;  // the lane's head's sink logit
     bf16x8 q[16];
 };
+
+// Waits for the next item's ids, position and sink now, at the end of an
+// item (its last copies have landed, the next query loads are not yet out).
+// The compiler's waits count only its own loads, so the first use of these
+// values in the next item's set-up would get a full wait that also covers
+// the query loads issued in between.  Reading them in an asm statement
+// moves that wait here without changing where the values live.
+__device__ __forceinline__ void settle_fetch(const ItemFetch& f) {
+    int s = static_cast<int>(f.t) ^ __float_as_int(f.sink);
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) s |= f.ids[j];
+    asm volatile("; fetched %0" ::"v"(s));
+}
+
+// The same for the query fragments, in the first tile of an item once its
+// own copies have landed (the query loads went out before them): without
+// it the first S^T waits for everything issued since, including the next
+// item's fetch and the copies of tile 2.  AGPR: where the prefill MFMAs
+// read them from; VGPR: the decode layout's.
+template <bool AGPR>
+__device__ __forceinline__ void settle_q_regs(const bf16x8 (&q)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if constexpr (AGPR) asm volatile("; query %0" ::"a"(q[i]));
+        else asm volatile("; query %0" ::"v"(q[i]));
+    }
+}
 
 // Work items are (query, split) pairs; with one split, item i is query
 // Q-1-i so that later positions (more entries) come first.  Persistent
@@ -200,6 +228,42 @@ struct ItemFetch {
 // spread those writes over the run.
 __device__ __forceinline__ int item_of(int round, int g, int G) {
     return round * G + ((round & 1) ? (G - 1 - g) : g);
+}
+
+// Compacts the item's valid record ids (0 <= id < N, in index order) into
+// sh.list() and returns their count (wave-uniform).  ids: this thread's
+// chunks of the index row (-1 past its end); sh.cnt holds the per-(chunk,
+// wave) counts.
+template <class SH>
+__device__ __forceinline__ int compact_ids(SH& sh, const int (&ids)[kIdsPerThread], int nids, int N, int wave,
+                                           int lane) {
+    int ok_bits = 0;
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+        if (j < nids) {
+            const int rec = ids[j];
+            const bool ok = rec >= 0 && rec < N;
+            const unsigned long long bal = __ballot(ok);
+            if (ok) ok_bits |= 1 << j;
+            if (lane == 0) sh.cnt[j][wave] = __popcll(bal);
+        }
+    }
+    lds_sync();
+    int nsel = 0;
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+        if (j < nids) {
+            int before = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) before += (w < wave) ? sh.cnt[j][w] : 0;
+            const bool ok = (ok_bits >> j) & 1;
+            const unsigned long long bal = __ballot(ok);
+            if (ok) sh.list()[nsel + before + __popcll(bal & ((1ull << lane) - 1ull))] = ids[j];
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) nsel += sh.cnt[j][w];
+        }
+    }
+    return __builtin_amdgcn_readfirstlane(nsel);
 }
 
 // Persistent: gridDim.x workgroups of 4 waves (one per SIMD) walk the work
@@ -290,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             f.ids[j] = (j < nids && c < p.K) ? irow[c] : -1;
         }
         f.t = p.q_pos[qr];
+        f.sink = p.sink[head_of(item)];
     };
     auto fetch_q = [&](int item, ItemFetch& f) {
         const uint16_t* qh = p.q + (static_cast<size_t>(query_of(item)) * kH + head_of(item)) * kD;
@@ -320,6 +385,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         fetch(item, nx);
         fetch_q(item, nx);
     }
+    settle_fetch(nx);
 
     // Output of an item.  It runs once the next item's first tile copies
     // are in flight (its stores then drain while those copies land), so O,
@@ -333,6 +399,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
     float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
     float l_run = 0.f;                     // this lane's share of the running sum
     int prev_qr = -1, prev_split = 0, prev_h = 0;  // the item whose output is pending
+    float prev_sink = 0.f;
+    // the sink logit was fetched with the item's inputs: a load here would
+    // wait for every copy and load in flight, including the next item's
     auto finish = [&](int qr_f, int split_f, int h_f) {
         const int hb = h_f - l16;  // first head of the wave's 16
         float f = 1.f;  // normalisation (one split) or none (partials)
@@ -340,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         size_t dst0;
         bool obf = false;
         if (p.nsplit == 1) {
-            const float sk = p.sink[h_f] * kLog2e;  // the head's sink logit, log2 units
+            const float sk = prev_sink * kLog2e;  // the head's sink logit, log2 units
             const float a = fmaxf(m_run, sk);
             f = 0.f;
             if (a != -__builtin_huge_valf()) {
@@ -434,37 +503,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         const int hh = head_of(item);
         const int b = qr / p.Tq;
         const int64_t t = nx.t;
+        const float sink = nx.sink;
         const int rd = p.rope_dims;
         bf16x8 qf[16];  // filled from nx just before the first S^T (its loads land meanwhile)
+        auto settle_q = [](const bf16x8 (&q)[16]) { settle_q_regs<!kDec>(q); };
 
         // ---- compact the valid selected records (in order) ----
-        int ok_bits = 0;
-#pragma unroll
-        for (int j = 0; j < kIdsPerThread; ++j) {
-            if (j < nids) {
-                const int rec = nx.ids[j];
-                const bool ok = rec >= 0 && rec < p.N;
-                const unsigned long long bal = __ballot(ok);
-                if (ok) ok_bits |= 1 << j;
-                if (lane == 0) sh.cnt[j][wave] = __popcll(bal);
-            }
-        }
-        lds_sync();
-        int nsel = 0;
-#pragma unroll
-        for (int j = 0; j < kIdsPerThread; ++j) {
-            if (j < nids) {
-                int before = 0;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) before += (w < wave) ? sh.cnt[j][w] : 0;
-                const bool ok = (ok_bits >> j) & 1;
-                const unsigned long long bal = __ballot(ok);
-                if (ok) sh.list()[nsel + before + __popcll(bal & ((1ull << lane) - 1ull))] = nx.ids[j];
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) nsel += sh.cnt[j][w];
-            }
-        }
-        nsel = __builtin_amdgcn_readfirstlane(nsel);
+        int nsel = compact_ids(sh, nx.ids, nids, p.N, wave, lane);
         if (p.dense_m) {  // dense: every visible record, in id order
             const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
             const int64_t v = t < 0 ? 0 : (t + 1) / p.dense_m;
@@ -610,6 +655,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
                 if (it + 1 < ntile) wait_copies_but_8();
                 else wait_copies_all();
                 lds_sync();  // tile `it` landed; the buffer two tiles ahead is free
+                if (it == 0) settle_q(qf);
                 if (it == 0 && nxt < n_items) fetch(nxt, nx);
                 // later copies go out from inside the MFMA stream (below)
                 if (it == 0 && it + 2 < ntile) issue(it + 2, (it + 2) % NB);
@@ -816,6 +862,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             bhi = packed(s.phi);
             blo = packed(s.plo);
         }
+        // Every path into the tile loop has now waited for the query loads
+        // (the first tile did, after its copies landed; an item without
+        // tiles does so here).  Otherwise the compiler, unable to tell the
+        // paths apart, waits for them inside the loop, before the S^T
+        // MFMAs, with counts that also cover the row copies just issued
+        // by the same step.
+        settle_q(qf);
         // Iteration `it`: one stream of MFMAs -- the P.V of tile it, with the
         // S^T of tile it+1 in its first half and that tile's softmax in its
         // second half.
@@ -874,11 +927,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         for (; it + 1 < ntile; ++it) step(it, std::false_type{});
         if (ntile > 0) tile_pv(ntile - 1, bhi, blo, [](int) {});
         if (ntile == 0 && nxt < n_items) fetch(nxt, nx);
+        settle_fetch(nx);
         if (nxt < n_items) fetch_q(nxt, nx);
         l_run = sum4_rows(l_run);  // the head's sum over the four lane groups
         prev_qr = qr;
         prev_split = split;
         prev_h = hh;
+        prev_sink = sink;
         item = nxt;
     }
     if (prev_qr >= 0) {

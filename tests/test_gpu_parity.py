@@ -326,18 +326,20 @@ def test_sparse_attn_mfma(kdt, Tq):
 
 
 @pytest.mark.parametrize("kdt", ["bf16", "e4m3"])
-def test_sparse_attn_sharp_logits(kdt):
+@pytest.mark.parametrize("Tq", [3, 150])
+def test_sparse_attn_sharp_logits(kdt, Tq):
     """Queries scaled by sqrt(D): logits of order 1-10 stress the online
-    max rescaling and the sink; the bf16 hi+lo split keeps P exact enough."""
-    _case(f"sparse_attn sharp logits {kdt}")
-    wl, inp, idx = _attn_case(kdt, 3, q_gain=math.sqrt(512), kv_std=1.0)
+    max rescaling and the sink; the bf16 hi+lo split keeps P exact enough
+    (decode and prefill layouts)."""
+    _case(f"sparse_attn sharp logits {kdt} Tq={Tq}")
+    wl, inp, idx = _attn_case(kdt, Tq, q_gain=math.sqrt(512), kv_std=1.0)
     sh, lay = inp["shared"], inp["layers"][0]
     out = Bd.csa2_sparse_attn(_dev(lay["q"]), _dev(sh["kv"]), _dev(sh["kv_scale"]), _dev(idx), _dev(lay["swa"]),
                               _dev(lay["swa_scale"]), wl.W, _dev(lay["q_pos"]), _dev(lay["sink"]), wl.rope_dims)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     for b in range(2):
-        for ti in range(3):
+        for ti in (range(Tq) if Tq < 10 else [0, 1, 2, 77, Tq - 1]):
             # unit-scale rows: the bound is the contract's 2e-3 itself
             err, tol = PR.check_attn_query(out[b, ti], sh, lay, b, ti, idx[b, ti], kdt, f"b={b} t={ti}")
             assert tol > 0.9 * PR.ATTN_TOL[kdt]
