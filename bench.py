@@ -52,7 +52,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU reaches its steady clocks after some tens of milliseconds of
+    # load: 50 steps (about 30 ms of C2) before the timed ones
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C6", "C7", "C8", "C9"])
     ap.add_argument("--only", action="store_true", help="measure the primary workload only")
     ap.add_argument("--extra", default="C2b,C3,C4,C5,C6,C7,C8,C9", help="further workloads measured in the same run")

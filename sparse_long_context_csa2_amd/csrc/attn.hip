@@ -389,12 +389,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
 
     // Output of an item.  It runs once the next item's first tile copies
     // are in flight (its stores then drain while those copies land), so O,
-    // m and l persist across items.  O leaves through LDS, staged in the
-    // last two tile buffers (the next item's first copies target the first
-    // two; rows padded so the lanes of one write pass hit distinct banks),
-    // so that every global store writes whole runs of one head's row: 1 KB
-    // (NHG = 64: each wave stages its 16 heads, 256 channels at a time) or
-    // 512 B (decode: each wave stages its 128 channels of the 16 heads).
+    // m and l persist across items.
     f32x4 acc[kU];
     float m_run = -__builtin_huge_valf();  // running max, log2 units (same in the 4 lanes of a head)
     float l_run = 0.f;                     // this lane's share of the running sum
@@ -431,43 +426,39 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
             }
         }
         // rotary channels [r0, kD) get the inverse rotation (one split
-        // only).  In the read-back layout a lane keeps the same 4 channels
-        // for all rows it stores, so it fetches its rotations once per pass
-        // (the table holds (cos, sin) for every channel pair, (1, 0) below r0)
+        // only); the table holds (cos, sin) for every channel pair, (1, 0)
+        // below r0.  Lane (head hb + l16, group g) holds channels ch0 + 16u
+        // + 4g .. +3, whose two rotary pairs are its own.
         int r0 = p.nsplit == 1 ? kD - p.rope_dims : kD;
-        asm volatile("" : "+s"(r0));  // tested per pass here, not hoisted out of the item loop
-        static_assert(kWaves * 16 * kStagePitch <= 2 * kBuf, "staging fits the last two tile buffers");
-        uint8_t* stage = &sh.xb[AttnShared<KVDT>::kNB - 2][0] + wave * 16 * kStagePitch;
+        asm volatile("" : "+s"(r0));  // tested per block here, not hoisted out of the item loop
         if constexpr (kDec) {
-            // channels ch0 .. ch0+127 of 16 heads: lane (head l16, group g)
-            // holds channels 16u + 4g + v; read back, lane l takes 4
-            // channels of two heads per pass (2 x 512 B per store)
+            // decode: straight from the accumulators (each store writes
+            // 64-byte runs of 16 heads' rows; the wave's 8 stores complete
+            // every 512-byte run)
+            const size_t e0 = dst0 + static_cast<size_t>(l16) * kD + ch0 + 4 * g;
 #pragma unroll
-            for (int u = 0; u < kU; ++u)
-                *reinterpret_cast<f32x4*>(stage + l16 * kStagePitch + 4 * (16 * u + 4 * g)) = acc[u] * f;
-            const int c = 4 * (lane & 31);  // channel offset within the wave's 128
-            const bool rot = ch0 + 128 > r0;
-            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sh.rope_cs[(ch0 + c) / 2][0]);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows visible to the wave
-            f32x4 rows[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                rows[r] = *reinterpret_cast<const f32x4*>(stage + (2 * r + (lane >> 5)) * kStagePitch + 4 * c);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                f32x4 v = rows[r];
-                if (rot) {
+            for (int u = 0; u < kU; ++u) {
+                f32x4 v = acc[u] * f;
+                if (ch0 + 16 * u + 16 > r0) {  // wave-uniform: the block holds rotary channels
+                    const f32x4 cs = *reinterpret_cast<const f32x4*>(&sh.rope_cs[(ch0 + 16 * u + 4 * g) / 2][0]);
                     const float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
                     v[0] = x0 * cs[0] + y0 * cs[1];
                     v[1] = y0 * cs[0] - x0 * cs[1];
                     v[2] = x1 * cs[2] + y1 * cs[3];
                     v[3] = y1 * cs[2] - x1 * cs[3];
                 }
-                store_out4(dst, dst0 + (2 * r + (lane >> 5)) * kD + ch0 + c, v, obf);
+                store_out4(dst, e0 + 16 * u, v, obf);
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             return;
         }
+        // prefill: 256 channels of the wave's 16 heads at a time go through
+        // LDS (the last two tile buffers; the next item's first copies target
+        // the first two; rows padded so that the lanes of one write pass hit
+        // distinct banks), so that every store writes whole 1 KB runs of one
+        // head's row (measured faster than the 64-byte runs of storing from
+        // the accumulators, for this layout's larger outputs)
+        static_assert(kWaves * 16 * kStagePitch <= 2 * kBuf, "staging fits the last two tile buffers");
+        uint8_t* stage = &sh.xb[AttnShared<KVDT>::kNB - 2][0] + wave * 16 * kStagePitch;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
 #pragma unroll
