@@ -155,7 +155,8 @@ size_t csa2_block_pool_workspace_bytes(int rows, int N, int blk);
  * record id ascending.  -INFINITY and NaN scores are never selected.
  *
  * Inputs
- *   rows, ncols, K  (K in 1..CSA2_MAX_K)
+ *   rows, ncols, K  (K in 1..CSA2_MAX_K; ncols up to 2^24, else
+ *              CSA2_EUNSUPPORTED)
  *   scores     [rows][ncols] float32
  *   pool, P, blk
  *              NULL/0/0: column c is record c.  Otherwise [rows][P] int32

@@ -195,6 +195,8 @@ int csa2_topk(int rows, int ncols, int K, const float* scores, const int32_t* po
     if (rows < 1 || ncols < 1 || K < 1)
         return fail(CSA2_EINVAL, "topk: sizes must be >= 1 (rows=%d ncols=%d K=%d)", rows, ncols, K);
     if (K > CSA2_MAX_K) return fail(CSA2_EINVAL, "topk: K=%d above %d", K, CSA2_MAX_K);
+    if (ncols > csa2::kTopkMaxCols)
+        return fail(CSA2_EUNSUPPORTED, "topk: ncols=%d above %d", ncols, csa2::kTopkMaxCols);
     if (!scores || !idx) return fail(CSA2_EINVAL, "topk: null required pointer");
     if (int e = check_align("topk", {scores, pool, idx}, ws)) return e;
     if (pool) {
@@ -334,6 +336,8 @@ static int plan_layer(const csa2_layer_desc* d, LayerPlan& pl) {
             return fail(CSA2_EINVAL, "layer: pool needs blk >= 1 and P >= 1");
         pl.ncols = d->P * d->blk;
     }
+    if (scores_needed && pl.ncols > csa2::kTopkMaxCols)
+        return fail(CSA2_EUNSUPPORTED, "layer: %d columns to select from, above %d", pl.ncols, csa2::kTopkMaxCols);
     size_t off = 0;
     pl.off_scores = off;
     if (scores_needed) off += align256(static_cast<size_t>(pl.rows) * pl.ncols * sizeof(float));

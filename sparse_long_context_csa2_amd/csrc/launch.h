@@ -38,6 +38,8 @@ struct TopkArgs {
     void* ws;
     size_t ws_bytes;
 };
+// Longest Top-K row (columns) the library takes.
+constexpr int kTopkMaxCols = 1 << 24;
 size_t topk_ws_bytes(int rows, int ncols, int K);
 int launch_topk(const TopkArgs& a, void* stream);
 

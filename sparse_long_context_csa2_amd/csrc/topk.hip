@@ -63,10 +63,10 @@ struct TopkP {
     // long-row workspace
     int* ghist;      // [rows][kBins]: histogram of the keys' top 12 bits; with at most
                      // kFewChunks chunks per row, [rows][nchunks][kBins]: each chunk's own
-    int* cnt;        // [rows][4]: candidate count, chosen count (one 64-bit word), finished chunks
-    int* sure;       // [rows][K]: columns chosen outright
-    uint32_t* ckey;  // [rows][ncols]: boundary-bin candidates (key, column)
-    int* ccol;
+    int* cnt;        // [rows][4]: finished chunks (word 2)
+    int* ccnt;       // [rows][nchunks]: entries of each chunk
+    uint32_t* ckey;  // [rows][ncols]: entries (key, column) -- keys in the boundary bin or above,
+    int* ccol;       //   chunk c's at [c kChunk, c kChunk + count), in column order
 };
 
 __device__ __forceinline__ int rec_of(const TopkP& p, const int32_t* prow, int c) {
@@ -75,12 +75,6 @@ __device__ __forceinline__ int rec_of(const TopkP& p, const int32_t* prow, int c
     return pb < 0 ? -1 : pb * p.blk + c % p.blk;
 }
 
-// Key of column c (0 = never selectable).
-__device__ __forceinline__ uint32_t key_of(const TopkP& p, const int32_t* prow, const float* srow, int c) {
-    const uint32_t k = score_key(srow[c]);
-    if (k == 0u) return 0u;
-    return rec_of(p, prow, c) >= 0 ? k : 0u;
-}
 
 // Keys of columns c0 + i * kNT + threadIdx.x, i < N (0 past c1).  All
 // loads are issued before any key is formed: branches between a load and
@@ -830,61 +824,61 @@ __global__ __launch_bounds__(kNT) void topk_hist_kernel(TopkP p) {
         if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
-constexpr int kBitWords = 8192;  // column bitmap of the final ordering: rows up to 262144 columns
-// word w of the bitmap lives at w + w / 32: a thread's run of 32 words then
-// starts one bank further than its neighbour's
-__device__ __forceinline__ int bit_slot(int w) { return w + (w >> 5); }
+// The last workgroup of a row holds the row's entries (keys in bin b1 or
+// above, at most kEntCap) in LDS; more go through the slower path that
+// reads them from the lists.
+constexpr int kEntCap = 4096;
+static_assert(kEntCap / kNT == kChunk / kNT, "entry rows and load rows share the per-wave count table");
+constexpr int kMaxChunks = 16 * kNT;  // rows up to 16M columns
 struct __align__(16) LongShared {
     union {
-        struct {
-            int hist[kBins];
-            int hist8[256];
-        } h;
-        unsigned bits[kBitWords + kBitWords / 32];  // once the selection is made
+        int hist[kBins];          // the row histogram, until the boundary bin is known
+        uint32_t key[kEntCap];    // last workgroup: the row's entries in column order
     } a;
-    union {
-        struct {                      // the row's final resolution
-            unsigned long long fin[kMaxK];
-            uint32_t key[kCandCap];   // the row's boundary candidates
-            int rec[kCandCap];
-            int col[kCandCap];
-        } fin;
-    } u;
+    int col[kEntCap];             // their columns (with sort_by_key, reused for the chosen composites)
+    int rec[kEntCap];             // their records
+    int hist8[256];
+    int cbase[kMaxChunks + 1];    // first entry of each chunk
+    int cnt_wi[kChunk / kNT][kNW];  // entries per (load row, wave)
     Scan scan;
     int misc[4];
 };
 
 __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     __shared__ LongShared sh;
+    constexpr int kPer = kChunk / kNT;
     const int row = blockIdx.y;
+    const int chunk = blockIdx.x;
     const int K = p.K;
-    const int c0 = blockIdx.x * kChunk;
+    const int nch = p.nchunks;
+    const int c0 = chunk * kChunk;
     const int c1 = min(p.ncols, c0 + kChunk);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float* srow = p.scores + static_cast<size_t>(row) * p.ncols;
     const int32_t* prow = p.pool ? p.pool + static_cast<size_t>(row) * p.P : nullptr;
     int* cnt = p.cnt + row * 4;
-    int* sure = p.sure + static_cast<size_t>(row) * K;
+    int* ccnt = p.ccnt + static_cast<size_t>(row) * nch;
     uint32_t* gkey = p.ckey + static_cast<size_t>(row) * p.ncols;
     int* gcol = p.ccol + static_cast<size_t>(row) * p.ncols;
 
     // the chunk's keys and the row histogram, all loads in flight at once
-    uint32_t kk[kChunk / kNT];
+    uint32_t kk[kPer];
     load_keys(p, prow, srow, c0, c1, kk);
-    if (p.nchunks <= kFewChunks) {
+    if (nch <= kFewChunks) {
         // the row histogram is the sum of its chunks' (all loads in flight at once)
-        const int* g = p.ghist + static_cast<size_t>(row) * p.nchunks * kBins;
+        const int* g = p.ghist + static_cast<size_t>(row) * nch * kBins;
         int hv[kFewChunks][kBins / kNT];
 #pragma unroll
         for (int c = 0; c < kFewChunks; ++c)
 #pragma unroll
             for (int j = 0; j < kBins / kNT; ++j)
-                hv[c][j] = g[static_cast<size_t>(min(c, p.nchunks - 1)) * kBins + j * kNT + threadIdx.x];
+                hv[c][j] = g[static_cast<size_t>(min(c, nch - 1)) * kBins + j * kNT + threadIdx.x];
 #pragma unroll
         for (int j = 0; j < kBins / kNT; ++j) {
             int t = 0;
 #pragma unroll
-            for (int c = 0; c < kFewChunks; ++c) t += c < p.nchunks ? hv[c][j] : 0;
-            sh.a.h.hist[j * kNT + threadIdx.x] = t;
+            for (int c = 0; c < kFewChunks; ++c) t += c < nch ? hv[c][j] : 0;
+            sh.a.hist[j * kNT + threadIdx.x] = t;
         }
     } else {
         const int* g = p.ghist + static_cast<size_t>(row) * kBins;
@@ -892,213 +886,231 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
 #pragma unroll
         for (int j = 0; j < kBins / kNT; ++j) hv[j] = g[j * kNT + threadIdx.x];
 #pragma unroll
-        for (int j = 0; j < kBins / kNT; ++j) sh.a.h.hist[j * kNT + threadIdx.x] = hv[j];
+        for (int j = 0; j < kBins / kNT; ++j) sh.a.hist[j * kNT + threadIdx.x] = hv[j];
     }
     __syncthreads();
     int need1;
-    const int b1 = find_from_top<kBins / kNT>(sh.a.h.hist, K, sh.scan, &need1);
-    // classify: keys above b1 are chosen outright (fewer than K in the row),
-    // keys inside b1 are candidates.  Each thread counts its own; one block
-    // scan of (chosen << 16 | candidates) places both lists.
-    int nu = 0, ni = 0;
+    const int b1 = find_from_top<kBins / kNT>(sh.a.hist, K, sh.scan, &need1);
+    // The chunk's entries -- keys in bin b1 or above (every valid key when
+    // the row holds fewer than K) -- go to the chunk's own columns' slots of
+    // the row's lists, in column order: column c0 + i kNT + t comes after
+    // those of the earlier load rows i, of the earlier waves in row i, and
+    // of the earlier lanes of its own wave (one ballot per load row).
+    auto entry = [&](uint32_t k) { return k != 0u && static_cast<int>(k >> kBinShift) >= b1; };
+    unsigned long long bal[kPer];
 #pragma unroll
-    for (int i = 0; i < kChunk / kNT; ++i) {
-        const uint32_t k = kk[i];
-        const int b = static_cast<int>(k >> kBinShift);
-        nu += (k != 0u && b > b1) ? 1 : 0;
-        ni += (k != 0u && b == b1) ? 1 : 0;
-    }
-    int tot;
-    const int off = block_excl_scan((nu << 16) | ni, sh.scan, &tot);
-    const int nloc = tot & 0xFFFF, nsu = tot >> 16;
-    // one atomic reserves room in both of the row's lists
-    if (threadIdx.x == 0) {
-        const unsigned long long add = (static_cast<unsigned long long>(nsu) << 32) | static_cast<unsigned>(nloc);
-        const unsigned long long base = (nloc | nsu) ? atomicAdd(reinterpret_cast<unsigned long long*>(cnt), add) : 0ull;
-        sh.misc[2] = static_cast<int>(base & 0xFFFFFFFFull);
-        sh.misc[3] = static_cast<int>(base >> 32);
+    for (int i = 0; i < kPer; ++i) bal[i] = __ballot(entry(kk[i]));
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) sh.cnt_wi[i][wave] = __popcll(bal[i]);
     }
     __syncthreads();
-    {
-        int sl = sh.misc[2] + (off & 0xFFFF), su = sh.misc[3] + (off >> 16);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int run = 0;
 #pragma unroll
-        for (int i = 0; i < kChunk / kNT; ++i) {
-            const int c = c0 + i * kNT + threadIdx.x;
-            const uint32_t k = kk[i];
-            const int b = static_cast<int>(k >> kBinShift);
-            if (k != 0u && b > b1) st_dev(sure + su++, c);
-            if (k != 0u && b == b1) {
-                st_dev(gkey + sl, k);
-                st_dev(gcol + sl, c);
-                ++sl;
-            }
+    for (int i = 0; i < kPer; ++i) {
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+            const int n = sh.cnt_wi[i][w];
+            before += w < wave ? n : 0;
+            tot += n;
         }
+        if ((bal[i] >> lane) & 1ull) {
+            const int at = c0 + run + before + __popcll(bal[i] & below);
+            st_dev(gkey + at, kk[i]);
+            st_dev(gcol + at, c0 + i * kNT + static_cast<int>(threadIdx.x));
+        }
+        run += tot;
     }
+    if (threadIdx.x == 0) st_dev(ccnt + chunk, run);
     wait_stores();  // this wave's list entries are visible device-wide
     __syncthreads();
-    if (threadIdx.x == 0) sh.misc[2] = atomicAdd(&cnt[2], 1) == p.nchunks - 1;
+    if (threadIdx.x == 0) sh.misc[2] = atomicAdd(&cnt[2], 1) == nch - 1;
     __syncthreads();
     if (!sh.misc[2]) return;
 
-    // ---- last workgroup of this row: resolve the boundary bin ----
-    const int ncand = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
-    const int nsure = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
-    unsigned long long* fin = sh.u.fin.fin;
-    // fin[i] for the i-th chosen element: its column, or with sort_by_key
-    // its composite key.  The chosen-outright ones take fin[0 .. nsure) in
-    // list order, the chosen candidates follow, placed by block scans.
-    auto fin_val = [&](int c, uint32_t key) -> unsigned long long {
-        return p.sort_by_key ? composite(key, rec_of(p, prow, c)) : static_cast<unsigned long long>(c);
-    };
-    int take = nsure;
-    // The list reads below are issued all at once per thread (clamped
-    // indices, unused results dropped): a loop that waits for each
-    // device-scope load before the next would pay a memory round trip per
-    // element.
-    {
-        constexpr int kPer = kMaxK / kNT;  // nsure < K <= kMaxK
-        int cs[kPer];
-        uint32_t kv[kPer];
-        const int last = max(nsure - 1, 0);
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) cs[j] = nsure > 0 ? ld_dev(sure + min(j * kNT + static_cast<int>(threadIdx.x), last)) : 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) kv[j] = p.sort_by_key && nsure > 0 ? key_of(p, prow, srow, cs[j]) : 0u;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = j * kNT + static_cast<int>(threadIdx.x);
-            if (i < nsure) fin[i] = fin_val(cs[j], kv[j]);
+    // ---- last workgroup of this row ----
+    // chunk c's entries sit at [c kChunk, c kChunk + n_c) of the lists;
+    // thread t sums the counts of its (contiguous) chunks, one scan places them
+    const int cpt = (nch + kNT - 1) / kNT;
+    int csum = 0;
+    for (int j = 0; j < cpt; ++j) {
+        const int c = static_cast<int>(threadIdx.x) * cpt + j;
+        csum += c < nch ? ld_dev(ccnt + c) : 0;
+    }
+    int total;
+    int cb = block_excl_scan(csum, sh.scan, &total);
+    for (int j = 0; j < cpt; ++j) {
+        const int c = static_cast<int>(threadIdx.x) * cpt + j;
+        if (c < nch) {
+            sh.cbase[c] = cb;
+            cb += ld_dev(ccnt + c);
         }
     }
-    if (b1 >= 0) {
-        // every candidate shares the key's top 12 bits (bin b1)
-        const unsigned long long known = static_cast<unsigned long long>(static_cast<uint32_t>(b1) << kBinShift) << 32;
-        unsigned long long thr;
-        if (ncand <= kCandCap) {
-            constexpr int kPer = kCandCap / kNT;
-            const int last = max(ncand - 1, 0);
-            int cc[kPer];
-            uint32_t ck[kPer];
+    if (threadIdx.x == 0) sh.cbase[nch] = total;
+    __syncthreads();
+    // list slot of entry e: its chunk is the last one starting at or below e
+    // (a binary search: the crowded path's; the LDS path uses a table)
+    auto slot_of = [&](int e) {
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.cbase[mid] <= e) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo * kChunk + (e - sh.cbase[lo]);
+    };
+    // every candidate shares the key's top 12 bits (bin b1)
+    const unsigned long long known = static_cast<unsigned long long>(static_cast<uint32_t>(b1 < 0 ? 0 : b1) << kBinShift) << 32;
+    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
+    int take = 0;
+    if (total == 0) {
+        // nothing selectable in the row
+    } else if (total <= kEntCap) {
+        // Entry e = j kNT + t is thread t's j-th (LDS accesses by consecutive
+        // threads hit consecutive words).  Its chunk comes from a table that
+        // each wave fills for its chunks, 64 entries at a time; then every
+        // entry's list loads go out at once.
+        constexpr int kEP = kEntCap / kNT;
+        int* owner = sh.col;  // the column array is filled only after the loads
+        for (int c = wave; c < nch; c += kNW) {
+            const int b0 = sh.cbase[c], n = sh.cbase[c + 1] - b0;
+            for (int i = lane; i < n; i += kWave) owner[b0 + i] = c;
+        }
+        __syncthreads();
+        uint32_t ek[kEP];
+        int ec[kEP];
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = min(j * kNT + static_cast<int>(threadIdx.x), last);
-                cc[j] = ncand > 0 ? ld_dev(gcol + i) : 0;
-                ck[j] = ncand > 0 ? ld_dev(gkey + i) : 0u;
+        for (int j = 0; j < kEP; ++j) {
+            const int e = min(j * kNT + static_cast<int>(threadIdx.x), total - 1);
+            const int c = owner[e];
+            const int s = c * kChunk + (e - sh.cbase[c]);
+            ek[j] = ld_dev(gkey + s);
+            ec[j] = ld_dev(gcol + s);
+        }
+        int er[kEP];
+#pragma unroll
+        for (int j = 0; j < kEP; ++j) er[j] = rec_of(p, prow, ec[j]);
+        __syncthreads();  // the histogram (overlaid by the key array) and the table are no longer read
+#pragma unroll
+        for (int j = 0; j < kEP; ++j) {
+            const int e = j * kNT + static_cast<int>(threadIdx.x);
+            if (e < total) {
+                sh.a.key[e] = ek[j];
+                sh.col[e] = ec[j];
+                sh.rec[e] = er[j];
             }
-            int cr[kPer];
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) cr[j] = rec_of(p, prow, cc[j]);
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = j * kNT + static_cast<int>(threadIdx.x);
-                if (i < ncand) {
-                    sh.u.fin.key[i] = ck[j];
-                    sh.u.fin.col[i] = cc[j];
-                    sh.u.fin.rec[i] = cr[j];
-                }
-            }
-            __syncthreads();
+        }
+        __syncthreads();
+        // the threshold among the boundary bin's entries (every entry is
+        // chosen when the row holds fewer than K)
+        unsigned long long thr = 0ull;
+        if (b1 >= 0) {
             auto src = [&](int i, uint32_t& key, int& rec) -> bool {
-                key = sh.u.fin.key[i];
-                rec = sh.u.fin.rec[i];
+                key = sh.a.key[i];
+                rec = sh.rec[i];
+                return static_cast<int>(key >> kBinShift) == b1;
+            };
+            thr = radix_select(src, total, need1, sh.hist8, sh.scan, 48, known);
+        }
+        // chosen entries in column order (= entry order): entry j kNT + t
+        // goes after the chosen ones of the earlier rows j, of the earlier
+        // waves in row j and of the earlier lanes of its wave (ballots)
+        bool cf[kEP];
+        unsigned long long cbal[kEP];
+#pragma unroll
+        for (int j = 0; j < kEP; ++j) {
+            const int e = j * kNT + static_cast<int>(threadIdx.x);
+            const int ei = min(e, total - 1);
+            const uint32_t k = sh.a.key[ei];
+            const int r = sh.rec[ei];
+            cf[j] = e < total && (static_cast<int>(k >> kBinShift) > b1 || composite(k, r) >= thr);
+            cbal[j] = __ballot(cf[j]);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < kEP; ++j) sh.cnt_wi[j][wave] = __popcll(cbal[j]);
+        }
+        __syncthreads();
+        const unsigned long long below = (1ull << lane) - 1ull;
+        int run2 = 0;
+        int at[kEP];
+#pragma unroll
+        for (int j = 0; j < kEP; ++j) {
+            int before = 0, tot = 0;
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) {
+                const int n = sh.cnt_wi[j][w];
+                before += w < wave ? n : 0;
+                tot += n;
+            }
+            at[j] = run2 + before + __popcll(cbal[j] & below);
+            run2 += tot;
+        }
+        take = min(run2, K);
+        if (!p.sort_by_key) {
+#pragma unroll
+            for (int j = 0; j < kEP; ++j)
+                if (cf[j] && at[j] < K) orow[at[j]] = sh.rec[j * kNT + static_cast<int>(threadIdx.x)];
+        } else {
+            // score order: the chosen composites, then a bitonic sort
+            unsigned long long cv[kEP];
+#pragma unroll
+            for (int j = 0; j < kEP; ++j) {
+                const int e = min(j * kNT + static_cast<int>(threadIdx.x), total - 1);
+                cv[j] = composite(sh.a.key[e], sh.rec[e]);
+            }
+            __syncthreads();  // the column array becomes the composite array
+            unsigned long long* fo = reinterpret_cast<unsigned long long*>(sh.col);
+#pragma unroll
+            for (int j = 0; j < kEP; ++j)
+                if (cf[j] && at[j] < K) fo[at[j]] = cv[j];
+        }
+    } else {
+        // a crowded boundary: select and filter straight from the lists
+        unsigned long long thr2 = 0ull;
+        if (b1 >= 0) {
+            auto src = [&](int i, uint32_t& key, int& rec) -> bool {
+                const int s = slot_of(i);
+                key = ld_dev(gkey + s);
+                if (static_cast<int>(key >> kBinShift) != b1) return false;
+                rec = rec_of(p, prow, ld_dev(gcol + s));
                 return true;
             };
-            thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
-            bool f[kPer];
-            int nf = 0;
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = j * kNT + static_cast<int>(threadIdx.x);
-                f[j] = i < ncand && composite(ck[j], cr[j]) >= thr;
-                nf += f[j] ? 1 : 0;
+            thr2 = radix_select(src, total, need1, sh.hist8, sh.scan, 48, known);
+        }
+        unsigned long long* fin = reinterpret_cast<unsigned long long*>(sh.col);
+        for (int base = 0; base < total; base += kNT) {
+            const int e = base + static_cast<int>(threadIdx.x);
+            bool f = false;
+            int r = 0;
+            uint32_t k = 0u;
+            if (e < total) {
+                const int s = slot_of(e);
+                k = ld_dev(gkey + s);
+                r = rec_of(p, prow, ld_dev(gcol + s));
+                f = static_cast<int>(k >> kBinShift) > b1 || composite(k, r) >= thr2;
             }
             int nt;
-            int at = nsure + block_excl_scan(nf, sh.scan, &nt);
-#pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                if (f[j]) fin[at++] = fin_val(cc[j], ck[j]);
+            const int at = take + block_excl_scan(f ? 1 : 0, sh.scan, &nt);
+            if (f && at < K) {
+                if (p.sort_by_key) fin[at] = composite(k, r);
+                else orow[at] = r;
+            }
             take += nt;
-        } else {  // a crowded boundary bin: select from the row's list
-            auto src = [&](int i, uint32_t& key, int& rec) -> bool {
-                key = ld_dev(gkey + i);
-                rec = rec_of(p, prow, ld_dev(gcol + i));
-                return true;
-            };
-            thr = radix_select(src, ncand, need1, sh.a.h.hist8, sh.scan, 48, known);
-            for (int base = 0; base < ncand; base += kNT) {
-                const int i = base + static_cast<int>(threadIdx.x);
-                uint32_t k = 0u;
-                int c = 0;
-                bool f = false;
-                if (i < ncand) {
-                    k = ld_dev(gkey + i);
-                    c = ld_dev(gcol + i);
-                    f = composite(k, rec_of(p, prow, c)) >= thr;
-                }
-                int nt;
-                const int at = take + block_excl_scan(f ? 1 : 0, sh.scan, &nt);
-                if (f) fin[at] = fin_val(c, k);
-                take += nt;
-            }
         }
+        take = min(take, K);
     }
-    __syncthreads();
-    take = min(take, K);
-    int32_t* orow = p.idx + static_cast<size_t>(row) * K;
-    auto out_of = [&](unsigned long long v) -> int32_t {
-        return p.sort_by_key ? static_cast<int32_t>(~static_cast<uint32_t>(v)) : rec_of(p, prow, static_cast<int>(v));
-    };
     for (int i = take + threadIdx.x; i < K; i += kNT) orow[i] = -1;
-    if (!p.sort_by_key && p.ncols <= kBitWords * 32) {
-        // column order: mark the chosen columns in a bitmap, then each
-        // thread writes the set bits of its run of words at its place
-        // from one block scan of the popcounts
-        const int nw = (p.ncols + 31) / 32;
-        const int nz = (bit_slot(nw) + 3) >> 2;  // 16-byte words; the array holds a multiple of 4
-        for (int i = threadIdx.x; i < nz; i += kNT) reinterpret_cast<uint4*>(sh.a.bits)[i] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
-        for (int i = threadIdx.x; i < take; i += kNT) {
-            const int c = static_cast<int>(fin[i]);
-            atomicOr(&sh.a.bits[bit_slot(c >> 5)], 1u << (c & 31));
-        }
-        __syncthreads();
-        constexpr int kWpt = kBitWords / kNT;  // words per thread at most
-        const int wpt = (nw + kNT - 1) / kNT;
-        const int w0 = static_cast<int>(threadIdx.x) * wpt;
-        unsigned wv[kWpt];  // this thread's words, all read at once
-        int cntb = 0;
-#pragma unroll
-        for (int k = 0; k < kWpt; ++k) wv[k] = sh.a.bits[bit_slot(w0 + k)];  // w0 + k < kBitWords always
-#pragma unroll
-        for (int k = 0; k < kWpt; ++k) {
-            if (!(k < wpt && w0 + k < nw)) wv[k] = 0u;  // not this thread's, or past the zeroed words
-            cntb += __popc(wv[k]);
-        }
-        int total;
-        int pos = block_excl_scan(cntb, sh.scan, &total);
-        // columns in order into LDS (fin is free once marked), then one
-        // coalesced pass maps them to records and writes the row (a store
-        // per set bit would also wait, at each pool read, for the stores
-        // before it)
-        int* outc = reinterpret_cast<int*>(fin);
-#pragma unroll
-        for (int k = 0; k < kWpt; ++k) {
-            unsigned bw = wv[k];
-            while (bw) {
-                const int bit = __ffs(static_cast<int>(bw)) - 1;
-                bw &= bw - 1u;
-                outc[pos++] = 32 * (w0 + k) + bit;
-            }
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < take; i += kNT) orow[i] = rec_of(p, prow, outc[i]);
-        return;
-    }
-    // otherwise a bitonic sort in LDS (log^2 stages, one block pass each)
+    if (!p.sort_by_key) return;
+    // score order: bitonic sort of the chosen composites (log^2 stages, one
+    // block pass each), descending
+    __syncthreads();
+    unsigned long long* fin = reinterpret_cast<unsigned long long*>(sh.col);
     int m2 = 1;
     while (m2 < take) m2 <<= 1;
-    // pad so the padding sorts last: descending by key, ascending by column
-    for (int i = take + threadIdx.x; i < m2; i += kNT) fin[i] = p.sort_by_key ? 0ull : ~0ull;
+    for (int i = take + threadIdx.x; i < m2; i += kNT) fin[i] = 0ull;  // padding sorts last
     __syncthreads();
     for (int k = 2; k <= m2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
@@ -1107,14 +1119,13 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
                 if (ij > i) {
                     const unsigned long long a = fin[i], b = fin[ij];
                     const bool first = (i & k) == 0;
-                    const bool swap = p.sort_by_key ? (first ? a < b : a > b) : (first ? a > b : a < b);
-                    if (swap) { fin[i] = b; fin[ij] = a; }
+                    if (first ? a < b : a > b) { fin[i] = b; fin[ij] = a; }
                 }
             }
             __syncthreads();
         }
     }
-    for (int i = threadIdx.x; i < take; i += kNT) orow[i] = out_of(fin[i]);
+    for (int i = threadIdx.x; i < take; i += kNT) orow[i] = static_cast<int32_t>(~static_cast<uint32_t>(fin[i]));
 }
 
 // One wave per block: beta[row][j] = max over columns [j*blk, min((j+1)*blk, N)).
@@ -1138,7 +1149,7 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* scores, int
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct LongLayout {
-    size_t hist, cnt, sure, ckey, ccol, total;
+    size_t hist, cnt, ccnt, ckey, ccol, total;
 };
 
 LongLayout long_layout(int rows, int ncols, int K) {
@@ -1149,8 +1160,8 @@ LongLayout long_layout(int rows, int ncols, int K) {
     off += align256(static_cast<size_t>(rows) * (nchk <= kFewChunks ? nchk : 1) * kBins * sizeof(int));
     L.cnt = off;
     off += align256(static_cast<size_t>(rows) * 4 * sizeof(int));
-    L.sure = off;
-    off += align256(static_cast<size_t>(rows) * K * sizeof(int));
+    L.ccnt = off;
+    off += align256(static_cast<size_t>(rows) * nchk * sizeof(int));
     L.ckey = off;
     off += align256(static_cast<size_t>(rows) * ncols * sizeof(uint32_t));
     L.ccol = off;
@@ -1196,10 +1207,11 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
     uint8_t* base = static_cast<uint8_t*>(ws);
     p.ghist = reinterpret_cast<int*>(base + L.hist);
     p.cnt = reinterpret_cast<int*>(base + L.cnt);
-    p.sure = reinterpret_cast<int*>(base + L.sure);
+    p.ccnt = reinterpret_cast<int*>(base + L.ccnt);
     p.ckey = reinterpret_cast<uint32_t*>(base + L.ckey);
     p.ccol = reinterpret_cast<int*>(base + L.ccol);
     p.nchunks = (p.ncols + kChunk - 1) / kChunk;
+    if (p.nchunks > kMaxChunks) return static_cast<int>(hipErrorInvalidValue);
     if (p.nchunks > kFewChunks) hipLaunchKernelGGL(topk_zero_kernel, dim3(p.rows), dim3(kNT), 0, st, p);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);
     hipLaunchKernelGGL(topk_select_kernel, dim3(p.nchunks, p.rows), dim3(kNT), 0, st, p);

@@ -273,6 +273,77 @@ def test_topk_many_rows(pooled, ncols):
             assert np.array_equal(got, ref), f"row {r}"
 
 
+def test_topk_long_rows_few_selectable():
+    """Rows over many chunks with nothing selectable (-inf, NaN), a single
+    selectable score, and fewer selectable scores than K."""
+    _case("topk long rows with few or no selectable scores")
+    n, K = 70000, 512
+    s = np.full((4, n), -np.inf, dtype=np.float32)
+    s[1, :] = np.nan
+    s[2, 54321] = 1.5
+    rng = np.random.default_rng(3)
+    cols = rng.choice(n, 300, replace=False)
+    s[3, cols] = rng.standard_normal(300).astype(np.float32)
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(4):
+        ref = np.sort(_ref_topk(s[r], K))
+        got = g[r][g[r] >= 0]
+        assert np.array_equal(got, ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1), f"row {r}"
+
+
+@pytest.mark.parametrize("blk,P,K", [(64, 700, 500), (2, 9000, 2048), (1, 12000, 300)])
+def test_topk_long_pooled_rows(blk, P, K):
+    """Pooled rows past the one-workgroup paths (P*blk columns: 44800 with
+    blk=64; 18000 and 12000 with blocks of 1-2, where the row's columns are
+    split over chunks, few enough with blk=1 that each keeps its own
+    histogram): exact ties, -inf scores and -1 pool blocks; the chosen
+    records in column order."""
+    _case(f"topk long pooled rows blk={blk} P={P} K={K}")
+    rows, ncols = 3, P * blk
+    rng = np.random.default_rng(blk + P + K)
+    s = (rng.integers(0, 60, size=(rows, ncols)) / 60.0).astype(np.float32)
+    s[0] = rng.standard_normal(ncols).astype(np.float32)
+    s[1, ::5] = -np.inf
+    pool = np.stack([rng.permutation(2 * P + 11)[:P] for _ in range(rows)]).astype(np.int32)
+    pool[2, ::9] = -1
+    g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K, pool=torch.from_numpy(pool).cuda(), blk=blk)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    cols = np.arange(ncols)
+    for r in range(rows):
+        pb = pool[r][cols // blk]
+        rec = np.where(pb < 0, -1, pb * blk + cols % blk)
+        ref = rec[_ref_topk(s[r], K, rec)]
+        got = g[r][g[r] >= 0]
+        assert set(got.tolist()) == set(ref.tolist()) and len(got) == len(ref), f"row {r}"
+        assert np.all(g[r][len(ref):] == -1), f"row {r}"
+        col_of = {int(v): i for i, v in enumerate(rec) if v >= 0}
+        assert all(col_of[int(a)] < col_of[int(b)] for a, b in zip(got[:-1], got[1:])), f"row {r}"
+
+
+@pytest.mark.parametrize("blk,P,N", [(4, 300, 80000), (2, 100, 20000)])
+def test_block_pool_long_rows(blk, P, N):
+    """Block pooling over 20000 and 10000 blocks: the score-ordered Top-K
+    over long rows (split over chunks; with 10000 blocks few enough chunks
+    that each keeps its own histogram), with ties between blocks."""
+    _case(f"block_pool long rows blk={blk} P={P} N={N}")
+    rng = np.random.default_rng(blk * P)
+    s = (rng.integers(0, 1000, size=(3, N)) / 1000.0).astype(np.float32)
+    s[0] = rng.standard_normal(N).astype(np.float32)
+    s[1, N // 2:] = -np.inf
+    g = Bd.csa2_block_pool(torch.from_numpy(s).cuda(), blk, P)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    for r in range(3):
+        fin = np.nonzero(np.isfinite(s[r]))[0]
+        ref = O.block_pool(s[r][fin].astype(np.float64), fin, blk, P)
+        got = g[r][g[r] >= 0]
+        assert np.array_equal(got, np.asarray(ref)), f"row {r}"
+
+
 @pytest.mark.parametrize("blk,P,N", [(4, 8, 128), (64, 64, 65536), (8, 2048, 20000)])
 def test_block_pool_exact(blk, P, N):
     _case(f"block_pool blk={blk} P={P} N={N}")
