@@ -1151,15 +1151,27 @@ constexpr int kCUs = 256;
 // groups fit on the chip at once; otherwise 64 heads per item.
 bool decode_layout(int Q) { return 4 * Q <= kCUs; }
 
+// Bytes of split partials (fp32 O, then (max, sum) per head) for Q
+// queries in ns splits.
+size_t part_bytes(int Q, int ns) {
+    if (ns <= 1) return 0;
+    const size_t o = static_cast<size_t>(Q) * ns * kH * kD * sizeof(float);
+    const size_t ml = static_cast<size_t>(Q) * ns * kH * 2 * sizeof(float);
+    return ((o + 255) & ~static_cast<size_t>(255)) + ((ml + 255) & ~static_cast<size_t>(255));
+}
+
 // Entry splits per query.  Every split writes an fp32 partial O of its
 // heads that attn_combine_kernel reads back, so splits are used only in
 // the decode layout, while its items would otherwise leave most compute
 // units idle: about 128 items in all (four per split; 256 in dense mode,
 // whose lists are long), and wherever a split would hold more entries than
-// the entry table (kMaxEnt).  Sparse shapes then never need more than 62
-// splits' worth of partials (7.8 MiB).  K is the longest list of records
+// the entry table (kMaxEnt).  (With 64-head items the partials' round trip
+// -- 128 KiB per split and query, written and read back -- costs as much as
+// the added parallelism gains: 80 queries in three splits measured slower
+// than unsplit.)  The splits taken only for parallelism are reduced until
+// the partials fit part_cap bytes.  K is the longest list of records
 // (dense mode: N).
-int choose_splits(int Q, int K, int W, bool dense, int& per) {
+int choose_splits(int Q, int K, int W, bool dense, int& per, size_t part_cap) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
     const int need = (ntiles * kTile + kMaxEnt - 1) / kMaxEnt;  // splits the entry table needs
@@ -1172,8 +1184,13 @@ int choose_splits(int Q, int K, int W, bool dense, int& per) {
     if (ns > ntiles) ns = ntiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
+    auto fit = [&](int n) {  // n splits as equal tile counts
+        const int tps = (ntiles + n - 1) / n;
+        return (ntiles + tps - 1) / tps;
+    };
+    ns = fit(ns);
+    while (ns > need && ns > 1 && part_bytes(Q, ns) > part_cap) ns = fit(ns - 1);
     const int tps = (ntiles + ns - 1) / ns;  // tiles per split
-    ns = (ntiles + tps - 1) / tps;
     per = tps * kTile;
     return ns;
 }
@@ -1226,22 +1243,14 @@ size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W) {
     if (H != kH || D != kD) return 0;
     int per;
     const int Q = B * Tq;
-    const int ns = choose_splits(Q, N, W, true, per);
-    if (ns == 1) return 0;
-    const size_t o = static_cast<size_t>(Q) * ns * kH * kD * sizeof(float);
-    const size_t ml = static_cast<size_t>(Q) * ns * kH * 2 * sizeof(float);
-    return ((o + 255) & ~static_cast<size_t>(255)) + ((ml + 255) & ~static_cast<size_t>(255));
+    return part_bytes(Q, choose_splits(Q, N, W, true, per, SIZE_MAX));
 }
 
-size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W) {
+size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W, size_t part_cap) {
     if (H != kH || D != kD) return 0;
     int per;
     const int Q = B * Tq;
-    const int ns = choose_splits(Q, K, W, false, per);
-    if (ns == 1) return 0;
-    const size_t o = static_cast<size_t>(Q) * ns * kH * kD * sizeof(float);
-    const size_t ml = static_cast<size_t>(Q) * ns * kH * 2 * sizeof(float);
-    return ((o + 255) & ~static_cast<size_t>(255)) + ((ml + 255) & ~static_cast<size_t>(255));
+    return part_bytes(Q, choose_splits(Q, K, W, false, per, part_cap));
 }
 
 int launch_sparse_attn(const AttnArgs& a, void* stream) {
@@ -1267,7 +1276,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         const bool dec = decode_layout(Q);
         p.dense_m = a.dense_m;
         p.n_rec = a.n_rec;
-        p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, a.dense_m > 0, p.per_split);
+        p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, a.dense_m > 0, p.per_split, a.part_cap);
         p.part_o = nullptr;
         p.part_ml = nullptr;
         if (p.nsplit > 1) {

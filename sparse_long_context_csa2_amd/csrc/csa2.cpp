@@ -260,8 +260,10 @@ int csa2_sparse_attn_noalloc(int B, int Tq, int H, int D, int N, int K, const vo
               q_pos, sink, sm_scale, rope_dims, rope_base, out, out_dtype, nullptr, 0);
     int e = validate_attn(a);
     if (e) return e;
-    const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W);
+    // splits taken only for parallelism give way to the static scratch size
     const size_t have = csa2::sparse_attn_scratch_bytes();
+    a.part_cap = have;
+    const size_t need = csa2::sparse_attn_ws_bytes(B, Tq, H, D, K, W, have);
     if (need > have)
         return fail(CSA2_EWORKSPACE,
                     "sparse_attn_noalloc: this shape needs %zu bytes of scratch, above the static %zu "

@@ -70,9 +70,10 @@ struct AttnArgs {
     size_t ws_bytes;
     int dense_m = 0;                // > 0: dense mode (no idx; all visible records at ratio dense_m)
     const int32_t* n_rec = nullptr;  // dense mode: [B] or null (= N)
+    size_t part_cap = SIZE_MAX;      // most bytes of split partials the splits taken for parallelism may use
 };
 bool sparse_attn_mfma_ok(const AttnArgs& a);
-size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W);
+size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W, size_t part_cap = SIZE_MAX);
 size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W);
 int launch_sparse_attn(const AttnArgs& a, void* stream);
 // The allocation-free entry point's static scratch: its size, and its

@@ -20,13 +20,13 @@ from tests import parity as PR
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(B, K, W, kdt, seed):
+def _inputs(B, K, W, kdt, seed, Tq=1):
     N = 4096
-    wl = WL.Workload(name="noalloc", seed=seed, B=B, Tq=1, N=N, m=4, Hi=32, Di=128, H=64, D=512, rope_dims=64,
-                     W=W, K=K, decode_pos=5 * N, k_dtype=kdt, kv_dtype=kdt, swa_dtype=kdt, swa_slots=W + 3)
+    wl = WL.Workload(name="noalloc", seed=seed, B=B, Tq=Tq, N=N, m=4, Hi=32, Di=128, H=64, D=512, rope_dims=64,
+                     W=W, K=K, decode_pos=5 * N, k_dtype=kdt, kv_dtype=kdt, swa_dtype=kdt, swa_slots=W + Tq + 3)
     inp = WL.make_inputs(wl)
     rng = np.random.default_rng(seed)
-    idx = np.stack([rng.permutation(N)[:K] for _ in range(B)])[:, None, :].astype(np.int32)
+    idx = np.stack([[rng.permutation(N)[:K] for _ in range(Tq)] for _ in range(B)]).astype(np.int32)
     idx[0, 0, 3] = -1
     return wl, inp, idx
 
@@ -68,3 +68,30 @@ def test_noalloc_matches_workspace_entry_point(kdt):
             for b in (0, B - 1):
                 PR.check_attn_query(g[b, 0], sh, lay, b, 0, idx[b, 0], kdt, f"call {call} b={b} vs oracle")
         print(f"max |noalloc - workspace| = {np.abs(g - r).max():.3g}", flush=True)
+
+
+def test_noalloc_fewer_splits_when_scratch_is_short():
+    """28 queries of one sequence: with a workspace the call splits every
+    query's entries two ways (7.3 MB of partials); without one the splits
+    taken only for parallelism give way to the 6 MiB scratch (here: none),
+    and the result agrees with the workspace call to the attention bound."""
+    L = Bd.lib()
+    B, Tq, K, W = 1, 28, 512, 128
+    print(f"[case] noalloc fewer splits: B={B} Tq={Tq} K={K} W={W}", flush=True)
+    wl, inp, idx = _inputs(B, K, W, "bf16", 50, Tq=Tq)
+    sh, lay = inp["shared"], inp["layers"][0]
+    assert L.csa2_sparse_attn_workspace_bytes(B, Tq, 64, 512, K, W) > 6 << 20
+    d = {k: R.to_device(v) for k, v in (("q", lay["q"]), ("kv", sh["kv"]), ("kvs", sh["kv_scale"]),
+                                        ("idx", idx), ("swa", lay["swa"]), ("swas", lay["swa_scale"]),
+                                        ("pos", lay["q_pos"]), ("sink", lay["sink"]))}
+    ref = Bd.csa2_sparse_attn(d["q"], d["kv"], d["kvs"], d["idx"], d["swa"], d["swas"], W, d["pos"], d["sink"], 64)
+    out = torch.full_like(ref, float("nan"))
+    rc = _noalloc(L, d["q"], d["kv"], d["kvs"], d["idx"], d["swa"], d["swas"], W, d["pos"], d["sink"], out)
+    assert rc == 0, L.csa2_status_str(rc).decode()
+    torch.cuda.synchronize()
+    g, r = out.cpu().numpy(), ref.cpu().numpy()
+    assert np.isfinite(g).all()
+    for ti in (0, 1, Tq // 2, Tq - 1):
+        rows = PR.entry_rows(sh, lay, 0, ti, idx[0, ti])
+        PR.check_attn(g[0, ti], r[0, ti], PR.attn_tol("bf16", rows), f"t={ti} vs csa2_sparse_attn")
+        PR.check_attn_query(g[0, ti], sh, lay, 0, ti, idx[0, ti], "bf16", f"t={ti} vs oracle")
