@@ -202,17 +202,18 @@ def _attn_noalloc(L, **kw):
 
 
 def test_sparse_attn_noalloc_validation(L):
-    """The allocation-free entry point validates like csa2_sparse_attn and
-    refuses, before touching any device, a shape whose split partials need
-    more than its 6 MiB static scratch (24 queries x 640 entries need
-    6.02 MiB)."""
+    """The allocation-free entry point validates like csa2_sparse_attn.  A
+    shape whose workspace call splits its queries into more partials than
+    the 6 MiB static scratch holds (24 queries x 640 entries at two splits:
+    6.02 MiB) is not refused: the splits taken only for parallelism give
+    way, so it passes validation and fails here only at the launch (no
+    device on this host)."""
     assert _attn_noalloc(L, W=129) == B.CSA2_EINVAL
     assert _attn_noalloc(L, out=FAKE + 8) == B.CSA2_EINVAL
     assert _attn_noalloc(L, kvdt=2) == B.CSA2_EINVAL
     need = L.csa2_sparse_attn_workspace_bytes(24, 1, 64, 512, 512, 128)
     assert need > 6 << 20
-    assert _attn_noalloc(L, B=24, K=512) == B.CSA2_EWORKSPACE
-    assert "static" in L.csa2_status_str(B.CSA2_EWORKSPACE).decode()
+    assert _attn_noalloc(L, B=24, K=512) == B.CSA2_EHIP
     # the decode shapes of the benchmark fit
     for Q in (8, 16, 64):
         assert L.csa2_sparse_attn_workspace_bytes(Q, 1, 64, 512, 512, 128) <= 6 << 20
