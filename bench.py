@@ -269,10 +269,15 @@ def traffic_for(workload, kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", rec.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+    files = rec.get("source", [])
+    files = [files] if isinstance(files, str) else files
+    h = hashlib.sha256()
+    for f in files:
+        src = os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if not files or h.hexdigest() != rec.get("source_sha256"):
         return None
     return rec.get("bytes_per_launch")
 

@@ -20,7 +20,11 @@ BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
-SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "compress.hip", "csa2.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "attn_dec.hip", "compress.hip", "csa2.cpp"]
+
+# Per-source flags: the decode attention layout accumulates its matrix
+# instructions in VGPRs (its output is small enough to stay there).
+EXTRA = {"attn_dec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -32,7 +36,7 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(SRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

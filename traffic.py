@@ -33,9 +33,19 @@ COPY_BYTES = 256 << 20
 MARK = "bitwise_not"   # kernel-name fragment of the group markers
 COPY = "MulFunctor"    # kernel-name fragment of the reference copy
 
-# source file of each ABI call's kernels
-SOURCE = {"attn": "attn.hip", "attn_dense": "attn.hip", "index_full": "indexer.hip", "index_pool": "indexer.hip",
-          "topk_full": "topk.hip", "topk_pool": "topk.hip", "block_pool": "topk.hip", "compress": "compress.hip"}
+# source files of each ABI call's kernels
+_ATTN = ["attn.hip", "attn_kernel.h", "attn_dec.hip"]
+SOURCE = {"attn": _ATTN, "attn_dense": _ATTN, "index_full": ["indexer.hip"], "index_pool": ["indexer.hip"],
+          "topk_full": ["topk.hip"], "topk_pool": ["topk.hip"], "block_pool": ["topk.hip"],
+          "compress": ["compress.hip"]}
+
+
+def source_sha256(files) -> str:
+    """SHA-256 over the listed kernel sources (csrc/), concatenated in order."""
+    h = hashlib.sha256()
+    for f in ([files] if isinstance(files, str) else files):
+        h.update(open(os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def _run(workload: str) -> None:
@@ -182,9 +192,8 @@ def _summarize(workload: str, fetch_dir: str, write_dir: str, calls) -> None:
                      for name, _ in groups[gi]}
         per = tot["FETCH_SIZE"] + tot["WRITE_SIZE"]
         src = SOURCE[call]
-        src_path = os.path.join(ROOT, "sparse_long_context_csa2_amd", "csrc", src)
         rec = {"workload": workload, "call": call, "source": src,
-               "source_sha256": hashlib.sha256(open(src_path, "rb").read()).hexdigest(),
+               "source_sha256": source_sha256(src),
                "kernels": sorted(kern),
                "fetch_bytes_per_launch": round(tot["FETCH_SIZE"]),
                "write_bytes_per_launch": round(tot["WRITE_SIZE"]),
