@@ -386,9 +386,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         for (int i = 0; i < kQS; ++i) f.q[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 8 * (4 * (kb + i) + g)));
     };
 
-    // the pow() is far costlier than the per-item angle, so it runs once
-    for (int i = tid; i < p.rope_dims / 2; i += kThreads) sh.rope_inv[i] = rope_inv_freq(i, p.rope_dims, p.rope_base);
-
     ItemFetch nx;
     const int R = (n_items + G - 1) / G;  // rounds
     // decode: rounds in order, item r*G + g (G is a multiple of 8, so a
@@ -409,6 +406,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         fetch(item, nx);
         fetch_q(item, nx);
     }
+    // the pow() is far costlier than the per-item angle, so it runs once,
+    // while the first item's inputs are on their way
+    for (int i = tid; i < p.rope_dims / 2; i += kThreads) sh.rope_inv[i] = rope_inv_freq(i, p.rope_dims, p.rope_base);
     settle_fetch(nx);
 
     // Output of an item.  It runs once the next item's first tile copies

@@ -105,10 +105,19 @@ __device__ __forceinline__ void key_operands(const u32x4 (&raw)[4], float scale,
 
 // Decode scoring: one query token per row (or any pooled row).  The four
 // waves of a workgroup take alternate 16-record tiles of the row's column
-// range; each lane loads its record's key bytes straight into registers
-// (non-temporal: every key row is read once per call), several tiles
-// ahead of the one being multiplied.  Scores collect in LDS and leave as whole
-// column runs at the end: no store sits between a prefetch and its wait.
+// range.  A tile's 16 key rows are loaded into registers as whole rows: load
+// i of the wave reads 1 KiB, lane l taking 16 bytes (chunk l mod C of row
+// 64 i / C + l / C, C = 16-byte chunks per row; non-temporal, as every key
+// row is read once per call), several tiles ahead of the one being
+// multiplied.  Before its MFMAs the wave passes the tile through its own
+// LDS buffer into the operand layout (lane (n, g) takes record n's chunks
+// of lane group g), chunk c of row r at slot c ^ (r mod C) so that neither
+// pass has bank conflicts.  (Loading the operand layout directly -- 16
+// rows x 64 bytes per instruction -- streams about 13% slower.)  MXFP4 rows
+// are 64 bytes, so a lane's operand chunk (record n, MX block g) is loaded
+// directly: one instruction then reads the tile's contiguous 1 KiB.  Scores
+// collect in LDS and leave as whole column runs at the end: no store sits
+// between a prefetch and its wait.
 constexpr int kDecTpbMax = 128;  // tiles per workgroup, at most
 
 // QMX (MXFP4 queries and keys): the scores come from gfx950's block-scaled
@@ -127,14 +136,25 @@ __device__ __forceinline__ f32x4 mfma_mx4(const u32x4& a, int sa, const u32x4& b
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, c, 4, 4, 0, sa, 0, sb);
 }
 
-template <int KDT, bool QMX = false>
+// POOL: the row's columns are pooled blocks of records (p.pool); otherwise
+// column c is record c and a tile's loads form one straight-line sequence,
+// so that the waits before each tile's multiply count only that tile's
+// loads (an invisible row is read from record 0 and its score dropped).
+template <int KDT, bool QMX, bool POOL>
 __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : (KDT == DT_MXFP4 ? kDi / 2 : kDi);
+    constexpr int kCPR = kRowBytes / 16;  // 16-byte chunks per key row
+    constexpr int kRPI = 64 / kCPR;       // rows per 1 KiB load
+    constexpr int kLI = 16 / kRPI;        // loads per 16-row tile
+    constexpr bool kTr = KDT != DT_MXFP4;  // tiles pass through LDS into the operand layout
     __shared__ float osc[kDecTpbMax * 16];
+    __shared__ __align__(16) uint8_t ktr[kTr ? 4 : 1][kTr ? 16 * kRowBytes : 16];  // per-wave tile transpose
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : (KDT == DT_MXFP4 ? kDi / 2 : kDi);
+    const int lr = lane / kCPR;  // the lane's row within a load
+    const int lc = lane % kCPR;  // and its chunk
 
     const int b = blockIdx.y / p.Tq;
     const int tok = blockIdx.y % p.Tq;
@@ -166,8 +186,9 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     const int ntiles = (p.ncols + 15) / 16;
     const int t_begin = blockIdx.x * p.tiles_per_block;
     const int t_end = min(ntiles, t_begin + p.tiles_per_block);
-    const int32_t* prow = p.pool ? p.pool + row * p.P : nullptr;
+    const int32_t* prow = POOL ? p.pool + row * p.P : nullptr;
     const uint8_t* kbase = p.k + static_cast<size_t>(b) * p.N * kRowBytes;
+    const int lim = min(vis, t_end * 16);  // !POOL: records this workgroup reads (vis <= N = ncols)
 
     struct Tile {
         int rec;
@@ -178,38 +199,72 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     };
     auto fetch = [&](int ti, Tile& T) {
         const int c = ti * 16 + n;
-        T.rec = -1;
-        if (c < p.ncols) {
-            if (prow) {
+        bool ld;
+        if constexpr (POOL) {
+            T.rec = -1;
+            if (c < p.ncols) {
                 const int pb = prow[c / p.blk];
                 T.rec = pb < 0 ? -1 : pb * p.blk + c % p.blk;
-            } else {
-                T.rec = c;
             }
+            ld = T.rec >= 0 && T.rec < vis;
+            T.any = __any(ld);
+        } else {
+            T.rec = c;
+            ld = c < lim;
+            T.any = ti * 16 < lim;
         }
-        const bool ld = T.rec >= 0 && T.rec < vis;
-        T.any = __any(ld);
         T.kscale = 1.f;
         T.kblk = 0;
-        if (T.any) {
+        if (POOL && !T.any) return;
+        if constexpr (!kTr) {  // MXFP4: the lane's operand chunk
             load_key_raw<KDT>(kbase + static_cast<size_t>(ld ? T.rec : 0) * kRowBytes, g, T.raw);
-            if (KDT == DT_E4M3)
-                T.kscale = ld ? static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
-            if (KDT == DT_MXFP4)
-                T.kblk = static_cast<const uint32_t*>(p.ks)[static_cast<size_t>(b) * p.N + (ld ? T.rec : 0)];
+        } else {
+            // whole rows: load i brings rows kRPI i .. +kRPI-1
+#pragma unroll
+            for (int i = 0; i < kLI; ++i) {
+                const int r = kRPI * i + lr;
+                const int rr = POOL ? __shfl(T.rec, r, 64) : ti * 16 + r;
+                const bool ok = rr >= 0 && rr < (POOL ? vis : lim);
+                T.raw[i] = ld16_nt(reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(ok ? rr : 0) * kRowBytes) + lc);
+            }
         }
+        // the scales of an invisible row are read from record 0 as well
+        if (KDT == DT_E4M3) T.kscale = static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + (ld ? T.rec : 0)];
+        if (KDT == DT_MXFP4)
+            T.kblk = static_cast<const uint32_t*>(p.ks)[static_cast<size_t>(b) * p.N + (ld ? T.rec : 0)];
     };
+    uint8_t* const tb = ktr[kTr ? wave : 0];
     auto score = [&](int ti, const Tile& T) {
         float val = -__builtin_huge_valf();
         if (T.any) {
+            u32x4 kr[4];  // the lane's chunks of record n, as load_key_raw lays them out
+            if constexpr (kTr) {
+                // rows -> operand layout through the wave's LDS buffer (one
+                // wave's LDS accesses complete in order: no wait between them)
+#pragma unroll
+                for (int i = 0; i < kLI; ++i) {
+                    const int r = kRPI * i + lr;
+                    *reinterpret_cast<u32x4*>(tb + r * kRowBytes + 16 * (lc ^ (r % kCPR))) = T.raw[i];
+                }
+                asm volatile("" ::: "memory");  // the reads below stay after the writes
+                constexpr int kChunks = (KDT == DT_BF16) ? 4 : 2;
+#pragma unroll
+                for (int j = 0; j < kChunks; ++j) {
+                    const int ch = g + 4 * j;
+                    kr[j] = *reinterpret_cast<const u32x4*>(tb + n * kRowBytes + 16 * (ch ^ (n % kCPR)));
+                }
+                asm volatile("" ::: "memory");  // and before the next tile's writes
+            } else {
+                kr[0] = T.raw[0];
+            }
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
             if constexpr (QMX) {
                 const int ksc = static_cast<int>((T.kblk >> (8 * g)) & 0xFFu);
-                acc0 = mfma_mx4(qmx[0], qmxs[0], T.raw[0], ksc, acc0);
-                acc1 = mfma_mx4(qmx[1], qmxs[1], T.raw[0], ksc, acc1);
+                acc0 = mfma_mx4(qmx[0], qmxs[0], kr[0], ksc, acc0);
+                acc1 = mfma_mx4(qmx[1], qmxs[1], kr[0], ksc, acc1);
             } else {
                 bf16x8 bk[4];
-                key_operands<KDT>(T.raw, KDT == DT_MXFP4 ? e8m0_to_f32(T.kblk >> (8 * g)) : 1.f, bk);
+                key_operands<KDT>(kr, KDT == DT_MXFP4 ? e8m0_to_f32(T.kblk >> (8 * g)) : 1.f, bk);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     acc0 = mfma16x16x32(qa[0][ks], bk[ks], acc0);
@@ -237,17 +292,35 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
     constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;  // MXFP4 tiles: a quarter of the bytes
     Tile tt[kRing];
     const int ti0 = t_begin + wave;
+    if constexpr (!POOL) {
+        // Every ring slot is always filled -- a tile past the range reads
+        // record 0 (an L2 hit) -- so no load is conditional and the wait
+        // before each tile's multiply leaves the later tiles' loads in
+        // flight (with conditional prefetches the compiler's count covers
+        // nearly all of them).
 #pragma unroll
-    for (int d = 0; d + 1 < kRing; ++d)
-        if (ti0 + 4 * d < t_end) fetch(ti0 + 4 * d, tt[d]);
-    for (int base = ti0; base < t_end; base += 4 * kRing) {
+        for (int d = 0; d + 1 < kRing; ++d) fetch(ti0 + 4 * d, tt[d]);
+        for (int base = ti0; base < t_end; base += 4 * kRing) {
 #pragma unroll
-        for (int d = 0; d < kRing; ++d) {
-            const int ti = base + 4 * d;
-            if (ti >= t_end) break;
-            const int tf = ti + 4 * (kRing - 1);
-            if (tf < t_end) fetch(tf, tt[(d + kRing - 1) % kRing]);
-            score(ti, tt[d]);
+            for (int d = 0; d < kRing; ++d) {
+                const int ti = base + 4 * d;
+                fetch(ti + 4 * (kRing - 1), tt[(d + kRing - 1) % kRing]);
+                if (ti < t_end) score(ti, tt[d]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d + 1 < kRing; ++d)
+            if (ti0 + 4 * d < t_end) fetch(ti0 + 4 * d, tt[d]);
+        for (int base = ti0; base < t_end; base += 4 * kRing) {
+#pragma unroll
+            for (int d = 0; d < kRing; ++d) {
+                const int ti = base + 4 * d;
+                if (ti >= t_end) break;
+                const int tf = ti + 4 * (kRing - 1);
+                if (tf < t_end) fetch(tf, tt[(d + kRing - 1) % kRing]);
+                score(ti, tt[d]);
+            }
         }
     }
     __syncthreads();
@@ -730,7 +803,8 @@ int launch_mfma(const IndexArgs& a, int tiles_per_block, hipStream_t st) {
     p.tiles_per_block = tiles_per_block;
     const int ntiles = (a.ncols + 15) / 16;
     dim3 grid((ntiles + tiles_per_block - 1) / tiles_per_block, a.B * a.Tq);
-    hipLaunchKernelGGL((idx_mfma_kernel<KDT, QMX>), grid, dim3(256), 0, st, p);
+    if (a.pool) hipLaunchKernelGGL((idx_mfma_kernel<KDT, QMX, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((idx_mfma_kernel<KDT, QMX, false>), grid, dim3(256), 0, st, p);
     return static_cast<int>(hipGetLastError());
 }
 

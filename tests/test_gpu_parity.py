@@ -101,10 +101,16 @@ def test_index_scores_mfma_prefill(kdt, Tq, N, n_rec):
             PR.check_scores(g[b, ti], O.full_row_scores(inp["shared"], inp["layers"][0], b, ti), f"b={b} t={ti}")
 
 
-@pytest.mark.parametrize("shape", ["mfma", "generic"])
+@pytest.mark.parametrize("shape", ["mfma", "mfma-blk4", "mfma-e4m3-blk8", "generic"])
 def test_index_scores_pool_mode(shape):
+    """Pool mode: blocks of 64 records (whole 16-record tiles), and blocks of
+    4 and 8 records, whose tiles gather rows from several pooled blocks."""
     if shape == "mfma":
         wl, blk, P = _small(N=2048, decode_pos=8000, n_rec=(2048, 1500, 2048)), 64, 6
+    elif shape == "mfma-blk4":
+        wl, blk, P = _small(N=2048, decode_pos=8000, n_rec=(2048, 1501, 7)), 4, 37
+    elif shape == "mfma-e4m3-blk8":
+        wl, blk, P = _small(N=1000, k_dtype="e4m3", decode_pos=3000, n_rec=(1000, 600, 999)), 8, 21
     else:
         wl, blk, P = _small(N=200, Hi=4, Di=16, q_idx_dtype="f32", k_dtype="f32", decode_pos=700), 4, 9
     _case(f"index_scores pool mode ({shape}, blk={blk}, P={P})")
