@@ -333,8 +333,9 @@ __global__ __launch_bounds__(256) void idx_mfma_kernel(IdxP p) {
 // Multi-query decode scoring: several query tokens of one sequence (2 .. 8,
 // e.g. the positions a speculative draft asks the model to verify, "Create
 // DeepSeek from scratch", "How DSpark drafts and verifies several tokens")
-// against all its records, no pool.  A key tile is loaded once, into
-// registers as in idx_mfma_kernel, and multiplied against every token: the
+// against all its records, no pool.  A key tile is loaded once, as whole
+// rows through a per-wave LDS transpose as in idx_mfma_kernel (with the same
+// unconditional prefetch ring), and multiplied against every token: the
 // M side of the products is Tq x 32 heads, so the keys cross HBM once per
 // sequence instead of once per token.  The tokens' queries sit in LDS (a
 // 256-byte head row keeps its 16-byte chunk c at slot c ^ (row mod 16), so
@@ -350,12 +351,19 @@ __global__ __launch_bounds__(256) void idx_multi_kernel(IdxP p) {
     uint8_t* qsh = msh;                                          // [Tq][32 heads][256 B], swizzled
     float* wsh = reinterpret_cast<float*>(msh + Tq * kHi * 256);  // [Tq][32]
     float* osc = wsh + Tq * kHi;                                 // [Tq][tpb * 16]
+    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    constexpr int kCPR = kRowBytes / 16;  // 16-byte chunks per key row
+    constexpr int kRPI = 64 / kCPR;       // rows per 1 KiB load
+    constexpr int kLI = 16 / kRPI;        // loads per 16-row tile
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    constexpr int kRowBytes = (KDT == DT_BF16) ? kDi * 2 : kDi;
+    const int lr = lane / kCPR;  // the lane's row within a load
+    const int lc = lane % kCPR;  // and its chunk
+    // per-wave tile transpose, after the scores
+    uint8_t* const tb = reinterpret_cast<uint8_t*>(osc + Tq * p.tiles_per_block * 16) + wave * 16 * kRowBytes;
     const int b = blockIdx.y;
     const int nrec = p.n_rec ? min(p.n_rec[b], p.N) : p.N;
     const int tpb = p.tiles_per_block;
@@ -384,21 +392,41 @@ __global__ __launch_bounds__(256) void idx_multi_kernel(IdxP p) {
         u32x4 raw[4];
         float kscale;
     };
+    const int lim = min(vmax, t_end * 16);  // records this workgroup reads (vmax <= N = ncols)
     auto fetch = [&](int ti, Tile& T) {
         const int c = ti * 16 + n;
-        T.rec = c < p.ncols ? c : -1;
-        const bool ld = T.rec >= 0 && T.rec < vmax;
-        T.any = __any(ld);
-        T.kscale = 1.f;
-        if (T.any) {
-            load_key_raw<KDT>(kbase + static_cast<size_t>(ld ? T.rec : 0) * kRowBytes, g, T.raw);
-            if (KDT == DT_E4M3)
-                T.kscale = ld ? static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + T.rec] : 0.f;
+        T.rec = c;
+        const bool ld = c < lim;
+        T.any = ti * 16 < lim;
+        // whole rows (a row no token may see is read from record 0)
+#pragma unroll
+        for (int i = 0; i < kLI; ++i) {
+            const int rr = ti * 16 + kRPI * i + lr;
+            T.raw[i] = ld16_nt(reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(rr < lim ? rr : 0) * kRowBytes) + lc);
         }
+        T.kscale = 1.f;
+        if (KDT == DT_E4M3) T.kscale = static_cast<const float*>(p.ks)[static_cast<size_t>(b) * p.N + (ld ? c : 0)];
     };
     auto score = [&](int ti, const Tile& T) {
         bf16x8 bk[4];
-        if (T.any) key_operands<KDT>(T.raw, 1.f, bk);
+        if (T.any) {
+            // rows -> operand layout through the wave's LDS buffer
+#pragma unroll
+            for (int i = 0; i < kLI; ++i) {
+                const int r = kRPI * i + lr;
+                *reinterpret_cast<u32x4*>(tb + r * kRowBytes + 16 * (lc ^ (r % kCPR))) = T.raw[i];
+            }
+            asm volatile("" ::: "memory");  // the reads below stay after the writes
+            u32x4 kr[4];
+            constexpr int kChunks = (KDT == DT_BF16) ? 4 : 2;
+#pragma unroll
+            for (int j = 0; j < kChunks; ++j) {
+                const int ch = g + 4 * j;
+                kr[j] = *reinterpret_cast<const u32x4*>(tb + n * kRowBytes + 16 * (ch ^ (n % kCPR)));
+            }
+            asm volatile("" ::: "memory");  // and before the next tile's writes
+            key_operands<KDT>(kr, 1.f, bk);
+        }
         for (int t = 0; t < Tq; ++t) {
             float val = -__builtin_huge_valf();
             if (T.any) {
@@ -430,17 +458,15 @@ __global__ __launch_bounds__(256) void idx_multi_kernel(IdxP p) {
     constexpr int kRing = (KDT == DT_BF16) ? 3 : 4;
     Tile tt[kRing];
     const int ti0 = t_begin + wave;
+    // every ring slot is always filled (tiles past the range read record 0)
 #pragma unroll
-    for (int d = 0; d + 1 < kRing; ++d)
-        if (ti0 + 4 * d < t_end) fetch(ti0 + 4 * d, tt[d]);
+    for (int d = 0; d + 1 < kRing; ++d) fetch(ti0 + 4 * d, tt[d]);
     for (int base = ti0; base < t_end; base += 4 * kRing) {
 #pragma unroll
         for (int d = 0; d < kRing; ++d) {
             const int ti = base + 4 * d;
-            if (ti >= t_end) break;
-            const int tf = ti + 4 * (kRing - 1);
-            if (tf < t_end) fetch(tf, tt[(d + kRing - 1) % kRing]);
-            score(ti, tt[d]);
+            fetch(ti + 4 * (kRing - 1), tt[(d + kRing - 1) % kRing]);
+            if (ti < t_end) score(ti, tt[d]);
         }
     }
     __syncthreads();
@@ -862,7 +888,8 @@ int launch_index_scores(const IndexArgs& a, void* stream) {
             p.pool = nullptr;
             p.out = a.scores;
             p.tiles_per_block = tpb;
-            const size_t lds = static_cast<size_t>(a.Tq) * (kHi * 256 + kHi * 4 + tpb * 16 * 4);
+            const size_t lds = static_cast<size_t>(a.Tq) * (kHi * 256 + kHi * 4 + tpb * 16 * 4) +
+                               4 * 16 * static_cast<size_t>(a.k_dtype == DT_BF16 ? kDi * 2 : kDi);
             const dim3 grid((ntiles + tpb - 1) / tpb, a.B);
             if (a.k_dtype == DT_BF16)
                 hipLaunchKernelGGL(idx_multi_kernel<DT_BF16>, grid, dim3(256), lds, st, p);
