@@ -265,9 +265,9 @@ size_t csa2_dense_attn_workspace_bytes(int B, int Tq, int H, int D, int N, int W
  * decode shapes with fewer than 32 queries), it uses a 6 MiB array that
  * the library holds in each GPU's memory for the life of the process.
  * Where the workspace call would split a shape's queries into more
- * partials than that (up to 7.8 MiB, 24-31 queries with long entry lists),
- * it takes fewer splits (those only add parallelism): same result to the
- * attention bound, not bit for bit.  CSA2_EWORKSPACE remains for a shape
+ * partials than that (up to 8 MiB: at most 64 partials of 128 KiB, e.g.
+ * 8 queries in 8 splits or 16 in 4), it takes fewer splits (those only add
+ * parallelism): same result to the attention bound, not bit for bit.  CSA2_EWORKSPACE remains for a shape
  * whose entry lists alone would need more.  All calls on one GPU share
  * that array, so calls that overlap on one GPU (other streams, other
  * threads) race; calls on different GPUs do not.  The first call on a

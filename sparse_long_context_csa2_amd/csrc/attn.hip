@@ -238,22 +238,24 @@ size_t part_bytes(int Q, int ns) {
 // Entry splits per query.  Every split writes an fp32 partial O of its
 // heads that attn_combine_kernel reads back, so splits are used only in
 // the decode layout, while its items would otherwise leave most compute
-// units idle: about 128 items in all (four per split; 256 in dense mode,
-// whose lists are long), and wherever a split would hold more entries than
+// units idle: at most 256 items in all, one per compute unit (four per
+// split; measured against 128 and 512: C4's 16 queries in four splits run
+// 8% faster than in two, and 21% faster than in eight), so at most 64
+// partials (8 MiB) for sparse lists; and wherever a split would hold more
+// entries than
 // the entry table (kMaxEnt).  (With 64-head items the partials' round trip
 // -- 128 KiB per split and query, written and read back -- costs as much as
 // the added parallelism gains: 80 queries in three splits measured slower
 // than unsplit.)  The splits taken only for parallelism are reduced until
 // the partials fit part_cap bytes.  K is the longest list of records
 // (dense mode: N).
-int choose_splits(int Q, int K, int W, bool dense, int& per, size_t part_cap) {
+int choose_splits(int Q, int K, int W, int& per, size_t part_cap) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
     const int need = (ntiles * kTile + kMaxEnt - 1) / kMaxEnt;  // splits the entry table needs
     int ns = need;
     if (decode_layout(Q)) {
-        const int target = dense ? 256 : 128;
-        const int want = (target + 4 * Q - 1) / (4 * Q);
+        const int want = 256 / (4 * Q);  // rounded down: never more items than compute units
         if (want > ns) ns = want;
     }
     if (ns > ntiles) ns = ntiles;
@@ -318,14 +320,14 @@ size_t dense_attn_ws_bytes(int B, int Tq, int H, int D, int N, int W) {
     if (H != kH || D != kD) return 0;
     int per;
     const int Q = B * Tq;
-    return part_bytes(Q, choose_splits(Q, N, W, true, per, SIZE_MAX));
+    return part_bytes(Q, choose_splits(Q, N, W, per, SIZE_MAX));
 }
 
 size_t sparse_attn_ws_bytes(int B, int Tq, int H, int D, int K, int W, size_t part_cap) {
     if (H != kH || D != kD) return 0;
     int per;
     const int Q = B * Tq;
-    return part_bytes(Q, choose_splits(Q, K, W, false, per, part_cap));
+    return part_bytes(Q, choose_splits(Q, K, W, per, part_cap));
 }
 
 int launch_sparse_attn(const AttnArgs& a, void* stream) {
@@ -351,7 +353,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         const bool dec = decode_layout(Q);
         p.dense_m = a.dense_m;
         p.n_rec = a.n_rec;
-        p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, a.dense_m > 0, p.per_split, a.part_cap);
+        p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, p.per_split, a.part_cap);
         p.part_o = nullptr;
         p.part_ml = nullptr;
         if (p.nsplit > 1) {

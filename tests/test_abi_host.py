@@ -204,19 +204,20 @@ def _attn_noalloc(L, **kw):
 def test_sparse_attn_noalloc_validation(L):
     """The allocation-free entry point validates like csa2_sparse_attn.  A
     shape whose workspace call splits its queries into more partials than
-    the 6 MiB static scratch holds (24 queries x 640 entries at two splits:
-    6.02 MiB) is not refused: the splits taken only for parallelism give
-    way, so it passes validation and fails here only at the launch (no
-    device on this host)."""
+    the 6 MiB static scratch holds (16 queries x 640 entries in four splits:
+    8 MiB) is not refused: the splits taken only for parallelism give way,
+    so it passes validation and fails here only at the launch (no device on
+    this host).  Sparse decode shapes split into at most 64 partials."""
     assert _attn_noalloc(L, W=129) == B.CSA2_EINVAL
     assert _attn_noalloc(L, out=FAKE + 8) == B.CSA2_EINVAL
     assert _attn_noalloc(L, kvdt=2) == B.CSA2_EINVAL
-    need = L.csa2_sparse_attn_workspace_bytes(24, 1, 64, 512, 512, 128)
+    need = L.csa2_sparse_attn_workspace_bytes(16, 1, 64, 512, 512, 128)
     assert need > 6 << 20
-    assert _attn_noalloc(L, B=24, K=512) == B.CSA2_EHIP
-    # the decode shapes of the benchmark fit
-    for Q in (8, 16, 64):
-        assert L.csa2_sparse_attn_workspace_bytes(Q, 1, 64, 512, 512, 128) <= 6 << 20
+    assert _attn_noalloc(L, B=16, K=512) == B.CSA2_EHIP
+    # at most 64 partials of 64 heads x 512 channels (fp32), plus (max, sum)
+    for Q in range(1, 65):
+        assert L.csa2_sparse_attn_workspace_bytes(Q, 1, 64, 512, 2048, 256) <= 64 * (128 << 10) + (32 << 10)
+    assert L.csa2_sparse_attn_workspace_bytes(64, 1, 64, 512, 512, 128) == 0
 
 
 def test_dense_attn_validation(L):
