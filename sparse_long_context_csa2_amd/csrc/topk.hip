@@ -750,24 +750,26 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
         }
         thr = prefix;
     }
-    // chosen columns, in column order: keys above the bin, and the bin's
-    // keys whose composite reaches the threshold
-    const uint32_t kbin = b1 >= 0 ? (common | (static_cast<uint32_t>(b1) << bsh)) >> bsh : 0u;
-    auto chosen = [&](int i) -> bool {
-        const uint32_t k = kk[i];
-        if (!k) return false;
-        if (b1 < 0) return true;
-        const uint32_t b = k >> bsh;
-        return b > kbin || (b == kbin && composite(k, rec_of_col(c0 + i)) >= thr);
-    };
-    int nc = 0;
+    // chosen columns, in column order: the composite key reaches the
+    // threshold, i.e. the key is above the threshold's key part, or equal
+    // to it with ~record reaching the low part (with at most K valid keys
+    // the threshold is 1 << 32: every valid key).  Decided once per key, as
+    // a bit mask, with 32-bit compares.
+    const uint32_t thr_k = b1 >= 0 ? static_cast<uint32_t>(thr >> 32) : 1u;
+    const uint32_t thr_lo = b1 >= 0 ? static_cast<uint32_t>(thr) : 0u;
+    uint32_t chosen = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) nc += chosen(i);
+    for (int i = 0; i < KPT; ++i) {
+        const uint32_t k = kk[i];
+        bool ch = k > thr_k;
+        if (k == thr_k) ch = ~static_cast<uint32_t>(rec_of_col(c0 + i)) >= thr_lo;
+        chosen |= static_cast<uint32_t>(ch) << i;
+    }
     int take;
-    int pos = row_excl_scan(nc, sh.scan, &take);
+    int pos = row_excl_scan(__popc(chosen), sh.scan, &take);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-        if (chosen(i) && pos < K) orow[pos++] = rec_of_col(c0 + i);
+        if (((chosen >> i) & 1u) && pos < K) orow[pos++] = rec_of_col(c0 + i);
     for (int i = take + t; i < K; i += kRT) orow[i] = -1;
 }
 
