@@ -549,7 +549,10 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
 
 // ---------------------------------------------------------------- rows up to 16384 columns, one workgroup each
 
-// One workgroup of 1024 threads per row, the row's keys in registers:
+// One workgroup of NT threads per row (1024 threads of 16 keys for rows up
+// to 16384 columns; 512 of 8 for rows up to 4096, whose eight waves meet
+// faster at the kernel's many barriers: 7% faster than 1024 threads of 4
+// keys, while 256 of 16 were 18% slower), the row's keys in registers:
 // thread t owns the KPT consecutive columns KPT*t .. KPT*t+KPT-1.  One LDS
 // histogram of the top 12 key bits finds the boundary bin; an exact radix
 // select over the composite keys of that bin runs straight over the
@@ -560,16 +563,20 @@ __global__ __launch_bounds__(kNT) void topk_small_kernel(TopkP p) {
 // one launch: for the few long rows of decode this replaces a chain of
 // kernels that hand lists from workgroup to workgroup.
 constexpr int kRT = 1024;
-constexpr int kRW = kRT / kWave;
 constexpr int kRowCols = kRT * 16;  // columns per row at most (16 keys per thread fit the registers)
+constexpr int kRTShort = 512;       // threads per row for rows up to kRTShort * 8 columns
 
+template <int NT>
 struct RowScan {
+    static constexpr int kRW = NT / kWave;
     int wave_tot[kRW];
     int res[3];
     uint32_t lo[kRW], hi[kRW];
 };
 
-__device__ int row_excl_scan(int v, RowScan& s, int* total) {
+template <int NT>
+__device__ int row_excl_scan(int v, RowScan<NT>& s, int* total) {
+    constexpr int kRW = NT / kWave;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
@@ -591,14 +598,14 @@ __device__ int row_excl_scan(int v, RowScan& s, int* total) {
     return off + x - v;
 }
 
-// Scanning nb = 4 * kRT (PER = 4) or 256 (PER = 0: threads below 256 hold
+// Scanning nb = NT * PER (PER > 0) or 256 (PER = 0: threads below 256 hold
 // one bin each) bins from the top, the bin where the running count first
 // reaches `need`: returns it (-1 if the total is below need) and the number
 // still needed from it, and that bin's count.
-template <int PER>
-__device__ int row_find(const int* hist, int need, RowScan& s, int* rest, int* bin_count) {
+template <int PER, int NT>
+__device__ int row_find(const int* hist, int need, RowScan<NT>& s, int* rest, int* bin_count) {
     constexpr int P = PER ? PER : 1;
-    constexpr int NB = PER ? kRT * PER : 256;
+    constexpr int NB = PER ? NT * PER : 256;
     int loc[P];
     int sum = 0;
     const int t = threadIdx.x;
@@ -633,16 +640,18 @@ __device__ int row_find(const int* hist, int need, RowScan& s, int* rest, int* b
     return bin;
 }
 
+template <int NT>
 struct __align__(16) RowShared {
     int hist[kBins];
     int hist8[256];
-    int pool[kRowCols / 4];  // the row's pool (blocks of at least 4 records)
-    RowScan scan;
+    int pool[NT * 4];  // the row's pool (NT * 16 columns, blocks of at least 4 records)
+    RowScan<NT> scan;
 };
 
-template <int KPT, bool POOL>
-__global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
-    __shared__ RowShared sh;
+template <int KPT, bool POOL, int NT>
+__global__ __launch_bounds__(NT) void topk_row_kernel(TopkP p) {
+    constexpr int kRW = NT / kWave;
+    __shared__ RowShared<NT> sh;
     const int row = blockIdx.x;
     const int n = p.ncols;
     const int K = p.K;
@@ -651,9 +660,9 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
     int32_t* orow = p.idx + static_cast<size_t>(row) * K;
     if constexpr (POOL) {
         const int32_t* prow = p.pool + static_cast<size_t>(row) * p.P;
-        for (int i = t; i < p.P; i += kRT) sh.pool[i] = prow[i];
+        for (int i = t; i < p.P; i += NT) sh.pool[i] = prow[i];
     }
-    for (int i = t; i < kBins; i += kRT) sh.hist[i] = 0;
+    for (int i = t; i < kBins; i += NT) sh.hist[i] = 0;
     const int lane = t & 63, wave = t >> 6;
     // the thread's scores, all loads in flight at once
     const int c0 = KPT * t;
@@ -721,7 +730,7 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
     unsigned long long thr = 0ull;
     if (nvalid > K) {
         int need, bc;
-        b1 = row_find<4>(sh.hist, K, sh.scan, &need, &bc);
+        b1 = row_find<kBins / NT>(sh.hist, K, sh.scan, &need, &bc);
         // radix select of the `need` largest composite keys of bin b1, over
         // the registers; the common prefix and the bin fix the composite's
         // bits from 32 + bsh up
@@ -770,7 +779,7 @@ __global__ __launch_bounds__(kRT) void topk_row_kernel(TopkP p) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
         if (((chosen >> i) & 1u) && pos < K) orow[pos++] = rec_of_col(c0 + i);
-    for (int i = take + t; i < K; i += kRT) orow[i] = -1;
+    for (int i = take + t; i < K; i += NT) orow[i] = -1;
 }
 
 // ---------------------------------------------------------------- long rows
@@ -1190,13 +1199,13 @@ int run_topk(TopkP p, void* ws, hipStream_t st) {
     }
     if (!p.sort_by_key && p.ncols <= kRowCols && (!p.pool || p.blk >= 4)) {
         // rows up to 16384 columns (record ids or pooled): one workgroup each
-#define CSA2_ROW(KPT)                                                                                    \
-    if (p.pool) hipLaunchKernelGGL((topk_row_kernel<KPT, true>), dim3(p.rows), dim3(kRT), 0, st, p);     \
-    else hipLaunchKernelGGL((topk_row_kernel<KPT, false>), dim3(p.rows), dim3(kRT), 0, st, p);
-        if (p.ncols <= 4 * kRT) {
-            CSA2_ROW(4)
+#define CSA2_ROW(KPT, NT)                                                                                \
+    if (p.pool) hipLaunchKernelGGL((topk_row_kernel<KPT, true, NT>), dim3(p.rows), dim3(NT), 0, st, p);  \
+    else hipLaunchKernelGGL((topk_row_kernel<KPT, false, NT>), dim3(p.rows), dim3(NT), 0, st, p);
+        if (p.ncols <= 8 * kRTShort) {
+            CSA2_ROW(8, kRTShort)
         } else {
-            CSA2_ROW(16)
+            CSA2_ROW(16, kRT)
         }
 #undef CSA2_ROW
         return static_cast<int>(hipGetLastError());
