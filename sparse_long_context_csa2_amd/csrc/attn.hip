@@ -223,8 +223,13 @@ int num_cus() {
 constexpr int kCUs = 256;
 
 // Decode layout (one 16-head group per item) when the queries' four head
-// groups fit on the chip at once; otherwise 64 heads per item.
-bool decode_layout(int Q) { return 4 * Q <= kCUs; }
+// groups fit on the chip at once and a query's list fits one item's entry
+// table (emax entries); otherwise 64 heads per item.  Long lists (dense
+// mode) thus take 64-head items split across the chip: their tiles are
+// computed once for all heads (the decode layout's four head groups would
+// each copy and multiply every tile), at twice the decode layout's matrix
+// work per wave and tile.
+bool decode_layout(int Q, int emax) { return 4 * Q <= kCUs && emax <= kMaxEnt; }
 
 // Bytes of split partials (fp32 O, then (max, sum) per head) for Q
 // queries in ns splits.
@@ -236,28 +241,30 @@ size_t part_bytes(int Q, int ns) {
 }
 
 // Entry splits per query.  Every split writes an fp32 partial O of its
-// heads that attn_combine_kernel reads back, so splits are used only in
-// the decode layout, while its items would otherwise leave most compute
-// units idle: at most 256 items in all, one per compute unit (four per
-// split; measured against 128 and 512: C4's 16 queries in four splits run
-// 8% faster than in two, and 21% faster than in eight), so at most 64
-// partials (8 MiB) for sparse lists; and wherever a split would hold more
-// entries than
-// the entry table (kMaxEnt).  (With 64-head items the partials' round trip
-// -- 128 KiB per split and query, written and read back -- costs as much as
-// the added parallelism gains: 80 queries in three splits measured slower
-// than unsplit.)  The splits taken only for parallelism are reduced until
-// the partials fit part_cap bytes.  K is the longest list of records
-// (dense mode: N).
+// heads that attn_combine_kernel reads back, so splits are used only while
+// the items would otherwise leave most compute units idle, and wherever a
+// split would hold more entries than the entry table (kMaxEnt):
+//  * decode layout: at most 256 items in all, one per compute unit (four
+//    per split; measured against 128 and 512: C4's 16 queries in four
+//    splits run 8% faster than in two, and 21% faster than in eight), so at
+//    most 64 partials (8 MiB);
+//  * 64-head items of lists longer than the entry table (dense mode): one
+//    item per compute unit as well (C6's 8 queries in 29 splits: 37 us;
+//    half as many splits: 42 us);
+//  * other 64-head items are not split for parallelism: the partials'
+//    round trip (128 KiB per split and query, written and read back) costs
+//    as much as it gains (80 queries in three splits: 37.3 against 35.7 us
+//    unsplit).
+// The splits taken only for parallelism are reduced until the partials fit
+// part_cap bytes.  K is the longest list of records (dense mode: N).
 int choose_splits(int Q, int K, int W, int& per, size_t part_cap) {
     const int emax = K + W;
     const int ntiles = (emax + kTile - 1) / kTile;
     const int need = (ntiles * kTile + kMaxEnt - 1) / kMaxEnt;  // splits the entry table needs
     int ns = need;
-    if (decode_layout(Q)) {
-        const int want = 256 / (4 * Q);  // rounded down: never more items than compute units
-        if (want > ns) ns = want;
-    }
+    // rounded down: never more items than compute units
+    const int want = decode_layout(Q, emax) ? kCUs / (4 * Q) : (emax > kMaxEnt ? kCUs / Q : 0);
+    if (want > ns) ns = want;
     if (ns > ntiles) ns = ntiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
@@ -350,7 +357,7 @@ int launch_sparse_attn(const AttnArgs& a, void* stream) {
         p.rope_base = a.rope_base;
         p.out = a.out;
         p.out_bf16 = a.out_dtype == DT_BF16;
-        const bool dec = decode_layout(Q);
+        const bool dec = decode_layout(Q, (a.dense_m ? a.N : a.K) + a.W);
         p.dense_m = a.dense_m;
         p.n_rec = a.n_rec;
         p.nsplit = choose_splits(Q, a.dense_m ? a.N : a.K, a.W, p.per_split, a.part_cap);
