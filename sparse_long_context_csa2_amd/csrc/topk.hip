@@ -944,19 +944,26 @@ __global__ __launch_bounds__(kNT) void topk_select_kernel(TopkP p) {
     // ---- last workgroup of this row ----
     // chunk c's entries sit at [c kChunk, c kChunk + n_c) of the lists;
     // thread t sums the counts of its (contiguous) chunks, one scan places them
+    // (the counts are loaded once, all at once, and kept for the placing)
     const int cpt = (nch + kNT - 1) / kNT;
+    constexpr int kCpt = kMaxChunks / kNT;
+    int cv[kCpt];
     int csum = 0;
-    for (int j = 0; j < cpt; ++j) {
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
         const int c = static_cast<int>(threadIdx.x) * cpt + j;
-        csum += c < nch ? ld_dev(ccnt + c) : 0;
+        cv[j] = j < cpt && c < nch ? ld_dev(ccnt + c) : 0;
     }
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) csum += cv[j];
     int total;
     int cb = block_excl_scan(csum, sh.scan, &total);
-    for (int j = 0; j < cpt; ++j) {
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
         const int c = static_cast<int>(threadIdx.x) * cpt + j;
-        if (c < nch) {
+        if (j < cpt && c < nch) {
             sh.cbase[c] = cb;
-            cb += ld_dev(ccnt + c);
+            cb += cv[j];
         }
     }
     if (threadIdx.x == 0) sh.cbase[nch] = total;
