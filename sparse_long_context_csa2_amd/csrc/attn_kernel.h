@@ -132,25 +132,6 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 __device__ __forceinline__ void wait_copies_but_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 __device__ __forceinline__ void wait_copies_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The first tile's wait of an item issued after the previous item's output
-// stores: the counter retires in issue order, so the n stores issued after
-// the tile copies are left in flight with them (they drain during the
-// tile, and the next tile's wait covers them).  n: 0, or the 64-head
-// layout's 32 stores per wave (34 with split partials); `more`: the next
-// tile's 8 copies went out as well.
-__device__ __forceinline__ void wait_first_tile(int n, bool more) {
-    if (n == 32) {
-        if (more) asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    } else if (n == 34) {
-        if (more) asm volatile("s_waitcnt vmcnt(42)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(34)" ::: "memory");
-    } else {
-        if (more) wait_copies_but_8();
-        else wait_copies_all();
-    }
-}
-
 // Copies the 1 KiB row at rp (a wave-uniform address, held in SGPRs)
 // straight into LDS at byte address lds: lane l moves the 16 bytes at
 // rp + voff with voff = 16 l (gfx950 global_load_lds_dwordx4, LDS address
@@ -662,14 +643,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         if constexpr (KVDT == DT_BF16) {
             if (ntile > 1) issue(1, 1);
         }
-        // the previous item's output stores, per wave, still in flight
-        // after its finish (64-head layout: 2 x 16 staged rows, and two
-        // (max, sum) stores with split partials)
-        int nfin = 0;
         if (prev_qr >= 0) {
             finish(prev_qr, prev_split, prev_h);
             lds_sync();  // every wave is done with the previous item's rope table
-            if constexpr (!kDec) nfin = p.nsplit == 1 ? 32 : 34;
         }
         m_run = -__builtin_huge_valf();
         l_run = 0.f;
@@ -691,8 +667,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnP p) {
         auto tile_ready = [&](int it) {
             const int buf = it % NB;
             if constexpr (KVDT == DT_BF16) {
-                if (it == 0) wait_first_tile(nfin, it + 1 < ntile);
-                else if (it + 1 < ntile) wait_copies_but_8();
+                if (it + 1 < ntile) wait_copies_but_8();
                 else wait_copies_all();
                 lds_sync();  // tile `it` landed; the buffer two tiles ahead is free
                 if (it == 0) settle_q(qf);
