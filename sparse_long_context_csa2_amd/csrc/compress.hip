@@ -31,7 +31,7 @@
 // (w = hi + lo to 2^-16 relative), float32 record rows likewise, so the
 // bf16 products accumulate in float32 to about float32 accuracy.  W_ik is
 // staged transposed in LDS 64 input channels at a time; the keys go
-// through LDS once more to be quantized one record per wave.
+// through LDS once more to be quantized, four threads per record.
 #include <stdint.h>
 
 #include <type_traits>
@@ -141,7 +141,8 @@ __device__ __forceinline__ float raw_at(const RawCh<CPL, BF>& r, int j) {
     else return __uint_as_float(r.w[j]);
 }
 
-// NB bytes (a power of two, the packed words w) to a naturally aligned address.
+// NB bytes (1, 2, 4, 8 or a multiple of 16; the packed words w) to an
+// address aligned to min(NB, 16).
 template <int NB>
 __device__ __forceinline__ void st_bytes(uint8_t* dst, const uint32_t* w) {
     if constexpr (NB == 1) {
@@ -550,38 +551,55 @@ __global__ __launch_bounds__(256) void keys_kernel(CompP p) {
                 kout[(rbase + 16 * a + 4 * g + v) * kp + 16 * (t_lo + t) + r] = acc[a][t][v] * rs[a][v];
     __syncthreads();
 
-    // ---- quantize the keys: one wave per record, lane l owns dims kpl*l ..
-    constexpr int kpl = Di / 64;
-    for (int rr = wave; rr < kKeyRows; rr += 4) {
-        const int sr = s_base + rr;
-        if (sr >= n_w) break;
-        const size_t cr = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + sr);
-        float v[kpl];
+    // ---- quantize the keys: thread t takes record t / 4, key columns
+    // kq*(t % 4) .. +kq (whole MXFP4 blocks: kq is 32 or 64 there); a
+    // record's maximum for its E4M3 scale is a reduction over its four
+    // neighbouring lanes
+    constexpr int kq = Di / 4;
+    const int rr = tid >> 2, qd = tid & 3, kd = kq * qd;
+    const int sr = s_base + rr;
+    const bool ok = sr < n_w;
+    const size_t cr = static_cast<size_t>(b) * p.N_out + static_cast<size_t>(s0 + (ok ? sr : 0));
+    float v[kq];
 #pragma unroll
-        for (int j = 0; j < kpl; ++j) v[j] = kout[rr * kp + kpl * lane + j];
-        const int kd = kpl * lane;
-        if (p.k_dt == DT_F32) {
+    for (int j = 0; j < kq / 4; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(kout + rr * kp + kd + 4 * j);
 #pragma unroll
-            for (int j = 0; j < kpl; ++j) reinterpret_cast<float*>(p.k)[cr * Di + kd + j] = v[j];
-        } else if (p.k_dt == DT_BF16) {
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
+    }
+    if (p.k_dt == DT_F32) {
+        f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.k) + cr * Di + kd);
 #pragma unroll
-            for (int j = 0; j < kpl; ++j)
-                reinterpret_cast<uint16_t*>(p.k)[cr * Di + kd + j] = static_cast<uint16_t>(f32_to_bf16_rne(v[j]));
-        } else if (p.k_dt == DT_E4M3) {
+        for (int j = 0; j < kq / 4; ++j)
+            if (ok) dst[j] = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+    } else if (p.k_dt == DT_BF16) {
+        uint32_t w[kq / 2];
+#pragma unroll
+        for (int j = 0; j < kq / 2; ++j) w[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        if (ok) st_bytes<2 * kq>(p.k + (cr * Di + kd) * 2, w);
+    } else if (p.k_dt == DT_E4M3) {
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < kq; ++j) am = fmaxf(am, fabsf(v[j]));
+        am = lanes_max<4>(am);
+        const float scl = am / 448.f;
+        const float inv = scl > 0.f ? 1.f / scl : 0.f;
+        uint32_t w[kq / 4];
+#pragma unroll
+        for (int j = 0; j < kq / 4; ++j)
+            w[j] = e4m3_encode2(v[4 * j] * inv, v[4 * j + 1] * inv) |
+                   (e4m3_encode2(v[4 * j + 2] * inv, v[4 * j + 3] * inv) << 16);
+        if (ok) {
+            st_bytes<kq>(p.k + cr * Di + kd, w);
+            if (qd == 0) reinterpret_cast<float*>(p.k_scale)[cr] = scl;
+        }
+    } else if constexpr (kq % 32 == 0) {  // MXFP4: blocks of 32 dims share 2^e, e = floor(log2 max|x|) - 2
+        uint32_t w[kq / 8], sc = 0u;
+#pragma unroll
+        for (int blk = 0; blk < kq / 32; ++blk) {
             float am = 0.f;
 #pragma unroll
-            for (int j = 0; j < kpl; ++j) am = fmaxf(am, fabsf(v[j]));
-            am = lanes_max<64>(am);
-            const float scl = am / 448.f;
-            const float inv = scl > 0.f ? 1.f / scl : 0.f;
-#pragma unroll
-            for (int j = 0; j < kpl; ++j) p.k[cr * Di + kd + j] = static_cast<uint8_t>(e4m3_encode(v[j] * inv));
-            if (lane == 0) reinterpret_cast<float*>(p.k_scale)[cr] = scl;
-        } else if constexpr (kpl % 2 == 0) {  // MXFP4: blocks of 32 dims share 2^e, e = floor(log2 max|x|) - 2
-            float am = 0.f;
-#pragma unroll
-            for (int j = 0; j < kpl; ++j) am = fmaxf(am, fabsf(v[j]));
-            am = lanes_max<32 / kpl>(am);
+            for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(v[32 * blk + j]));
             int e = -127;
             if (am > 0.f) {
                 const int be = static_cast<int>((__float_as_uint(am) >> 23) & 0xFFu);
@@ -589,10 +607,19 @@ __global__ __launch_bounds__(256) void keys_kernel(CompP p) {
                 e = e < -127 ? -127 : (e > 127 ? 127 : e);
             }
             const float inv = __builtin_amdgcn_ldexpf(1.f, -e);
-            uint32_t w[1] = {e2m1_encode2<0>(0u, v[0] * inv, v[1] * inv)};
-            if constexpr (kpl == 4) w[0] = e2m1_encode2<1>(w[0], v[2] * inv, v[3] * inv);
-            st_bytes<kpl / 2>(p.k + cr * (Di / 2) + kd / 2, w);
-            if (kd % 32 == 0) p.k_scale[cr * (Di / 32) + kd / 32] = static_cast<uint8_t>(e + 127);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float* x = v + 32 * blk + 8 * j;
+                uint32_t wd = e2m1_encode2<0>(0u, x[0] * inv, x[1] * inv);
+                wd = e2m1_encode2<1>(wd, x[2] * inv, x[3] * inv);
+                wd = e2m1_encode2<2>(wd, x[4] * inv, x[5] * inv);
+                w[4 * blk + j] = e2m1_encode2<3>(wd, x[6] * inv, x[7] * inv);
+            }
+            sc |= static_cast<uint32_t>(e + 127) << (8 * blk);
+        }
+        if (ok) {
+            st_bytes<kq / 2>(p.k + cr * (Di / 2) + kd / 2, w);
+            st_bytes<kq / 32>(p.k_scale + cr * (Di / 32) + kd / 32, &sc);
         }
     }
 }
