@@ -20,10 +20,11 @@
 // CPL*l+CPL-1 and loads them with 16-byte loads, four tokens at once; the
 // softmax runs over each group of four tokens with one exponential per
 // token and channel; the row's mean square is a wave reduction; the
-// rotary angles are computed one pair per lane (angle in double precision
-// from a per-workgroup table of inverse frequencies) and shuffled to the
-// lanes that own the pairs; the quantized row is written with one packed
-// store per lane.
+// cosines and sines of all the workgroup's records are tabulated in LDS at
+// the start (angle in double precision, every thread a few), so a rotation
+// is a table read by the lanes that own the pair; the quantized row is
+// written with one packed store per lane.  Each record's first token group
+// is loaded while the previous record is finished.
 //
 // keys_kernel forms the keys as a matrix product on the matrix cores: 64
 // records (rows, read back from the cache just written, dequantized
@@ -162,29 +163,57 @@ __device__ __forceinline__ void st_bytes(uint8_t* dst, const uint32_t* w) {
 
 // ---------------------------------------------------------------- records
 
-template <int CPL, bool BF>
+template <int CPL, bool BF, bool G4>
 __global__ __launch_bounds__(kPoolWaves * 64) void pool_kernel(CompP p) {
-    __shared__ double inv_sh[kMaxRopePairs];
+    __shared__ double inv_sh[kMaxRopePairs];  // inverse frequencies
+    extern __shared__ float2 rot_sh[];  // [kPoolRecPerWG][rope_dims / 2] cos, sin per record and pair
     constexpr int D = CPL * 64;
+    constexpr int kG = G4 ? 4 : 1;  // tokens of a record's first group (m >= 4: four)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int b = blockIdx.y;
-    const int64_t t0 = p.t0[b];
-    if (t0 < 0) return;  // nothing of this sequence is written (workgroup-uniform)
-    const int64_t s0 = t0 / p.m;
     const int n_rec = p.T / p.m;
+    const int d0 = CPL * lane;
+    auto rec_of = [&](int k) { return blockIdx.x * kPoolRecPerWG + k * kPoolWaves + wave; };
+    auto row_of = [&](int s) {  // element of this lane's first channel in the record's first token row
+        return (static_cast<size_t>(b) * p.T + static_cast<size_t>(min(s, n_rec - 1)) * p.m) * D + d0;
+    };
+    // A record's first token group is requested while the previous record
+    // is normalized, rotated and stored (the first record's before the
+    // set-up below).
+    RawCh<CPL, BF> gc[kG], gz[kG];
+    auto load_group = [&](size_t row0) {
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            load_raw(p.c, row0 + static_cast<size_t>(u) * D, gc[u]);
+            load_raw(p.z, row0 + static_cast<size_t>(u) * D, gz[u]);
+        }
+    };
+    const int64_t t0 = p.t0[b];
     const int npairs = p.rope_dims / 2;
     const int r0 = D - p.rope_dims;
-    const int d0 = CPL * lane;
     for (int j = tid; j < npairs; j += kPoolWaves * 64) inv_sh[j] = rope_inv_freq(j, p.rope_dims, p.rope_base);
+    load_group(row_of(rec_of(0)));
+    if (t0 < 0) return;  // nothing of this sequence is written (workgroup-uniform)
+    const int64_t s0 = t0 / p.m;
+    __syncthreads();
+    // cosines and sines of the workgroup's records (record kr = k * kPoolWaves
+    // + wave is rotated to position t0 + s m + m - 1), all threads at once
+    for (int e = tid; e < kPoolRecPerWG * npairs; e += kPoolWaves * 64) {
+        const int kr = e / npairs, j = e - kr * npairs;
+        const int64_t pos = t0 + static_cast<int64_t>(blockIdx.x * kPoolRecPerWG + kr) * p.m + p.m - 1;
+        float cs, sn;
+        rope_cos_sin(pos, inv_sh[j], cs, sn);
+        rot_sh[e] = make_float2(cs, sn);
+    }
     __syncthreads();
     float gain[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) gain[j] = p.gain[d0 + j];
 
     for (int k = 0; k < kPoolRecPerWave; ++k) {
-        const int s = blockIdx.x * kPoolRecPerWG + k * kPoolWaves + wave;
+        const int s = rec_of(k);
         if (s >= n_rec || s0 + s >= p.N_out) break;  // wave-uniform; s grows with k
         // ---- channel-wise softmax pooling over the block's m tokens, four at a time
         float mx[CPL], sm[CPL], ac[CPL];
@@ -194,19 +223,13 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_kernel(CompP p) {
             sm[j] = 0.f;
             ac[j] = 0.f;
         }
-        const size_t row0 = (static_cast<size_t>(b) * p.T + static_cast<size_t>(s) * p.m) * D + d0;
+        const size_t row0 = row_of(s);
         // weights 2^(z log2(e) - max log2(e)); the running sums are rescaled
         // when a later group of tokens raises the maximum
         constexpr float kL2E = 1.4426950408889634f;
-        auto tokens = [&](int i0, auto nt_c, auto first_c) {
-            constexpr int NT = decltype(nt_c)::value;
+        auto fold = [&](const auto& cr, const auto& zr, auto first_c) {
+            constexpr int NT = sizeof(cr) / sizeof(cr[0]);
             constexpr bool kFirst = decltype(first_c)::value;
-            RawCh<CPL, BF> cr[NT], zr[NT];
-#pragma unroll
-            for (int u = 0; u < NT; ++u) {
-                load_raw(p.c, row0 + static_cast<size_t>(i0 + u) * D, cr[u]);
-                load_raw(p.z, row0 + static_cast<size_t>(i0 + u) * D, zr[u]);
-            }
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 float nm = mx[j];
@@ -230,17 +253,27 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_kernel(CompP p) {
                 ac[j] = aa;
             }
         };
-        using Four = std::integral_constant<int, 4>;
+        auto tokens = [&](int i0, auto nt_c) {
+            constexpr int NT = decltype(nt_c)::value;
+            RawCh<CPL, BF> cr[NT], zr[NT];
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                load_raw(p.c, row0 + static_cast<size_t>(i0 + u) * D, cr[u]);
+                load_raw(p.z, row0 + static_cast<size_t>(i0 + u) * D, zr[u]);
+            }
+            fold(cr, zr, std::false_type{});
+        };
+        fold(gc, gz, std::true_type{});
         using One = std::integral_constant<int, 1>;
-        int i0 = 0;
-        if (p.m >= 4) {
-            tokens(0, Four{}, std::true_type{});
-            for (i0 = 4; i0 + 4 <= p.m; i0 += 4) tokens(i0, Four{}, std::false_type{});
-        } else {
-            tokens(0, One{}, std::true_type{});
-            i0 = 1;
+        int i0 = kG;
+        if constexpr (G4) {  // further groups of four go through the same registers
+            for (; i0 + 4 <= p.m; i0 += 4) {
+                load_group(row0 + static_cast<size_t>(i0) * D);
+                fold(gc, gz, std::false_type{});
+            }
         }
-        for (; i0 < p.m; ++i0) tokens(i0, One{}, std::false_type{});
+        for (; i0 < p.m; ++i0) tokens(i0, One{});
+        if (k + 1 < kPoolRecPerWave) load_group(row_of(rec_of(k + 1)));
         // ---- RMSNorm
         float x[CPL];
         float ss = 0.f;
@@ -253,21 +286,17 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_kernel(CompP p) {
         const float rn = rsqrtf(ss / static_cast<float>(D) + p.eps);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) x[j] *= rn * gain[j];
-        // ---- RoPE at the block's last token: lane l computes pair 64*q + l,
-        // the owners of each pair's two channels fetch its cos / sin
-        const int64_t pos = t0 + static_cast<int64_t>(s) * p.m + p.m - 1;
-        for (int q = 0; 64 * q < npairs; ++q) {
-            float cs = 1.f, sn = 0.f;
-            if (64 * q + lane < npairs) rope_cos_sin(pos, inv_sh[64 * q + lane], cs, sn);
+        // ---- RoPE at the block's last token (pairs never straddle lanes: CPL
+        // and r0 are even)
+        if (d0 + CPL > r0) {
+            const float2* rot = rot_sh + (k * kPoolWaves + wave) * npairs;
 #pragma unroll
             for (int j = 0; j < CPL; j += 2) {
-                const int src = ((d0 + j - r0) >> 1) - 64 * q;  // lane holding this pair's angle now
-                const float c2 = __shfl(cs, src & 63, kWave);
-                const float s2 = __shfl(sn, src & 63, kWave);
-                if (d0 + j >= r0 && src >= 0 && src < 64) {
+                if (d0 + j >= r0) {
+                    const float2 cs = rot[(d0 + j - r0) >> 1];
                     const float a = x[j], bb = x[j + 1];
-                    x[j] = a * c2 - bb * s2;
-                    x[j + 1] = a * s2 + bb * c2;
+                    x[j] = a * cs.x - bb * cs.y;
+                    x[j + 1] = a * cs.y + bb * cs.x;
                 }
             }
         }
@@ -650,9 +679,13 @@ int launch_compress(const CompressArgs& a, void* stream) {
     const dim3 pgrid((n_rec + kPoolRecPerWG - 1) / kPoolRecPerWG, a.B);
     const dim3 pblk(kPoolWaves * 64);
     const bool bf = a.in_dtype == DT_BF16;
-#define CSA2_POOL(C)                                                                     \
-    if (bf) hipLaunchKernelGGL((pool_kernel<C, true>), pgrid, pblk, 0, st, p);            \
-    else hipLaunchKernelGGL((pool_kernel<C, false>), pgrid, pblk, 0, st, p);
+    const bool g4 = a.m >= 4;
+    const size_t rot = static_cast<size_t>(kPoolRecPerWG) * (a.rope_dims / 2) * sizeof(float2);
+#define CSA2_POOL(C)                                                                          \
+    if (bf && g4) hipLaunchKernelGGL((pool_kernel<C, true, true>), pgrid, pblk, rot, st, p);      \
+    else if (bf) hipLaunchKernelGGL((pool_kernel<C, true, false>), pgrid, pblk, rot, st, p);      \
+    else if (g4) hipLaunchKernelGGL((pool_kernel<C, false, true>), pgrid, pblk, rot, st, p);      \
+    else hipLaunchKernelGGL((pool_kernel<C, false, false>), pgrid, pblk, rot, st, p);
     switch (a.D / 64) {
         case 2: CSA2_POOL(2) break;
         case 4: CSA2_POOL(4) break;

@@ -965,6 +965,8 @@ def test_group_graph_replay():
     (256, 192, 48, 8, "f32", ("fp4", "bf16")),
     (256, 256, 48, 8, "f32", ("e4m3", "mxfp4")),
     (1024, 64, 32, 2, "bf16", ("fp4", "e4m3")),
+    (512, 128, 48, 6, "bf16", ("bf16", "e4m3")),
+    (256, 128, 1040, 8, "bf16", ("fp4", "mxfp4")),
 ])
 def test_compress_records_and_keys(D, Di, T, m, idt, fmts):
     """Records pooled from token rows (channel-wise softmax gates), RMS-
