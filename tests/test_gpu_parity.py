@@ -153,8 +153,12 @@ def _score_rows(rows, n, seed):
 
 
 @pytest.mark.parametrize("n,K", [(5, 8), (700, 8), (1024, 512), (1500, 300), (2048, 1), (2049, 2048), (4096, 100),
-                                 (4097, 2048), (12345, 700), (16384, 512), (16385, 64), (20000, 2048), (65536, 512)])
+                                 (4097, 2048), (12345, 700), (16384, 512), (16385, 64), (20000, 2048), (65536, 512),
+                                 (150000, 2048)])
 def test_topk_exact(n, K):
+    """Rows from one wave's keys to many workgroups': sub-rows whose K best
+    fit one second pass (16385 .. 65536 columns) and a row whose do not
+    (150000 columns, K = 2048: chunk histograms and a last-workgroup merge)."""
     _case(f"topk rows=4 n={n} K={K}")
     s = _score_rows(4, n, n + K)
     g = Bd.csa2_topk(torch.from_numpy(s).cuda(), K)
