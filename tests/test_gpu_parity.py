@@ -304,10 +304,12 @@ def test_topk_long_rows_few_selectable():
         assert np.all(g[r][len(ref):] == -1), f"row {r}"
 
 
-@pytest.mark.parametrize("blk,P,K", [(64, 700, 500), (2, 9000, 2048), (1, 12000, 300)])
+@pytest.mark.parametrize("blk,P,K", [(64, 700, 500), (4, 5000, 300), (2, 9000, 2048), (1, 12000, 300)])
 def test_topk_long_pooled_rows(blk, P, K):
     """Pooled rows past the one-workgroup paths (P*blk columns: 44800 with
-    blk=64; 18000 and 12000 with blocks of 1-2, where the row's columns are
+    blk=64 and 20000 with blk=4 take two passes over 8192-column sub-rows,
+    the last one partial, each sub-row's 2048 blocks of 4 filling its pool
+    slice; 18000 and 12000 with blocks of 1-2, where the row's columns are
     split over chunks, few enough with blk=1 that each keeps its own
     histogram): exact ties, -inf scores and -1 pool blocks; the chosen
     records in column order."""
